@@ -1,0 +1,253 @@
+"""Checks that pin the oracle to facts outside itself.
+
+Each ``check_*`` raises AssertionError on failure.  They are run one by one by
+``test_oracle_pins.py`` and, with mistakes planted into the oracle, by
+``test_oracle_mutations.py`` (every planted mistake must trip at least one).
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle
+from oracle import attention as A
+from oracle import cache as Cc
+from oracle import sizes as Z
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden_lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+# ------------------------------------------------------------------ sizes
+
+def check_printed_kv_sizes():
+    for name, L, n_kv, d, T, e, want in _golden_lines("kv_sizes.txt"):
+        got = Z.kv_cache_bytes(int(L), int(n_kv), int(d), int(T), int(e))
+        assert got == int(want), (name, got, want)
+
+
+def check_effective_context():
+    kv = {k: v for k, v in _golden_lines("effective_context.txt")}
+    got = Z.duo_effective_context(float(kv["R"]), int(kv["T"]), int(kv["S"]), int(kv["W"]))
+    assert abs(got - float(kv["tokens"])) < 1e-9, got
+
+
+def check_mixed_payload_closed_forms():
+    # All-retrieval mask -> the full-cache formula of the guide's section 1.
+    mask = [[1] * 8 for _ in range(80)]
+    assert Z.mixed_payload_bytes(mask, 1, 128000, 64, 1024, 128, 2) == 41943040000
+    # R = 2/8 in every layer -> the Memory_Duo formula of the guide's section 2.
+    mask = [[1, 1, 0, 0, 0, 0, 0, 0] for _ in range(80)]
+    got = Z.mixed_payload_bytes(mask, 1, 128000, 64, 1024, 128, 2)
+    assert got == Z.duo_cache_bytes(0.25, 128000, 64, 1024, 80, 8, 128, 2) == 10753146880
+    # Local/global layer formula reduces to the uniform one with L1 = 0.
+    assert Z.local_global_bytes(8, 128, 2, 0, 32, 4096, 1024) == Z.kv_cache_bytes(32, 8, 128, 4096, 2)
+    # ...and counts min(T, W) tokens for windowed layers.
+    assert Z.local_global_bytes(8, 128, 2, 32, 0, 4096, 1024) == Z.kv_cache_bytes(32, 8, 128, 1024, 2)
+
+
+# ------------------------------------------------------------------ cache placement
+
+def check_ring_example():
+    lines = _golden_lines("ring_window3.txt")
+    kv = {ln[0]: ln[1:] for ln in lines}
+    W = int(kv["window_size"][0])
+    ring = Cc.RingWindow(W)
+    for p in map(int, kv["appended"]):
+        ring.append(p, 10 * p)
+    want = [tuple(int(x) for x in s.strip("()").split(",")) for s in kv["ordered"]]
+    assert ring.ordered() == want, ring.ordered()
+    # The same example through a streaming head with no sinks: same slots.
+    h = Cc.StreamingHeadCache(0, W)
+    slots = [h.append(p, 10 * p) for p in map(int, kv["appended"])]
+    assert slots == [0, 1, 2, 0, 1]
+    assert {s: e for s, e in h.slots().items()} == {0: (3, 30), 1: (4, 40), 2: (2, 20)}
+
+
+def check_streaming_composition():
+    # A streaming head = the guide's append rule (sinks fill first, later tokens go
+    # to the window) composed with the ring of "Sliding-Window and Mixed Attention"
+    # fed only the tokens that arrive after the sinks are full.
+    for S, W, T in [(2, 3, 11), (4, 5, 23), (1, 4, 9), (3, 3, 3), (5, 2, 4)]:
+        h = Cc.StreamingHeadCache(S, W)
+        ring = Cc.RingWindow(W)
+        for p in range(T):
+            h.append(p, p)
+            if p >= S:
+                ring.append(p, p)
+        slots = h.slots()
+        for i in range(min(S, T)):
+            assert slots[i] == (i, i)
+        for r, e in enumerate(ring.items):
+            if e is not None:
+                assert slots[S + r] == e, (S, W, T, r)
+        assert len(slots) == min(T, S + W)
+
+
+def check_simulation_counts():
+    # The guide's simulation: 4 layers x 8 heads, S=4, W=16, R=0.25, 512 tokens,
+    # needle at 240.  Hand-derived: 8 retrieval heads (layers 1 and 2, even heads)
+    # hold 512 slots each, 24 streaming heads hold 4 + 16 slots each.
+    m = Cc.DuoKVManagerCounts(4, 8, 4, 16, 0.25)
+    m.ingest(512)
+    assert sum(m.mask.values()) == 8
+    assert [k for k, v in m.mask.items() if v] == [(1, 0), (1, 2), (1, 4), (1, 6), (2, 0), (2, 2), (2, 4), (2, 6)]
+    held = m.held_slots()
+    assert held == 8 * 512 + 24 * 20 == 4576
+    dense = 512 * 32
+    assert round(dense / held, 2) == 3.58
+    assert round((1 - held / dense) * 100, 2) == 72.07
+    assert m.heads_holding(240) == (8, 0)
+    assert m.heads_holding(3) == (8, 24)     # a sink token survives everywhere
+    assert m.heads_holding(500) == (8, 24)   # a recent token survives everywhere
+    assert m.heads_holding(495) == (8, 0)    # 17th most recent: just evicted
+
+
+def check_keep_set_is_visible_set():
+    # Route A (what a simulated cache keeps after T appends) equals route B
+    # (positions the newest query may see, by the visibility rule), every T.
+    for S, W in [(0, 1), (0, 3), (1, 1), (2, 3), (4, 5), (3, 1)]:
+        for T in range(1, 3 * (S + W) + 2):
+            kept = Cc.kept_positions(T, False, S, W)
+            vis = [j for j in range(T) if A.visible(T - 1, j, False, S, W)]
+            assert kept == vis, (S, W, T, kept, vis)
+            assert len(kept) == min(T, S + W)
+            assert Cc.kept_positions(T, True, S, W) == list(range(T))
+
+
+# ------------------------------------------------------------------ attention values
+
+def check_hand_cases():
+    # T=3, d=1, q=1, all keys 0 -> uniform weights over what is visible.
+    q = np.array([1.0]); K = np.zeros((3, 1)); V = np.array([[1.0], [2.0], [4.0]])
+    pos = [0, 1, 2]
+    assert abs(A.attend_row(q, K, V, pos, 2, True, 0, 1, 1.0)[0] - 7 / 3) < 1e-15
+    assert abs(A.attend_row(q, K, V, pos, 2, False, 1, 1, 1.0)[0] - 5 / 2) < 1e-15
+    assert abs(A.attend_row(q, K, V, pos, 2, False, 2, 1, 1.0)[0] - 7 / 3) < 1e-15
+    assert abs(A.attend_row(q, K, V, pos, 2, False, 0, 2, 1.0)[0] - 3.0) < 1e-15
+    # d=4, scale 1/2: scores 0 and ln 2 -> weights 1/3, 2/3 (pins sign and scale).
+    q = np.array([1.0, 0, 0, 0]); K = np.array([[0.0, 0, 0, 0], [2 * math.log(2), 0, 0, 0]])
+    V = np.array([[3.0, 0, 0, 0], [6.0, 0, 0, 0]])
+    o = A.attend_row(q, K, V, [0, 1], 1, True, 0, 1, 0.5)
+    assert abs(o[0] - 5.0) < 1e-12, o
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def check_bruteforce_agrees():
+    # Route A (cache + numpy) vs route B (pure-Python enumeration), tiny inputs.
+    rng_seed = 7
+    for (n_q, n_kv, d, S, W, T) in [(2, 2, 3, 1, 2, 6), (4, 2, 2, 2, 3, 9), (3, 1, 4, 0, 2, 5), (2, 2, 1, 3, 1, 8)]:
+        q = _rand((n_q, d), rng_seed); K = _rand((n_kv, T, d), rng_seed + 1); V = _rand((n_kv, T, d), rng_seed + 2)
+        rng_seed += 3
+        for mask in ([1] * n_kv, [0] * n_kv, [(k + 1) % 2 for k in range(n_kv)]):
+            got = A.decode_step(q, K, V, mask, S, W, 0.7, route="cache")
+            for h in range(n_q):
+                k = h // (n_q // n_kv)
+                ref = A.attend_row_bruteforce(list(q[h]), K[k].tolist(), V[k].tolist(), T - 1,
+                                              bool(mask[k]), S, W, 0.7)
+                assert np.allclose(got[h], ref, atol=1e-12, rtol=0), (h, mask, got[h], ref)
+
+
+def _sdpa(Qh, Kh, Vh, attn_mask=None, is_causal=False, enable_gqa=False):
+    import torch.nn.functional as F
+    return F.scaled_dot_product_attention(torch.from_numpy(Qh), torch.from_numpy(Kh), torch.from_numpy(Vh),
+                                          attn_mask=attn_mask, is_causal=is_causal,
+                                          enable_gqa=enable_gqa).numpy()
+
+
+def check_library_special_cases():
+    N, d = 37, 8
+    for n_q, n_kv in [(4, 4), (6, 2)]:
+        Q = _rand((n_q, N, d), 11); K = _rand((n_kv, N, d), 12); V = _rand((n_kv, N, d), 13)
+        scale = 1.0 / math.sqrt(d)
+        # All heads retrieval == causal attention (torch SDPA, float64 CPU, GQA by the library).
+        got = A.prefill_full(Q, K, V, [1] * n_kv, 4, 5, scale)
+        ref = _sdpa(Q[None], K[None], V[None], is_causal=True, enable_gqa=(n_q != n_kv))[0]
+        assert np.allclose(got, ref, atol=1e-12, rtol=0)
+        # Streaming with S + W >= N is full causal attention too.
+        got = A.prefill_full(Q, K, V, [0] * n_kv, 10, N - 10, scale)
+        assert np.allclose(got, ref, atol=1e-12, rtol=0)
+        # Streaming with S = 0 is a pure sliding window of W keys: band mask from tril differences.
+        W = 6
+        band = torch.ones(N, N, dtype=torch.bool).tril() & ~torch.ones(N, N, dtype=torch.bool).tril(-W)
+        got = A.prefill_full(Q, K, V, [0] * n_kv, 0, W, scale)
+        ref = _sdpa(Q[None], K[None], V[None], attn_mask=band, enable_gqa=(n_q != n_kv))[0]
+        assert np.allclose(got, ref, atol=1e-12, rtol=0)
+        # Decode step (newest query only) agrees with the last row of the same library result.
+        dec = A.decode_step(Q[:, -1], K, V, [0] * n_kv, 0, W, scale)
+        assert np.allclose(dec, ref[:, -1], atol=1e-12, rtol=0)
+
+
+def check_softmax_invariants():
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        T = int(rng.integers(1, 60)); d = 5; S = int(rng.integers(0, 6)); W = int(rng.integers(1, 9))
+        q = rng.standard_normal(d); K = rng.standard_normal((T, d)) * 3; V = rng.standard_normal((T, d))
+        for ret in (True, False):
+            pos, w = A.softmax_weights(q, K, np.arange(T), T - 1, ret, S, W, 0.5)
+            assert abs(w.sum() - 1.0) < 1e-12 and (w >= 0).all()
+            o = A.attend_row(q, K, V, np.arange(T), T - 1, ret, S, W, 0.5)
+            lo = V[pos].min(axis=0); hi = V[pos].max(axis=0)
+            assert (o >= lo - 1e-12).all() and (o <= hi + 1e-12).all()
+            # Shuffling the key order (ring slots are out of order) changes nothing.
+            perm = rng.permutation(T)
+            o2 = A.attend_row(q, K[perm], V[perm], np.arange(T)[perm], T - 1, ret, S, W, 0.5)
+            assert np.allclose(o, o2, atol=1e-12, rtol=0)
+
+
+def check_chunk_invariance():
+    # Chunked prefill through a cache that evicts == one pass over the whole sequence.
+    n_q, n_kv, N, d, S, W = 4, 2, 45, 6, 3, 7
+    Q = _rand((n_q, N, d), 21); K = _rand((n_kv, N, d), 22); V = _rand((n_kv, N, d), 23)
+    for mask in ([1, 0], [0, 0], [1, 1]):
+        ref = A.prefill_full(Q, K, V, mask, S, W, 0.4)
+        for C in (1, 7, 8, 16, N):
+            got = A.prefill_chunked(Q, K, V, mask, S, W, 0.4, C)
+            assert np.allclose(got, ref, atol=1e-12, rtol=0), (mask, C)
+
+
+def check_gqa_expansion():
+    # Result == the same computation on K/V expanded with repeat_interleave (one KV head per query head).
+    n_q, n_kv, T, d, S, W = 8, 2, 30, 4, 2, 5
+    q = _rand((n_q, d), 31); K = _rand((n_kv, T, d), 32); V = _rand((n_kv, T, d), 33)
+    mask = [1, 0]
+    got = A.decode_step(q, K, V, mask, S, W, 0.3)
+    g = n_q // n_kv
+    Ke = torch.from_numpy(K).repeat_interleave(g, dim=0).numpy()
+    Ve = torch.from_numpy(V).repeat_interleave(g, dim=0).numpy()
+    me = torch.tensor(mask).repeat_interleave(g).tolist()
+    ref = A.decode_step(q, Ke, Ve, me, S, W, 0.3)
+    assert np.allclose(got, ref, atol=1e-13, rtol=0)
+    # And against the library's own GQA handling (causal SDPA, all retrieval, newest row).
+    Qf = _rand((n_q, T, d), 34); Qf[:, -1] = q
+    lib = _sdpa(Qf[None], K[None], V[None], is_causal=True, enable_gqa=True)[0][:, -1]
+    got = A.decode_step(q, K, V, [1, 1], S, W, 1 / math.sqrt(d))
+    assert np.allclose(got, lib, atol=1e-12, rtol=0)
+
+
+ALL_CHECKS = [
+    check_printed_kv_sizes, check_effective_context, check_mixed_payload_closed_forms,
+    check_ring_example, check_streaming_composition, check_simulation_counts, check_keep_set_is_visible_set,
+    check_hand_cases, check_bruteforce_agrees, check_library_special_cases,
+    check_softmax_invariants, check_chunk_invariance, check_gqa_expansion,
+]
+
+
+def failing_checks():
+    bad = []
+    for c in ALL_CHECKS:
+        try:
+            c()
+        except AssertionError:
+            bad.append(c.__name__)
+    return bad

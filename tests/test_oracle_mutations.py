@@ -1,0 +1,89 @@
+"""Plant plausible mistakes into the oracle (on the CPU) and check that at
+least one pin catches each of them."""
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from oracle import cache as Cc
+from oracle import sizes as Z
+from tests import oracle_checks as OC
+
+
+def _window_too_wide(t_rows, positions, is_retrieval, S, W):
+    t = np.asarray(t_rows)[:, None]; pos = np.asarray(positions)[None, :]
+    ok = (pos >= 0) & (pos <= t)
+    if not is_retrieval:
+        ok &= (pos < S) | (pos >= t - W)          # W+1 recent tokens
+    return ok
+
+
+def _sinks_off_by_one(t_rows, positions, is_retrieval, S, W):
+    t = np.asarray(t_rows)[:, None]; pos = np.asarray(positions)[None, :]
+    ok = (pos >= 0) & (pos <= t)
+    if not is_retrieval:
+        ok &= (pos <= S) | (pos >= t - W + 1)      # S+1 sinks
+    return ok
+
+
+def _no_causal(t_rows, positions, is_retrieval, S, W):
+    t = np.asarray(t_rows)[:, None]; pos = np.asarray(positions)[None, :] + 0 * t
+    ok = pos >= 0
+    if not is_retrieval:
+        ok &= (pos < S) | (pos >= t - W + 1)
+    return ok
+
+
+def _wrong_scalar_window(t, j, is_retrieval, S, W):
+    if j < 0 or j > t:
+        return False
+    return is_retrieval or j < S or j > t - W + 1  # W-1 recent tokens
+
+
+def _head_mod(h, n_q, n_kv):
+    return h % n_kv                                # transposed GQA mapping
+
+
+def _attend_no_scale(q, keys, values, key_pos, t, is_retrieval, S, W, scale):
+    return _orig_attend_row(q, keys, values, key_pos, t, is_retrieval, S, W, 1.0)
+
+
+def _attend_sign(q, keys, values, key_pos, t, is_retrieval, S, W, scale):
+    return _orig_attend_row(q, keys, values, key_pos, t, is_retrieval, S, W, -scale)
+
+
+_orig_attend_row = A.attend_row
+
+
+def _ring_slot_by_position(self, position, payload=None):
+    if len(self.sinks) < self.S:
+        self.sinks.append((position, payload))
+        return len(self.sinks) - 1
+    slot = position % self.W                       # ring indexed by absolute position
+    self.ring.items[slot] = (position, payload)
+    self.ring.length += 1
+    return self.S + slot
+
+
+def _kv_bytes_one_factor(L, n_kv, d_head, T, elem_bytes=2):
+    return elem_bytes * L * n_kv * d_head * T      # dropped K+V factor
+
+
+MUTATIONS = {
+    "window_too_wide": (A, "visible_matrix", _window_too_wide),
+    "sinks_off_by_one": (A, "visible_matrix", _sinks_off_by_one),
+    "no_causal": (A, "visible_matrix", _no_causal),
+    "scalar_window_narrow": (A, "visible", _wrong_scalar_window),
+    "gqa_mod_mapping": (A, "kv_head_of", _head_mod),
+    "dropped_scale": (A, "attend_row", _attend_no_scale),
+    "flipped_sign": (A, "attend_row", _attend_sign),
+    "ring_by_position": (Cc.StreamingHeadCache, "append", _ring_slot_by_position),
+    "kv_bytes_factor": (Z, "kv_cache_bytes", _kv_bytes_one_factor),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    owner, attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(owner, attr, fn)
+    bad = OC.failing_checks()
+    assert bad, f"planted mistake {name} went unnoticed"
