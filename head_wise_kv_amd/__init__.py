@@ -1,0 +1,230 @@
+"""Python binding of libduo (include/duo.h): argument marshalling only.
+
+Every step of the hot path runs in the HIP kernels of libduo.so; this module
+checks shapes, dtypes and devices of torch tensors, hands their device
+pointers and the current HIP stream to the C ABI, and turns error codes into
+exceptions.  There is no fallback: if libduo.so is missing this import fails.
+
+Build the library first with ``python -m head_wise_kv_amd.build`` (or
+``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libduo.so")
+
+DUO_OK, DUO_EINVAL, DUO_EUNSUPPORTED, DUO_ECAPACITY, DUO_EEMPTY, DUO_EWORKSPACE, DUO_EHIP = 0, -1, -2, -3, -4, -5, -6
+DUO_F32, DUO_BF16 = 0, 1
+ERROR_NAMES = {DUO_EINVAL: "DUO_EINVAL", DUO_EUNSUPPORTED: "DUO_EUNSUPPORTED", DUO_ECAPACITY: "DUO_ECAPACITY",
+               DUO_EEMPTY: "DUO_EEMPTY", DUO_EWORKSPACE: "DUO_EWORKSPACE", DUO_EHIP: "DUO_EHIP"}
+
+# Every entry point declared in include/duo.h.
+EXPORTS = ("duo_cache_bytes", "duo_cache_payload_bytes", "duo_cache_init", "duo_append", "duo_decode",
+           "duo_prefill_chunk", "duo_cache_seq_len", "duo_cache_head_view", "duo_cache_free", "duo_last_error")
+
+
+class DuoError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{ERROR_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class duo_config(ctypes.Structure):
+    _fields_ = [("L", ctypes.c_int32), ("B", ctypes.c_int32), ("n_q", ctypes.c_int32), ("n_kv", ctypes.c_int32),
+                ("d_head", ctypes.c_int32), ("T_cap", ctypes.c_int64), ("sink", ctypes.c_int32),
+                ("recent", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("retrieval_mask", ctypes.POINTER(ctypes.c_uint8))]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"libduo.so is not built ({_LIB_PATH}); run `python -m head_wise_kv_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    cfgp = ctypes.POINTER(duo_config)
+    lib.duo_cache_bytes.argtypes = [cfgp, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.duo_cache_payload_bytes.argtypes = [cfgp, ctypes.POINTER(sz)]
+    lib.duo_cache_init.argtypes = [cfgp, vp, sz, vp, ctypes.POINTER(vp)]
+    lib.duo_append.argtypes = [vp, i32, vp, vp, i64, vp]
+    lib.duo_decode.argtypes = [vp, i32, vp, vp, ctypes.c_float, vp, sz, vp]
+    lib.duo_prefill_chunk.argtypes = [vp, i32, vp, vp, vp, i64, vp, ctypes.c_float, vp, sz, vp]
+    lib.duo_cache_seq_len.argtypes = [vp, i32, ctypes.POINTER(i64)]
+    lib.duo_cache_head_view.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(vp),
+                                        ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(i64),
+                                        ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.duo_cache_free.argtypes = [vp]
+    lib.duo_cache_free.restype = None
+    lib.duo_last_error.argtypes = []
+    lib.duo_last_error.restype = ctypes.c_char_p
+    for name in EXPORTS:
+        if name not in ("duo_cache_free", "duo_last_error"):
+            getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+LIB_PATH = _LIB_PATH
+
+
+def _check(rc: int) -> None:
+    if rc != DUO_OK:
+        raise DuoError(rc, lib.duo_last_error().decode(errors="replace"))
+
+
+def _dtype_code(dtype) -> int:
+    if dtype in ("bf16", torch.bfloat16):
+        return DUO_BF16
+    if dtype in ("f32", "fp32", torch.float32):
+        return DUO_F32
+    raise ValueError(f"unsupported dtype {dtype}")
+
+
+def make_config(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask):
+    """(duo_config, keep-alive mask buffer)."""
+    import numpy as np
+    m = torch.from_numpy(np.asarray(mask, dtype=np.uint8).reshape(-1).copy())
+    if m.numel() != L * n_kv:
+        raise ValueError(f"mask must hold L*n_kv = {L * n_kv} entries, got {m.numel()}")
+    buf = (ctypes.c_uint8 * m.numel())(*m.tolist())
+    cfg = duo_config(L, B, n_q, n_kv, d_head, int(T_cap), sink, recent, _dtype_code(dtype),
+                     ctypes.cast(buf, ctypes.POINTER(ctypes.c_uint8)))
+    return cfg, buf
+
+
+def cache_bytes(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask):
+    """(arena bytes, workspace bytes, K+V payload bytes) -- host-only size query."""
+    cfg, _buf = make_config(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask)
+    a, w, p = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib.duo_cache_bytes(ctypes.byref(cfg), ctypes.byref(a), ctypes.byref(w)))
+    _check(lib.duo_cache_payload_bytes(ctypes.byref(cfg), ctypes.byref(p)))
+    return a.value, w.value, p.value
+
+
+def _stream_handle(stream: Optional[torch.cuda.Stream]):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class DuoCache:
+    """A mixed retrieval/streaming KV cache in one caller-owned device arena.
+
+    Tensors: K/V inputs [B][n_kv][n][d], queries/outputs [B][n_q][d] (decode)
+    or [B][n_q][C][d] (prefill), all contiguous in the cache dtype on the
+    cache's device.
+    """
+
+    def __init__(self, L: int, B: int, n_q: int, n_kv: int, d_head: int, T_cap: int, sink: int, recent: int,
+                 dtype, mask: Sequence, device="cuda", stream: Optional[torch.cuda.Stream] = None):
+        self.L, self.B, self.n_q, self.n_kv, self.d = L, B, n_q, n_kv, d_head
+        self.T_cap, self.S, self.W = int(T_cap), sink, recent
+        self.torch_dtype = torch.bfloat16 if _dtype_code(dtype) == DUO_BF16 else torch.float32
+        self.device = torch.device(device)
+        self._cfg, self._mask_buf = make_config(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask)
+        import numpy as np
+        self.mask = torch.from_numpy(np.asarray(mask, dtype=np.uint8).reshape(L, n_kv).copy())
+        a, w = ctypes.c_size_t(), ctypes.c_size_t()
+        _check(lib.duo_cache_bytes(ctypes.byref(self._cfg), ctypes.byref(a), ctypes.byref(w)))
+        self.arena_bytes, self.workspace_bytes = a.value, w.value
+        self.arena = torch.empty(self.arena_bytes, dtype=torch.uint8, device=self.device)
+        self.workspace = torch.empty(max(self.workspace_bytes, 256), dtype=torch.uint8, device=self.device)
+        self._h = ctypes.c_void_p()
+        _check(lib.duo_cache_init(ctypes.byref(self._cfg), ctypes.c_void_p(self.arena.data_ptr()),
+                                  self.arena_bytes, _stream_handle(stream), ctypes.byref(self._h)))
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            lib.duo_cache_free(h)
+            self._h = None
+
+    # ------------------------------------------------------------ checks
+    def _chk(self, t: torch.Tensor, shape, name: str):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a tensor")
+        if t.device != self.device and not (t.is_cuda and self.device.type == "cuda" and self.device.index is None):
+            raise ValueError(f"{name} must be on {self.device}, got {t.device}")
+        if t.dtype != self.torch_dtype:
+            raise ValueError(f"{name} must be {self.torch_dtype}, got {t.dtype}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+    # ------------------------------------------------------------ entry points
+    def append(self, layer: int, k: torch.Tensor, v: torch.Tensor, stream=None) -> None:
+        n = k.shape[2] if k.dim() == 4 else -1
+        self._chk(k, (self.B, self.n_kv, n, self.d), "k")
+        self._chk(v, (self.B, self.n_kv, n, self.d), "v")
+        _check(lib.duo_append(self._h, layer, ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()), n,
+                              _stream_handle(stream)))
+
+    def decode(self, layer: int, q: torch.Tensor, out: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+               stream=None) -> torch.Tensor:
+        self._chk(q, (self.B, self.n_q, self.d), "q")
+        if out is None:
+            out = torch.empty_like(q)
+        self._chk(out, (self.B, self.n_q, self.d), "out")
+        sc = float(self.d ** -0.5 if scale is None else scale)
+        _check(lib.duo_decode(self._h, layer, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(out.data_ptr()), sc,
+                              ctypes.c_void_p(self.workspace.data_ptr()), self.workspace.numel(),
+                              _stream_handle(stream)))
+        return out
+
+    def prefill_chunk(self, layer: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                      out: Optional[torch.Tensor] = None, scale: Optional[float] = None, stream=None) -> torch.Tensor:
+        C = q.shape[2] if q.dim() == 4 else -1
+        self._chk(q, (self.B, self.n_q, C, self.d), "q")
+        self._chk(k, (self.B, self.n_kv, C, self.d), "k")
+        self._chk(v, (self.B, self.n_kv, C, self.d), "v")
+        if out is None:
+            out = torch.empty_like(q)
+        self._chk(out, (self.B, self.n_q, C, self.d), "out")
+        sc = float(self.d ** -0.5 if scale is None else scale)
+        _check(lib.duo_prefill_chunk(self._h, layer, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                     ctypes.c_void_p(v.data_ptr()), C, ctypes.c_void_p(out.data_ptr()), sc,
+                                     ctypes.c_void_p(self.workspace.data_ptr()), self.workspace.numel(),
+                                     _stream_handle(stream)))
+        return out
+
+    def seq_len(self, layer: int) -> int:
+        x = ctypes.c_int64()
+        _check(lib.duo_cache_seq_len(self._h, layer, ctypes.byref(x)))
+        return x.value
+
+    def head_view(self, layer: int, kv_head: int) -> dict:
+        """Device addresses and strides of one KV head's rows (for layout checks)."""
+        ir = ctypes.c_int()
+        kb, vb, pp = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_void_p()
+        ns, rb, hs, ps = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(lib.duo_cache_head_view(self._h, layer, kv_head, ctypes.byref(ir), ctypes.byref(kb), ctypes.byref(vb),
+                                       ctypes.byref(pp), ctypes.byref(ns), ctypes.byref(rb), ctypes.byref(hs),
+                                       ctypes.byref(ps)))
+        return dict(is_retrieval=bool(ir.value), k_base=kb.value, v_base=vb.value, pos=pp.value,
+                    n_slots=ns.value, row_bytes=rb.value, head_stride_bytes=hs.value, pos_stride=ps.value)
+
+    def read_head(self, layer: int, kv_head: int):
+        """Copy one KV head's slots to the host: (K [B][n_slots][d], V, pos [B][n_slots] or None).
+        The bytes come from the arena tensor by offset (a plain device copy)."""
+        hv = self.head_view(layer, kv_head)
+        base = self.arena.data_ptr()
+        es = 2 if self.torch_dtype == torch.bfloat16 else 4
+        rows = hv["n_slots"]
+        out = []
+        for key in ("k_base", "v_base"):
+            off = hv[key] - base
+            seg = torch.stack([self.arena[off + b * hv["head_stride_bytes"]: off + b * hv["head_stride_bytes"]
+                                          + rows * hv["row_bytes"]] for b in range(self.B)])
+            out.append(seg.cpu().view(self.torch_dtype).reshape(self.B, rows, self.d))
+        pos = None
+        if hv["pos"]:
+            off = hv["pos"] - base
+            seg = torch.stack([self.arena[off + b * hv["pos_stride"] * 4: off + (b * hv["pos_stride"] + rows) * 4]
+                               for b in range(self.B)])
+            pos = seg.cpu().view(torch.int32).reshape(self.B, rows)
+        assert es in (2, 4)
+        return out[0], out[1], pos

@@ -1,0 +1,385 @@
+// libduo host side: the C ABI of include/duo.h.  Validates arguments, plans
+// the arena layout and the decode work split, keeps the per-layer token
+// counts, and enqueues the HIP kernels of duo_kernels.hip.  It never allocates
+// device memory: the arena and workspace belong to the caller.
+#include "duo.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "duo_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return DUO_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(DUO_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct LayerPlan {
+  int n_ret = 0, n_str = 0;
+  size_t off_kr = 0, off_vr = 0, off_ks = 0, off_vs = 0, off_pos = 0, off_cnt1 = 0, off_cnt2 = 0;
+  duo::HeadMap map{};
+};
+
+struct Plan {
+  std::vector<LayerPlan> layers;
+  size_t arena = 0, workspace = 0, payload = 0;
+};
+
+bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+int validate(const duo_config* c) {
+  if (!c) return fail(DUO_EINVAL, "config is NULL");
+  if (c->L < 1 || c->B < 1 || c->n_q < 1 || c->n_kv < 1)
+    return fail(DUO_EINVAL, "L, B, n_q, n_kv must be >= 1 (got %d, %d, %d, %d)", c->L, c->B, c->n_q, c->n_kv);
+  if (c->n_q % c->n_kv != 0) return fail(DUO_EINVAL, "n_q (%d) must be a multiple of n_kv (%d)", c->n_q, c->n_kv);
+  if (c->n_kv > duo::kMaxKV) return fail(DUO_EUNSUPPORTED, "n_kv %d > %d", c->n_kv, duo::kMaxKV);
+  if (!supported_group(c->n_q / c->n_kv))
+    return fail(DUO_EUNSUPPORTED, "group size g = %d not built (1, 2, 4, 8)", c->n_q / c->n_kv);
+  if (c->d_head != 64 && c->d_head != 128) return fail(DUO_EUNSUPPORTED, "d_head %d not built (64, 128)", c->d_head);
+  if (c->dtype != DUO_F32 && c->dtype != DUO_BF16) return fail(DUO_EUNSUPPORTED, "dtype %d", c->dtype);
+  if (c->T_cap < 1) return fail(DUO_EINVAL, "T_cap must be >= 1");
+  if (c->T_cap > INT32_MAX) return fail(DUO_EINVAL, "T_cap must fit int32 (positions are int32)");
+  if (c->sink < 0 || c->recent < 1) return fail(DUO_EINVAL, "need sink >= 0 and recent >= 1");
+  if (!c->retrieval_mask) return fail(DUO_EINVAL, "retrieval_mask is NULL");
+  for (int i = 0; i < c->L * c->n_kv; ++i)
+    if (c->retrieval_mask[i] > 1) return fail(DUO_EINVAL, "retrieval_mask[%d] = %d, must be 0 or 1", i, c->retrieval_mask[i]);
+  return DUO_OK;
+}
+
+int elem_bytes(const duo_config* c) { return c->dtype == DUO_BF16 ? 2 : 4; }
+
+size_t decode_rec_floats(const duo_config* c) {
+  const int g = c->n_q / c->n_kv;
+  return (size_t)g * (c->d_head + 2);
+}
+
+void make_plan(const duo_config* c, Plan* p) {
+  const size_t row = (size_t)c->d_head * elem_bytes(c);
+  const int64_t cap_str = (int64_t)c->sink + c->recent;
+  p->layers.assign(c->L, LayerPlan{});
+  size_t off = 0;
+  p->payload = 0;
+  for (int l = 0; l < c->L; ++l) {
+    LayerPlan& lp = p->layers[l];
+    std::memset(&lp.map, 0, sizeof lp.map);
+    for (int h = 0; h < c->n_kv; ++h) {
+      const bool ret = c->retrieval_mask[(size_t)l * c->n_kv + h] != 0;
+      lp.map.kind[h] = ret ? 1 : 0;
+      if (ret) {
+        lp.map.cidx[h] = (int8_t)lp.n_ret;
+        lp.map.orig_ret[lp.n_ret++] = (int8_t)h;
+      } else {
+        lp.map.cidx[h] = (int8_t)lp.n_str;
+        lp.map.orig_str[lp.n_str++] = (int8_t)h;
+      }
+    }
+    const size_t ret_bytes = (size_t)c->B * lp.n_ret * c->T_cap * row;
+    const size_t str_bytes = (size_t)c->B * lp.n_str * cap_str * row;
+    lp.off_kr = off; off = align_up(off + ret_bytes);
+    lp.off_vr = off; off = align_up(off + ret_bytes);
+    lp.off_ks = off; off = align_up(off + str_bytes);
+    lp.off_vs = off; off = align_up(off + str_bytes);
+    lp.off_pos = off; off = align_up(off + (size_t)c->B * lp.n_str * cap_str * sizeof(int32_t));
+    lp.off_cnt1 = off; off = align_up(off + (size_t)c->B * c->n_kv * duo::kMaxGroups * sizeof(int32_t));
+    lp.off_cnt2 = off; off = align_up(off + (size_t)c->B * c->n_kv * sizeof(int32_t));
+    p->payload += 2 * (ret_bytes + str_bytes);
+  }
+  p->arena = off;
+  const size_t rec = decode_rec_floats(c) * sizeof(float);
+  const size_t ws1 = align_up(((size_t)duo::kTargetBlocks + (size_t)c->B * c->n_kv) * rec);
+  const size_t ws2 = align_up((size_t)c->B * c->n_kv * duo::kMaxGroups * rec);
+  p->workspace = ws1 + ws2;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+struct duo_cache {
+  duo_config cfg{};
+  std::vector<uint8_t> mask;
+  Plan plan;
+  char* arena = nullptr;
+  size_t arena_bytes = 0;
+  std::vector<int64_t> seq_len;
+
+  duo::LayerPtrs ptrs(int l) const {
+    const LayerPlan& lp = plan.layers[l];
+    duo::LayerPtrs p;
+    p.k_ret = arena + lp.off_kr;
+    p.v_ret = arena + lp.off_vr;
+    p.k_str = arena + lp.off_ks;
+    p.v_str = arena + lp.off_vs;
+    p.pos = reinterpret_cast<int32_t*>(arena + lp.off_pos);
+    p.cnt1 = reinterpret_cast<int32_t*>(arena + lp.off_cnt1);
+    p.cnt2 = reinterpret_cast<int32_t*>(arena + lp.off_cnt2);
+    return p;
+  }
+  int64_t cap_str() const { return (int64_t)cfg.sink + cfg.recent; }
+  int row_bytes() const { return cfg.d_head * elem_bytes(&cfg); }
+};
+
+namespace {
+
+int check_layer(const duo_cache* c, int layer) {
+  if (!c) return fail(DUO_EINVAL, "cache handle is NULL");
+  if (layer < 0 || layer >= c->cfg.L) return fail(DUO_EINVAL, "layer %d out of range [0, %d)", layer, c->cfg.L);
+  return DUO_OK;
+}
+
+// Enqueue the append of n_new tokens at positions p0.. (no validation).
+hipError_t enqueue_append(duo_cache* c, int layer, const void* k, const void* v, int64_t p0, int64_t n_new,
+                          hipStream_t s) {
+  const LayerPlan& lp = c->plan.layers[layer];
+  duo::AppendArgs a{};
+  a.k = static_cast<const char*>(k);
+  a.v = static_cast<const char*>(v);
+  a.lp = c->ptrs(layer);
+  a.map = lp.map;
+  a.B = c->cfg.B;
+  a.n_kv = c->cfg.n_kv;
+  a.n_ret = lp.n_ret;
+  a.n_str = lp.n_str;
+  a.row_bytes = c->row_bytes();
+  a.cap_ret = c->cfg.T_cap;
+  a.cap_str = c->cap_str();
+  a.p0 = p0;
+  a.n_new = n_new;
+  a.S = c->cfg.sink;
+  a.W = c->cfg.recent;
+  a.keep_from = std::max<int64_t>(a.S, p0 + n_new - a.W);
+  return duo::launch_append(a, c->cfg.dtype, c->cfg.d_head, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int duo_cache_bytes(const duo_config* cfg, size_t* arena_bytes, size_t* workspace_bytes) {
+  if (int e = validate(cfg)) return e;
+  Plan p;
+  make_plan(cfg, &p);
+  if (arena_bytes) *arena_bytes = p.arena;
+  if (workspace_bytes) *workspace_bytes = p.workspace;
+  return ok();
+}
+
+int duo_cache_payload_bytes(const duo_config* cfg, size_t* payload_bytes) {
+  if (int e = validate(cfg)) return e;
+  if (!payload_bytes) return fail(DUO_EINVAL, "payload_bytes is NULL");
+  Plan p;
+  make_plan(cfg, &p);
+  *payload_bytes = p.payload;
+  return ok();
+}
+
+int duo_cache_init(const duo_config* cfg, void* arena, size_t arena_bytes, void* stream, duo_cache** out) {
+  if (int e = validate(cfg)) return e;
+  if (!out) return fail(DUO_EINVAL, "out is NULL");
+  if (!arena) return fail(DUO_EINVAL, "arena is NULL");
+  if ((reinterpret_cast<uintptr_t>(arena) % kAlign) != 0) return fail(DUO_EINVAL, "arena must be 256-byte aligned");
+  Plan p;
+  make_plan(cfg, &p);
+  if (arena_bytes < p.arena)
+    return fail(DUO_EINVAL, "arena holds %zu bytes, %zu needed", arena_bytes, p.arena);
+  duo_cache* c = new (std::nothrow) duo_cache;
+  if (!c) return fail(DUO_EINVAL, "out of host memory");
+  c->cfg = *cfg;
+  c->mask.assign(cfg->retrieval_mask, cfg->retrieval_mask + (size_t)cfg->L * cfg->n_kv);
+  c->cfg.retrieval_mask = c->mask.data();
+  c->plan = p;
+  c->arena = static_cast<char*>(arena);
+  c->arena_bytes = arena_bytes;
+  c->seq_len.assign(cfg->L, 0);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int l = 0; l < cfg->L; ++l) {
+    const LayerPlan& lp = p.layers[l];
+    // positions and merge tickets start at zero (payload rows need no clearing)
+    hipError_t e = duo::launch_fill_zero(c->arena + lp.off_pos, p.layers[l].off_cnt2 + align_up((size_t)cfg->B * cfg->n_kv * 4) - lp.off_pos, s);
+    if (e != hipSuccess) {
+      delete c;
+      return hip_fail(e, "zeroing positions/counters");
+    }
+  }
+  *out = c;
+  return ok();
+}
+
+int duo_append(duo_cache* c, int layer, const void* k, const void* v, int64_t n_new, void* stream) {
+  if (int e = check_layer(c, layer)) return e;
+  if (!k || !v) return fail(DUO_EINVAL, "k or v is NULL");
+  if (!aligned16(k) || !aligned16(v)) return fail(DUO_EINVAL, "k and v must be 16-byte aligned");
+  if (n_new < 1) return fail(DUO_EINVAL, "n_new must be >= 1 (got %lld)", (long long)n_new);
+  const int64_t p0 = c->seq_len[layer];
+  if (p0 + n_new > c->cfg.T_cap)
+    return fail(DUO_ECAPACITY, "layer %d holds %lld tokens; %lld more exceed T_cap %lld", layer, (long long)p0,
+                (long long)n_new, (long long)c->cfg.T_cap);
+  hipError_t e = enqueue_append(c, layer, k, v, p0, n_new, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  c->seq_len[layer] = p0 + n_new;
+  return ok();
+}
+
+int duo_decode(duo_cache* c, int layer, const void* q, void* out, float scale, void* ws, size_t ws_bytes,
+               void* stream) {
+  if (int e = check_layer(c, layer)) return e;
+  if (!q || !out) return fail(DUO_EINVAL, "q or out is NULL");
+  if (!aligned16(q) || !aligned16(out)) return fail(DUO_EINVAL, "q and out must be 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(DUO_EINVAL, "scale must be finite");
+  const int64_t T = c->seq_len[layer];
+  if (T < 1) return fail(DUO_EEMPTY, "layer %d holds no token", layer);
+  if (!ws || ws_bytes < c->plan.workspace)
+    return fail(DUO_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", c->plan.workspace, ws_bytes);
+  if (!aligned16(ws)) return fail(DUO_EINVAL, "workspace must be 16-byte aligned");
+  const LayerPlan& lp = c->plan.layers[layer];
+  const duo_config& cf = c->cfg;
+  duo::DecodeArgs a{};
+  a.q = q;
+  a.out = out;
+  a.lp = c->ptrs(layer);
+  a.map = lp.map;
+  a.B = cf.B;
+  a.n_q = cf.n_q;
+  a.n_kv = cf.n_kv;
+  a.n_ret = lp.n_ret;
+  a.n_str = lp.n_str;
+  a.cap_ret = cf.T_cap;
+  a.cap_str = c->cap_str();
+  a.rows_ret = T;
+  a.rows_str = std::min<int64_t>(T, c->cap_str());
+  // Uniform work items of `chunk` rows (a multiple of 4 wavefronts x 64 rows)
+  // over both head kinds, aiming at kTargetBlocks items per call.
+  const int64_t total = (int64_t)cf.B * (lp.n_ret * a.rows_ret + lp.n_str * a.rows_str);
+  const int64_t tile = (int64_t)duo::kDecodeThreads / 64 * duo::kDecodeRowsPerTile;
+  int64_t chunk = std::max<int64_t>(tile, ceil_div(total, duo::kTargetBlocks));
+  chunk = std::max<int64_t>(chunk, ceil_div(std::max(a.rows_ret, a.rows_str), (int64_t)duo::kSplitGroup * duo::kMaxGroups));
+  chunk = ceil_div(chunk, tile) * tile;
+  a.chunk = chunk;
+  a.split_ret = lp.n_ret ? (int)ceil_div(a.rows_ret, chunk) : 0;
+  a.split_str = lp.n_str ? (int)ceil_div(a.rows_str, chunk) : 0;
+  a.blocks_ret = cf.B * lp.n_ret * a.split_ret;
+  const int blocks = a.blocks_ret + cf.B * lp.n_str * a.split_str;
+  const size_t rec = decode_rec_floats(&cf);
+  a.ws1 = static_cast<float*>(ws);
+  a.ws2 = a.ws1 + align_up(((size_t)duo::kTargetBlocks + (size_t)cf.B * cf.n_kv) * rec * sizeof(float)) / sizeof(float);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = duo::launch_decode(a, cf.dtype, cf.d_head, cf.n_q / cf.n_kv, blocks, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+int duo_prefill_chunk(duo_cache* c, int layer, const void* q, const void* k, const void* v, int64_t C, void* out,
+                      float scale, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (int e = check_layer(c, layer)) return e;
+  if (!q || !k || !v || !out) return fail(DUO_EINVAL, "q, k, v or out is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(DUO_EINVAL, "q, k, v and out must be 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(DUO_EINVAL, "scale must be finite");
+  if (C < 1) return fail(DUO_EINVAL, "chunk length must be >= 1 (got %lld)", (long long)C);
+  const int64_t P = c->seq_len[layer];
+  if (P + C > c->cfg.T_cap)
+    return fail(DUO_ECAPACITY, "layer %d holds %lld tokens; a chunk of %lld exceeds T_cap %lld", layer,
+                (long long)P, (long long)C, (long long)c->cfg.T_cap);
+  const LayerPlan& lp = c->plan.layers[layer];
+  const duo_config& cf = c->cfg;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  duo::PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lp = c->ptrs(layer);
+  a.map = lp.map;
+  a.B = cf.B;
+  a.n_q = cf.n_q;
+  a.n_kv = cf.n_kv;
+  a.n_ret = lp.n_ret;
+  a.n_str = lp.n_str;
+  a.cap_ret = cf.T_cap;
+  a.cap_str = c->cap_str();
+  a.P = P;
+  a.C = C;
+  a.held_str = std::min<int64_t>(P, c->cap_str());
+  a.S = cf.sink;
+  a.W = cf.recent;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const int rows = duo::prefill_rows_per_tile(cf.dtype, cf.d_head);
+  a.q_tiles = (int)ceil_div(C, rows);
+  const int g = cf.n_q / cf.n_kv;
+  a.items_ret = cf.B * lp.n_ret * g * a.q_tiles;
+  hipError_t e = duo::launch_prefill(a, cf.dtype, cf.d_head, g, s);
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  // Commit the chunk after attention has read the cache (same stream).
+  e = enqueue_append(c, layer, k, v, P, C, s);
+  if (e != hipSuccess) return hip_fail(e, "prefill commit launch");
+  c->seq_len[layer] = P + C;
+  return ok();
+}
+
+int duo_cache_seq_len(const duo_cache* c, int layer, int64_t* out) {
+  if (int e = check_layer(c, layer)) return e;
+  if (!out) return fail(DUO_EINVAL, "out is NULL");
+  *out = c->seq_len[layer];
+  return ok();
+}
+
+int duo_cache_head_view(const duo_cache* c, int layer, int kv_head, int* is_retrieval, void** k_base, void** v_base,
+                        int32_t** pos, int64_t* n_slots, int64_t* row_bytes, int64_t* head_stride_bytes,
+                        int64_t* pos_stride) {
+  if (int e = check_layer(c, layer)) return e;
+  if (kv_head < 0 || kv_head >= c->cfg.n_kv) return fail(DUO_EINVAL, "kv_head %d out of range", kv_head);
+  const LayerPlan& lp = c->plan.layers[layer];
+  const duo::LayerPtrs p = c->ptrs(layer);
+  const bool ret = lp.map.kind[kv_head] != 0;
+  const int ci = lp.map.cidx[kv_head];
+  const int64_t rb = c->row_bytes();
+  const int64_t slots = ret ? c->cfg.T_cap : c->cap_str();
+  const int n_kind = ret ? lp.n_ret : lp.n_str;
+  if (is_retrieval) *is_retrieval = ret ? 1 : 0;
+  if (n_slots) *n_slots = slots;
+  if (row_bytes) *row_bytes = rb;
+  if (head_stride_bytes) *head_stride_bytes = (int64_t)n_kind * slots * rb;
+  if (pos_stride) *pos_stride = ret ? 0 : (int64_t)n_kind * slots;
+  if (k_base) *k_base = (ret ? p.k_ret : p.k_str) + (size_t)ci * slots * rb;
+  if (v_base) *v_base = (ret ? p.v_ret : p.v_str) + (size_t)ci * slots * rb;
+  if (pos) *pos = ret ? nullptr : p.pos + (size_t)ci * slots;
+  return ok();
+}
+
+void duo_cache_free(duo_cache* c) { delete c; }
+
+const char* duo_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

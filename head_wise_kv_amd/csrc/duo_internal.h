@@ -1,0 +1,92 @@
+// Internal declarations shared by the host library (duo_host.cpp) and the HIP
+// kernels (duo_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace duo {
+
+constexpr int kMaxKV = 128;        // KV heads per layer the head maps can hold
+constexpr int kSplitGroup = 16;    // decode partials merged by one first-level merge
+constexpr int kMaxGroups = 64;     // first-level groups per head (so <= 1024 splits)
+constexpr int kTargetBlocks = 1024;  // decode work items aimed for per call
+constexpr int kDecodeThreads = 256;  // 4 wavefronts of 64
+constexpr int kDecodeRowsPerTile = 64;
+
+// Per-layer head tables: role and compact index of each KV head, and the KV
+// head behind each compact retrieval / streaming index.
+struct HeadMap {
+  int8_t kind[kMaxKV];      // kv head -> 1 retrieval, 0 streaming
+  int8_t cidx[kMaxKV];      // kv head -> index among heads of its kind
+  int8_t orig_ret[kMaxKV];  // compact retrieval index -> kv head
+  int8_t orig_str[kMaxKV];  // compact streaming index -> kv head
+};
+
+// Device addresses of one layer inside the arena.
+struct LayerPtrs {
+  char* k_ret;     // [B][n_ret][cap_ret][d]
+  char* v_ret;
+  char* k_str;     // [B][n_str][cap_str][d]
+  char* v_str;
+  int32_t* pos;    // [B][n_str][cap_str]
+  int32_t* cnt1;   // [B*n_kv][kMaxGroups] first-level merge tickets
+  int32_t* cnt2;   // [B*n_kv] second-level merge tickets
+};
+
+struct AppendArgs {
+  const char* k;   // [B][n_kv][n_new][d]
+  const char* v;
+  LayerPtrs lp;
+  HeadMap map;
+  int B, n_kv, n_ret, n_str, row_bytes;
+  int64_t cap_ret, cap_str;
+  int64_t p0, n_new;      // first position, tokens
+  int64_t keep_from;      // streaming ring writes only for p >= keep_from
+  int S, W;
+};
+
+struct DecodeArgs {
+  const void* q;   // [B][n_q][d]
+  void* out;       // [B][n_q][d]
+  LayerPtrs lp;
+  HeadMap map;
+  float* ws1;      // [blocks][rec] per-block partials
+  float* ws2;      // [B*n_kv][kMaxGroups][rec] group partials
+  int B, n_q, n_kv, n_ret, n_str;
+  int64_t cap_ret, cap_str;     // rows reserved per head
+  int64_t rows_ret, rows_str;   // rows held per head
+  int64_t chunk;                // rows per work item
+  int split_ret, split_str;     // work items per head
+  int blocks_ret;               // B * n_ret * split_ret
+  float scale_log2;             // softmax scale * log2(e)
+};
+
+struct PrefillArgs {
+  const void* q;     // [B][n_q][C][d]
+  const void* k;     // [B][n_kv][C][d]
+  const void* v;
+  void* out;         // [B][n_q][C][d]
+  LayerPtrs lp;
+  HeadMap map;
+  int B, n_q, n_kv, n_ret, n_str;
+  int64_t cap_ret, cap_str;
+  int64_t P;          // tokens cached before the chunk
+  int64_t C;          // chunk length
+  int64_t held_str;   // streaming slots holding a token before the chunk: min(P, S+W)
+  int S, W;
+  float scale_log2;
+  int q_tiles;        // ceil(C / rows per query tile)
+  int items_ret;      // B * n_ret * g * q_tiles (retrieval work items come first)
+};
+
+// Launchers (duo_kernels.hip).  dtype: 0 = fp32, 1 = bf16.
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, int dtype, int d, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int g, int blocks, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int g, hipStream_t s);
+int prefill_rows_per_tile(int dtype, int d);
+
+}  // namespace duo

@@ -1,0 +1,147 @@
+/*
+ * duo.h -- C ABI of libduo: attention over a per-KV-head mixed KV cache on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (DuoAttention): each KV head of each layer is either a retrieval
+ * head, which keeps every token and attends over the whole context, or a
+ * streaming head, which keeps only S attention-sink tokens plus the W most
+ * recent tokens and attends over those ("DuoAttention: Dual Retrieval &
+ * Streaming Heads Guide", section "2. DuoAttention Cache Partitioning
+ * Mechanics"; the static binary mask M of section "3. Automated Head
+ * Identification via Lightweight Optimization").  The mask lives at KV-head
+ * granularity so that grouped query heads share their KV head's role (same
+ * guide, "Practical Deployment Checklist for Enterprise AI Serving").
+ *
+ * Notation: L layers, B batch rows, n_q query heads, n_kv KV heads,
+ * g = n_q / n_kv, d = d_head, S = sink, W = recent, T_cap = most tokens a
+ * retrieval head can hold.  Query head h reads KV head h / g (the
+ * repeat_interleave mapping of "Attention Variants and Memory Efficiency",
+ * "Multi-Query and Grouped-Query Attention").  Positions are 0-based.
+ *
+ * Conventions for every entry point:
+ *   - Ownership: the caller owns every device buffer (arena, inputs, outputs,
+ *     workspace).  The library never allocates or frees device memory; the
+ *     only thing it allocates is the small host-side handle.
+ *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     default stream) with no implicit synchronisation.  Calls on one cache
+ *     must be issued in order on one stream.  The host-side token count of a
+ *     layer advances when a call is enqueued.
+ *   - Errors: 0 (DUO_OK) or a negative DUO_E* code.  Every argument is
+ *     validated before anything is enqueued, so a failing call changes no
+ *     state.  duo_last_error() returns a message for the calling thread.
+ *   - Layout: all tensors are dense row-major in the cache dtype; d is the
+ *     fastest axis.
+ */
+#ifndef DUO_H_
+#define DUO_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DUO_OK 0
+#define DUO_EINVAL (-1)        /* bad argument, shape, pointer or layer index     */
+#define DUO_EUNSUPPORTED (-2)  /* d_head, dtype or group size not built           */
+#define DUO_ECAPACITY (-3)     /* seq_len + n_new would exceed T_cap              */
+#define DUO_EEMPTY (-4)        /* decode on a layer that holds no token           */
+#define DUO_EWORKSPACE (-5)    /* workspace missing or smaller than required      */
+#define DUO_EHIP (-6)          /* a HIP call or kernel launch failed              */
+
+typedef enum { DUO_F32 = 0, DUO_BF16 = 1 } duo_dtype;
+
+/* Cache configuration.  d_head in {64, 128}; g = n_q / n_kv in {1, 2, 4, 8};
+ * n_kv <= 128; S >= 0; W >= 1; T_cap >= 1.  retrieval_mask is a host array
+ * uint8 [L][n_kv] (1 = retrieval head, 0 = streaming head); it is copied. */
+typedef struct {
+  int32_t L, B, n_q, n_kv, d_head;
+  int64_t T_cap;
+  int32_t sink, recent;
+  int32_t dtype; /* duo_dtype: Q, K, V and outputs; accumulation is fp32 */
+  const uint8_t* retrieval_mask;
+} duo_config;
+
+typedef struct duo_cache duo_cache; /* opaque host handle */
+
+/* Sizes (host only, no device work).  *arena_bytes: the device arena for
+ * duo_cache_init.  It holds, per layer, K and V as [B][n_ret][T_cap][d] for
+ * the retrieval heads and [B][n_str][S+W][d] for the streaming heads (the two
+ * buffer kinds of the guide's section 2), an int32 position per streaming
+ * slot, and a few counters.  *workspace_bytes: the device scratch that
+ * duo_decode and duo_prefill_chunk need (partial softmax results).  Either
+ * output pointer may be NULL.  Returns DUO_OK or DUO_EINVAL/DUO_EUNSUPPORTED. */
+int duo_cache_bytes(const duo_config* cfg, size_t* arena_bytes, size_t* workspace_bytes);
+
+/* K+V payload bytes of the arena (the KV-cache size the guide's section 2
+ * formula counts: retrieval heads T_cap rows, streaming heads S+W rows). */
+int duo_cache_payload_bytes(const duo_config* cfg, size_t* payload_bytes);
+
+/* Bind a cache to a caller-owned device arena of at least duo_cache_bytes()
+ * bytes, 256-byte aligned.  Enqueues the zeroing of positions and counters on
+ * `stream`; every layer starts empty.  On success *out receives a handle that
+ * must be released with duo_cache_free (the arena must outlive it). */
+int duo_cache_init(const duo_config* cfg, void* arena, size_t arena_bytes, void* stream,
+                   duo_cache** out);
+
+/* Append n_new >= 1 tokens to `layer` at positions seq_len .. seq_len+n_new-1.
+ * k, v: device [B][n_kv][n_new][d].  A retrieval head stores position p in
+ * row p.  A streaming head stores p in slot p while p < S, and otherwise in
+ * ring slot S + ((p - S) mod W) (sinks fill first, then the window of the
+ * guide's section 2; the ring slot rule of "Attention Variants and Memory
+ * Efficiency", "Sliding-Window and Mixed Attention"); tokens of the batch that
+ * would be evicted before the call ends are not written.  Each written
+ * streaming slot records p in its position array.  DUO_ECAPACITY if
+ * seq_len + n_new > T_cap. */
+int duo_append(duo_cache* c, int layer, const void* k, const void* v, int64_t n_new, void* stream);
+
+/* One decode step on `layer`: the query of every head is the token at
+ * position seq_len-1, which the caller has appended.  q, out: device
+ * [B][n_q][d].  Retrieval heads attend over positions 0..seq_len-1; streaming
+ * heads over their min(seq_len, S+W) held tokens (exactly the sinks and the W
+ * most recent positions the query may see).  out = softmax(scale * q K^T) V
+ * over those keys, accumulated in fp32 and rounded to the cache dtype.
+ * ws: device workspace of ws_bytes >= duo_cache_bytes' workspace_bytes.
+ * DUO_EEMPTY if the layer holds no token. */
+int duo_decode(duo_cache* c, int layer, const void* q, void* out, float scale, void* ws,
+               size_t ws_bytes, void* stream);
+
+/* Chunked prefill of C >= 1 tokens on `layer`, at positions P .. P+C-1 with
+ * P = seq_len ("Attention Variants and KV-Cache Compression", "When Is Reuse
+ * Exact?": chunk row i attends through absolute key position P + i, and
+ * evicted tokens keep their original positions).  q, out: device
+ * [B][n_q][C][d]; k, v: device [B][n_kv][C][d].  Retrieval heads: causal
+ * attention over positions 0 .. P+i.  Streaming heads: the sink+window mask,
+ * key j visible to row i iff j <= P+i and (j < S or j >= P+i-W+1), with keys
+ * taken from the held sink and ring slots and from the chunk.  The chunk is
+ * attended first and then appended as by duo_append.  DUO_ECAPACITY if
+ * P + C > T_cap. */
+int duo_prefill_chunk(duo_cache* c, int layer, const void* q, const void* k, const void* v,
+                      int64_t C, void* out, float scale, void* ws, size_t ws_bytes, void* stream);
+
+/* Host-side token count of a layer (advanced at enqueue time). */
+int duo_cache_seq_len(const duo_cache* c, int layer, int64_t* out);
+
+/* Where one KV head's rows live, for bit-exact inspection of the layout.
+ * *k_base / *v_base: device address of the head's first row (batch row b at
+ * + b * head_stride_bytes); *pos: device int32 [n_slots] slot positions of a
+ * streaming head (NULL for a retrieval head, whose row index is the
+ * position); *n_slots: T_cap or S+W; *row_bytes: d * element size;
+ * *head_stride_bytes: distance between consecutive batch rows of this head;
+ * *pos_stride: int32 elements between consecutive batch rows of *pos. */
+int duo_cache_head_view(const duo_cache* c, int layer, int kv_head, int* is_retrieval,
+                        void** k_base, void** v_base, int32_t** pos, int64_t* n_slots,
+                        int64_t* row_bytes, int64_t* head_stride_bytes, int64_t* pos_stride);
+
+/* Release the host handle (device memory is the caller's). NULL is ignored. */
+void duo_cache_free(duo_cache* c);
+
+/* Message for the most recent failing call on this thread ("" if none). */
+const char* duo_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DUO_H_ */

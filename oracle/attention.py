@@ -133,11 +133,14 @@ def decode_step(q: np.ndarray, K: np.ndarray, V: np.ndarray, mask: Sequence[int]
     n_kv, T, _ = K.shape
     out = np.zeros((n_q, d), dtype=np.float64)
     t = T - 1
+    held = {}  # the keep set depends only on the head kind; simulate each kind once
     for h in range(n_q):
         k = kv_head_of(h, n_q, n_kv)
         ret = bool(mask[k])
         if route == "cache":
-            pos = np.asarray(_cache.kept_positions(T, ret, S, W), dtype=np.int64)
+            if ret not in held:
+                held[ret] = np.asarray(_cache.kept_positions(T, ret, S, W), dtype=np.int64)
+            pos = held[ret]
         else:
             pos = np.arange(T, dtype=np.int64)
         out[h] = attend_row(q[h], K[k][pos], V[k][pos], pos, t, ret, S, W, scale)

@@ -1,0 +1,54 @@
+"""Helpers for the GPU parity tests: seeded inputs, the library call, the
+oracle, and the tolerance check."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as WL
+from oracle import attention as OA
+from oracle import cache as OC
+
+# Tolerances.  bf16 inputs with fp32 accumulation: max |err| <= 2e-2 and
+# relative RMS <= 1e-2.  fp32 inputs: the kernel rounds nothing but the
+# order of fp32 sums, so 1e-3 / 1e-4.
+TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-3, 1e-4)}
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import head_wise_kv_amd  # noqa: F401  (fails loudly if libduo.so is missing)
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x_f32: np.ndarray, dtype: str) -> torch.Tensor:
+    return WL.to_torch(x_f32, dtype).cuda()
+
+
+def stored(x_f32: np.ndarray, dtype: str) -> np.ndarray:
+    """The float64 values the library actually sees after rounding."""
+    return WL.round_to_dtype(x_f32, dtype)
+
+
+def check_close(got: torch.Tensor, ref: np.ndarray, dtype: str, what: str = ""):
+    g = got.detach().float().cpu().double().numpy()
+    atol, rrms = TOL[dtype]
+    err = np.abs(g - ref)
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    max_err = float(err.max()) if err.size else 0.0
+    rel = float(np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30)) if err.size else 0.0
+    assert max_err <= atol and rel <= rrms, f"{what}: max|err| {max_err:.3e} (tol {atol}), rel-RMS {rel:.3e} (tol {rrms})"
+    return max_err, rel
+
+
+def oracle_decode(q64, K64, V64, mask, S, W, scale):
+    """q64 [B][n_q][d], K64/V64 [B][n_kv][T][d] -> [B][n_q][d] via the oracle's cache route."""
+    return np.stack([OA.decode_step(q64[b], K64[b], V64[b], mask, S, W, scale) for b in range(q64.shape[0])])

@@ -1,0 +1,96 @@
+"""libduo on the CPU: it loads, exports every entry point of include/duo.h,
+and its host-only logic (validation, layout sizes) is right.  No GPU work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import head_wise_kv_amd as H
+import workloads as WL
+from oracle import sizes as Z
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    txt = open(os.path.join(ROOT, "include", "duo.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(duo_[a-z_]+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 10, names
+    assert set(names) == set(H.EXPORTS)
+    lib = ctypes.CDLL(H.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("name", WL.ORDER)
+def test_payload_matches_closed_form(name):
+    w = WL.WORKLOADS[name]
+    mask = WL.mask_table(w)
+    T_cap = w.T
+    _, ws, payload = H.cache_bytes(w.L, w.B, w.n_q, w.n_kv, w.d, T_cap, w.S, w.W, w.dtype, mask)
+    assert payload == Z.mixed_payload_bytes(mask.tolist(), w.B, T_cap, w.S, w.W, w.d, w.elem_bytes)
+    assert ws > 0
+
+
+def test_payload_reproduces_printed_examples():
+    # 70B GQA, all heads retrieval: the printed 41,943,040,000 bytes.
+    _, _, p = H.cache_bytes(80, 1, 64, 8, 128, 128000, 64, 1024, "bf16", [[1] * 8] * 80)
+    assert p == 41943040000
+    # 2 of 8 heads retrieval per layer: the Memory_Duo formula with R = 0.25.
+    _, _, p = H.cache_bytes(80, 1, 64, 8, 128, 128000, 64, 1024, "bf16", [[1, 1, 0, 0, 0, 0, 0, 0]] * 80)
+    assert p == Z.duo_cache_bytes(0.25, 128000, 64, 1024, 80, 8, 128, 2) == 10753146880
+    # L=32, 4096 tokens, 8 KV heads of 128, 2-byte: 512 MiB; MHA (32 KV heads) 2 GiB.
+    _, _, p = H.cache_bytes(32, 1, 32, 8, 128, 4096, 0, 1, "bf16", [[1] * 8] * 32)
+    assert p == 536870912
+    _, _, p = H.cache_bytes(32, 1, 32, 32, 128, 4096, 0, 1, "bf16", [[1] * 32] * 32)
+    assert p == 2 * 1024 ** 3
+
+
+BAD = [
+    (dict(n_q=6, n_kv=4), H.DUO_EINVAL),
+    (dict(d_head=96), H.DUO_EUNSUPPORTED),
+    (dict(n_q=12, n_kv=4), H.DUO_EUNSUPPORTED),   # g = 3
+    (dict(n_q=32, n_kv=2), H.DUO_EUNSUPPORTED),   # g = 16
+    (dict(sink=-1), H.DUO_EINVAL),
+    (dict(recent=0), H.DUO_EINVAL),
+    (dict(T_cap=0), H.DUO_EINVAL),
+    (dict(L=0), H.DUO_EINVAL),
+    (dict(mask_value=2), H.DUO_EINVAL),
+    (dict(dtype_code=7), H.DUO_EUNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("over,code", BAD)
+def test_validation_codes(over, code):
+    base = dict(L=2, B=1, n_q=8, n_kv=4, d_head=128, T_cap=100, sink=2, recent=8)
+    base.update({k: v for k, v in over.items() if k in base})
+    n_mask = max(base["L"], 0) * base["n_kv"]
+    mv = over.get("mask_value", 1)
+    buf = (ctypes.c_uint8 * max(n_mask, 1))(*([mv] * max(n_mask, 1)))
+    cfg = H.duo_config(base["L"], base["B"], base["n_q"], base["n_kv"], base["d_head"], base["T_cap"],
+                       base["sink"], base["recent"], over.get("dtype_code", H.DUO_BF16),
+                       ctypes.cast(buf, ctypes.POINTER(ctypes.c_uint8)))
+    a = ctypes.c_size_t()
+    rc = H.lib.duo_cache_bytes(ctypes.byref(cfg), ctypes.byref(a), None)
+    assert rc == code, H.lib.duo_last_error()
+    assert H.lib.duo_last_error()
+
+
+def test_null_config_and_mask():
+    assert H.lib.duo_cache_bytes(None, None, None) == H.DUO_EINVAL
+    cfg = H.duo_config(1, 1, 4, 2, 64, 10, 1, 2, H.DUO_F32, None)
+    assert H.lib.duo_cache_bytes(ctypes.byref(cfg), None, None) == H.DUO_EINVAL
+
+
+def test_calls_on_null_handle_fail_cleanly():
+    x = ctypes.c_int64()
+    assert H.lib.duo_cache_seq_len(None, 0, ctypes.byref(x)) == H.DUO_EINVAL
+    assert H.lib.duo_append(None, 0, None, None, 1, None) == H.DUO_EINVAL
+    assert H.lib.duo_decode(None, 0, None, None, 1.0, None, 0, None) == H.DUO_EINVAL
+    H.lib.duo_cache_free(None)

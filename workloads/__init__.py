@@ -166,6 +166,13 @@ def stacked_rows_f32(w: Workload, layer: int, tensor_id: int, heads: int, p0: in
                      for b in bs])
 
 
+def normal_f32(shape, seed: int) -> np.ndarray:
+    """float32 standard normals for ad-hoc test shapes, seeded like the
+    workloads (SeedSequence([SEED_ROOT, 1000, seed]))."""
+    ss = np.random.SeedSequence([SEED_ROOT, 1000, int(seed)])
+    return np.random.Generator(np.random.PCG64(ss)).standard_normal(shape, dtype=np.float32)
+
+
 def device_fill_normal(t, seed: int, sink_rows: int = 0, sink_scale: float = 1.0):
     """Fill a device tensor [..., positions, d] with seeded standard normals from
     torch's device generator (used where host generation would take minutes,
