@@ -1,0 +1,335 @@
+"""Benchmark of the mixed retrieval/streaming KV attention hot path on one GPU.
+
+Default workload: one full-model decode step of a 70B-GQA-shaped model
+(80 layers, n_q=64, n_kv=8, d=128, bf16, 128,000-token context, S=64,
+W=1024, 2 of 8 KV heads retrieval per layer): per layer, duo_append of one
+new token per KV head, then duo_decode.  The step is captured once in a HIP
+graph and replayed; every replay re-does the full work (append writes,
+decode reads every held K/V row).
+
+Prints one JSON line.  `value` is the step's algorithmic KV bytes (held K+V
+rows read once per KV head, plus the appended rows, queries and outputs)
+divided by the measured step time.  `roofline` is for the decode kernel,
+timed with HIP events around each decode launch on the launch stream.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads as WL  # noqa: E402
+
+METRIC = "mixed-head decode attention: KV GB/s (% HBM peak), µs/step at 128k ctx"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "head_wise_kv_amd", "csrc", "duo_kernels.hip")
+PREFILL_SRC = os.path.join(ROOT, "head_wise_kv_amd", "csrc", "duo_prefill.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def src_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(name: str, kernel_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if there is none or the kernel source changed since it was taken."""
+    path = os.path.join(PROFILES, name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for ln in open(path):
+        if "=" in ln and not ln.startswith("#"):
+            k, v = ln.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_src_sha256_16") != kernel_hash:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ decode
+
+def decode_layer_bytes(w: WL.Workload, mask_row, T: int, append: bool) -> int:
+    """Algorithmic bytes of one layer's step: every held K and V row once per
+    KV head, the queries and outputs, and (if appending) the new K/V rows
+    read from the input and written to the cache."""
+    n_ret = int(np.sum(mask_row))
+    n_str = w.n_kv - n_ret
+    rows = w.B * (n_ret * T + n_str * min(T, w.S + w.W))
+    kv = rows * w.d * w.elem_bytes * 2
+    qo = 2 * w.B * w.n_q * w.d * w.elem_bytes
+    app = 2 * 2 * w.B * w.n_kv * w.d * w.elem_bytes if append else 0
+    return kv + qo + app
+
+
+def bench_decode(w: WL.Workload, steps: int, warmup: int, layers: int):
+    import torch
+    import head_wise_kv_amd as H
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = layers
+    mask = WL.mask_table(w, L)
+    append = w.mode == "decode_append"
+    T = w.T
+    fill = T - 1 if append else T
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    cache = H.DuoCache(L, w.B, w.n_q, w.n_kv, w.d, T, w.S, w.W, w.dtype, mask, device=dev)
+    log(f"{w.name}: arena {cache.arena_bytes / 1e9:.2f} GB, filling {L} layers x {fill} tokens")
+    t0 = time.time()
+    buf_k = torch.empty(w.B, w.n_kv, fill, w.d, dtype=dt, device=dev)
+    buf_v = torch.empty_like(buf_k)
+    for l in range(L):
+        WL.device_fill_normal(buf_k, WL.device_seed(w, l, WL.TENSOR_K), w.S, w.sink_scale)
+        WL.device_fill_normal(buf_v, WL.device_seed(w, l, WL.TENSOR_V))
+        cache.append(l, buf_k, buf_v)
+    del buf_k, buf_v
+    q = torch.empty(L, w.B, w.n_q, w.d, dtype=dt, device=dev)
+    WL.device_fill_normal(q, WL.device_seed(w, 0, WL.TENSOR_Q))
+    out = torch.empty_like(q)
+    k_new = torch.empty(L, w.B, w.n_kv, 1, w.d, dtype=dt, device=dev)
+    v_new = torch.empty_like(k_new)
+    WL.device_fill_normal(k_new, WL.device_seed(w, 0, WL.TENSOR_K, 1))
+    WL.device_fill_normal(v_new, WL.device_seed(w, 0, WL.TENSOR_V, 1))
+    q_l = [q[l] for l in range(L)]
+    o_l = [out[l] for l in range(L)]
+    kn_l = [k_new[l] for l in range(L)]
+    vn_l = [v_new[l] for l in range(L)]
+    torch.cuda.synchronize()
+    log(f"filled in {time.time() - t0:.1f} s")
+
+    stream = torch.cuda.Stream(device=dev)
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        for l in range(L):
+            if append:
+                cache.append(l, kn_l[l], vn_l[l])
+            cache.decode(l, q_l[l], out=o_l[l], scale=w.scale)
+    torch.cuda.synchronize()
+    T_step = T  # tokens held at the measured step (the graph re-appends position T-1)
+    step_bytes = sum(decode_layer_bytes(w, mask[l], T_step, append) for l in range(L))
+
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / steps
+    log(f"graph: {ms_step * 1e3:.1f} us/step (wall {wall / steps * 1e6:.1f} us/step)")
+
+    # Decode kernel alone: HIP events around each launch, on the launch stream.
+    reps = max(2, min(steps, 10))
+    durs = []
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            for l in range(L):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                cache.decode(l, q_l[l], out=o_l[l], scale=w.scale, stream=stream)
+                e1.record(stream)
+                durs.append((e0, e1, l))
+    torch.cuda.synchronize()
+    per_layer_bytes = [decode_layer_bytes(w, mask[l], T_step, False) for l in range(L)]
+    times = [e0.elapsed_time(e1) * 1e-3 for e0, e1, _ in durs]
+    avg_s = float(np.mean(times))
+    avg_bytes = float(np.mean([per_layer_bytes[l] for _, _, l in durs]))
+    return dict(ms_step=ms_step, step_bytes=step_bytes, decode_avg_s=avg_s, decode_avg_bytes=avg_bytes,
+                mask=mask, T=T_step, layers=L, graph_wall_us=wall / steps * 1e6)
+
+
+# ------------------------------------------------------------------ prefill (secondary)
+
+def prefill_flops(w: WL.Workload, mask_row) -> float:
+    """Visible (query, key) pairs x 4 d flops over the whole sequence."""
+    N, S, W, d, g = w.T, w.S, w.W, w.d, w.g
+    t = np.arange(N, dtype=np.float64)
+    causal = float(np.sum(t + 1))
+    lam = float(np.sum(np.minimum(t + 1, np.minimum(S, t + 1) + np.minimum(W, np.maximum(t + 1 - S, 0)))))
+    n_ret = int(np.sum(mask_row))
+    return 4.0 * d * w.B * g * (n_ret * causal + (w.n_kv - n_ret) * lam)
+
+
+def bench_prefill(w: WL.Workload, reps: int = 2):
+    import torch
+    import head_wise_kv_amd as H
+
+    dev = torch.device("cuda:0")
+    mask = WL.mask_table(w, 1)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    N, C = w.T, w.chunk
+    q = torch.empty(w.B, w.n_q, N, w.d, dtype=dt, device=dev)
+    k = torch.empty(w.B, w.n_kv, N, w.d, dtype=dt, device=dev)
+    v = torch.empty_like(k)
+    WL.device_fill_normal(q, WL.device_seed(w, 0, WL.TENSOR_Q))
+    WL.device_fill_normal(k, WL.device_seed(w, 0, WL.TENSOR_K))
+    WL.device_fill_normal(v, WL.device_seed(w, 0, WL.TENSOR_V))
+    qc = [q[:, :, p:p + C].contiguous() for p in range(0, N, C)]
+    kc = [k[:, :, p:p + C].contiguous() for p in range(0, N, C)]
+    vc = [v[:, :, p:p + C].contiguous() for p in range(0, N, C)]
+    oc = [torch.empty_like(x) for x in qc]
+    best = None
+    for r in range(reps + 1):
+        cache = H.DuoCache(1, w.B, w.n_q, w.n_kv, w.d, N, w.S, w.W, w.dtype, mask, device=dev)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(len(qc)):
+            cache.prefill_chunk(0, qc[i], kc[i], vc[i], out=oc[i], scale=w.scale)
+        e1.record()
+        torch.cuda.synchronize()
+        s = e0.elapsed_time(e1) * 1e-3
+        if r > 0:
+            best = s if best is None else min(best, s)
+        del cache
+    flops = prefill_flops(w, mask[0])
+    tf = flops / best / 1e12
+    return dict(workload=w.name, seconds=best, tflops=tf, mfma_frac=tf / BF16_DENSE_TFLOPS, algorithmic_tflop=flops / 1e12)
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+
+def cpu_baseline(w: WL.Workload, budget_s: float = 15.0):
+    """The oracle's decode on host cores over as many whole layers of the
+    workload as fit in about `budget_s` seconds (inputs generated on the host
+    by the seeded recipe; generation is not timed)."""
+    from oracle import attention as OA
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    append = w.mode == "decode_append"
+    spent, nbytes, layers = 0.0, 0, 0
+    for l in range(w.L):
+        mask = WL.retrieval_mask(w, l)
+        K = WL.round_to_dtype(WL.stacked_rows_f32(w, l, WL.TENSOR_K, w.n_kv, 0, w.T), w.dtype)
+        V = WL.round_to_dtype(WL.stacked_rows_f32(w, l, WL.TENSOR_V, w.n_kv, 0, w.T), w.dtype)
+        Q = WL.round_to_dtype(WL.stacked_rows_f32(w, l, WL.TENSOR_Q, w.n_q, w.T - 1, w.T)[:, :, 0], w.dtype)
+        t0 = time.perf_counter()
+        for b in range(w.B):
+            OA.decode_step(Q[b], K[b], V[b], mask, w.S, w.W, w.scale)
+        spent += time.perf_counter() - t0
+        nbytes += decode_layer_bytes(w, mask, w.T, append)
+        layers += 1
+        del K, V
+        if spent >= budget_s:
+            break
+    return dict(value=nbytes / spent / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+                sample=f"{layers} of {w.L} layers of {w.name}, fp64 numpy oracle, {spent:.1f} s")
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa70b_decode_128k",
+                    choices=[n for n, w in WL.WORKLOADS.items() if w.mode != "prefill"])
+    ap.add_argument("--layers", type=int, default=0, help="limit layers (profiling only; 0 = all)")
+    ap.add_argument("--also", default="mha7b_decode_128k",
+                    help="comma-separated extra decode workloads reported under 'also' ('' for none)")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the decode and prefill kernels run on one device); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    w = WL.WORKLOADS[args.workload]
+    L = args.layers if args.layers > 0 else w.L
+    if args.calibrate_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("calibration copy: 1073741824 bytes read, 1073741824 bytes written")
+        del a, b
+    r = bench_decode(w, args.steps, args.warmup, L)
+    value = r["step_bytes"] / (r["ms_step"] * 1e-3) / 1e9
+    achieved = r["decode_avg_bytes"] / r["decode_avg_s"] / 1e9
+    traffic = stored_traffic(f"decode_{w.name}_traffic.txt", src_hash(KERNEL_SRC))
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_step"], 4),
+        "us_per_step": round(r["ms_step"] * 1e3, 1),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) on device; mask seeded per layer)",
+        "config": {"workload": w.name, "layers": L, "batch": w.B, "n_q": w.n_q, "n_kv": w.n_kv, "d_head": w.d,
+                   "context": r["T"], "sink": w.S, "recent": w.W, "retrieval_kv_heads_per_layer": w.n_ret,
+                   "step": "append 1 token + decode, every layer" if w.mode == "decode_append" else "decode, every layer",
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "avg_launch_us": round(r["decode_avg_s"] * 1e6, 2),
+                     "algorithmic_bytes_per_launch": int(r["decode_avg_bytes"])},
+    }
+    also = []
+    for name in [x for x in args.also.split(",") if x and x != w.name]:
+        import gc
+        gc.collect()
+        torch.cuda.empty_cache()
+        wa = WL.WORKLOADS[name]
+        ra = bench_decode(wa, args.steps, args.warmup, wa.L)
+        va = ra["step_bytes"] / (ra["ms_step"] * 1e-3) / 1e9
+        also.append({"workload": name, "value": round(va, 2), "unit": "GB/s", "us_per_step": round(ra["ms_step"] * 1e3, 1),
+                     "hbm_frac": round(va / HBM_PEAK_GBS, 4),
+                     "decode_kernel_gbs": round(ra["decode_avg_bytes"] / ra["decode_avg_s"] / 1e9, 2),
+                     "decode_kernel_us": round(ra["decode_avg_s"] * 1e6, 2)})
+    if also:
+        line["also"] = also
+    if not args.no_prefill:
+        pw = WL.WORKLOADS["llama3_8b_prefill_64k"]
+        p = bench_prefill(pw)
+        line["prefill"] = {"workload": p["workload"], "ms": round(p["seconds"] * 1e3, 3),
+                           "tflops": round(p["tflops"], 2), "mfma_frac": round(p["mfma_frac"], 4),
+                           "peak_tflops": BF16_DENSE_TFLOPS, "algorithmic_tflop": round(p["algorithmic_tflop"], 4)}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -69,6 +69,8 @@ int validate(const duo_config* c) {
   if (c->dtype != DUO_F32 && c->dtype != DUO_BF16) return fail(DUO_EUNSUPPORTED, "dtype %d", c->dtype);
   if (c->T_cap < 1) return fail(DUO_EINVAL, "T_cap must be >= 1");
   if (c->T_cap > INT32_MAX) return fail(DUO_EINVAL, "T_cap must fit int32 (positions are int32)");
+  if ((uint64_t)c->T_cap * (uint64_t)c->d_head * (c->dtype == DUO_BF16 ? 2u : 4u) > 0xffffffffull)
+    return fail(DUO_EUNSUPPORTED, "one head's rows (T_cap * d_head * element size) must fit 4 GiB");
   if (c->sink < 0 || c->recent < 1) return fail(DUO_EINVAL, "need sink >= 0 and recent >= 1");
   if (!c->retrieval_mask) return fail(DUO_EINVAL, "retrieval_mask is NULL");
   for (int i = 0; i < c->L * c->n_kv; ++i)
@@ -116,7 +118,7 @@ void make_plan(const duo_config* c, Plan* p) {
   }
   p->arena = off;
   const size_t rec = decode_rec_floats(c) * sizeof(float);
-  const size_t ws1 = align_up(((size_t)duo::kTargetBlocks + (size_t)c->B * c->n_kv) * rec);
+  const size_t ws1 = align_up(((size_t)duo::kMaxDecodeBlocks + (size_t)c->B * c->n_kv) * rec);
   const size_t ws2 = align_up((size_t)c->B * c->n_kv * duo::kMaxGroups * rec);
   p->workspace = ws1 + ws2;
 }
@@ -132,6 +134,7 @@ struct duo_cache {
   char* arena = nullptr;
   size_t arena_bytes = 0;
   std::vector<int64_t> seq_len;
+  int num_cu = 256;  // compute units of the device current at init (decode work items per call)
 
   duo::LayerPtrs ptrs(int l) const {
     const LayerPlan& lp = plan.layers[l];
@@ -221,6 +224,12 @@ int duo_cache_init(const duo_config* cfg, void* arena, size_t arena_bytes, void*
   c->arena = static_cast<char*>(arena);
   c->arena_bytes = arena_bytes;
   c->seq_len.assign(cfg->L, 0);
+  {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      c->num_cu = n;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int l = 0; l < cfg->L; ++l) {
     const LayerPlan& lp = p.layers[l];
@@ -255,7 +264,7 @@ int duo_decode(duo_cache* c, int layer, const void* q, void* out, float scale, v
   if (int e = check_layer(c, layer)) return e;
   if (!q || !out) return fail(DUO_EINVAL, "q or out is NULL");
   if (!aligned16(q) || !aligned16(out)) return fail(DUO_EINVAL, "q and out must be 16-byte aligned");
-  if (!std::isfinite(scale)) return fail(DUO_EINVAL, "scale must be finite");
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(DUO_EINVAL, "scale must be finite and > 0");
   const int64_t T = c->seq_len[layer];
   if (T < 1) return fail(DUO_EEMPTY, "layer %d holds no token", layer);
   if (!ws || ws_bytes < c->plan.workspace)
@@ -277,21 +286,16 @@ int duo_decode(duo_cache* c, int layer, const void* q, void* out, float scale, v
   a.cap_str = c->cap_str();
   a.rows_ret = T;
   a.rows_str = std::min<int64_t>(T, c->cap_str());
-  // Uniform work items of `chunk` rows (a multiple of 4 wavefronts x 64 rows)
-  // over both head kinds, aiming at kTargetBlocks items per call.
-  const int64_t total = (int64_t)cf.B * (lp.n_ret * a.rows_ret + lp.n_str * a.rows_str);
-  const int64_t tile = (int64_t)duo::kDecodeThreads / 64 * duo::kDecodeRowsPerTile;
-  int64_t chunk = std::max<int64_t>(tile, ceil_div(total, duo::kTargetBlocks));
-  chunk = std::max<int64_t>(chunk, ceil_div(std::max(a.rows_ret, a.rows_str), (int64_t)duo::kSplitGroup * duo::kMaxGroups));
-  chunk = ceil_div(chunk, tile) * tile;
-  a.chunk = chunk;
-  a.split_ret = lp.n_ret ? (int)ceil_div(a.rows_ret, chunk) : 0;
-  a.split_str = lp.n_str ? (int)ceil_div(a.rows_str, chunk) : 0;
-  a.blocks_ret = cf.B * lp.n_ret * a.split_ret;
-  const int blocks = a.blocks_ret + cf.B * lp.n_str * a.split_str;
+  // Work items over the flattened row space of all held rows (retrieval
+  // heads first, then streaming heads): as many as run concurrently, i.e.
+  // one workgroup of four wavefronts per SIMD-wave slot of every CU.
+  a.total_rows = (int64_t)cf.B * (lp.n_ret * a.rows_ret + lp.n_str * a.rows_str);
+  const int64_t target = std::max(1, std::min(c->num_cu * duo::decode_blocks_per_cu(), duo::kMaxDecodeBlocks));
+  a.chunk = std::max<int64_t>(1, ceil_div(a.total_rows, target));
+  const int blocks = (int)ceil_div(a.total_rows, a.chunk);
   const size_t rec = decode_rec_floats(&cf);
   a.ws1 = static_cast<float*>(ws);
-  a.ws2 = a.ws1 + align_up(((size_t)duo::kTargetBlocks + (size_t)cf.B * cf.n_kv) * rec * sizeof(float)) / sizeof(float);
+  a.ws2 = a.ws1 + align_up(((size_t)duo::kMaxDecodeBlocks + (size_t)cf.B * cf.n_kv) * rec * sizeof(float)) / sizeof(float);
   a.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = duo::launch_decode(a, cf.dtype, cf.d_head, cf.n_q / cf.n_kv, blocks, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");

@@ -12,9 +12,8 @@ namespace duo {
 constexpr int kMaxKV = 128;        // KV heads per layer the head maps can hold
 constexpr int kSplitGroup = 16;    // decode partials merged by one first-level merge
 constexpr int kMaxGroups = 64;     // first-level groups per head (so <= 1024 splits)
-constexpr int kTargetBlocks = 1024;  // decode work items aimed for per call
+constexpr int kMaxDecodeBlocks = 1024;  // decode work items per call at most
 constexpr int kDecodeThreads = 256;  // 4 wavefronts of 64
-constexpr int kDecodeRowsPerTile = 64;
 
 // Per-layer head tables: role and compact index of each KV head, and the KV
 // head behind each compact retrieval / streaming index.
@@ -58,9 +57,8 @@ struct DecodeArgs {
   int B, n_q, n_kv, n_ret, n_str;
   int64_t cap_ret, cap_str;     // rows reserved per head
   int64_t rows_ret, rows_str;   // rows held per head
-  int64_t chunk;                // rows per work item
-  int split_ret, split_str;     // work items per head
-  int blocks_ret;               // B * n_ret * split_ret
+  int64_t total_rows;           // B * (n_ret * rows_ret + n_str * rows_str)
+  int64_t chunk;                // rows of the flattened row space per work item
   float scale_log2;             // softmax scale * log2(e)
 };
 
@@ -86,6 +84,7 @@ struct PrefillArgs {
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, int dtype, int d, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int g, int blocks, hipStream_t s);
+int decode_blocks_per_cu();
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int g, hipStream_t s);
 int prefill_rows_per_tile(int dtype, int d);
 
