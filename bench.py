@@ -144,22 +144,27 @@ def bench_decode(w: WL.Workload, steps: int, warmup: int, layers: int):
     ms_step = ev0.elapsed_time(ev1) / steps
     log(f"graph: {ms_step * 1e3:.1f} us/step (wall {wall / steps * 1e6:.1f} us/step)")
 
-    # Decode kernel alone: HIP events around each launch, on the launch stream.
-    reps = max(2, min(steps, 10))
-    durs = []
+    # Decode kernel alone: the L decode launches of one step captured in a
+    # second graph, replayed back to back; HIP events on the launch stream
+    # bracket the replays, so the average covers each kernel plus the graph's
+    # dispatch gap between kernels.
+    dgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(dgraph, stream=stream):
+        for l in range(L):
+            cache.decode(l, q_l[l], out=o_l[l], scale=w.scale)
+    torch.cuda.synchronize()
+    reps = max(3, min(steps, 10))
+    dgraph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
     with torch.cuda.stream(stream):
         for _ in range(reps):
-            for l in range(L):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                cache.decode(l, q_l[l], out=o_l[l], scale=w.scale, stream=stream)
-                e1.record(stream)
-                durs.append((e0, e1, l))
+            dgraph.replay()
+    e1.record(stream)
     torch.cuda.synchronize()
-    per_layer_bytes = [decode_layer_bytes(w, mask[l], T_step, False) for l in range(L)]
-    times = [e0.elapsed_time(e1) * 1e-3 for e0, e1, _ in durs]
-    avg_s = float(np.mean(times))
-    avg_bytes = float(np.mean([per_layer_bytes[l] for _, _, l in durs]))
+    avg_s = e0.elapsed_time(e1) * 1e-3 / (reps * L)
+    avg_bytes = float(np.mean([decode_layer_bytes(w, mask[l], T_step, False) for l in range(L)]))
     return dict(ms_step=ms_step, step_bytes=step_bytes, decode_avg_s=avg_s, decode_avg_bytes=avg_bytes,
                 mask=mask, T=T_step, layers=L, graph_wall_us=wall / steps * 1e6)
 
