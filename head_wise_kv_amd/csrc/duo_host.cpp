@@ -310,7 +310,7 @@ int duo_prefill_chunk(duo_cache* c, int layer, const void* q, const void* k, con
   if (!q || !k || !v || !out) return fail(DUO_EINVAL, "q, k, v or out is NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(DUO_EINVAL, "q, k, v and out must be 16-byte aligned");
-  if (!std::isfinite(scale)) return fail(DUO_EINVAL, "scale must be finite");
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(DUO_EINVAL, "scale must be finite and > 0");
   if (C < 1) return fail(DUO_EINVAL, "chunk length must be >= 1 (got %lld)", (long long)C);
   const int64_t P = c->seq_len[layer];
   if (P + C > c->cfg.T_cap)
@@ -339,10 +339,11 @@ int duo_prefill_chunk(duo_cache* c, int layer, const void* q, const void* k, con
   a.S = cf.sink;
   a.W = cf.recent;
   a.scale_log2 = scale * 1.4426950408889634f;
-  const int rows = duo::prefill_rows_per_tile(cf.dtype, cf.d_head);
-  a.q_tiles = (int)ceil_div(C, rows);
   const int g = cf.n_q / cf.n_kv;
-  a.items_ret = cf.B * lp.n_ret * g * a.q_tiles;
+  int rows = 1, hpi = 1;
+  duo::prefill_plan(cf.dtype, cf.d_head, g, &rows, &hpi);
+  a.q_tiles = (int)ceil_div(C, rows);
+  a.items_ret = cf.B * lp.n_ret * (g / hpi) * a.q_tiles;
   hipError_t e = duo::launch_prefill(a, cf.dtype, cf.d_head, g, s);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   // Commit the chunk after attention has read the cache (same stream).

@@ -76,8 +76,8 @@ struct PrefillArgs {
   int64_t held_str;   // streaming slots holding a token before the chunk: min(P, S+W)
   int S, W;
   float scale_log2;
-  int q_tiles;        // ceil(C / rows per query tile)
-  int items_ret;      // B * n_ret * g * q_tiles (retrieval work items come first)
+  int q_tiles;        // ceil(C / rows per work item)
+  int items_ret;      // B * n_ret * (g / heads per item) * q_tiles (retrieval items come first)
 };
 
 // Launchers (duo_kernels.hip).  dtype: 0 = fp32, 1 = bf16.
@@ -86,6 +86,7 @@ hipError_t launch_append(const AppendArgs& a, int dtype, int d, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int g, int blocks, hipStream_t s);
 int decode_blocks_per_cu();
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int g, hipStream_t s);
-int prefill_rows_per_tile(int dtype, int d);
+// Query rows and query heads one prefill work item covers.
+void prefill_plan(int dtype, int d, int g, int* rows_per_item, int* heads_per_item);
 
 }  // namespace duo
