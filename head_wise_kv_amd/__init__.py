@@ -133,14 +133,21 @@ class DuoCache:
         self.arena = torch.empty(self.arena_bytes, dtype=torch.uint8, device=self.device)
         self.workspace = torch.empty(max(self.workspace_bytes, 256), dtype=torch.uint8, device=self.device)
         self._h = ctypes.c_void_p()
+        self._free = lib.duo_cache_free  # held so teardown at interpreter exit still finds it
         _check(lib.duo_cache_init(ctypes.byref(self._cfg), ctypes.c_void_p(self.arena.data_ptr()),
                                   self.arena_bytes, _stream_handle(stream), ctypes.byref(self._h)))
 
-    def __del__(self):
+    def close(self) -> None:
+        """Free the host handle (the arena and workspace tensors stay with
+        Python's garbage collector)."""
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
-            lib.duo_cache_free(h)
-            self._h = None
+        free = getattr(self, "_free", None)
+        if h is not None and h.value and free is not None:
+            free(h)
+        self._h = None
+
+    def __del__(self):
+        self.close()
 
     # ------------------------------------------------------------ checks
     def _chk(self, t: torch.Tensor, shape, name: str):

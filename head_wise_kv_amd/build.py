@@ -53,7 +53,9 @@ def build(verbose: bool = True, jobs: int = 4) -> str:
         if verbose and text.strip():
             print(text, file=sys.stderr)
     tmp = LIB + ".tmp"
-    link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # -z defs: an unresolved symbol (say, a kernel whose host stub the compiler
+    # dropped) fails the link instead of the first load
+    link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]
     r = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(link)}\n{r.stdout.decode(errors='replace')}")

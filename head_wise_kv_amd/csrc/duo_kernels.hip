@@ -449,7 +449,7 @@ void decode_kernel(DecodeArgs a) {
   const int rg = lane >> 3, s = lane & 7;
   const int64_t blk = blockIdx.x;
   const int64_t b0 = blk * a.chunk;
-  const int64_t b1 = min(b0 + a.chunk, a.total_rows);
+  const int64_t b1 = b0 + a.chunk < a.total_rows ? b0 + a.chunk : a.total_rows;
   const int64_t r_ret = (int64_t)a.B * a.n_ret * a.rows_ret;  // rows of all retrieval heads
 
   for (int64_t pos = b0; pos < b1;) {
@@ -479,7 +479,7 @@ void decode_kernel(DecodeArgs a) {
       kbase = a.lp.k_str + off;
       vbase = a.lp.v_str + off;
     }
-    const int64_t seg_end = min(b1, h0 + hrows);
+    const int64_t seg_end = b1 < h0 + hrows ? b1 : h0 + hrows;
     const int64_t r0 = pos - h0, r1 = seg_end - h0;   // rows of this head in this segment
     pos = seg_end;
     const int fh = b * a.n_kv + kvh;

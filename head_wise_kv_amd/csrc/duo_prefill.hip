@@ -8,17 +8,19 @@
 // chunk is committed to the cache by the append kernel afterwards.
 //
 // bf16: a dense contraction, tiled on MFMA (v_mfma_f32_32x32x16_bf16).
-//   * Work item = one workgroup of two wavefronts; each wavefront owns 64
-//     query rows of one query head (two 32-row MFMA N tiles), and the two
-//     wavefronts share the K/V tiles of their KV head (two heads of a GQA
-//     group, or two row blocks of one head).  64 query rows per wavefront is
-//     what keeps LDS reads (K and V operands, re-read by every wavefront) under
-//     the LDS bandwidth at full MFMA rate.
-//   * K and V tiles of 64 keys are brought into LDS with direct global->LDS
-//     loads, double buffered: the next tile streams in while the current one
-//     is consumed.  Rows are XOR-swizzled in 16-byte chunks (the swizzle is
-//     applied on the global side of the copy) so operand reads are free of
-//     bank conflicts.
+//   * Work item = one workgroup of four wavefronts: two row wavefronts, each
+//     owning 64 query rows of one query head (two 32-row MFMA N tiles; two
+//     heads of a GQA group, or two row blocks of one head), times two key
+//     halves that take the even and the odd key tiles of the same rows.  The
+//     halves merge their softmax states through LDS at the end, so every SIMD
+//     has a wavefront even when the item count is small.  64 query rows per
+//     wavefront keeps the LDS operand traffic (K and V re-read by every
+//     wavefront) well under the LDS bandwidth at full MFMA rate.
+//   * K and V tiles of 64 keys are brought into LDS with direct buffer->LDS
+//     loads, double buffered per half: the next tile streams in while the
+//     current one is consumed.  Rows are XOR-swizzled in 16-byte chunks (the
+//     swizzle is applied on the global side of the copy) so operand reads are
+//     free of bank conflicts.
 //   * Scores S^T = K Q^T put keys on the MFMA M axis and queries on N, so each
 //     lane holds one query's scores and the softmax needs one exchange with
 //     the partner lane.  P^T then feeds O^T = V^T P^T directly from the
@@ -26,7 +28,10 @@
 //     row-major V tile through LDS transpose reads (ds_read_b64_tr_b16).
 //   * Streaming heads visit only the sink tiles, the ring tiles some row's
 //     window reaches, and the local band of the chunk; retrieval heads the
-//     causal prefix.  Tiles every row sees in full skip the mask.
+//     causal prefix.  Tiles every row of the item sees in full skip the mask;
+//     the rest test each key's visible-row interval with one compare.
+//   * The online softmax rescales the O accumulators only when a row's
+//     running max has grown by more than a fixed slack.
 //
 // fp32: a plain vector-ALU path (one wavefront per query row) kept for
 // completeness of the dtype surface; it is not tuned.
@@ -45,10 +50,15 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kPfWaves = 2;                       // wavefronts per workgroup
-constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kPfRowWaves = 2;                    // wavefronts per key half (one 64-row block each)
+constexpr int kPfHalves = 2;                      // key halves: even / odd key tiles
+constexpr int kPfThreads = 64 * kPfRowWaves * kPfHalves;
 constexpr int kPfRowsPerWave = 64;                // query rows per wavefront
 constexpr int kBN = 64;                           // keys per tile
+
+// Integer min / max by plain comparison (kept off any floating-point path).
+__device__ __forceinline__ int64_t min64(int64_t x, int64_t y) { return x < y ? x : y; }
+__device__ __forceinline__ int64_t max64(int64_t x, int64_t y) { return x > y ? x : y; }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
@@ -62,6 +72,35 @@ __device__ __forceinline__ bool visible(int64_t kp, int64_t t, bool ret, int S, 
   return kp >= 0 && kp <= t && (ret || kp < S || kp >= t - W + 1);
 }
 
+// Visibility of a key as an interval of chunk rows: the key at absolute
+// position kp is seen by the rows i (absolute position P + i) with
+// lo <= i <= lo + span, where lo = kp - P and span is unbounded for keys under
+// the causal mask alone (retrieval heads, sink keys) and W - 1 otherwise (the
+// local window).  The test is one unsigned compare: (unsigned)(i - lo) <= span.
+// Keys that do not exist get lo = -1, span = 0, which no row i >= 0 passes.
+// Positions stay below 2^31, so every difference fits in 32 bits.
+struct KeySpan {
+  int32_t lo;
+  uint32_t span;
+};
+__device__ __forceinline__ KeySpan key_span(int64_t kp, int64_t P, bool ret, int S, int W) {
+  KeySpan k;
+  if (kp < 0) {
+    k.lo = -1;
+    k.span = 0;
+  } else {
+    k.lo = (int32_t)(kp - P);
+    k.span = (ret || kp < S) ? (uint32_t)0x7fffffff - (uint32_t)k.lo : (uint32_t)(W - 1);
+  }
+  return k;
+}
+__device__ __forceinline__ bool sees(int32_t i, int32_t lo, uint32_t span) { return (uint32_t)(i - lo) <= span; }
+
+// Skip the O rescale until the running max has grown by more than this many
+// log2 units; probabilities then stay below 2^kRescaleSlack, well inside bf16
+// and fp32 range.
+constexpr float kRescaleSlack = 8.f;
+
 // Key tile sources.
 enum : int { SRC_CACHE_LINEAR = 0, SRC_CACHE_SLOTS = 1, SRC_CHUNK = 2 };
 
@@ -74,7 +113,7 @@ struct TileRanges {
 __device__ __forceinline__ TileRanges plan_tiles(const PrefillArgs& a, bool ret, int64_t i0, int64_t i1) {
   // rows [i0, i1) of the chunk; query positions P+i0 .. P+i1-1
   TileRanges tr;
-  const int64_t chunk_hi = (min(i1, a.C) + kBN - 1) / kBN;  // causal: keys jj <= i < i1
+  const int64_t chunk_hi = (min64(i1, a.C) + kBN - 1) / kBN;  // causal: keys jj <= i < i1
   if (ret) {
     tr.cache_lo = 0;
     tr.cache_hi = (a.P + kBN - 1) / kBN;
@@ -85,20 +124,20 @@ __device__ __forceinline__ TileRanges plan_tiles(const PrefillArgs& a, bool ret,
     // cache slots: sinks always; ring slots only if some row's window reaches back before P
     const int64_t held = a.held_str;
     const bool ring_needed = (i0 < (int64_t)a.W - 1);
-    const int64_t last_slot = ring_needed ? held : min<int64_t>(held, a.S);
+    const int64_t last_slot = ring_needed ? held : min64(held, a.S);
     tr.cache_lo = 0;
     tr.cache_hi = (last_slot + kBN - 1) / kBN;
     // chunk: sink keys (positions < S) and the band jj >= i0 - W + 1
-    const int64_t sink_rows = max<int64_t>(0, min<int64_t>(a.C, (int64_t)a.S - a.P));
+    const int64_t sink_rows = max64(0, min64(a.C, (int64_t)a.S - a.P));
     const int64_t sink_tiles = (sink_rows + kBN - 1) / kBN;
-    const int64_t band_lo = max<int64_t>(0, i0 - a.W + 1) / kBN;
+    const int64_t band_lo = max64(0, i0 - a.W + 1) / kBN;
     if (band_lo <= sink_tiles) {
       tr.chunk_lo0 = 0;
       tr.chunk_hi0 = chunk_hi;
       tr.chunk_lo1 = tr.chunk_hi1 = 0;
     } else {
       tr.chunk_lo0 = 0;
-      tr.chunk_hi0 = min(sink_tiles, chunk_hi);
+      tr.chunk_hi0 = min64(sink_tiles, chunk_hi);
       tr.chunk_lo1 = band_lo;
       tr.chunk_hi1 = chunk_hi;
     }
@@ -115,7 +154,7 @@ struct PfShape {
   static constexpr int DMA_PER_TILE = TILE_BYTES / 1024;  // 1 KB per wavefront-wide direct load
   static constexpr int KSTEPS = D / 16;             // MFMA k-steps over d for S^T
   static constexpr int DT = D / 32;                 // 32-row tiles of O^T over d
-  static_assert(DMA_PER_TILE % kPfWaves == 0, "tile loads split over the wavefronts");
+  static_assert(DMA_PER_TILE % kPfRowWaves == 0, "tile loads split over the wavefronts");
   // K rows: chunk c of key r sits at chunk slot c ^ swz_k(r) (A-operand reads
   // of 16 consecutive keys at one chunk hit 16 distinct bank groups).
   __device__ static __forceinline__ int swz_k(int r) { return CPR == 16 ? (r & 15) : ((r >> 1) & 7); }
@@ -156,27 +195,45 @@ __device__ __forceinline__ PfItem pf_item(const PrefillArgs& a, int g, int hpi) 
   return w;
 }
 
-// Direct global->LDS copy of one 64-row tile (K or V): wavefront `wave`
-// issues every kPfWaves-th 1 KB piece.  Piece n covers LDS bytes
-// [n*1024, n*1024+1024): lane i writes 16 bytes at n*1024 + i*16, i.e. row
-// (n*1024 + i*16) / (16*CPR), chunk slot ((n*64 + i) % CPR); the global
-// chunk it fetches is that slot XOR the row's swizzle.  Rows past `limit`
-// are clamped to the last valid row (their keys are masked).
+// Direct global->LDS copies of a 64-row tile (K or V) through a buffer
+// resource.  The tile is 1 KB pieces; piece n covers LDS bytes
+// [n*1024, n*1024+1024), lane i writing 16 bytes at n*1024 + i*16, i.e. row
+// (n*64 + i) / CPR at chunk slot (n*64 + i) % CPR; the global chunk it fetches
+// is that slot XOR the row's swizzle.  The byte offset of that chunk within the
+// tile depends only on (n, lane), so it is computed once per kernel; each tile
+// only rebuilds the scalar resource (base = first row, size = rows present).
+// Rows past the end are out of range for the resource and read as zero.
 template <int D, bool IS_V>
-__device__ __forceinline__ void dma_tile(char* lds_tile, const char* src, int64_t base, int64_t limit, int wave,
-                                         int lane) {
+__device__ __forceinline__ uint32_t dma_offset(int n, int lane) {
   using SH = PfShape<D>;
+  const int piece = n * 64 + lane;
+  const int r = piece / SH::CPR;
+  const int c = (piece % SH::CPR) ^ (IS_V ? SH::swz_v(r) : SH::swz_k(r));
+  return (uint32_t)(r * (D * 2) + c * 16);
+}
+
+constexpr int kBufferRsrcWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
+
+// Issue this wavefront's pieces (wave, wave + kPfRowWaves, ...) of one tile.
+template <int N>
+__device__ __forceinline__ void dma_pieces(__amdgpu_buffer_rsrc_t rsrc, char* lds_tile, int wave,
+                                           const uint32_t (&off)[N]) {
 #pragma unroll
-  for (int n = wave; n < SH::DMA_PER_TILE; n += kPfWaves) {
-    const int piece = n * 64 + lane;              // 16-byte slot index within the tile
-    const int r = piece / SH::CPR;
-    const int slot = piece % SH::CPR;
-    const int c = slot ^ (IS_V ? SH::swz_v(r) : SH::swz_k(r));
-    const int64_t row = min<int64_t>(base + r, limit - 1);
-    const char* g = src + (size_t)row * (D * 2) + c * 16;
-    __builtin_amdgcn_global_load_lds((const void*)g, (__attribute__((address_space(3))) void*)(lds_tile + n * 1024),
-                                     16, 0, 0);
-  }
+  for (int j = 0; j < N; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(lds_tile + (wave + kPfRowWaves * j) * 1024), 16, off[j], 0, 0,
+        0);
+}
+
+// Values that are the same in every lane, moved to scalar registers (a buffer
+// resource must live there).
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  return reinterpret_cast<const char*>(uniform64(reinterpret_cast<int64_t>(p)));
 }
 
 template <int D>
@@ -184,32 +241,37 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
   using SH = PfShape<D>;
   constexpr int CPR = SH::CPR, KSTEPS = SH::KSTEPS, DT = SH::DT;
 
-  __shared__ __attribute__((aligned(1024))) char k_lds[2][SH::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char v_lds[2][SH::TILE_BYTES];
-  __shared__ int64_t kpos_lds[2][kBN];
-  __shared__ int s_full[2];
+  // [key half][buffer]
+  __shared__ __attribute__((aligned(1024))) char k_lds[kPfHalves][2][SH::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds[kPfHalves][2][SH::TILE_BYTES];
+  __shared__ int32_t klo_lds[kPfHalves][2][kBN];
+  __shared__ uint32_t kspan_lds[kPfHalves][2][kBN];
+  __shared__ int s_full[kPfHalves][2];
 
   const PfItem w = pf_item(a, g, hpi);
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = wave / kPfRowWaves;   // key half: tiles kh, kh + 2, kh + 4, ...
+  const int sub = wave % kPfRowWaves;  // row wavefront within the half
   const int n = lane & 31, hf = lane >> 5;
-  // this wavefront's head and rows: hpi heads x (kPfWaves / hpi) row blocks
-  const int h = w.h_first + (wave % hpi);
-  const int rows_item = kPfRowsPerWave * (kPfWaves / hpi);
+  // this wavefront's head and rows: hpi heads x (kPfRowWaves / hpi) row blocks
+  const int h = w.h_first + (sub % hpi);
+  const int rows_item = kPfRowsPerWave * (kPfRowWaves / hpi);
   const int64_t i0 = (int64_t)w.qt * rows_item;                       // item's first chunk row
-  const int64_t i1 = min<int64_t>(i0 + rows_item, a.C);
-  const int64_t wr0 = i0 + (int64_t)(wave / hpi) * kPfRowsPerWave;   // wavefront's first row
+  const int64_t i1 = min64(i0 + rows_item, a.C);
+  const int64_t wr0 = i0 + (int64_t)(sub / hpi) * kPfRowsPerWave;    // wavefront's first row
   const size_t rowb = (size_t)D * 2;
 
   // Q^T operands: lane holds 8 consecutive d of query row (wr0 + 32*nt + n) per k-step.
   bf16x8_t qb[2][KSTEPS];
-  int64_t tq[2];
+  int32_t iq[2];  // chunk row of the lane's query in tile nt
   bool qvalid[2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int64_t qrow = wr0 + 32 * nt + n;
     qvalid[nt] = qrow < a.C;
-    tq[nt] = a.P + qrow;
+    iq[nt] = (int32_t)qrow;
     const char* qp = static_cast<const char*>(a.q) + (((size_t)w.b * a.n_q + h) * a.C + (qvalid[nt] ? qrow : 0)) * rowb;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -241,8 +303,25 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
   const int64_t n_c0 = tr.chunk_hi0 - tr.chunk_lo0;
   const int64_t n_c1 = tr.chunk_hi1 - tr.chunk_lo1;
   const int64_t n_tiles = n_cache + n_c0 + n_c1;
-  // query positions the item covers (for the "every row sees every key" test)
-  const int64_t t_lo = a.P + i0;
+
+  // per-lane byte offsets of this wavefront's pieces within a K / V tile
+  constexpr int kPieces = SH::DMA_PER_TILE / kPfRowWaves;
+  uint32_t koff[kPieces], voff[kPieces];
+#pragma unroll
+  for (int j = 0; j < kPieces; ++j) {
+    koff[j] = dma_offset<D, false>(sub + kPfRowWaves * j, lane);
+    voff[j] = dma_offset<D, true>(sub + kPfRowWaves * j, lane);
+  }
+  // Rows past a source's end read as zero; clear both buffers once so no
+  // stale bit pattern (which could be a NaN) ever meets a zero probability.
+  {
+    const u32x4_t z = {0, 0, 0, 0};
+    for (int off = tid * 16; off < kPfHalves * 2 * SH::TILE_BYTES; off += kPfThreads * 16) {
+      *reinterpret_cast<u32x4_t*>(&k_lds[0][0][0] + off) = z;
+      *reinterpret_cast<u32x4_t*>(&v_lds[0][0][0] + off) = z;
+    }
+    __syncthreads();
+  }
 
   // Tile `it` -> (source, first row, row limit).
   auto tile_src = [&](int64_t it, int& src, int64_t& base, int64_t& limit) {
@@ -260,36 +339,39 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
       limit = a.C;
     }
   };
-  // Issue tile `it` into buffer `buf`: K/V by direct loads, positions by plain
-  // stores (thread < kBN), and a flag telling whether every row of the item
-  // sees every key of the tile (then the mask is skipped).
+  // Issue tile `it` into buffer `buf` of this wavefront's key half: K/V by
+  // direct loads (pieces split over the half's wavefronts), key visibility by
+  // plain stores (the half's first wavefront), and a flag telling whether
+  // every row of the item sees every key of the tile (then the mask is skipped).
   auto issue = [&](int64_t it, int buf) {
     int src;
     int64_t base, limit;
     tile_src(it, src, base, limit);
     const char* ks = (src == SRC_CHUNK) ? kn : kc;
     const char* vs = (src == SRC_CHUNK) ? vn : vc;
-    dma_tile<D, false>(k_lds[buf], ks, base, limit, wave, lane);
-    dma_tile<D, true>(v_lds[buf], vs, base, limit, wave, lane);
-    if (tid < kBN) {
-      const int64_t row = base + tid;
-      int64_t kp = INT64_MIN;  // past the end: never visible
+    const int nbytes = __builtin_amdgcn_readfirstlane((int)min64(limit - base, kBN) * (int)rowb);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)uniform_ptr(ks + (size_t)base * rowb), (short)0, nbytes, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)uniform_ptr(vs + (size_t)base * rowb), (short)0, nbytes, kBufferRsrcWord3);
+    dma_pieces(rk, k_lds[kh][buf], sub, koff);
+    dma_pieces(rv, v_lds[kh][buf], sub, voff);
+    if (sub == 0) {  // one wavefront, all lanes: lane = key of the tile
+      const int64_t row = base + lane;
+      int64_t kp = -1;  // past the end: never visible
       if (row < limit) {
         if (src == SRC_CACHE_LINEAR) kp = row;
         else if (src == SRC_CACHE_SLOTS) kp = posc[row];
         else kp = a.P + row;
       }
-      kpos_lds[buf][tid] = kp;
-    }
-    if (tid == 0) {
-      // full iff all 64 rows exist and (retrieval: the last key precedes the
-      // first query) -- streaming tiles are always masked (the window moves).
-      const bool all_rows = base + kBN <= limit;
-      int64_t last_pos;
-      if (src == SRC_CACHE_LINEAR) last_pos = base + kBN - 1;
-      else if (src == SRC_CHUNK) last_pos = a.P + base + kBN - 1;
-      else last_pos = INT64_MAX;
-      s_full[buf] = (w.ret && all_rows && last_pos <= t_lo) ? 1 : 0;
+      const KeySpan ks = key_span(kp, a.P, w.ret, a.S, a.W);
+      klo_lds[kh][buf][lane] = ks.lo;
+      kspan_lds[kh][buf][lane] = ks.span;
+      // the tile needs no mask iff every key is seen by the item's first and
+      // last row (the visible rows of a key form an interval)
+      const bool all = sees((int32_t)i0, ks.lo, ks.span) && sees((int32_t)(i1 - 1), ks.lo, ks.span);
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(all);
+      if (lane == 0) s_full[kh][buf] = (bal == ~0ull) ? 1 : 0;
     }
   };
 
@@ -302,93 +384,114 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
       for (int r = 0; r < 16; ++r) o[dt][nt][r] = 0.f;
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
-  if (n_tiles > 0) issue(0, 0);
-  for (int64_t it = 0; it < n_tiles; ++it) {
-    const int buf = (int)(it & 1);
-    // this wavefront's direct loads for tile `it` have landed; after the
-    // barrier every wavefront's have, and the previous tile is consumed.
+  // The two halves walk the tile list in lockstep, one barrier per step.
+  const int64_t n_steps = (n_tiles + 1) / 2;
+  if (kh < n_tiles) issue(kh, 0);
+  for (int64_t step = 0; step < n_steps; ++step) {
+    const int buf = (int)(step & 1);
+    // this wavefront's direct loads for the current tile have landed; after
+    // the barrier every wavefront's have, and the previous tile is consumed.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (it + 1 < n_tiles) issue(it + 1, buf ^ 1);
+    if (2 * (step + 1) + kh < n_tiles) issue(2 * (step + 1) + kh, buf ^ 1);
+    if (2 * step + kh >= n_tiles) continue;  // this half has no tile left (wavefront-uniform)
 
-    const char* kt = k_lds[buf];
-    const char* vt = v_lds[buf];
-    // ---- S^T = K Q^T: [key half ct][query tile nt]
-    f32x16_t s[2][2];
+    const char* kt = k_lds[kh][buf];
+    const char* vt = v_lds[kh][buf];
+    const bool full = s_full[kh][buf] != 0;
+    // The tile is consumed in two halves of 32 keys (ct): scores, softmax and
+    // the P V product of one half before the next, which halves the score and
+    // probability registers.
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
+      // ---- S^T = K Q^T for keys ct*32 .. ct*32+31: [query tile nt]
+      f32x16_t s[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[ct][nt][r] = 0.f;
+        for (int r = 0; r < 16; ++r) s[nt][r] = 0.f;
       const int key = ct * 32 + n;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         const int c = 2 * ks + hf;
-        const u32x4_t av =
-            *reinterpret_cast<const u32x4_t*>(kt + key * (CPR * 16) + ((c ^ SH::swz_k(key)) * 16));
+        const u32x4_t av = *reinterpret_cast<const u32x4_t*>(kt + key * (CPR * 16) + ((c ^ SH::swz_k(key)) * 16));
         const bf16x8_t aop = __builtin_bit_cast(bf16x8_t, av);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
-          s[ct][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qb[nt][ks], s[ct][nt], 0, 0, 0);
+          s[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qb[nt][ks], s[nt], 0, 0, 0);
       }
-    }
 
-    // ---- mask (unless every row sees every key), online softmax in log2 units
-    if (!s_full[buf]) {
+      // ---- mask (unless every row sees every key of the tile); register r
+      // of the lane holds key ct*32 + 8*(r/4) + 4*hf + r%4
+      if (!full) {
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int key0 = ct * 32 + 8 * r4 + 4 * hf;
+          const int4 lo4 = *reinterpret_cast<const int4*>(&klo_lds[kh][buf][key0]);
+          const uint4 sp4 = *reinterpret_cast<const uint4*>(&kspan_lds[kh][buf][key0]);
+          const int32_t lo[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
+          const uint32_t sp[4] = {sp4.x, sp4.y, sp4.z, sp4.w};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = ct * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const int64_t kp = kpos_lds[buf][key];
+          for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-            if (!visible(kp, tq[nt], w.ret, a.S, a.W)) s[ct][nt][r] = -INFINITY;
+            for (int nt = 0; nt < 2; ++nt)
+              if (!sees(iq[nt], lo[j], sp[j])) s[nt][4 * r4 + j] = -INFINITY;
         }
-    }
-    uint32_t pb[2][2][2][4];  // [nt][ct][k-step][dword]: P^T as bf16 pairs
+      }
+
+      // ---- online softmax in log2 units; the accumulators are rescaled only
+      // when some lane's running max has grown past the slack (a
+      // wavefront-uniform decision)
+      float mx[2];
+      bool grow = false;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float mx = -INFINITY;
+      for (int nt = 0; nt < 2; ++nt) {
+        float v = s[nt][0];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+        for (int r = 1; r < 16; ++r) v = fmaxf(v, s[nt][r]);
+        mx[nt] = fmaxf(v, __shfl_xor(v, 32)) * a.scale_log2;
+        grow |= mx[nt] > m_run[nt] + kRescaleSlack;
+      }
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[ct][nt][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
-      const float m_new = fmaxf(m_run[nt], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[nt] - m_use);
-      m_run[nt] = m_new;
-      float psum = 0.f;
+        for (int nt = 0; nt < 2; ++nt) {
+          const float m_new = fmaxf(m_run[nt], mx[nt]);
+          const float alpha = fast_exp2(m_run[nt] - ((m_new == -INFINITY) ? 0.f : m_new));
+          m_run[nt] = m_new;
+          l_run[nt] *= alpha;
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[dt][nt][r] *= alpha;
+        }
+      }
+      // P^T as bf16 pairs: [nt][k-step st][dword]; k-step st covers keys
+      // ct*32 + 16*st .. +15, i.e. registers 8*st .. 8*st+7
+      uint32_t pb[2][2][4];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float m_use = (m_run[nt] == -INFINITY) ? 0.f : m_run[nt];
+        float psum = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(fmaf(s[ct][nt][r], a.scale_log2, -m_use));
-          const float p1 = fast_exp2(fmaf(s[ct][nt][r + 1], a.scale_log2, -m_use));
+          const float p0 = fast_exp2(fmaf(s[nt][r], a.scale_log2, -m_use));
+          const float p1 = fast_exp2(fmaf(s[nt][r + 1], a.scale_log2, -m_use));
           psum += p0 + p1;
-          pb[nt][ct][r >> 3][(r & 7) >> 1] = pack_bf16(p0, p1);
+          pb[nt][r >> 3][(r & 7) >> 1] = pack_bf16(p0, p1);
         }
-      l_run[nt] = l_run[nt] * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][nt][r] *= alpha;
-    }
+        l_run[nt] += psum;
+      }
 
-    // ---- O^T += V^T P^T; V^T operands by transpose reads of the V tile:
-    // lane (group g = lane/16, i = lane%16) reads row kb + i/4 at columns
-    // dt*32 + 16*(g%2) + 4*(i%4); lane receives V[kb + 0..3][its d].
-    const int g16 = lane >> 4, i16 = lane & 15;
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+      // ---- O^T += V^T P^T; V^T operands by transpose reads of the V tile:
+      // lane (group g16 = lane/16, i16 = lane%16) reads row kb + i16/4 at
+      // columns dt*32 + 16*(g16%2) + 4*(i16%4) and receives V[kb + 0..3][its d].
+      const int g16 = lane >> 4, i16 = lane & 15;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         bf16x8_t bop[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          const u32x4_t bw = {pb[nt][ct][st][0], pb[nt][ct][st][1], pb[nt][ct][st][2], pb[nt][ct][st][3]};
+          const u32x4_t bw = {pb[nt][st][0], pb[nt][st][1], pb[nt][st][2], pb[nt][st][3]};
           bop[nt] = __builtin_bit_cast(bf16x8_t, bw);
         }
 #pragma unroll
@@ -411,6 +514,44 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
             o[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop[nt], o[dt][nt], 0, 0, 0);
         }
       }
+    }
+  }
+
+  // ---- merge the odd half into the even half through LDS (the tile buffers
+  // are free now): per lane, registers in order (dt, nt, r), then m and l.
+  constexpr int NREG = DT * 2 * 16;
+  static_assert(kPfRowWaves * NREG * 64 * 4 <= kPfHalves * 2 * SH::TILE_BYTES, "exchange fits the K buffers");
+  static_assert(kPfRowWaves * 4 * 64 * 4 <= kPfHalves * 2 * SH::TILE_BYTES, "m, l fit the V buffers");
+  float* xo = reinterpret_cast<float*>(&k_lds[0][0][0]) + sub * NREG * 64 + lane;
+  float* xml = reinterpret_cast<float*>(&v_lds[0][0][0]) + sub * 4 * 64 + lane;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (kh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[((dt * 2 + nt) * 16 + r) * 64] = o[dt][nt][r];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      xml[nt * 64] = m_run[nt];
+      xml[(2 + nt) * 64] = l_run[nt];
+    }
+  }
+  __syncthreads();
+  if (kh == 1) return;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const float m2 = xml[nt * 64], l2 = xml[(2 + nt) * 64];
+    const float m_new = fmaxf(m_run[nt], m2);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float a1 = fast_exp2(m_run[nt] - m_use), a2 = fast_exp2(m2 - m_use);
+    l_run[nt] = l_run[nt] * a1 + l2 * a2;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][nt][r] = o[dt][nt][r] * a1 + xo[((dt * 2 + nt) * 16 + r) * 64] * a2;
   }
 
   // ---- normalise and store: lane holds d = dt*32 + 8*(r/4) + 4*hf + r%4 of query 32*nt + n
@@ -499,7 +640,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a, int g) 
     l_run = l_run * alpha + p;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
-    const int nk = (int)min<int64_t>(64, n_keys - k0);
+    const int nk = (int)min64(64, n_keys - k0);
     for (int j = 0; j < nk; ++j) {
       const float pj = __shfl(p, j);
       if (pj == 0.f) continue;
@@ -523,9 +664,9 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a, int g) 
 void prefill_plan(int dtype, int d, int g, int* rows_per_item, int* heads_per_item) {
   (void)d;
   if (dtype == 1) {
-    const int hpi = g >= kPfWaves ? kPfWaves : g;  // query heads per work item
+    const int hpi = g >= kPfRowWaves ? kPfRowWaves : g;  // query heads per work item
     *heads_per_item = hpi;
-    *rows_per_item = kPfRowsPerWave * (kPfWaves / hpi);
+    *rows_per_item = kPfRowsPerWave * (kPfRowWaves / hpi);
   } else {
     *heads_per_item = 1;
     *rows_per_item = 1;
