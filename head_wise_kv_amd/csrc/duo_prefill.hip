@@ -67,6 +67,10 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float max3(float x, float y, float z) { return fmaxf(fmaxf(x, y), z); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+constexpr bf16x2_t kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 __device__ __forceinline__ bool visible(int64_t kp, int64_t t, bool ret, int S, int W) {
   return kp >= 0 && kp <= t && (ret || kp < S || kp >= t - W + 1);
@@ -236,10 +240,203 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   return reinterpret_cast<const char*>(uniform64(reinterpret_cast<int64_t>(p)));
 }
 
+// ---- per-tile pieces of the MFMA path (one wavefront, 64 query rows = two
+// 32-row N tiles nt, one 64-key tile = two 32-key halves ct)
+
+// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
+
+// S^T = K Q^T for the keys ct*32 .. ct*32+31 of the tile: s[nt] register r of
+// lane (n, hf) is the score of key ct*32 + 8*(r/4) + 4*hf + r%4 and query
+// 32*nt + n.
+template <int D>
+__device__ __forceinline__ void pf_scores(f32x16_t (&s)[2], const bf16x8_t (&qb)[2][D / 16], const char* kt, int ct,
+                                          int lane) {
+  using SH = PfShape<D>;
+  const int key = ct * 32 + (lane & 31);
+  const int hf = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < SH::KSTEPS; ++ks) {
+    const int c = 2 * ks + hf;
+    const u32x4_t av = *reinterpret_cast<const u32x4_t*>(kt + key * (SH::CPR * 16) + ((c ^ SH::swz_k(key)) * 16));
+    const bf16x8_t aop = __builtin_bit_cast(bf16x8_t, av);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      s[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qb[nt][ks], ks == 0 ? f32x16_t{} : s[nt], 0, 0, 0);
+  }
+}
+
+// Scores of keys a row does not see (half ct of the tile) become -inf.
+__device__ __forceinline__ void pf_mask(f32x16_t (&s)[2], const int32_t* klo, const uint32_t* kspan,
+                                        const int32_t (&iq)[2], int ct, int lane) {
+  const int hf = lane >> 5;
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    const int key0 = ct * 32 + 8 * r4 + 4 * hf;  // keys key0 .. key0+3 in registers 4*r4 .. 4*r4+3
+    const int4 lo4 = *reinterpret_cast<const int4*>(klo + key0);
+    const uint4 sp4 = *reinterpret_cast<const uint4*>(kspan + key0);
+    const int32_t lo[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
+    const uint32_t sp[4] = {sp4.x, sp4.y, sp4.z, sp4.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        if (!sees(iq[nt], lo[j], sp[j])) s[nt][4 * r4 + j] = -INFINITY;
+  }
+}
+
+// Online softmax of one half: updates the running max m (lazily: a row's
+// max moves only when it has grown past the slack), the running sum l, and
+// returns P^T as bf16 pairs pb[nt][k-step st][dword] plus the factor
+// alpha[nt] the accumulators must be scaled by; the result says whether any
+// lane's alpha differs from 1.
+__device__ __forceinline__ bool pf_softmax(const f32x16_t (&s)[2], float (&m_run)[2], float (&l_run)[2],
+                                           uint32_t (&pb)[2][2][4], float (&alpha)[2], float scale_log2) {
+  bool grow = false;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const f32x16_t& x = s[nt];
+    const float v = fmaxf(max3(max3(x[0], x[1], x[2]), max3(x[3], x[4], x[5]), max3(x[6], x[7], x[8])),
+                          max3(max3(x[9], x[10], x[11]), max3(x[12], x[13], x[14]), x[15]));
+    const float mx = fmaxf(v, __shfl_xor(v, 32)) * scale_log2;
+    const bool g = mx > m_run[nt] + kRescaleSlack;
+    grow |= g;
+    const float m_new = g ? mx : m_run[nt];  // mx > m_run here
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    alpha[nt] = fast_exp2(m_run[nt] - m_use);
+    m_run[nt] = m_new;
+    // the row sum adds the bf16-rounded probabilities, the same values the
+    // P V product uses
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = fast_exp2(fmaf(x[r], scale_log2, -m_use));
+      const float p1 = fast_exp2(fmaf(x[r + 1], scale_log2, -m_use));
+      const uint32_t pp = pack_bf16(p0, p1);
+      pb[nt][r >> 3][(r & 7) >> 1] = pp;
+      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), kOnesBf16x2, psum, false);
+    }
+    l_run[nt] = l_run[nt] * alpha[nt] + psum;
+  }
+  return __builtin_amdgcn_ballot_w64(grow) != 0;
+}
+
+// Keeps the probabilities computed where they are written in the source: an
+// empty asm statement that reads them (it emits no instruction), so the
+// compiler cannot sink their computation past the branch that follows.
+__device__ __forceinline__ void pf_pin(const uint32_t (&pb)[2][2][4], const float (&l_run)[2]) {
+  asm volatile("" ::"v"(l_run[0]), "v"(l_run[1]));
+  asm volatile("" ::"v"(pb[0][0][0]), "v"(pb[0][0][1]), "v"(pb[0][0][2]), "v"(pb[0][0][3]), "v"(pb[0][1][0]),
+               "v"(pb[0][1][1]), "v"(pb[0][1][2]), "v"(pb[0][1][3]), "v"(pb[1][0][0]), "v"(pb[1][0][1]),
+               "v"(pb[1][0][2]), "v"(pb[1][0][3]), "v"(pb[1][1][0]), "v"(pb[1][1][1]), "v"(pb[1][1][2]),
+               "v"(pb[1][1][3]));
+}
+
+template <int DT>
+__device__ __forceinline__ void pf_rescale(f32x16_t (&o)[DT][2], const float (&alpha)[2]) {
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][nt][r] *= alpha[nt];
+}
+
+// O^T += V^T P^T for the keys of half ct.  V^T operands come from transpose
+// reads of the row-major V tile: lane (g16 = lane/16, i16 = lane%16) reads
+// row kb + i16/4 at columns dt*32 + 16*(g16%2) + 4*(i16%4) and receives
+// V[kb + 0..3][its d].
+template <int D>
+__device__ __forceinline__ void pf_pv(f32x16_t (&o)[D / 32][2], const uint32_t (&pb)[2][2][4], const char* vt,
+                                      int ct, int lane) {
+  using SH = PfShape<D>;
+  const int hf = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    bf16x8_t bop[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const u32x4_t bw = {pb[nt][st][0], pb[nt][st][1], pb[nt][st][2], pb[nt][st][3]};
+      bop[nt] = __builtin_bit_cast(bf16x8_t, bw);
+    }
+#pragma unroll
+    for (int dt = 0; dt < SH::DT; ++dt) {
+      i16x4_t half[2];
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int row = ct * 32 + 16 * st + 8 * rr + 4 * hf + (i16 >> 2);
+        const int col = dt * 32 + 16 * (g16 & 1) + 4 * (i16 & 3);
+        const int c = col >> 3;
+        const char* p = vt + row * (SH::CPR * 16) + ((c ^ SH::swz_v(row)) * 16) + (col & 7) * 2;
+        half[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
+      }
+      const u32x2_t h0 = __builtin_bit_cast(u32x2_t, half[0]);
+      const u32x2_t h1 = __builtin_bit_cast(u32x2_t, half[1]);
+      const u32x4_t aw = {h0[0], h0[1], h1[0], h1[1]};
+      const bf16x8_t aop = __builtin_bit_cast(bf16x8_t, aw);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        o[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop[nt], o[dt][nt], 0, 0, 0);
+    }
+  }
+}
+
+// One 64-key tile, software pipelined over its halves so that MFMA work of
+// one half overlaps the softmax of the other:
+//   S(0) | mask(0) | S(1) + softmax(0) | rescale(0), mask(1) | P V(0) + softmax(1) | rescale(1) | P V(1)
+// The masks and rescales are wavefront-uniform branches between the
+// overlapped regions.
+template <int D>
+__device__ __forceinline__ void pf_tile(f32x16_t (&o)[D / 32][2], float (&m_run)[2], float (&l_run)[2],
+                                        const bf16x8_t (&qb)[2][D / 16], const char* kt, const char* vt,
+                                        bool masked, const int32_t* klo, const uint32_t* kspan,
+                                        const int32_t (&iq)[2], float scale_log2, int lane) {
+  constexpr int KSTEPS = D / 16, DT = D / 32;
+  constexpr int kMfmaHalf = 2 * KSTEPS;  // MFMAs per half for S, and 2 * 2 * DT for P V (equal for both)
+  static_assert(2 * 2 * DT == kMfmaHalf, "S and P V halves carry equal MFMA counts");
+  constexpr int kValuPerMfma = 8;
+  f32x16_t s0[2], s1[2];
+  uint32_t p0[2][2][4], p1[2][2][4];
+  float a0[2], a1[2];
+
+  pf_scores<D>(s0, qb, kt, 0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  if (masked) pf_mask(s0, klo, kspan, iq, 0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  pf_scores<D>(s1, qb, kt, 1, lane);
+  const bool g0 = pf_softmax(s0, m_run, l_run, p0, a0, scale_log2);
+#pragma unroll
+  for (int i = 0; i < kMfmaHalf; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerMfma, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  pf_pin(p0, l_run);
+  if (g0) pf_rescale<DT>(o, a0);
+  if (masked) pf_mask(s1, klo, kspan, iq, 1, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  pf_pv<D>(o, p0, vt, 0, lane);
+  const bool g1 = pf_softmax(s1, m_run, l_run, p1, a1, scale_log2);
+#pragma unroll
+  for (int i = 0; i < kMfmaHalf; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerMfma, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  pf_pin(p1, l_run);
+  if (g1) pf_rescale<DT>(o, a1);
+  __builtin_amdgcn_sched_barrier(0);
+  pf_pv<D>(o, p1, vt, 1, lane);
+  // all V operand reads of the last half first, then its MFMAs
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4 * DT, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMfmaHalf, 0);
+}
+
 template <int D>
 __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a, int g, int hpi) {
   using SH = PfShape<D>;
-  constexpr int CPR = SH::CPR, KSTEPS = SH::KSTEPS, DT = SH::DT;
+  constexpr int KSTEPS = SH::KSTEPS, DT = SH::DT;
 
   // [key half][buffer]
   __shared__ __attribute__((aligned(1024))) char k_lds[kPfHalves][2][SH::TILE_BYTES];
@@ -398,123 +595,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
 
     const char* kt = k_lds[kh][buf];
     const char* vt = v_lds[kh][buf];
-    const bool full = s_full[kh][buf] != 0;
-    // The tile is consumed in two halves of 32 keys (ct): scores, softmax and
-    // the P V product of one half before the next, which halves the score and
-    // probability registers.
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      // ---- S^T = K Q^T for keys ct*32 .. ct*32+31: [query tile nt]
-      f32x16_t s[2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[nt][r] = 0.f;
-      const int key = ct * 32 + n;
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int c = 2 * ks + hf;
-        const u32x4_t av = *reinterpret_cast<const u32x4_t*>(kt + key * (CPR * 16) + ((c ^ SH::swz_k(key)) * 16));
-        const bf16x8_t aop = __builtin_bit_cast(bf16x8_t, av);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          s[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qb[nt][ks], s[nt], 0, 0, 0);
-      }
-
-      // ---- mask (unless every row sees every key of the tile); register r
-      // of the lane holds key ct*32 + 8*(r/4) + 4*hf + r%4
-      if (!full) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int key0 = ct * 32 + 8 * r4 + 4 * hf;
-          const int4 lo4 = *reinterpret_cast<const int4*>(&klo_lds[kh][buf][key0]);
-          const uint4 sp4 = *reinterpret_cast<const uint4*>(&kspan_lds[kh][buf][key0]);
-          const int32_t lo[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
-          const uint32_t sp[4] = {sp4.x, sp4.y, sp4.z, sp4.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-              if (!sees(iq[nt], lo[j], sp[j])) s[nt][4 * r4 + j] = -INFINITY;
-        }
-      }
-
-      // ---- online softmax in log2 units; the accumulators are rescaled only
-      // when some lane's running max has grown past the slack (a
-      // wavefront-uniform decision)
-      float mx[2];
-      bool grow = false;
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        float v = s[nt][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) v = fmaxf(v, s[nt][r]);
-        mx[nt] = fmaxf(v, __shfl_xor(v, 32)) * a.scale_log2;
-        grow |= mx[nt] > m_run[nt] + kRescaleSlack;
-      }
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const float m_new = fmaxf(m_run[nt], mx[nt]);
-          const float alpha = fast_exp2(m_run[nt] - ((m_new == -INFINITY) ? 0.f : m_new));
-          m_run[nt] = m_new;
-          l_run[nt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][nt][r] *= alpha;
-        }
-      }
-      // P^T as bf16 pairs: [nt][k-step st][dword]; k-step st covers keys
-      // ct*32 + 16*st .. +15, i.e. registers 8*st .. 8*st+7
-      uint32_t pb[2][2][4];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const float m_use = (m_run[nt] == -INFINITY) ? 0.f : m_run[nt];
-        float psum = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(fmaf(s[nt][r], a.scale_log2, -m_use));
-          const float p1 = fast_exp2(fmaf(s[nt][r + 1], a.scale_log2, -m_use));
-          psum += p0 + p1;
-          pb[nt][r >> 3][(r & 7) >> 1] = pack_bf16(p0, p1);
-        }
-        l_run[nt] += psum;
-      }
-
-      // ---- O^T += V^T P^T; V^T operands by transpose reads of the V tile:
-      // lane (group g16 = lane/16, i16 = lane%16) reads row kb + i16/4 at
-      // columns dt*32 + 16*(g16%2) + 4*(i16%4) and receives V[kb + 0..3][its d].
-      const int g16 = lane >> 4, i16 = lane & 15;
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        bf16x8_t bop[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const u32x4_t bw = {pb[nt][st][0], pb[nt][st][1], pb[nt][st][2], pb[nt][st][3]};
-          bop[nt] = __builtin_bit_cast(bf16x8_t, bw);
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          i16x4_t half[2];
-#pragma unroll
-          for (int rr = 0; rr < 2; ++rr) {
-            const int row = ct * 32 + 16 * st + 8 * rr + 4 * hf + (i16 >> 2);
-            const int col = dt * 32 + 16 * (g16 & 1) + 4 * (i16 & 3);
-            const int c = col >> 3;
-            const char* p = vt + row * (CPR * 16) + ((c ^ SH::swz_v(row)) * 16) + (col & 7) * 2;
-            half[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
-          }
-          const u32x2_t h0 = __builtin_bit_cast(u32x2_t, half[0]);
-          const u32x2_t h1 = __builtin_bit_cast(u32x2_t, half[1]);
-          const u32x4_t aw = {h0[0], h0[1], h1[0], h1[1]};
-          const bf16x8_t aop = __builtin_bit_cast(bf16x8_t, aw);
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-            o[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop[nt], o[dt][nt], 0, 0, 0);
-        }
-      }
-    }
+    pf_tile<D>(o, m_run, l_run, qb, kt, vt, s_full[kh][buf] == 0, klo_lds[kh][buf], kspan_lds[kh][buf], iq,
+               a.scale_log2, lane);
   }
 
   // ---- merge the odd half into the even half through LDS (the tile buffers
