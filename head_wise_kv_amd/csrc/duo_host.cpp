@@ -46,7 +46,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct LayerPlan {
   int n_ret = 0, n_str = 0;
-  size_t off_kr = 0, off_vr = 0, off_ks = 0, off_vs = 0, off_pos = 0, off_cnt1 = 0, off_cnt2 = 0;
+  size_t off_kr = 0, off_vr = 0, off_ks = 0, off_vs = 0, off_pos = 0;
   duo::HeadMap map{};
 };
 
@@ -112,15 +112,13 @@ void make_plan(const duo_config* c, Plan* p) {
     lp.off_ks = off; off = align_up(off + str_bytes);
     lp.off_vs = off; off = align_up(off + str_bytes);
     lp.off_pos = off; off = align_up(off + (size_t)c->B * lp.n_str * cap_str * sizeof(int32_t));
-    lp.off_cnt1 = off; off = align_up(off + (size_t)c->B * c->n_kv * duo::kMaxGroups * sizeof(int32_t));
-    lp.off_cnt2 = off; off = align_up(off + (size_t)c->B * c->n_kv * sizeof(int32_t));
     p->payload += 2 * (ret_bytes + str_bytes);
   }
   p->arena = off;
+  // decode partial records: one per (work item, head) overlap, indexed by
+  // first work item of the head + flat head index + segment
   const size_t rec = decode_rec_floats(c) * sizeof(float);
-  const size_t ws1 = align_up(((size_t)duo::kMaxDecodeBlocks + (size_t)c->B * c->n_kv) * rec);
-  const size_t ws2 = align_up((size_t)c->B * c->n_kv * duo::kMaxGroups * rec);
-  p->workspace = ws1 + ws2;
+  p->workspace = align_up(((size_t)duo::kMaxDecodeBlocks + (size_t)c->B * c->n_kv) * rec);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -144,8 +142,6 @@ struct duo_cache {
     p.k_str = arena + lp.off_ks;
     p.v_str = arena + lp.off_vs;
     p.pos = reinterpret_cast<int32_t*>(arena + lp.off_pos);
-    p.cnt1 = reinterpret_cast<int32_t*>(arena + lp.off_cnt1);
-    p.cnt2 = reinterpret_cast<int32_t*>(arena + lp.off_cnt2);
     return p;
   }
   int64_t cap_str() const { return (int64_t)cfg.sink + cfg.recent; }
@@ -233,11 +229,11 @@ int duo_cache_init(const duo_config* cfg, void* arena, size_t arena_bytes, void*
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int l = 0; l < cfg->L; ++l) {
     const LayerPlan& lp = p.layers[l];
-    // positions and merge tickets start at zero (payload rows need no clearing)
-    hipError_t e = duo::launch_fill_zero(c->arena + lp.off_pos, p.layers[l].off_cnt2 + align_up((size_t)cfg->B * cfg->n_kv * 4) - lp.off_pos, s);
+    // positions start at zero (payload rows need no clearing)
+    hipError_t e = duo::launch_fill_zero(c->arena + lp.off_pos, (size_t)cfg->B * lp.n_str * c->cap_str() * sizeof(int32_t), s);
     if (e != hipSuccess) {
       delete c;
-      return hip_fail(e, "zeroing positions/counters");
+      return hip_fail(e, "zeroing positions");
     }
   }
   *out = c;
@@ -286,18 +282,30 @@ int duo_decode(duo_cache* c, int layer, const void* q, void* out, float scale, v
   a.cap_str = c->cap_str();
   a.rows_ret = T;
   a.rows_str = std::min<int64_t>(T, c->cap_str());
-  // Work items over the flattened row space of all held rows (retrieval
-  // heads first, then streaming heads): as many as run concurrently, i.e.
-  // one workgroup of four wavefronts per SIMD-wave slot of every CU.
-  a.total_rows = (int64_t)cf.B * (lp.n_ret * a.rows_ret + lp.n_str * a.rows_str);
-  const int64_t target = std::max(1, std::min(c->num_cu * duo::decode_blocks_per_cu(), duo::kMaxDecodeBlocks));
-  a.chunk = std::max<int64_t>(1, ceil_div(a.total_rows, target));
-  const int blocks = (int)ceil_div(a.total_rows, a.chunk);
-  const size_t rec = decode_rec_floats(&cf);
+  // Work items: contiguous row ranges of one head, about equal in rows, as
+  // many as one workgroup per compute unit (or one per head if there are
+  // more heads).  Every item holds at least one row.
+  const int g = cf.n_q / cf.n_kv;
+  const int64_t heads_ret = (int64_t)cf.B * lp.n_ret, heads_str = (int64_t)cf.B * lp.n_str;
+  const int64_t total = heads_ret * a.rows_ret + heads_str * a.rows_str;
+  const int64_t slots = std::max<int64_t>(std::min(c->num_cu, duo::kMaxDecodeBlocks), heads_ret + heads_str);
+  int64_t t = std::max<int64_t>(duo::decode_round_rows(cf.dtype, cf.d_head, g), ceil_div(total, slots));
+  // items per head: the head's rows over the target, rounded to nearest
+  int64_t nb_r = 1, nb_s = 1;
+  for (;;) {
+    nb_r = std::max<int64_t>(1, (a.rows_ret + t / 2) / t);
+    nb_s = std::max<int64_t>(1, (a.rows_str + t / 2) / t);
+    if (heads_ret * nb_r + heads_str * nb_s <= slots) break;
+    t += std::max<int64_t>(1, t / 64);
+  }
+  nb_r = ceil_div(a.rows_ret, ceil_div(a.rows_ret, nb_r));  // no empty item
+  nb_s = ceil_div(a.rows_str, ceil_div(a.rows_str, nb_s));
+  a.nb_ret = (int)nb_r;
+  a.nb_str = (int)nb_s;
+  const int blocks = (int)(heads_ret * nb_r + heads_str * nb_s);
   a.ws1 = static_cast<float*>(ws);
-  a.ws2 = a.ws1 + align_up(((size_t)duo::kMaxDecodeBlocks + (size_t)cf.B * cf.n_kv) * rec * sizeof(float)) / sizeof(float);
   a.scale_log2 = scale * 1.4426950408889634f;
-  hipError_t e = duo::launch_decode(a, cf.dtype, cf.d_head, cf.n_q / cf.n_kv, blocks, static_cast<hipStream_t>(stream));
+  hipError_t e = duo::launch_decode(a, cf.dtype, cf.d_head, g, blocks, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
 }

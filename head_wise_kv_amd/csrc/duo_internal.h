@@ -10,10 +10,8 @@
 namespace duo {
 
 constexpr int kMaxKV = 128;        // KV heads per layer the head maps can hold
-constexpr int kSplitGroup = 16;    // decode partials merged by one first-level merge
-constexpr int kMaxGroups = 64;     // first-level groups per head (so <= 1024 splits)
 constexpr int kMaxDecodeBlocks = 1024;  // decode work items per call at most
-constexpr int kDecodeThreads = 256;  // 4 wavefronts of 64
+constexpr int kDecodeThreads = 512;  // 8 wavefronts of 64
 
 // Per-layer head tables: role and compact index of each KV head, and the KV
 // head behind each compact retrieval / streaming index.
@@ -31,8 +29,6 @@ struct LayerPtrs {
   char* k_str;     // [B][n_str][cap_str][d]
   char* v_str;
   int32_t* pos;    // [B][n_str][cap_str]
-  int32_t* cnt1;   // [B*n_kv][kMaxGroups] first-level merge tickets
-  int32_t* cnt2;   // [B*n_kv] second-level merge tickets
 };
 
 struct AppendArgs {
@@ -52,13 +48,11 @@ struct DecodeArgs {
   void* out;       // [B][n_q][d]
   LayerPtrs lp;
   HeadMap map;
-  float* ws1;      // [blocks][rec] per-block partials
-  float* ws2;      // [B*n_kv][kMaxGroups][rec] group partials
+  float* ws1;      // partial records [work item][g][d + 2]
   int B, n_q, n_kv, n_ret, n_str;
   int64_t cap_ret, cap_str;     // rows reserved per head
   int64_t rows_ret, rows_str;   // rows held per head
-  int64_t total_rows;           // B * (n_ret * rows_ret + n_str * rows_str)
-  int64_t chunk;                // rows of the flattened row space per work item
+  int nb_ret, nb_str;           // work items per retrieval / streaming head (each >= 1 row)
   float scale_log2;             // softmax scale * log2(e)
 };
 
@@ -83,8 +77,11 @@ struct PrefillArgs {
 // Launchers (duo_kernels.hip).  dtype: 0 = fp32, 1 = bf16.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, int dtype, int d, hipStream_t s);
+// Split phase over `blocks` work items (retrieval heads' items first), then
+// the combine of heads cut into several items.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int g, int blocks, hipStream_t s);
-int decode_blocks_per_cu();
+// Rows one round of the decode kernel covers (a work item should span at least one).
+int64_t decode_round_rows(int dtype, int d, int g);
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int g, hipStream_t s);
 // Query rows and query heads one prefill work item covers.
 void prefill_plan(int dtype, int d, int g, int* rows_per_item, int* heads_per_item);

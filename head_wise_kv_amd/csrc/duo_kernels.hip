@@ -17,6 +17,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 namespace duo {
 namespace {
 
@@ -118,29 +120,71 @@ __global__ void append_kernel(AppendArgs a) {
   }
 }
 
+// One wavefront-wide direct buffer->LDS load of 16 bytes per lane: lane i
+// writes LDS bytes [lds + 16 i, lds + 16 i + 16) from byte offset voff of the
+// buffer resource; offsets out of the resource's range read as zero.
+//
+// Written as inline assembly on purpose: the load has no register result
+// (its data goes to LDS), and the compiler, not knowing that it writes LDS,
+// adds no wait of its own before later LDS reads.  Every read of a unit is
+// ordered after its loads by an explicit vmcnt wait and a barrier (see
+// wait_vmcnt / lds_barrier), which keeps three units in flight; the compiler's
+// own analysis would wait for all of them.  The "memory" clobber stops the
+// compiler from assuming LDS contents across the load.  M0 (the LDS base of
+// the load) is saved and restored.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4_t dec_rsrc(const char* base, int nbytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return i32x4_t{(int)__builtin_amdgcn_readfirstlane((uint32_t)b),
+                 (int)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu),  // stride 0
+                 __builtin_amdgcn_readfirstlane(nbytes), 0x00020000};                 // raw buffer
+}
+
+__device__ __forceinline__ void dec_dma(i32x4_t rsrc, char* lds, uint32_t voff) {
+  const uint32_t m0v =
+      __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) char*)lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0v), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+
 // ------------------------------------------------------------------ decode
 //
-// Lane layout: 8 lanes share a K/V row.  Lane l has row group rg = l / 8 and
-// slice s = l % 8; it holds the 16-byte chunks s, s+8, ... of its rows, so one
-// wavefront load instruction reads 8 rows x 128 contiguous bytes.  The g query
-// vectors of the KV head live in the same slice layout in registers for the
-// whole work item.  Scores: packed bf16 dot products over the lane's slice,
-// then an all-reduce over the 8 lanes of the row with DPP adds.  Softmax
-// statistics are kept per lane (each lane group sees its own rows); P.V uses
-// bf16 dot products over pairs of rows.  Row groups and wavefronts are merged
-// once at the end of a work item.
+// One workgroup of 8 wavefronts per compute unit walks a contiguous range of
+// the flattened row space.  K and V rows reach LDS through direct buffer->LDS
+// loads into a ring of four 32 KB units (the K rows, then the V rows, of one
+// round of tiles); three units are in flight while one is consumed, so the
+// prefetch depth costs no registers.  A round is SLOTS tiles of TR rows; the
+// wavefronts of a slot split the g query heads (HW heads each) and read the
+// slot's tile from LDS, so no row is fetched twice.  Rounds never straddle two
+// heads: a range that covers parts of several heads is a sequence of
+// segments, and at the end of each segment the wavefronts' softmax states are
+// merged into one partial (max, sum, acc) per query head.  A segment that is a
+// whole head writes the output; otherwise its partial goes to the workspace
+// and the combine kernel merges the partials of the head.
+//
+// Lane layout within a tile: 8 lanes share a row.  Lane l has row group
+// rg = l / 8 and slice s = l % 8; it holds the 16-byte chunks s, s+8, ... of
+// rows rg, rg+8, ...  Rows are XOR-swizzled in LDS (odd rows swap the two
+// halves of every 256 bytes) so the 8-row reads are free of bank conflicts.
+// Scores: packed bf16 dot products over the lane's slice, then an all-reduce
+// over the 8 lanes of the row with DPP adds.  P.V: bf16 dot products over
+// pairs of rows.
 
-// Tuning knobs (compile time): query heads per wavefront, prefetch depth in
-// tiles, and wavefronts per SIMD the kernel is built for.
-#ifndef DUO_DECODE_HW_MAX
-#define DUO_DECODE_HW_MAX 4
-#endif
-#ifndef DUO_DECODE_STAGES
-#define DUO_DECODE_STAGES 1
-#endif
-#ifndef DUO_DECODE_WAVES_PER_EU
-#define DUO_DECODE_WAVES_PER_EU 2
-#endif
+constexpr int kDecWaves = kDecodeThreads / 64;              // 8
+constexpr int kUnitBytes = 32768;                           // K (or V) rows of one round
+constexpr int kRingUnits = 4;                               // 128 KB of LDS
+constexpr int kUnitPieces = kUnitBytes / 1024;              // wavefront-wide 16-byte loads per unit
+constexpr int kPiecesPerWave = kUnitPieces / kDecWaves;     // 4
+static_assert(kUnitPieces % kDecWaves == 0, "unit pieces split evenly over the wavefronts");
 
 template <bool BF16, int D, int G>
 struct DecodeCfg {
@@ -149,20 +193,26 @@ struct DecodeCfg {
   static constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
   static constexpr int CPL = CPR / 8;            // chunks per lane
   static constexpr int EPC = 16 / ES;            // elements per chunk
-  static constexpr int HW = G < DUO_DECODE_HW_MAX ? G : DUO_DECODE_HW_MAX;  // query heads per wavefront
-  static constexpr int HSPLIT = G / HW;          // wavefronts sharing one tile stream
-  static constexpr int NW = kDecodeThreads / 64;
-  static constexpr int NSTREAM = NW / HSPLIT;    // independent tile streams per workgroup
-  static constexpr int RPL_RAW = 8 / CPL;
-  static constexpr int RPL = RPL_RAW < 2 ? 2 : RPL_RAW;  // rows per lane per tile (2*RPL*CPL loads)
-  static constexpr int STAGES = DUO_DECODE_STAGES;       // tiles in the prefetch ring
-  static constexpr int TR = 8 * RPL;             // rows per wavefront tile
+  static constexpr int HW = G < 4 ? G : 4;       // query heads per wavefront
+  static constexpr int HSPLIT = G / HW;          // wavefronts per slot
+  static constexpr int SLOTS_W = kDecWaves / HSPLIT;
+  static constexpr int SLOTS_B = kUnitBytes / (16 * ROWB);  // keeps TR >= 16
+  static constexpr int SLOTS = SLOTS_W < SLOTS_B ? SLOTS_W : SLOTS_B;
+  static constexpr int TR = kUnitBytes / (SLOTS * ROWB);    // rows per tile
+  static constexpr int RPL = TR / 8;             // rows per lane
+  static constexpr int SLOT_BYTES = TR * ROWB;
+  static constexpr int ROUND_ROWS = SLOTS * TR;
   static constexpr int NACC = CPL * EPC;         // output elements per lane per head
+  static constexpr int REC = G * (D + 2);        // floats per partial record
   static_assert(CPR % 8 == 0, "rows must span a multiple of 8 chunks");
-  static_assert(RPL % 2 == 0, "rows are paired for the weighted sum");
-  static_assert(G % HW == 0 && NW % HSPLIT == 0, "head split must tile the workgroup");
-  static_assert(STAGES >= 1 && STAGES <= 4, "prefetch ring of 1..4 tiles");
+  static_assert(RPL >= 2 && RPL % 2 == 0, "rows are paired for the weighted sum");
+  static_assert(SLOT_BYTES % 1024 == 0, "a load piece stays within one tile");
+  static_assert(G % HW == 0, "head split must tile the group");
 };
+
+// Chunk slot of chunk c of row r in LDS.
+template <int CPR>
+__device__ __forceinline__ int dec_swz(int r) { return CPR >= 16 ? 8 * (r & 1) : 0; }
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -176,131 +226,107 @@ __device__ __forceinline__ float row8_sum(float x) {
   return x;
 }
 
+// Combine each lane's value with those of lanes l ^ 8, l ^ 16 and l ^ 32 (the
+// 8 row groups holding the same slice), on the vector ALU: DPP row_ror:8 is
+// l ^ 8 within a row of 16 lanes, and the lane-swap instructions exchange
+// rows (16 lanes) and halves (32 lanes) between two registers, so the sum
+// (or max) of the two results is the value combined with its partner lane.
+__device__ __forceinline__ float swap16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float rowgroups_sum(float x) {
+  x += dpp<0x128>(x);  // row_ror:8
+  return swap32_sum(swap16_sum(x));
+}
+__device__ __forceinline__ float rowgroups_max(float x) {
+  x = fmaxf(x, dpp<0x128>(x));
+  return swap32_max(swap16_max(x));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
   bf2 v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Partial records pass between workgroups (possibly on different XCDs, each
-// with its own L2) as agent-scope relaxed atomic stores and loads.  These are
-// write-through / coherent accesses (the `sc1` cache policy), so no L2
-// write-back or invalidate is needed.  A writer waits until its stores are
-// acknowledged (vmcnt(0)) before taking its merge ticket; the merging
-// workgroup reads the records only after the last ticket, with coherent loads.
-// This replaces agent-scope release/acquire fences, whose full-L2
-// write-back/invalidate per workgroup costs far more than the merge itself.
-__device__ __forceinline__ void rec_store(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-__device__ __forceinline__ float rec_load(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wait_stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Elements of the g x d output a thread of the workgroup owns in the merge
-// steps: consecutive ones, all in the same head.
-template <int D, int G>
-struct MergeShape {
-  static constexpr int OPT = (G * D) >= kDecodeThreads ? (G * D) / kDecodeThreads : 1;
-  static_assert(D % OPT == 0, "a thread's elements must stay in one head");
+// Workgroup barrier that waits only for this wavefront's LDS operations:
+// direct buffer->LDS loads stay in flight across it (their completion is
+// waited for explicitly with wait_vmcnt before the barrier that publishes
+// them).  __syncthreads would wait for every outstanding vector-memory load,
+// draining the prefetch ring at each step.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// A work item is a contiguous row range of one head.  Heads are numbered
+// retrieval first ((b, r) -> b * n_ret + r), then streaming; each retrieval
+// head is cut into nb_ret items and each streaming head into nb_str.
+struct DecodeItem {
+  int64_t hh;       // head number
+  int64_t r0, r1;   // rows of the head
+  int part, nparts;
+  int b, kvh;
+  const char* kbase;
+  const char* vbase;
 };
 
-// Merge `n` partial records (acc[G][D], m[G], l[G]; m in log2 units) into
-// either the final output or one record at `dst_rec`.  Records are taken in
-// batches of kSplitGroup; every load of a batch is issued before any is used,
-// so a batch costs one memory round trip (a merge is normally one batch).
-template <bool BF16, int D, int G>
-__device__ void merge_records(const float* src, int n, float* dst_rec, void* out, size_t out_off) {
-  constexpr int REC = G * (D + 2);
-  constexpr int NB = kSplitGroup;
-  constexpr int OPT = MergeShape<D, G>::OPT;
-  const int e0 = threadIdx.x * OPT;
-  if (e0 >= G * D) return;
-  const int h = e0 / D;
-  float M = -INFINITY, L = 0.f, A[OPT];
-#pragma unroll
-  for (int o = 0; o < OPT; ++o) A[o] = 0.f;
-  for (int i0 = 0; i0 < n; i0 += NB) {
-    float mv[NB], lv[NB], av[NB][OPT];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int i = min(i0 + j, n - 1);  // in range; entries past n are weighted out below
-      const float* r = src + (size_t)i * REC;
-      mv[j] = rec_load(r + G * D + h);
-      lv[j] = rec_load(r + G * D + G + h);
-#pragma unroll
-      for (int o = 0; o < OPT; ++o) av[j][o] = rec_load(r + e0 + o);
-    }
-    float Mb = M;
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-      if (i0 + j < n) Mb = fmaxf(Mb, mv[j]);
-    const float f = (M == -INFINITY) ? 0.f : fast_exp2(M - Mb);
-    L *= f;
-#pragma unroll
-    for (int o = 0; o < OPT; ++o) A[o] *= f;
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      if (i0 + j < n) {
-        const float w = (mv[j] == -INFINITY) ? 0.f : fast_exp2(mv[j] - Mb);
-        L += lv[j] * w;
-#pragma unroll
-        for (int o = 0; o < OPT; ++o) A[o] += av[j][o] * w;
-      }
-    }
-    M = Mb;
-  }
-  if (dst_rec) {
-#pragma unroll
-    for (int o = 0; o < OPT; ++o) rec_store(dst_rec + e0 + o, A[o]);
-    if (e0 % D == 0) {
-      rec_store(dst_rec + G * D + h, M);
-      rec_store(dst_rec + G * D + G + h, L);
-    }
+template <int ROWB>
+__device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a, int64_t blk) {
+  DecodeItem w;
+  const int64_t n_ret_items = (int64_t)a.B * a.n_ret * a.nb_ret;
+  int64_t rows;
+  if (blk < n_ret_items) {
+    w.hh = blk / a.nb_ret;
+    w.part = (int)(blk % a.nb_ret);
+    w.nparts = a.nb_ret;
+    rows = a.rows_ret;
+    w.b = (int)(w.hh / a.n_ret);
+    const int r = (int)(w.hh % a.n_ret);
+    w.kvh = a.map.orig_ret[r];
+    const size_t off = ((size_t)w.b * a.n_ret + r) * a.cap_ret * ROWB;
+    w.kbase = a.lp.k_ret + off;
+    w.vbase = a.lp.v_ret + off;
   } else {
-    const float inv = 1.f / L;
-#pragma unroll
-    for (int o = 0; o < OPT; ++o) {
-      if (BF16) {
-        reinterpret_cast<uint16_t*>(out)[out_off + e0 + o] = (uint16_t)f32_to_bf16_bits(A[o] * inv);
-      } else {
-        reinterpret_cast<float*>(out)[out_off + e0 + o] = A[o] * inv;
-      }
-    }
+    const int64_t x = (blk - n_ret_items) / a.nb_str;
+    w.hh = (int64_t)a.B * a.n_ret + x;
+    w.part = (int)((blk - n_ret_items) % a.nb_str);
+    w.nparts = a.nb_str;
+    rows = a.rows_str;
+    w.b = (int)(x / a.n_str);
+    const int si = (int)(x % a.n_str);
+    w.kvh = a.map.orig_str[si];
+    const size_t off = ((size_t)w.b * a.n_str + si) * a.cap_str * ROWB;
+    w.kbase = a.lp.k_str + off;
+    w.vbase = a.lp.v_str + off;
   }
-}
-
-template <bool BF16, int D, int G>
-struct DecodeTile {
-  using C = DecodeCfg<BF16, D, G>;
-  uint4 k[C::RPL][C::CPL];
-  uint4 v[C::RPL][C::CPL];
-};
-
-// Rows tb + rg + 8*j, chunks s + 8*cc.  Rows at or past `last` are clamped to
-// `last` (a held row), so the load is always issued and always in bounds;
-// process_tile masks those rows out.  Keeping the loads unconditional lets
-// the compiler count outstanding loads exactly across the prefetch ring.
-// Offsets within one head fit 32 bits (T_cap * row bytes < 2^32 is checked
-// by the host), so the loads use a uniform base plus a 32-bit lane offset.
-template <bool BF16, int D, int G>
-__device__ __forceinline__ void load_tile(DecodeTile<BF16, D, G>& t, const char* kb, const char* vb, int64_t tb,
-                                          int64_t last, int rg, int s) {
-  using C = DecodeCfg<BF16, D, G>;
-#pragma unroll
-  for (int j = 0; j < C::RPL; ++j) {
-    const uint32_t row = (uint32_t)min(tb + rg + 8 * j, last);
-#pragma unroll
-    for (int cc = 0; cc < C::CPL; ++cc) {
-      const uint32_t o = row * (uint32_t)C::ROWB + (uint32_t)(s + 8 * cc) * 16u;
-      t.k[j][cc] = ld16(kb + o);
-      t.v[j][cc] = ld16(vb + o);
-    }
-  }
-  // Keep the requests where they are issued: the scheduler would otherwise
-  // sink them next to their use and shorten the prefetch distance.
-  __builtin_amdgcn_sched_barrier(0);
+  const int64_t per = (rows + w.nparts - 1) / w.nparts;
+  w.r0 = w.part * per;
+  w.r1 = w.r0 + per < rows ? w.r0 + per : rows;
+  return w;
 }
 
 // Per-lane softmax state.  m is a reference maximum (log2 units); l and acc
@@ -316,36 +342,44 @@ struct DecodeState {
   float acc[C::HW][C::NACC];
 };
 
+// Scores of the lane's rows against its HW queries, online-softmax update,
+// and the probabilities p[j][h] for the weighted sum.  `kt` is the tile in
+// LDS, `nv` its valid rows.
 template <bool BF16, int D, int G>
-__device__ __forceinline__ void process_tile(DecodeState<BF16, D, G>& st, const DecodeTile<BF16, D, G>& t,
-                                             const uint4 (&q)[DecodeCfg<BF16, D, G>::HW][DecodeCfg<BF16, D, G>::CPL],
-                                             int64_t nv, int rg, float scale_log2) {
+__device__ __forceinline__ void tile_scores(DecodeState<BF16, D, G>& st, float (&p)[DecodeCfg<BF16, D, G>::RPL][DecodeCfg<BF16, D, G>::HW],
+                                            const char* kt, const uint4 (&q)[DecodeCfg<BF16, D, G>::HW][DecodeCfg<BF16, D, G>::CPL],
+                                            int nv, int rg, int s, float scale_log2) {
   using C = DecodeCfg<BF16, D, G>;
   constexpr int HW = C::HW;
   float sc[C::RPL][HW];
-  // ---- partial scores over the lane's slice, then the 8-lane all-reduce
 #pragma unroll
-  for (int j = 0; j < C::RPL; ++j)
+  for (int j = 0; j < C::RPL; ++j) {
+    const int row = rg + 8 * j;
+    uint4 k[C::CPL];
+#pragma unroll
+    for (int cc = 0; cc < C::CPL; ++cc)
+      k[cc] = *reinterpret_cast<const uint4*>(kt + row * C::ROWB + (((s + 8 * cc) ^ dec_swz<C::CPR>(row)) * 16));
 #pragma unroll
     for (int h = 0; h < HW; ++h) {
-      float a = 0.f;
+      float acc = 0.f;
 #pragma unroll
       for (int cc = 0; cc < C::CPL; ++cc) {
         if constexpr (BF16) {
-          a = dot2_bf16(q[h][cc].x, t.k[j][cc].x, a);
-          a = dot2_bf16(q[h][cc].y, t.k[j][cc].y, a);
-          a = dot2_bf16(q[h][cc].z, t.k[j][cc].z, a);
-          a = dot2_bf16(q[h][cc].w, t.k[j][cc].w, a);
+          acc = dot2_bf16(q[h][cc].x, k[cc].x, acc);
+          acc = dot2_bf16(q[h][cc].y, k[cc].y, acc);
+          acc = dot2_bf16(q[h][cc].z, k[cc].z, acc);
+          acc = dot2_bf16(q[h][cc].w, k[cc].w, acc);
         } else {
-          a = fmaf(__uint_as_float(q[h][cc].x), __uint_as_float(t.k[j][cc].x), a);
-          a = fmaf(__uint_as_float(q[h][cc].y), __uint_as_float(t.k[j][cc].y), a);
-          a = fmaf(__uint_as_float(q[h][cc].z), __uint_as_float(t.k[j][cc].z), a);
-          a = fmaf(__uint_as_float(q[h][cc].w), __uint_as_float(t.k[j][cc].w), a);
+          acc = fmaf(__uint_as_float(q[h][cc].x), __uint_as_float(k[cc].x), acc);
+          acc = fmaf(__uint_as_float(q[h][cc].y), __uint_as_float(k[cc].y), acc);
+          acc = fmaf(__uint_as_float(q[h][cc].z), __uint_as_float(k[cc].z), acc);
+          acc = fmaf(__uint_as_float(q[h][cc].w), __uint_as_float(k[cc].w), acc);
         }
       }
-      sc[j][h] = row8_sum(a);
+      sc[j][h] = row8_sum(acc);
     }
-  // ---- rows past the end (only in a segment's last tile) score -inf
+  }
+  // rows past the segment's end (only in its last tiles) score -inf
   if (nv < C::TR) {
 #pragma unroll
     for (int j = 0; j < C::RPL; ++j) {
@@ -354,8 +388,7 @@ __device__ __forceinline__ void process_tile(DecodeState<BF16, D, G>& st, const 
       for (int h = 0; h < HW; ++h) sc[j][h] = ok ? sc[j][h] : -INFINITY;
     }
   }
-  // ---- online softmax in log2 units (scale > 0, so max commutes with it)
-  float p[C::RPL][HW];
+  // online softmax in log2 units (scale > 0, so max commutes with it)
   float mt[HW];
   bool need = false;
 #pragma unroll
@@ -366,7 +399,7 @@ __device__ __forceinline__ void process_tile(DecodeState<BF16, D, G>& st, const 
     mt[h] = x * scale_log2;
     need |= mt[h] > st.m[h] + kRescaleSlack;
   }
-  if (__builtin_amdgcn_read_exec() & __ballot(need)) {  // any lane: raise the reference
+  if (__builtin_amdgcn_ballot_w64(need) != 0) {  // some lane raises its reference
 #pragma unroll
     for (int h = 0; h < HW; ++h) {
       const float mn = fmaxf(st.m[h], mt[h]);
@@ -388,20 +421,31 @@ __device__ __forceinline__ void process_tile(DecodeState<BF16, D, G>& st, const 
     }
     st.l[h] += ps;
   }
-  // ---- weighted sum of V rows
+}
+
+// acc += sum over the lane's rows of p[j][h] * V[row]; `vt` is the V tile in LDS.
+template <bool BF16, int D, int G>
+__device__ __forceinline__ void tile_pv(DecodeState<BF16, D, G>& st, const float (&p)[DecodeCfg<BF16, D, G>::RPL][DecodeCfg<BF16, D, G>::HW],
+                                        const char* vt, int rg, int s) {
+  using C = DecodeCfg<BF16, D, G>;
+  constexpr int HW = C::HW;
   if constexpr (BF16) {
 #pragma unroll
     for (int jp = 0; jp < C::RPL; jp += 2) {
+      const int row0 = rg + 8 * jp, row1 = row0 + 8;  // same parity: same swizzle
       uint32_t P[HW];
 #pragma unroll
       for (int h = 0; h < HW; ++h) P[h] = pack_bf16x2(p[jp][h], p[jp + 1][h]);
 #pragma unroll
       for (int cc = 0; cc < C::CPL; ++cc) {
-        const uint32_t a4[4] = {t.v[jp][cc].x, t.v[jp][cc].y, t.v[jp][cc].z, t.v[jp][cc].w};
-        const uint32_t b4[4] = {t.v[jp + 1][cc].x, t.v[jp + 1][cc].y, t.v[jp + 1][cc].z, t.v[jp + 1][cc].w};
+        const int off = ((s + 8 * cc) ^ dec_swz<C::CPR>(row0)) * 16;
+        const uint4 va = *reinterpret_cast<const uint4*>(vt + row0 * C::ROWB + off);
+        const uint4 vb = *reinterpret_cast<const uint4*>(vt + row1 * C::ROWB + off);
+        const uint32_t a4[4] = {va.x, va.y, va.z, va.w};
+        const uint32_t b4[4] = {vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t lo = __builtin_amdgcn_perm(b4[i], a4[i], 0x05040100u);  // (row jp, row jp+1) at d = 2i
+          const uint32_t lo = __builtin_amdgcn_perm(b4[i], a4[i], 0x05040100u);  // (row0, row1) at d = 2i
           const uint32_t hi = __builtin_amdgcn_perm(b4[i], a4[i], 0x07060302u);  // at d = 2i+1
 #pragma unroll
           for (int h = 0; h < HW; ++h) {
@@ -413,255 +457,309 @@ __device__ __forceinline__ void process_tile(DecodeState<BF16, D, G>& st, const 
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < C::RPL; ++j)
+    for (int j = 0; j < C::RPL; ++j) {
+      const int row = rg + 8 * j;
 #pragma unroll
       for (int cc = 0; cc < C::CPL; ++cc) {
-        const float v4[4] = {__uint_as_float(t.v[j][cc].x), __uint_as_float(t.v[j][cc].y),
-                             __uint_as_float(t.v[j][cc].z), __uint_as_float(t.v[j][cc].w)};
+        const uint4 vv = *reinterpret_cast<const uint4*>(vt + row * C::ROWB + (((s + 8 * cc) ^ dec_swz<C::CPR>(row)) * 16));
+        const float v4[4] = {__uint_as_float(vv.x), __uint_as_float(vv.y), __uint_as_float(vv.z), __uint_as_float(vv.w)};
 #pragma unroll
         for (int h = 0; h < HW; ++h)
 #pragma unroll
           for (int e = 0; e < 4; ++e) st.acc[h][cc * 4 + e] = fmaf(p[j][h], v4[e], st.acc[h][cc * 4 + e]);
       }
+    }
   }
 }
 
-// The flattened row space: retrieval heads (b, r) first, each `rows_ret`
-// rows, then streaming heads (b, s), each `rows_str` rows.  Work item i covers
-// rows [i*chunk, (i+1)*chunk) of it, which may span several heads; each
-// (item, head) overlap is one segment with its own partial result.
-template <bool BF16, int D, int G>
-__global__ __launch_bounds__(kDecodeThreads)
-__attribute__((amdgpu_waves_per_eu(DUO_DECODE_WAVES_PER_EU, DUO_DECODE_WAVES_PER_EU)))
-void decode_kernel(DecodeArgs a) {
-  using C = DecodeCfg<BF16, D, G>;
-  constexpr int REC = G * (D + 2);
-  constexpr int HW = C::HW, NS = C::NSTREAM;
+template <int X>
+using UnitTag = std::integral_constant<int, X>;
 
-  __shared__ float w_acc[NS][G * D];
-  __shared__ float w_m[NS][G], w_l[NS][G];
-  __shared__ int s_ticket;
+template <bool BF16, int D, int G>
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
+  using C = DecodeCfg<BF16, D, G>;
+  constexpr int HW = C::HW, SLOTS = C::SLOTS, TR = C::TR;
+
+  // The four ring units are separate arrays so that the compiler can tell a
+  // unit being read from the units the direct loads are filling (it would
+  // otherwise wait for every load in flight before each LDS read).
+  __shared__ __attribute__((aligned(1024))) char ring0[kUnitBytes];
+  __shared__ __attribute__((aligned(1024))) char ring1[kUnitBytes];
+  __shared__ __attribute__((aligned(1024))) char ring2[kUnitBytes];
+  __shared__ __attribute__((aligned(1024))) char ring3[kUnitBytes];
+  __shared__ float w_acc[SLOTS][G * D];
+  __shared__ float w_m[SLOTS][G], w_l[SLOTS][G];
+  char* const rings[kRingUnits] = {ring0, ring1, ring2, ring3};
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int hg = wave % C::HSPLIT;       // which HW query heads of the group this wavefront scores
-  const int stream = wave / C::HSPLIT;   // which tile stream it walks
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slot = wave / C::HSPLIT;   // tile of the round this wavefront reads
+  const int hg = wave % C::HSPLIT;     // which HW query heads of the group it scores
+  const bool active = slot < SLOTS;
   const int rg = lane >> 3, s = lane & 7;
-  const int64_t blk = blockIdx.x;
-  const int64_t b0 = blk * a.chunk;
-  const int64_t b1 = b0 + a.chunk < a.total_rows ? b0 + a.chunk : a.total_rows;
-  const int64_t r_ret = (int64_t)a.B * a.n_ret * a.rows_ret;  // rows of all retrieval heads
+  const DecodeItem w = decode_item<C::ROWB>(a, blockIdx.x);
+  const int64_t nrounds = ((w.r1 - w.r0 + TR - 1) / TR + SLOTS - 1) / SLOTS;
+  const size_t q_off = ((size_t)w.b * a.n_q + (size_t)w.kvh * G) * D;  // first query of the group
 
-  for (int64_t pos = b0; pos < b1;) {
-    // ---- which head, and which of its rows
-    int64_t hh, h0, hrows;
-    const char *kbase, *vbase;
-    int b, kvh;
-    if (pos < r_ret) {
-      hh = pos / a.rows_ret;
-      h0 = hh * a.rows_ret;
-      hrows = a.rows_ret;
-      b = (int)(hh / a.n_ret);
-      const int r = (int)(hh % a.n_ret);
-      kvh = a.map.orig_ret[r];
-      const size_t off = ((size_t)b * a.n_ret + r) * a.cap_ret * C::ROWB;
-      kbase = a.lp.k_ret + off;
-      vbase = a.lp.v_ret + off;
+  // this wavefront's HW queries, in the lane's slice layout; loaded (and
+  // waited for) before any direct load is in flight
+  uint4 q[HW][C::CPL];
+  {
+    const char* qb = static_cast<const char*>(a.q) + (q_off + (size_t)hg * HW * D) * C::ES;
+#pragma unroll
+    for (int h = 0; h < HW; ++h)
+#pragma unroll
+      for (int c2 = 0; c2 < C::CPL; ++c2) q[h][c2] = ld16(qb + (size_t)h * C::ROWB + (s + 8 * c2) * 16);
+  }
+  // per-lane byte offsets (within a tile) of this wavefront's load pieces, and
+  // the tile (slot) each piece belongs to
+  uint32_t poff[kPiecesPerWave];
+  int pslot[kPiecesPerWave];
+#pragma unroll
+  for (int j = 0; j < kPiecesPerWave; ++j) {
+    const int n = wave + kDecWaves * j;
+    const int off = n * 1024 + lane * 16;
+    pslot[j] = (n * 1024) / C::SLOT_BYTES;
+    const int o = off % C::SLOT_BYTES;
+    const int r = o / C::ROWB;
+    const int c = ((o % C::ROWB) / 16) ^ dec_swz<C::CPR>(r);
+    poff[j] = (uint32_t)(r * C::ROWB + c * 16);
+  }
+  // Rows past the item's end read as zero; clearing the ring once means no
+  // stale bit pattern (possibly a NaN) ever meets a zero probability.
+#pragma unroll
+  for (int x = 0; x < kRingUnits; ++x)
+    for (int off = threadIdx.x * 16; off < kUnitBytes; off += kDecodeThreads * 16)
+      *reinterpret_cast<uint4*>(rings[x] + off) = make_uint4(0, 0, 0, 0);
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // Issue unit `uu` (round uu / 2; K rows if uu is even, else V rows) into
+  // `dst`.  Past the last round every piece is out of range (nothing is read)
+  // but still issued, so each wavefront has the same number of loads per unit.
+  auto issue = [&](int64_t uu, char* dst) {
+    const int64_t rnd = uu >> 1;
+    const char* src = (uu & 1) ? w.vbase : w.kbase;
+#pragma unroll
+    for (int j = 0; j < kPiecesPerWave; ++j) {
+      const int64_t row0 = w.r0 + (rnd * SLOTS + pslot[j]) * (int64_t)TR;
+      const int64_t left = w.r1 - row0;
+      const int rows = rnd < nrounds ? (int)(left < 0 ? 0 : (left > TR ? TR : left)) : 0;
+      dec_dma(dec_rsrc(src + (size_t)(rows > 0 ? row0 : 0) * C::ROWB, rows * C::ROWB),
+              dst + (wave + kDecWaves * j) * 1024, poff[j]);
+    }
+  };
+  issue(0, ring0);
+  issue(1, ring1);
+  issue(2, ring2);
+
+  DecodeState<BF16, D, G> st;
+#pragma unroll
+  for (int h = 0; h < HW; ++h) {
+    st.m[h] = -INFINITY;
+    st.l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < C::NACC; ++e) st.acc[h][e] = 0.f;
+  }
+  float p[C::RPL][HW];
+
+  // Unit u of the stream, held in ring unit X = u % 4 (K rows when X is even).
+  auto unit = [&](auto tag, int64_t u) {
+    constexpr int X = decltype(tag)::value;
+    constexpr bool V_PART = (X & 1) != 0;
+    wait_vmcnt<2 * kPiecesPerWave>();  // unit u has landed; u+1, u+2 may be in flight
+    lds_barrier();                     // ... for every wavefront; unit u-1 is consumed
+    issue(u + 3, rings[(X + 3) % kRingUnits]);
+    const int64_t row0 = w.r0 + ((u >> 1) * SLOTS + slot) * (int64_t)TR;
+    const int64_t left = w.r1 - row0;
+    const int nv = active ? (int)(left < 0 ? 0 : (left > TR ? TR : left)) : 0;
+    const char* tile = rings[X] + slot * C::SLOT_BYTES;
+    if (V_PART) {
+      if (nv > 0) tile_pv<BF16, D, G>(st, p, tile, rg, s);
     } else {
-      const int64_t x = (pos - r_ret) / a.rows_str;
-      hh = (int64_t)a.B * a.n_ret + x;
-      h0 = r_ret + x * a.rows_str;
-      hrows = a.rows_str;
-      b = (int)(x / a.n_str);
-      const int sidx = (int)(x % a.n_str);
-      kvh = a.map.orig_str[sidx];
-      const size_t off = ((size_t)b * a.n_str + sidx) * a.cap_str * C::ROWB;
-      kbase = a.lp.k_str + off;
-      vbase = a.lp.v_str + off;
+      if (nv > 0) tile_scores<BF16, D, G>(st, p, tile, q, nv, rg, s, a.scale_log2);
     }
-    const int64_t seg_end = b1 < h0 + hrows ? b1 : h0 + hrows;
-    const int64_t r0 = pos - h0, r1 = seg_end - h0;   // rows of this head in this segment
-    pos = seg_end;
-    const int fh = b * a.n_kv + kvh;
-    const size_t q_off = ((size_t)b * a.n_q + (size_t)kvh * G) * D;
+  };
+  const int64_t n_units = 2 * nrounds;
+  for (int64_t u = 0; u < n_units; u += 4) {  // n_units is even
+    unit(UnitTag<0>{}, u);
+    unit(UnitTag<1>{}, u + 1);
+    if (u + 2 >= n_units) break;
+    unit(UnitTag<2>{}, u + 2);
+    unit(UnitTag<3>{}, u + 3);
+  }
 
-    // ---- this wavefront's HW queries, in the lane's slice layout
-    uint4 q[HW][C::CPL];
-    {
-      const char* qb = static_cast<const char*>(a.q) + (q_off + (size_t)hg * HW * D) * C::ES;
-#pragma unroll
-      for (int h = 0; h < HW; ++h)
-#pragma unroll
-        for (int cc = 0; cc < C::CPL; ++cc) q[h][cc] = ld16(qb + (size_t)h * C::ROWB + (s + 8 * cc) * 16);
-    }
+  // the loads issued past the last unit (out of range, nothing read) land
+  // before the workgroup can leave
+  wait_vmcnt<0>();
 
-    DecodeState<BF16, D, G> st;
+  // ---- merge the 8 row groups of each wavefront (lanes xor 8, 16, 32), then
+  // the slots through LDS
+  if (active) {
 #pragma unroll
     for (int h = 0; h < HW; ++h) {
-      st.m[h] = -INFINITY;
-      st.l[h] = 0.f;
-#pragma unroll
-      for (int e = 0; e < C::NACC; ++e) st.acc[h][e] = 0.f;
-    }
-
-    // ---- tiles r0 + (stream + NS*i) * TR through a ring of STAGES register
-    // tiles: tile i+STAGES-1 is requested before tile i is processed.
-    const int64_t step = (int64_t)NS * C::TR;
-    const int64_t t0 = r0 + (int64_t)stream * C::TR;
-    const int64_t ntiles = t0 < r1 ? (r1 - t0 + step - 1) / step : 0;
-    const int64_t last = r1 - 1;
-    DecodeTile<BF16, D, G> T[C::STAGES];
-    if (ntiles > 0) {
-#pragma unroll
-      for (int k = 0; k + 1 < C::STAGES; ++k) load_tile<BF16, D, G>(T[k], kbase, vbase, t0 + k * step, last, rg, s);
-      for (int64_t i = 0; i < ntiles; i += C::STAGES) {
-#pragma unroll
-        for (int k = 0; k < C::STAGES; ++k) {
-          if (i + k < ntiles) {
-            const int64_t ti = t0 + (i + k) * step;
-            load_tile<BF16, D, G>(T[(k + C::STAGES - 1) % C::STAGES], kbase, vbase, ti + (C::STAGES - 1) * step, last,
-                                  rg, s);
-            process_tile<BF16, D, G>(st, T[k], q, r1 - ti, rg, a.scale_log2);
-          }
-        }
-      }
-    }
-
-    // ---- merge the 8 row groups of the wavefront (lanes xor 8, 16, 32)
-#pragma unroll
-    for (int h = 0; h < HW; ++h) {
-      float M = st.m[h];
-      M = fmaxf(M, __shfl_xor(M, 8));
-      M = fmaxf(M, __shfl_xor(M, 16));
-      M = fmaxf(M, __shfl_xor(M, 32));
+      const float M = rowgroups_max(st.m[h]);
       const float f = (M == -INFINITY) ? 0.f : fast_exp2(st.m[h] - M);
-      float L = st.l[h] * f;
-      L += __shfl_xor(L, 8);
-      L += __shfl_xor(L, 16);
-      L += __shfl_xor(L, 32);
+      st.l[h] = rowgroups_sum(st.l[h] * f);
 #pragma unroll
-      for (int e = 0; e < C::NACC; ++e) {
-        float x = st.acc[h][e] * f;
-        x += __shfl_xor(x, 8);
-        x += __shfl_xor(x, 16);
-        x += __shfl_xor(x, 32);
-        st.acc[h][e] = x;
-      }
+      for (int e = 0; e < C::NACC; ++e) st.acc[h][e] = rowgroups_sum(st.acc[h][e] * f);
       st.m[h] = M;
-      st.l[h] = L;
     }
     if (lane < 8) {
 #pragma unroll
       for (int h = 0; h < HW; ++h)
 #pragma unroll
-        for (int cc = 0; cc < C::CPL; ++cc)
+        for (int c2 = 0; c2 < C::CPL; ++c2)
 #pragma unroll
           for (int e = 0; e < C::EPC; ++e)
-            w_acc[stream][(hg * HW + h) * D + (cc * 8 + s) * C::EPC + e] = st.acc[h][cc * C::EPC + e];
+            w_acc[slot][(hg * HW + h) * D + (c2 * 8 + s) * C::EPC + e] = st.acc[h][c2 * C::EPC + e];
     }
     if (lane == 0) {
 #pragma unroll
       for (int h = 0; h < HW; ++h) {
-        w_m[stream][hg * HW + h] = st.m[h];
-        w_l[stream][hg * HW + h] = st.l[h];
+        w_m[slot][hg * HW + h] = st.m[h];
+        w_l[slot][hg * HW + h] = st.l[h];
       }
     }
-    __syncthreads();
-
-    // ---- merge the tile streams; segment result
-    const int64_t first_blk = h0 / a.chunk;
-    const int n_seg = (int)((h0 + hrows - 1) / a.chunk - first_blk + 1);
-    const int seg = (int)(blk - first_blk);
-    float* rec = a.ws1 + ((size_t)first_blk + (size_t)hh + seg) * REC;
-    {
-      constexpr int OPT = MergeShape<D, G>::OPT;
-      const int e0 = threadIdx.x * OPT;
-      if (e0 < G * D) {
-        const int h = e0 / D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < NS; ++w) M = fmaxf(M, w_m[w][h]);
-        float L = 0.f, A[OPT];
-#pragma unroll
-        for (int o = 0; o < OPT; ++o) A[o] = 0.f;
-#pragma unroll
-        for (int w = 0; w < NS; ++w) {
-          const float f = (w_m[w][h] == -INFINITY) ? 0.f : fast_exp2(w_m[w][h] - M);
-          L += w_l[w][h] * f;
-#pragma unroll
-          for (int o = 0; o < OPT; ++o) A[o] += w_acc[w][e0 + o] * f;
-        }
-        if (n_seg == 1) {
-          const float inv = 1.f / L;
-#pragma unroll
-          for (int o = 0; o < OPT; ++o) {
-            if (BF16) {
-              reinterpret_cast<uint16_t*>(a.out)[q_off + e0 + o] = (uint16_t)f32_to_bf16_bits(A[o] * inv);
-            } else {
-              reinterpret_cast<float*>(a.out)[q_off + e0 + o] = A[o] * inv;
-            }
-          }
-        } else {
-#pragma unroll
-          for (int o = 0; o < OPT; ++o) rec_store(rec + e0 + o, A[o]);
-          if (e0 % D == 0) {
-            rec_store(rec + G * D + h, M);
-            rec_store(rec + G * D + G + h, L);
-          }
-        }
-      }
-    }
-    wait_stores_done();
-    __syncthreads();  // LDS is reused by the next segment; records are written
-    if (n_seg == 1) continue;
-
-    // ---- first-level merge: the last segment of each group of kSplitGroup
-    const int grp = seg / kSplitGroup;
-    const int g0 = grp * kSplitGroup;
-    const int gsz = min(kSplitGroup, n_seg - g0);
-    const int ngrp = (n_seg + kSplitGroup - 1) / kSplitGroup;
-    if (threadIdx.x == 0)
-      s_ticket = __hip_atomic_fetch_add(&a.lp.cnt1[fh * kMaxGroups + grp], 1, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const bool last_in_group = (s_ticket == gsz - 1);
-    __syncthreads();  // s_ticket is reused below
-    if (!last_in_group) continue;
-    if (threadIdx.x == 0)
-      __hip_atomic_store(&a.lp.cnt1[fh * kMaxGroups + grp], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const float* grp_src = a.ws1 + ((size_t)first_blk + (size_t)hh + g0) * REC;
-    if (ngrp == 1) {
-      merge_records<BF16, D, G>(grp_src, gsz, nullptr, a.out, q_off);
-      continue;
-    }
-    float* grp_dst = a.ws2 + ((size_t)fh * kMaxGroups + grp) * REC;
-    merge_records<BF16, D, G>(grp_src, gsz, grp_dst, nullptr, 0);
-
-    // ---- second-level merge: the last group of the head
-    wait_stores_done();
-    __syncthreads();
-    if (threadIdx.x == 0)
-      s_ticket = __hip_atomic_fetch_add(&a.lp.cnt2[fh], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const bool last_group = (s_ticket == ngrp - 1);
-    __syncthreads();
-    if (!last_group) continue;
-    if (threadIdx.x == 0) __hip_atomic_store(&a.lp.cnt2[fh], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    merge_records<BF16, D, G>(a.ws2 + (size_t)fh * kMaxGroups * REC, ngrp, nullptr, a.out, q_off);
-    __syncthreads();
   }
+  __syncthreads();
+  float* rec = a.ws1 + (size_t)blockIdx.x * C::REC;
+  for (int e = threadIdx.x; e < G * D; e += kDecodeThreads) {
+    const int h = e / D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < SLOTS; ++x) M = fmaxf(M, w_m[x][h]);
+    float L = 0.f, A = 0.f;
+#pragma unroll
+    for (int x = 0; x < SLOTS; ++x) {
+      const float f = (w_m[x][h] == -INFINITY) ? 0.f : fast_exp2(w_m[x][h] - M);
+      L += w_l[x][h] * f;
+      A += w_acc[x][e] * f;
+    }
+    if (w.nparts == 1) {
+      if (BF16) reinterpret_cast<uint16_t*>(a.out)[q_off + e] = (uint16_t)f32_to_bf16_bits(A / L);
+      else reinterpret_cast<float*>(a.out)[q_off + e] = A / L;
+    } else {
+      rec[e] = A;
+      if (e % D == 0) {
+        rec[G * D + h] = M;
+        rec[G * D + G + h] = L;
+      }
+    }
+  }
+}
+
+// Merges the partial records of every head that spans several work items.
+// Workgroup = (flat head, query head, 32 output elements); its 512 threads are
+// 16 record groups x 32 elements, each thread folding every 16th record.
+constexpr int kCombineElems = 32;
+constexpr int kCombineGroups = kDecodeThreads / kCombineElems;  // 16
+
+template <bool BF16, int D, int G>
+__global__ __launch_bounds__(kDecodeThreads) void combine_kernel(DecodeArgs a) {
+  using C = DecodeCfg<BF16, D, G>;
+  constexpr int DC = D / kCombineElems;
+  __shared__ float c_m[kCombineGroups][kCombineElems], c_l[kCombineGroups][kCombineElems],
+      c_a[kCombineGroups][kCombineElems];
+  const int64_t hh = blockIdx.x / (G * DC);
+  const int h = (int)((blockIdx.x / DC) % G);
+  const int dcn = (int)(blockIdx.x % DC);
+  const int64_t n_ret_heads = (int64_t)a.B * a.n_ret;
+  int64_t first;
+  int n_seg, b, kvh;
+  if (hh < n_ret_heads) {
+    first = hh * a.nb_ret;
+    n_seg = a.nb_ret;
+    b = (int)(hh / a.n_ret);
+    kvh = a.map.orig_ret[hh % a.n_ret];
+  } else {
+    const int64_t x = hh - n_ret_heads;
+    first = n_ret_heads * a.nb_ret + x * a.nb_str;
+    n_seg = a.nb_str;
+    b = (int)(x / a.n_str);
+    kvh = a.map.orig_str[x % a.n_str];
+  }
+  if (n_seg == 1) return;  // written by the decode kernel
+  const float* rec0 = a.ws1 + (size_t)first * C::REC;
+  const int el = threadIdx.x % kCombineElems, grp = threadIdx.x / kCombineElems;
+  const int e = h * D + dcn * kCombineElems + el;
+  float M = -INFINITY, L = 0.f, A = 0.f;
+  constexpr int NB = 8;  // records per batch, loads issued together
+  for (int i0 = grp; i0 < n_seg; i0 += NB * kCombineGroups) {
+    float mv[NB], lv[NB], av[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int i = i0 + j * kCombineGroups;
+      const float* r = rec0 + (size_t)(i < n_seg ? i : i0) * C::REC;
+      mv[j] = i < n_seg ? r[G * D + h] : -INFINITY;
+      lv[j] = r[G * D + G + h];
+      av[j] = r[e];
+    }
+    float Mb = M;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) Mb = fmaxf(Mb, mv[j]);
+    const float f = (M == -INFINITY) ? 0.f : fast_exp2(M - Mb);
+    L *= f;
+    A *= f;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const float w = (mv[j] == -INFINITY) ? 0.f : fast_exp2(mv[j] - Mb);
+      L += lv[j] * w;
+      A += av[j] * w;
+    }
+    M = Mb;
+  }
+  c_m[grp][el] = M;
+  c_l[grp][el] = L;
+  c_a[grp][el] = A;
+  __syncthreads();
+  if (grp != 0) return;
+  float Mt = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kCombineGroups; ++k) Mt = fmaxf(Mt, c_m[k][el]);
+  float Lt = 0.f, At = 0.f;
+#pragma unroll
+  for (int k = 0; k < kCombineGroups; ++k) {
+    const float w = (c_m[k][el] == -INFINITY) ? 0.f : fast_exp2(c_m[k][el] - Mt);
+    Lt += c_l[k][el] * w;
+    At += c_a[k][el] * w;
+  }
+  const size_t o = ((size_t)b * a.n_q + (size_t)kvh * G) * D + e;
+  if (BF16) reinterpret_cast<uint16_t*>(a.out)[o] = (uint16_t)f32_to_bf16_bits(At / Lt);
+  else reinterpret_cast<float*>(a.out)[o] = At / Lt;
+}
+
+template <bool BF16, int D, int G>
+hipError_t launch_decode_g(const DecodeArgs& a, int blocks, hipStream_t s) {
+  decode_kernel<BF16, D, G><<<blocks, kDecodeThreads, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.nb_ret == 1 && a.nb_str == 1) return hipSuccess;  // every head finished in one item
+  const int64_t heads = (int64_t)a.B * (a.n_ret + a.n_str);
+  combine_kernel<BF16, D, G><<<(unsigned)(heads * G * (D / kCombineElems)), kDecodeThreads, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 template <bool BF16, int D>
 hipError_t launch_decode_d(const DecodeArgs& a, int g, int blocks, hipStream_t s) {
   switch (g) {
-    case 1: decode_kernel<BF16, D, 1><<<blocks, kDecodeThreads, 0, s>>>(a); break;
-    case 2: decode_kernel<BF16, D, 2><<<blocks, kDecodeThreads, 0, s>>>(a); break;
-    case 4: decode_kernel<BF16, D, 4><<<blocks, kDecodeThreads, 0, s>>>(a); break;
-    case 8: decode_kernel<BF16, D, 8><<<blocks, kDecodeThreads, 0, s>>>(a); break;
+    case 1: return launch_decode_g<BF16, D, 1>(a, blocks, s);
+    case 2: return launch_decode_g<BF16, D, 2>(a, blocks, s);
+    case 4: return launch_decode_g<BF16, D, 4>(a, blocks, s);
+    case 8: return launch_decode_g<BF16, D, 8>(a, blocks, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+}
+
+template <bool BF16, int D>
+int64_t round_rows_d(int g) {
+  switch (g) {
+    case 1: return DecodeCfg<BF16, D, 1>::ROUND_ROWS;
+    case 2: return DecodeCfg<BF16, D, 2>::ROUND_ROWS;
+    case 4: return DecodeCfg<BF16, D, 4>::ROUND_ROWS;
+    case 8: return DecodeCfg<BF16, D, 8>::ROUND_ROWS;
+    default: return 0;
+  }
 }
 
 }  // namespace
@@ -688,7 +786,10 @@ hipError_t launch_append(const AppendArgs& a, int dtype, int d, hipStream_t s) {
   return hipGetLastError();
 }
 
-int decode_blocks_per_cu() { return DUO_DECODE_WAVES_PER_EU; }
+int64_t decode_round_rows(int dtype, int d, int g) {
+  if (dtype == 1) return d == 128 ? round_rows_d<true, 128>(g) : round_rows_d<true, 64>(g);
+  return d == 128 ? round_rows_d<false, 128>(g) : round_rows_d<false, 64>(g);
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int g, int blocks, hipStream_t s) {
   if (dtype == 1) {

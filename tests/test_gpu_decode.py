@@ -86,17 +86,19 @@ def test_decode_after_ragged_appends():
 
 
 @pytest.mark.gpu
-def test_decode_two_level_merge():
-    """One retrieval head long enough to need many first-level merge groups."""
+def test_decode_single_head_many_partials():
+    """One retrieval head spread over every work item: the combine kernel merges
+    one partial per compute unit."""
     need_gpu()
-    say("two-level merge")
+    say("single head, many partials")
     out, ref = _decode_case(1, 8, 1, 128, "bf16", 300000, 4, 64, [1], seed=11, sink_scale=1.0)
-    check_close(out, ref, "bf16", "two-level")
+    check_close(out, ref, "bf16", "many partials")
 
 
 @pytest.mark.gpu
-def test_decode_repeated_calls_reuse_tickets():
-    """Merge tickets reset themselves: the same decode twice gives the same bits."""
+def test_decode_repeated_calls_bitwise_equal():
+    """The workspace keeps no state between calls: the same decode twice gives
+    the same bits."""
     need_gpu()
     from head_wise_kv_amd import DuoCache
     say("repeat")
