@@ -2,15 +2,17 @@
 
 Default workload: one full-model decode step of a 70B-GQA-shaped model
 (80 layers, n_q=64, n_kv=8, d=128, bf16, 128,000-token context, S=64,
-W=1024, 2 of 8 KV heads retrieval per layer): per layer, duo_append of one
-new token per KV head, then duo_decode.  The step is captured once in a HIP
-graph and replayed; every replay re-does the full work (append writes,
-decode reads every held K/V row).
+W=1024, 2 of 8 KV heads retrieval per layer): per layer, one new token per
+KV head is appended and the layer's queries decoded, in one duo_decode_append
+call (the same work as duo_append of the token followed by duo_decode).  The
+step is captured once in a HIP graph and replayed; every replay re-does the
+full work (the append writes, the decode reads every held K/V row).
 
 Prints one JSON line.  `value` is the step's algorithmic KV bytes (held K+V
 rows read once per KV head, plus the appended rows, queries and outputs)
-divided by the measured step time.  `roofline` is for the decode kernel,
-timed with HIP events around each decode launch on the launch stream.
+divided by the measured step time.  `roofline` is for one duo_decode launch
+(the split kernel plus the combine kernel of its partials), timed with HIP
+events on the launch stream around graph replays of the layers' decodes.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
@@ -124,8 +126,9 @@ def bench_decode(w: WL.Workload, steps: int, warmup: int, layers: int):
     with torch.cuda.graph(graph, stream=stream):
         for l in range(L):
             if append:
-                cache.append(l, kn_l[l], vn_l[l])
-            cache.decode(l, q_l[l], out=o_l[l], scale=w.scale)
+                cache.decode_append(l, kn_l[l], vn_l[l], q_l[l], out=o_l[l], scale=w.scale)
+            else:
+                cache.decode(l, q_l[l], out=o_l[l], scale=w.scale)
     torch.cuda.synchronize()
     T_step = T  # tokens held at the measured step (the graph re-appends position T-1)
     step_bytes = sum(decode_layer_bytes(w, mask[l], T_step, append) for l in range(L))
@@ -144,10 +147,10 @@ def bench_decode(w: WL.Workload, steps: int, warmup: int, layers: int):
     ms_step = ev0.elapsed_time(ev1) / steps
     log(f"graph: {ms_step * 1e3:.1f} us/step (wall {wall / steps * 1e6:.1f} us/step)")
 
-    # Decode kernel alone: the L decode launches of one step captured in a
-    # second graph, replayed back to back; HIP events on the launch stream
-    # bracket the replays, so the average covers each kernel plus the graph's
-    # dispatch gap between kernels.
+    # Decode alone: the L duo_decode calls of one step (split kernel + combine
+    # kernel each, over the T held rows) captured in a second graph, replayed
+    # back to back; HIP events on the launch stream bracket the replays, so
+    # the average covers both kernels of a call plus the graph's dispatch gaps.
     dgraph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(dgraph, stream=stream):
         for l in range(L):
@@ -304,9 +307,10 @@ def main():
         "data": "synthetic (seeded N(0,1) on device; mask seeded per layer)",
         "config": {"workload": w.name, "layers": L, "batch": w.B, "n_q": w.n_q, "n_kv": w.n_kv, "d_head": w.d,
                    "context": r["T"], "sink": w.S, "recent": w.W, "retrieval_kv_heads_per_layer": w.n_ret,
-                   "step": "append 1 token + decode, every layer" if w.mode == "decode_append" else "decode, every layer",
+                   "step": ("append 1 token + decode, every layer (duo_decode_append)" if w.mode == "decode_append"
+                            else "decode, every layer"),
                    "parallelism": "single GPU"},
-        "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+        "roofline": {"kernel": "duo_decode: decode_kernel + combine_kernel", "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "avg_launch_us": round(r["decode_avg_s"] * 1e6, 2),
                      "algorithmic_bytes_per_launch": int(r["decode_avg_bytes"])},

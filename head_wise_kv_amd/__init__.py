@@ -25,7 +25,8 @@ ERROR_NAMES = {DUO_EINVAL: "DUO_EINVAL", DUO_EUNSUPPORTED: "DUO_EUNSUPPORTED", D
 
 # Every entry point declared in include/duo.h.
 EXPORTS = ("duo_cache_bytes", "duo_cache_payload_bytes", "duo_cache_init", "duo_append", "duo_decode",
-           "duo_prefill_chunk", "duo_cache_seq_len", "duo_cache_head_view", "duo_cache_free", "duo_last_error")
+           "duo_decode_append", "duo_prefill_chunk", "duo_cache_seq_len", "duo_cache_head_view", "duo_cache_free",
+           "duo_last_error")
 
 
 class DuoError(RuntimeError):
@@ -52,6 +53,7 @@ def _load():
     lib.duo_cache_init.argtypes = [cfgp, vp, sz, vp, ctypes.POINTER(vp)]
     lib.duo_append.argtypes = [vp, i32, vp, vp, i64, vp]
     lib.duo_decode.argtypes = [vp, i32, vp, vp, ctypes.c_float, vp, sz, vp]
+    lib.duo_decode_append.argtypes = [vp, i32, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp]
     lib.duo_prefill_chunk.argtypes = [vp, i32, vp, vp, vp, i64, vp, ctypes.c_float, vp, sz, vp]
     lib.duo_cache_seq_len.argtypes = [vp, i32, ctypes.POINTER(i64)]
     lib.duo_cache_head_view.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(vp),
@@ -180,6 +182,23 @@ class DuoCache:
         _check(lib.duo_decode(self._h, layer, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(out.data_ptr()), sc,
                               ctypes.c_void_p(self.workspace.data_ptr()), self.workspace.numel(),
                               _stream_handle(stream)))
+        return out
+
+    def decode_append(self, layer: int, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor,
+                      out: Optional[torch.Tensor] = None, scale: Optional[float] = None, stream=None) -> torch.Tensor:
+        """Append one token (k, v: [B][n_kv][1][d]) and decode q at its
+        position, in one launch (duo_decode_append)."""
+        self._chk(k, (self.B, self.n_kv, 1, self.d), "k")
+        self._chk(v, (self.B, self.n_kv, 1, self.d), "v")
+        self._chk(q, (self.B, self.n_q, self.d), "q")
+        if out is None:
+            out = torch.empty_like(q)
+        self._chk(out, (self.B, self.n_q, self.d), "out")
+        sc = float(self.d ** -0.5 if scale is None else scale)
+        _check(lib.duo_decode_append(self._h, layer, ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                                     ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(out.data_ptr()), sc,
+                                     ctypes.c_void_p(self.workspace.data_ptr()), self.workspace.numel(),
+                                     _stream_handle(stream)))
         return out
 
     def prefill_chunk(self, layer: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -255,17 +255,24 @@ int duo_append(duo_cache* c, int layer, const void* k, const void* v, int64_t n_
   return ok();
 }
 
-int duo_decode(duo_cache* c, int layer, const void* q, void* out, float scale, void* ws, size_t ws_bytes,
-               void* stream) {
-  if (int e = check_layer(c, layer)) return e;
+namespace {
+
+// Checks shared by the decode entry points (the layer is already checked).
+int check_decode_args(const duo_cache* c, const void* q, void* out, float scale, void* ws, size_t ws_bytes) {
   if (!q || !out) return fail(DUO_EINVAL, "q or out is NULL");
   if (!aligned16(q) || !aligned16(out)) return fail(DUO_EINVAL, "q and out must be 16-byte aligned");
   if (!std::isfinite(scale) || !(scale > 0.f)) return fail(DUO_EINVAL, "scale must be finite and > 0");
-  const int64_t T = c->seq_len[layer];
-  if (T < 1) return fail(DUO_EEMPTY, "layer %d holds no token", layer);
   if (!ws || ws_bytes < c->plan.workspace)
     return fail(DUO_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", c->plan.workspace, ws_bytes);
   if (!aligned16(ws)) return fail(DUO_EINVAL, "workspace must be 16-byte aligned");
+  return DUO_OK;
+}
+
+// Enqueue the decode kernels over rows_ret / rows_str held rows per head; with
+// new_k / new_v set, the token at position `held` (rows held per retrieval
+// head) is appended and attended by the same launch.
+hipError_t enqueue_decode(duo_cache* c, int layer, const void* q, void* out, float scale, void* ws, int64_t held,
+                          const void* new_k, const void* new_v, hipStream_t stream) {
   const LayerPlan& lp = c->plan.layers[layer];
   const duo_config& cf = c->cfg;
   duo::DecodeArgs a{};
@@ -280,8 +287,19 @@ int duo_decode(duo_cache* c, int layer, const void* q, void* out, float scale, v
   a.n_str = lp.n_str;
   a.cap_ret = cf.T_cap;
   a.cap_str = c->cap_str();
-  a.rows_ret = T;
-  a.rows_str = std::min<int64_t>(T, c->cap_str());
+  a.rows_ret = held;
+  a.rows_str = std::min<int64_t>(held, c->cap_str());
+  if (new_k) {
+    const int64_t p = held, S = cf.sink, W = cf.recent;
+    a.new_k = static_cast<const char*>(new_k);
+    a.new_v = static_cast<const char*>(new_v);
+    a.new_row_ret = p;
+    a.new_slot_str = p < S ? p : S + (p - S) % W;
+    a.excl_str = p >= S + W ? a.new_slot_str : -1;  // the ring is full: the new token evicts
+    a.new_pos = (int32_t)p;
+  } else {
+    a.excl_str = -1;
+  }
   // Work items: contiguous row ranges of one head, about equal in rows, as
   // many as one workgroup per compute unit (or one per head if there are
   // more heads).  Every item holds at least one row.
@@ -305,8 +323,42 @@ int duo_decode(duo_cache* c, int layer, const void* q, void* out, float scale, v
   const int blocks = (int)(heads_ret * nb_r + heads_str * nb_s);
   a.ws1 = static_cast<float*>(ws);
   a.scale_log2 = scale * 1.4426950408889634f;
-  hipError_t e = duo::launch_decode(a, cf.dtype, cf.d_head, g, blocks, static_cast<hipStream_t>(stream));
+  return duo::launch_decode(a, cf.dtype, cf.d_head, g, blocks, stream);
+}
+
+}  // namespace
+
+int duo_decode(duo_cache* c, int layer, const void* q, void* out, float scale, void* ws, size_t ws_bytes,
+               void* stream) {
+  if (int e = check_layer(c, layer)) return e;
+  if (int e = check_decode_args(c, q, out, scale, ws, ws_bytes)) return e;
+  const int64_t T = c->seq_len[layer];
+  if (T < 1) return fail(DUO_EEMPTY, "layer %d holds no token", layer);
+  hipError_t e = enqueue_decode(c, layer, q, out, scale, ws, T, nullptr, nullptr, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+int duo_decode_append(duo_cache* c, int layer, const void* k, const void* v, const void* q, void* out, float scale,
+                      void* ws, size_t ws_bytes, void* stream) {
+  if (int e = check_layer(c, layer)) return e;
+  if (!k || !v) return fail(DUO_EINVAL, "k or v is NULL");
+  if (!aligned16(k) || !aligned16(v)) return fail(DUO_EINVAL, "k and v must be 16-byte aligned");
+  if (int e = check_decode_args(c, q, out, scale, ws, ws_bytes)) return e;
+  const int64_t p = c->seq_len[layer];
+  if (p + 1 > c->cfg.T_cap)
+    return fail(DUO_ECAPACITY, "layer %d holds %lld tokens; one more exceeds T_cap %lld", layer, (long long)p,
+                (long long)c->cfg.T_cap);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (p == 0) {  // nothing held yet: append, then decode over the one token
+    e = enqueue_append(c, layer, k, v, 0, 1, s);
+    if (e == hipSuccess) e = enqueue_decode(c, layer, q, out, scale, ws, 1, nullptr, nullptr, s);
+  } else {
+    e = enqueue_decode(c, layer, q, out, scale, ws, p, k, v, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  c->seq_len[layer] = p + 1;
   return ok();
 }
 

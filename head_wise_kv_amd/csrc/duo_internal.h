@@ -54,6 +54,16 @@ struct DecodeArgs {
   int64_t rows_ret, rows_str;   // rows held per head
   int nb_ret, nb_str;           // work items per retrieval / streaming head (each >= 1 row)
   float scale_log2;             // softmax scale * log2(e)
+  // Fused append (decode of a token appended by the same call); new_k is
+  // null for a plain decode.  rows_ret / rows_str then count the rows held
+  // before the append; the last work item of every head adds the new token
+  // and writes it to the cache.
+  const char* new_k;            // [B][n_kv][d]
+  const char* new_v;
+  int64_t new_row_ret;          // row of the new token in a retrieval head (its position)
+  int64_t new_slot_str;         // slot of the new token in a streaming head
+  int64_t excl_str;             // streaming slot whose old token the new one evicts (-1: none)
+  int32_t new_pos;              // position of the new token
 };
 
 struct PrefillArgs {

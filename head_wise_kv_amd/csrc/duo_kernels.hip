@@ -290,8 +290,8 @@ struct DecodeItem {
   int64_t r0, r1;   // rows of the head
   int part, nparts;
   int b, kvh;
-  const char* kbase;
-  const char* vbase;
+  char* kbase;
+  char* vbase;
 };
 
 template <int ROWB>
@@ -348,7 +348,7 @@ struct DecodeState {
 template <bool BF16, int D, int G>
 __device__ __forceinline__ void tile_scores(DecodeState<BF16, D, G>& st, float (&p)[DecodeCfg<BF16, D, G>::RPL][DecodeCfg<BF16, D, G>::HW],
                                             const char* kt, const uint4 (&q)[DecodeCfg<BF16, D, G>::HW][DecodeCfg<BF16, D, G>::CPL],
-                                            int nv, int rg, int s, float scale_log2) {
+                                            int nv, int excl, int rg, int s, float scale_log2) {
   using C = DecodeCfg<BF16, D, G>;
   constexpr int HW = C::HW;
   float sc[C::RPL][HW];
@@ -379,11 +379,12 @@ __device__ __forceinline__ void tile_scores(DecodeState<BF16, D, G>& st, float (
       sc[j][h] = row8_sum(acc);
     }
   }
-  // rows past the segment's end (only in its last tiles) score -inf
-  if (nv < C::TR) {
+  // rows past the item's end (only in its last tiles), and a row whose token
+  // is being evicted (excl, tile-relative; -1 if none), score -inf
+  if (nv < C::TR || excl >= 0) {
 #pragma unroll
     for (int j = 0; j < C::RPL; ++j) {
-      const bool ok = rg + 8 * j < nv;
+      const bool ok = rg + 8 * j < nv && rg + 8 * j != excl;
 #pragma unroll
       for (int h = 0; h < HW; ++h) sc[j][h] = ok ? sc[j][h] : -INFINITY;
     }
@@ -511,6 +512,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int c2 = 0; c2 < C::CPL; ++c2) q[h][c2] = ld16(qb + (size_t)h * C::ROWB + (s + 8 * c2) * 16);
   }
+  // fused append: the last item of every head adds the new token; wavefront 0
+  // holds it (lanes 0..CPR-1 its K chunks, CPR..2*CPR-1 its V chunks)
+  const bool add_new = a.new_k != nullptr && w.part == w.nparts - 1;
+  const bool ret_head = w.hh < (int64_t)a.B * a.n_ret;
+  uint4 nkv = make_uint4(0, 0, 0, 0);
+  if (add_new && wave == 0 && lane < 2 * C::CPR) {
+    const size_t src = ((size_t)w.b * a.n_kv + w.kvh) * C::ROWB + (size_t)(lane % C::CPR) * 16;
+    nkv = ld16((lane < C::CPR ? a.new_k : a.new_v) + src);
+  }
+  // streaming slot masked in the held rows (its token is evicted by the new one)
+  const int64_t excl_row = (a.new_k != nullptr && !ret_head) ? a.excl_str : -1;
   // per-lane byte offsets (within a tile) of this wavefront's load pieces, and
   // the tile (slot) each piece belongs to
   uint32_t poff[kPiecesPerWave];
@@ -577,7 +589,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     if (V_PART) {
       if (nv > 0) tile_pv<BF16, D, G>(st, p, tile, rg, s);
     } else {
-      if (nv > 0) tile_scores<BF16, D, G>(st, p, tile, q, nv, rg, s, a.scale_log2);
+      const int64_t ex = excl_row - row0;
+      if (nv > 0) tile_scores<BF16, D, G>(st, p, tile, q, nv, (ex >= 0 && ex < TR) ? (int)ex : -1, rg, s, a.scale_log2);
     }
   };
   const int64_t n_units = 2 * nrounds;
@@ -592,6 +605,28 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   // the loads issued past the last unit (out of range, nothing read) land
   // before the workgroup can leave
   wait_vmcnt<0>();
+
+  // ---- fused append: score the new token as a one-row tile (K in row 0 of
+  // ring0, V in row 0 of ring1; the other rows are masked), then store it
+  if (add_new) {
+    lds_barrier();  // every wavefront is done with the ring
+    if (wave == 0 && lane < 2 * C::CPR)
+      *reinterpret_cast<uint4*>((lane < C::CPR ? ring0 : ring1) + (lane % C::CPR) * 16) = nkv;  // row 0: no swizzle
+    lds_barrier();
+    if (slot == 0) {
+      tile_scores<BF16, D, G>(st, p, ring0, q, 1, -1, rg, s, a.scale_log2);
+      tile_pv<BF16, D, G>(st, p, ring1, rg, s);
+    }
+    if (wave == 0 && lane < 2 * C::CPR) {
+      const int64_t row = ret_head ? a.new_row_ret : a.new_slot_str;
+      char* dst = (lane < C::CPR ? w.kbase : w.vbase) + (size_t)row * C::ROWB + (lane % C::CPR) * 16;
+      *reinterpret_cast<uint4*>(dst) = nkv;
+      if (!ret_head && lane == 0) {
+        const int64_t si = w.hh - (int64_t)a.B * a.n_ret;  // b * n_str + streaming index
+        a.lp.pos[si * a.cap_str + a.new_slot_str] = a.new_pos;
+      }
+    }
+  }
 
   // ---- merge the 8 row groups of each wavefront (lanes xor 8, 16, 32), then
   // the slots through LDS

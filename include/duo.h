@@ -68,9 +68,9 @@ typedef struct duo_cache duo_cache; /* opaque host handle */
 /* Sizes (host only, no device work).  *arena_bytes: the device arena for
  * duo_cache_init.  It holds, per layer, K and V as [B][n_ret][T_cap][d] for
  * the retrieval heads and [B][n_str][S+W][d] for the streaming heads (the two
- * buffer kinds of the guide's section 2), an int32 position per streaming
- * slot, and a few counters.  *workspace_bytes: the device scratch that
- * duo_decode and duo_prefill_chunk need (partial softmax results).  Either
+ * buffer kinds of the guide's section 2) and an int32 position per streaming
+ * slot.  *workspace_bytes: the device scratch that duo_decode,
+ * duo_decode_append and duo_prefill_chunk need (partial softmax results).  Either
  * output pointer may be NULL.  Returns DUO_OK or DUO_EINVAL/DUO_EUNSUPPORTED. */
 int duo_cache_bytes(const duo_config* cfg, size_t* arena_bytes, size_t* workspace_bytes);
 
@@ -79,7 +79,7 @@ int duo_cache_bytes(const duo_config* cfg, size_t* arena_bytes, size_t* workspac
 int duo_cache_payload_bytes(const duo_config* cfg, size_t* payload_bytes);
 
 /* Bind a cache to a caller-owned device arena of at least duo_cache_bytes()
- * bytes, 256-byte aligned.  Enqueues the zeroing of positions and counters on
+ * bytes, 256-byte aligned.  Enqueues the zeroing of the positions on
  * `stream`; every layer starts empty.  On success *out receives a handle that
  * must be released with duo_cache_free (the arena must outlive it). */
 int duo_cache_init(const duo_config* cfg, void* arena, size_t arena_bytes, void* stream,
@@ -106,6 +106,22 @@ int duo_append(duo_cache* c, int layer, const void* k, const void* v, int64_t n_
  * DUO_EEMPTY if the layer holds no token. */
 int duo_decode(duo_cache* c, int layer, const void* q, void* out, float scale, void* ws,
                size_t ws_bytes, void* stream);
+
+/* One generation step in a single launch: append one token and decode the
+ * query at its position.  Same result and cache state as duo_append(k, v, 1)
+ * followed by duo_decode(q): the new token attends to the cached keys of the
+ * earlier tokens and to its own, and appending leaves the earlier cached
+ * states unchanged ("Attention Variants and KV-Cache Compression", "When Is
+ * Reuse Exact?").  Fusing the two neighbouring operations saves a launch per
+ * layer and step ("Attention Variants and Memory Efficiency", "What the
+ * Inference Runtime Can Change").  The token is written to its row or ring
+ * slot while the held rows are read; a streaming slot whose token it evicts
+ * is left out of the attention.  k, v: device [B][n_kv][1][d]; q, out: device
+ * [B][n_q][d]; ws as for duo_decode.  DUO_ECAPACITY if the layer is full;
+ * other errors as duo_append and duo_decode.  The layer advances by one
+ * token. */
+int duo_decode_append(duo_cache* c, int layer, const void* k, const void* v, const void* q, void* out,
+                      float scale, void* ws, size_t ws_bytes, void* stream);
 
 /* Chunked prefill of C >= 1 tokens on `layer`, at positions P .. P+C-1 with
  * P = seq_len ("Attention Variants and KV-Cache Compression", "When Is Reuse

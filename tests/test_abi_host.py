@@ -93,4 +93,5 @@ def test_calls_on_null_handle_fail_cleanly():
     assert H.lib.duo_cache_seq_len(None, 0, ctypes.byref(x)) == H.DUO_EINVAL
     assert H.lib.duo_append(None, 0, None, None, 1, None) == H.DUO_EINVAL
     assert H.lib.duo_decode(None, 0, None, None, 1.0, None, 0, None) == H.DUO_EINVAL
+    assert H.lib.duo_decode_append(None, 0, None, None, None, None, 1.0, None, 0, None) == H.DUO_EINVAL
     H.lib.duo_cache_free(None)
