@@ -80,9 +80,9 @@ int validate(const duo_config* c) {
 
 int elem_bytes(const duo_config* c) { return c->dtype == DUO_BF16 ? 2 : 4; }
 
-size_t decode_rec_floats(const duo_config* c) {
+size_t decode_rec_floats(const duo_config* c) {  // acc[g][d], max[g], sum[g], padded to 16 bytes
   const int g = c->n_q / c->n_kv;
-  return (size_t)g * (c->d_head + 2);
+  return ((size_t)g * (c->d_head + 2) + 3) / 4 * 4;
 }
 
 void make_plan(const duo_config* c, Plan* p) {

@@ -203,7 +203,7 @@ struct DecodeCfg {
   static constexpr int SLOT_BYTES = TR * ROWB;
   static constexpr int ROUND_ROWS = SLOTS * TR;
   static constexpr int NACC = CPL * EPC;         // output elements per lane per head
-  static constexpr int REC = G * (D + 2);        // floats per partial record
+  static constexpr int REC = (G * (D + 2) + 3) / 4 * 4;  // floats per partial record (16-byte multiple)
   static_assert(CPR % 8 == 0, "rows must span a multiple of 8 chunks");
   static_assert(RPL >= 2 && RPL % 2 == 0, "rows are paired for the weighted sum");
   static_assert(SLOT_BYTES % 1024 == 0, "a load piece stays within one tile");
@@ -488,9 +488,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char ring1[kUnitBytes];
   __shared__ __attribute__((aligned(1024))) char ring2[kUnitBytes];
   __shared__ __attribute__((aligned(1024))) char ring3[kUnitBytes];
-  __shared__ float w_acc[SLOTS][G * D];
-  __shared__ float w_m[SLOTS][G], w_l[SLOTS][G];
-  char* const rings[kRingUnits] = {ring0, ring1, ring2, ring3};
+  // merge state: max and sum of every (slot, row group, query head) partial,
+  // its weight in the merged result, and the merged max and sum per head
+  __shared__ __attribute__((aligned(16))) float w_m[G][SLOTS * 8], w_l[G][SLOTS * 8], w_w[G][SLOTS * 8],
+      w_lw[G][SLOTS * 8];
+  __shared__ float w_mt[G];
+  char* const rings[kRingUnits] = {ring0, ring1, ring2, ring3};  // indexed by constants only
+  auto ring_at = [&](int i) -> char* { return i == 0 ? ring0 : i == 1 ? ring1 : i == 2 ? ring2 : ring3; };
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -628,56 +632,87 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     }
   }
 
-  // ---- merge the 8 row groups of each wavefront (lanes xor 8, 16, 32), then
-  // the slots through LDS
+  // ---- merge the partials of the SLOTS x 8 row groups through LDS.  The ring
+  // is free now; it holds every lane's accumulators as X[slot][rg][h][d]
+  // (SLOTS * 8 * G * D floats <= 128 KB), split over the four ring arrays.
+  constexpr int XB = kUnitBytes;  // bytes per ring array
+  static_assert(SLOTS * 8 * G * D * 4 <= kRingUnits * XB, "partials fit the ring");
+  lds_barrier();  // every wavefront is done with the ring
   if (active) {
 #pragma unroll
     for (int h = 0; h < HW; ++h) {
-      const float M = rowgroups_max(st.m[h]);
-      const float f = (M == -INFINITY) ? 0.f : fast_exp2(st.m[h] - M);
-      st.l[h] = rowgroups_sum(st.l[h] * f);
+      const int hG = hg * HW + h;
 #pragma unroll
-      for (int e = 0; e < C::NACC; ++e) st.acc[h][e] = rowgroups_sum(st.acc[h][e] * f);
-      st.m[h] = M;
-    }
-    if (lane < 8) {
+      for (int c2 = 0; c2 < C::CPL; ++c2) {
+        const int off = ((((slot * 8 + rg) * G + hG) * D) + (c2 * 8 + s) * C::EPC) * 4;
+        float* dst = reinterpret_cast<float*>(ring_at(off / XB) + off % XB);
 #pragma unroll
-      for (int h = 0; h < HW; ++h)
-#pragma unroll
-        for (int c2 = 0; c2 < C::CPL; ++c2)
-#pragma unroll
-          for (int e = 0; e < C::EPC; ++e)
-            w_acc[slot][(hg * HW + h) * D + (c2 * 8 + s) * C::EPC + e] = st.acc[h][c2 * C::EPC + e];
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int h = 0; h < HW; ++h) {
-        w_m[slot][hg * HW + h] = st.m[h];
-        w_l[slot][hg * HW + h] = st.l[h];
+        for (int e = 0; e < C::EPC; e += 4)
+          *reinterpret_cast<float4*>(dst + e) =
+              make_float4(st.acc[h][c2 * C::EPC + e], st.acc[h][c2 * C::EPC + e + 1], st.acc[h][c2 * C::EPC + e + 2],
+                          st.acc[h][c2 * C::EPC + e + 3]);
+      }
+      if (s == 0) {
+        w_m[hG][slot * 8 + rg] = st.m[h];
+        w_l[hG][slot * 8 + rg] = st.l[h];
       }
     }
   }
   __syncthreads();
-  float* rec = a.ws1 + (size_t)blockIdx.x * C::REC;
-  for (int e = threadIdx.x; e < G * D; e += kDecodeThreads) {
-    const int h = e / D;
+  constexpr int NP = SLOTS * 8;  // partials per query head
+  static_assert(NP * G <= kDecodeThreads && NP % 4 == 0, "one thread per (partial, head)");
+  if (threadIdx.x < NP * G) {  // weight of partial i of head h in the merged result
+    const int h = threadIdx.x / NP, i = threadIdx.x % NP;
     float M = -INFINITY;
 #pragma unroll
-    for (int x = 0; x < SLOTS; ++x) M = fmaxf(M, w_m[x][h]);
-    float L = 0.f, A = 0.f;
+    for (int j = 0; j < NP; j += 4) {
+      const float4 m4 = *reinterpret_cast<const float4*>(&w_m[h][j]);
+      M = fmaxf(fmaxf(M, fmaxf(m4.x, m4.y)), fmaxf(m4.z, m4.w));
+    }
+    const float wt = (w_m[h][i] == -INFINITY) ? 0.f : fast_exp2(w_m[h][i] - M);
+    w_w[h][i] = wt;
+    w_lw[h][i] = w_l[h][i] * wt;
+    if (i == 0) w_mt[h] = M;
+  }
+  __syncthreads();
+  // four consecutive output elements per thread
+  float* rec = a.ws1 + (size_t)blockIdx.x * C::REC;
+  for (int e4 = threadIdx.x * 4; e4 < G * D; e4 += kDecodeThreads * 4) {
+    const int h = e4 / D, d = e4 % D;
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+    float L = 0.f;
 #pragma unroll
-    for (int x = 0; x < SLOTS; ++x) {
-      const float f = (w_m[x][h] == -INFINITY) ? 0.f : fast_exp2(w_m[x][h] - M);
-      L += w_l[x][h] * f;
-      A += w_acc[x][e] * f;
+    for (int i0 = 0; i0 < NP; i0 += 4) {
+      const float4 wt4 = *reinterpret_cast<const float4*>(&w_w[h][i0]);
+      const float4 lw4 = *reinterpret_cast<const float4*>(&w_lw[h][i0]);
+      L += (lw4.x + lw4.y) + (lw4.z + lw4.w);
+      const float wv[4] = {wt4.x, wt4.y, wt4.z, wt4.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int off = (((i0 + k) * G + h) * D + d) * 4;
+        const float4 x = *reinterpret_cast<const float4*>(ring_at(off / XB) + off % XB);
+        A.x = fmaf(x.x, wv[k], A.x);
+        A.y = fmaf(x.y, wv[k], A.y);
+        A.z = fmaf(x.z, wv[k], A.z);
+        A.w = fmaf(x.w, wv[k], A.w);
+      }
     }
     if (w.nparts == 1) {
-      if (BF16) reinterpret_cast<uint16_t*>(a.out)[q_off + e] = (uint16_t)f32_to_bf16_bits(A / L);
-      else reinterpret_cast<float*>(a.out)[q_off + e] = A / L;
+      const float inv = 1.f / L;
+      if (BF16) {
+        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + q_off + e4;
+        o[0] = (uint16_t)f32_to_bf16_bits(A.x * inv);
+        o[1] = (uint16_t)f32_to_bf16_bits(A.y * inv);
+        o[2] = (uint16_t)f32_to_bf16_bits(A.z * inv);
+        o[3] = (uint16_t)f32_to_bf16_bits(A.w * inv);
+      } else {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + q_off + e4) =
+            make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
+      }
     } else {
-      rec[e] = A;
-      if (e % D == 0) {
-        rec[G * D + h] = M;
+      *reinterpret_cast<float4*>(rec + e4) = A;
+      if (d == 0) {
+        rec[G * D + h] = w_mt[h];
         rec[G * D + G + h] = L;
       }
     }
