@@ -261,7 +261,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gqa70b_decode_128k",
-                    choices=[n for n, w in WL.WORKLOADS.items() if w.mode != "prefill"])
+                    choices=[n for n, w in WL.WORKLOADS.items() if w.mode in ("decode", "decode_append")])
     ap.add_argument("--layers", type=int, default=0, help="limit layers (profiling only; 0 = all)")
     ap.add_argument("--also", default="mha7b_decode_128k",
                     help="comma-separated extra decode workloads reported under 'also' ('' for none)")

@@ -15,6 +15,7 @@ import torch
 import oracle
 from oracle import attention as A
 from oracle import cache as Cc
+from oracle import gating as G
 from oracle import sizes as Z
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -235,11 +236,78 @@ def check_gqa_expansion():
     assert np.allclose(got, lib, atol=1e-12, rtol=0)
 
 
+# ------------------------------------------------------------------ head-gated forward
+
+def check_gated_hand_case():
+    # golden/gated_tiny.txt: the hand-derived blend on N=3, d=1, S=1, W=1.
+    Q = np.ones((1, 3, 1)); K = np.zeros((1, 3, 1)); V = np.array([[[1.0], [2.0], [4.0]]])
+    keys = K[0].tolist(); vals = V[0].tolist()
+    for a_s, t_s, num, den in _golden_lines("gated_tiny.txt"):
+        alpha, t, want = float(a_s), int(t_s), int(num) / int(den)
+        got = G.gated_forward(Q, K, V, [alpha], 1, 1, 1.0, rows=np.array([t]))[0, 0, 0]
+        assert abs(got - want) < 1e-15, (alpha, t, got, want)
+        got_b = G.gated_row_bruteforce([1.0], keys, vals, t, alpha, 1, 1, 1.0)[0]
+        assert abs(got_b - want) < 1e-15, (alpha, t, got_b, want)
+
+
+def check_gated_library_endpoints():
+    # alpha = 1 is causal attention and alpha = 0 (S = 0) a band of W keys: torch SDPA,
+    # float64 CPU; a mixed per-KV-head gate blends the two library results per query head.
+    N, d, W = 29, 8, 5
+    for n_q, n_kv in [(3, 3), (8, 2)]:
+        Q = _rand((n_q, N, d), 41); K = _rand((n_kv, N, d), 42); V = _rand((n_kv, N, d), 43)
+        scale = 1.0 / math.sqrt(d)
+        gqa = n_q != n_kv
+        causal = _sdpa(Q[None], K[None], V[None], is_causal=True, enable_gqa=gqa)[0]
+        band = torch.ones(N, N, dtype=torch.bool).tril() & ~torch.ones(N, N, dtype=torch.bool).tril(-W)
+        window = _sdpa(Q[None], K[None], V[None], attn_mask=band, enable_gqa=gqa)[0]
+        assert np.allclose(G.gated_forward(Q, K, V, [1.0] * n_kv, 0, W, scale), causal, atol=1e-12, rtol=0)
+        assert np.allclose(G.gated_forward(Q, K, V, [0.0] * n_kv, 0, W, scale), window, atol=1e-12, rtol=0)
+        alpha = [0.125 + 0.25 * k for k in range(n_kv)]
+        got = G.gated_forward(Q, K, V, alpha, 0, W, scale)
+        g = n_q // n_kv
+        for h in range(n_q):
+            a = alpha[h // g]
+            assert np.allclose(got[h], a * causal[h] + (1 - a) * window[h], atol=1e-12, rtol=0), h
+
+
+def check_gated_bruteforce_agrees():
+    # numpy route vs pure-Python enumeration on tiny inputs, with sinks.
+    seed = 51
+    for (n_q, n_kv, d, S, W, N) in [(2, 2, 3, 1, 2, 7), (4, 2, 2, 2, 3, 9), (3, 1, 2, 0, 1, 5)]:
+        Q = _rand((n_q, N, d), seed); K = _rand((n_kv, N, d), seed + 1); V = _rand((n_kv, N, d), seed + 2)
+        alpha = list(np.random.default_rng(seed).uniform(0, 1, n_kv))
+        seed += 3
+        got = G.gated_forward(Q, K, V, alpha, S, W, 0.6)
+        for h in range(n_q):
+            k = h // (n_q // n_kv)
+            for t in range(N):
+                ref = G.gated_row_bruteforce(list(Q[h, t]), K[k, :t + 1].tolist(), V[k, :t + 1].tolist(),
+                                             t, alpha[k], S, W, 0.6)
+                assert np.allclose(got[h, t], ref, atol=1e-12, rtol=0), (h, t)
+
+
+def check_gated_gqa_expansion():
+    # Result == the same forward on K/V and gates expanded with repeat_interleave.
+    n_q, n_kv, N, d, S, W = 8, 2, 21, 4, 2, 4
+    Q = _rand((n_q, N, d), 61); K = _rand((n_kv, N, d), 62); V = _rand((n_kv, N, d), 63)
+    alpha = [0.3, 0.9]
+    got = G.gated_forward(Q, K, V, alpha, S, W, 0.5)
+    g = n_q // n_kv
+    Ke = torch.from_numpy(K).repeat_interleave(g, dim=0).numpy()
+    Ve = torch.from_numpy(V).repeat_interleave(g, dim=0).numpy()
+    ae = torch.tensor(alpha, dtype=torch.float64).repeat_interleave(g).tolist()
+    ref = G.gated_forward(Q, Ke, Ve, ae, S, W, 0.5)
+    assert np.allclose(got, ref, atol=1e-13, rtol=0)
+
+
 ALL_CHECKS = [
     check_printed_kv_sizes, check_effective_context, check_mixed_payload_closed_forms,
     check_ring_example, check_streaming_composition, check_simulation_counts, check_keep_set_is_visible_set,
     check_hand_cases, check_bruteforce_agrees, check_library_special_cases,
     check_softmax_invariants, check_chunk_invariance, check_gqa_expansion,
+    check_gated_hand_case, check_gated_library_endpoints, check_gated_bruteforce_agrees,
+    check_gated_gqa_expansion,
 ]
 
 

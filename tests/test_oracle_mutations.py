@@ -5,6 +5,7 @@ import pytest
 
 from oracle import attention as A
 from oracle import cache as Cc
+from oracle import gating as G
 from oracle import sizes as Z
 from tests import oracle_checks as OC
 
@@ -64,6 +65,15 @@ def _ring_slot_by_position(self, position, payload=None):
     return self.S + slot
 
 
+def _blend_swapped(full, stream, a):
+    return (1.0 - a) * full + a * stream          # gate applied to the wrong attention
+
+
+def _gate_by_query_mod(alpha, n_q):
+    n_kv = len(alpha)
+    return np.array([float(alpha[h % n_kv]) for h in range(n_q)])  # transposed gate mapping
+
+
 def _kv_bytes_one_factor(L, n_kv, d_head, T, elem_bytes=2):
     return elem_bytes * L * n_kv * d_head * T      # dropped K+V factor
 
@@ -78,6 +88,8 @@ MUTATIONS = {
     "flipped_sign": (A, "attend_row", _attend_sign),
     "ring_by_position": (Cc.StreamingHeadCache, "append", _ring_slot_by_position),
     "kv_bytes_factor": (Z, "kv_cache_bytes", _kv_bytes_one_factor),
+    "gate_swapped": (G, "blend", _blend_swapped),
+    "gate_mod_mapping": (G, "gate_of_query_heads", _gate_by_query_mod),
 }
 
 

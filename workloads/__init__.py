@@ -7,7 +7,7 @@ attention arithmetic: no visibility rule, no softmax, no cache slot placement.
 Recipe (every tensor):
   * values are drawn as float32 standard normals from numpy's PCG64, seeded by
     ``SeedSequence([241010819, cfg_index, layer, batch, head, tensor_id, block])``
-    where tensor_id is 0=Q, 1=K, 2=V, 3=mask and ``block`` counts GEN_BLOCK-row
+    where tensor_id is 0=Q, 1=K, 2=V, 3=mask, 4=gate and ``block`` counts GEN_BLOCK-row
     slabs along the position axis, so any position range can be regenerated on
     its own;
   * for workloads that say so, the K rows of the first ``sink`` positions are
@@ -19,9 +19,13 @@ The retrieval/streaming role of each KV head is drawn per layer with the same
 seeding (tensor_id 3): a seeded permutation of the KV heads whose first
 ``n_ret`` entries are the retrieval heads.
 
-The five workloads follow the shapes the DuoAttention pages use as examples
+Head gates (one per KV head and layer, for the gated full/streaming forward)
+are float32 uniforms on [0, 1) from the same seeding (tensor_id 4).
+
+The five cache workloads follow the shapes the DuoAttention pages use as examples
 (a LLaMA-3-8B-like GQA layer, a 7B MHA model, a 70B GQA model at 128k context,
-and a chunked prefill), with synthetic values standing in for model
+and a chunked prefill), plus one gated-forward workload on the LLaMA-3-8B layer
+shape, with synthetic values standing in for model
 activations: no weights or datasets are involved.
 """
 from __future__ import annotations
@@ -33,7 +37,7 @@ import numpy as np
 
 SEED_ROOT = 241010819
 GEN_BLOCK = 4096  # rows per independently seeded slab along the position axis
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_MASK = 0, 1, 2, 3
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_MASK, TENSOR_GATE = 0, 1, 2, 3, 4
 
 
 @dataclasses.dataclass(frozen=True)
@@ -51,7 +55,7 @@ class Workload:
     W: int                  # recent-window tokens kept by streaming heads
     n_ret: int              # retrieval KV heads per layer
     sink_scale: float       # multiplier on K rows at positions < S (1.0 = none)
-    mode: str               # "decode" | "decode_append" | "prefill"
+    mode: str               # "decode" | "decode_append" | "prefill" | "gated"
     chunk: int = 0          # prefill chunk length
     fixed_mask: Optional[tuple] = None  # explicit per-layer mask rows, else seeded
 
@@ -92,8 +96,14 @@ WORKLOADS: Dict[str, Workload] = {
     "llama3_8b_prefill_64k": Workload("llama3_8b_prefill_64k", 4, L=1, B=1, n_q=32, n_kv=8, d=128,
                                       dtype="bf16", T=65536, S=64, W=1024, n_ret=2,
                                       sink_scale=1.0, mode="prefill", chunk=4096),
+    # Gated full/streaming forward over one 32,768-token sequence of a LLaMA-3-8B-shaped layer
+    # (one gate per KV head; the retrieval mask does not apply).
+    "llama3_8b_gated_32k": Workload("llama3_8b_gated_32k", 5, L=1, B=1, n_q=32, n_kv=8, d=128,
+                                    dtype="bf16", T=32768, S=64, W=1024, n_ret=0,
+                                    sink_scale=1.0, mode="gated"),
 }
-ORDER: List[str] = list(WORKLOADS)
+# Workloads that run on the mixed cache (the gated forward does not).
+ORDER: List[str] = [n for n, w in WORKLOADS.items() if w.mode != "gated"]
 
 
 def _rng(w: Workload, layer: int, b: int, head: int, tensor_id: int, block: int) -> np.random.Generator:
@@ -115,6 +125,11 @@ def mask_table(w: Workload, layers: Optional[int] = None) -> np.ndarray:
     """uint8 [L][n_kv] retrieval mask."""
     L = w.L if layers is None else layers
     return np.stack([retrieval_mask(w, l) for l in range(L)])
+
+
+def gate_values(w: Workload, layer: int) -> np.ndarray:
+    """Seeded head gates for one layer: float32 uniforms on [0, 1), one per KV head."""
+    return _rng(w, layer, 0, 0, TENSOR_GATE, 0).uniform(0.0, 1.0, w.n_kv).astype(np.float32)
 
 
 def rows_f32(w: Workload, layer: int, b: int, head: int, tensor_id: int, p0: int, p1: int) -> np.ndarray:
