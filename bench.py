@@ -221,6 +221,46 @@ def bench_prefill(w: WL.Workload, reps: int = 2):
     return dict(workload=w.name, seconds=best, tflops=tf, mfma_frac=tf / BF16_DENSE_TFLOPS, algorithmic_tflop=flops / 1e12)
 
 
+# ------------------------------------------------------------------ gated forward (secondary)
+
+def gated_flops(w: WL.Workload) -> float:
+    """Causal (query, key) pairs x 4 d flops: every pair's score and P V product
+    is needed once (the sink+window pairs are a subset of the causal ones)."""
+    N = w.T
+    return 4.0 * w.d * w.B * w.n_q * (N * (N + 1) / 2.0)
+
+
+def bench_gated(w: WL.Workload, reps: int = 3):
+    import torch
+    import head_wise_kv_amd as H
+
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q = torch.empty(w.B, w.n_q, w.T, w.d, dtype=dt, device=dev)
+    k = torch.empty(w.B, w.n_kv, w.T, w.d, dtype=dt, device=dev)
+    v = torch.empty_like(k)
+    WL.device_fill_normal(q, WL.device_seed(w, 0, WL.TENSOR_Q))
+    WL.device_fill_normal(k, WL.device_seed(w, 0, WL.TENSOR_K))
+    WL.device_fill_normal(v, WL.device_seed(w, 0, WL.TENSOR_V))
+    alpha = torch.from_numpy(WL.gate_values(w, 0)).to(dev)
+    out = torch.empty_like(q)
+    H.gated_attention(q, k, v, alpha, w.S, w.W, out=out, scale=w.scale)  # warm-up
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        H.gated_attention(q, k, v, alpha, w.S, w.W, out=out, scale=w.scale)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+    best = min(times)
+    flops = gated_flops(w)
+    tf = flops / best / 1e12
+    return dict(workload=w.name, seconds=best, median_s=float(np.median(times)), tflops=tf,
+                mfma_frac=tf / BF16_DENSE_TFLOPS, algorithmic_tflop=flops / 1e12)
+
+
 # ------------------------------------------------------------------ CPU oracle baseline
 
 def cpu_baseline(w: WL.Workload, budget_s: float = 15.0):
@@ -266,6 +306,7 @@ def main():
     ap.add_argument("--also", default="mha7b_decode_128k",
                     help="comma-separated extra decode workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-gated", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -335,6 +376,13 @@ def main():
         line["prefill"] = {"workload": p["workload"], "ms": round(p["seconds"] * 1e3, 3),
                            "tflops": round(p["tflops"], 2), "mfma_frac": round(p["mfma_frac"], 4),
                            "peak_tflops": BF16_DENSE_TFLOPS, "algorithmic_tflop": round(p["algorithmic_tflop"], 4)}
+    if not args.no_gated:
+        gw = WL.WORKLOADS["llama3_8b_gated_32k"]
+        gr = bench_gated(gw)
+        line["gated"] = {"workload": gr["workload"], "ms": round(gr["seconds"] * 1e3, 3),
+                         "ms_median": round(gr["median_s"] * 1e3, 3), "tflops": round(gr["tflops"], 2),
+                         "mfma_frac": round(gr["mfma_frac"], 4), "peak_tflops": BF16_DENSE_TFLOPS,
+                         "algorithmic_tflop": round(gr["algorithmic_tflop"], 4)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(line), flush=True)

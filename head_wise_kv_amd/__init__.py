@@ -26,7 +26,7 @@ ERROR_NAMES = {DUO_EINVAL: "DUO_EINVAL", DUO_EUNSUPPORTED: "DUO_EUNSUPPORTED", D
 # Every entry point declared in include/duo.h.
 EXPORTS = ("duo_cache_bytes", "duo_cache_payload_bytes", "duo_cache_init", "duo_append", "duo_decode",
            "duo_decode_append", "duo_prefill_chunk", "duo_cache_seq_len", "duo_cache_head_view", "duo_cache_free",
-           "duo_last_error")
+           "duo_last_error", "duo_gated_attention")
 
 
 class DuoError(RuntimeError):
@@ -40,6 +40,11 @@ class duo_config(ctypes.Structure):
                 ("d_head", ctypes.c_int32), ("T_cap", ctypes.c_int64), ("sink", ctypes.c_int32),
                 ("recent", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("retrieval_mask", ctypes.POINTER(ctypes.c_uint8))]
+
+
+class duo_gated_shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("n_q", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("d_head", ctypes.c_int32),
+                ("N", ctypes.c_int64), ("sink", ctypes.c_int32), ("recent", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 def _load():
@@ -59,6 +64,7 @@ def _load():
     lib.duo_cache_head_view.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(vp),
                                         ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(i64),
                                         ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.duo_gated_attention.argtypes = [ctypes.POINTER(duo_gated_shape), vp, vp, vp, vp, vp, ctypes.c_float, vp]
     lib.duo_cache_free.argtypes = [vp]
     lib.duo_cache_free.restype = None
     lib.duo_last_error.argtypes = []
@@ -254,3 +260,39 @@ class DuoCache:
             pos = seg.cpu().view(torch.int32).reshape(self.B, rows)
         assert es in (2, 4)
         return out[0], out[1], pos
+
+
+def gated_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor, sink: int, recent: int,
+                    out: Optional[torch.Tensor] = None, scale: Optional[float] = None, stream=None) -> torch.Tensor:
+    """Head-gated forward (duo_gated_attention): per query head,
+    alpha[kv head] * causal attention + (1 - alpha[kv head]) * sink + window
+    attention over one whole sequence.  q: [B][n_q][N][d]; k, v: [B][n_kv][N][d]
+    (bf16 or float32, contiguous, one device); alpha: float32 [n_kv] on the
+    same device."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B][n_q][N][d]; k and v [B][n_kv][N][d]")
+    B, n_q, N, d = q.shape
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    n_kv = k.shape[1]
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    if alpha.dtype != torch.float32 or tuple(alpha.shape) != (n_kv,):
+        raise ValueError(f"alpha must be float32 [{n_kv}]")
+    if any(t.device != q.device for t in (k, v, alpha)):
+        raise ValueError("q, k, v and alpha must be on one device")
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    shape = duo_gated_shape(B, n_q, n_kv, d, N, sink, recent, _dtype_code(q.dtype))
+    sc = float(d ** -0.5 if scale is None else scale)
+    _check(lib.duo_gated_attention(ctypes.byref(shape), ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                   ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(alpha.data_ptr()),
+                                   ctypes.c_void_p(out.data_ptr()), sc, _stream_handle(stream)))
+    return out

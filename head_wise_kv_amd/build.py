@@ -12,17 +12,18 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libduo.so")
 ARCH = "gfx950"
-SOURCES = ["duo_host.cpp", "duo_kernels.hip", "duo_prefill.hip"]
+SOURCES = ["duo_host.cpp", "duo_kernels.hip", "duo_prefill.hip", "duo_gated.hip"]
 
 # Packed fp32 VALU ops are turned off for device code (the host pass warns that
 # it does not know the feature; that is expected).
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
-# Per-source device flags.  The prefill kernel's MFMA results (scores and the
+# Per-source device flags.  The prefill and gated kernels' MFMA results (scores and the
 # output accumulators) are read by the softmax and the final scaling on the
 # vector ALU; asking for the VGPR form of MFMA keeps them out of the
 # accumulation registers, which saves a read-out and a zero fill per tile.
-SOURCE_FLAGS = {"duo_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {"duo_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "duo_gated.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -440,6 +441,47 @@ int duo_cache_head_view(const duo_cache* c, int layer, int kv_head, int* is_retr
   if (k_base) *k_base = (ret ? p.k_ret : p.k_str) + (size_t)ci * slots * rb;
   if (v_base) *v_base = (ret ? p.v_ret : p.v_str) + (size_t)ci * slots * rb;
   if (pos) *pos = ret ? nullptr : p.pos + (size_t)ci * slots;
+  return ok();
+}
+
+int duo_gated_attention(const duo_gated_shape* shape, const void* q, const void* k, const void* v,
+                        const float* alpha, void* out, float scale, void* stream) {
+  if (!shape) return fail(DUO_EINVAL, "shape is NULL");
+  const duo_gated_shape& sh = *shape;
+  if (sh.B < 1 || sh.n_q < 1 || sh.n_kv < 1)
+    return fail(DUO_EINVAL, "B, n_q, n_kv must be >= 1 (got %d, %d, %d)", sh.B, sh.n_q, sh.n_kv);
+  if (sh.n_q % sh.n_kv != 0) return fail(DUO_EINVAL, "n_q (%d) must be a multiple of n_kv (%d)", sh.n_q, sh.n_kv);
+  if (sh.d_head != 64 && sh.d_head != 128) return fail(DUO_EUNSUPPORTED, "d_head %d not built (64, 128)", sh.d_head);
+  if (sh.dtype != DUO_F32 && sh.dtype != DUO_BF16) return fail(DUO_EUNSUPPORTED, "dtype %d", sh.dtype);
+  if (sh.N < 1) return fail(DUO_EINVAL, "N must be >= 1 (got %lld)", (long long)sh.N);
+  if (sh.sink < 0 || sh.recent < 1) return fail(DUO_EINVAL, "need sink >= 0 and recent >= 1");
+  if (sh.N + (int64_t)sh.recent > INT32_MAX)
+    return fail(DUO_EINVAL, "N + recent must fit int32 (positions are int32)");
+  if (!q || !k || !v || !alpha || !out) return fail(DUO_EINVAL, "q, k, v, alpha or out is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(DUO_EINVAL, "q, k, v and out must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(alpha) & 3u) != 0) return fail(DUO_EINVAL, "alpha must be 4-byte aligned");
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(DUO_EINVAL, "scale must be finite and > 0");
+  const int g = sh.n_q / sh.n_kv;
+  duo::GatedArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.out = out;
+  a.B = sh.B;
+  a.n_q = sh.n_q;
+  a.n_kv = sh.n_kv;
+  a.S = sh.sink;
+  a.W = sh.recent;
+  a.N = sh.N;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const int64_t rows = duo::gated_rows_per_item(sh.dtype, g);
+  const int64_t q_tiles = ceil_div(sh.N, rows);
+  if (q_tiles * sh.B * sh.n_q > INT32_MAX) return fail(DUO_EUNSUPPORTED, "too many work items for one launch");
+  a.q_tiles = (int)q_tiles;
+  const hipError_t e = duo::launch_gated(a, sh.dtype, sh.d_head, g, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gated forward launch");
   return ok();
 }
 

@@ -1,5 +1,6 @@
 // Internal declarations shared by the host library (duo_host.cpp) and the HIP
-// kernels (duo_kernels.hip).  Not part of the public ABI.
+// kernels (duo_kernels.hip, duo_prefill.hip, duo_gated.hip).  Not part of the
+// public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -84,7 +85,22 @@ struct PrefillArgs {
   int items_ret;      // B * n_ret * (g / heads per item) * q_tiles (retrieval items come first)
 };
 
-// Launchers (duo_kernels.hip).  dtype: 0 = fp32, 1 = bf16.
+// Head-gated forward over one whole sequence (no cache): row t of query head
+// h gets alpha[h / g] * causal attention + (1 - alpha[h / g]) * sink + window
+// attention.
+struct GatedArgs {
+  const void* q;       // [B][n_q][N][d]
+  const void* k;       // [B][n_kv][N][d]
+  const void* v;
+  const float* alpha;  // [n_kv]
+  void* out;           // [B][n_q][N][d]
+  int B, n_q, n_kv, S, W;
+  int64_t N;           // tokens, positions 0 .. N-1
+  float scale_log2;
+  int q_tiles;         // ceil(N / rows per work item)
+};
+
+// Launchers (duo_kernels.hip, duo_prefill.hip, duo_gated.hip).  dtype: 0 = fp32, 1 = bf16.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, int dtype, int d, hipStream_t s);
 // Split phase over `blocks` work items (retrieval heads' items first), then
@@ -95,5 +111,8 @@ int64_t decode_round_rows(int dtype, int d, int g);
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int g, hipStream_t s);
 // Query rows and query heads one prefill work item covers.
 void prefill_plan(int dtype, int d, int g, int* rows_per_item, int* heads_per_item);
+hipError_t launch_gated(const GatedArgs& a, int dtype, int d, int g, hipStream_t s);
+// Query rows one gated-forward work item covers.
+int gated_rows_per_item(int dtype, int g);
 
 }  // namespace duo

@@ -35,6 +35,7 @@
 //
 // fp32: a plain vector-ALU path (one wavefront per query row) kept for
 // completeness of the dtype surface; it is not tuned.
+#include "duo_attn_tile.h"
 #include "duo_internal.h"
 
 #include <hip/hip_runtime.h>
@@ -44,49 +45,14 @@
 namespace duo {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-
-constexpr int kPfRowWaves = 2;                    // wavefronts per key half (one 64-row block each)
-constexpr int kPfHalves = 2;                      // key halves: even / odd key tiles
-constexpr int kPfThreads = 64 * kPfRowWaves * kPfHalves;
-constexpr int kPfRowsPerWave = 64;                // query rows per wavefront
-constexpr int kBN = 64;                           // keys per tile
-
-// Integer min / max by plain comparison (kept off any floating-point path).
-__device__ __forceinline__ int64_t min64(int64_t x, int64_t y) { return x < y ? x : y; }
-__device__ __forceinline__ int64_t max64(int64_t x, int64_t y) { return x > y ? x : y; }
-
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-  bf2 v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float max3(float x, float y, float z) { return fmaxf(fmaxf(x, y), z); }
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-constexpr bf16x2_t kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
-
 __device__ __forceinline__ bool visible(int64_t kp, int64_t t, bool ret, int S, int W) {
   return kp >= 0 && kp <= t && (ret || kp < S || kp >= t - W + 1);
 }
 
-// Visibility of a key as an interval of chunk rows: the key at absolute
-// position kp is seen by the rows i (absolute position P + i) with
-// lo <= i <= lo + span, where lo = kp - P and span is unbounded for keys under
-// the causal mask alone (retrieval heads, sink keys) and W - 1 otherwise (the
-// local window).  The test is one unsigned compare: (unsigned)(i - lo) <= span.
-// Keys that do not exist get lo = -1, span = 0, which no row i >= 0 passes.
-// Positions stay below 2^31, so every difference fits in 32 bits.
-struct KeySpan {
-  int32_t lo;
-  uint32_t span;
-};
+// The rows of the chunk (absolute position P + i) that see the key at absolute
+// position kp: i >= kp - P, for every later row under the causal mask alone
+// (retrieval heads, sink keys) and for W rows otherwise (the local window).
+// Keys that do not exist (kp < 0) are seen by no row.
 __device__ __forceinline__ KeySpan key_span(int64_t kp, int64_t P, bool ret, int S, int W) {
   KeySpan k;
   if (kp < 0) {
@@ -98,12 +64,6 @@ __device__ __forceinline__ KeySpan key_span(int64_t kp, int64_t P, bool ret, int
   }
   return k;
 }
-__device__ __forceinline__ bool sees(int32_t i, int32_t lo, uint32_t span) { return (uint32_t)(i - lo) <= span; }
-
-// Skip the O rescale until the running max has grown by more than this many
-// log2 units; probabilities then stay below 2^kRescaleSlack, well inside bf16
-// and fp32 range.
-constexpr float kRescaleSlack = 8.f;
 
 // Key tile sources.
 enum : int { SRC_CACHE_LINEAR = 0, SRC_CACHE_SLOTS = 1, SRC_CHUNK = 2 };
@@ -151,22 +111,6 @@ __device__ __forceinline__ TileRanges plan_tiles(const PrefillArgs& a, bool ret,
 
 // ------------------------------------------------------------------ bf16 MFMA path
 
-template <int D>
-struct PfShape {
-  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  static constexpr int TILE_BYTES = kBN * D * 2;    // one K (or V) tile
-  static constexpr int DMA_PER_TILE = TILE_BYTES / 1024;  // 1 KB per wavefront-wide direct load
-  static constexpr int KSTEPS = D / 16;             // MFMA k-steps over d for S^T
-  static constexpr int DT = D / 32;                 // 32-row tiles of O^T over d
-  static_assert(DMA_PER_TILE % kPfRowWaves == 0, "tile loads split over the wavefronts");
-  // K rows: chunk c of key r sits at chunk slot c ^ swz_k(r) (A-operand reads
-  // of 16 consecutive keys at one chunk hit 16 distinct bank groups).
-  __device__ static __forceinline__ int swz_k(int r) { return CPR == 16 ? (r & 15) : ((r >> 1) & 7); }
-  // V rows: chunk c of key r at c ^ swz_v(r) (a transpose read of 4 rows x
-  // 4 chunks by 32 lanes hits 16 distinct bank groups).
-  __device__ static __forceinline__ int swz_v(int r) { return CPR == 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
-};
-
 struct PfItem {
   int b, kvh, cidx, h_first, qt;
   bool ret;
@@ -199,239 +143,6 @@ __device__ __forceinline__ PfItem pf_item(const PrefillArgs& a, int g, int hpi) 
   return w;
 }
 
-// Direct global->LDS copies of a 64-row tile (K or V) through a buffer
-// resource.  The tile is 1 KB pieces; piece n covers LDS bytes
-// [n*1024, n*1024+1024), lane i writing 16 bytes at n*1024 + i*16, i.e. row
-// (n*64 + i) / CPR at chunk slot (n*64 + i) % CPR; the global chunk it fetches
-// is that slot XOR the row's swizzle.  The byte offset of that chunk within the
-// tile depends only on (n, lane), so it is computed once per kernel; each tile
-// only rebuilds the scalar resource (base = first row, size = rows present).
-// Rows past the end are out of range for the resource and read as zero.
-template <int D, bool IS_V>
-__device__ __forceinline__ uint32_t dma_offset(int n, int lane) {
-  using SH = PfShape<D>;
-  const int piece = n * 64 + lane;
-  const int r = piece / SH::CPR;
-  const int c = (piece % SH::CPR) ^ (IS_V ? SH::swz_v(r) : SH::swz_k(r));
-  return (uint32_t)(r * (D * 2) + c * 16);
-}
-
-constexpr int kBufferRsrcWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
-
-// Issue this wavefront's pieces (wave, wave + kPfRowWaves, ...) of one tile.
-template <int N>
-__device__ __forceinline__ void dma_pieces(__amdgpu_buffer_rsrc_t rsrc, char* lds_tile, int wave,
-                                           const uint32_t (&off)[N]) {
-#pragma unroll
-  for (int j = 0; j < N; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc, (__attribute__((address_space(3))) void*)(lds_tile + (wave + kPfRowWaves * j) * 1024), 16, off[j], 0, 0,
-        0);
-}
-
-// Values that are the same in every lane, moved to scalar registers (a buffer
-// resource must live there).
-__device__ __forceinline__ int64_t uniform64(int64_t x) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-__device__ __forceinline__ const char* uniform_ptr(const char* p) {
-  return reinterpret_cast<const char*>(uniform64(reinterpret_cast<int64_t>(p)));
-}
-
-// ---- per-tile pieces of the MFMA path (one wavefront, 64 query rows = two
-// 32-row N tiles nt, one 64-key tile = two 32-key halves ct)
-
-// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
-
-// S^T = K Q^T for the keys ct*32 .. ct*32+31 of the tile: s[nt] register r of
-// lane (n, hf) is the score of key ct*32 + 8*(r/4) + 4*hf + r%4 and query
-// 32*nt + n.
-template <int D>
-__device__ __forceinline__ void pf_scores(f32x16_t (&s)[2], const bf16x8_t (&qb)[2][D / 16], const char* kt, int ct,
-                                          int lane) {
-  using SH = PfShape<D>;
-  const int key = ct * 32 + (lane & 31);
-  const int hf = lane >> 5;
-#pragma unroll
-  for (int ks = 0; ks < SH::KSTEPS; ++ks) {
-    const int c = 2 * ks + hf;
-    const u32x4_t av = *reinterpret_cast<const u32x4_t*>(kt + key * (SH::CPR * 16) + ((c ^ SH::swz_k(key)) * 16));
-    const bf16x8_t aop = __builtin_bit_cast(bf16x8_t, av);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-      s[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qb[nt][ks], ks == 0 ? f32x16_t{} : s[nt], 0, 0, 0);
-  }
-}
-
-// Scores of keys a row does not see (half ct of the tile) become -inf.
-__device__ __forceinline__ void pf_mask(f32x16_t (&s)[2], const int32_t* klo, const uint32_t* kspan,
-                                        const int32_t (&iq)[2], int ct, int lane) {
-  const int hf = lane >> 5;
-#pragma unroll
-  for (int r4 = 0; r4 < 4; ++r4) {
-    const int key0 = ct * 32 + 8 * r4 + 4 * hf;  // keys key0 .. key0+3 in registers 4*r4 .. 4*r4+3
-    const int4 lo4 = *reinterpret_cast<const int4*>(klo + key0);
-    const uint4 sp4 = *reinterpret_cast<const uint4*>(kspan + key0);
-    const int32_t lo[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
-    const uint32_t sp[4] = {sp4.x, sp4.y, sp4.z, sp4.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        if (!sees(iq[nt], lo[j], sp[j])) s[nt][4 * r4 + j] = -INFINITY;
-  }
-}
-
-// Online softmax of one half: updates the running max m (lazily: a row's
-// max moves only when it has grown past the slack), the running sum l, and
-// returns P^T as bf16 pairs pb[nt][k-step st][dword] plus the factor
-// alpha[nt] the accumulators must be scaled by; the result says whether any
-// lane's alpha differs from 1.
-__device__ __forceinline__ bool pf_softmax(const f32x16_t (&s)[2], float (&m_run)[2], float (&l_run)[2],
-                                           uint32_t (&pb)[2][2][4], float (&alpha)[2], float scale_log2) {
-  bool grow = false;
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const f32x16_t& x = s[nt];
-    const float v = fmaxf(max3(max3(x[0], x[1], x[2]), max3(x[3], x[4], x[5]), max3(x[6], x[7], x[8])),
-                          max3(max3(x[9], x[10], x[11]), max3(x[12], x[13], x[14]), x[15]));
-    const float mx = fmaxf(v, __shfl_xor(v, 32)) * scale_log2;
-    const bool g = mx > m_run[nt] + kRescaleSlack;
-    grow |= g;
-    const float m_new = g ? mx : m_run[nt];  // mx > m_run here
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    alpha[nt] = fast_exp2(m_run[nt] - m_use);
-    m_run[nt] = m_new;
-    // the row sum adds the bf16-rounded probabilities, the same values the
-    // P V product uses
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = fast_exp2(fmaf(x[r], scale_log2, -m_use));
-      const float p1 = fast_exp2(fmaf(x[r + 1], scale_log2, -m_use));
-      const uint32_t pp = pack_bf16(p0, p1);
-      pb[nt][r >> 3][(r & 7) >> 1] = pp;
-      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), kOnesBf16x2, psum, false);
-    }
-    l_run[nt] = l_run[nt] * alpha[nt] + psum;
-  }
-  return __builtin_amdgcn_ballot_w64(grow) != 0;
-}
-
-// Keeps the probabilities computed where they are written in the source: an
-// empty asm statement that reads them (it emits no instruction), so the
-// compiler cannot sink their computation past the branch that follows.
-__device__ __forceinline__ void pf_pin(const uint32_t (&pb)[2][2][4], const float (&l_run)[2]) {
-  asm volatile("" ::"v"(l_run[0]), "v"(l_run[1]));
-  asm volatile("" ::"v"(pb[0][0][0]), "v"(pb[0][0][1]), "v"(pb[0][0][2]), "v"(pb[0][0][3]), "v"(pb[0][1][0]),
-               "v"(pb[0][1][1]), "v"(pb[0][1][2]), "v"(pb[0][1][3]), "v"(pb[1][0][0]), "v"(pb[1][0][1]),
-               "v"(pb[1][0][2]), "v"(pb[1][0][3]), "v"(pb[1][1][0]), "v"(pb[1][1][1]), "v"(pb[1][1][2]),
-               "v"(pb[1][1][3]));
-}
-
-template <int DT>
-__device__ __forceinline__ void pf_rescale(f32x16_t (&o)[DT][2], const float (&alpha)[2]) {
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][nt][r] *= alpha[nt];
-}
-
-// O^T += V^T P^T for the keys of half ct.  V^T operands come from transpose
-// reads of the row-major V tile: lane (g16 = lane/16, i16 = lane%16) reads
-// row kb + i16/4 at columns dt*32 + 16*(g16%2) + 4*(i16%4) and receives
-// V[kb + 0..3][its d].
-template <int D>
-__device__ __forceinline__ void pf_pv(f32x16_t (&o)[D / 32][2], const uint32_t (&pb)[2][2][4], const char* vt,
-                                      int ct, int lane) {
-  using SH = PfShape<D>;
-  const int hf = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
-#pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    bf16x8_t bop[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const u32x4_t bw = {pb[nt][st][0], pb[nt][st][1], pb[nt][st][2], pb[nt][st][3]};
-      bop[nt] = __builtin_bit_cast(bf16x8_t, bw);
-    }
-#pragma unroll
-    for (int dt = 0; dt < SH::DT; ++dt) {
-      i16x4_t half[2];
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        const int row = ct * 32 + 16 * st + 8 * rr + 4 * hf + (i16 >> 2);
-        const int col = dt * 32 + 16 * (g16 & 1) + 4 * (i16 & 3);
-        const int c = col >> 3;
-        const char* p = vt + row * (SH::CPR * 16) + ((c ^ SH::swz_v(row)) * 16) + (col & 7) * 2;
-        half[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
-      }
-      const u32x2_t h0 = __builtin_bit_cast(u32x2_t, half[0]);
-      const u32x2_t h1 = __builtin_bit_cast(u32x2_t, half[1]);
-      const u32x4_t aw = {h0[0], h0[1], h1[0], h1[1]};
-      const bf16x8_t aop = __builtin_bit_cast(bf16x8_t, aw);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        o[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop[nt], o[dt][nt], 0, 0, 0);
-    }
-  }
-}
-
-// One 64-key tile, software pipelined over its halves so that MFMA work of
-// one half overlaps the softmax of the other:
-//   S(0) | mask(0) | S(1) + softmax(0) | rescale(0), mask(1) | P V(0) + softmax(1) | rescale(1) | P V(1)
-// The masks and rescales are wavefront-uniform branches between the
-// overlapped regions.
-template <int D>
-__device__ __forceinline__ void pf_tile(f32x16_t (&o)[D / 32][2], float (&m_run)[2], float (&l_run)[2],
-                                        const bf16x8_t (&qb)[2][D / 16], const char* kt, const char* vt,
-                                        bool masked, const int32_t* klo, const uint32_t* kspan,
-                                        const int32_t (&iq)[2], float scale_log2, int lane) {
-  constexpr int KSTEPS = D / 16, DT = D / 32;
-  constexpr int kMfmaHalf = 2 * KSTEPS;  // MFMAs per half for S, and 2 * 2 * DT for P V (equal for both)
-  static_assert(2 * 2 * DT == kMfmaHalf, "S and P V halves carry equal MFMA counts");
-  constexpr int kValuPerMfma = 8;
-  f32x16_t s0[2], s1[2];
-  uint32_t p0[2][2][4], p1[2][2][4];
-  float a0[2], a1[2];
-
-  pf_scores<D>(s0, qb, kt, 0, lane);
-  __builtin_amdgcn_sched_barrier(0);
-  if (masked) pf_mask(s0, klo, kspan, iq, 0, lane);
-  __builtin_amdgcn_sched_barrier(0);
-  pf_scores<D>(s1, qb, kt, 1, lane);
-  const bool g0 = pf_softmax(s0, m_run, l_run, p0, a0, scale_log2);
-#pragma unroll
-  for (int i = 0; i < kMfmaHalf; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerMfma, 0);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  pf_pin(p0, l_run);
-  if (g0) pf_rescale<DT>(o, a0);
-  if (masked) pf_mask(s1, klo, kspan, iq, 1, lane);
-  __builtin_amdgcn_sched_barrier(0);
-  pf_pv<D>(o, p0, vt, 0, lane);
-  const bool g1 = pf_softmax(s1, m_run, l_run, p1, a1, scale_log2);
-#pragma unroll
-  for (int i = 0; i < kMfmaHalf; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerMfma, 0);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  pf_pin(p1, l_run);
-  if (g1) pf_rescale<DT>(o, a1);
-  __builtin_amdgcn_sched_barrier(0);
-  pf_pv<D>(o, p1, vt, 1, lane);
-  // all V operand reads of the last half first, then its MFMAs
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4 * DT, 0);
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMfmaHalf, 0);
-}
 
 template <int D>
 __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a, int g, int hpi) {

@@ -150,6 +150,32 @@ int duo_cache_head_view(const duo_cache* c, int layer, int kv_head, int* is_retr
                         void** k_base, void** v_base, int32_t** pos, int64_t* n_slots,
                         int64_t* row_bytes, int64_t* head_stride_bytes, int64_t* pos_stride);
 
+/* Shape of a head-gated forward: one whole sequence of N tokens at positions
+ * 0 .. N-1, no cache.  d_head in {64, 128}; n_q a multiple of n_kv (any group
+ * size); S = sink >= 0; W = recent >= 1; N >= 1 and N + W < 2^31. */
+typedef struct {
+  int32_t B, n_q, n_kv, d_head;
+  int64_t N;
+  int32_t sink, recent;
+  int32_t dtype; /* duo_dtype of q, k, v and out; accumulation is fp32 */
+} duo_gated_shape;
+
+/* Head-gated attention forward, the pass through which head identification
+ * trains its gates ("DuoAttention: Dual Retrieval & Streaming Heads Guide",
+ * section 3, item 2: a continuous gate per head mixes full attention and
+ * streaming attention over the same queries, keys and values).  For query
+ * head h of KV head k = h / g and the row at position t:
+ *   out = alpha[k] * A_full + (1 - alpha[k]) * A_stream,
+ * where A_full = softmax(scale q K^T) V over the keys j <= t (causal) and
+ * A_stream the same over the keys j <= t with j < S or j >= t - W + 1 (the
+ * sinks and the window the cache keeps for a streaming head).  One gate per
+ * KV head: the roles it relaxes are per KV head.  q, out: device
+ * [B][n_q][N][d]; k, v: device [B][n_kv][N][d]; alpha: device float32
+ * [n_kv], used as given (not clipped to [0, 1]).  Needs no cache and no
+ * workspace; enqueued on `stream`. */
+int duo_gated_attention(const duo_gated_shape* shape, const void* q, const void* k, const void* v,
+                        const float* alpha, void* out, float scale, void* stream);
+
 /* Release the host handle (device memory is the caller's). NULL is ignored. */
 void duo_cache_free(duo_cache* c);
 

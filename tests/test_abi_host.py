@@ -95,3 +95,29 @@ def test_calls_on_null_handle_fail_cleanly():
     assert H.lib.duo_decode(None, 0, None, None, 1.0, None, 0, None) == H.DUO_EINVAL
     assert H.lib.duo_decode_append(None, 0, None, None, None, None, 1.0, None, 0, None) == H.DUO_EINVAL
     H.lib.duo_cache_free(None)
+
+
+GATED_BAD = [
+    (dict(n_q=6, n_kv=4), H.DUO_EINVAL),
+    (dict(B=0), H.DUO_EINVAL),
+    (dict(d_head=96), H.DUO_EUNSUPPORTED),
+    (dict(N=0), H.DUO_EINVAL),
+    (dict(sink=-1), H.DUO_EINVAL),
+    (dict(recent=0), H.DUO_EINVAL),
+    (dict(N=2 ** 31 - 10, recent=64), H.DUO_EINVAL),
+    (dict(dtype=7), H.DUO_EUNSUPPORTED),
+    (dict(), H.DUO_EINVAL),  # valid shape, NULL tensors
+]
+
+
+@pytest.mark.parametrize("over,code", GATED_BAD)
+def test_gated_validation_codes(over, code):
+    """duo_gated_attention validates its shape and pointers before any launch."""
+    base = dict(B=1, n_q=8, n_kv=4, d_head=128, N=100, sink=4, recent=16, dtype=H.DUO_BF16)
+    base.update(over)
+    shape = H.duo_gated_shape(base["B"], base["n_q"], base["n_kv"], base["d_head"], base["N"], base["sink"],
+                              base["recent"], base["dtype"])
+    rc = H.lib.duo_gated_attention(ctypes.byref(shape), None, None, None, None, None, 1.0, None)
+    assert rc == code, H.lib.duo_last_error()
+    assert H.lib.duo_last_error()
+    assert H.lib.duo_gated_attention(None, None, None, None, None, None, 1.0, None) == H.DUO_EINVAL
