@@ -359,25 +359,24 @@ __device__ __forceinline__ void tile_scores(DecodeState<BF16, D, G>& st, float (
 #pragma unroll
     for (int cc = 0; cc < C::CPL; ++cc)
       k[cc] = *reinterpret_cast<const uint4*>(kt + row * C::ROWB + (((s + 8 * cc) ^ dec_swz<C::CPR>(row)) * 16));
+    // the HW dot products advance together (independent chains for the ALU)
+    float acc[HW];
 #pragma unroll
-    for (int h = 0; h < HW; ++h) {
-      float acc = 0.f;
+    for (int h = 0; h < HW; ++h) acc[h] = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < C::CPL; ++cc) {
-        if constexpr (BF16) {
-          acc = dot2_bf16(q[h][cc].x, k[cc].x, acc);
-          acc = dot2_bf16(q[h][cc].y, k[cc].y, acc);
-          acc = dot2_bf16(q[h][cc].z, k[cc].z, acc);
-          acc = dot2_bf16(q[h][cc].w, k[cc].w, acc);
-        } else {
-          acc = fmaf(__uint_as_float(q[h][cc].x), __uint_as_float(k[cc].x), acc);
-          acc = fmaf(__uint_as_float(q[h][cc].y), __uint_as_float(k[cc].y), acc);
-          acc = fmaf(__uint_as_float(q[h][cc].z), __uint_as_float(k[cc].z), acc);
-          acc = fmaf(__uint_as_float(q[h][cc].w), __uint_as_float(k[cc].w), acc);
+    for (int cc = 0; cc < C::CPL; ++cc) {
+      const uint32_t kw[4] = {k[cc].x, k[cc].y, k[cc].z, k[cc].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < HW; ++h) {
+          const uint32_t qw[4] = {q[h][cc].x, q[h][cc].y, q[h][cc].z, q[h][cc].w};
+          if constexpr (BF16) acc[h] = dot2_bf16(qw[i], kw[i], acc[h]);
+          else acc[h] = fmaf(__uint_as_float(qw[i]), __uint_as_float(kw[i]), acc[h]);
         }
-      }
-      sc[j][h] = row8_sum(acc);
     }
+#pragma unroll
+    for (int h = 0; h < HW; ++h) sc[j][h] = row8_sum(acc[h]);
   }
   // rows past the item's end (only in its last tiles), and a row whose token
   // is being evicted (excl, tile-relative; -1 if none), score -inf
@@ -493,6 +492,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float w_m[G][SLOTS * 8], w_l[G][SLOTS * 8], w_w[G][SLOTS * 8],
       w_lw[G][SLOTS * 8];
   __shared__ float w_mt[G];
+  // the group's queries and the new token's K and V rows, loaded by direct loads
+  constexpr int QSTAGE = (G * C::ROWB + 1023) / 1024 * 1024;
+  constexpr int NSTAGE = (C::ROWB + 1023) / 1024 * 1024;
+  static_assert(QSTAGE / 1024 + 2 <= kDecWaves, "one staging piece per wavefront");
+  __shared__ __attribute__((aligned(1024))) char stage[QSTAGE + 2 * NSTAGE];
   char* const rings[kRingUnits] = {ring0, ring1, ring2, ring3};  // indexed by constants only
   auto ring_at = [&](int i) -> char* { return i == 0 ? ring0 : i == 1 ? ring1 : i == 2 ? ring2 : ring3; };
 
@@ -506,68 +510,65 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   const int64_t nrounds = ((w.r1 - w.r0 + TR - 1) / TR + SLOTS - 1) / SLOTS;
   const size_t q_off = ((size_t)w.b * a.n_q + (size_t)w.kvh * G) * D;  // first query of the group
 
-  // this wavefront's HW queries, in the lane's slice layout; loaded (and
-  // waited for) before any direct load is in flight
-  uint4 q[HW][C::CPL];
-  {
-    const char* qb = static_cast<const char*>(a.q) + (q_off + (size_t)hg * HW * D) * C::ES;
-#pragma unroll
-    for (int h = 0; h < HW; ++h)
-#pragma unroll
-      for (int c2 = 0; c2 < C::CPL; ++c2) q[h][c2] = ld16(qb + (size_t)h * C::ROWB + (s + 8 * c2) * 16);
-  }
-  // fused append: the last item of every head adds the new token; wavefront 0
-  // holds it (lanes 0..CPR-1 its K chunks, CPR..2*CPR-1 its V chunks)
+  // fused append: the last item of every head adds the new token
   const bool add_new = a.new_k != nullptr && w.part == w.nparts - 1;
   const bool ret_head = w.hh < (int64_t)a.B * a.n_ret;
-  uint4 nkv = make_uint4(0, 0, 0, 0);
-  if (add_new && wave == 0 && lane < 2 * C::CPR) {
-    const size_t src = ((size_t)w.b * a.n_kv + w.kvh) * C::ROWB + (size_t)(lane % C::CPR) * 16;
-    nkv = ld16((lane < C::CPR ? a.new_k : a.new_v) + src);
-  }
   // streaming slot masked in the held rows (its token is evicted by the new one)
   const int64_t excl_row = (a.new_k != nullptr && !ret_head) ? a.excl_str : -1;
-  // per-lane byte offsets (within a tile) of this wavefront's load pieces, and
-  // the tile (slot) each piece belongs to
+  // per-lane byte offset, within a round of rows, of this wavefront's load
+  // pieces: piece n of a unit covers LDS bytes [n*1024, n*1024+1024), lane i
+  // byte n*1024 + 16 i, i.e. row (n*1024 + 16 i) / ROWB of the round at a
+  // chunk slot that is the row's swizzle applied to the global chunk
   uint32_t poff[kPiecesPerWave];
-  int pslot[kPiecesPerWave];
 #pragma unroll
   for (int j = 0; j < kPiecesPerWave; ++j) {
-    const int n = wave + kDecWaves * j;
-    const int off = n * 1024 + lane * 16;
-    pslot[j] = (n * 1024) / C::SLOT_BYTES;
-    const int o = off % C::SLOT_BYTES;
-    const int r = o / C::ROWB;
-    const int c = ((o % C::ROWB) / 16) ^ dec_swz<C::CPR>(r);
+    const int off = (wave + kDecWaves * j) * 1024 + lane * 16;
+    const int r = off / C::ROWB;  // row of the round; a slot's tile starts at an even row (TR is even)
+    const int c = ((off % C::ROWB) / 16) ^ dec_swz<C::CPR>(r % TR);
     poff[j] = (uint32_t)(r * C::ROWB + c * 16);
   }
-  // Rows past the item's end read as zero; clearing the ring once means no
-  // stale bit pattern (possibly a NaN) ever meets a zero probability.
-#pragma unroll
-  for (int x = 0; x < kRingUnits; ++x)
-    for (int off = threadIdx.x * 16; off < kUnitBytes; off += kDecodeThreads * 16)
-      *reinterpret_cast<uint4*>(rings[x] + off) = make_uint4(0, 0, 0, 0);
-  wait_vmcnt<0>();
-  __syncthreads();
 
   // Issue unit `uu` (round uu / 2; K rows if uu is even, else V rows) into
-  // `dst`.  Past the last round every piece is out of range (nothing is read)
-  // but still issued, so each wavefront has the same number of loads per unit.
+  // `dst`: the round's rows are contiguous, so one buffer resource covers
+  // them, sized to the rows the item still has.  Past the item's end every
+  // piece is out of range (it reads nothing and writes zeros to LDS) but is
+  // still issued, so each wavefront has the same number of loads per unit,
+  // and every byte of a unit is written before it is read.
   auto issue = [&](int64_t uu, char* dst) {
-    const int64_t rnd = uu >> 1;
-    const char* src = (uu & 1) ? w.vbase : w.kbase;
+    const int64_t row0 = w.r0 + (uu >> 1) * (int64_t)C::ROUND_ROWS;
+    const int64_t left = w.r1 - row0;
+    const int rows = (int)(left <= 0 ? 0 : (left > C::ROUND_ROWS ? C::ROUND_ROWS : left));
+    const char* src = ((uu & 1) ? w.vbase : w.kbase) + (size_t)(rows > 0 ? row0 : 0) * C::ROWB;
+    const i32x4_t rs = dec_rsrc(src, rows * C::ROWB);
 #pragma unroll
-    for (int j = 0; j < kPiecesPerWave; ++j) {
-      const int64_t row0 = w.r0 + (rnd * SLOTS + pslot[j]) * (int64_t)TR;
-      const int64_t left = w.r1 - row0;
-      const int rows = rnd < nrounds ? (int)(left < 0 ? 0 : (left > TR ? TR : left)) : 0;
-      dec_dma(dec_rsrc(src + (size_t)(rows > 0 ? row0 : 0) * C::ROWB, rows * C::ROWB),
-              dst + (wave + kDecWaves * j) * 1024, poff[j]);
-    }
+    for (int j = 0; j < kPiecesPerWave; ++j) dec_dma(rs, dst + (wave + kDecWaves * j) * 1024, poff[j]);
   };
+  // The first unit, then the group's queries and the new token's K and V rows
+  // into the staging area (one load piece per wavefront for the first
+  // wavefronts), then two more units.  Unit 0's wait below covers the staging
+  // loads, which were issued before units 1 and 2.
   issue(0, ring0);
+  {
+    constexpr int NQP = QSTAGE / 1024;  // query pieces
+    if (wave < NQP) {
+      const char* qsrc = static_cast<const char*>(a.q) + q_off * C::ES;
+      dec_dma(dec_rsrc(qsrc, G * C::ROWB), stage + wave * 1024, (uint32_t)(wave * 1024 + lane * 16));
+    } else if (add_new && wave < NQP + 2) {
+      const char* nsrc = (wave == NQP ? a.new_k : a.new_v) + ((size_t)w.b * a.n_kv + w.kvh) * C::ROWB;
+      dec_dma(dec_rsrc(nsrc, C::ROWB), stage + QSTAGE + (wave - NQP) * NSTAGE, (uint32_t)(lane * 16));
+    }
+  }
   issue(1, ring1);
   issue(2, ring2);
+  wait_vmcnt<2 * kPiecesPerWave>();  // unit 0 and the staging loads have landed
+  lds_barrier();
+  // this wavefront's HW queries, in the lane's slice layout
+  uint4 q[HW][C::CPL];
+#pragma unroll
+  for (int h = 0; h < HW; ++h)
+#pragma unroll
+    for (int c2 = 0; c2 < C::CPL; ++c2)
+      q[h][c2] = *reinterpret_cast<const uint4*>(stage + (size_t)(hg * HW + h) * C::ROWB + (s + 8 * c2) * 16);
 
   DecodeState<BF16, D, G> st;
 #pragma unroll
@@ -612,10 +613,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
 
   // ---- fused append: score the new token as a one-row tile (K in row 0 of
   // ring0, V in row 0 of ring1; the other rows are masked), then store it
+  uint4 nkv = make_uint4(0, 0, 0, 0);
   if (add_new) {
     lds_barrier();  // every wavefront is done with the ring
-    if (wave == 0 && lane < 2 * C::CPR)
+    if (wave == 0 && lane < 2 * C::CPR) {
+      nkv = *reinterpret_cast<const uint4*>(stage + QSTAGE + (lane < C::CPR ? 0 : NSTAGE) + (lane % C::CPR) * 16);
       *reinterpret_cast<uint4*>((lane < C::CPR ? ring0 : ring1) + (lane % C::CPR) * 16) = nkv;  // row 0: no swizzle
+    }
     lds_barrier();
     if (slot == 0) {
       tile_scores<BF16, D, G>(st, p, ring0, q, 1, -1, rg, s, a.scale_log2);
