@@ -472,6 +472,146 @@ __device__ __forceinline__ void tile_pv(DecodeState<BF16, D, G>& st, const float
   }
 }
 
+// ---- four-lane score layout (bf16, four query heads per wavefront)
+//
+// With four query heads per wavefront the scores are computed with 4 lanes
+// per row instead of 8: lane l has row group r16 = l / 4 (rows r16, r16 + 16,
+// ... of the tile) and slice s4 = l % 4 (16-byte chunks s4, s4 + 4, ... of the
+// row).  After a 4-lane all-reduce each lane keeps only the scores of query
+// head s4, so the lanes of a row do not repeat each other's exponentials.
+// The softmax state of (row group rg, head h) -- the rows rg + 8 j that lane
+// (rg, s) of the weighted sum accumulates -- is kept by the two lanes
+// (r16 = rg, s4 = h) and (r16 = rg + 8, s4 = h), 32 lanes apart, which share
+// one reference max.  The probabilities reach the weighted-sum layout through
+// a small per-wavefront LDS buffer, already as the bf16 pairs (rows
+// rg + 16 q and rg + 16 q + 8) the weighted sum's dot products take; the
+// rescale factors of a raised reference go the same way.
+template <bool BF16, int D, int G>
+struct Score4 {
+  using C = DecodeCfg<BF16, D, G>;
+  static constexpr bool ON = BF16 && C::HW == 4;
+  static constexpr int CPL4 = C::CPR / 4;  // chunks per lane
+  static constexpr int RPL4 = C::TR / 16;  // rows per lane
+  static constexpr int NQ = C::RPL / 2;    // row pairs per weighted-sum lane
+  static constexpr int PBUF = 8 * NQ * 4;  // probability pairs per wavefront (dwords)
+};
+
+// K-tile chunk swizzle of the 4-lane layout: the 4 rows a group of 16 lanes
+// reads fall into 4 distinct quarters of the 256-byte bank space.
+template <int CPR>
+__device__ __forceinline__ int dec_swz_k4(int r) { return CPR >= 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+// all-reduce over the 4 lanes of a row
+__device__ __forceinline__ float row4_sum(float x) {
+  x += dpp<0xB1>(x);  // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);  // quad_perm [2,3,0,1]
+  return x;
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
+// Scores of the lane's rows against query head s4, the online-softmax update
+// of the lane's (m, l), and the probabilities written to `pbuf` (this
+// wavefront's pairs, dword (rg, q, h) = rows rg + 16 q and rg + 16 q + 8).
+// Rescale factors go to `abuf` [rg][h]; the result says whether any lane of
+// the wavefront raised its reference (then every (rg, h) factor is written).
+template <bool BF16, int D, int G>
+__device__ __forceinline__ bool tile_scores4(float& m, float& l, uint16_t* pbuf, float* abuf, const char* kt,
+                                             const uint4 (&q)[4][Score4<BF16, D, G>::CPL4], int nv, int excl,
+                                             int r16, int s4, float scale_log2) {
+  using C = DecodeCfg<BF16, D, G>;
+  using S4 = Score4<BF16, D, G>;
+  float sc[S4::RPL4];
+#pragma unroll
+  for (int j = 0; j < S4::RPL4; ++j) {
+    const int row = r16 + 16 * j;
+    uint4 k[S4::CPL4];
+#pragma unroll
+    for (int cc = 0; cc < S4::CPL4; ++cc)
+      k[cc] = *reinterpret_cast<const uint4*>(kt + row * C::ROWB + (((s4 + 4 * cc) ^ dec_swz_k4<C::CPR>(row)) * 16));
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cc = 0; cc < S4::CPL4; ++cc) {
+      const uint32_t kw[4] = {k[cc].x, k[cc].y, k[cc].z, k[cc].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const uint32_t qw[4] = {q[h][cc].x, q[h][cc].y, q[h][cc].z, q[h][cc].w};
+          acc[h] = dot2_bf16(qw[i], kw[i], acc[h]);
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < 4; ++h) acc[h] = row4_sum(acc[h]);
+    const float own = s4 == 0 ? acc[0] : s4 == 1 ? acc[1] : s4 == 2 ? acc[2] : acc[3];
+    sc[j] = (row < nv && row != excl) ? own : -INFINITY;
+  }
+  // reference max of (rg, s4), shared with the partner lane 32 away
+  float x = sc[0];
+#pragma unroll
+  for (int j = 1; j < S4::RPL4; ++j) x = fmaxf(x, sc[j]);
+  x = fmaxf(x, __shfl_xor(x, 32));
+  const float mt = x * scale_log2;  // scale > 0, so max commutes with it
+  const bool any = __builtin_amdgcn_ballot_w64(mt > m + kRescaleSlack) != 0;
+  if (any) {
+    const float mn = fmaxf(m, mt);
+    const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m - mn);
+    m = mn;
+    l *= alpha;
+    if (r16 < 8) abuf[r16 * 4 + s4] = alpha;
+  }
+  const float mu = (m == -INFINITY) ? 0.f : m;
+  const int rg = r16 & 7, half = r16 >> 3;
+#pragma unroll
+  for (int j = 0; j < S4::RPL4; ++j) {
+    const float pj = fast_exp2(fmaf(sc[j], scale_log2, -mu));
+    l += pj;
+    pbuf[((rg * S4::NQ + j) * 4 + s4) * 2 + half] = bf16_bits(pj);
+  }
+  return any;
+}
+
+// acc += sum over the lane's rows of p * V[row], with the probability pairs
+// and rescale factors from tile_scores4.
+template <bool BF16, int D, int G>
+__device__ __forceinline__ void tile_pv4(DecodeState<BF16, D, G>& st, const uint16_t* pbuf, const float* abuf,
+                                         bool rescale, const char* vt, int rg, int s) {
+  using C = DecodeCfg<BF16, D, G>;
+  using S4 = Score4<BF16, D, G>;
+  if (rescale) {
+    const float4 al = *reinterpret_cast<const float4*>(abuf + rg * 4);
+    const float a4[4] = {al.x, al.y, al.z, al.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int e = 0; e < C::NACC; ++e) st.acc[h][e] *= a4[h];
+  }
+#pragma unroll
+  for (int qq = 0; qq < S4::NQ; ++qq) {
+    const int row0 = rg + 16 * qq, row1 = row0 + 8;  // same parity: same swizzle
+    const uint4 pw = *reinterpret_cast<const uint4*>(pbuf + (rg * S4::NQ + qq) * 8);
+    const uint32_t P[4] = {pw.x, pw.y, pw.z, pw.w};
+#pragma unroll
+    for (int cc = 0; cc < C::CPL; ++cc) {
+      const int off = ((s + 8 * cc) ^ dec_swz<C::CPR>(row0)) * 16;
+      const uint4 va = *reinterpret_cast<const uint4*>(vt + row0 * C::ROWB + off);
+      const uint4 vb = *reinterpret_cast<const uint4*>(vt + row1 * C::ROWB + off);
+      const uint32_t a4[4] = {va.x, va.y, va.z, va.w};
+      const uint32_t b4[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = __builtin_amdgcn_perm(b4[i], a4[i], 0x05040100u);  // (row0, row1) at d = 2i
+        const uint32_t hi = __builtin_amdgcn_perm(b4[i], a4[i], 0x07060302u);  // at d = 2i+1
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          st.acc[h][cc * 8 + 2 * i] = dot2_bf16(P[h], lo, st.acc[h][cc * 8 + 2 * i]);
+          st.acc[h][cc * 8 + 2 * i + 1] = dot2_bf16(P[h], hi, st.acc[h][cc * 8 + 2 * i + 1]);
+        }
+      }
+    }
+  }
+}
+
 template <int X>
 using UnitTag = std::integral_constant<int, X>;
 
@@ -497,6 +637,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   constexpr int NSTAGE = (C::ROWB + 1023) / 1024 * 1024;
   static_assert(QSTAGE / 1024 + 2 <= kDecWaves, "one staging piece per wavefront");
   __shared__ __attribute__((aligned(1024))) char stage[QSTAGE + 2 * NSTAGE];
+  using S4 = Score4<BF16, D, G>;
+  constexpr bool SC4 = S4::ON;
+  // four-lane score layout: per-wavefront probability pairs and rescale factors
+  __shared__ __attribute__((aligned(16))) uint16_t pbuf_all[SC4 ? kDecWaves : 1][SC4 ? 2 * S4::PBUF : 8];
+  __shared__ __attribute__((aligned(16))) float abuf_all[SC4 ? kDecWaves : 1][32];
   char* const rings[kRingUnits] = {ring0, ring1, ring2, ring3};  // indexed by constants only
   auto ring_at = [&](int i) -> char* { return i == 0 ? ring0 : i == 1 ? ring1 : i == 2 ? ring2 : ring3; };
 
@@ -519,14 +664,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   // pieces: piece n of a unit covers LDS bytes [n*1024, n*1024+1024), lane i
   // byte n*1024 + 16 i, i.e. row (n*1024 + 16 i) / ROWB of the round at a
   // chunk slot that is the row's swizzle applied to the global chunk
-  uint32_t poff[kPiecesPerWave];
+  // (K units use the four-lane score layout's swizzle when it is on)
+  uint32_t poff_k[kPiecesPerWave], poff_v[kPiecesPerWave];
 #pragma unroll
   for (int j = 0; j < kPiecesPerWave; ++j) {
     const int off = (wave + kDecWaves * j) * 1024 + lane * 16;
-    const int r = off / C::ROWB;  // row of the round; a slot's tile starts at an even row (TR is even)
-    const int c = ((off % C::ROWB) / 16) ^ dec_swz<C::CPR>(r % TR);
-    poff[j] = (uint32_t)(r * C::ROWB + c * 16);
+    const int r = off / C::ROWB;  // row of the round; a slot's tile starts at a multiple of 4 rows
+    const int c = (off % C::ROWB) / 16;
+    const int ck = c ^ (SC4 ? dec_swz_k4<C::CPR>(r % TR) : dec_swz<C::CPR>(r % TR));
+    poff_k[j] = (uint32_t)(r * C::ROWB + ck * 16);
+    poff_v[j] = (uint32_t)(r * C::ROWB + (c ^ dec_swz<C::CPR>(r % TR)) * 16);
   }
+  static_assert(TR % 4 == 0, "tiles start at a multiple of 4 rows");
 
   // Issue unit `uu` (round uu / 2; K rows if uu is even, else V rows) into
   // `dst`: the round's rows are contiguous, so one buffer resource covers
@@ -541,7 +690,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     const char* src = ((uu & 1) ? w.vbase : w.kbase) + (size_t)(rows > 0 ? row0 : 0) * C::ROWB;
     const i32x4_t rs = dec_rsrc(src, rows * C::ROWB);
 #pragma unroll
-    for (int j = 0; j < kPiecesPerWave; ++j) dec_dma(rs, dst + (wave + kDecWaves * j) * 1024, poff[j]);
+    for (int j = 0; j < kPiecesPerWave; ++j)
+      dec_dma(rs, dst + (wave + kDecWaves * j) * 1024, (uu & 1) ? poff_v[j] : poff_k[j]);
   };
   // The first unit, then the group's queries and the new token's K and V rows
   // into the staging area (one load piece per wavefront for the first
@@ -562,13 +712,21 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   issue(2, ring2);
   wait_vmcnt<2 * kPiecesPerWave>();  // unit 0 and the staging loads have landed
   lds_barrier();
-  // this wavefront's HW queries, in the lane's slice layout
-  uint4 q[HW][C::CPL];
+  // this wavefront's HW queries, in the lane's slice layout (of the four-lane
+  // score layout when it is on)
+  constexpr int QCPL = SC4 ? S4::CPL4 : C::CPL;
+  const int r16 = lane >> 2, s4 = lane & 3;
+  uint4 q[HW][QCPL];
 #pragma unroll
   for (int h = 0; h < HW; ++h)
 #pragma unroll
-    for (int c2 = 0; c2 < C::CPL; ++c2)
-      q[h][c2] = *reinterpret_cast<const uint4*>(stage + (size_t)(hg * HW + h) * C::ROWB + (s + 8 * c2) * 16);
+    for (int c2 = 0; c2 < QCPL; ++c2)
+      q[h][c2] = *reinterpret_cast<const uint4*>(stage + (size_t)(hg * HW + h) * C::ROWB +
+                                                 (SC4 ? (s4 + 4 * c2) : (s + 8 * c2)) * 16);
+  uint16_t* const pbuf = pbuf_all[SC4 ? wave : 0];
+  float* const abuf = abuf_all[SC4 ? wave : 0];
+  float m4 = -INFINITY, l4 = 0.f;  // four-lane layout: softmax state of (r16 % 8, head s4)
+  bool resc = false;               // four-lane layout: the K unit raised a reference
 
   DecodeState<BF16, D, G> st;
 #pragma unroll
@@ -592,10 +750,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     const int nv = active ? (int)(left < 0 ? 0 : (left > TR ? TR : left)) : 0;
     const char* tile = rings[X] + slot * C::SLOT_BYTES;
     if (V_PART) {
-      if (nv > 0) tile_pv<BF16, D, G>(st, p, tile, rg, s);
+      if constexpr (SC4) {
+        if (nv > 0) tile_pv4<BF16, D, G>(st, pbuf, abuf, resc, tile, rg, s);
+      } else {
+        if (nv > 0) tile_pv<BF16, D, G>(st, p, tile, rg, s);
+      }
     } else {
       const int64_t ex = excl_row - row0;
-      if (nv > 0) tile_scores<BF16, D, G>(st, p, tile, q, nv, (ex >= 0 && ex < TR) ? (int)ex : -1, rg, s, a.scale_log2);
+      const int exr = (ex >= 0 && ex < TR) ? (int)ex : -1;
+      if constexpr (SC4) {
+        resc = false;
+        if (nv > 0) resc = tile_scores4<BF16, D, G>(m4, l4, pbuf, abuf, tile, q, nv, exr, r16, s4, a.scale_log2);
+      } else {
+        if (nv > 0) tile_scores<BF16, D, G>(st, p, tile, q, nv, exr, rg, s, a.scale_log2);
+      }
     }
   };
   const int64_t n_units = 2 * nrounds;
@@ -622,8 +790,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     }
     lds_barrier();
     if (slot == 0) {
-      tile_scores<BF16, D, G>(st, p, ring0, q, 1, -1, rg, s, a.scale_log2);
-      tile_pv<BF16, D, G>(st, p, ring1, rg, s);
+      if constexpr (SC4) {
+        const bool r1 = tile_scores4<BF16, D, G>(m4, l4, pbuf, abuf, ring0, q, 1, -1, r16, s4, a.scale_log2);
+        tile_pv4<BF16, D, G>(st, pbuf, abuf, r1, ring1, rg, s);
+      } else {
+        tile_scores<BF16, D, G>(st, p, ring0, q, 1, -1, rg, s, a.scale_log2);
+        tile_pv<BF16, D, G>(st, p, ring1, rg, s);
+      }
     }
     if (wave == 0 && lane < 2 * C::CPR) {
       const int64_t row = ret_head ? a.new_row_ret : a.new_slot_str;
@@ -656,9 +829,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
               make_float4(st.acc[h][c2 * C::EPC + e], st.acc[h][c2 * C::EPC + e + 1], st.acc[h][c2 * C::EPC + e + 2],
                           st.acc[h][c2 * C::EPC + e + 3]);
       }
-      if (s == 0) {
-        w_m[hG][slot * 8 + rg] = st.m[h];
-        w_l[hG][slot * 8 + rg] = st.l[h];
+      if constexpr (!SC4) {
+        if (s == 0) {
+          w_m[hG][slot * 8 + rg] = st.m[h];
+          w_l[hG][slot * 8 + rg] = st.l[h];
+        }
+      }
+    }
+    if constexpr (SC4) {  // (rg, h) state: lanes (r16 = rg, s4 = h) and (rg + 8, h)
+      const float l_pair = l4 + __shfl_xor(l4, 32);
+      if (r16 < 8) {
+        w_m[hg * HW + s4][slot * 8 + r16] = m4;
+        w_l[hg * HW + s4][slot * 8 + r16] = l_pair;
       }
     }
   }
