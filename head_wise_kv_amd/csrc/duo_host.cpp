@@ -301,21 +301,31 @@ hipError_t enqueue_decode(duo_cache* c, int layer, const void* q, void* out, flo
   } else {
     a.excl_str = -1;
   }
-  // Work items: contiguous row ranges of one head, about equal in rows, as
-  // many as one workgroup per compute unit (or one per head if there are
-  // more heads).  Every item holds at least one row.
+  // Work items: contiguous row ranges of one head, as many as one workgroup
+  // per compute unit (or one per head if there are more heads), none shorter
+  // than one round of the kernel where the head allows.  The split between
+  // retrieval and streaming heads minimises the longest item (the launch ends
+  // with it): e.g. cutting each streaming head in two can beat leaving it
+  // whole when its held rows exceed a retrieval item's share.
   const int g = cf.n_q / cf.n_kv;
   const int64_t heads_ret = (int64_t)cf.B * lp.n_ret, heads_str = (int64_t)cf.B * lp.n_str;
-  const int64_t total = heads_ret * a.rows_ret + heads_str * a.rows_str;
   const int64_t slots = std::max<int64_t>(std::min(c->num_cu, duo::kMaxDecodeBlocks), heads_ret + heads_str);
-  int64_t t = std::max<int64_t>(duo::decode_round_rows(cf.dtype, cf.d_head, g), ceil_div(total, slots));
-  // items per head: the head's rows over the target, rounded to nearest
-  int64_t nb_r = 1, nb_s = 1;
-  for (;;) {
-    nb_r = std::max<int64_t>(1, (a.rows_ret + t / 2) / t);
-    nb_s = std::max<int64_t>(1, (a.rows_str + t / 2) / t);
-    if (heads_ret * nb_r + heads_str * nb_s <= slots) break;
-    t += std::max<int64_t>(1, t / 64);
+  const int64_t R = duo::decode_round_rows(cf.dtype, cf.d_head, g);
+  const int64_t max_r = std::max<int64_t>(1, ceil_div(a.rows_ret, R));
+  const int64_t max_s = std::max<int64_t>(1, ceil_div(a.rows_str, R));
+  int64_t nb_r = 1, nb_s = 1, best = -1;
+  for (int64_t ns = 1; ns <= max_s; ++ns) {
+    const int64_t left = slots - heads_str * ns;
+    if (left < heads_ret) break;
+    const int64_t nr = heads_ret > 0 ? std::min(max_r, left / heads_ret) : 1;
+    const int64_t cost = std::max(heads_ret > 0 ? ceil_div(a.rows_ret, nr) : 0,
+                                  heads_str > 0 ? ceil_div(a.rows_str, ns) : 0);
+    if (best < 0 || cost < best) {
+      best = cost;
+      nb_r = nr;
+      nb_s = ns;
+    }
+    if (heads_str == 0) break;
   }
   nb_r = ceil_div(a.rows_ret, ceil_div(a.rows_ret, nb_r));  // no empty item
   nb_s = ceil_div(a.rows_str, ceil_div(a.rows_str, nb_s));
