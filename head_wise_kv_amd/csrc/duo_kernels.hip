@@ -474,26 +474,29 @@ __device__ __forceinline__ void tile_pv(DecodeState<BF16, D, G>& st, const float
 
 // ---- four-lane score layout (bf16, four query heads per wavefront)
 //
-// With four query heads per wavefront the scores are computed with 4 lanes
-// per row instead of 8: lane l has row group r16 = l / 4 (rows r16, r16 + 16,
-// ... of the tile) and slice s4 = l % 4 (16-byte chunks s4, s4 + 4, ... of the
-// row).  After a 4-lane all-reduce each lane keeps only the scores of query
-// head s4, so the lanes of a row do not repeat each other's exponentials.
+// In bf16 the scores are computed with 4 lanes per row instead of 8: lane l
+// has row group r16 = l / 4 (rows r16, r16 + 16, ... of the tile) and slice
+// s4 = l % 4 (16-byte chunks s4, s4 + 4, ... of the row).  After a 4-lane
+// all-reduce each lane keeps only the scores of query head s4 % HW, so with
+// four heads per wavefront the lanes of a row do not repeat each other's
+// exponentials (with fewer heads, lanes s4 and s4 + HW hold the same head).
 // The softmax state of (row group rg, head h) -- the rows rg + 8 j that lane
-// (rg, s) of the weighted sum accumulates -- is kept by the two lanes
-// (r16 = rg, s4 = h) and (r16 = rg + 8, s4 = h), 32 lanes apart, which share
-// one reference max.  The probabilities reach the weighted-sum layout through
+// (rg, s) of the weighted sum accumulates -- is kept by the lanes
+// (r16 = rg, s4) and (r16 = rg + 8, s4) with s4 % HW = h, 32 lanes apart,
+// which share one reference max.  The probabilities reach the weighted-sum layout through
 // a small per-wavefront LDS buffer, already as the bf16 pairs (rows
 // rg + 16 q and rg + 16 q + 8) the weighted sum's dot products take; the
 // rescale factors of a raised reference go the same way.
 template <bool BF16, int D, int G>
 struct Score4 {
   using C = DecodeCfg<BF16, D, G>;
-  static constexpr bool ON = BF16 && C::HW == 4;
-  static constexpr int CPL4 = C::CPR / 4;  // chunks per lane
-  static constexpr int RPL4 = C::TR / 16;  // rows per lane
-  static constexpr int NQ = C::RPL / 2;    // row pairs per weighted-sum lane
-  static constexpr int PBUF = 8 * NQ * 4;  // probability pairs per wavefront (dwords)
+  static constexpr bool ON = BF16;
+  static constexpr int HW = C::HW;
+  static constexpr int CPL4 = C::CPR / 4;   // chunks per lane
+  static constexpr int RPL4 = C::TR / 16;   // rows per lane
+  static constexpr int NQ = C::RPL / 2;     // row pairs per weighted-sum lane
+  static constexpr int PBUF = 8 * NQ * HW;  // probability pairs per wavefront (dwords)
+  static_assert(4 % HW == 0, "heads per wavefront divide the 4 lanes of a row");
 };
 
 // K-tile chunk swizzle of the 4-lane layout: the 4 rows a group of 16 lanes
@@ -517,10 +520,12 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_ca
 // the wavefront raised its reference (then every (rg, h) factor is written).
 template <bool BF16, int D, int G>
 __device__ __forceinline__ bool tile_scores4(float& m, float& l, uint16_t* pbuf, float* abuf, const char* kt,
-                                             const uint4 (&q)[4][Score4<BF16, D, G>::CPL4], int nv, int excl,
-                                             int r16, int s4, float scale_log2) {
+                                             const uint4 (&q)[Score4<BF16, D, G>::HW][Score4<BF16, D, G>::CPL4],
+                                             int nv, int excl, int r16, int s4, float scale_log2) {
   using C = DecodeCfg<BF16, D, G>;
   using S4 = Score4<BF16, D, G>;
+  constexpr int HW = S4::HW;
+  const int hown = s4 % HW;  // the head whose state this lane keeps
   float sc[S4::RPL4];
 #pragma unroll
   for (int j = 0; j < S4::RPL4; ++j) {
@@ -529,21 +534,25 @@ __device__ __forceinline__ bool tile_scores4(float& m, float& l, uint16_t* pbuf,
 #pragma unroll
     for (int cc = 0; cc < S4::CPL4; ++cc)
       k[cc] = *reinterpret_cast<const uint4*>(kt + row * C::ROWB + (((s4 + 4 * cc) ^ dec_swz_k4<C::CPR>(row)) * 16));
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float acc[HW];
+#pragma unroll
+    for (int h = 0; h < HW; ++h) acc[h] = 0.f;
 #pragma unroll
     for (int cc = 0; cc < S4::CPL4; ++cc) {
       const uint32_t kw[4] = {k[cc].x, k[cc].y, k[cc].z, k[cc].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
+        for (int h = 0; h < HW; ++h) {
           const uint32_t qw[4] = {q[h][cc].x, q[h][cc].y, q[h][cc].z, q[h][cc].w};
           acc[h] = dot2_bf16(qw[i], kw[i], acc[h]);
         }
     }
 #pragma unroll
-    for (int h = 0; h < 4; ++h) acc[h] = row4_sum(acc[h]);
-    const float own = s4 == 0 ? acc[0] : s4 == 1 ? acc[1] : s4 == 2 ? acc[2] : acc[3];
+    for (int h = 0; h < HW; ++h) acc[h] = row4_sum(acc[h]);
+    float own = acc[0];
+#pragma unroll
+    for (int h = 1; h < HW; ++h) own = hown == h ? acc[h] : own;
     sc[j] = (row < nv && row != excl) ? own : -INFINITY;
   }
   // reference max of (rg, s4), shared with the partner lane 32 away
@@ -558,7 +567,7 @@ __device__ __forceinline__ bool tile_scores4(float& m, float& l, uint16_t* pbuf,
     const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m - mn);
     m = mn;
     l *= alpha;
-    if (r16 < 8) abuf[r16 * 4 + s4] = alpha;
+    if (r16 < 8 && s4 < HW) abuf[r16 * HW + s4] = alpha;
   }
   const float mu = (m == -INFINITY) ? 0.f : m;
   const int rg = r16 & 7, half = r16 >> 3;
@@ -566,7 +575,7 @@ __device__ __forceinline__ bool tile_scores4(float& m, float& l, uint16_t* pbuf,
   for (int j = 0; j < S4::RPL4; ++j) {
     const float pj = fast_exp2(fmaf(sc[j], scale_log2, -mu));
     l += pj;
-    pbuf[((rg * S4::NQ + j) * 4 + s4) * 2 + half] = bf16_bits(pj);
+    if (s4 < HW) pbuf[((rg * S4::NQ + j) * HW + s4) * 2 + half] = bf16_bits(pj);
   }
   return any;
 }
@@ -578,19 +587,22 @@ __device__ __forceinline__ void tile_pv4(DecodeState<BF16, D, G>& st, const uint
                                          bool rescale, const char* vt, int rg, int s) {
   using C = DecodeCfg<BF16, D, G>;
   using S4 = Score4<BF16, D, G>;
+  constexpr int HW = S4::HW;
   if (rescale) {
-    const float4 al = *reinterpret_cast<const float4*>(abuf + rg * 4);
-    const float a4[4] = {al.x, al.y, al.z, al.w};
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
+    for (int h = 0; h < HW; ++h) {
+      const float al = abuf[rg * HW + h];
 #pragma unroll
-      for (int e = 0; e < C::NACC; ++e) st.acc[h][e] *= a4[h];
+      for (int e = 0; e < C::NACC; ++e) st.acc[h][e] *= al;
+    }
   }
 #pragma unroll
   for (int qq = 0; qq < S4::NQ; ++qq) {
     const int row0 = rg + 16 * qq, row1 = row0 + 8;  // same parity: same swizzle
-    const uint4 pw = *reinterpret_cast<const uint4*>(pbuf + (rg * S4::NQ + qq) * 8);
-    const uint32_t P[4] = {pw.x, pw.y, pw.z, pw.w};
+    uint32_t P[HW];
+    const uint32_t* pq = reinterpret_cast<const uint32_t*>(pbuf) + (rg * S4::NQ + qq) * HW;
+#pragma unroll
+    for (int h = 0; h < HW; ++h) P[h] = pq[h];
 #pragma unroll
     for (int cc = 0; cc < C::CPL; ++cc) {
       const int off = ((s + 8 * cc) ^ dec_swz<C::CPR>(row0)) * 16;
@@ -603,7 +615,7 @@ __device__ __forceinline__ void tile_pv4(DecodeState<BF16, D, G>& st, const uint
         const uint32_t lo = __builtin_amdgcn_perm(b4[i], a4[i], 0x05040100u);  // (row0, row1) at d = 2i
         const uint32_t hi = __builtin_amdgcn_perm(b4[i], a4[i], 0x07060302u);  // at d = 2i+1
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
+        for (int h = 0; h < HW; ++h) {
           st.acc[h][cc * 8 + 2 * i] = dot2_bf16(P[h], lo, st.acc[h][cc * 8 + 2 * i]);
           st.acc[h][cc * 8 + 2 * i + 1] = dot2_bf16(P[h], hi, st.acc[h][cc * 8 + 2 * i + 1]);
         }
@@ -836,9 +848,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
         }
       }
     }
-    if constexpr (SC4) {  // (rg, h) state: lanes (r16 = rg, s4 = h) and (rg + 8, h)
+    if constexpr (SC4) {  // (rg, h) state: lanes (r16 = rg, s4) and (rg + 8, s4), s4 % HW = h
       const float l_pair = l4 + __shfl_xor(l4, 32);
-      if (r16 < 8) {
+      if (r16 < 8 && s4 < HW) {
         w_m[hg * HW + s4][slot * 8 + r16] = m4;
         w_l[hg * HW + s4][slot * 8 + r16] = l_pair;
       }
