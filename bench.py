@@ -78,9 +78,9 @@ def decode_layer_bytes(w: WL.Workload, mask_row, T: int, append: bool) -> int:
     n_ret = int(np.sum(mask_row))
     n_str = w.n_kv - n_ret
     rows = w.B * (n_ret * T + n_str * min(T, w.S + w.W))
-    kv = rows * w.d * w.elem_bytes * 2
+    kv = rows * w.kv_row_bytes * 2  # FP8 rows: codes plus the row scale
     qo = 2 * w.B * w.n_q * w.d * w.elem_bytes
-    app = 2 * 2 * w.B * w.n_kv * w.d * w.elem_bytes if append else 0
+    app = 2 * w.B * w.n_kv * (w.d * w.elem_bytes + w.kv_row_bytes) if append else 0
     return kv + qo + app
 
 
@@ -96,7 +96,7 @@ def bench_decode(w: WL.Workload, steps: int, warmup: int, layers: int):
     T = w.T
     fill = T - 1 if append else T
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    cache = H.DuoCache(L, w.B, w.n_q, w.n_kv, w.d, T, w.S, w.W, w.dtype, mask, device=dev)
+    cache = H.DuoCache(L, w.B, w.n_q, w.n_kv, w.d, T, w.S, w.W, w.dtype, mask, device=dev, kv_format=w.kv_format)
     log(f"{w.name}: arena {cache.arena_bytes / 1e9:.2f} GB, filling {L} layers x {fill} tokens")
     t0 = time.time()
     buf_k = torch.empty(w.B, w.n_kv, fill, w.d, dtype=dt, device=dev)
@@ -303,7 +303,7 @@ def main():
     ap.add_argument("--workload", default="gqa70b_decode_128k",
                     choices=[n for n, w in WL.WORKLOADS.items() if w.mode in ("decode", "decode_append")])
     ap.add_argument("--layers", type=int, default=0, help="limit layers (profiling only; 0 = all)")
-    ap.add_argument("--also", default="mha7b_decode_128k",
+    ap.add_argument("--also", default="mha7b_decode_128k,gqa70b_decode_128k_fp8,mha7b_decode_128k_fp8",
                     help="comma-separated extra decode workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-gated", action="store_true")
@@ -364,7 +364,8 @@ def main():
         wa = WL.WORKLOADS[name]
         ra = bench_decode(wa, args.steps, args.warmup, wa.L)
         va = ra["step_bytes"] / (ra["ms_step"] * 1e-3) / 1e9
-        also.append({"workload": name, "value": round(va, 2), "unit": "GB/s", "us_per_step": round(ra["ms_step"] * 1e3, 1),
+        also.append({"workload": name, "kv_rows": wa.kv_format or wa.dtype,
+                     "value": round(va, 2), "unit": "GB/s", "us_per_step": round(ra["ms_step"] * 1e3, 1),
                      "hbm_frac": round(va / HBM_PEAK_GBS, 4),
                      "decode_kernel_gbs": round(ra["decode_avg_bytes"] / ra["decode_avg_s"] / 1e9, 2),
                      "decode_kernel_us": round(ra["decode_avg_s"] * 1e6, 2)})

@@ -20,13 +20,14 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libduo.so"
 
 DUO_OK, DUO_EINVAL, DUO_EUNSUPPORTED, DUO_ECAPACITY, DUO_EEMPTY, DUO_EWORKSPACE, DUO_EHIP = 0, -1, -2, -3, -4, -5, -6
 DUO_F32, DUO_BF16 = 0, 1
+DUO_KV_NATIVE, DUO_KV_FP8 = 0, 1
 ERROR_NAMES = {DUO_EINVAL: "DUO_EINVAL", DUO_EUNSUPPORTED: "DUO_EUNSUPPORTED", DUO_ECAPACITY: "DUO_ECAPACITY",
                DUO_EEMPTY: "DUO_EEMPTY", DUO_EWORKSPACE: "DUO_EWORKSPACE", DUO_EHIP: "DUO_EHIP"}
 
 # Every entry point declared in include/duo.h.
 EXPORTS = ("duo_cache_bytes", "duo_cache_payload_bytes", "duo_cache_init", "duo_append", "duo_decode",
            "duo_decode_append", "duo_prefill_chunk", "duo_cache_seq_len", "duo_cache_head_view", "duo_cache_free",
-           "duo_last_error", "duo_gated_attention")
+           "duo_last_error", "duo_gated_attention", "duo_cache_head_scales")
 
 
 class DuoError(RuntimeError):
@@ -39,7 +40,7 @@ class duo_config(ctypes.Structure):
     _fields_ = [("L", ctypes.c_int32), ("B", ctypes.c_int32), ("n_q", ctypes.c_int32), ("n_kv", ctypes.c_int32),
                 ("d_head", ctypes.c_int32), ("T_cap", ctypes.c_int64), ("sink", ctypes.c_int32),
                 ("recent", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("retrieval_mask", ctypes.POINTER(ctypes.c_uint8))]
+                ("retrieval_mask", ctypes.POINTER(ctypes.c_uint8)), ("kv_format", ctypes.c_int32)]
 
 
 class duo_gated_shape(ctypes.Structure):
@@ -65,6 +66,7 @@ def _load():
                                         ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(i64),
                                         ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
     lib.duo_gated_attention.argtypes = [ctypes.POINTER(duo_gated_shape), vp, vp, vp, vp, vp, ctypes.c_float, vp]
+    lib.duo_cache_head_scales.argtypes = [vp, i32, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(i64)]
     lib.duo_cache_free.argtypes = [vp]
     lib.duo_cache_free.restype = None
     lib.duo_last_error.argtypes = []
@@ -92,7 +94,17 @@ def _dtype_code(dtype) -> int:
     raise ValueError(f"unsupported dtype {dtype}")
 
 
-def make_config(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask):
+def _kv_code(kv_format) -> int:
+    if kv_format in (None, 0, "native"):
+        return DUO_KV_NATIVE
+    if kv_format in (1, "fp8"):
+        return DUO_KV_FP8
+    if isinstance(kv_format, int):
+        return kv_format  # passed through; the library rejects unknown codes
+    raise ValueError(f"unknown kv_format {kv_format}")
+
+
+def make_config(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask, kv_format=None):
     """(duo_config, keep-alive mask buffer)."""
     import numpy as np
     m = torch.from_numpy(np.asarray(mask, dtype=np.uint8).reshape(-1).copy())
@@ -100,13 +112,13 @@ def make_config(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask):
         raise ValueError(f"mask must hold L*n_kv = {L * n_kv} entries, got {m.numel()}")
     buf = (ctypes.c_uint8 * m.numel())(*m.tolist())
     cfg = duo_config(L, B, n_q, n_kv, d_head, int(T_cap), sink, recent, _dtype_code(dtype),
-                     ctypes.cast(buf, ctypes.POINTER(ctypes.c_uint8)))
+                     ctypes.cast(buf, ctypes.POINTER(ctypes.c_uint8)), _kv_code(kv_format))
     return cfg, buf
 
 
-def cache_bytes(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask):
+def cache_bytes(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask, kv_format=None):
     """(arena bytes, workspace bytes, K+V payload bytes) -- host-only size query."""
-    cfg, _buf = make_config(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask)
+    cfg, _buf = make_config(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask, kv_format)
     a, w, p = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
     _check(lib.duo_cache_bytes(ctypes.byref(cfg), ctypes.byref(a), ctypes.byref(w)))
     _check(lib.duo_cache_payload_bytes(ctypes.byref(cfg), ctypes.byref(p)))
@@ -123,16 +135,18 @@ class DuoCache:
 
     Tensors: K/V inputs [B][n_kv][n][d], queries/outputs [B][n_q][d] (decode)
     or [B][n_q][C][d] (prefill), all contiguous in the cache dtype on the
-    cache's device.
+    cache's device.  kv_format "fp8" stores the K/V rows as FP8 codes with one
+    scale per row (bf16 caches with d_head 128).
     """
 
     def __init__(self, L: int, B: int, n_q: int, n_kv: int, d_head: int, T_cap: int, sink: int, recent: int,
-                 dtype, mask: Sequence, device="cuda", stream: Optional[torch.cuda.Stream] = None):
+                 dtype, mask: Sequence, device="cuda", stream: Optional[torch.cuda.Stream] = None, kv_format=None):
         self.L, self.B, self.n_q, self.n_kv, self.d = L, B, n_q, n_kv, d_head
         self.T_cap, self.S, self.W = int(T_cap), sink, recent
         self.torch_dtype = torch.bfloat16 if _dtype_code(dtype) == DUO_BF16 else torch.float32
+        self.kv_format = _kv_code(kv_format)
         self.device = torch.device(device)
-        self._cfg, self._mask_buf = make_config(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask)
+        self._cfg, self._mask_buf = make_config(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask, kv_format)
         import numpy as np
         self.mask = torch.from_numpy(np.asarray(mask, dtype=np.uint8).reshape(L, n_kv).copy())
         a, w = ctypes.c_size_t(), ctypes.c_size_t()
@@ -239,26 +253,45 @@ class DuoCache:
         return dict(is_retrieval=bool(ir.value), k_base=kb.value, v_base=vb.value, pos=pp.value,
                     n_slots=ns.value, row_bytes=rb.value, head_stride_bytes=hs.value, pos_stride=ps.value)
 
+    def head_scales(self, layer: int, kv_head: int):
+        """FP8 caches: (K scales [B][n_slots], V scales) of one KV head copied to
+        the host as float32 tensors; (None, None) for a native cache."""
+        ks, vs, st = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_int64()
+        _check(lib.duo_cache_head_scales(self._h, layer, kv_head, ctypes.byref(ks), ctypes.byref(vs), ctypes.byref(st)))
+        if not ks.value:
+            return None, None
+        rows = self.head_view(layer, kv_head)["n_slots"]
+        base = self.arena.data_ptr()
+        out = []
+        for ptr in (ks.value, vs.value):
+            off = ptr - base
+            seg = torch.stack([self.arena[off + b * st.value * 4: off + (b * st.value + rows) * 4] for b in range(self.B)])
+            out.append(seg.cpu().view(torch.float32).reshape(self.B, rows))
+        return out[0], out[1]
+
     def read_head(self, layer: int, kv_head: int):
         """Copy one KV head's slots to the host: (K [B][n_slots][d], V, pos [B][n_slots] or None).
-        The bytes come from the arena tensor by offset (a plain device copy)."""
+        The bytes come from the arena tensor by offset (a plain device copy).
+        FP8 caches give the codes as uint8."""
         hv = self.head_view(layer, kv_head)
         base = self.arena.data_ptr()
         es = 2 if self.torch_dtype == torch.bfloat16 else 4
+        if self.kv_format == DUO_KV_FP8:
+            es = 1
         rows = hv["n_slots"]
         out = []
         for key in ("k_base", "v_base"):
             off = hv[key] - base
             seg = torch.stack([self.arena[off + b * hv["head_stride_bytes"]: off + b * hv["head_stride_bytes"]
                                           + rows * hv["row_bytes"]] for b in range(self.B)])
-            out.append(seg.cpu().view(self.torch_dtype).reshape(self.B, rows, self.d))
+            out.append(seg.cpu().view(torch.uint8 if es == 1 else self.torch_dtype).reshape(self.B, rows, self.d))
         pos = None
         if hv["pos"]:
             off = hv["pos"] - base
             seg = torch.stack([self.arena[off + b * hv["pos_stride"] * 4: off + (b * hv["pos_stride"] + rows) * 4]
                                for b in range(self.B)])
             pos = seg.cpu().view(torch.int32).reshape(self.B, rows)
-        assert es in (2, 4)
+        assert es in (1, 2, 4)
         return out[0], out[1], pos
 
 

@@ -48,12 +48,16 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct LayerPlan {
   int n_ret = 0, n_str = 0;
   size_t off_kr = 0, off_vr = 0, off_ks = 0, off_vs = 0, off_pos = 0;
+  // FP8 caches: per-row scales of K and V (retrieval, then streaming heads)
+  size_t off_skr = 0, off_svr = 0, off_sks = 0, off_svs = 0;
   duo::HeadMap map{};
 };
 
 struct Plan {
   std::vector<LayerPlan> layers;
   size_t arena = 0, workspace = 0, payload = 0;
+  size_t ws_records = 0;  // decode partial records at the start of the workspace
+  size_t ws_dequant = 0;  // FP8 caches: one layer's held rows in bf16 for prefill (after the records)
 };
 
 bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
@@ -68,6 +72,10 @@ int validate(const duo_config* c) {
     return fail(DUO_EUNSUPPORTED, "group size g = %d not built (1, 2, 4, 8)", c->n_q / c->n_kv);
   if (c->d_head != 64 && c->d_head != 128) return fail(DUO_EUNSUPPORTED, "d_head %d not built (64, 128)", c->d_head);
   if (c->dtype != DUO_F32 && c->dtype != DUO_BF16) return fail(DUO_EUNSUPPORTED, "dtype %d", c->dtype);
+  if (c->kv_format != DUO_KV_NATIVE && c->kv_format != DUO_KV_FP8)
+    return fail(DUO_EUNSUPPORTED, "kv_format %d", c->kv_format);
+  if (c->kv_format == DUO_KV_FP8 && (c->dtype != DUO_BF16 || c->d_head != 128))
+    return fail(DUO_EUNSUPPORTED, "FP8 K/V rows are built for bf16 and d_head 128");
   if (c->T_cap < 1) return fail(DUO_EINVAL, "T_cap must be >= 1");
   if (c->T_cap > INT32_MAX) return fail(DUO_EINVAL, "T_cap must fit int32 (positions are int32)");
   if ((uint64_t)c->T_cap * (uint64_t)c->d_head * (c->dtype == DUO_BF16 ? 2u : 4u) > 0xffffffffull)
@@ -80,6 +88,8 @@ int validate(const duo_config* c) {
 }
 
 int elem_bytes(const duo_config* c) { return c->dtype == DUO_BF16 ? 2 : 4; }
+// bytes per stored K/V element (FP8 rows: one byte)
+int kv_elem_bytes(const duo_config* c) { return c->kv_format == DUO_KV_FP8 ? 1 : elem_bytes(c); }
 
 size_t decode_rec_floats(const duo_config* c) {  // acc[g][d], max[g], sum[g], padded to 16 bytes
   const int g = c->n_q / c->n_kv;
@@ -87,7 +97,9 @@ size_t decode_rec_floats(const duo_config* c) {  // acc[g][d], max[g], sum[g], p
 }
 
 void make_plan(const duo_config* c, Plan* p) {
-  const size_t row = (size_t)c->d_head * elem_bytes(c);
+  const size_t row = (size_t)c->d_head * kv_elem_bytes(c);
+  const bool fp8 = c->kv_format == DUO_KV_FP8;
+  size_t dequant = 0;
   const int64_t cap_str = (int64_t)c->sink + c->recent;
   p->layers.assign(c->L, LayerPlan{});
   size_t off = 0;
@@ -114,12 +126,28 @@ void make_plan(const duo_config* c, Plan* p) {
     lp.off_vs = off; off = align_up(off + str_bytes);
     lp.off_pos = off; off = align_up(off + (size_t)c->B * lp.n_str * cap_str * sizeof(int32_t));
     p->payload += 2 * (ret_bytes + str_bytes);
+    if (fp8) {
+      const size_t ret_sc = (size_t)c->B * lp.n_ret * c->T_cap * sizeof(float);
+      const size_t str_sc = (size_t)c->B * lp.n_str * cap_str * sizeof(float);
+      lp.off_skr = off; off = align_up(off + ret_sc);
+      lp.off_svr = off; off = align_up(off + ret_sc);
+      lp.off_sks = off; off = align_up(off + str_sc);
+      lp.off_svs = off; off = align_up(off + str_sc);
+      p->payload += 2 * (ret_sc + str_sc);
+      // prefill reads a layer's held rows dequantized to bf16: K and V of
+      // every retrieval and streaming head
+      const size_t bf_row = (size_t)c->d_head * 2;
+      dequant = std::max(dequant, 2 * (align_up((size_t)c->B * lp.n_ret * c->T_cap * bf_row) +
+                                       align_up((size_t)c->B * lp.n_str * cap_str * bf_row)));
+    }
   }
   p->arena = off;
   // decode partial records: one per (work item, head) overlap, indexed by
   // first work item of the head + flat head index + segment
   const size_t rec = decode_rec_floats(c) * sizeof(float);
-  p->workspace = align_up(((size_t)duo::kMaxDecodeBlocks + (size_t)c->B * c->n_kv) * rec);
+  p->ws_records = align_up(((size_t)duo::kMaxDecodeBlocks + (size_t)c->B * c->n_kv) * rec);
+  p->ws_dequant = dequant;
+  p->workspace = p->ws_records + p->ws_dequant;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -143,10 +171,17 @@ struct duo_cache {
     p.k_str = arena + lp.off_ks;
     p.v_str = arena + lp.off_vs;
     p.pos = reinterpret_cast<int32_t*>(arena + lp.off_pos);
+    const bool fp8 = cfg.kv_format == DUO_KV_FP8;
+    p.ksc_ret = fp8 ? reinterpret_cast<float*>(arena + lp.off_skr) : nullptr;
+    p.vsc_ret = fp8 ? reinterpret_cast<float*>(arena + lp.off_svr) : nullptr;
+    p.ksc_str = fp8 ? reinterpret_cast<float*>(arena + lp.off_sks) : nullptr;
+    p.vsc_str = fp8 ? reinterpret_cast<float*>(arena + lp.off_svs) : nullptr;
     return p;
   }
   int64_t cap_str() const { return (int64_t)cfg.sink + cfg.recent; }
-  int row_bytes() const { return cfg.d_head * elem_bytes(&cfg); }
+  int row_bytes() const { return cfg.d_head * kv_elem_bytes(&cfg); }     // stored K/V row
+  int in_row_bytes() const { return cfg.d_head * elem_bytes(&cfg); }     // input / query row
+  bool fp8() const { return cfg.kv_format == DUO_KV_FP8; }
 };
 
 namespace {
@@ -171,6 +206,7 @@ hipError_t enqueue_append(duo_cache* c, int layer, const void* k, const void* v,
   a.n_ret = lp.n_ret;
   a.n_str = lp.n_str;
   a.row_bytes = c->row_bytes();
+  a.in_row_bytes = c->in_row_bytes();
   a.cap_ret = c->cfg.T_cap;
   a.cap_str = c->cap_str();
   a.p0 = p0;
@@ -178,7 +214,7 @@ hipError_t enqueue_append(duo_cache* c, int layer, const void* k, const void* v,
   a.S = c->cfg.sink;
   a.W = c->cfg.recent;
   a.keep_from = std::max<int64_t>(a.S, p0 + n_new - a.W);
-  return duo::launch_append(a, c->cfg.dtype, c->cfg.d_head, s);
+  return duo::launch_append(a, c->cfg.dtype, c->cfg.d_head, c->fp8(), s);
 }
 
 }  // namespace
@@ -263,8 +299,8 @@ int check_decode_args(const duo_cache* c, const void* q, void* out, float scale,
   if (!q || !out) return fail(DUO_EINVAL, "q or out is NULL");
   if (!aligned16(q) || !aligned16(out)) return fail(DUO_EINVAL, "q and out must be 16-byte aligned");
   if (!std::isfinite(scale) || !(scale > 0.f)) return fail(DUO_EINVAL, "scale must be finite and > 0");
-  if (!ws || ws_bytes < c->plan.workspace)
-    return fail(DUO_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", c->plan.workspace, ws_bytes);
+  if (!ws || ws_bytes < c->plan.ws_records)
+    return fail(DUO_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", c->plan.ws_records, ws_bytes);
   if (!aligned16(ws)) return fail(DUO_EINVAL, "workspace must be 16-byte aligned");
   return DUO_OK;
 }
@@ -310,7 +346,7 @@ hipError_t enqueue_decode(duo_cache* c, int layer, const void* q, void* out, flo
   const int g = cf.n_q / cf.n_kv;
   const int64_t heads_ret = (int64_t)cf.B * lp.n_ret, heads_str = (int64_t)cf.B * lp.n_str;
   const int64_t slots = std::max<int64_t>(std::min(c->num_cu, duo::kMaxDecodeBlocks), heads_ret + heads_str);
-  const int64_t R = duo::decode_round_rows(cf.dtype, cf.d_head, g);
+  const int64_t R = duo::decode_round_rows(cf.dtype, cf.d_head, g, c->fp8());
   const int64_t max_r = std::max<int64_t>(1, ceil_div(a.rows_ret, R));
   const int64_t max_s = std::max<int64_t>(1, ceil_div(a.rows_str, R));
   int64_t nb_r = 1, nb_s = 1, best = -1;
@@ -334,7 +370,7 @@ hipError_t enqueue_decode(duo_cache* c, int layer, const void* q, void* out, flo
   const int blocks = (int)(heads_ret * nb_r + heads_str * nb_s);
   a.ws1 = static_cast<float*>(ws);
   a.scale_log2 = scale * 1.4426950408889634f;
-  return duo::launch_decode(a, cf.dtype, cf.d_head, g, blocks, stream);
+  return duo::launch_decode(a, cf.dtype, cf.d_head, g, c->fp8(), blocks, stream);
 }
 
 }  // namespace
@@ -375,9 +411,12 @@ int duo_decode_append(duo_cache* c, int layer, const void* k, const void* v, con
 
 int duo_prefill_chunk(duo_cache* c, int layer, const void* q, const void* k, const void* v, int64_t C, void* out,
                       float scale, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (int e = check_layer(c, layer)) return e;
+  if (c->fp8()) {
+    if (!ws || ws_bytes < c->plan.workspace)
+      return fail(DUO_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", c->plan.workspace, ws_bytes);
+    if ((reinterpret_cast<uintptr_t>(ws) % kAlign) != 0) return fail(DUO_EINVAL, "workspace must be 256-byte aligned");
+  }
   if (!q || !k || !v || !out) return fail(DUO_EINVAL, "q, k, v or out is NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(DUO_EINVAL, "q, k, v and out must be 16-byte aligned");
@@ -415,7 +454,39 @@ int duo_prefill_chunk(duo_cache* c, int layer, const void* q, const void* k, con
   duo::prefill_plan(cf.dtype, cf.d_head, g, &rows, &hpi);
   a.q_tiles = (int)ceil_div(C, rows);
   a.items_ret = cf.B * lp.n_ret * (g / hpi) * a.q_tiles;
-  hipError_t e = duo::launch_prefill(a, cf.dtype, cf.d_head, g, s);
+  hipError_t e = hipSuccess;
+  if (c->fp8()) {
+    // the held rows, dequantized to bf16 in the workspace (after the decode
+    // records), stand in for the cache's rows during the attention
+    const int64_t cap_r = std::max<int64_t>(P, 1);
+    const size_t bf_row = (size_t)cf.d_head * 2;
+    char* base = static_cast<char*>(ws) + c->plan.ws_records;
+    const size_t ret_b = align_up((size_t)cf.B * lp.n_ret * cap_r * bf_row);
+    const size_t str_b = align_up((size_t)cf.B * lp.n_str * c->cap_str() * bf_row);
+    duo::DequantArgs d{};
+    d.src = c->ptrs(layer);
+    d.dst = duo::LayerPtrs{};
+    d.dst.k_ret = base;
+    d.dst.v_ret = base + ret_b;
+    d.dst.k_str = base + 2 * ret_b;
+    d.dst.v_str = base + 2 * ret_b + str_b;
+    d.heads_ret = (int64_t)cf.B * lp.n_ret;
+    d.heads_str = (int64_t)cf.B * lp.n_str;
+    d.cap_ret_src = cf.T_cap;
+    d.cap_ret_dst = cap_r;
+    d.rows_ret = P;
+    d.cap_str = c->cap_str();
+    d.rows_str = a.held_str;
+    d.d = cf.d_head;
+    e = duo::launch_dequant(d, s);
+    if (e != hipSuccess) return hip_fail(e, "dequant launch");
+    a.lp.k_ret = d.dst.k_ret;
+    a.lp.v_ret = d.dst.v_ret;
+    a.lp.k_str = d.dst.k_str;
+    a.lp.v_str = d.dst.v_str;
+    a.cap_ret = cap_r;
+  }
+  e = duo::launch_prefill(a, cf.dtype, cf.d_head, g, s);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   // Commit the chunk after attention has read the cache (same stream).
   e = enqueue_append(c, layer, k, v, P, C, s);
@@ -492,6 +563,23 @@ int duo_gated_attention(const duo_gated_shape* shape, const void* q, const void*
   a.q_tiles = (int)q_tiles;
   const hipError_t e = duo::launch_gated(a, sh.dtype, sh.d_head, g, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gated forward launch");
+  return ok();
+}
+
+int duo_cache_head_scales(const duo_cache* c, int layer, int kv_head, float** k_scale, float** v_scale,
+                          int64_t* scale_stride) {
+  if (int e = check_layer(c, layer)) return e;
+  if (kv_head < 0 || kv_head >= c->cfg.n_kv) return fail(DUO_EINVAL, "kv_head %d out of range", kv_head);
+  const LayerPlan& lp = c->plan.layers[layer];
+  const duo::LayerPtrs p = c->ptrs(layer);
+  const bool ret = lp.map.kind[kv_head] != 0;
+  const int ci = lp.map.cidx[kv_head];
+  const int64_t slots = ret ? c->cfg.T_cap : c->cap_str();
+  const int n_kind = ret ? lp.n_ret : lp.n_str;
+  const bool f8 = c->fp8();
+  if (k_scale) *k_scale = f8 ? (ret ? p.ksc_ret : p.ksc_str) + (size_t)ci * slots : nullptr;
+  if (v_scale) *v_scale = f8 ? (ret ? p.vsc_ret : p.vsc_str) + (size_t)ci * slots : nullptr;
+  if (scale_stride) *scale_stride = f8 ? (int64_t)n_kind * slots : 0;
   return ok();
 }
 

@@ -30,6 +30,11 @@ struct LayerPtrs {
   char* k_str;     // [B][n_str][cap_str][d]
   char* v_str;
   int32_t* pos;    // [B][n_str][cap_str]
+  // FP8 rows only (else null): one fp32 scale per stored row
+  float* ksc_ret;  // [B][n_ret][cap_ret]
+  float* vsc_ret;
+  float* ksc_str;  // [B][n_str][cap_str]
+  float* vsc_str;
 };
 
 struct AppendArgs {
@@ -37,7 +42,9 @@ struct AppendArgs {
   const char* v;
   LayerPtrs lp;
   HeadMap map;
-  int B, n_kv, n_ret, n_str, row_bytes;
+  int B, n_kv, n_ret, n_str;
+  int row_bytes;      // bytes per stored row
+  int in_row_bytes;   // bytes per input row (equal unless the rows are stored as FP8)
   int64_t cap_ret, cap_str;
   int64_t p0, n_new;      // first position, tokens
   int64_t keep_from;      // streaming ring writes only for p >= keep_from
@@ -102,12 +109,22 @@ struct GatedArgs {
 
 // Launchers (duo_kernels.hip, duo_prefill.hip, duo_gated.hip).  dtype: 0 = fp32, 1 = bf16.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
-hipError_t launch_append(const AppendArgs& a, int dtype, int d, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, int dtype, int d, bool fp8, hipStream_t s);
+// FP8 caches: the held rows of one layer, dequantized to bf16 for prefill.
+struct DequantArgs {
+  LayerPtrs src;               // codes and scales in the arena
+  LayerPtrs dst;               // bf16 rows (k/v pointers only), [B][n_ret][cap_ret_dst][d] and [B][n_str][cap_str][d]
+  int64_t heads_ret, heads_str;
+  int64_t cap_ret_src, cap_ret_dst, rows_ret;
+  int64_t cap_str, rows_str;
+  int d;
+};
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
 // Split phase over `blocks` work items (retrieval heads' items first), then
 // the combine of heads cut into several items.
-hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int g, int blocks, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int g, bool fp8, int blocks, hipStream_t s);
 // Rows one round of the decode kernel covers (a work item should span at least one).
-int64_t decode_round_rows(int dtype, int d, int g);
+int64_t decode_round_rows(int dtype, int d, int g, bool fp8);
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int g, hipStream_t s);
 // Query rows and query heads one prefill work item covers.
 void prefill_plan(int dtype, int d, int g, int* rows_per_item, int* heads_per_item);

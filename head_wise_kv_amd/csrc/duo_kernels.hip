@@ -17,6 +17,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <climits>
 #include <type_traits>
 
 namespace duo {
@@ -156,6 +158,22 @@ __device__ __forceinline__ void dec_dma(i32x4_t rsrc, char* lds, uint32_t voff) 
       : "memory");
 }
 
+// The same with 4 bytes per lane: lane i writes LDS bytes [lds + 4 i, lds + 4 i + 4).
+__device__ __forceinline__ void dec_dma4(i32x4_t rsrc, char* lds, uint32_t voff) {
+  const uint32_t m0v =
+      __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) char*)lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0v), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+
 // ------------------------------------------------------------------ decode
 //
 // One workgroup of 8 wavefronts per compute unit walks a contiguous range of
@@ -186,13 +204,19 @@ constexpr int kUnitPieces = kUnitBytes / 1024;              // wavefront-wide 16
 constexpr int kPiecesPerWave = kUnitPieces / kDecWaves;     // 4
 static_assert(kUnitPieces % kDecWaves == 0, "unit pieces split evenly over the wavefronts");
 
-template <bool BF16, int D, int G>
+// KT: 0 = fp32 everywhere, 1 = bf16 everywhere, 2 = bf16 queries, inputs and
+// outputs with FP8 (E4M3) K/V rows in the cache plus one fp32 scale per row.
+template <int KT, int D, int G>
 struct DecodeCfg {
-  static constexpr int ES = BF16 ? 2 : 4;        // element bytes
-  static constexpr int ROWB = D * ES;            // bytes per row
-  static constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
+  static constexpr bool BF16 = KT != 0;          // queries, inputs, outputs in bf16
+  static constexpr bool KV8 = KT == 2;           // K/V rows stored as FP8 codes + row scales
+  static constexpr int ES = BF16 ? 2 : 4;        // query / input / output element bytes
+  static constexpr int IROWB = D * ES;           // bytes per query or input row
+  static constexpr int KES = KV8 ? 1 : ES;       // stored K/V element bytes
+  static constexpr int ROWB = D * KES;           // bytes per stored K/V row
+  static constexpr int CPR = ROWB / 16;          // 16-byte chunks per stored row
   static constexpr int CPL = CPR / 8;            // chunks per lane
-  static constexpr int EPC = 16 / ES;            // elements per chunk
+  static constexpr int EPC = 16 / KES;           // elements per chunk
   static constexpr int HW = G < 4 ? G : 4;       // query heads per wavefront
   static constexpr int HSPLIT = G / HW;          // wavefronts per slot
   static constexpr int SLOTS_W = kDecWaves / HSPLIT;
@@ -262,6 +286,129 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// ------------------------------------------------------------------ FP8 rows
+// A row stored as FP8 (E4M3) holds code_i = E4M3(x_i / s) with s = max|x| / 448
+// (both quotients correctly rounded fp32 divisions, the conversion rounding to
+// nearest even); a row of zeros has s = 0 and codes 0.  Rows are quantized by
+// groups of 16 lanes (one DPP row), 8 bf16 values per lane.
+
+// E4M3 codes of four quotients x / s.  |x / s| <= 448 up to the rounding of
+// the two divisions; the clamp maps that overshoot of the row maximum to 448,
+// where rounding to nearest puts it as well.
+__device__ __forceinline__ uint32_t fp8x4(float y0, float y1, float y2, float y3) {
+  auto c = [](float y) { return fminf(fmaxf(y, -448.f), 448.f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c(y0), c(y1), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c(y2), c(y3), w, true);
+  return (uint32_t)w;
+}
+
+// The 8 codes of this lane's bf16 values x (one 16-byte piece of a row whose
+// 16 pieces sit in the 16 lanes of a DPP row), and the row's scale.
+__device__ __forceinline__ uint2 quant_row16(uint4 x, float& scale) {
+  const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf_lo(w4[i]);
+    f[2 * i + 1] = bf_hi(w4[i]);
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+  m = fmaxf(m, dpp<0xB1>(m));   // quad_perm [1,0,3,2]
+  m = fmaxf(m, dpp<0x4E>(m));   // quad_perm [2,3,0,1]
+  m = fmaxf(m, dpp<0x141>(m));  // row_half_mirror
+  m = fmaxf(m, dpp<0x140>(m));  // row_mirror
+  scale = m / 448.f;
+  if (!(scale > 0.f)) return make_uint2(0u, 0u);
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = f[i] / scale;
+  return make_uint2(fp8x4(y[0], y[1], y[2], y[3]), fp8x4(y[4], y[5], y[6], y[7]));
+}
+
+// Append to an FP8 cache: one group of 16 lanes per (batch row, KV head,
+// token, K or V) row, each lane taking 8 consecutive bf16 values.  Slot rules
+// as append_kernel.
+__global__ void append_fp8_kernel(AppendArgs a) {
+  const int64_t rows = (int64_t)a.B * a.n_kv * a.n_new * 2;
+  const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+  const int j = threadIdx.x & 15;
+  if (row >= rows) return;  // whole groups of 16 leave together
+  const int tensor = (int)(row & 1);  // 0 = K, 1 = V
+  int64_t rest = row >> 1;
+  const int64_t i = rest % a.n_new;
+  rest /= a.n_new;
+  const int kvh = (int)(rest % a.n_kv);
+  const int b = (int)(rest / a.n_kv);
+  const int64_t p = a.p0 + i;
+  const size_t src = (((size_t)b * a.n_kv + kvh) * a.n_new + i) * a.in_row_bytes + (size_t)j * 16;
+  float sc;
+  const uint2 codes = quant_row16(ld16((tensor ? a.v : a.k) + src), sc);
+  char* dst;
+  float* sdst;
+  if (a.map.kind[kvh]) {
+    const size_t hrow = ((size_t)b * a.n_ret + a.map.cidx[kvh]) * a.cap_ret + p;
+    dst = (tensor ? a.lp.v_ret : a.lp.k_ret) + hrow * a.row_bytes;
+    sdst = (tensor ? a.lp.vsc_ret : a.lp.ksc_ret) + hrow;
+  } else {
+    int64_t slot;
+    if (p < a.S) slot = p;
+    else if (p >= a.keep_from) slot = a.S + (p - a.S) % a.W;
+    else return;
+    const size_t hrow = ((size_t)b * a.n_str + a.map.cidx[kvh]) * a.cap_str + slot;
+    dst = (tensor ? a.lp.v_str : a.lp.k_str) + hrow * a.row_bytes;
+    sdst = (tensor ? a.lp.vsc_str : a.lp.ksc_str) + hrow;
+    if (tensor == 0 && j == 0) a.lp.pos[hrow] = (int32_t)p;
+  }
+  *reinterpret_cast<uint2*>(dst + j * 8) = codes;
+  if (j == 0) *sdst = sc;
+}
+
+// FP8 rows -> bf16 rows (code value times the row scale, rounded to nearest
+// even), 8 values per thread.
+__global__ void dequant_kernel(DequantArgs a) {
+  const int pieces = a.d / 8;
+  const int64_t n_ret = a.heads_ret * a.rows_ret, n_str = a.heads_str * a.rows_str;
+  const int64_t total = (n_ret + n_str) * 2 * pieces;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total; idx += stride) {
+    const int pc = (int)(idx % pieces);
+    const int64_t rest = idx / pieces;
+    const int tensor = (int)(rest & 1);
+    int64_t rr = rest >> 1;
+    const uint8_t* codes;
+    const float* sc;
+    uint16_t* dst;
+    if (rr < n_ret) {
+      const int64_t h = rr / a.rows_ret, r = rr % a.rows_ret;
+      const int64_t srow = h * a.cap_ret_src + r, drow = h * a.cap_ret_dst + r;
+      codes = reinterpret_cast<const uint8_t*>(tensor ? a.src.v_ret : a.src.k_ret) + srow * a.d;
+      sc = (tensor ? a.src.vsc_ret : a.src.ksc_ret) + srow;
+      dst = reinterpret_cast<uint16_t*>(tensor ? a.dst.v_ret : a.dst.k_ret) + drow * a.d;
+    } else {
+      rr -= n_ret;
+      const int64_t h = rr / a.rows_str, r = rr % a.rows_str;
+      const int64_t row = h * a.cap_str + r;
+      codes = reinterpret_cast<const uint8_t*>(tensor ? a.src.v_str : a.src.k_str) + row * a.d;
+      sc = (tensor ? a.src.vsc_str : a.src.ksc_str) + row;
+      dst = reinterpret_cast<uint16_t*>(tensor ? a.dst.v_str : a.dst.k_str) + row * a.d;
+    }
+    const uint2 c8 = *reinterpret_cast<const uint2*>(codes + pc * 8);
+    const float s = *sc;
+    const uint32_t cw[2] = {c8.x, c8.y};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[k], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[k], true);
+      o[2 * k] = f32_to_bf16_bits(lo[0] * s) | (f32_to_bf16_bits(lo[1] * s) << 16);
+      o[2 * k + 1] = f32_to_bf16_bits(hi[0] * s) | (f32_to_bf16_bits(hi[1] * s) << 16);
+    }
+    *reinterpret_cast<uint4*>(dst + pc * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
 template <int N>
@@ -292,6 +439,8 @@ struct DecodeItem {
   int b, kvh;
   char* kbase;
   char* vbase;
+  float* ksc;       // FP8 rows: per-row scales of the head (else null)
+  float* vsc;
 };
 
 template <int ROWB>
@@ -310,6 +459,9 @@ __device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a, int64_t b
     const size_t off = ((size_t)w.b * a.n_ret + r) * a.cap_ret * ROWB;
     w.kbase = a.lp.k_ret + off;
     w.vbase = a.lp.v_ret + off;
+    const size_t srow = ((size_t)w.b * a.n_ret + r) * a.cap_ret;
+    w.ksc = a.lp.ksc_ret ? a.lp.ksc_ret + srow : nullptr;
+    w.vsc = a.lp.vsc_ret ? a.lp.vsc_ret + srow : nullptr;
   } else {
     const int64_t x = (blk - n_ret_items) / a.nb_str;
     w.hh = (int64_t)a.B * a.n_ret + x;
@@ -322,6 +474,9 @@ __device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a, int64_t b
     const size_t off = ((size_t)w.b * a.n_str + si) * a.cap_str * ROWB;
     w.kbase = a.lp.k_str + off;
     w.vbase = a.lp.v_str + off;
+    const size_t srow = ((size_t)w.b * a.n_str + si) * a.cap_str;
+    w.ksc = a.lp.ksc_str ? a.lp.ksc_str + srow : nullptr;
+    w.vsc = a.lp.vsc_str ? a.lp.vsc_str + srow : nullptr;
   }
   const int64_t per = (rows + w.nparts - 1) / w.nparts;
   w.r0 = w.part * per;
@@ -335,9 +490,9 @@ __device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a, int64_t b
 // rescale of acc and l is rare after the first tiles.
 constexpr float kRescaleSlack = 8.f;
 
-template <bool BF16, int D, int G>
+template <int KT, int D, int G>
 struct DecodeState {
-  using C = DecodeCfg<BF16, D, G>;
+  using C = DecodeCfg<KT, D, G>;
   float m[C::HW], l[C::HW];
   float acc[C::HW][C::NACC];
 };
@@ -345,11 +500,12 @@ struct DecodeState {
 // Scores of the lane's rows against its HW queries, online-softmax update,
 // and the probabilities p[j][h] for the weighted sum.  `kt` is the tile in
 // LDS, `nv` its valid rows.
-template <bool BF16, int D, int G>
-__device__ __forceinline__ void tile_scores(DecodeState<BF16, D, G>& st, float (&p)[DecodeCfg<BF16, D, G>::RPL][DecodeCfg<BF16, D, G>::HW],
-                                            const char* kt, const uint4 (&q)[DecodeCfg<BF16, D, G>::HW][DecodeCfg<BF16, D, G>::CPL],
+template <int KT, int D, int G>
+__device__ __forceinline__ void tile_scores(DecodeState<KT, D, G>& st, float (&p)[DecodeCfg<KT, D, G>::RPL][DecodeCfg<KT, D, G>::HW],
+                                            const char* kt, const uint4 (&q)[DecodeCfg<KT, D, G>::HW][DecodeCfg<KT, D, G>::CPL],
                                             int nv, int excl, int rg, int s, float scale_log2) {
-  using C = DecodeCfg<BF16, D, G>;
+  using C = DecodeCfg<KT, D, G>;
+  [[maybe_unused]] constexpr bool BF16 = C::BF16;
   constexpr int HW = C::HW;
   float sc[C::RPL][HW];
 #pragma unroll
@@ -424,10 +580,11 @@ __device__ __forceinline__ void tile_scores(DecodeState<BF16, D, G>& st, float (
 }
 
 // acc += sum over the lane's rows of p[j][h] * V[row]; `vt` is the V tile in LDS.
-template <bool BF16, int D, int G>
-__device__ __forceinline__ void tile_pv(DecodeState<BF16, D, G>& st, const float (&p)[DecodeCfg<BF16, D, G>::RPL][DecodeCfg<BF16, D, G>::HW],
+template <int KT, int D, int G>
+__device__ __forceinline__ void tile_pv(DecodeState<KT, D, G>& st, const float (&p)[DecodeCfg<KT, D, G>::RPL][DecodeCfg<KT, D, G>::HW],
                                         const char* vt, int rg, int s) {
-  using C = DecodeCfg<BF16, D, G>;
+  using C = DecodeCfg<KT, D, G>;
+  [[maybe_unused]] constexpr bool BF16 = C::BF16;
   constexpr int HW = C::HW;
   if constexpr (BF16) {
 #pragma unroll
@@ -487,17 +644,25 @@ __device__ __forceinline__ void tile_pv(DecodeState<BF16, D, G>& st, const float
 // a small per-wavefront LDS buffer, already as the bf16 pairs (rows
 // rg + 16 q and rg + 16 q + 8) the weighted sum's dot products take; the
 // rescale factors of a raised reference go the same way.
-template <bool BF16, int D, int G>
+template <int KT, int D, int G>
 struct Score4 {
-  using C = DecodeCfg<BF16, D, G>;
-  static constexpr bool ON = BF16;
+  using C = DecodeCfg<KT, D, G>;
+  static constexpr bool ON = C::BF16;
   static constexpr int HW = C::HW;
   static constexpr int CPL4 = C::CPR / 4;   // chunks per lane
   static constexpr int RPL4 = C::TR / 16;   // rows per lane
   static constexpr int NQ = C::RPL / 2;     // row pairs per weighted-sum lane
   static constexpr int PBUF = 8 * NQ * HW;  // probability pairs per wavefront (dwords)
+  static constexpr int QPC = C::EPC >= 8 ? C::EPC / 8 : 1;  // 16-byte query pieces per stored chunk (FP8 rows: 2)
   static_assert(4 % HW == 0, "heads per wavefront divide the 4 lanes of a row");
 };
+
+// Two bf16 values (exact) from the FP8 codes in bytes 0, 1 (hi = false) or
+// 2, 3 (hi = true) of w.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
+}
 
 // K-tile chunk swizzle of the 4-lane layout: the 4 rows a group of 16 lanes
 // reads fall into 4 distinct quarters of the 256-byte bank space.
@@ -518,12 +683,15 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_ca
 // wavefront's pairs, dword (rg, q, h) = rows rg + 16 q and rg + 16 q + 8).
 // Rescale factors go to `abuf` [rg][h]; the result says whether any lane of
 // the wavefront raised its reference (then every (rg, h) factor is written).
-template <bool BF16, int D, int G>
+template <int KT, int D, int G>
 __device__ __forceinline__ bool tile_scores4(float& m, float& l, uint16_t* pbuf, float* abuf, const char* kt,
-                                             const uint4 (&q)[Score4<BF16, D, G>::HW][Score4<BF16, D, G>::CPL4],
-                                             int nv, int excl, int r16, int s4, float scale_log2) {
-  using C = DecodeCfg<BF16, D, G>;
-  using S4 = Score4<BF16, D, G>;
+                                             const uint4 (&q)[Score4<KT, D, G>::HW]
+                                                             [Score4<KT, D, G>::CPL4 * Score4<KT, D, G>::QPC],
+                                             const float* ksc, const float* vsc, int nv, int excl, int r16, int s4,
+                                             float scale_log2) {
+  using C = DecodeCfg<KT, D, G>;
+  [[maybe_unused]] constexpr bool BF16 = C::BF16;
+  using S4 = Score4<KT, D, G>;
   constexpr int HW = S4::HW;
   const int hown = s4 % HW;  // the head whose state this lane keeps
   float sc[S4::RPL4];
@@ -540,19 +708,36 @@ __device__ __forceinline__ bool tile_scores4(float& m, float& l, uint16_t* pbuf,
 #pragma unroll
     for (int cc = 0; cc < S4::CPL4; ++cc) {
       const uint32_t kw[4] = {k[cc].x, k[cc].y, k[cc].z, k[cc].w};
+      if constexpr (C::KV8) {
+        // 16 codes -> 8 bf16 pairs (exact), dotted with the query's values
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t kb[2] = {fp8x2_bf16<false>(kw[i]), fp8x2_bf16<true>(kw[i])};
 #pragma unroll
-        for (int h = 0; h < HW; ++h) {
-          const uint32_t qw[4] = {q[h][cc].x, q[h][cc].y, q[h][cc].z, q[h][cc].w};
-          acc[h] = dot2_bf16(qw[i], kw[i], acc[h]);
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int h = 0; h < HW; ++h) {
+              const uint4 qv = q[h][2 * cc + i / 2];
+              const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+              acc[h] = dot2_bf16(qw[(2 * i + t) % 4], kb[t], acc[h]);
+            }
         }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int h = 0; h < HW; ++h) {
+            const uint32_t qw[4] = {q[h][cc].x, q[h][cc].y, q[h][cc].z, q[h][cc].w};
+            acc[h] = dot2_bf16(qw[i], kw[i], acc[h]);
+          }
+      }
     }
 #pragma unroll
     for (int h = 0; h < HW; ++h) acc[h] = row4_sum(acc[h]);
     float own = acc[0];
 #pragma unroll
     for (int h = 1; h < HW; ++h) own = hown == h ? acc[h] : own;
+    if constexpr (C::KV8) own *= ksc[row];  // the K row's scale
     sc[j] = (row < nv && row != excl) ? own : -INFINITY;
   }
   // reference max of (rg, s4), shared with the partner lane 32 away
@@ -575,18 +760,21 @@ __device__ __forceinline__ bool tile_scores4(float& m, float& l, uint16_t* pbuf,
   for (int j = 0; j < S4::RPL4; ++j) {
     const float pj = fast_exp2(fmaf(sc[j], scale_log2, -mu));
     l += pj;
-    if (s4 < HW) pbuf[((rg * S4::NQ + j) * HW + s4) * 2 + half] = bf16_bits(pj);
+    // FP8 rows: the V row's scale joins the probability the weighted sum uses
+    const float pw = C::KV8 ? pj * vsc[r16 + 16 * j] : pj;
+    if (s4 < HW) pbuf[((rg * S4::NQ + j) * HW + s4) * 2 + half] = bf16_bits(pw);
   }
   return any;
 }
 
 // acc += sum over the lane's rows of p * V[row], with the probability pairs
 // and rescale factors from tile_scores4.
-template <bool BF16, int D, int G>
-__device__ __forceinline__ void tile_pv4(DecodeState<BF16, D, G>& st, const uint16_t* pbuf, const float* abuf,
+template <int KT, int D, int G>
+__device__ __forceinline__ void tile_pv4(DecodeState<KT, D, G>& st, const uint16_t* pbuf, const float* abuf,
                                          bool rescale, const char* vt, int rg, int s) {
-  using C = DecodeCfg<BF16, D, G>;
-  using S4 = Score4<BF16, D, G>;
+  using C = DecodeCfg<KT, D, G>;
+  [[maybe_unused]] constexpr bool BF16 = C::BF16;
+  using S4 = Score4<KT, D, G>;
   constexpr int HW = S4::HW;
   if (rescale) {
 #pragma unroll
@@ -612,12 +800,26 @@ __device__ __forceinline__ void tile_pv4(DecodeState<BF16, D, G>& st, const uint
       const uint32_t b4[4] = {vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = __builtin_amdgcn_perm(b4[i], a4[i], 0x05040100u);  // (row0, row1) at d = 2i
-        const uint32_t hi = __builtin_amdgcn_perm(b4[i], a4[i], 0x07060302u);  // at d = 2i+1
+        if constexpr (C::KV8) {
+          // codes of d = 4i .. 4i+3 of the two rows, interleaved by row, then
+          // converted to the (row0, row1) bf16 pairs the dot products take
+          const uint32_t x0 = __builtin_amdgcn_perm(b4[i], a4[i], 0x05010400u);  // d = 4i, 4i+1
+          const uint32_t x1 = __builtin_amdgcn_perm(b4[i], a4[i], 0x07030602u);  // d = 4i+2, 4i+3
+          const uint32_t pr[4] = {fp8x2_bf16<false>(x0), fp8x2_bf16<true>(x0), fp8x2_bf16<false>(x1),
+                                  fp8x2_bf16<true>(x1)};
 #pragma unroll
-        for (int h = 0; h < HW; ++h) {
-          st.acc[h][cc * 8 + 2 * i] = dot2_bf16(P[h], lo, st.acc[h][cc * 8 + 2 * i]);
-          st.acc[h][cc * 8 + 2 * i + 1] = dot2_bf16(P[h], hi, st.acc[h][cc * 8 + 2 * i + 1]);
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int h = 0; h < HW; ++h)
+              st.acc[h][cc * 16 + 4 * i + t] = dot2_bf16(P[h], pr[t], st.acc[h][cc * 16 + 4 * i + t]);
+        } else {
+          const uint32_t lo = __builtin_amdgcn_perm(b4[i], a4[i], 0x05040100u);  // (row0, row1) at d = 2i
+          const uint32_t hi = __builtin_amdgcn_perm(b4[i], a4[i], 0x07060302u);  // at d = 2i+1
+#pragma unroll
+          for (int h = 0; h < HW; ++h) {
+            st.acc[h][cc * 8 + 2 * i] = dot2_bf16(P[h], lo, st.acc[h][cc * 8 + 2 * i]);
+            st.acc[h][cc * 8 + 2 * i + 1] = dot2_bf16(P[h], hi, st.acc[h][cc * 8 + 2 * i + 1]);
+          }
         }
       }
     }
@@ -627,9 +829,10 @@ __device__ __forceinline__ void tile_pv4(DecodeState<BF16, D, G>& st, const uint
 template <int X>
 using UnitTag = std::integral_constant<int, X>;
 
-template <bool BF16, int D, int G>
+template <int KT, int D, int G>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
-  using C = DecodeCfg<BF16, D, G>;
+  using C = DecodeCfg<KT, D, G>;
+  [[maybe_unused]] constexpr bool BF16 = C::BF16;
   constexpr int HW = C::HW, SLOTS = C::SLOTS, TR = C::TR;
 
   // The four ring units are separate arrays so that the compiler can tell a
@@ -645,15 +848,23 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
       w_lw[G][SLOTS * 8];
   __shared__ float w_mt[G];
   // the group's queries and the new token's K and V rows, loaded by direct loads
-  constexpr int QSTAGE = (G * C::ROWB + 1023) / 1024 * 1024;
-  constexpr int NSTAGE = (C::ROWB + 1023) / 1024 * 1024;
+  constexpr int QSTAGE = (G * C::IROWB + 1023) / 1024 * 1024;
+  constexpr int NSTAGE = (C::IROWB + 1023) / 1024 * 1024;
   static_assert(QSTAGE / 1024 + 2 <= kDecWaves, "one staging piece per wavefront");
   __shared__ __attribute__((aligned(1024))) char stage[QSTAGE + 2 * NSTAGE];
-  using S4 = Score4<BF16, D, G>;
+  using S4 = Score4<KT, D, G>;
   constexpr bool SC4 = S4::ON;
   // four-lane score layout: per-wavefront probability pairs and rescale factors
   __shared__ __attribute__((aligned(16))) uint16_t pbuf_all[SC4 ? kDecWaves : 1][SC4 ? 2 * S4::PBUF : 8];
   __shared__ __attribute__((aligned(16))) float abuf_all[SC4 ? kDecWaves : 1][32];
+  // FP8 rows: the K scales, then the V scales, of the rows of a round; one
+  // buffer per K unit of the ring (units 0 and 2), loaded with that unit
+  constexpr bool KV8 = C::KV8;
+  __shared__ __attribute__((aligned(16))) float sbuf[KV8 ? 2 : 1][KV8 ? 2 * C::ROUND_ROWS : 4];
+  static_assert(!KV8 || C::ROUND_ROWS == 4 * 64, "a round's scales are 4 wavefront loads per tensor");
+  // vector-memory loads per unit and wavefront: the ring pieces, plus one
+  // scale load with each K unit of FP8 rows; units u+1 and u+2 hold WAITN
+  constexpr int WAITN = 2 * kPiecesPerWave + (KV8 ? 1 : 0);
   char* const rings[kRingUnits] = {ring0, ring1, ring2, ring3};  // indexed by constants only
   auto ring_at = [&](int i) -> char* { return i == 0 ? ring0 : i == 1 ? ring1 : i == 2 ? ring2 : ring3; };
 
@@ -704,6 +915,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < kPiecesPerWave; ++j)
       dec_dma(rs, dst + (wave + kDecWaves * j) * 1024, (uu & 1) ? poff_v[j] : poff_k[j]);
+    if constexpr (KV8) {
+      if ((uu & 1) == 0) {  // wavefronts 0-3: K scales, 4-7: V scales, 64 rows each
+        const int tensor = wave >> 2, part = wave & 3;
+        const float* ssrc = (tensor ? w.vsc : w.ksc) + (rows > 0 ? row0 : 0);
+        dec_dma4(dec_rsrc(reinterpret_cast<const char*>(ssrc), rows * 4),
+                 reinterpret_cast<char*>(&sbuf[(uu >> 1) & 1][tensor * C::ROUND_ROWS + part * 64]),
+                 (uint32_t)((part * 64 + lane) * 4));
+      }
+    }
   };
   // The first unit, then the group's queries and the new token's K and V rows
   // into the staging area (one load piece per wavefront for the first
@@ -714,33 +934,34 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     constexpr int NQP = QSTAGE / 1024;  // query pieces
     if (wave < NQP) {
       const char* qsrc = static_cast<const char*>(a.q) + q_off * C::ES;
-      dec_dma(dec_rsrc(qsrc, G * C::ROWB), stage + wave * 1024, (uint32_t)(wave * 1024 + lane * 16));
+      dec_dma(dec_rsrc(qsrc, G * C::IROWB), stage + wave * 1024, (uint32_t)(wave * 1024 + lane * 16));
     } else if (add_new && wave < NQP + 2) {
-      const char* nsrc = (wave == NQP ? a.new_k : a.new_v) + ((size_t)w.b * a.n_kv + w.kvh) * C::ROWB;
-      dec_dma(dec_rsrc(nsrc, C::ROWB), stage + QSTAGE + (wave - NQP) * NSTAGE, (uint32_t)(lane * 16));
+      const char* nsrc = (wave == NQP ? a.new_k : a.new_v) + ((size_t)w.b * a.n_kv + w.kvh) * C::IROWB;
+      dec_dma(dec_rsrc(nsrc, C::IROWB), stage + QSTAGE + (wave - NQP) * NSTAGE, (uint32_t)(lane * 16));
     }
   }
   issue(1, ring1);
   issue(2, ring2);
-  wait_vmcnt<2 * kPiecesPerWave>();  // unit 0 and the staging loads have landed
+  wait_vmcnt<WAITN>();  // unit 0 and the staging loads have landed
   lds_barrier();
   // this wavefront's HW queries, in the lane's slice layout (of the four-lane
   // score layout when it is on)
-  constexpr int QCPL = SC4 ? S4::CPL4 : C::CPL;
+  constexpr int QCPL = SC4 ? S4::CPL4 * S4::QPC : C::CPL;
   const int r16 = lane >> 2, s4 = lane & 3;
   uint4 q[HW][QCPL];
 #pragma unroll
   for (int h = 0; h < HW; ++h)
 #pragma unroll
     for (int c2 = 0; c2 < QCPL; ++c2)
-      q[h][c2] = *reinterpret_cast<const uint4*>(stage + (size_t)(hg * HW + h) * C::ROWB +
-                                                 (SC4 ? (s4 + 4 * c2) : (s + 8 * c2)) * 16);
+      q[h][c2] = *reinterpret_cast<const uint4*>(
+          stage + (size_t)(hg * HW + h) * C::IROWB +
+          (SC4 ? ((s4 + 4 * (c2 / S4::QPC)) * S4::QPC + c2 % S4::QPC) : (s + 8 * c2)) * 16);
   uint16_t* const pbuf = pbuf_all[SC4 ? wave : 0];
   float* const abuf = abuf_all[SC4 ? wave : 0];
   float m4 = -INFINITY, l4 = 0.f;  // four-lane layout: softmax state of (r16 % 8, head s4)
   bool resc = false;               // four-lane layout: the K unit raised a reference
 
-  DecodeState<BF16, D, G> st;
+  DecodeState<KT, D, G> st;
 #pragma unroll
   for (int h = 0; h < HW; ++h) {
     st.m[h] = -INFINITY;
@@ -754,7 +975,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   auto unit = [&](auto tag, int64_t u) {
     constexpr int X = decltype(tag)::value;
     constexpr bool V_PART = (X & 1) != 0;
-    wait_vmcnt<2 * kPiecesPerWave>();  // unit u has landed; u+1, u+2 may be in flight
+    wait_vmcnt<WAITN>();  // unit u has landed; u+1, u+2 may be in flight
     lds_barrier();                     // ... for every wavefront; unit u-1 is consumed
     issue(u + 3, rings[(X + 3) % kRingUnits]);
     const int64_t row0 = w.r0 + ((u >> 1) * SLOTS + slot) * (int64_t)TR;
@@ -763,18 +984,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     const char* tile = rings[X] + slot * C::SLOT_BYTES;
     if (V_PART) {
       if constexpr (SC4) {
-        if (nv > 0) tile_pv4<BF16, D, G>(st, pbuf, abuf, resc, tile, rg, s);
+        if (nv > 0) tile_pv4<KT, D, G>(st, pbuf, abuf, resc, tile, rg, s);
       } else {
-        if (nv > 0) tile_pv<BF16, D, G>(st, p, tile, rg, s);
+        if (nv > 0) tile_pv<KT, D, G>(st, p, tile, rg, s);
       }
     } else {
       const int64_t ex = excl_row - row0;
       const int exr = (ex >= 0 && ex < TR) ? (int)ex : -1;
       if constexpr (SC4) {
         resc = false;
-        if (nv > 0) resc = tile_scores4<BF16, D, G>(m4, l4, pbuf, abuf, tile, q, nv, exr, r16, s4, a.scale_log2);
+        const float* ks = &sbuf[KV8 ? (u >> 1) & 1 : 0][KV8 ? slot * TR : 0];
+        const float* vs = ks + (KV8 ? C::ROUND_ROWS : 0);
+        if (nv > 0) resc = tile_scores4<KT, D, G>(m4, l4, pbuf, abuf, tile, q, ks, vs, nv, exr, r16, s4, a.scale_log2);
       } else {
-        if (nv > 0) tile_scores<BF16, D, G>(st, p, tile, q, nv, exr, rg, s, a.scale_log2);
+        if (nv > 0) tile_scores<KT, D, G>(st, p, tile, q, nv, exr, rg, s, a.scale_log2);
       }
     }
   };
@@ -794,30 +1017,52 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   // ---- fused append: score the new token as a one-row tile (K in row 0 of
   // ring0, V in row 0 of ring1; the other rows are masked), then store it
   uint4 nkv = make_uint4(0, 0, 0, 0);
+  uint2 ncodes = make_uint2(0u, 0u);  // FP8 rows: the new token's codes (lanes 0-31 of wavefront 0)
+  float nscale = 0.f;
   if (add_new) {
     lds_barrier();  // every wavefront is done with the ring
-    if (wave == 0 && lane < 2 * C::CPR) {
-      nkv = *reinterpret_cast<const uint4*>(stage + QSTAGE + (lane < C::CPR ? 0 : NSTAGE) + (lane % C::CPR) * 16);
-      *reinterpret_cast<uint4*>((lane < C::CPR ? ring0 : ring1) + (lane % C::CPR) * 16) = nkv;  // row 0: no swizzle
+    if constexpr (KV8) {
+      // quantize the new K (lanes 0-15) and V (lanes 16-31) rows as the
+      // append would, and place them in row 0 of ring0 / ring1
+      if (wave == 0 && lane < 32) {
+        const int t = lane >> 4, j = lane & 15;
+        ncodes = quant_row16(*reinterpret_cast<const uint4*>(stage + QSTAGE + t * NSTAGE + j * 16), nscale);
+        *reinterpret_cast<uint2*>((t ? ring1 : ring0) + j * 8) = ncodes;  // row 0: no swizzle
+        if (j == 0) sbuf[0][t * C::ROUND_ROWS] = nscale;
+      }
+    } else {
+      if (wave == 0 && lane < 2 * C::CPR) {
+        nkv = *reinterpret_cast<const uint4*>(stage + QSTAGE + (lane < C::CPR ? 0 : NSTAGE) + (lane % C::CPR) * 16);
+        *reinterpret_cast<uint4*>((lane < C::CPR ? ring0 : ring1) + (lane % C::CPR) * 16) = nkv;  // row 0: no swizzle
+      }
     }
     lds_barrier();
     if (slot == 0) {
       if constexpr (SC4) {
-        const bool r1 = tile_scores4<BF16, D, G>(m4, l4, pbuf, abuf, ring0, q, 1, -1, r16, s4, a.scale_log2);
-        tile_pv4<BF16, D, G>(st, pbuf, abuf, r1, ring1, rg, s);
+        const bool r1 = tile_scores4<KT, D, G>(m4, l4, pbuf, abuf, ring0, q, &sbuf[0][0], &sbuf[0][KV8 ? C::ROUND_ROWS : 0],
+                                               1, -1, r16, s4, a.scale_log2);
+        tile_pv4<KT, D, G>(st, pbuf, abuf, r1, ring1, rg, s);
       } else {
-        tile_scores<BF16, D, G>(st, p, ring0, q, 1, -1, rg, s, a.scale_log2);
-        tile_pv<BF16, D, G>(st, p, ring1, rg, s);
+        tile_scores<KT, D, G>(st, p, ring0, q, 1, -1, rg, s, a.scale_log2);
+        tile_pv<KT, D, G>(st, p, ring1, rg, s);
       }
     }
-    if (wave == 0 && lane < 2 * C::CPR) {
-      const int64_t row = ret_head ? a.new_row_ret : a.new_slot_str;
-      char* dst = (lane < C::CPR ? w.kbase : w.vbase) + (size_t)row * C::ROWB + (lane % C::CPR) * 16;
-      *reinterpret_cast<uint4*>(dst) = nkv;
-      if (!ret_head && lane == 0) {
-        const int64_t si = w.hh - (int64_t)a.B * a.n_ret;  // b * n_str + streaming index
-        a.lp.pos[si * a.cap_str + a.new_slot_str] = a.new_pos;
+    const int64_t row = ret_head ? a.new_row_ret : a.new_slot_str;
+    if constexpr (KV8) {
+      if (wave == 0 && lane < 32) {
+        const int t = lane >> 4, j = lane & 15;
+        *reinterpret_cast<uint2*>((t ? w.vbase : w.kbase) + (size_t)row * C::ROWB + j * 8) = ncodes;
+        if (j == 0) (t ? w.vsc : w.ksc)[row] = nscale;
       }
+    } else {
+      if (wave == 0 && lane < 2 * C::CPR) {
+        char* dst = (lane < C::CPR ? w.kbase : w.vbase) + (size_t)row * C::ROWB + (lane % C::CPR) * 16;
+        *reinterpret_cast<uint4*>(dst) = nkv;
+      }
+    }
+    if (wave == 0 && lane == 0 && !ret_head) {
+      const int64_t si = w.hh - (int64_t)a.B * a.n_ret;  // b * n_str + streaming index
+      a.lp.pos[si * a.cap_str + a.new_slot_str] = a.new_pos;
     }
   }
 
@@ -923,9 +1168,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
 constexpr int kCombineElems = 32;
 constexpr int kCombineGroups = kDecodeThreads / kCombineElems;  // 16
 
-template <bool BF16, int D, int G>
+template <int KT, int D, int G>
 __global__ __launch_bounds__(kDecodeThreads) void combine_kernel(DecodeArgs a) {
-  using C = DecodeCfg<BF16, D, G>;
+  using C = DecodeCfg<KT, D, G>;
+  [[maybe_unused]] constexpr bool BF16 = C::BF16;
   constexpr int DC = D / kCombineElems;
   __shared__ float c_m[kCombineGroups][kCombineElems], c_l[kCombineGroups][kCombineElems],
       c_a[kCombineGroups][kCombineElems];
@@ -997,35 +1243,35 @@ __global__ __launch_bounds__(kDecodeThreads) void combine_kernel(DecodeArgs a) {
   else reinterpret_cast<float*>(a.out)[o] = At / Lt;
 }
 
-template <bool BF16, int D, int G>
+template <int KT, int D, int G>
 hipError_t launch_decode_g(const DecodeArgs& a, int blocks, hipStream_t s) {
-  decode_kernel<BF16, D, G><<<blocks, kDecodeThreads, 0, s>>>(a);
+  decode_kernel<KT, D, G><<<blocks, kDecodeThreads, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.nb_ret == 1 && a.nb_str == 1) return hipSuccess;  // every head finished in one item
   const int64_t heads = (int64_t)a.B * (a.n_ret + a.n_str);
-  combine_kernel<BF16, D, G><<<(unsigned)(heads * G * (D / kCombineElems)), kDecodeThreads, 0, s>>>(a);
+  combine_kernel<KT, D, G><<<(unsigned)(heads * G * (D / kCombineElems)), kDecodeThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <bool BF16, int D>
+template <int KT, int D>
 hipError_t launch_decode_d(const DecodeArgs& a, int g, int blocks, hipStream_t s) {
   switch (g) {
-    case 1: return launch_decode_g<BF16, D, 1>(a, blocks, s);
-    case 2: return launch_decode_g<BF16, D, 2>(a, blocks, s);
-    case 4: return launch_decode_g<BF16, D, 4>(a, blocks, s);
-    case 8: return launch_decode_g<BF16, D, 8>(a, blocks, s);
+    case 1: return launch_decode_g<KT, D, 1>(a, blocks, s);
+    case 2: return launch_decode_g<KT, D, 2>(a, blocks, s);
+    case 4: return launch_decode_g<KT, D, 4>(a, blocks, s);
+    case 8: return launch_decode_g<KT, D, 8>(a, blocks, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <bool BF16, int D>
+template <int KT, int D>
 int64_t round_rows_d(int g) {
   switch (g) {
-    case 1: return DecodeCfg<BF16, D, 1>::ROUND_ROWS;
-    case 2: return DecodeCfg<BF16, D, 2>::ROUND_ROWS;
-    case 4: return DecodeCfg<BF16, D, 4>::ROUND_ROWS;
-    case 8: return DecodeCfg<BF16, D, 8>::ROUND_ROWS;
+    case 1: return DecodeCfg<KT, D, 1>::ROUND_ROWS;
+    case 2: return DecodeCfg<KT, D, 2>::ROUND_ROWS;
+    case 4: return DecodeCfg<KT, D, 4>::ROUND_ROWS;
+    case 8: return DecodeCfg<KT, D, 8>::ROUND_ROWS;
     default: return 0;
   }
 }
@@ -1043,9 +1289,16 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_append(const AppendArgs& a, int dtype, int d, hipStream_t s) {
+hipError_t launch_append(const AppendArgs& a, int dtype, int d, bool fp8, hipStream_t s) {
   (void)dtype;
   (void)d;
+  if (fp8) {
+    const int64_t threads = (int64_t)a.B * a.n_kv * a.n_new * 2 * 16;
+    const int64_t grid = (threads + 255) / 256;
+    if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
+    append_fp8_kernel<<<(unsigned)grid, 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
   const int64_t total = (int64_t)a.B * a.n_kv * a.n_new * (a.row_bytes / 16);
   const int threads = 256;
   const int64_t want = (total + threads - 1) / threads;
@@ -1054,18 +1307,32 @@ hipError_t launch_append(const AppendArgs& a, int dtype, int d, hipStream_t s) {
   return hipGetLastError();
 }
 
-int64_t decode_round_rows(int dtype, int d, int g) {
-  if (dtype == 1) return d == 128 ? round_rows_d<true, 128>(g) : round_rows_d<true, 64>(g);
-  return d == 128 ? round_rows_d<false, 128>(g) : round_rows_d<false, 64>(g);
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t s) {
+  const int64_t total = (a.heads_ret * a.rows_ret + a.heads_str * a.rows_str) * 2 * (a.d / 8);
+  if (total == 0) return hipSuccess;
+  const int64_t want = (total + 255) / 256;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, 65536));
+  dequant_kernel<<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int g, int blocks, hipStream_t s) {
+int64_t decode_round_rows(int dtype, int d, int g, bool fp8) {
+  if (fp8) return round_rows_d<2, 128>(g);
+  if (dtype == 1) return d == 128 ? round_rows_d<1, 128>(g) : round_rows_d<1, 64>(g);
+  return d == 128 ? round_rows_d<0, 128>(g) : round_rows_d<0, 64>(g);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int g, bool fp8, int blocks, hipStream_t s) {
+  if (fp8) {
+    if (dtype == 1 && d == 128) return launch_decode_d<2, 128>(a, g, blocks, s);
+    return hipErrorInvalidValue;
+  }
   if (dtype == 1) {
-    if (d == 128) return launch_decode_d<true, 128>(a, g, blocks, s);
-    if (d == 64) return launch_decode_d<true, 64>(a, g, blocks, s);
+    if (d == 128) return launch_decode_d<1, 128>(a, g, blocks, s);
+    if (d == 64) return launch_decode_d<1, 64>(a, g, blocks, s);
   } else {
-    if (d == 128) return launch_decode_d<false, 128>(a, g, blocks, s);
-    if (d == 64) return launch_decode_d<false, 64>(a, g, blocks, s);
+    if (d == 128) return launch_decode_d<0, 128>(a, g, blocks, s);
+    if (d == 64) return launch_decode_d<0, 64>(a, g, blocks, s);
   }
   return hipErrorInvalidValue;
 }

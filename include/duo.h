@@ -52,6 +52,19 @@ extern "C" {
 
 typedef enum { DUO_F32 = 0, DUO_BF16 = 1 } duo_dtype;
 
+/* How the cache stores K and V rows.  DUO_KV_NATIVE: in the cache dtype.
+ * DUO_KV_FP8: as 8-bit E4M3 codes (OCP format: bias 7, largest finite 448)
+ * with one fp32 scale per stored row, K and V separately: s = max|x| / 448,
+ * code_i = E4M3(x_i / s) rounded to nearest even (a zero row: s = 0, codes 0);
+ * attention sees code value * s.  Low-bit KV rows cut the cache to half the
+ * bytes on top of the head split ("DuoAttention: Dual Retrieval & Streaming
+ * Heads Guide", "Production Advantages and Deployment Considerations", item 2;
+ * "Attention Variants and Memory Efficiency", "What the Inference Runtime Can
+ * Change": cache precision changes the bytes per stored element, not the
+ * attention rule).  Built for dtype bf16 and d_head 128; queries, new tokens
+ * and outputs stay bf16. */
+typedef enum { DUO_KV_NATIVE = 0, DUO_KV_FP8 = 1 } duo_kv_format;
+
 /* Cache configuration.  d_head in {64, 128}; g = n_q / n_kv in {1, 2, 4, 8};
  * n_kv <= 128; S >= 0; W >= 1; T_cap >= 1.  retrieval_mask is a host array
  * uint8 [L][n_kv] (1 = retrieval head, 0 = streaming head); it is copied. */
@@ -61,6 +74,7 @@ typedef struct {
   int32_t sink, recent;
   int32_t dtype; /* duo_dtype: Q, K, V and outputs; accumulation is fp32 */
   const uint8_t* retrieval_mask;
+  int32_t kv_format; /* duo_kv_format of the stored K/V rows (0 = native) */
 } duo_config;
 
 typedef struct duo_cache duo_cache; /* opaque host handle */
@@ -68,14 +82,17 @@ typedef struct duo_cache duo_cache; /* opaque host handle */
 /* Sizes (host only, no device work).  *arena_bytes: the device arena for
  * duo_cache_init.  It holds, per layer, K and V as [B][n_ret][T_cap][d] for
  * the retrieval heads and [B][n_str][S+W][d] for the streaming heads (the two
- * buffer kinds of the guide's section 2) and an int32 position per streaming
- * slot.  *workspace_bytes: the device scratch that duo_decode,
- * duo_decode_append and duo_prefill_chunk need (partial softmax results).  Either
- * output pointer may be NULL.  Returns DUO_OK or DUO_EINVAL/DUO_EUNSUPPORTED. */
+ * buffer kinds of the guide's section 2), an int32 position per streaming
+ * slot, and for DUO_KV_FP8 an fp32 scale per stored K and V row.
+ * *workspace_bytes: the device scratch that duo_decode, duo_decode_append and
+ * duo_prefill_chunk need (partial softmax results; for DUO_KV_FP8 also room
+ * for one layer's held rows in bf16, which prefill reads).  Either output
+ * pointer may be NULL.  Returns DUO_OK or DUO_EINVAL/DUO_EUNSUPPORTED. */
 int duo_cache_bytes(const duo_config* cfg, size_t* arena_bytes, size_t* workspace_bytes);
 
 /* K+V payload bytes of the arena (the KV-cache size the guide's section 2
- * formula counts: retrieval heads T_cap rows, streaming heads S+W rows). */
+ * formula counts: retrieval heads T_cap rows, streaming heads S+W rows; for
+ * DUO_KV_FP8 the codes plus the row scales). */
 int duo_cache_payload_bytes(const duo_config* cfg, size_t* payload_bytes);
 
 /* Bind a cache to a caller-owned device arena of at least duo_cache_bytes()
@@ -131,7 +148,10 @@ int duo_decode_append(duo_cache* c, int layer, const void* k, const void* v, con
  * attention over positions 0 .. P+i.  Streaming heads: the sink+window mask,
  * key j visible to row i iff j <= P+i and (j < S or j >= P+i-W+1), with keys
  * taken from the held sink and ring slots and from the chunk.  The chunk is
- * attended first and then appended as by duo_append.  DUO_ECAPACITY if
+ * attended first and then appended as by duo_append.  With DUO_KV_FP8 the held
+ * rows are read as stored (code value * scale) and the chunk's own rows as
+ * given, and ws must hold duo_cache_bytes' workspace_bytes (DUO_EWORKSPACE
+ * otherwise); a native cache needs no workspace here.  DUO_ECAPACITY if
  * P + C > T_cap. */
 int duo_prefill_chunk(duo_cache* c, int layer, const void* q, const void* k, const void* v,
                       int64_t C, void* out, float scale, void* ws, size_t ws_bytes, void* stream);
@@ -175,6 +195,13 @@ typedef struct {
  * workspace; enqueued on `stream`. */
 int duo_gated_attention(const duo_gated_shape* shape, const void* q, const void* k, const void* v,
                         const float* alpha, void* out, float scale, void* stream);
+
+/* Row scales of one KV head of a DUO_KV_FP8 cache: *k_scale / *v_scale
+ * receive the device float [n_slots] scales of batch row 0 (batch row b at
+ * + b * *scale_stride floats), in the slot order of duo_cache_head_view.  For
+ * a native cache both are set to NULL.  For bit-exact inspection. */
+int duo_cache_head_scales(const duo_cache* c, int layer, int kv_head, float** k_scale, float** v_scale,
+                          int64_t* scale_stride);
 
 /* Release the host handle (device memory is the caller's). NULL is ignored. */
 void duo_cache_free(duo_cache* c);

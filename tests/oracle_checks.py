@@ -16,6 +16,7 @@ import oracle
 from oracle import attention as A
 from oracle import cache as Cc
 from oracle import gating as G
+from oracle import quant as QZ
 from oracle import sizes as Z
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -301,13 +302,94 @@ def check_gated_gqa_expansion():
     assert np.allclose(got, ref, atol=1e-13, rtol=0)
 
 
+# ------------------------------------------------------------------ FP8 rows
+
+def _e4m3_sweep():
+    """float32 inputs covering every E4M3 rounding decision: each representable
+    magnitude, each midpoint between neighbours (the ties), points just off the
+    midpoints, the subnormal range and values past 448 up to the overflow edge."""
+    vals = np.unique(np.abs(QZ.e4m3_decode(np.arange(0, 127, dtype=np.uint8))))  # finite magnitudes
+    mids = (vals[:-1] + vals[1:]) / 2.0
+    ulp = np.float32(2.0 ** -20)
+    pts = np.concatenate([vals, mids, mids * (1 + ulp), mids * (1 - ulp), [448.0, 450.0, 463.5],
+                          np.linspace(0, 2.0 ** -6, 1000), np.linspace(0, 463.9, 20000)])
+    pts = pts.astype(np.float32)
+    return np.concatenate([pts, -pts])
+
+
+def check_e4m3_against_library():
+    # Encoder == torch's float8_e4m3fn cast (round to nearest, ties to even) on the sweep.
+    x = _e4m3_sweep()
+    got = QZ.e4m3_encode(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref), int(np.sum(got != ref))
+    # Decoder == the library's conversion back to float on all 256 codes.
+    c = np.arange(256, dtype=np.uint8)
+    d = QZ.e4m3_decode(c)
+    dl = torch.from_numpy(c).view(torch.float8_e4m3fn).double().numpy()
+    assert np.all((d == dl) | (np.isnan(d) & np.isnan(dl)))
+
+
+def check_fp8_row_quantizer():
+    rng = np.random.default_rng(71)
+    X = (rng.standard_normal((300, 64)) * np.exp(rng.uniform(-8, 8, (300, 1)))).astype(np.float32)
+    X[5] = 0.0
+    codes, scale = QZ.quantize_rows(X)
+    # scale = max |x| / 448 in float32; the zero row keeps scale 0 and codes 0
+    assert np.array_equal(scale, (np.max(np.abs(X), axis=1) / np.float32(448.0)).astype(np.float32))
+    assert scale[5] == 0 and not codes[5].any()
+    R = QZ.dequantize_rows(codes, scale)
+    x64 = X.astype(np.float64)
+    # the largest element of every nonzero row takes magnitude code 0x7E (448)
+    nz = scale > 0
+    big = np.argmax(np.abs(X), axis=1)
+    assert np.all((codes[np.arange(300), big][nz] & 0x7F) == 0x7E)
+    # error within half a quantum of the E4M3 binade of x / s (plus the float32 rounding of x / s)
+    t = np.where(nz[:, None], np.abs(x64) / np.where(nz, scale, 1)[:, None].astype(np.float64), 0)
+    e = np.maximum(np.floor(np.log2(np.maximum(t, 2.0 ** -6))), -6)
+    half_quantum = np.exp2(e - 4) * scale[:, None]
+    assert np.all(np.abs(R - x64) <= half_quantum * (1 + 2.0 ** -20) + np.abs(x64) * 2.0 ** -23)
+    # rows already on the E4M3 grid times a power-of-two scale come back exactly
+    grid = QZ.e4m3_decode(rng.integers(0, 126, (10, 64)).astype(np.uint8)).astype(np.float32)
+    grid[:, 0] = 448.0
+    c2, s2 = QZ.quantize_rows(grid * np.float32(0.25))
+    assert np.array_equal(QZ.dequantize_rows(c2, s2), grid.astype(np.float64) * 0.25)
+
+
+def check_fp8_attention_routes():
+    # Rows already on the E4M3 grid times a power-of-two scale are stored exactly,
+    # so the FP8 routes reduce to the native ones; with a single chunk nothing is
+    # held and prefill sees only the chunk, as given.
+    rng = np.random.default_rng(81)
+    n_q, n_kv, N, d, S, W = 4, 2, 23, 8, 2, 5
+    codes = rng.integers(0, 126, (n_kv, N, d)).astype(np.uint8)
+    K = (QZ.e4m3_decode(codes) * 0.5).astype(np.float32); K[..., 0] = 224.0
+    V = (QZ.e4m3_decode(rng.integers(0, 126, (n_kv, N, d)).astype(np.uint8)) * 0.25).astype(np.float32)
+    V[..., 0] = 112.0
+    Q = rng.standard_normal((n_q, N, d)) * 0.05
+    for mask in ([1, 0], [0, 1]):
+        ref = A.prefill_full(Q, K, V, mask, S, W, 0.3)
+        for C in (1, 5, N):
+            assert np.allclose(QZ.prefill_chunked_fp8(Q, K, V, mask, S, W, 0.3, C), ref, atol=1e-12, rtol=0)
+        assert np.allclose(QZ.decode_step_fp8(Q[:, -1], K, V, mask, S, W, 0.3), ref[:, -1], atol=1e-12, rtol=0)
+    # Off the grid, a single chunk still equals full attention on the exact rows,
+    # while decode sees the stored rows.
+    K2 = rng.standard_normal((n_kv, N, d)).astype(np.float32)
+    V2 = rng.standard_normal((n_kv, N, d)).astype(np.float32)
+    ref = A.prefill_full(Q, K2, V2, [1, 0], S, W, 0.3)
+    assert np.allclose(QZ.prefill_chunked_fp8(Q, K2, V2, [1, 0], S, W, 0.3, N), ref, atol=1e-12, rtol=0)
+    dq = A.decode_step(Q[:, -1], QZ.stored_values(K2), QZ.stored_values(V2), [1, 0], S, W, 0.3)
+    assert np.allclose(QZ.decode_step_fp8(Q[:, -1], K2, V2, [1, 0], S, W, 0.3), dq, atol=1e-12, rtol=0)
+
+
 ALL_CHECKS = [
     check_printed_kv_sizes, check_effective_context, check_mixed_payload_closed_forms,
     check_ring_example, check_streaming_composition, check_simulation_counts, check_keep_set_is_visible_set,
     check_hand_cases, check_bruteforce_agrees, check_library_special_cases,
     check_softmax_invariants, check_chunk_invariance, check_gqa_expansion,
     check_gated_hand_case, check_gated_library_endpoints, check_gated_bruteforce_agrees,
-    check_gated_gqa_expansion,
+    check_gated_gqa_expansion, check_e4m3_against_library, check_fp8_row_quantizer,
+    check_fp8_attention_routes,
 ]
 
 

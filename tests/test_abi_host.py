@@ -38,6 +38,19 @@ def test_payload_matches_closed_form(name):
     assert ws > 0
 
 
+@pytest.mark.parametrize("name", ["gqa70b_decode_128k", "mha7b_decode_128k", "llama3_8b_prefill_64k"])
+def test_fp8_payload_closed_form(name):
+    """FP8 rows: one byte per element plus one fp32 scale per stored K and V row."""
+    w = WL.WORKLOADS[name]
+    mask = WL.mask_table(w)
+    _, ws, payload = H.cache_bytes(w.L, w.B, w.n_q, w.n_kv, w.d, w.T, w.S, w.W, w.dtype, mask, "fp8")
+    codes = Z.mixed_payload_bytes(mask.tolist(), w.B, w.T, w.S, w.W, w.d, 1)
+    scales = Z.mixed_payload_bytes(mask.tolist(), w.B, w.T, w.S, w.W, 1, 4)
+    assert payload == codes + scales
+    _, ws_native, native = H.cache_bytes(w.L, w.B, w.n_q, w.n_kv, w.d, w.T, w.S, w.W, w.dtype, mask)
+    assert payload < native * 0.52 and ws > ws_native
+
+
 def test_payload_reproduces_printed_examples():
     # 70B GQA, all heads retrieval: the printed 41,943,040,000 bytes.
     _, _, p = H.cache_bytes(80, 1, 64, 8, 128, 128000, 64, 1024, "bf16", [[1] * 8] * 80)
@@ -63,6 +76,9 @@ BAD = [
     (dict(L=0), H.DUO_EINVAL),
     (dict(mask_value=2), H.DUO_EINVAL),
     (dict(dtype_code=7), H.DUO_EUNSUPPORTED),
+    (dict(kv_format=5), H.DUO_EUNSUPPORTED),
+    (dict(kv_format=1, dtype_code=0), H.DUO_EUNSUPPORTED),   # FP8 rows need bf16
+    (dict(kv_format=1, d_head=64), H.DUO_EUNSUPPORTED),      # FP8 rows are built for d_head 128
 ]
 
 
@@ -75,7 +91,7 @@ def test_validation_codes(over, code):
     buf = (ctypes.c_uint8 * max(n_mask, 1))(*([mv] * max(n_mask, 1)))
     cfg = H.duo_config(base["L"], base["B"], base["n_q"], base["n_kv"], base["d_head"], base["T_cap"],
                        base["sink"], base["recent"], over.get("dtype_code", H.DUO_BF16),
-                       ctypes.cast(buf, ctypes.POINTER(ctypes.c_uint8)))
+                       ctypes.cast(buf, ctypes.POINTER(ctypes.c_uint8)), over.get("kv_format", 0))
     a = ctypes.c_size_t()
     rc = H.lib.duo_cache_bytes(ctypes.byref(cfg), ctypes.byref(a), None)
     assert rc == code, H.lib.duo_last_error()
@@ -94,6 +110,7 @@ def test_calls_on_null_handle_fail_cleanly():
     assert H.lib.duo_append(None, 0, None, None, 1, None) == H.DUO_EINVAL
     assert H.lib.duo_decode(None, 0, None, None, 1.0, None, 0, None) == H.DUO_EINVAL
     assert H.lib.duo_decode_append(None, 0, None, None, None, None, 1.0, None, 0, None) == H.DUO_EINVAL
+    assert H.lib.duo_cache_head_scales(None, 0, 0, None, None, None) == H.DUO_EINVAL
     H.lib.duo_cache_free(None)
 
 

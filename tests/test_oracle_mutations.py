@@ -6,6 +6,7 @@ import pytest
 from oracle import attention as A
 from oracle import cache as Cc
 from oracle import gating as G
+from oracle import quant as QZ
 from oracle import sizes as Z
 from tests import oracle_checks as OC
 
@@ -74,6 +75,17 @@ def _gate_by_query_mod(alpha, n_q):
     return np.array([float(alpha[h % n_kv]) for h in range(n_q)])  # transposed gate mapping
 
 
+def _round_half_up(y):
+    return np.floor(y + 0.5)                       # ties away from even
+
+
+def _quantize_rows_256(X):
+    X = np.asarray(X, dtype=np.float32)
+    scale = (np.max(np.abs(X), axis=-1) / np.float32(256.0)).astype(np.float32)  # wrong range
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    return QZ.e4m3_encode((X / safe[..., None]).astype(np.float32)), scale
+
+
 def _kv_bytes_one_factor(L, n_kv, d_head, T, elem_bytes=2):
     return elem_bytes * L * n_kv * d_head * T      # dropped K+V factor
 
@@ -90,6 +102,8 @@ MUTATIONS = {
     "kv_bytes_factor": (Z, "kv_cache_bytes", _kv_bytes_one_factor),
     "gate_swapped": (G, "blend", _blend_swapped),
     "gate_mod_mapping": (G, "gate_of_query_heads", _gate_by_query_mod),
+    "e4m3_ties_up": (QZ, "_round_half_even", _round_half_up),
+    "fp8_scale_range": (QZ, "quantize_rows", _quantize_rows_256),
 }
 
 

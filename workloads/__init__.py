@@ -58,6 +58,7 @@ class Workload:
     mode: str               # "decode" | "decode_append" | "prefill" | "gated"
     chunk: int = 0          # prefill chunk length
     fixed_mask: Optional[tuple] = None  # explicit per-layer mask rows, else seeded
+    kv_format: Optional[str] = None     # "fp8": K/V rows stored as FP8 codes + row scales
 
     @property
     def g(self) -> int:
@@ -66,6 +67,11 @@ class Workload:
     @property
     def elem_bytes(self) -> int:
         return 4 if self.dtype == "f32" else 2
+
+    @property
+    def kv_row_bytes(self) -> int:
+        """Bytes of one stored K (or V) row: d elements, plus an fp32 scale for FP8 rows."""
+        return self.d + 4 if self.kv_format == "fp8" else self.d * self.elem_bytes
 
     @property
     def scale(self) -> float:
@@ -102,8 +108,13 @@ WORKLOADS: Dict[str, Workload] = {
                                     dtype="bf16", T=32768, S=64, W=1024, n_ret=0,
                                     sink_scale=1.0, mode="gated"),
 }
-# Workloads that run on the mixed cache (the gated forward does not).
-ORDER: List[str] = [n for n, w in WORKLOADS.items() if w.mode != "gated"]
+# The two 128k decode workloads again with the cache's K/V rows stored as FP8
+# (same shapes and inputs).
+for _n in ("gqa70b_decode_128k", "mha7b_decode_128k"):
+    WORKLOADS[_n + "_fp8"] = WORKLOADS[_n].with_(name=_n + "_fp8", kv_format="fp8")
+# Workloads that run on the mixed cache in the cache dtype (the gated forward
+# runs on none, the FP8 variants repeat shapes already listed).
+ORDER: List[str] = [n for n, w in WORKLOADS.items() if w.mode != "gated" and w.kv_format is None]
 
 
 def _rng(w: Workload, layer: int, b: int, head: int, tensor_id: int, block: int) -> np.random.Generator:
