@@ -27,7 +27,8 @@ ERROR_NAMES = {DUO_EINVAL: "DUO_EINVAL", DUO_EUNSUPPORTED: "DUO_EUNSUPPORTED", D
 # Every entry point declared in include/duo.h.
 EXPORTS = ("duo_cache_bytes", "duo_cache_payload_bytes", "duo_cache_init", "duo_append", "duo_decode",
            "duo_decode_append", "duo_prefill_chunk", "duo_cache_seq_len", "duo_cache_head_view", "duo_cache_free",
-           "duo_last_error", "duo_gated_attention", "duo_cache_head_scales")
+           "duo_last_error", "duo_gated_attention", "duo_cache_head_scales", "duo_append_row", "duo_prefill_chunk_row",
+           "duo_cache_row_len")
 
 
 class DuoError(RuntimeError):
@@ -67,6 +68,9 @@ def _load():
                                         ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
     lib.duo_gated_attention.argtypes = [ctypes.POINTER(duo_gated_shape), vp, vp, vp, vp, vp, ctypes.c_float, vp]
     lib.duo_cache_head_scales.argtypes = [vp, i32, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(i64)]
+    lib.duo_append_row.argtypes = [vp, i32, i32, vp, vp, i64, vp]
+    lib.duo_prefill_chunk_row.argtypes = [vp, i32, i32, vp, vp, vp, i64, vp, ctypes.c_float, vp, sz, vp]
+    lib.duo_cache_row_len.argtypes = [vp, i32, i32, ctypes.POINTER(i64)]
     lib.duo_cache_free.argtypes = [vp]
     lib.duo_cache_free.restype = None
     lib.duo_last_error.argtypes = []
@@ -238,9 +242,40 @@ class DuoCache:
         return out
 
     def seq_len(self, layer: int) -> int:
+        """Token count of the layer's rows (they must hold equal counts)."""
         x = ctypes.c_int64()
         _check(lib.duo_cache_seq_len(self._h, layer, ctypes.byref(x)))
         return x.value
+
+    def row_len(self, layer: int, row: int) -> int:
+        x = ctypes.c_int64()
+        _check(lib.duo_cache_row_len(self._h, layer, row, ctypes.byref(x)))
+        return x.value
+
+    def append_row(self, layer: int, row: int, k: torch.Tensor, v: torch.Tensor, stream=None) -> None:
+        """Append n tokens (k, v: [1][n_kv][n][d]) to batch row `row` alone."""
+        n = k.shape[2] if k.dim() == 4 else -1
+        self._chk(k, (1, self.n_kv, n, self.d), "k")
+        self._chk(v, (1, self.n_kv, n, self.d), "v")
+        _check(lib.duo_append_row(self._h, layer, row, ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                                  n, _stream_handle(stream)))
+
+    def prefill_chunk_row(self, layer: int, row: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          out: Optional[torch.Tensor] = None, scale: Optional[float] = None, stream=None) -> torch.Tensor:
+        """Chunked prefill of batch row `row` alone (q: [1][n_q][C][d], k, v: [1][n_kv][C][d])."""
+        C = q.shape[2] if q.dim() == 4 else -1
+        self._chk(q, (1, self.n_q, C, self.d), "q")
+        self._chk(k, (1, self.n_kv, C, self.d), "k")
+        self._chk(v, (1, self.n_kv, C, self.d), "v")
+        if out is None:
+            out = torch.empty_like(q)
+        self._chk(out, (1, self.n_q, C, self.d), "out")
+        sc = float(self.d ** -0.5 if scale is None else scale)
+        _check(lib.duo_prefill_chunk_row(self._h, layer, row, ctypes.c_void_p(q.data_ptr()),
+                                         ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()), C,
+                                         ctypes.c_void_p(out.data_ptr()), sc, ctypes.c_void_p(self.workspace.data_ptr()),
+                                         self.workspace.numel(), _stream_handle(stream)))
+        return out
 
     def head_view(self, layer: int, kv_head: int) -> dict:
         """Device addresses and strides of one KV head's rows (for layout checks)."""

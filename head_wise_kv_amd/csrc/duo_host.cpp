@@ -68,6 +68,7 @@ int validate(const duo_config* c) {
     return fail(DUO_EINVAL, "L, B, n_q, n_kv must be >= 1 (got %d, %d, %d, %d)", c->L, c->B, c->n_q, c->n_kv);
   if (c->n_q % c->n_kv != 0) return fail(DUO_EINVAL, "n_q (%d) must be a multiple of n_kv (%d)", c->n_q, c->n_kv);
   if (c->n_kv > duo::kMaxKV) return fail(DUO_EUNSUPPORTED, "n_kv %d > %d", c->n_kv, duo::kMaxKV);
+  if (c->B > duo::kMaxRows) return fail(DUO_EUNSUPPORTED, "B %d > %d batch rows", c->B, duo::kMaxRows);
   if (!supported_group(c->n_q / c->n_kv))
     return fail(DUO_EUNSUPPORTED, "group size g = %d not built (1, 2, 4, 8)", c->n_q / c->n_kv);
   if (c->d_head != 64 && c->d_head != 128) return fail(DUO_EUNSUPPORTED, "d_head %d not built (64, 128)", c->d_head);
@@ -160,7 +161,7 @@ struct duo_cache {
   Plan plan;
   char* arena = nullptr;
   size_t arena_bytes = 0;
-  std::vector<int64_t> seq_len;
+  std::vector<int64_t> row_len;  // tokens held by each (layer, batch row), advanced at enqueue time
   int num_cu = 256;  // compute units of the device current at init (decode work items per call)
 
   duo::LayerPtrs ptrs(int l) const {
@@ -179,6 +180,39 @@ struct duo_cache {
     return p;
   }
   int64_t cap_str() const { return (int64_t)cfg.sink + cfg.recent; }
+  int64_t len(int l, int b) const { return row_len[(size_t)l * cfg.B + b]; }
+  int64_t& len(int l, int b) { return row_len[(size_t)l * cfg.B + b]; }
+  // the common token count of a layer's rows, or -1 if they differ
+  int64_t uniform_len(int l) const {
+    for (int b = 1; b < cfg.B; ++b)
+      if (len(l, b) != len(l, 0)) return -1;
+    return len(l, 0);
+  }
+  int64_t max_len(int l) const {
+    int64_t m = 0;
+    for (int b = 0; b < cfg.B; ++b) m = std::max(m, len(l, b));
+    return m;
+  }
+  // The layer seen as a cache of one batch row (row b): every region starts at
+  // that row's part of the [B][...] arrays.
+  duo::LayerPtrs row_ptrs(int l, int b) const {
+    const LayerPlan& lp = plan.layers[l];
+    duo::LayerPtrs p = ptrs(l);
+    const size_t ret_rows = (size_t)b * lp.n_ret * cfg.T_cap, str_rows = (size_t)b * lp.n_str * cap_str();
+    const size_t rb = (size_t)row_bytes();
+    p.k_ret += ret_rows * rb;
+    p.v_ret += ret_rows * rb;
+    p.k_str += str_rows * rb;
+    p.v_str += str_rows * rb;
+    p.pos += str_rows;
+    if (p.ksc_ret) {
+      p.ksc_ret += ret_rows;
+      p.vsc_ret += ret_rows;
+      p.ksc_str += str_rows;
+      p.vsc_str += str_rows;
+    }
+    return p;
+  }
   int row_bytes() const { return cfg.d_head * kv_elem_bytes(&cfg); }     // stored K/V row
   int in_row_bytes() const { return cfg.d_head * elem_bytes(&cfg); }     // input / query row
   bool fp8() const { return cfg.kv_format == DUO_KV_FP8; }
@@ -192,16 +226,18 @@ int check_layer(const duo_cache* c, int layer) {
   return DUO_OK;
 }
 
-// Enqueue the append of n_new tokens at positions p0.. (no validation).
-hipError_t enqueue_append(duo_cache* c, int layer, const void* k, const void* v, int64_t p0, int64_t n_new,
-                          hipStream_t s) {
+// Enqueue the append of n_new tokens to every batch row at its own token
+// count, or (row >= 0) to that one row only, the inputs then being
+// [1][n_kv][n_new][d] (no validation).
+hipError_t enqueue_append(duo_cache* c, int layer, const void* k, const void* v, int64_t n_new, hipStream_t s,
+                          int row = -1) {
   const LayerPlan& lp = c->plan.layers[layer];
   duo::AppendArgs a{};
   a.k = static_cast<const char*>(k);
   a.v = static_cast<const char*>(v);
-  a.lp = c->ptrs(layer);
+  a.lp = row < 0 ? c->ptrs(layer) : c->row_ptrs(layer, row);
   a.map = lp.map;
-  a.B = c->cfg.B;
+  a.B = row < 0 ? c->cfg.B : 1;
   a.n_kv = c->cfg.n_kv;
   a.n_ret = lp.n_ret;
   a.n_str = lp.n_str;
@@ -209,11 +245,10 @@ hipError_t enqueue_append(duo_cache* c, int layer, const void* k, const void* v,
   a.in_row_bytes = c->in_row_bytes();
   a.cap_ret = c->cfg.T_cap;
   a.cap_str = c->cap_str();
-  a.p0 = p0;
+  for (int b = 0; b < a.B; ++b) a.p0[b] = (int32_t)c->len(layer, row < 0 ? b : row);
   a.n_new = n_new;
   a.S = c->cfg.sink;
   a.W = c->cfg.recent;
-  a.keep_from = std::max<int64_t>(a.S, p0 + n_new - a.W);
   return duo::launch_append(a, c->cfg.dtype, c->cfg.d_head, c->fp8(), s);
 }
 
@@ -256,7 +291,7 @@ int duo_cache_init(const duo_config* cfg, void* arena, size_t arena_bytes, void*
   c->plan = p;
   c->arena = static_cast<char*>(arena);
   c->arena_bytes = arena_bytes;
-  c->seq_len.assign(cfg->L, 0);
+  c->row_len.assign((size_t)cfg->L * cfg->B, 0);
   {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
@@ -282,13 +317,29 @@ int duo_append(duo_cache* c, int layer, const void* k, const void* v, int64_t n_
   if (!k || !v) return fail(DUO_EINVAL, "k or v is NULL");
   if (!aligned16(k) || !aligned16(v)) return fail(DUO_EINVAL, "k and v must be 16-byte aligned");
   if (n_new < 1) return fail(DUO_EINVAL, "n_new must be >= 1 (got %lld)", (long long)n_new);
-  const int64_t p0 = c->seq_len[layer];
-  if (p0 + n_new > c->cfg.T_cap)
-    return fail(DUO_ECAPACITY, "layer %d holds %lld tokens; %lld more exceed T_cap %lld", layer, (long long)p0,
-                (long long)n_new, (long long)c->cfg.T_cap);
-  hipError_t e = enqueue_append(c, layer, k, v, p0, n_new, static_cast<hipStream_t>(stream));
+  const int64_t pmax = c->max_len(layer);
+  if (pmax + n_new > c->cfg.T_cap)
+    return fail(DUO_ECAPACITY, "layer %d has a row of %lld tokens; %lld more exceed T_cap %lld", layer,
+                (long long)pmax, (long long)n_new, (long long)c->cfg.T_cap);
+  hipError_t e = enqueue_append(c, layer, k, v, n_new, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "append launch");
-  c->seq_len[layer] = p0 + n_new;
+  for (int b = 0; b < c->cfg.B; ++b) c->len(layer, b) += n_new;
+  return ok();
+}
+
+int duo_append_row(duo_cache* c, int layer, int row, const void* k, const void* v, int64_t n_new, void* stream) {
+  if (int e = check_layer(c, layer)) return e;
+  if (row < 0 || row >= c->cfg.B) return fail(DUO_EINVAL, "row %d out of range [0, %d)", row, c->cfg.B);
+  if (!k || !v) return fail(DUO_EINVAL, "k or v is NULL");
+  if (!aligned16(k) || !aligned16(v)) return fail(DUO_EINVAL, "k and v must be 16-byte aligned");
+  if (n_new < 1) return fail(DUO_EINVAL, "n_new must be >= 1 (got %lld)", (long long)n_new);
+  const int64_t p0 = c->len(layer, row);
+  if (p0 + n_new > c->cfg.T_cap)
+    return fail(DUO_ECAPACITY, "row %d of layer %d holds %lld tokens; %lld more exceed T_cap %lld", row, layer,
+                (long long)p0, (long long)n_new, (long long)c->cfg.T_cap);
+  hipError_t e = enqueue_append(c, layer, k, v, n_new, static_cast<hipStream_t>(stream), row);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  c->len(layer, row) = p0 + n_new;
   return ok();
 }
 
@@ -305,10 +356,10 @@ int check_decode_args(const duo_cache* c, const void* q, void* out, float scale,
   return DUO_OK;
 }
 
-// Enqueue the decode kernels over rows_ret / rows_str held rows per head; with
-// new_k / new_v set, the token at position `held` (rows held per retrieval
-// head) is appended and attended by the same launch.
-hipError_t enqueue_decode(duo_cache* c, int layer, const void* q, void* out, float scale, void* ws, int64_t held,
+// Enqueue the decode kernels over the rows each batch row holds (its token
+// count); with new_k / new_v set, every row's next token (at its token count)
+// is appended and attended by the same launch.
+hipError_t enqueue_decode(duo_cache* c, int layer, const void* q, void* out, float scale, void* ws,
                           const void* new_k, const void* new_v, hipStream_t stream) {
   const LayerPlan& lp = c->plan.layers[layer];
   const duo_config& cf = c->cfg;
@@ -324,50 +375,68 @@ hipError_t enqueue_decode(duo_cache* c, int layer, const void* q, void* out, flo
   a.n_str = lp.n_str;
   a.cap_ret = cf.T_cap;
   a.cap_str = c->cap_str();
-  a.rows_ret = held;
-  a.rows_str = std::min<int64_t>(held, c->cap_str());
+  const int64_t S = cf.sink, W = cf.recent;
+  for (int b = 0; b < cf.B; ++b) {
+    duo::DecodeRow& R = a.rows[b];
+    const int64_t held = c->len(layer, b);
+    R.rows_ret = (int32_t)held;
+    R.rows_str = (int32_t)std::min<int64_t>(held, c->cap_str());
+    R.new_pos = (int32_t)held;
+    R.new_slot_str = (int32_t)(held < S ? held : S + (held - S) % W);
+    R.excl_str = (new_k && held >= S + W) ? R.new_slot_str : -1;  // the ring is full: the new token evicts
+  }
   if (new_k) {
-    const int64_t p = held, S = cf.sink, W = cf.recent;
     a.new_k = static_cast<const char*>(new_k);
     a.new_v = static_cast<const char*>(new_v);
-    a.new_row_ret = p;
-    a.new_slot_str = p < S ? p : S + (p - S) % W;
-    a.excl_str = p >= S + W ? a.new_slot_str : -1;  // the ring is full: the new token evicts
-    a.new_pos = (int32_t)p;
-  } else {
-    a.excl_str = -1;
   }
-  // Work items: contiguous row ranges of one head, as many as one workgroup
-  // per compute unit (or one per head if there are more heads), none shorter
-  // than one round of the kernel where the head allows.  The split between
-  // retrieval and streaming heads minimises the longest item (the launch ends
-  // with it): e.g. cutting each streaming head in two can beat leaving it
-  // whole when its held rows exceed a retrieval item's share.
+  // Work items: contiguous row ranges of one head, at most one workgroup per
+  // compute unit (or one per head if there are more heads), none shorter
+  // than one round of the kernel where the head allows.  All heads are cut to
+  // a common item length t, the smallest with which the items fit: the
+  // launch ends with its longest item, so the items' lengths are balanced
+  // across retrieval and streaming heads and across batch rows of different
+  // lengths (e.g. a 1,088-row streaming head is cut in two when a 128k
+  // retrieval head's items hold about 1,050 rows).
   const int g = cf.n_q / cf.n_kv;
-  const int64_t heads_ret = (int64_t)cf.B * lp.n_ret, heads_str = (int64_t)cf.B * lp.n_str;
-  const int64_t slots = std::max<int64_t>(std::min(c->num_cu, duo::kMaxDecodeBlocks), heads_ret + heads_str);
-  const int64_t R = duo::decode_round_rows(cf.dtype, cf.d_head, g, c->fp8());
-  const int64_t max_r = std::max<int64_t>(1, ceil_div(a.rows_ret, R));
-  const int64_t max_s = std::max<int64_t>(1, ceil_div(a.rows_str, R));
-  int64_t nb_r = 1, nb_s = 1, best = -1;
-  for (int64_t ns = 1; ns <= max_s; ++ns) {
-    const int64_t left = slots - heads_str * ns;
-    if (left < heads_ret) break;
-    const int64_t nr = heads_ret > 0 ? std::min(max_r, left / heads_ret) : 1;
-    const int64_t cost = std::max(heads_ret > 0 ? ceil_div(a.rows_ret, nr) : 0,
-                                  heads_str > 0 ? ceil_div(a.rows_str, ns) : 0);
-    if (best < 0 || cost < best) {
-      best = cost;
-      nb_r = nr;
-      nb_s = ns;
-    }
-    if (heads_str == 0) break;
+  const int64_t heads = (int64_t)cf.B * (lp.n_ret + lp.n_str);
+  const int64_t slots = std::max<int64_t>(std::min(c->num_cu, duo::kMaxDecodeBlocks), heads);
+  const int64_t R0 = duo::decode_round_rows(cf.dtype, cf.d_head, g, c->fp8());
+  auto items = [&](int64_t rows, int64_t t) { return std::max<int64_t>(1, ceil_div(rows, t)); };
+  auto count = [&](int64_t t) {
+    int64_t n = 0;
+    for (int b = 0; b < cf.B; ++b)
+      n += lp.n_ret * items(a.rows[b].rows_ret, t) + lp.n_str * items(a.rows[b].rows_str, t);
+    return n;
+  };
+  int64_t longest = 1;
+  for (int b = 0; b < cf.B; ++b) longest = std::max<int64_t>(longest, std::max(a.rows[b].rows_ret, a.rows[b].rows_str));
+  int64_t lo = std::min(R0, longest), hi = longest;  // count(hi) <= heads <= slots
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (count(mid) <= slots) hi = mid;
+    else lo = mid + 1;
   }
-  nb_r = ceil_div(a.rows_ret, ceil_div(a.rows_ret, nb_r));  // no empty item
-  nb_s = ceil_div(a.rows_str, ceil_div(a.rows_str, nb_s));
-  a.nb_ret = (int)nb_r;
-  a.nb_str = (int)nb_s;
-  const int blocks = (int)(heads_ret * nb_r + heads_str * nb_s);
+  const int64_t t = lo;
+  int32_t next = 0;
+  a.multi = 0;
+  for (int b = 0; b < cf.B; ++b) {  // retrieval items of every row, then streaming
+    duo::DecodeRow& R = a.rows[b];
+    const int64_t nr = items(R.rows_ret, t);
+    R.nb_ret = (int32_t)(R.rows_ret > 0 ? ceil_div(R.rows_ret, ceil_div(R.rows_ret, nr)) : 1);  // no empty item
+    R.first_ret = next;
+    next += lp.n_ret * R.nb_ret;
+    if (lp.n_ret > 0 && R.nb_ret > 1) a.multi = 1;
+  }
+  a.items_ret = next;
+  for (int b = 0; b < cf.B; ++b) {
+    duo::DecodeRow& R = a.rows[b];
+    const int64_t ns = items(R.rows_str, t);
+    R.nb_str = (int32_t)(R.rows_str > 0 ? ceil_div(R.rows_str, ceil_div(R.rows_str, ns)) : 1);
+    R.first_str = next;
+    next += lp.n_str * R.nb_str;
+    if (lp.n_str > 0 && R.nb_str > 1) a.multi = 1;
+  }
+  const int blocks = (int)next;
   a.ws1 = static_cast<float*>(ws);
   a.scale_log2 = scale * 1.4426950408889634f;
   return duo::launch_decode(a, cf.dtype, cf.d_head, g, c->fp8(), blocks, stream);
@@ -379,9 +448,9 @@ int duo_decode(duo_cache* c, int layer, const void* q, void* out, float scale, v
                void* stream) {
   if (int e = check_layer(c, layer)) return e;
   if (int e = check_decode_args(c, q, out, scale, ws, ws_bytes)) return e;
-  const int64_t T = c->seq_len[layer];
-  if (T < 1) return fail(DUO_EEMPTY, "layer %d holds no token", layer);
-  hipError_t e = enqueue_decode(c, layer, q, out, scale, ws, T, nullptr, nullptr, static_cast<hipStream_t>(stream));
+  for (int b = 0; b < c->cfg.B; ++b)
+    if (c->len(layer, b) < 1) return fail(DUO_EEMPTY, "row %d of layer %d holds no token", b, layer);
+  hipError_t e = enqueue_decode(c, layer, q, out, scale, ws, nullptr, nullptr, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
 }
@@ -392,26 +461,29 @@ int duo_decode_append(duo_cache* c, int layer, const void* k, const void* v, con
   if (!k || !v) return fail(DUO_EINVAL, "k or v is NULL");
   if (!aligned16(k) || !aligned16(v)) return fail(DUO_EINVAL, "k and v must be 16-byte aligned");
   if (int e = check_decode_args(c, q, out, scale, ws, ws_bytes)) return e;
-  const int64_t p = c->seq_len[layer];
-  if (p + 1 > c->cfg.T_cap)
-    return fail(DUO_ECAPACITY, "layer %d holds %lld tokens; one more exceeds T_cap %lld", layer, (long long)p,
-                (long long)c->cfg.T_cap);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (p == 0) {  // nothing held yet: append, then decode over the one token
-    e = enqueue_append(c, layer, k, v, 0, 1, s);
-    if (e == hipSuccess) e = enqueue_decode(c, layer, q, out, scale, ws, 1, nullptr, nullptr, s);
-  } else {
-    e = enqueue_decode(c, layer, q, out, scale, ws, p, k, v, s);
-  }
+  const int64_t pmax = c->max_len(layer);
+  if (pmax + 1 > c->cfg.T_cap)
+    return fail(DUO_ECAPACITY, "layer %d has a row of %lld tokens; one more exceeds T_cap %lld", layer,
+                (long long)pmax, (long long)c->cfg.T_cap);
+  // one launch: each row attends over what it holds and its new token, which
+  // the kernel also stores (a row that holds nothing yet attends to the new
+  // token alone)
+  hipError_t e = enqueue_decode(c, layer, q, out, scale, ws, k, v, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
-  c->seq_len[layer] = p + 1;
+  for (int b = 0; b < c->cfg.B; ++b) c->len(layer, b) += 1;
   return ok();
 }
 
-int duo_prefill_chunk(duo_cache* c, int layer, const void* q, const void* k, const void* v, int64_t C, void* out,
-                      float scale, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Chunked prefill of every batch row (row < 0; the rows must hold equal
+// counts) or of batch row `row` alone (inputs [1][...]).
+int prefill_impl(duo_cache* c, int layer, int row, const void* q, const void* k, const void* v, int64_t C, void* out,
+                 float scale, void* ws, size_t ws_bytes, void* stream) {
   if (int e = check_layer(c, layer)) return e;
+  if (row >= c->cfg.B) return fail(DUO_EINVAL, "row %d out of range [0, %d)", row, c->cfg.B);
   if (c->fp8()) {
     if (!ws || ws_bytes < c->plan.workspace)
       return fail(DUO_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", c->plan.workspace, ws_bytes);
@@ -422,7 +494,10 @@ int duo_prefill_chunk(duo_cache* c, int layer, const void* q, const void* k, con
     return fail(DUO_EINVAL, "q, k, v and out must be 16-byte aligned");
   if (!std::isfinite(scale) || !(scale > 0.f)) return fail(DUO_EINVAL, "scale must be finite and > 0");
   if (C < 1) return fail(DUO_EINVAL, "chunk length must be >= 1 (got %lld)", (long long)C);
-  const int64_t P = c->seq_len[layer];
+  const int64_t P = row < 0 ? c->uniform_len(layer) : c->len(layer, row);
+  if (P < 0)
+    return fail(DUO_EINVAL, "the rows of layer %d hold different token counts; prefill them one at a time "
+                "(duo_prefill_chunk_row)", layer);
   if (P + C > c->cfg.T_cap)
     return fail(DUO_ECAPACITY, "layer %d holds %lld tokens; a chunk of %lld exceeds T_cap %lld", layer,
                 (long long)P, (long long)C, (long long)c->cfg.T_cap);
@@ -434,9 +509,9 @@ int duo_prefill_chunk(duo_cache* c, int layer, const void* q, const void* k, con
   a.k = k;
   a.v = v;
   a.out = out;
-  a.lp = c->ptrs(layer);
+  a.lp = row < 0 ? c->ptrs(layer) : c->row_ptrs(layer, row);
   a.map = lp.map;
-  a.B = cf.B;
+  a.B = row < 0 ? cf.B : 1;
   a.n_q = cf.n_q;
   a.n_kv = cf.n_kv;
   a.n_ret = lp.n_ret;
@@ -453,7 +528,7 @@ int duo_prefill_chunk(duo_cache* c, int layer, const void* q, const void* k, con
   int rows = 1, hpi = 1;
   duo::prefill_plan(cf.dtype, cf.d_head, g, &rows, &hpi);
   a.q_tiles = (int)ceil_div(C, rows);
-  a.items_ret = cf.B * lp.n_ret * (g / hpi) * a.q_tiles;
+  a.items_ret = a.B * lp.n_ret * (g / hpi) * a.q_tiles;
   hipError_t e = hipSuccess;
   if (c->fp8()) {
     // the held rows, dequantized to bf16 in the workspace (after the decode
@@ -461,17 +536,17 @@ int duo_prefill_chunk(duo_cache* c, int layer, const void* q, const void* k, con
     const int64_t cap_r = std::max<int64_t>(P, 1);
     const size_t bf_row = (size_t)cf.d_head * 2;
     char* base = static_cast<char*>(ws) + c->plan.ws_records;
-    const size_t ret_b = align_up((size_t)cf.B * lp.n_ret * cap_r * bf_row);
-    const size_t str_b = align_up((size_t)cf.B * lp.n_str * c->cap_str() * bf_row);
+    const size_t ret_b = align_up((size_t)a.B * lp.n_ret * cap_r * bf_row);
+    const size_t str_b = align_up((size_t)a.B * lp.n_str * c->cap_str() * bf_row);
     duo::DequantArgs d{};
-    d.src = c->ptrs(layer);
+    d.src = a.lp;
     d.dst = duo::LayerPtrs{};
     d.dst.k_ret = base;
     d.dst.v_ret = base + ret_b;
     d.dst.k_str = base + 2 * ret_b;
     d.dst.v_str = base + 2 * ret_b + str_b;
-    d.heads_ret = (int64_t)cf.B * lp.n_ret;
-    d.heads_str = (int64_t)cf.B * lp.n_str;
+    d.heads_ret = (int64_t)a.B * lp.n_ret;
+    d.heads_str = (int64_t)a.B * lp.n_str;
     d.cap_ret_src = cf.T_cap;
     d.cap_ret_dst = cap_r;
     d.rows_ret = P;
@@ -489,16 +564,44 @@ int duo_prefill_chunk(duo_cache* c, int layer, const void* q, const void* k, con
   e = duo::launch_prefill(a, cf.dtype, cf.d_head, g, s);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   // Commit the chunk after attention has read the cache (same stream).
-  e = enqueue_append(c, layer, k, v, P, C, s);
+  e = enqueue_append(c, layer, k, v, C, s, row);
   if (e != hipSuccess) return hip_fail(e, "prefill commit launch");
-  c->seq_len[layer] = P + C;
+  if (row < 0)
+    for (int b = 0; b < cf.B; ++b) c->len(layer, b) = P + C;
+  else
+    c->len(layer, row) = P + C;
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int duo_prefill_chunk(duo_cache* c, int layer, const void* q, const void* k, const void* v, int64_t C, void* out,
+                      float scale, void* ws, size_t ws_bytes, void* stream) {
+  return prefill_impl(c, layer, -1, q, k, v, C, out, scale, ws, ws_bytes, stream);
+}
+
+int duo_prefill_chunk_row(duo_cache* c, int layer, int row, const void* q, const void* k, const void* v, int64_t C,
+                          void* out, float scale, void* ws, size_t ws_bytes, void* stream) {
+  if (row < 0) return fail(DUO_EINVAL, "row %d out of range", row);
+  return prefill_impl(c, layer, row, q, k, v, C, out, scale, ws, ws_bytes, stream);
 }
 
 int duo_cache_seq_len(const duo_cache* c, int layer, int64_t* out) {
   if (int e = check_layer(c, layer)) return e;
   if (!out) return fail(DUO_EINVAL, "out is NULL");
-  *out = c->seq_len[layer];
+  const int64_t n = c->uniform_len(layer);
+  if (n < 0) return fail(DUO_EINVAL, "the rows of layer %d hold different token counts (duo_cache_row_len)", layer);
+  *out = n;
+  return ok();
+}
+
+int duo_cache_row_len(const duo_cache* c, int layer, int row, int64_t* out) {
+  if (int e = check_layer(c, layer)) return e;
+  if (row < 0 || row >= c->cfg.B) return fail(DUO_EINVAL, "row %d out of range [0, %d)", row, c->cfg.B);
+  if (!out) return fail(DUO_EINVAL, "out is NULL");
+  *out = c->len(layer, row);
   return ok();
 }
 

@@ -11,6 +11,7 @@
 namespace duo {
 
 constexpr int kMaxKV = 128;        // KV heads per layer the head maps can hold
+constexpr int kMaxRows = 64;       // batch rows per cache (each row keeps its own token count)
 constexpr int kMaxDecodeBlocks = 1024;  // decode work items per call at most
 constexpr int kDecodeThreads = 512;  // 8 wavefronts of 64
 
@@ -46,9 +47,20 @@ struct AppendArgs {
   int row_bytes;      // bytes per stored row
   int in_row_bytes;   // bytes per input row (equal unless the rows are stored as FP8)
   int64_t cap_ret, cap_str;
-  int64_t p0, n_new;      // first position, tokens
-  int64_t keep_from;      // streaming ring writes only for p >= keep_from
+  int64_t n_new;          // tokens per batch row
+  int32_t p0[kMaxRows];   // first position of each batch row (its token count before the call)
   int S, W;
+};
+
+// Per batch row of a decode: its held rows, its work items and, for a fused
+// append, where its new token goes.
+struct DecodeRow {
+  int32_t rows_ret, rows_str;    // rows held per retrieval / streaming head (before a fused append)
+  int32_t nb_ret, nb_str;        // work items per retrieval / streaming head of this row (each >= 1)
+  int32_t first_ret, first_str;  // index of the first work item of the row's retrieval / streaming heads
+  int32_t new_pos;               // fused append: position of the new token (its retrieval row)
+  int32_t new_slot_str;          // ... its streaming slot
+  int32_t excl_str;              // ... the streaming slot whose old token it evicts (-1: none)
 };
 
 struct DecodeArgs {
@@ -59,19 +71,16 @@ struct DecodeArgs {
   float* ws1;      // partial records [work item][g][d + 2]
   int B, n_q, n_kv, n_ret, n_str;
   int64_t cap_ret, cap_str;     // rows reserved per head
-  int64_t rows_ret, rows_str;   // rows held per head
-  int nb_ret, nb_str;           // work items per retrieval / streaming head (each >= 1 row)
+  int32_t items_ret;            // work items of all retrieval heads (they come first)
+  int32_t multi;                // nonzero if some head spans several work items
   float scale_log2;             // softmax scale * log2(e)
   // Fused append (decode of a token appended by the same call); new_k is
-  // null for a plain decode.  rows_ret / rows_str then count the rows held
-  // before the append; the last work item of every head adds the new token
-  // and writes it to the cache.
+  // null for a plain decode.  The rows counts are then those held before the
+  // append; the last work item of every head adds the new token and writes
+  // it to the cache.
   const char* new_k;            // [B][n_kv][d]
   const char* new_v;
-  int64_t new_row_ret;          // row of the new token in a retrieval head (its position)
-  int64_t new_slot_str;         // slot of the new token in a streaming head
-  int64_t excl_str;             // streaming slot whose old token the new one evicts (-1: none)
-  int32_t new_pos;              // position of the new token
+  DecodeRow rows[kMaxRows];     // items ordered: row 0's retrieval heads, row 1's, ..., then streaming likewise
 };
 
 struct PrefillArgs {

@@ -42,6 +42,8 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+__device__ __forceinline__ int64_t max64d(int64_t x, int64_t y) { return x > y ? x : y; }
+
 // Orders LDS traffic between lanes of one wavefront.
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -76,11 +78,13 @@ __global__ void fill_zero_kernel(uint4* p, size_t n16, unsigned char* tail, size
 }
 
 // ------------------------------------------------------------------ append
-// One thread per 16-byte chunk of an input row.  Position p = p0 + i goes to
-// row p of a retrieval head; for a streaming head to slot p while p < S, else
-// to ring slot S + (p - S) mod W, but only if the token is among the last W of
-// the batch (p >= keep_from); earlier ones would be evicted by later tokens of
-// the same call, and skipping them keeps every slot written at most once.
+// One thread per 16-byte chunk of an input row.  Token i of batch row b is at
+// position p = p0[b] + i; it goes to row p of a retrieval head; for a
+// streaming head to slot p while p < S, else to ring slot S + (p - S) mod W,
+// but only if the token is among the last W of the call's tokens for its row
+// (p >= max(S, p0[b] + n_new - W)); earlier ones would be evicted by later
+// tokens of the same call, and skipping them keeps every slot written at most
+// once.
 
 __global__ void append_kernel(AppendArgs a) {
   const int cpr = a.row_bytes / 16;
@@ -93,7 +97,8 @@ __global__ void append_kernel(AppendArgs a) {
     rest /= a.n_new;
     const int kvh = (int)(rest % a.n_kv);
     const int b = (int)(rest / a.n_kv);
-    const int64_t p = a.p0 + i;
+    const int64_t p = a.p0[b] + i;
+    const int64_t keep_from = max64d((int64_t)a.S, (int64_t)a.p0[b] + a.n_new - a.W);
     const size_t src = (size_t)idx * 16;
     char *kd, *vd;
     if (a.map.kind[kvh]) {
@@ -105,7 +110,7 @@ __global__ void append_kernel(AppendArgs a) {
       int64_t slot;
       if (p < a.S) {
         slot = p;
-      } else if (p >= a.keep_from) {
+      } else if (p >= keep_from) {
         slot = a.S + (p - a.S) % a.W;
       } else {
         continue;
@@ -341,7 +346,8 @@ __global__ void append_fp8_kernel(AppendArgs a) {
   rest /= a.n_new;
   const int kvh = (int)(rest % a.n_kv);
   const int b = (int)(rest / a.n_kv);
-  const int64_t p = a.p0 + i;
+  const int64_t p = a.p0[b] + i;
+  const int64_t keep_from = max64d((int64_t)a.S, (int64_t)a.p0[b] + a.n_new - a.W);
   const size_t src = (((size_t)b * a.n_kv + kvh) * a.n_new + i) * a.in_row_bytes + (size_t)j * 16;
   float sc;
   const uint2 codes = quant_row16(ld16((tensor ? a.v : a.k) + src), sc);
@@ -354,7 +360,7 @@ __global__ void append_fp8_kernel(AppendArgs a) {
   } else {
     int64_t slot;
     if (p < a.S) slot = p;
-    else if (p >= a.keep_from) slot = a.S + (p - a.S) % a.W;
+    else if (p >= keep_from) slot = a.S + (p - a.S) % a.W;
     else return;
     const size_t hrow = ((size_t)b * a.n_str + a.map.cidx[kvh]) * a.cap_str + slot;
     dst = (tensor ? a.lp.v_str : a.lp.k_str) + hrow * a.row_bytes;
@@ -430,13 +436,15 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // A work item is a contiguous row range of one head.  Heads are numbered
-// retrieval first ((b, r) -> b * n_ret + r), then streaming; each retrieval
-// head is cut into nb_ret items and each streaming head into nb_str.
+// retrieval first ((b, r) -> b * n_ret + r), then streaming; the retrieval
+// heads of batch row b are cut into rows[b].nb_ret items each and its
+// streaming heads into rows[b].nb_str; items follow the same order.
 struct DecodeItem {
   int64_t hh;       // head number
   int64_t r0, r1;   // rows of the head
   int part, nparts;
   int b, kvh;
+  int row;          // batch row (index into DecodeArgs::rows)
   char* kbase;
   char* vbase;
   float* ksc;       // FP8 rows: per-row scales of the head (else null)
@@ -446,41 +454,50 @@ struct DecodeItem {
 template <int ROWB>
 __device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a, int64_t blk) {
   DecodeItem w;
-  const int64_t n_ret_items = (int64_t)a.B * a.n_ret * a.nb_ret;
   int64_t rows;
-  if (blk < n_ret_items) {
-    w.hh = blk / a.nb_ret;
-    w.part = (int)(blk % a.nb_ret);
-    w.nparts = a.nb_ret;
-    rows = a.rows_ret;
-    w.b = (int)(w.hh / a.n_ret);
-    const int r = (int)(w.hh % a.n_ret);
+  if (blk < a.items_ret) {
+    int b = 0;
+    while (b + 1 < a.B && blk >= a.rows[b + 1].first_ret) ++b;  // batch row of the item (uniform)
+    const DecodeRow& R = a.rows[b];
+    const int64_t rel = blk - R.first_ret;
+    const int r = (int)(rel / R.nb_ret);
+    w.part = (int)(rel % R.nb_ret);
+    w.nparts = R.nb_ret;
+    rows = R.rows_ret;
+    w.row = b;
+    w.b = b;
+    w.hh = (int64_t)b * a.n_ret + r;
     w.kvh = a.map.orig_ret[r];
-    const size_t off = ((size_t)w.b * a.n_ret + r) * a.cap_ret * ROWB;
+    const size_t off = ((size_t)b * a.n_ret + r) * a.cap_ret * ROWB;
     w.kbase = a.lp.k_ret + off;
     w.vbase = a.lp.v_ret + off;
-    const size_t srow = ((size_t)w.b * a.n_ret + r) * a.cap_ret;
+    const size_t srow = ((size_t)b * a.n_ret + r) * a.cap_ret;
     w.ksc = a.lp.ksc_ret ? a.lp.ksc_ret + srow : nullptr;
     w.vsc = a.lp.vsc_ret ? a.lp.vsc_ret + srow : nullptr;
   } else {
-    const int64_t x = (blk - n_ret_items) / a.nb_str;
-    w.hh = (int64_t)a.B * a.n_ret + x;
-    w.part = (int)((blk - n_ret_items) % a.nb_str);
-    w.nparts = a.nb_str;
-    rows = a.rows_str;
-    w.b = (int)(x / a.n_str);
-    const int si = (int)(x % a.n_str);
+    int b = 0;
+    while (b + 1 < a.B && blk >= a.rows[b + 1].first_str) ++b;
+    const DecodeRow& R = a.rows[b];
+    const int64_t rel = blk - R.first_str;
+    const int si = (int)(rel / R.nb_str);
+    w.part = (int)(rel % R.nb_str);
+    w.nparts = R.nb_str;
+    rows = R.rows_str;
+    w.row = b;
+    w.b = b;
+    w.hh = (int64_t)a.B * a.n_ret + (int64_t)b * a.n_str + si;
     w.kvh = a.map.orig_str[si];
-    const size_t off = ((size_t)w.b * a.n_str + si) * a.cap_str * ROWB;
+    const size_t off = ((size_t)b * a.n_str + si) * a.cap_str * ROWB;
     w.kbase = a.lp.k_str + off;
     w.vbase = a.lp.v_str + off;
-    const size_t srow = ((size_t)w.b * a.n_str + si) * a.cap_str;
+    const size_t srow = ((size_t)b * a.n_str + si) * a.cap_str;
     w.ksc = a.lp.ksc_str ? a.lp.ksc_str + srow : nullptr;
     w.vsc = a.lp.vsc_str ? a.lp.vsc_str + srow : nullptr;
   }
   const int64_t per = (rows + w.nparts - 1) / w.nparts;
   w.r0 = w.part * per;
   w.r1 = w.r0 + per < rows ? w.r0 + per : rows;
+  if (w.r0 > rows) w.r0 = rows;
   return w;
 }
 
@@ -882,7 +899,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   const bool add_new = a.new_k != nullptr && w.part == w.nparts - 1;
   const bool ret_head = w.hh < (int64_t)a.B * a.n_ret;
   // streaming slot masked in the held rows (its token is evicted by the new one)
-  const int64_t excl_row = (a.new_k != nullptr && !ret_head) ? a.excl_str : -1;
+  const int64_t excl_row = (a.new_k != nullptr && !ret_head) ? a.rows[w.row].excl_str : -1;
   // per-lane byte offset, within a round of rows, of this wavefront's load
   // pieces: piece n of a unit covers LDS bytes [n*1024, n*1024+1024), lane i
   // byte n*1024 + 16 i, i.e. row (n*1024 + 16 i) / ROWB of the round at a
@@ -1047,7 +1064,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
         tile_pv<KT, D, G>(st, p, ring1, rg, s);
       }
     }
-    const int64_t row = ret_head ? a.new_row_ret : a.new_slot_str;
+    const int64_t row = ret_head ? a.rows[w.row].new_pos : a.rows[w.row].new_slot_str;
     if constexpr (KV8) {
       if (wave == 0 && lane < 32) {
         const int t = lane >> 4, j = lane & 15;
@@ -1062,7 +1079,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     }
     if (wave == 0 && lane == 0 && !ret_head) {
       const int64_t si = w.hh - (int64_t)a.B * a.n_ret;  // b * n_str + streaming index
-      a.lp.pos[si * a.cap_str + a.new_slot_str] = a.new_pos;
+      a.lp.pos[si * a.cap_str + a.rows[w.row].new_slot_str] = a.rows[w.row].new_pos;
     }
   }
 
@@ -1182,16 +1199,18 @@ __global__ __launch_bounds__(kDecodeThreads) void combine_kernel(DecodeArgs a) {
   int64_t first;
   int n_seg, b, kvh;
   if (hh < n_ret_heads) {
-    first = hh * a.nb_ret;
-    n_seg = a.nb_ret;
     b = (int)(hh / a.n_ret);
-    kvh = a.map.orig_ret[hh % a.n_ret];
+    const int r = (int)(hh % a.n_ret);
+    first = a.rows[b].first_ret + (int64_t)r * a.rows[b].nb_ret;
+    n_seg = a.rows[b].nb_ret;
+    kvh = a.map.orig_ret[r];
   } else {
     const int64_t x = hh - n_ret_heads;
-    first = n_ret_heads * a.nb_ret + x * a.nb_str;
-    n_seg = a.nb_str;
     b = (int)(x / a.n_str);
-    kvh = a.map.orig_str[x % a.n_str];
+    const int si = (int)(x % a.n_str);
+    first = a.rows[b].first_str + (int64_t)si * a.rows[b].nb_str;
+    n_seg = a.rows[b].nb_str;
+    kvh = a.map.orig_str[si];
   }
   if (n_seg == 1) return;  // written by the decode kernel
   const float* rec0 = a.ws1 + (size_t)first * C::REC;
@@ -1248,7 +1267,7 @@ hipError_t launch_decode_g(const DecodeArgs& a, int blocks, hipStream_t s) {
   decode_kernel<KT, D, G><<<blocks, kDecodeThreads, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.nb_ret == 1 && a.nb_str == 1) return hipSuccess;  // every head finished in one item
+  if (!a.multi) return hipSuccess;  // every head finished in one item
   const int64_t heads = (int64_t)a.B * (a.n_ret + a.n_str);
   combine_kernel<KT, D, G><<<(unsigned)(heads * G * (D / kCombineElems)), kDecodeThreads, 0, s>>>(a);
   return hipGetLastError();

@@ -66,7 +66,9 @@ typedef enum { DUO_F32 = 0, DUO_BF16 = 1 } duo_dtype;
 typedef enum { DUO_KV_NATIVE = 0, DUO_KV_FP8 = 1 } duo_kv_format;
 
 /* Cache configuration.  d_head in {64, 128}; g = n_q / n_kv in {1, 2, 4, 8};
- * n_kv <= 128; S >= 0; W >= 1; T_cap >= 1.  retrieval_mask is a host array
+ * n_kv <= 128; 1 <= B <= 64; S >= 0; W >= 1; T_cap >= 1.  Each batch row keeps
+ * its own token count (a ragged batch allocates T_cap rows per retrieval head
+ * and row, and attends over what each row holds).  retrieval_mask is a host array
  * uint8 [L][n_kv] (1 = retrieval head, 0 = streaming head); it is copied. */
 typedef struct {
   int32_t L, B, n_q, n_kv, d_head;
@@ -102,31 +104,42 @@ int duo_cache_payload_bytes(const duo_config* cfg, size_t* payload_bytes);
 int duo_cache_init(const duo_config* cfg, void* arena, size_t arena_bytes, void* stream,
                    duo_cache** out);
 
-/* Append n_new >= 1 tokens to `layer` at positions seq_len .. seq_len+n_new-1.
- * k, v: device [B][n_kv][n_new][d].  A retrieval head stores position p in
+/* Append n_new >= 1 tokens to every batch row of `layer`, row b at positions
+ * len_b .. len_b+n_new-1 where len_b is its token count.  k, v: device
+ * [B][n_kv][n_new][d].  A retrieval head stores position p in
  * row p.  A streaming head stores p in slot p while p < S, and otherwise in
  * ring slot S + ((p - S) mod W) (sinks fill first, then the window of the
  * guide's section 2; the ring slot rule of "Attention Variants and Memory
  * Efficiency", "Sliding-Window and Mixed Attention"); tokens of the batch that
  * would be evicted before the call ends are not written.  Each written
  * streaming slot records p in its position array.  DUO_ECAPACITY if
- * seq_len + n_new > T_cap. */
+ * some row would exceed T_cap. */
 int duo_append(duo_cache* c, int layer, const void* k, const void* v, int64_t n_new, void* stream);
 
-/* One decode step on `layer`: the query of every head is the token at
- * position seq_len-1, which the caller has appended.  q, out: device
- * [B][n_q][d].  Retrieval heads attend over positions 0..seq_len-1; streaming
- * heads over their min(seq_len, S+W) held tokens (exactly the sinks and the W
+/* duo_append for batch row `row` alone: k, v device [1][n_kv][n_new][d],
+ * positions len_row .. len_row+n_new-1.  With it and duo_prefill_chunk_row
+ * the rows of a batch grow independently (a ragged batch: the cache a request
+ * needs is its own rows, "Attention Variants and Memory Efficiency", "A
+ * Closer Look at Attention Memory"). */
+int duo_append_row(duo_cache* c, int layer, int row, const void* k, const void* v, int64_t n_new, void* stream);
+
+/* One decode step on `layer`: the query of every head of batch row b is the
+ * token at position len_b-1 (its row's token count less one), which the
+ * caller has appended; rows may hold different counts.  q, out: device
+ * [B][n_q][d].  Retrieval heads attend over positions 0..len_b-1; streaming
+ * heads over their min(len_b, S+W) held tokens (exactly the sinks and the W
  * most recent positions the query may see).  out = softmax(scale * q K^T) V
  * over those keys, accumulated in fp32 and rounded to the cache dtype.
  * ws: device workspace of ws_bytes >= duo_cache_bytes' workspace_bytes.
- * DUO_EEMPTY if the layer holds no token. */
+ * DUO_EEMPTY if a row holds no token. */
 int duo_decode(duo_cache* c, int layer, const void* q, void* out, float scale, void* ws,
                size_t ws_bytes, void* stream);
 
-/* One generation step in a single launch: append one token and decode the
- * query at its position.  Same result and cache state as duo_append(k, v, 1)
- * followed by duo_decode(q): the new token attends to the cached keys of the
+/* One generation step in a single launch: append one token to every batch
+ * row (at that row's own count) and decode the query at its position.  Same
+ * result and cache state as duo_append(k, v, 1) followed by duo_decode(q)
+ * (also for a row that held no token yet): the new token attends to the
+ * cached keys of the
  * earlier tokens and to its own, and appending leaves the earlier cached
  * states unchanged ("Attention Variants and KV-Cache Compression", "When Is
  * Reuse Exact?").  Fusing the two neighbouring operations saves a launch per
@@ -134,14 +147,15 @@ int duo_decode(duo_cache* c, int layer, const void* q, void* out, float scale, v
  * Inference Runtime Can Change").  The token is written to its row or ring
  * slot while the held rows are read; a streaming slot whose token it evicts
  * is left out of the attention.  k, v: device [B][n_kv][1][d]; q, out: device
- * [B][n_q][d]; ws as for duo_decode.  DUO_ECAPACITY if the layer is full;
- * other errors as duo_append and duo_decode.  The layer advances by one
+ * [B][n_q][d]; ws as for duo_decode.  DUO_ECAPACITY if some row is full;
+ * other errors as duo_append and duo_decode.  Every row advances by one
  * token. */
 int duo_decode_append(duo_cache* c, int layer, const void* k, const void* v, const void* q, void* out,
                       float scale, void* ws, size_t ws_bytes, void* stream);
 
 /* Chunked prefill of C >= 1 tokens on `layer`, at positions P .. P+C-1 with
- * P = seq_len ("Attention Variants and KV-Cache Compression", "When Is Reuse
+ * P = the rows' token count, equal in every row (DUO_EINVAL otherwise)
+ * ("Attention Variants and KV-Cache Compression", "When Is Reuse
  * Exact?": chunk row i attends through absolute key position P + i, and
  * evicted tokens keep their original positions).  q, out: device
  * [B][n_q][C][d]; k, v: device [B][n_kv][C][d].  Retrieval heads: causal
@@ -156,8 +170,17 @@ int duo_decode_append(duo_cache* c, int layer, const void* k, const void* v, con
 int duo_prefill_chunk(duo_cache* c, int layer, const void* q, const void* k, const void* v,
                       int64_t C, void* out, float scale, void* ws, size_t ws_bytes, void* stream);
 
-/* Host-side token count of a layer (advanced at enqueue time). */
+/* duo_prefill_chunk for batch row `row` alone, at P = that row's token count:
+ * q, out device [1][n_q][C][d]; k, v device [1][n_kv][C][d]. */
+int duo_prefill_chunk_row(duo_cache* c, int layer, int row, const void* q, const void* k, const void* v, int64_t C,
+                          void* out, float scale, void* ws, size_t ws_bytes, void* stream);
+
+/* Host-side token count of a layer whose rows hold equal counts (advanced at
+ * enqueue time); DUO_EINVAL if the rows differ. */
 int duo_cache_seq_len(const duo_cache* c, int layer, int64_t* out);
+
+/* Host-side token count of one batch row of a layer. */
+int duo_cache_row_len(const duo_cache* c, int layer, int row, int64_t* out);
 
 /* Where one KV head's rows live, for bit-exact inspection of the layout.
  * *k_base / *v_base: device address of the head's first row (batch row b at

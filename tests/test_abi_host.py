@@ -77,6 +77,7 @@ BAD = [
     (dict(mask_value=2), H.DUO_EINVAL),
     (dict(dtype_code=7), H.DUO_EUNSUPPORTED),
     (dict(kv_format=5), H.DUO_EUNSUPPORTED),
+    (dict(B=65), H.DUO_EUNSUPPORTED),                          # at most 64 batch rows
     (dict(kv_format=1, dtype_code=0), H.DUO_EUNSUPPORTED),   # FP8 rows need bf16
     (dict(kv_format=1, d_head=64), H.DUO_EUNSUPPORTED),      # FP8 rows are built for d_head 128
 ]
@@ -111,6 +112,9 @@ def test_calls_on_null_handle_fail_cleanly():
     assert H.lib.duo_decode(None, 0, None, None, 1.0, None, 0, None) == H.DUO_EINVAL
     assert H.lib.duo_decode_append(None, 0, None, None, None, None, 1.0, None, 0, None) == H.DUO_EINVAL
     assert H.lib.duo_cache_head_scales(None, 0, 0, None, None, None) == H.DUO_EINVAL
+    assert H.lib.duo_append_row(None, 0, 0, None, None, 1, None) == H.DUO_EINVAL
+    assert H.lib.duo_prefill_chunk_row(None, 0, 0, None, None, None, 1, None, 1.0, None, 0, None) == H.DUO_EINVAL
+    assert H.lib.duo_cache_row_len(None, 0, 0, ctypes.byref(x)) == H.DUO_EINVAL
     H.lib.duo_cache_free(None)
 
 
