@@ -16,6 +16,7 @@ import oracle
 from oracle import attention as A
 from oracle import cache as Cc
 from oracle import gating as G
+from oracle import paging as PG
 from oracle import quant as QZ
 from oracle import sizes as Z
 
@@ -382,6 +383,64 @@ def check_fp8_attention_routes():
     assert np.allclose(QZ.decode_step_fp8(Q[:, -1], K2, V2, [1, 0], S, W, 0.3), dq, atol=1e-12, rtol=0)
 
 
+# ------------------------------------------------------------------ paged rows
+
+def check_paging_closed_forms():
+    P = 256
+    # rows that never share: each holds ceil(n / P) pages (a ragged batch
+    # allocates per request, not the padded B * ceil(max n / P))
+    lens = [1, 255, 256, 257, 1000, 0, 4096]
+    m = PG.PagedRows(P, 10_000, len(lens))
+    for b, n in enumerate(lens):
+        if n:
+            m.append(b, n)
+    assert m.pages_in_use() == 1 + 1 + 1 + 2 + 4 + 0 + 16
+    assert m.pages_in_use() < len(lens) * (4096 // P)
+    # a prefix of n tokens forked from row 0 to rows 1..k, then row r appends
+    # m_r: floor(n/P) shared pages + each row's own ceil((n + m_r)/P) - floor(n/P)
+    for n in (0, 100, 256, 600, 1024):
+        ms = [0, 5, 300, 1, 700]
+        m = PG.PagedRows(P, 10_000, len(ms))
+        if n:
+            m.append(0, n)
+        for r in range(1, len(ms)):
+            m.fork(0, r)
+        for r, mr in enumerate(ms):
+            if mr:
+                m.append(r, mr)
+        want = n // P + sum(-(-(n + mr) // P) - n // P for mr in ms)
+        assert m.pages_in_use() == want, (n, m.pages_in_use(), want)
+        for r in range(1, len(ms)):
+            assert m.shared_pages(0, r) == n // P
+        # every row holds the prefix (from row 0) and then its own tokens
+        for r, mr in enumerate(ms):
+            assert m.content(r) == [(0, p) for p in range(n)] + [(r, p) for p in range(n, n + mr)]
+        # resets return everything
+        for r in range(len(ms)):
+            m.reset(r)
+        assert m.pages_in_use() == 0 and m.free_pages() == 10_000
+
+
+def check_paging_capacity():
+    m = PG.PagedRows(256, 3, 2)
+    m.append(0, 600)                         # 3 pages
+    before = (m.pages_in_use(), list(m.count))
+    for grow in ([(1, 1)], [(0, 200)], [(0, 1), (1, 1)]):
+        try:
+            m.append_rows(grow)
+            raise AssertionError("grew past the pool")
+        except MemoryError:
+            pass
+        assert (m.pages_in_use(), list(m.count)) == before
+    m.append(0, 168)                         # fills page 3 exactly: no new page
+    assert m.pages_in_use() == 3 and m.count[0] == 768
+    try:
+        m.fork(0, 1)                         # all pages full: shared, nothing copied
+    except MemoryError:
+        raise AssertionError("a fork of full pages needs no page")
+    assert m.pages_in_use() == 3 and m.shared_pages(0, 1) == 3
+
+
 ALL_CHECKS = [
     check_printed_kv_sizes, check_effective_context, check_mixed_payload_closed_forms,
     check_ring_example, check_streaming_composition, check_simulation_counts, check_keep_set_is_visible_set,
@@ -389,7 +448,7 @@ ALL_CHECKS = [
     check_softmax_invariants, check_chunk_invariance, check_gqa_expansion,
     check_gated_hand_case, check_gated_library_endpoints, check_gated_bruteforce_agrees,
     check_gated_gqa_expansion, check_e4m3_against_library, check_fp8_row_quantizer,
-    check_fp8_attention_routes,
+    check_fp8_attention_routes, check_paging_closed_forms, check_paging_capacity,
 ]
 
 
@@ -398,6 +457,6 @@ def failing_checks():
     for c in ALL_CHECKS:
         try:
             c()
-        except AssertionError:
+        except Exception:  # a failed assertion, or a planted mistake that crashes a check
             bad.append(c.__name__)
     return bad

@@ -6,6 +6,7 @@ import pytest
 from oracle import attention as A
 from oracle import cache as Cc
 from oracle import gating as G
+from oracle import paging as PG
 from oracle import quant as QZ
 from oracle import sizes as Z
 from tests import oracle_checks as OC
@@ -90,6 +91,26 @@ def _kv_bytes_one_factor(L, n_kv, d_head, T, elem_bytes=2):
     return elem_bytes * L * n_kv * d_head * T      # dropped K+V factor
 
 
+def _fork_copies_all(self, src, dst):
+    n = self.count[src]
+    pages = []
+    for pg in self.rows[src]:                      # every page copied: no sharing
+        c = PG._Page(self.P)
+        c.slots = list(pg.slots)
+        pages.append(c)
+    self.rows[dst] = pages
+    self.count[dst] = n
+
+
+def _fork_shares_partial(self, src, dst):
+    self.rows[dst] = list(self.rows[src])          # the partly filled page shared too
+    self.count[dst] = self.count[src]
+
+
+def _pages_floor(self, n):
+    return n // self.P                             # a partial page not counted
+
+
 MUTATIONS = {
     "window_too_wide": (A, "visible_matrix", _window_too_wide),
     "sinks_off_by_one": (A, "visible_matrix", _sinks_off_by_one),
@@ -104,6 +125,9 @@ MUTATIONS = {
     "gate_mod_mapping": (G, "gate_of_query_heads", _gate_by_query_mod),
     "e4m3_ties_up": (QZ, "_round_half_even", _round_half_up),
     "fp8_scale_range": (QZ, "quantize_rows", _quantize_rows_256),
+    "fork_copies_all": (PG.PagedRows, "fork", _fork_copies_all),
+    "fork_shares_partial": (PG.PagedRows, "fork", _fork_shares_partial),
+    "pages_floor": (PG.PagedRows, "pages_needed", _pages_floor),
 }
 
 
