@@ -28,7 +28,8 @@ ERROR_NAMES = {DUO_EINVAL: "DUO_EINVAL", DUO_EUNSUPPORTED: "DUO_EUNSUPPORTED", D
 EXPORTS = ("duo_cache_bytes", "duo_cache_payload_bytes", "duo_cache_init", "duo_append", "duo_decode",
            "duo_decode_append", "duo_prefill_chunk", "duo_cache_seq_len", "duo_cache_head_view", "duo_cache_free",
            "duo_last_error", "duo_gated_attention", "duo_cache_head_scales", "duo_append_row", "duo_prefill_chunk_row",
-           "duo_cache_row_len")
+           "duo_cache_row_len", "duo_cache_reset_row", "duo_cache_fork_row", "duo_cache_free_pages",
+           "duo_cache_row_pages")
 
 
 class DuoError(RuntimeError):
@@ -41,7 +42,8 @@ class duo_config(ctypes.Structure):
     _fields_ = [("L", ctypes.c_int32), ("B", ctypes.c_int32), ("n_q", ctypes.c_int32), ("n_kv", ctypes.c_int32),
                 ("d_head", ctypes.c_int32), ("T_cap", ctypes.c_int64), ("sink", ctypes.c_int32),
                 ("recent", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("retrieval_mask", ctypes.POINTER(ctypes.c_uint8)), ("kv_format", ctypes.c_int32)]
+                ("retrieval_mask", ctypes.POINTER(ctypes.c_uint8)), ("kv_format", ctypes.c_int32),
+                ("page_rows", ctypes.c_int32), ("n_pages", ctypes.c_int32)]
 
 
 class duo_gated_shape(ctypes.Structure):
@@ -108,21 +110,25 @@ def _kv_code(kv_format) -> int:
     raise ValueError(f"unknown kv_format {kv_format}")
 
 
-def make_config(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask, kv_format=None):
-    """(duo_config, keep-alive mask buffer)."""
+def make_config(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask, kv_format=None, page_rows=0,
+                n_pages=0):
+    """(duo_config, keep-alive mask buffer).  page_rows > 0 stores retrieval
+    rows in pages of that many rows, n_pages per layer."""
     import numpy as np
     m = torch.from_numpy(np.asarray(mask, dtype=np.uint8).reshape(-1).copy())
     if m.numel() != L * n_kv:
         raise ValueError(f"mask must hold L*n_kv = {L * n_kv} entries, got {m.numel()}")
     buf = (ctypes.c_uint8 * m.numel())(*m.tolist())
     cfg = duo_config(L, B, n_q, n_kv, d_head, int(T_cap), sink, recent, _dtype_code(dtype),
-                     ctypes.cast(buf, ctypes.POINTER(ctypes.c_uint8)), _kv_code(kv_format))
+                     ctypes.cast(buf, ctypes.POINTER(ctypes.c_uint8)), _kv_code(kv_format), int(page_rows),
+                     int(n_pages))
     return cfg, buf
 
 
-def cache_bytes(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask, kv_format=None):
+def cache_bytes(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask, kv_format=None, page_rows=0, n_pages=0):
     """(arena bytes, workspace bytes, K+V payload bytes) -- host-only size query."""
-    cfg, _buf = make_config(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask, kv_format)
+    cfg, _buf = make_config(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask, kv_format, page_rows,
+                            n_pages)
     a, w, p = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
     _check(lib.duo_cache_bytes(ctypes.byref(cfg), ctypes.byref(a), ctypes.byref(w)))
     _check(lib.duo_cache_payload_bytes(ctypes.byref(cfg), ctypes.byref(p)))
@@ -140,17 +146,22 @@ class DuoCache:
     Tensors: K/V inputs [B][n_kv][n][d], queries/outputs [B][n_q][d] (decode)
     or [B][n_q][C][d] (prefill), all contiguous in the cache dtype on the
     cache's device.  kv_format "fp8" stores the K/V rows as FP8 codes with one
-    scale per row (bf16 caches with d_head 128).
+    scale per row (bf16 caches with d_head 128).  page_rows > 0 stores the
+    retrieval rows in pages (n_pages per layer) that rows take as they grow
+    and can share (fork_row).
     """
 
     def __init__(self, L: int, B: int, n_q: int, n_kv: int, d_head: int, T_cap: int, sink: int, recent: int,
-                 dtype, mask: Sequence, device="cuda", stream: Optional[torch.cuda.Stream] = None, kv_format=None):
+                 dtype, mask: Sequence, device="cuda", stream: Optional[torch.cuda.Stream] = None, kv_format=None,
+                 page_rows: int = 0, n_pages: int = 0):
         self.L, self.B, self.n_q, self.n_kv, self.d = L, B, n_q, n_kv, d_head
         self.T_cap, self.S, self.W = int(T_cap), sink, recent
+        self.page_rows, self.n_pages = int(page_rows), int(n_pages)
         self.torch_dtype = torch.bfloat16 if _dtype_code(dtype) == DUO_BF16 else torch.float32
         self.kv_format = _kv_code(kv_format)
         self.device = torch.device(device)
-        self._cfg, self._mask_buf = make_config(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask, kv_format)
+        self._cfg, self._mask_buf = make_config(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask, kv_format,
+                                                page_rows, n_pages)
         import numpy as np
         self.mask = torch.from_numpy(np.asarray(mask, dtype=np.uint8).reshape(L, n_kv).copy())
         a, w = ctypes.c_size_t(), ctypes.c_size_t()
@@ -252,6 +263,27 @@ class DuoCache:
         _check(lib.duo_cache_row_len(self._h, layer, row, ctypes.byref(x)))
         return x.value
 
+    def reset_row(self, layer: int, row: int) -> None:
+        """Empty batch row `row` of `layer` (its pages return to the pool)."""
+        _check(lib.duo_cache_reset_row(self._h, layer, row))
+
+    def fork_row(self, layer: int, src_row: int, dst_row: int, stream=None) -> None:
+        """Make empty row dst_row a copy of row src_row (paged: sharing its full pages)."""
+        _check(lib.duo_cache_fork_row(self._h, layer, src_row, dst_row, _stream_handle(stream)))
+
+    def free_pages(self, layer: int) -> int:
+        x = ctypes.c_int64()
+        _check(lib.duo_cache_free_pages(self._h, layer, ctypes.byref(x)))
+        return x.value
+
+    def row_pages(self, layer: int, row: int) -> list:
+        """Page numbers batch row `row` of a paged layer holds, in position order."""
+        n = ctypes.c_int64()
+        _check(lib.duo_cache_row_pages(self._h, layer, row, None, 0, ctypes.byref(n)))
+        buf = (ctypes.c_int32 * max(n.value, 1))()
+        _check(lib.duo_cache_row_pages(self._h, layer, row, buf, n.value, ctypes.byref(n)))
+        return list(buf[: n.value])
+
     def append_row(self, layer: int, row: int, k: torch.Tensor, v: torch.Tensor, stream=None) -> None:
         """Append n tokens (k, v: [1][n_kv][n][d]) to batch row `row` alone."""
         n = k.shape[2] if k.dim() == 4 else -1
@@ -295,8 +327,12 @@ class DuoCache:
         _check(lib.duo_cache_head_scales(self._h, layer, kv_head, ctypes.byref(ks), ctypes.byref(vs), ctypes.byref(st)))
         if not ks.value:
             return None, None
-        rows = self.head_view(layer, kv_head)["n_slots"]
+        hv = self.head_view(layer, kv_head)
         base = self.arena.data_ptr()
+        if self._paged_head(hv):
+            return tuple(self._gather_pages(layer, ptr - base, st.value * 4, 4).view(torch.float32)
+                         .reshape(self.B, -1) for ptr in (ks.value, vs.value))
+        rows = hv["n_slots"]
         out = []
         for ptr in (ks.value, vs.value):
             off = ptr - base
@@ -304,15 +340,38 @@ class DuoCache:
             out.append(seg.cpu().view(torch.float32).reshape(self.B, rows))
         return out[0], out[1]
 
+    def _paged_head(self, hv: dict) -> bool:
+        return bool(hv["is_retrieval"]) and self.page_rows > 0
+
+    def _gather_pages(self, layer: int, off: int, page_stride: int, row_bytes: int) -> torch.Tensor:
+        """Bytes of one paged head's positions 0 .. ceil(T_cap / page_rows) * page_rows - 1
+        for every batch row, [B][positions * row_bytes] on the host, read through
+        the row's page table (positions on no page read as zero bytes)."""
+        P = self.page_rows
+        n_pos = -(-self.T_cap // P) * P
+        out = torch.zeros(self.B, n_pos * row_bytes, dtype=torch.uint8)
+        for b in range(self.B):
+            for i, pg in enumerate(self.row_pages(layer, b)):
+                src = off + pg * page_stride
+                out[b, i * P * row_bytes:(i + 1) * P * row_bytes] = self.arena[src: src + P * row_bytes].cpu()
+        return out
+
     def read_head(self, layer: int, kv_head: int):
         """Copy one KV head's slots to the host: (K [B][n_slots][d], V, pos [B][n_slots] or None).
         The bytes come from the arena tensor by offset (a plain device copy).
-        FP8 caches give the codes as uint8."""
+        FP8 caches give the codes as uint8.  A paged retrieval head gives its
+        positions 0 .. ceil(T_cap / page_rows) * page_rows - 1 read through each
+        row's page table (positions on no page read as zeros)."""
         hv = self.head_view(layer, kv_head)
         base = self.arena.data_ptr()
         es = 2 if self.torch_dtype == torch.bfloat16 else 4
         if self.kv_format == DUO_KV_FP8:
             es = 1
+        if self._paged_head(hv):
+            kv = [self._gather_pages(layer, hv[key] - base, hv["head_stride_bytes"], hv["row_bytes"])
+                  .view(torch.uint8 if es == 1 else self.torch_dtype).reshape(self.B, -1, self.d)
+                  for key in ("k_base", "v_base")]
+            return kv[0], kv[1], None
         rows = hv["n_slots"]
         out = []
         for key in ("k_base", "v_base"):

@@ -48,6 +48,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct LayerPlan {
   int n_ret = 0, n_str = 0;
   size_t off_kr = 0, off_vr = 0, off_ks = 0, off_vs = 0, off_pos = 0;
+  size_t off_tab = 0;  // paged caches: int32 page table [B][max_pages]
   // FP8 caches: per-row scales of K and V (retrieval, then streaming heads)
   size_t off_skr = 0, off_svr = 0, off_sks = 0, off_svs = 0;
   duo::HeadMap map{};
@@ -79,8 +80,13 @@ int validate(const duo_config* c) {
     return fail(DUO_EUNSUPPORTED, "FP8 K/V rows are built for bf16 and d_head 128");
   if (c->T_cap < 1) return fail(DUO_EINVAL, "T_cap must be >= 1");
   if (c->T_cap > INT32_MAX) return fail(DUO_EINVAL, "T_cap must fit int32 (positions are int32)");
-  if ((uint64_t)c->T_cap * (uint64_t)c->d_head * (c->dtype == DUO_BF16 ? 2u : 4u) > 0xffffffffull)
+  if (c->page_rows != 0) {
+    if (c->page_rows < 256 || c->page_rows > (1 << 20) || (c->page_rows & (c->page_rows - 1)) != 0)
+      return fail(DUO_EINVAL, "page_rows %d must be 0 or a power of two in [256, 2^20]", c->page_rows);
+    if (c->n_pages < 1) return fail(DUO_EINVAL, "a paged cache needs n_pages >= 1 (got %d)", c->n_pages);
+  } else if ((uint64_t)c->T_cap * (uint64_t)c->d_head * (c->dtype == DUO_BF16 ? 2u : 4u) > 0xffffffffull) {
     return fail(DUO_EUNSUPPORTED, "one head's rows (T_cap * d_head * element size) must fit 4 GiB");
+  }
   if (c->sink < 0 || c->recent < 1) return fail(DUO_EINVAL, "need sink >= 0 and recent >= 1");
   if (!c->retrieval_mask) return fail(DUO_EINVAL, "retrieval_mask is NULL");
   for (int i = 0; i < c->L * c->n_kv; ++i)
@@ -119,16 +125,22 @@ void make_plan(const duo_config* c, Plan* p) {
         lp.map.orig_str[lp.n_str++] = (int8_t)h;
       }
     }
-    const size_t ret_bytes = (size_t)c->B * lp.n_ret * c->T_cap * row;
+    // retrieval rows per head: T_cap per batch row, or the page pool's rows
+    const size_t ret_rows = c->page_rows ? (size_t)c->n_pages * c->page_rows : (size_t)c->B * c->T_cap;
+    const size_t ret_bytes = ret_rows * lp.n_ret * row;
     const size_t str_bytes = (size_t)c->B * lp.n_str * cap_str * row;
     lp.off_kr = off; off = align_up(off + ret_bytes);
     lp.off_vr = off; off = align_up(off + ret_bytes);
     lp.off_ks = off; off = align_up(off + str_bytes);
     lp.off_vs = off; off = align_up(off + str_bytes);
     lp.off_pos = off; off = align_up(off + (size_t)c->B * lp.n_str * cap_str * sizeof(int32_t));
+    if (c->page_rows) {
+      lp.off_tab = off;
+      off = align_up(off + (size_t)c->B * ceil_div(c->T_cap, c->page_rows) * sizeof(int32_t));
+    }
     p->payload += 2 * (ret_bytes + str_bytes);
     if (fp8) {
-      const size_t ret_sc = (size_t)c->B * lp.n_ret * c->T_cap * sizeof(float);
+      const size_t ret_sc = ret_rows * lp.n_ret * sizeof(float);
       const size_t str_sc = (size_t)c->B * lp.n_str * cap_str * sizeof(float);
       lp.off_skr = off; off = align_up(off + ret_sc);
       lp.off_svr = off; off = align_up(off + ret_sc);
@@ -163,6 +175,14 @@ struct duo_cache {
   size_t arena_bytes = 0;
   std::vector<int64_t> row_len;  // tokens held by each (layer, batch row), advanced at enqueue time
   int num_cu = 256;  // compute units of the device current at init (decode work items per call)
+  // Paged caches, per layer: the pages each batch row holds (in position
+  // order), how many rows hold each page, and the free pages (a stack).
+  struct Pages {
+    std::vector<std::vector<int32_t>> rows;
+    std::vector<int32_t> refs;
+    std::vector<int32_t> free_list;
+  };
+  std::vector<Pages> pages;
 
   duo::LayerPtrs ptrs(int l) const {
     const LayerPlan& lp = plan.layers[l];
@@ -177,8 +197,21 @@ struct duo_cache {
     p.vsc_ret = fp8 ? reinterpret_cast<float*>(arena + lp.off_svr) : nullptr;
     p.ksc_str = fp8 ? reinterpret_cast<float*>(arena + lp.off_sks) : nullptr;
     p.vsc_str = fp8 ? reinterpret_cast<float*>(arena + lp.off_svs) : nullptr;
+    p.table = paged(l) ? reinterpret_cast<int32_t*>(arena + lp.off_tab) : nullptr;
+    p.max_pages = paged(l) ? (int32_t)max_pages() : 0;
+    p.page_shift = paged(l) ? page_shift() : 0;
     return p;
   }
+  // a layer stores paged retrieval rows (a layer with no retrieval head needs no pages)
+  bool paged(int l) const { return cfg.page_rows != 0 && plan.layers[l].n_ret > 0; }
+  int64_t max_pages() const { return ceil_div(cfg.T_cap, cfg.page_rows); }
+  int page_shift() const {
+    int sh = 0;
+    while ((1 << sh) < cfg.page_rows) ++sh;
+    return sh;
+  }
+  // pages a row of n tokens holds
+  int64_t pages_for(int64_t n) const { return ceil_div(n, cfg.page_rows); }
   int64_t cap_str() const { return (int64_t)cfg.sink + cfg.recent; }
   int64_t len(int l, int b) const { return row_len[(size_t)l * cfg.B + b]; }
   int64_t& len(int l, int b) { return row_len[(size_t)l * cfg.B + b]; }
@@ -198,7 +231,9 @@ struct duo_cache {
   duo::LayerPtrs row_ptrs(int l, int b) const {
     const LayerPlan& lp = plan.layers[l];
     duo::LayerPtrs p = ptrs(l);
-    const size_t ret_rows = (size_t)b * lp.n_ret * cfg.T_cap, str_rows = (size_t)b * lp.n_str * cap_str();
+    // a paged layer's pool is shared by the rows: only the table moves
+    const size_t ret_rows = p.table ? 0 : (size_t)b * lp.n_ret * cfg.T_cap;
+    const size_t str_rows = (size_t)b * lp.n_str * cap_str();
     const size_t rb = (size_t)row_bytes();
     p.k_ret += ret_rows * rb;
     p.v_ret += ret_rows * rb;
@@ -211,6 +246,7 @@ struct duo_cache {
       p.ksc_str += str_rows;
       p.vsc_str += str_rows;
     }
+    if (p.table) p.table += (size_t)b * p.max_pages;
     return p;
   }
   int row_bytes() const { return cfg.d_head * kv_elem_bytes(&cfg); }     // stored K/V row
@@ -223,6 +259,46 @@ namespace {
 int check_layer(const duo_cache* c, int layer) {
   if (!c) return fail(DUO_EINVAL, "cache handle is NULL");
   if (layer < 0 || layer >= c->cfg.L) return fail(DUO_EINVAL, "layer %d out of range [0, %d)", layer, c->cfg.L);
+  return DUO_OK;
+}
+
+// Paged layers: give every growing row (row < 0: every batch row) the pages
+// it needs to hold n_new more tokens, and enqueue the page-table writes ahead
+// of the kernels that use them.  DUO_ECAPACITY (nothing taken) if the pool
+// has too few free pages.  A row never holds fewer pages than its count
+// needs; it may hold more after a failed launch, which later growth reuses.
+int reserve_pages(duo_cache* c, int layer, int row, int64_t n_new, hipStream_t s) {
+  if (!c->paged(layer)) return DUO_OK;
+  duo_cache::Pages& pg = c->pages[layer];
+  const int b0 = row < 0 ? 0 : row, b1 = row < 0 ? c->cfg.B : row + 1;
+  int64_t need = 0;
+  for (int b = b0; b < b1; ++b)
+    need += std::max<int64_t>(0, c->pages_for(c->len(layer, b) + n_new) - (int64_t)pg.rows[b].size());
+  if (need > (int64_t)pg.free_list.size())
+    return fail(DUO_ECAPACITY, "layer %d needs %lld more pages; %zu of %d are free", layer, (long long)need,
+                pg.free_list.size(), c->cfg.n_pages);
+  duo::TableUpdateArgs u{};
+  u.table = c->ptrs(layer).table;
+  auto flush = [&]() -> hipError_t {
+    const hipError_t e = duo::launch_table_update(u, s);
+    u.n = 0;
+    return e;
+  };
+  for (int b = b0; b < b1; ++b) {
+    const int64_t want = c->pages_for(c->len(layer, b) + n_new);
+    while ((int64_t)pg.rows[b].size() < want) {
+      const int32_t page = pg.free_list.back();
+      pg.free_list.pop_back();
+      pg.refs[page] = 1;
+      u.index[u.n] = (int32_t)((int64_t)b * c->max_pages() + (int64_t)pg.rows[b].size());
+      u.page[u.n] = page;
+      ++u.n;
+      pg.rows[b].push_back(page);
+      if (u.n == duo::kMaxTableUpdates)
+        if (hipError_t e = flush()) return hip_fail(e, "page table update launch");
+    }
+  }
+  if (hipError_t e = flush()) return hip_fail(e, "page table update launch");
   return DUO_OK;
 }
 
@@ -292,6 +368,16 @@ int duo_cache_init(const duo_config* cfg, void* arena, size_t arena_bytes, void*
   c->arena = static_cast<char*>(arena);
   c->arena_bytes = arena_bytes;
   c->row_len.assign((size_t)cfg->L * cfg->B, 0);
+  if (cfg->page_rows) {
+    c->pages.resize(cfg->L);
+    for (int l = 0; l < cfg->L; ++l) {
+      duo_cache::Pages& pg = c->pages[l];
+      pg.rows.assign(cfg->B, {});
+      pg.refs.assign(cfg->n_pages, 0);
+      pg.free_list.resize(cfg->n_pages);
+      for (int i = 0; i < cfg->n_pages; ++i) pg.free_list[i] = cfg->n_pages - 1 - i;  // page 0 is taken first
+    }
+  }
   {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
@@ -321,6 +407,7 @@ int duo_append(duo_cache* c, int layer, const void* k, const void* v, int64_t n_
   if (pmax + n_new > c->cfg.T_cap)
     return fail(DUO_ECAPACITY, "layer %d has a row of %lld tokens; %lld more exceed T_cap %lld", layer,
                 (long long)pmax, (long long)n_new, (long long)c->cfg.T_cap);
+  if (int r = reserve_pages(c, layer, -1, n_new, static_cast<hipStream_t>(stream))) return r;
   hipError_t e = enqueue_append(c, layer, k, v, n_new, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "append launch");
   for (int b = 0; b < c->cfg.B; ++b) c->len(layer, b) += n_new;
@@ -337,6 +424,7 @@ int duo_append_row(duo_cache* c, int layer, int row, const void* k, const void* 
   if (p0 + n_new > c->cfg.T_cap)
     return fail(DUO_ECAPACITY, "row %d of layer %d holds %lld tokens; %lld more exceed T_cap %lld", row, layer,
                 (long long)p0, (long long)n_new, (long long)c->cfg.T_cap);
+  if (int r = reserve_pages(c, layer, row, n_new, static_cast<hipStream_t>(stream))) return r;
   hipError_t e = enqueue_append(c, layer, k, v, n_new, static_cast<hipStream_t>(stream), row);
   if (e != hipSuccess) return hip_fail(e, "append launch");
   c->len(layer, row) = p0 + n_new;
@@ -401,11 +489,15 @@ hipError_t enqueue_decode(duo_cache* c, int layer, const void* q, void* out, flo
   const int64_t heads = (int64_t)cf.B * (lp.n_ret + lp.n_str);
   const int64_t slots = std::max<int64_t>(std::min(c->num_cu, duo::kMaxDecodeBlocks), heads);
   const int64_t R0 = duo::decode_round_rows(cf.dtype, cf.d_head, g, c->fp8());
+  const bool paged = a.lp.table != nullptr;
   auto items = [&](int64_t rows, int64_t t) { return std::max<int64_t>(1, ceil_div(rows, t)); };
+  // A paged head's items start at multiples of R0 rows (the kernel rounds
+  // its item length up to R0), so that each round of rows lies in one page.
+  auto items_ret = [&](int64_t rows, int64_t t) { return items(rows, paged ? ceil_div(t, R0) * R0 : t); };
   auto count = [&](int64_t t) {
     int64_t n = 0;
     for (int b = 0; b < cf.B; ++b)
-      n += lp.n_ret * items(a.rows[b].rows_ret, t) + lp.n_str * items(a.rows[b].rows_str, t);
+      n += lp.n_ret * items_ret(a.rows[b].rows_ret, t) + lp.n_str * items(a.rows[b].rows_str, t);
     return n;
   };
   int64_t longest = 1;
@@ -421,8 +513,10 @@ hipError_t enqueue_decode(duo_cache* c, int layer, const void* q, void* out, flo
   a.multi = 0;
   for (int b = 0; b < cf.B; ++b) {  // retrieval items of every row, then streaming
     duo::DecodeRow& R = a.rows[b];
-    const int64_t nr = items(R.rows_ret, t);
-    R.nb_ret = (int32_t)(R.rows_ret > 0 ? ceil_div(R.rows_ret, ceil_div(R.rows_ret, nr)) : 1);  // no empty item
+    const int64_t nr = items_ret(R.rows_ret, t);
+    // no empty item: contiguous heads are cut evenly; a paged head's items of
+    // ceil(rows / nr) rows rounded up to R0 all hold rows
+    R.nb_ret = (int32_t)(paged || R.rows_ret == 0 ? nr : ceil_div(R.rows_ret, ceil_div(R.rows_ret, nr)));
     R.first_ret = next;
     next += lp.n_ret * R.nb_ret;
     if (lp.n_ret > 0 && R.nb_ret > 1) a.multi = 1;
@@ -468,6 +562,7 @@ int duo_decode_append(duo_cache* c, int layer, const void* k, const void* v, con
   // one launch: each row attends over what it holds and its new token, which
   // the kernel also stores (a row that holds nothing yet attends to the new
   // token alone)
+  if (int r = reserve_pages(c, layer, -1, 1, static_cast<hipStream_t>(stream))) return r;
   hipError_t e = enqueue_decode(c, layer, q, out, scale, ws, k, v, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   for (int b = 0; b < c->cfg.B; ++b) c->len(layer, b) += 1;
@@ -529,6 +624,8 @@ int prefill_impl(duo_cache* c, int layer, int row, const void* q, const void* k,
   duo::prefill_plan(cf.dtype, cf.d_head, g, &rows, &hpi);
   a.q_tiles = (int)ceil_div(C, rows);
   a.items_ret = a.B * lp.n_ret * (g / hpi) * a.q_tiles;
+  // pages for the chunk's rows (the attention reads only the held rows)
+  if (int r = reserve_pages(c, layer, row, C, s)) return r;
   hipError_t e = hipSuccess;
   if (c->fp8()) {
     // the held rows, dequantized to bf16 in the workspace (after the decode
@@ -553,12 +650,14 @@ int prefill_impl(duo_cache* c, int layer, int row, const void* q, const void* k,
     d.cap_str = c->cap_str();
     d.rows_str = a.held_str;
     d.d = cf.d_head;
+    d.n_ret = lp.n_ret;
     e = duo::launch_dequant(d, s);
     if (e != hipSuccess) return hip_fail(e, "dequant launch");
     a.lp.k_ret = d.dst.k_ret;
     a.lp.v_ret = d.dst.v_ret;
     a.lp.k_str = d.dst.k_str;
     a.lp.v_str = d.dst.v_str;
+    a.lp.table = nullptr;  // the copies are contiguous rows
     a.cap_ret = cap_r;
   }
   e = duo::launch_prefill(a, cf.dtype, cf.d_head, g, s);
@@ -605,6 +704,128 @@ int duo_cache_row_len(const duo_cache* c, int layer, int row, int64_t* out) {
   return ok();
 }
 
+int duo_cache_reset_row(duo_cache* c, int layer, int row) {
+  if (int e = check_layer(c, layer)) return e;
+  if (row < 0 || row >= c->cfg.B) return fail(DUO_EINVAL, "row %d out of range [0, %d)", row, c->cfg.B);
+  if (c->paged(layer)) {
+    duo_cache::Pages& pg = c->pages[layer];
+    for (int32_t page : pg.rows[row])
+      if (--pg.refs[page] == 0) pg.free_list.push_back(page);
+    pg.rows[row].clear();
+  }
+  c->len(layer, row) = 0;
+  return ok();
+}
+
+int duo_cache_fork_row(duo_cache* c, int layer, int src_row, int dst_row, void* stream) {
+  if (int e = check_layer(c, layer)) return e;
+  const duo_config& cf = c->cfg;
+  if (src_row < 0 || src_row >= cf.B || dst_row < 0 || dst_row >= cf.B)
+    return fail(DUO_EINVAL, "rows %d, %d out of range [0, %d)", src_row, dst_row, cf.B);
+  if (src_row == dst_row) return fail(DUO_EINVAL, "src_row and dst_row are the same row");
+  if (c->len(layer, dst_row) != 0)
+    return fail(DUO_EINVAL, "row %d of layer %d holds %lld tokens; reset it before a fork", dst_row, layer,
+                (long long)c->len(layer, dst_row));
+  const int64_t n = c->len(layer, src_row);
+  if (n == 0) return ok();
+  const LayerPlan& lp = c->plan.layers[layer];
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const duo::LayerPtrs src = c->row_ptrs(layer, src_row), dst = c->row_ptrs(layer, dst_row);
+  const int64_t rb = c->row_bytes();
+  duo::CopyArgs cp{};
+  auto seg = [&](const void* from, void* to, int64_t bytes, int64_t count = 1, int64_t stride = 0) {
+    if (bytes <= 0 || count <= 0) return;
+    cp.seg[cp.n++] = duo::CopySegment{static_cast<const char*>(from), static_cast<char*>(to), bytes, count, stride,
+                                      stride};
+  };
+  const bool f8 = c->fp8();
+  if (c->paged(layer)) {
+    duo_cache::Pages& pg = c->pages[layer];
+    for (int32_t page : pg.rows[dst_row])  // spares left by a failed launch
+      if (--pg.refs[page] == 0) pg.free_list.push_back(page);
+    pg.rows[dst_row].clear();
+    const int64_t full = n / cf.page_rows;
+    const bool partial = n % cf.page_rows != 0;
+    if (partial && pg.free_list.empty())
+      return fail(DUO_ECAPACITY, "layer %d has no free page for the copy of row %d's last page", layer, src_row);
+    duo::TableUpdateArgs u{};
+    u.table = c->ptrs(layer).table;
+    std::vector<int32_t> pages(pg.rows[src_row].begin(), pg.rows[src_row].begin() + full);
+    for (int32_t page : pages) ++pg.refs[page];
+    if (partial) {
+      const int32_t from = pg.rows[src_row][full];
+      const int32_t page = pg.free_list.back();
+      pg.free_list.pop_back();
+      pg.refs[page] = 1;
+      pages.push_back(page);
+      // the whole page: every retrieval head's rows, K and V (and scales)
+      const int64_t rows = (int64_t)lp.n_ret * cf.page_rows;
+      const duo::LayerPtrs L = c->ptrs(layer);
+      seg(L.k_ret + from * rows * rb, L.k_ret + page * rows * rb, rows * rb);
+      seg(L.v_ret + from * rows * rb, L.v_ret + page * rows * rb, rows * rb);
+      if (f8) {
+        seg(L.ksc_ret + from * rows, L.ksc_ret + page * rows, rows * 4);
+        seg(L.vsc_ret + from * rows, L.vsc_ret + page * rows, rows * 4);
+      }
+    }
+    // the table entries go in launches of at most kMaxTableUpdates
+    for (size_t i = 0; i < pages.size(); i += duo::kMaxTableUpdates) {
+      u.n = (int)std::min<size_t>(duo::kMaxTableUpdates, pages.size() - i);
+      for (int j = 0; j < u.n; ++j) {
+        u.index[j] = (int32_t)((int64_t)dst_row * c->max_pages() + (int64_t)(i + j));
+        u.page[j] = pages[i + j];
+      }
+      if (hipError_t e = duo::launch_table_update(u, s)) return hip_fail(e, "page table update launch");
+    }
+    pg.rows[dst_row] = pages;
+  } else if (lp.n_ret > 0) {
+    // held rows [0, n) of every retrieval head (heads T_cap rows apart)
+    seg(src.k_ret, dst.k_ret, n * rb, lp.n_ret, cf.T_cap * rb);
+    seg(src.v_ret, dst.v_ret, n * rb, lp.n_ret, cf.T_cap * rb);
+    if (f8) {
+      seg(src.ksc_ret, dst.ksc_ret, n * 4, lp.n_ret, cf.T_cap * 4);
+      seg(src.vsc_ret, dst.vsc_ret, n * 4, lp.n_ret, cf.T_cap * 4);
+    }
+  }
+  // the streaming heads' slots, positions and scales of the row
+  const int64_t slots = (int64_t)lp.n_str * c->cap_str();
+  seg(src.k_str, dst.k_str, slots * rb);
+  seg(src.v_str, dst.v_str, slots * rb);
+  seg(src.pos, dst.pos, slots * 4);
+  if (f8) {
+    seg(src.ksc_str, dst.ksc_str, slots * 4);
+    seg(src.vsc_str, dst.vsc_str, slots * 4);
+  }
+  if (hipError_t e = duo::launch_copy(cp, s)) return hip_fail(e, "row copy launch");
+  c->len(layer, dst_row) = n;
+  return ok();
+}
+
+int duo_cache_free_pages(const duo_cache* c, int layer, int64_t* out) {
+  if (int e = check_layer(c, layer)) return e;
+  if (!out) return fail(DUO_EINVAL, "out is NULL");
+  if (c->cfg.page_rows == 0) *out = 0;
+  else if (!c->paged(layer)) *out = c->cfg.n_pages;  // no retrieval head: no page is ever taken
+  else *out = (int64_t)c->pages[layer].free_list.size();
+  return ok();
+}
+
+int duo_cache_row_pages(const duo_cache* c, int layer, int row, int32_t* pages, int64_t cap, int64_t* n) {
+  if (int e = check_layer(c, layer)) return e;
+  if (row < 0 || row >= c->cfg.B) return fail(DUO_EINVAL, "row %d out of range [0, %d)", row, c->cfg.B);
+  if (!n) return fail(DUO_EINVAL, "n is NULL");
+  if (cap > 0 && !pages) return fail(DUO_EINVAL, "pages is NULL");
+  if (!c->paged(layer)) {
+    *n = 0;
+    return ok();
+  }
+  const std::vector<int32_t>& rp = c->pages[layer].rows[row];
+  const int64_t held = c->pages_for(c->len(layer, row));  // pages in use (a failed launch may have left spares)
+  *n = held;
+  for (int64_t i = 0; i < std::min(held, cap); ++i) pages[i] = rp[i];
+  return ok();
+}
+
 int duo_cache_head_view(const duo_cache* c, int layer, int kv_head, int* is_retrieval, void** k_base, void** v_base,
                         int32_t** pos, int64_t* n_slots, int64_t* row_bytes, int64_t* head_stride_bytes,
                         int64_t* pos_stride) {
@@ -615,7 +836,8 @@ int duo_cache_head_view(const duo_cache* c, int layer, int kv_head, int* is_retr
   const bool ret = lp.map.kind[kv_head] != 0;
   const int ci = lp.map.cidx[kv_head];
   const int64_t rb = c->row_bytes();
-  const int64_t slots = ret ? c->cfg.T_cap : c->cap_str();
+  // a paged head: its rows in page 0, pages n_ret * page_rows rows apart
+  const int64_t slots = ret ? (c->paged(layer) ? c->cfg.page_rows : c->cfg.T_cap) : c->cap_str();
   const int n_kind = ret ? lp.n_ret : lp.n_str;
   if (is_retrieval) *is_retrieval = ret ? 1 : 0;
   if (n_slots) *n_slots = slots;
@@ -677,7 +899,7 @@ int duo_cache_head_scales(const duo_cache* c, int layer, int kv_head, float** k_
   const duo::LayerPtrs p = c->ptrs(layer);
   const bool ret = lp.map.kind[kv_head] != 0;
   const int ci = lp.map.cidx[kv_head];
-  const int64_t slots = ret ? c->cfg.T_cap : c->cap_str();
+  const int64_t slots = ret ? (c->paged(layer) ? c->cfg.page_rows : c->cfg.T_cap) : c->cap_str();
   const int n_kind = ret ? lp.n_ret : lp.n_str;
   const bool f8 = c->fp8();
   if (k_scale) *k_scale = f8 ? (ret ? p.ksc_ret : p.ksc_str) + (size_t)ci * slots : nullptr;

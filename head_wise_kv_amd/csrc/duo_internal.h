@@ -26,7 +26,7 @@ struct HeadMap {
 
 // Device addresses of one layer inside the arena.
 struct LayerPtrs {
-  char* k_ret;     // [B][n_ret][cap_ret][d]
+  char* k_ret;     // [B][n_ret][cap_ret][d]; paged: [n_pages][n_ret][page rows][d]
   char* v_ret;
   char* k_str;     // [B][n_str][cap_str][d]
   char* v_str;
@@ -36,6 +36,34 @@ struct LayerPtrs {
   float* vsc_ret;
   float* ksc_str;  // [B][n_str][cap_str]
   float* vsc_str;
+  // Paged retrieval rows (table null: contiguous).  table[b * max_pages + i]
+  // is the page holding positions [i << page_shift, (i + 1) << page_shift)
+  // of every retrieval head of batch row b.
+  int32_t* table;
+  int32_t max_pages;
+  int32_t page_shift;
+};
+
+// Page table entries written before the kernels that read them (same stream).
+constexpr int kMaxTableUpdates = 240;
+struct TableUpdateArgs {
+  int32_t* table;
+  int n;
+  int32_t index[kMaxTableUpdates];
+  int32_t page[kMaxTableUpdates];
+};
+
+// Device copies of byte ranges: segment i copies `count` blocks of `bytes`
+// (a multiple of 4) from src + j * src_stride to dst + j * dst_stride.
+constexpr int kMaxCopySegments = 12;
+struct CopySegment {
+  const char* src;
+  char* dst;
+  int64_t bytes, count, src_stride, dst_stride;
+};
+struct CopyArgs {
+  int n;
+  CopySegment seg[kMaxCopySegments];
 };
 
 struct AppendArgs {
@@ -118,15 +146,18 @@ struct GatedArgs {
 
 // Launchers (duo_kernels.hip, duo_prefill.hip, duo_gated.hip).  dtype: 0 = fp32, 1 = bf16.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_table_update(const TableUpdateArgs& a, hipStream_t s);
+hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, int dtype, int d, bool fp8, hipStream_t s);
 // FP8 caches: the held rows of one layer, dequantized to bf16 for prefill.
 struct DequantArgs {
   LayerPtrs src;               // codes and scales in the arena
   LayerPtrs dst;               // bf16 rows (k/v pointers only), [B][n_ret][cap_ret_dst][d] and [B][n_str][cap_str][d]
-  int64_t heads_ret, heads_str;
+  int64_t heads_ret, heads_str;  // B * n_ret, B * n_str
   int64_t cap_ret_src, cap_ret_dst, rows_ret;
   int64_t cap_str, rows_str;
   int d;
+  int n_ret;
 };
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
 // Split phase over `blocks` work items (retrieval heads' items first), then

@@ -7,13 +7,16 @@
 // head) -- all T rows of a retrieval head, the min(T, S+W) sink and ring slots
 // of a streaming head -- form one flattened row space cut into equal work
 // items, one per compute unit, so long retrieval heads and short streaming
-// heads are balanced by bytes.  Within an item each wavefront streams tiles of
-// rows with coalesced 16-byte loads, two tiles in flight, scores them with
-// packed bf16 dot products against the GQA query group held in registers,
-// keeps online softmax statistics per lane, and accumulates P.V with bf16 dot
-// products.  Partial (max, sum, acc) results of items that share a head are
-// merged in-kernel by the last-arriving item of each group, then of the head.
+// heads are balanced by bytes.  Within an item, K and V rows reach LDS by
+// direct buffer->LDS loads into a ring of four 32 KB units (three in flight);
+// the wavefronts score them with packed bf16 dot products against the GQA
+// query group held in registers, keep online softmax statistics per lane, and
+// accumulate P.V with bf16 dot products.  Partial (max, sum, acc) results of
+// items that share a head are merged by a second kernel (combine_kernel).
+// Retrieval rows may live in pages (a per-row page table); a paged head's
+// items then start at round boundaries so that every round lies in one page.
 #include "duo_internal.h"
+#include "duo_rows.h"
 
 #include <hip/hip_runtime.h>
 
@@ -77,6 +80,29 @@ __global__ void fill_zero_kernel(uint4* p, size_t n16, unsigned char* tail, size
   if (i < ntail) tail[i] = 0;
 }
 
+// ------------------------------------------------------------------ page tables and row copies
+
+__global__ void table_update_kernel(TableUpdateArgs a) {
+  const int i = threadIdx.x;
+  if (i < a.n) a.table[a.index[i]] = a.page[i];
+}
+
+// Grid-stride over the 4-byte words of every segment (a few rows per call:
+// a forked row's partial page and streaming slots).
+__global__ void copy_kernel(CopyArgs a) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (int i = 0; i < a.n; ++i) {
+    const CopySegment& g = a.seg[i];
+    const int64_t words = g.bytes / 4, total = words * g.count;
+    for (int64_t t = t0; t < total; t += stride) {
+      const int64_t j = t / words, w = t % words;
+      reinterpret_cast<uint32_t*>(g.dst + j * g.dst_stride)[w] =
+          reinterpret_cast<const uint32_t*>(g.src + j * g.src_stride)[w];
+    }
+  }
+}
+
 // ------------------------------------------------------------------ append
 // One thread per 16-byte chunk of an input row.  Token i of batch row b is at
 // position p = p0[b] + i; it goes to row p of a retrieval head; for a
@@ -103,7 +129,7 @@ __global__ void append_kernel(AppendArgs a) {
     char *kd, *vd;
     if (a.map.kind[kvh]) {
       const int r = a.map.cidx[kvh];
-      const size_t off = (((size_t)b * a.n_ret + r) * a.cap_ret + p) * a.row_bytes + (size_t)c * 16;
+      const size_t off = (size_t)ret_row(a.lp, a.n_ret, a.cap_ret, b, r, p) * a.row_bytes + (size_t)c * 16;
       kd = a.lp.k_ret + off;
       vd = a.lp.v_ret + off;
     } else {
@@ -354,7 +380,7 @@ __global__ void append_fp8_kernel(AppendArgs a) {
   char* dst;
   float* sdst;
   if (a.map.kind[kvh]) {
-    const size_t hrow = ((size_t)b * a.n_ret + a.map.cidx[kvh]) * a.cap_ret + p;
+    const size_t hrow = (size_t)ret_row(a.lp, a.n_ret, a.cap_ret, b, a.map.cidx[kvh], p);
     dst = (tensor ? a.lp.v_ret : a.lp.k_ret) + hrow * a.row_bytes;
     sdst = (tensor ? a.lp.vsc_ret : a.lp.ksc_ret) + hrow;
   } else {
@@ -388,7 +414,8 @@ __global__ void dequant_kernel(DequantArgs a) {
     uint16_t* dst;
     if (rr < n_ret) {
       const int64_t h = rr / a.rows_ret, r = rr % a.rows_ret;
-      const int64_t srow = h * a.cap_ret_src + r, drow = h * a.cap_ret_dst + r;
+      const int64_t srow = ret_row(a.src, a.n_ret, a.cap_ret_src, h / a.n_ret, (int)(h % a.n_ret), r);
+      const int64_t drow = h * a.cap_ret_dst + r;
       codes = reinterpret_cast<const uint8_t*>(tensor ? a.src.v_ret : a.src.k_ret) + srow * a.d;
       sc = (tensor ? a.src.vsc_ret : a.src.ksc_ret) + srow;
       dst = reinterpret_cast<uint16_t*>(tensor ? a.dst.v_ret : a.dst.k_ret) + drow * a.d;
@@ -449,11 +476,24 @@ struct DecodeItem {
   char* vbase;
   float* ksc;       // FP8 rows: per-row scales of the head (else null)
   float* vsc;
+  // Paged retrieval head: the batch row's page table (else null); kbase,
+  // vbase, ksc and vsc then point at the head's rows in page 0.
+  const int32_t* ptab;
+  int shift;
+  int64_t pstride;  // rows from one page of the head to the next
+
+  // Row of position `row` of the head, counted from kbase / ksc (uniform
+  // `row`: the table read adds no vector-memory load to the counts the
+  // ring's waits rely on).
+  __device__ __forceinline__ int64_t at(int64_t row) const { return ptab ? paged_row(ptab, shift, pstride, row) : row; }
 };
 
-template <int ROWB>
+template <int ROWB, int RR>
 __device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a, int64_t blk) {
   DecodeItem w;
+  w.ptab = nullptr;
+  w.shift = 0;
+  w.pstride = 0;
   int64_t rows;
   if (blk < a.items_ret) {
     int b = 0;
@@ -468,10 +508,16 @@ __device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a, int64_t b
     w.b = b;
     w.hh = (int64_t)b * a.n_ret + r;
     w.kvh = a.map.orig_ret[r];
-    const size_t off = ((size_t)b * a.n_ret + r) * a.cap_ret * ROWB;
-    w.kbase = a.lp.k_ret + off;
-    w.vbase = a.lp.v_ret + off;
-    const size_t srow = ((size_t)b * a.n_ret + r) * a.cap_ret;
+    // first row of the head: row 0 of its contiguous rows, or its part of page 0
+    size_t srow = ((size_t)b * a.n_ret + r) * a.cap_ret;
+    if (a.lp.table) {
+      w.ptab = a.lp.table + (size_t)b * a.lp.max_pages;
+      w.shift = a.lp.page_shift;
+      w.pstride = (int64_t)a.n_ret << a.lp.page_shift;
+      srow = (size_t)r << a.lp.page_shift;
+    }
+    w.kbase = a.lp.k_ret + srow * ROWB;
+    w.vbase = a.lp.v_ret + srow * ROWB;
     w.ksc = a.lp.ksc_ret ? a.lp.ksc_ret + srow : nullptr;
     w.vsc = a.lp.vsc_ret ? a.lp.vsc_ret + srow : nullptr;
   } else {
@@ -494,7 +540,8 @@ __device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a, int64_t b
     w.ksc = a.lp.ksc_str ? a.lp.ksc_str + srow : nullptr;
     w.vsc = a.lp.vsc_str ? a.lp.vsc_str + srow : nullptr;
   }
-  const int64_t per = (rows + w.nparts - 1) / w.nparts;
+  int64_t per = (rows + w.nparts - 1) / w.nparts;
+  if (w.ptab) per = (per + RR - 1) / RR * RR;  // paged: every round of rows lies in one page
   w.r0 = w.part * per;
   w.r1 = w.r0 + per < rows ? w.r0 + per : rows;
   if (w.r0 > rows) w.r0 = rows;
@@ -891,7 +938,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   const int hg = wave % C::HSPLIT;     // which HW query heads of the group it scores
   const bool active = slot < SLOTS;
   const int rg = lane >> 3, s = lane & 7;
-  const DecodeItem w = decode_item<C::ROWB>(a, blockIdx.x);
+  const DecodeItem w = decode_item<C::ROWB, C::ROUND_ROWS>(a, blockIdx.x);
   const int64_t nrounds = ((w.r1 - w.r0 + TR - 1) / TR + SLOTS - 1) / SLOTS;
   const size_t q_off = ((size_t)w.b * a.n_q + (size_t)w.kvh * G) * D;  // first query of the group
 
@@ -927,7 +974,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     const int64_t row0 = w.r0 + (uu >> 1) * (int64_t)C::ROUND_ROWS;
     const int64_t left = w.r1 - row0;
     const int rows = (int)(left <= 0 ? 0 : (left > C::ROUND_ROWS ? C::ROUND_ROWS : left));
-    const char* src = ((uu & 1) ? w.vbase : w.kbase) + (size_t)(rows > 0 ? row0 : 0) * C::ROWB;
+    const int64_t roff = rows > 0 ? w.at(row0) : 0;
+    const char* src = ((uu & 1) ? w.vbase : w.kbase) + (size_t)roff * C::ROWB;
     const i32x4_t rs = dec_rsrc(src, rows * C::ROWB);
 #pragma unroll
     for (int j = 0; j < kPiecesPerWave; ++j)
@@ -935,7 +983,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     if constexpr (KV8) {
       if ((uu & 1) == 0) {  // wavefronts 0-3: K scales, 4-7: V scales, 64 rows each
         const int tensor = wave >> 2, part = wave & 3;
-        const float* ssrc = (tensor ? w.vsc : w.ksc) + (rows > 0 ? row0 : 0);
+        const float* ssrc = (tensor ? w.vsc : w.ksc) + roff;
         dec_dma4(dec_rsrc(reinterpret_cast<const char*>(ssrc), rows * 4),
                  reinterpret_cast<char*>(&sbuf[(uu >> 1) & 1][tensor * C::ROUND_ROWS + part * 64]),
                  (uint32_t)((part * 64 + lane) * 4));
@@ -1064,7 +1112,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
         tile_pv<KT, D, G>(st, p, ring1, rg, s);
       }
     }
-    const int64_t row = ret_head ? a.rows[w.row].new_pos : a.rows[w.row].new_slot_str;
+    const int64_t row = ret_head ? w.at(a.rows[w.row].new_pos) : a.rows[w.row].new_slot_str;
     if constexpr (KV8) {
       if (wave == 0 && lane < 32) {
         const int t = lane >> 4, j = lane & 15;
@@ -1296,6 +1344,21 @@ int64_t round_rows_d(int g) {
 }
 
 }  // namespace
+
+hipError_t launch_table_update(const TableUpdateArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  table_update_kernel<<<1, kMaxTableUpdates, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(const CopyArgs& a, hipStream_t s) {
+  int64_t words = 0;
+  for (int i = 0; i < a.n; ++i) words += a.seg[i].bytes / 4 * a.seg[i].count;
+  if (words == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((words + 255) / 256, 2048);
+  copy_kernel<<<(unsigned)blocks, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
   if (bytes == 0) return hipSuccess;

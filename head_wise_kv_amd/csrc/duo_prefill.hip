@@ -37,6 +37,7 @@
 // completeness of the dtype surface; it is not tuned.
 #include "duo_attn_tile.h"
 #include "duo_internal.h"
+#include "duo_rows.h"
 
 #include <hip/hip_runtime.h>
 
@@ -192,7 +193,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
   const char *kc, *vc;
   const int32_t* posc = nullptr;
   if (w.ret) {
-    const size_t off = ((size_t)w.b * a.n_ret + w.cidx) * a.cap_ret * rowb;
+    // the head's row 0 (contiguous), or its rows in page 0 (paged)
+    const size_t off = (a.lp.table ? ((size_t)w.cidx << a.lp.page_shift)
+                                   : ((size_t)w.b * a.n_ret + w.cidx) * a.cap_ret) * rowb;
     kc = a.lp.k_ret + off;
     vc = a.lp.v_ret + off;
   } else {
@@ -258,10 +261,15 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
     const char* ks = (src == SRC_CHUNK) ? kn : kc;
     const char* vs = (src == SRC_CHUNK) ? vn : vc;
     const int nbytes = __builtin_amdgcn_readfirstlane((int)min64(limit - base, kBN) * (int)rowb);
+    // a paged head's tile (64 rows from a multiple of 64) lies in one page
+    const int64_t roff = (src == SRC_CACHE_LINEAR && a.lp.table)
+                             ? paged_row(a.lp.table + (size_t)w.b * a.lp.max_pages, a.lp.page_shift,
+                                         (int64_t)a.n_ret << a.lp.page_shift, base)
+                             : base;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)uniform_ptr(ks + (size_t)base * rowb), (short)0, nbytes, kBufferRsrcWord3);
+        (void*)uniform_ptr(ks + (size_t)roff * rowb), (short)0, nbytes, kBufferRsrcWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)uniform_ptr(vs + (size_t)base * rowb), (short)0, nbytes, kBufferRsrcWord3);
+        (void*)uniform_ptr(vs + (size_t)roff * rowb), (short)0, nbytes, kBufferRsrcWord3);
     dma_pieces(rk, k_lds[kh][buf], sub, koff);
     dma_pieces(rv, v_lds[kh][buf], sub, voff);
     if (sub == 0) {  // one wavefront, all lanes: lane = key of the tile
@@ -385,21 +393,24 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a, int g) 
   const int ci = a.map.cidx[kvh];
   const int64_t t = a.P + qrow;
   const float* q = static_cast<const float*>(a.q) + (((size_t)b * a.n_q + h) * a.C + qrow) * D;
+  // cache rows: row r of the head is row crow(r) of the layer's K / V array
   const float *kc, *vc;
   const int32_t* posc = nullptr;
   int64_t cache_rows;
+  const size_t hrow = ((size_t)b * a.n_str + ci) * a.cap_str;
   if (ret) {
-    const size_t off = ((size_t)b * a.n_ret + ci) * a.cap_ret * D;
-    kc = reinterpret_cast<const float*>(a.lp.k_ret) + off;
-    vc = reinterpret_cast<const float*>(a.lp.v_ret) + off;
+    kc = reinterpret_cast<const float*>(a.lp.k_ret);
+    vc = reinterpret_cast<const float*>(a.lp.v_ret);
     cache_rows = a.P;
   } else {
-    const size_t hrow = ((size_t)b * a.n_str + ci) * a.cap_str;
-    kc = reinterpret_cast<const float*>(a.lp.k_str) + hrow * D;
-    vc = reinterpret_cast<const float*>(a.lp.v_str) + hrow * D;
+    kc = reinterpret_cast<const float*>(a.lp.k_str);
+    vc = reinterpret_cast<const float*>(a.lp.v_str);
     posc = a.lp.pos + hrow;
     cache_rows = a.held_str;
   }
+  auto crow = [&](int64_t r) -> size_t {
+    return ret ? (size_t)ret_row(a.lp, a.n_ret, a.cap_ret, b, ci, r) : hrow + (size_t)r;
+  };
   const size_t coff = ((size_t)b * a.n_kv + kvh) * a.C * D;
   const float* kn = static_cast<const float*>(a.k) + coff;
   const float* vn = static_cast<const float*>(a.v) + coff;
@@ -417,7 +428,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a, int g) 
       const int64_t row = from_cache ? kk : kk - cache_rows;
       const int64_t kp = from_cache ? (ret ? row : (int64_t)posc[row]) : a.P + row;
       if (visible(kp, t, ret, a.S, a.W)) {
-        const float* kr = (from_cache ? kc : kn) + (size_t)row * D;
+        const float* kr = from_cache ? kc + crow(row) * D : kn + (size_t)row * D;
         float s = 0.f;
         for (int d = 0; d < D; ++d) s = fmaf(q[d], kr[d], s);
         sv = s * a.scale_log2;
@@ -440,7 +451,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a, int g) 
       const int64_t kj = k0 + j;
       const bool from_cache = kj < cache_rows;
       const int64_t row = from_cache ? kj : kj - cache_rows;
-      const float* vr = (from_cache ? vc : vn) + (size_t)row * D;
+      const float* vr = from_cache ? vc + crow(row) * D : vn + (size_t)row * D;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pj, vr[lane + 64 * e], acc[e]);
     }

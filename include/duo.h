@@ -45,7 +45,7 @@ extern "C" {
 #define DUO_OK 0
 #define DUO_EINVAL (-1)        /* bad argument, shape, pointer or layer index     */
 #define DUO_EUNSUPPORTED (-2)  /* d_head, dtype or group size not built           */
-#define DUO_ECAPACITY (-3)     /* seq_len + n_new would exceed T_cap              */
+#define DUO_ECAPACITY (-3)     /* seq_len + n_new would exceed T_cap, or no free page */
 #define DUO_EEMPTY (-4)        /* decode on a layer that holds no token           */
 #define DUO_EWORKSPACE (-5)    /* workspace missing or smaller than required      */
 #define DUO_EHIP (-6)          /* a HIP call or kernel launch failed              */
@@ -67,9 +67,21 @@ typedef enum { DUO_KV_NATIVE = 0, DUO_KV_FP8 = 1 } duo_kv_format;
 
 /* Cache configuration.  d_head in {64, 128}; g = n_q / n_kv in {1, 2, 4, 8};
  * n_kv <= 128; 1 <= B <= 64; S >= 0; W >= 1; T_cap >= 1.  Each batch row keeps
- * its own token count (a ragged batch allocates T_cap rows per retrieval head
- * and row, and attends over what each row holds).  retrieval_mask is a host array
- * uint8 [L][n_kv] (1 = retrieval head, 0 = streaming head); it is copied. */
+ * its own token count and attends over what it holds (a ragged batch).
+ * retrieval_mask is a host array uint8 [L][n_kv] (1 = retrieval head,
+ * 0 = streaming head); it is copied.
+ *
+ * Retrieval rows are stored one of two ways.  page_rows = 0: contiguous, T_cap
+ * rows per retrieval head and batch row.  page_rows > 0 (a power of two, at
+ * least 256): paged ("Attention Variants and Memory Efficiency", "What the
+ * Inference Runtime Can Change": a request's cache in fixed-size blocks that
+ * need not be contiguous, shareable between requests; "A Closer Look at
+ * Attention Memory": a ragged batch then holds only what each request needs).
+ * Each layer has a pool of n_pages pages; a page holds page_rows consecutive
+ * positions of every retrieval head of one batch row, and a row takes a page
+ * from the pool when it grows past its last page.  T_cap still bounds each
+ * row (it sizes the page tables).  Streaming heads keep their S + W slots per
+ * batch row either way. */
 typedef struct {
   int32_t L, B, n_q, n_kv, d_head;
   int64_t T_cap;
@@ -77,6 +89,8 @@ typedef struct {
   int32_t dtype; /* duo_dtype: Q, K, V and outputs; accumulation is fp32 */
   const uint8_t* retrieval_mask;
   int32_t kv_format; /* duo_kv_format of the stored K/V rows (0 = native) */
+  int32_t page_rows; /* 0: contiguous retrieval rows; else rows per page (power of two >= 256) */
+  int32_t n_pages;   /* paged: pages per layer (>= 1); ignored when page_rows = 0 */
 } duo_config;
 
 typedef struct duo_cache duo_cache; /* opaque host handle */
@@ -85,7 +99,10 @@ typedef struct duo_cache duo_cache; /* opaque host handle */
  * duo_cache_init.  It holds, per layer, K and V as [B][n_ret][T_cap][d] for
  * the retrieval heads and [B][n_str][S+W][d] for the streaming heads (the two
  * buffer kinds of the guide's section 2), an int32 position per streaming
- * slot, and for DUO_KV_FP8 an fp32 scale per stored K and V row.
+ * slot, and for DUO_KV_FP8 an fp32 scale per stored K and V row.  A paged
+ * cache holds instead K and V pools [n_pages][n_ret][page_rows][d] (scales
+ * [n_pages][n_ret][page_rows]) and an int32 page table
+ * [B][ceil(T_cap / page_rows)] per layer.
  * *workspace_bytes: the device scratch that duo_decode, duo_decode_append and
  * duo_prefill_chunk need (partial softmax results; for DUO_KV_FP8 also room
  * for one layer's held rows in bf16, which prefill reads).  Either output
@@ -94,7 +111,8 @@ int duo_cache_bytes(const duo_config* cfg, size_t* arena_bytes, size_t* workspac
 
 /* K+V payload bytes of the arena (the KV-cache size the guide's section 2
  * formula counts: retrieval heads T_cap rows, streaming heads S+W rows; for
- * DUO_KV_FP8 the codes plus the row scales). */
+ * DUO_KV_FP8 the codes plus the row scales; for a paged cache the pools,
+ * n_pages * page_rows rows per retrieval head, in place of B * T_cap). */
 int duo_cache_payload_bytes(const duo_config* cfg, size_t* payload_bytes);
 
 /* Bind a cache to a caller-owned device arena of at least duo_cache_bytes()
@@ -113,7 +131,8 @@ int duo_cache_init(const duo_config* cfg, void* arena, size_t arena_bytes, void*
  * Efficiency", "Sliding-Window and Mixed Attention"); tokens of the batch that
  * would be evicted before the call ends are not written.  Each written
  * streaming slot records p in its position array.  DUO_ECAPACITY if
- * some row would exceed T_cap. */
+ * some row would exceed T_cap, or a paged layer has fewer free pages than the
+ * rows' growth needs. */
 int duo_append(duo_cache* c, int layer, const void* k, const void* v, int64_t n_new, void* stream);
 
 /* duo_append for batch row `row` alone: k, v device [1][n_kv][n_new][d],
@@ -147,7 +166,8 @@ int duo_decode(duo_cache* c, int layer, const void* q, void* out, float scale, v
  * Inference Runtime Can Change").  The token is written to its row or ring
  * slot while the held rows are read; a streaming slot whose token it evicts
  * is left out of the attention.  k, v: device [B][n_kv][1][d]; q, out: device
- * [B][n_q][d]; ws as for duo_decode.  DUO_ECAPACITY if some row is full;
+ * [B][n_q][d]; ws as for duo_decode.  DUO_ECAPACITY if some row is full
+ * (or, paged, no page is free for a row that starts one);
  * other errors as duo_append and duo_decode.  Every row advances by one
  * token. */
 int duo_decode_append(duo_cache* c, int layer, const void* k, const void* v, const void* q, void* out,
@@ -166,7 +186,7 @@ int duo_decode_append(duo_cache* c, int layer, const void* k, const void* v, con
  * rows are read as stored (code value * scale) and the chunk's own rows as
  * given, and ws must hold duo_cache_bytes' workspace_bytes (DUO_EWORKSPACE
  * otherwise); a native cache needs no workspace here.  DUO_ECAPACITY if
- * P + C > T_cap. */
+ * P + C > T_cap or (paged) the chunk needs more pages than are free. */
 int duo_prefill_chunk(duo_cache* c, int layer, const void* q, const void* k, const void* v,
                       int64_t C, void* out, float scale, void* ws, size_t ws_bytes, void* stream);
 
@@ -183,6 +203,10 @@ int duo_cache_seq_len(const duo_cache* c, int layer, int64_t* out);
 int duo_cache_row_len(const duo_cache* c, int layer, int row, int64_t* out);
 
 /* Where one KV head's rows live, for bit-exact inspection of the layout.
+ * For a retrieval head of a paged cache, *k_base / *v_base are the head's
+ * rows in page 0, *n_slots = page_rows and *head_stride_bytes the distance
+ * between consecutive pages; position p of batch row b is then row
+ * p mod page_rows of page duo_cache_row_pages(b)[p / page_rows].
  * *k_base / *v_base: device address of the head's first row (batch row b at
  * + b * head_stride_bytes); *pos: device int32 [n_slots] slot positions of a
  * streaming head (NULL for a retrieval head, whose row index is the
@@ -221,10 +245,38 @@ int duo_gated_attention(const duo_gated_shape* shape, const void* q, const void*
 
 /* Row scales of one KV head of a DUO_KV_FP8 cache: *k_scale / *v_scale
  * receive the device float [n_slots] scales of batch row 0 (batch row b at
- * + b * *scale_stride floats), in the slot order of duo_cache_head_view.  For
+ * + b * *scale_stride floats), in the slot order of duo_cache_head_view (a
+ * paged retrieval head: the scales of its rows in page 0, page i at
+ * + i * *scale_stride floats).  For
  * a native cache both are set to NULL.  For bit-exact inspection. */
 int duo_cache_head_scales(const duo_cache* c, int layer, int kv_head, float** k_scale, float** v_scale,
                           int64_t* scale_stride);
+
+/* Forget batch row `row` of `layer`: its token count becomes 0 and the pages
+ * it alone held return to the layer's pool (a finished request of a ragged
+ * batch leaves room for the next).  Host only, no device work; later calls
+ * on the row see an empty row. */
+int duo_cache_reset_row(duo_cache* c, int layer, int row);
+
+/* Prefix sharing: batch row dst (which must hold no token) becomes a copy of
+ * batch row src of `layer`, with src's token count ("Attention Variants and
+ * Memory Efficiency", "What the Inference Runtime Can Change": matching
+ * prefixes need not be stored twice).  In a paged cache the full pages of src
+ * are shared, not copied: both rows' tables name them, and since a row only
+ * ever writes positions past its own count, a full page is never written
+ * again.  src's last page, if partly filled, is copied to a page of dst's own;
+ * so are the streaming heads' slots, positions and scales.  A contiguous cache
+ * copies every held row.  Enqueued on `stream`.  DUO_ECAPACITY if no page is
+ * free for the copy. */
+int duo_cache_fork_row(duo_cache* c, int layer, int src_row, int dst_row, void* stream);
+
+/* Pages of `layer` not held by any row (0 for a contiguous cache). */
+int duo_cache_free_pages(const duo_cache* c, int layer, int64_t* out);
+
+/* The page table of batch row `row` of a paged layer, as the host keeps it:
+ * *n receives the number of pages the row holds (ceil(count / page_rows));
+ * the first min(*n, cap) page numbers are written to the host array pages. */
+int duo_cache_row_pages(const duo_cache* c, int layer, int row, int32_t* pages, int64_t cap, int64_t* n);
 
 /* Release the host handle (device memory is the caller's). NULL is ignored. */
 void duo_cache_free(duo_cache* c);

@@ -51,6 +51,28 @@ def test_fp8_payload_closed_form(name):
     assert payload < native * 0.52 and ws > ws_native
 
 
+@pytest.mark.parametrize("kvf", [None, "fp8"])
+def test_paged_payload_closed_form(kvf):
+    """A paged cache's retrieval payload is its pools (n_pages * page_rows rows
+    per retrieval head and layer) instead of B * T_cap rows; the streaming
+    heads' part is unchanged."""
+    w = WL.WORKLOADS["llama3_8b_decode_b8_32k"]
+    mask = WL.mask_table(w)
+    P, n_pages = 256, 300
+    _, ws, paged = H.cache_bytes(w.L, w.B, w.n_q, w.n_kv, w.d, w.T, w.S, w.W, w.dtype, mask, kvf, P, n_pages)
+    e = 1 if kvf == "fp8" else w.elem_bytes
+    n_ret = int(mask.sum())
+    n_str = mask.size - n_ret
+    want = 2 * (n_ret * n_pages * P + w.B * n_str * (w.S + w.W)) * w.d * e
+    if kvf == "fp8":
+        want += 2 * (n_ret * n_pages * P + w.B * n_str * (w.S + w.W)) * 4
+    assert paged == want
+    # the same pool as the contiguous rows (n_pages * P = B * T_cap) holds the same payload
+    _, _, same = H.cache_bytes(w.L, w.B, w.n_q, w.n_kv, w.d, w.T, w.S, w.W, w.dtype, mask, kvf, P, w.B * w.T // P)
+    _, _, contiguous = H.cache_bytes(w.L, w.B, w.n_q, w.n_kv, w.d, w.T, w.S, w.W, w.dtype, mask, kvf)
+    assert same == contiguous
+
+
 def test_payload_reproduces_printed_examples():
     # 70B GQA, all heads retrieval: the printed 41,943,040,000 bytes.
     _, _, p = H.cache_bytes(80, 1, 64, 8, 128, 128000, 64, 1024, "bf16", [[1] * 8] * 80)
@@ -80,6 +102,10 @@ BAD = [
     (dict(B=65), H.DUO_EUNSUPPORTED),                          # at most 64 batch rows
     (dict(kv_format=1, dtype_code=0), H.DUO_EUNSUPPORTED),   # FP8 rows need bf16
     (dict(kv_format=1, d_head=64), H.DUO_EUNSUPPORTED),      # FP8 rows are built for d_head 128
+    (dict(page_rows=128, n_pages=4), H.DUO_EINVAL),          # pages of at least 256 rows
+    (dict(page_rows=384, n_pages=4), H.DUO_EINVAL),          # a power of two
+    (dict(page_rows=256, n_pages=0), H.DUO_EINVAL),          # an empty pool
+    (dict(page_rows=-256, n_pages=4), H.DUO_EINVAL),
 ]
 
 
@@ -92,7 +118,8 @@ def test_validation_codes(over, code):
     buf = (ctypes.c_uint8 * max(n_mask, 1))(*([mv] * max(n_mask, 1)))
     cfg = H.duo_config(base["L"], base["B"], base["n_q"], base["n_kv"], base["d_head"], base["T_cap"],
                        base["sink"], base["recent"], over.get("dtype_code", H.DUO_BF16),
-                       ctypes.cast(buf, ctypes.POINTER(ctypes.c_uint8)), over.get("kv_format", 0))
+                       ctypes.cast(buf, ctypes.POINTER(ctypes.c_uint8)), over.get("kv_format", 0),
+                       over.get("page_rows", 0), over.get("n_pages", 0))
     a = ctypes.c_size_t()
     rc = H.lib.duo_cache_bytes(ctypes.byref(cfg), ctypes.byref(a), None)
     assert rc == code, H.lib.duo_last_error()
@@ -115,6 +142,10 @@ def test_calls_on_null_handle_fail_cleanly():
     assert H.lib.duo_append_row(None, 0, 0, None, None, 1, None) == H.DUO_EINVAL
     assert H.lib.duo_prefill_chunk_row(None, 0, 0, None, None, None, 1, None, 1.0, None, 0, None) == H.DUO_EINVAL
     assert H.lib.duo_cache_row_len(None, 0, 0, ctypes.byref(x)) == H.DUO_EINVAL
+    assert H.lib.duo_cache_reset_row(None, 0, 0) == H.DUO_EINVAL
+    assert H.lib.duo_cache_fork_row(None, 0, 0, 1, None) == H.DUO_EINVAL
+    assert H.lib.duo_cache_free_pages(None, 0, ctypes.byref(x)) == H.DUO_EINVAL
+    assert H.lib.duo_cache_row_pages(None, 0, 0, None, 0, ctypes.byref(x)) == H.DUO_EINVAL
     H.lib.duo_cache_free(None)
 
 
