@@ -17,6 +17,7 @@ from oracle import attention as A
 from oracle import cache as Cc
 from oracle import gating as G
 from oracle import paging as PG
+from oracle import rope as RP
 from oracle import quant as QZ
 from oracle import sizes as Z
 
@@ -441,6 +442,87 @@ def check_paging_capacity():
     assert m.pages_in_use() == 3 and m.shared_pages(0, 1) == 3
 
 
+# ------------------------------------------------------------------ rotary positions
+
+def check_rope_unit_vectors():
+    # d = 8, theta = 10^4: pair frequencies 10^(-i) = 1, 0.1, 0.01, 0.001.  At
+    # position p, unit vector e_i (i < 4) turns into cos(p f_i) e_i + sin(p f_i) e_(i+4)
+    # and e_(i+4) into -sin(p f_i) e_i + cos(p f_i) e_(i+4).
+    f = [1.0, 0.1, 0.01, 0.001]
+    for p in (1, 7, 1000):
+        R = RP.rotate(np.eye(8), [p] * 8, 1e4)     # row i: unit vector e_i at position p
+        for i in range(4):
+            want = np.zeros(8)
+            want[i], want[i + 4] = math.cos(p * f[i]), math.sin(p * f[i])
+            assert np.allclose(R[i], want, atol=1e-12), (p, i, R[i])
+            want = np.zeros(8)
+            want[i], want[i + 4] = -math.sin(p * f[i]), math.cos(p * f[i])
+            assert np.allclose(R[i + 4], want, atol=1e-12), (p, i + 4, R[i + 4])
+    X = np.random.default_rng(3).standard_normal((5, 16))
+    assert np.array_equal(RP.rotate(X, [0] * 5, 5e5), X)  # position 0: no rotation
+
+
+def check_rope_complex_form():
+    # pair (x_i, x_(i+d/2)) as the complex number x_i + j x_(i+d/2), multiplied
+    # by exp(j p f_i) with f_i = theta^(-2i/d)
+    rng = np.random.default_rng(4)
+    d, theta = 64, 5e5
+    X = rng.standard_normal((3, 9, d))
+    pos = np.array([0, 1, 2, 63, 64, 1000, 4095, 70000, 131071])
+    z = X[..., : d // 2] + 1j * X[..., d // 2:]
+    f = np.array([theta ** (-(2.0 * i) / d) for i in range(d // 2)])
+    w = z * np.exp(1j * pos[:, None] * f[None, :])
+    want = np.concatenate([w.real, w.imag], axis=-1)
+    assert np.allclose(RP.rotate(X, pos, theta), want, atol=1e-9, rtol=0)
+
+
+def check_rope_relative_positions():
+    # scores of rotated queries and keys depend only on the position difference
+    rng = np.random.default_rng(5)
+    d = 128
+    q, k = rng.standard_normal(d), rng.standard_normal(d)
+    def score(pq, pk):
+        return float(RP.rotate(q[None], [pq], 1e4)[0] @ RP.rotate(k[None], [pk], 1e4)[0])
+    for pq, pk in ((10, 3), (5000, 4990), (7, 7), (2, 9)):
+        for shift in (1, 100, 65536):
+            assert abs(score(pq, pk) - score(pq + shift, pk + shift)) < 1e-9
+        assert abs(score(pq, pk) - float(q @ RP.rotate(k[None], [pk - pq], 1e4)[0])) < 1e-9
+
+
+def check_bf16_rounding_against_library():
+    mags = 10.0 ** np.random.default_rng(8).uniform(-3, 3, 20000)
+    ties = [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 1.0 + 2 ** -9, 255.5, 0.0]  # halfway cases
+    x = np.concatenate([np.random.default_rng(6).standard_normal(20000) * mags, ties])
+    x32 = x.astype(np.float32)                      # float32-representable values: no double rounding
+    want = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(RP.round_bf16(x32.astype(np.float64)), want)
+
+
+def check_rope_cache_route_uses_logical_positions():
+    # a streaming head's ring holds keys rotated at their own positions: the
+    # decode over the cache's slots equals the visibility rule over positions
+    rng = np.random.default_rng(7)
+    n_q, n_kv, T, d, S, W = 4, 2, 40, 16, 3, 8
+    q = rng.standard_normal((n_q, d))
+    K, V = rng.standard_normal((n_kv, T, d)), rng.standard_normal((n_kv, T, d))
+    for mask in ([1, 0], [0, 0]):
+        a = RP.decode_step_rope(q, K, V, mask, S, W, 0.25, 1e4, "f32", route="cache")
+        b = RP.decode_step_rope(q, K, V, mask, S, W, 0.25, 1e4, "f32", route="definition")
+        assert np.allclose(a, b, atol=1e-12)
+    # chunked prefill with rotary positions: every chunking gives the same rows
+    # up to the rounding of the held keys (a single chunk holds none)
+    Q = rng.standard_normal((n_q, T, d))
+    one = RP.prefill_chunked_rope(Q, K, V, [1, 0], S, W, 0.25, 1e4, "f32", [T])
+    many = RP.prefill_chunked_rope(Q, K, V, [1, 0], S, W, 0.25, 1e4, "f32", [7, 1, 20, 12])
+    assert np.allclose(one, many, atol=1e-5)
+    # the last row of a prefill is a decode step at that position
+    dec = RP.decode_step_rope(q, K, V, [1, 0], S, W, 0.25, 1e4, "f32")
+    Q2 = Q.copy()
+    Q2[:, T - 1] = q
+    pre = RP.prefill_chunked_rope(Q2, K, V, [1, 0], S, W, 0.25, 1e4, "f32", [T - 1, 1])
+    assert np.allclose(pre[:, T - 1], dec, atol=1e-12)
+
+
 ALL_CHECKS = [
     check_printed_kv_sizes, check_effective_context, check_mixed_payload_closed_forms,
     check_ring_example, check_streaming_composition, check_simulation_counts, check_keep_set_is_visible_set,
@@ -449,6 +531,8 @@ ALL_CHECKS = [
     check_gated_hand_case, check_gated_library_endpoints, check_gated_bruteforce_agrees,
     check_gated_gqa_expansion, check_e4m3_against_library, check_fp8_row_quantizer,
     check_fp8_attention_routes, check_paging_closed_forms, check_paging_capacity,
+    check_rope_unit_vectors, check_rope_complex_form, check_rope_relative_positions,
+    check_bf16_rounding_against_library, check_rope_cache_route_uses_logical_positions,
 ]
 
 

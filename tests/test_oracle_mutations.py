@@ -7,6 +7,7 @@ from oracle import attention as A
 from oracle import cache as Cc
 from oracle import gating as G
 from oracle import paging as PG
+from oracle import rope as RP
 from oracle import quant as QZ
 from oracle import sizes as Z
 from tests import oracle_checks as OC
@@ -111,6 +112,36 @@ def _pages_floor(self, n):
     return n // self.P                             # a partial page not counted
 
 
+_orig_rotate = RP.rotate
+
+
+def _rope_adjacent_pairs(X, positions, theta):
+    X = np.asarray(X, dtype=np.float64)
+    d = X.shape[-1]
+    perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])  # pairs (2i, 2i+1)
+    inv = np.argsort(perm)
+    return _orig_rotate(X[..., perm], positions, theta)[..., inv]
+
+
+def _rope_sign(X, positions, theta):
+    return _orig_rotate(X, -np.asarray(positions, dtype=np.float64), theta)  # turned the other way
+
+
+def _rope_freq(d, theta):
+    return np.power(float(theta), -1.0 * np.arange(d // 2, dtype=np.float64) / d)  # exponent -i/d
+
+
+def _bf16_half_up(x):
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.ldexp(np.floor(m * 256.0 + 0.5), e - 8)  # ties away from even
+
+
+def _decode_query_unrotated(q, K, V, mask, S, W, scale, theta, dtype, route="cache"):
+    K = np.asarray(K, dtype=np.float64)
+    return A.decode_step(np.asarray(q, dtype=np.float64), RP.stored_keys(K, theta, dtype),
+                         np.asarray(V, dtype=np.float64), mask, S, W, scale, route=route)
+
+
 MUTATIONS = {
     "window_too_wide": (A, "visible_matrix", _window_too_wide),
     "sinks_off_by_one": (A, "visible_matrix", _sinks_off_by_one),
@@ -128,6 +159,11 @@ MUTATIONS = {
     "fork_copies_all": (PG.PagedRows, "fork", _fork_copies_all),
     "fork_shares_partial": (PG.PagedRows, "fork", _fork_shares_partial),
     "pages_floor": (PG.PagedRows, "pages_needed", _pages_floor),
+    "rope_adjacent_pairs": (RP, "rotate", _rope_adjacent_pairs),
+    "rope_sign": (RP, "rotate", _rope_sign),
+    "rope_freq": (RP, "inv_freq", _rope_freq),
+    "bf16_half_up": (RP, "round_bf16", _bf16_half_up),
+    "rope_query_unrotated": (RP, "decode_step_rope", _decode_query_unrotated),
 }
 
 
