@@ -29,7 +29,7 @@ EXPORTS = ("duo_cache_bytes", "duo_cache_payload_bytes", "duo_cache_init", "duo_
            "duo_decode_append", "duo_prefill_chunk", "duo_cache_seq_len", "duo_cache_head_view", "duo_cache_free",
            "duo_last_error", "duo_gated_attention", "duo_cache_head_scales", "duo_append_row", "duo_prefill_chunk_row",
            "duo_cache_row_len", "duo_cache_reset_row", "duo_cache_fork_row", "duo_cache_free_pages",
-           "duo_cache_row_pages")
+           "duo_cache_row_pages", "duo_prefill_workspace_bytes")
 
 
 class DuoError(RuntimeError):
@@ -43,7 +43,7 @@ class duo_config(ctypes.Structure):
                 ("d_head", ctypes.c_int32), ("T_cap", ctypes.c_int64), ("sink", ctypes.c_int32),
                 ("recent", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("retrieval_mask", ctypes.POINTER(ctypes.c_uint8)), ("kv_format", ctypes.c_int32),
-                ("page_rows", ctypes.c_int32), ("n_pages", ctypes.c_int32)]
+                ("page_rows", ctypes.c_int32), ("n_pages", ctypes.c_int32), ("rope_theta", ctypes.c_float)]
 
 
 class duo_gated_shape(ctypes.Structure):
@@ -73,6 +73,11 @@ def _load():
     lib.duo_append_row.argtypes = [vp, i32, i32, vp, vp, i64, vp]
     lib.duo_prefill_chunk_row.argtypes = [vp, i32, i32, vp, vp, vp, i64, vp, ctypes.c_float, vp, sz, vp]
     lib.duo_cache_row_len.argtypes = [vp, i32, i32, ctypes.POINTER(i64)]
+    lib.duo_cache_reset_row.argtypes = [vp, i32, i32]
+    lib.duo_cache_fork_row.argtypes = [vp, i32, i32, i32, vp]
+    lib.duo_cache_free_pages.argtypes = [vp, i32, ctypes.POINTER(i64)]
+    lib.duo_cache_row_pages.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_int32), i64, ctypes.POINTER(i64)]
+    lib.duo_prefill_workspace_bytes.argtypes = [vp, i32, i64, ctypes.POINTER(sz)]
     lib.duo_cache_free.argtypes = [vp]
     lib.duo_cache_free.restype = None
     lib.duo_last_error.argtypes = []
@@ -111,9 +116,10 @@ def _kv_code(kv_format) -> int:
 
 
 def make_config(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask, kv_format=None, page_rows=0,
-                n_pages=0):
+                n_pages=0, rope_theta=0.0):
     """(duo_config, keep-alive mask buffer).  page_rows > 0 stores retrieval
-    rows in pages of that many rows, n_pages per layer."""
+    rows in pages of that many rows, n_pages per layer; rope_theta > 0 turns
+    on rotary positions with that base."""
     import numpy as np
     m = torch.from_numpy(np.asarray(mask, dtype=np.uint8).reshape(-1).copy())
     if m.numel() != L * n_kv:
@@ -121,14 +127,15 @@ def make_config(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask, kv_fo
     buf = (ctypes.c_uint8 * m.numel())(*m.tolist())
     cfg = duo_config(L, B, n_q, n_kv, d_head, int(T_cap), sink, recent, _dtype_code(dtype),
                      ctypes.cast(buf, ctypes.POINTER(ctypes.c_uint8)), _kv_code(kv_format), int(page_rows),
-                     int(n_pages))
+                     int(n_pages), float(rope_theta))
     return cfg, buf
 
 
-def cache_bytes(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask, kv_format=None, page_rows=0, n_pages=0):
+def cache_bytes(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask, kv_format=None, page_rows=0, n_pages=0,
+                rope_theta=0.0):
     """(arena bytes, workspace bytes, K+V payload bytes) -- host-only size query."""
     cfg, _buf = make_config(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask, kv_format, page_rows,
-                            n_pages)
+                            n_pages, rope_theta)
     a, w, p = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
     _check(lib.duo_cache_bytes(ctypes.byref(cfg), ctypes.byref(a), ctypes.byref(w)))
     _check(lib.duo_cache_payload_bytes(ctypes.byref(cfg), ctypes.byref(p)))
@@ -148,20 +155,22 @@ class DuoCache:
     cache's device.  kv_format "fp8" stores the K/V rows as FP8 codes with one
     scale per row (bf16 caches with d_head 128).  page_rows > 0 stores the
     retrieval rows in pages (n_pages per layer) that rows take as they grow
-    and can share (fork_row).
+    and can share (fork_row).  rope_theta > 0 applies rotary positions (keys
+    stored rotated, queries rotated by decode and prefill).
     """
 
     def __init__(self, L: int, B: int, n_q: int, n_kv: int, d_head: int, T_cap: int, sink: int, recent: int,
                  dtype, mask: Sequence, device="cuda", stream: Optional[torch.cuda.Stream] = None, kv_format=None,
-                 page_rows: int = 0, n_pages: int = 0):
+                 page_rows: int = 0, n_pages: int = 0, rope_theta: float = 0.0):
         self.L, self.B, self.n_q, self.n_kv, self.d = L, B, n_q, n_kv, d_head
         self.T_cap, self.S, self.W = int(T_cap), sink, recent
         self.page_rows, self.n_pages = int(page_rows), int(n_pages)
+        self.rope_theta = float(rope_theta)
         self.torch_dtype = torch.bfloat16 if _dtype_code(dtype) == DUO_BF16 else torch.float32
         self.kv_format = _kv_code(kv_format)
         self.device = torch.device(device)
         self._cfg, self._mask_buf = make_config(L, B, n_q, n_kv, d_head, T_cap, sink, recent, dtype, mask, kv_format,
-                                                page_rows, n_pages)
+                                                page_rows, n_pages, rope_theta)
         import numpy as np
         self.mask = torch.from_numpy(np.asarray(mask, dtype=np.uint8).reshape(L, n_kv).copy())
         a, w = ctypes.c_size_t(), ctypes.c_size_t()
@@ -246,6 +255,7 @@ class DuoCache:
             out = torch.empty_like(q)
         self._chk(out, (self.B, self.n_q, C, self.d), "out")
         sc = float(self.d ** -0.5 if scale is None else scale)
+        self._ensure_prefill_workspace(self.B, C)
         _check(lib.duo_prefill_chunk(self._h, layer, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
                                      ctypes.c_void_p(v.data_ptr()), C, ctypes.c_void_p(out.data_ptr()), sc,
                                      ctypes.c_void_p(self.workspace.data_ptr()), self.workspace.numel(),
@@ -262,6 +272,16 @@ class DuoCache:
         x = ctypes.c_int64()
         _check(lib.duo_cache_row_len(self._h, layer, row, ctypes.byref(x)))
         return x.value
+
+    def _ensure_prefill_workspace(self, rows: int, C: int) -> None:
+        """Grow the workspace tensor to what a prefill of `rows` rows and C
+        tokens needs (rotary positions need room for the rotated chunk)."""
+        if C < 1:
+            return
+        need = ctypes.c_size_t()
+        _check(lib.duo_prefill_workspace_bytes(self._h, rows, C, ctypes.byref(need)))
+        if need.value > self.workspace.numel():
+            self.workspace = torch.empty(need.value, dtype=torch.uint8, device=self.device)
 
     def reset_row(self, layer: int, row: int) -> None:
         """Empty batch row `row` of `layer` (its pages return to the pool)."""
@@ -303,6 +323,7 @@ class DuoCache:
             out = torch.empty_like(q)
         self._chk(out, (1, self.n_q, C, self.d), "out")
         sc = float(self.d ** -0.5 if scale is None else scale)
+        self._ensure_prefill_workspace(1, C)
         _check(lib.duo_prefill_chunk_row(self._h, layer, row, ctypes.c_void_p(q.data_ptr()),
                                          ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()), C,
                                          ctypes.c_void_p(out.data_ptr()), sc, ctypes.c_void_p(self.workspace.data_ptr()),

@@ -88,6 +88,8 @@ int validate(const duo_config* c) {
     return fail(DUO_EUNSUPPORTED, "one head's rows (T_cap * d_head * element size) must fit 4 GiB");
   }
   if (c->sink < 0 || c->recent < 1) return fail(DUO_EINVAL, "need sink >= 0 and recent >= 1");
+  if (!std::isfinite(c->rope_theta) || c->rope_theta < 0.f || (c->rope_theta > 0.f && c->rope_theta <= 1.f))
+    return fail(DUO_EINVAL, "rope_theta must be 0 (off) or a finite base > 1 (got %g)", (double)c->rope_theta);
   if (!c->retrieval_mask) return fail(DUO_EINVAL, "retrieval_mask is NULL");
   for (int i = 0; i < c->L * c->n_kv; ++i)
     if (c->retrieval_mask[i] > 1) return fail(DUO_EINVAL, "retrieval_mask[%d] = %d, must be 0 or 1", i, c->retrieval_mask[i]);
@@ -249,6 +251,18 @@ struct duo_cache {
     if (p.table) p.table += (size_t)b * p.max_pages;
     return p;
   }
+  duo::Rope rope() const {
+    duo::Rope r{};
+    r.on = cfg.rope_theta > 0.f ? 1 : 0;
+    r.log2_theta = r.on ? std::log2((double)cfg.rope_theta) : 0.0;
+    return r;
+  }
+  // prefill with rotary positions: the chunk's rotated queries and keys in the
+  // workspace, after the decode records and the FP8 prefill copies
+  size_t rope_ws_bytes(int64_t B, int64_t C) const {
+    const size_t row = (size_t)cfg.d_head * elem_bytes(&cfg);
+    return align_up((size_t)B * cfg.n_q * C * row) + align_up((size_t)B * cfg.n_kv * C * row);
+  }
   int row_bytes() const { return cfg.d_head * kv_elem_bytes(&cfg); }     // stored K/V row
   int in_row_bytes() const { return cfg.d_head * elem_bytes(&cfg); }     // input / query row
   bool fp8() const { return cfg.kv_format == DUO_KV_FP8; }
@@ -306,7 +320,7 @@ int reserve_pages(duo_cache* c, int layer, int row, int64_t n_new, hipStream_t s
 // count, or (row >= 0) to that one row only, the inputs then being
 // [1][n_kv][n_new][d] (no validation).
 hipError_t enqueue_append(duo_cache* c, int layer, const void* k, const void* v, int64_t n_new, hipStream_t s,
-                          int row = -1) {
+                          int row = -1, bool rotate = true) {
   const LayerPlan& lp = c->plan.layers[layer];
   duo::AppendArgs a{};
   a.k = static_cast<const char*>(k);
@@ -325,6 +339,9 @@ hipError_t enqueue_append(duo_cache* c, int layer, const void* k, const void* v,
   a.n_new = n_new;
   a.S = c->cfg.sink;
   a.W = c->cfg.recent;
+  a.dtype = c->cfg.dtype;
+  a.d = c->cfg.d_head;
+  if (rotate) a.rope = c->rope();  // else the keys come rotated already
   return duo::launch_append(a, c->cfg.dtype, c->cfg.d_head, c->fp8(), s);
 }
 
@@ -477,6 +494,7 @@ hipError_t enqueue_decode(duo_cache* c, int layer, const void* q, void* out, flo
     a.new_k = static_cast<const char*>(new_k);
     a.new_v = static_cast<const char*>(new_v);
   }
+  a.rope = c->rope();
   // Work items: contiguous row ranges of one head, at most one workgroup per
   // compute unit (or one per head if there are more heads), none shorter
   // than one round of the kernel where the head allows.  All heads are cut to
@@ -573,22 +591,30 @@ int duo_decode_append(duo_cache* c, int layer, const void* k, const void* v, con
 
 namespace {
 
+// Workspace a chunked prefill of B rows and C tokens needs: FP8 caches hold
+// the dequantized rows after the decode records; rotary positions add the
+// rotated chunk after those.  0 if none.
+size_t prefill_ws_bytes(const duo_cache* c, int64_t B, int64_t C) {
+  if (c->rope().on) return c->plan.workspace + c->rope_ws_bytes(B, C);
+  return c->fp8() ? c->plan.workspace : 0;
+}
+
 // Chunked prefill of every batch row (row < 0; the rows must hold equal
 // counts) or of batch row `row` alone (inputs [1][...]).
 int prefill_impl(duo_cache* c, int layer, int row, const void* q, const void* k, const void* v, int64_t C, void* out,
                  float scale, void* ws, size_t ws_bytes, void* stream) {
   if (int e = check_layer(c, layer)) return e;
   if (row >= c->cfg.B) return fail(DUO_EINVAL, "row %d out of range [0, %d)", row, c->cfg.B);
-  if (c->fp8()) {
-    if (!ws || ws_bytes < c->plan.workspace)
-      return fail(DUO_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", c->plan.workspace, ws_bytes);
-    if ((reinterpret_cast<uintptr_t>(ws) % kAlign) != 0) return fail(DUO_EINVAL, "workspace must be 256-byte aligned");
-  }
   if (!q || !k || !v || !out) return fail(DUO_EINVAL, "q, k, v or out is NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(DUO_EINVAL, "q, k, v and out must be 16-byte aligned");
   if (!std::isfinite(scale) || !(scale > 0.f)) return fail(DUO_EINVAL, "scale must be finite and > 0");
   if (C < 1) return fail(DUO_EINVAL, "chunk length must be >= 1 (got %lld)", (long long)C);
+  const size_t need = prefill_ws_bytes(c, row < 0 ? c->cfg.B : 1, C);
+  if (need) {
+    if (!ws || ws_bytes < need) return fail(DUO_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    if ((reinterpret_cast<uintptr_t>(ws) % kAlign) != 0) return fail(DUO_EINVAL, "workspace must be 256-byte aligned");
+  }
   const int64_t P = row < 0 ? c->uniform_len(layer) : c->len(layer, row);
   if (P < 0)
     return fail(DUO_EINVAL, "the rows of layer %d hold different token counts; prefill them one at a time "
@@ -660,10 +686,34 @@ int prefill_impl(duo_cache* c, int layer, int row, const void* q, const void* k,
     a.lp.table = nullptr;  // the copies are contiguous rows
     a.cap_ret = cap_r;
   }
+  const duo::Rope rope = c->rope();
+  if (rope.on) {
+    // the chunk's queries and keys rotated at positions P + i, into the
+    // workspace after the records and the FP8 copies
+    duo::RopeArgs r{};
+    char* base = static_cast<char*>(ws) + c->plan.workspace;
+    r.q = q;
+    r.k = k;
+    r.q_out = base;
+    r.k_out = base + align_up((size_t)a.B * cf.n_q * C * c->in_row_bytes());
+    r.B = a.B;
+    r.n_q = cf.n_q;
+    r.n_kv = cf.n_kv;
+    r.d = cf.d_head;
+    r.dtype = cf.dtype;
+    r.C = C;
+    for (int b = 0; b < a.B; ++b) r.p0[b] = (int32_t)P;
+    r.rope = rope;
+    e = duo::launch_rope(r, s);
+    if (e != hipSuccess) return hip_fail(e, "rotary launch");
+    a.q = r.q_out;
+    a.k = r.k_out;
+  }
   e = duo::launch_prefill(a, cf.dtype, cf.d_head, g, s);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
-  // Commit the chunk after attention has read the cache (same stream).
-  e = enqueue_append(c, layer, k, v, C, s, row);
+  // Commit the chunk after attention has read the cache (same stream); with
+  // rotary positions its keys are the rotated copies.
+  e = enqueue_append(c, layer, a.k, v, C, s, row, /*rotate=*/false);
   if (e != hipSuccess) return hip_fail(e, "prefill commit launch");
   if (row < 0)
     for (int b = 0; b < cf.B; ++b) c->len(layer, b) = P + C;
@@ -685,6 +735,15 @@ int duo_prefill_chunk_row(duo_cache* c, int layer, int row, const void* q, const
                           void* out, float scale, void* ws, size_t ws_bytes, void* stream) {
   if (row < 0) return fail(DUO_EINVAL, "row %d out of range", row);
   return prefill_impl(c, layer, row, q, k, v, C, out, scale, ws, ws_bytes, stream);
+}
+
+int duo_prefill_workspace_bytes(const duo_cache* c, int rows, int64_t C, size_t* bytes) {
+  if (!c) return fail(DUO_EINVAL, "cache handle is NULL");
+  if (rows < 1 || rows > c->cfg.B) return fail(DUO_EINVAL, "rows %d out of range [1, %d]", rows, c->cfg.B);
+  if (C < 1) return fail(DUO_EINVAL, "chunk length must be >= 1 (got %lld)", (long long)C);
+  if (!bytes) return fail(DUO_EINVAL, "bytes is NULL");
+  *bytes = prefill_ws_bytes(c, rows, C);
+  return ok();
 }
 
 int duo_cache_seq_len(const duo_cache* c, int layer, int64_t* out) {

@@ -44,6 +44,14 @@ struct LayerPtrs {
   int32_t page_shift;
 };
 
+// Rotary position embedding (on = 0: keys and queries are used as given).
+// Pair i of a head's dimensions, (i, i + d/2), turns by p * theta^(-2i/d) at
+// position p.
+struct Rope {
+  double log2_theta;
+  int on;
+};
+
 // Page table entries written before the kernels that read them (same stream).
 constexpr int kMaxTableUpdates = 240;
 struct TableUpdateArgs {
@@ -78,6 +86,9 @@ struct AppendArgs {
   int64_t n_new;          // tokens per batch row
   int32_t p0[kMaxRows];   // first position of each batch row (its token count before the call)
   int S, W;
+  int dtype;              // 0 = fp32, 1 = bf16 (of the inputs)
+  int d;
+  Rope rope;              // K rows are rotated at their position before they are stored
 };
 
 // Per batch row of a decode: its held rows, its work items and, for a fused
@@ -108,6 +119,9 @@ struct DecodeArgs {
   // it to the cache.
   const char* new_k;            // [B][n_kv][d]
   const char* new_v;
+  // Queries (and a fused append's new K row) are rotated at the query's
+  // position: rows[b].new_pos for a fused append, rows[b].new_pos - 1 otherwise.
+  Rope rope;
   DecodeRow rows[kMaxRows];     // items ordered: row 0's retrieval heads, row 1's, ..., then streaming likewise
 };
 
@@ -144,10 +158,24 @@ struct GatedArgs {
   int q_tiles;         // ceil(N / rows per work item)
 };
 
+// Prefill with rotary positions: the chunk's queries and keys rotated at
+// positions p0[b] + i into the workspace (same layouts), before the attention.
+struct RopeArgs {
+  const void* q;   // [B][n_q][C][d]
+  const void* k;   // [B][n_kv][C][d]
+  void* q_out;
+  void* k_out;
+  int B, n_q, n_kv, d, dtype;
+  int64_t C;
+  int32_t p0[kMaxRows];
+  Rope rope;
+};
+
 // Launchers (duo_kernels.hip, duo_prefill.hip, duo_gated.hip).  dtype: 0 = fp32, 1 = bf16.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_table_update(const TableUpdateArgs& a, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
+hipError_t launch_rope(const RopeArgs& a, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, int dtype, int d, bool fp8, hipStream_t s);
 // FP8 caches: the held rows of one layer, dequantized to bf16 for prefill.
 struct DequantArgs {

@@ -16,6 +16,7 @@
 // Retrieval rows may live in pages (a per-row page table); a paged head's
 // items then start at round boundaries so that every round lies in one page.
 #include "duo_internal.h"
+#include "duo_rope.h"
 #include "duo_rows.h"
 
 #include <hip/hip_runtime.h>
@@ -112,24 +113,54 @@ __global__ void copy_kernel(CopyArgs a) {
 // tokens of the same call, and skipping them keeps every slot written at most
 // once.
 
+// Rotate the pairs of chunk x (dimensions c * E .. c * E + E - 1, E = 16 /
+// element size) and chunk y (the same dimensions + d/2) at position p.
+__device__ __forceinline__ void rope_chunks(uint4& x, uint4& y, const Rope& r, int d, int64_t p, int c, int dtype) {
+  uint32_t xw[4] = {x.x, x.y, x.z, x.w}, yw[4] = {y.x, y.y, y.z, y.w};
+  if (dtype == 1) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float cs0, sn0, cs1, sn1;
+      rope_cs(r, d, p, c * 8 + 2 * w, cs0, sn0);
+      rope_cs(r, d, p, c * 8 + 2 * w + 1, cs1, sn1);
+      const float x0 = bf_lo(xw[w]), x1 = bf_hi(xw[w]), y0 = bf_lo(yw[w]), y1 = bf_hi(yw[w]);
+      xw[w] = f32_to_bf16_bits(x0 * cs0 - y0 * sn0) | (f32_to_bf16_bits(x1 * cs1 - y1 * sn1) << 16);
+      yw[w] = f32_to_bf16_bits(y0 * cs0 + x0 * sn0) | (f32_to_bf16_bits(y1 * cs1 + x1 * sn1) << 16);
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float cs, sn;
+      rope_cs(r, d, p, c * 4 + w, cs, sn);
+      const float xv = __uint_as_float(xw[w]), yv = __uint_as_float(yw[w]);
+      xw[w] = __float_as_uint(xv * cs - yv * sn);
+      yw[w] = __float_as_uint(yv * cs + xv * sn);
+    }
+  }
+  x = make_uint4(xw[0], xw[1], xw[2], xw[3]);
+  y = make_uint4(yw[0], yw[1], yw[2], yw[3]);
+}
+
 __global__ void append_kernel(AppendArgs a) {
   const int cpr = a.row_bytes / 16;
-  const int64_t total = (int64_t)a.B * a.n_kv * a.n_new * cpr;
+  // work per row: its 16-byte chunks, or with rotary positions its chunk
+  // pairs (c, c + cpr/2), which hold the rotation's dimension pairs
+  const int units = a.rope.on ? cpr / 2 : cpr;
+  const int64_t total = (int64_t)a.B * a.n_kv * a.n_new * units;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total; idx += stride) {
-    const int c = (int)(idx % cpr);
-    int64_t rest = idx / cpr;
+    const int c = (int)(idx % units);
+    const int64_t rest = idx / units;  // input row (b, kvh, i)
     const int64_t i = rest % a.n_new;
-    rest /= a.n_new;
-    const int kvh = (int)(rest % a.n_kv);
-    const int b = (int)(rest / a.n_kv);
+    const int kvh = (int)((rest / a.n_new) % a.n_kv);
+    const int b = (int)(rest / a.n_new / a.n_kv);
     const int64_t p = a.p0[b] + i;
     const int64_t keep_from = max64d((int64_t)a.S, (int64_t)a.p0[b] + a.n_new - a.W);
-    const size_t src = (size_t)idx * 16;
+    const size_t src = (size_t)rest * a.row_bytes;
     char *kd, *vd;
     if (a.map.kind[kvh]) {
       const int r = a.map.cidx[kvh];
-      const size_t off = (size_t)ret_row(a.lp, a.n_ret, a.cap_ret, b, r, p) * a.row_bytes + (size_t)c * 16;
+      const size_t off = (size_t)ret_row(a.lp, a.n_ret, a.cap_ret, b, r, p) * a.row_bytes;
       kd = a.lp.k_ret + off;
       vd = a.lp.v_ret + off;
     } else {
@@ -143,13 +174,56 @@ __global__ void append_kernel(AppendArgs a) {
       }
       const int s = a.map.cidx[kvh];
       const size_t hrow = ((size_t)b * a.n_str + s) * a.cap_str + slot;
-      const size_t off = hrow * a.row_bytes + (size_t)c * 16;
+      const size_t off = hrow * a.row_bytes;
       kd = a.lp.k_str + off;
       vd = a.lp.v_str + off;
       if (c == 0) a.lp.pos[hrow] = (int32_t)p;
     }
-    st16(kd, ld16(a.k + src));
-    st16(vd, ld16(a.v + src));
+    if (!a.rope.on) {
+      st16(kd + c * 16, ld16(a.k + src + c * 16));
+      st16(vd + c * 16, ld16(a.v + src + c * 16));
+    } else {
+      const int c2 = c + cpr / 2;
+      uint4 x = ld16(a.k + src + c * 16), y = ld16(a.k + src + c2 * 16);
+      rope_chunks(x, y, a.rope, a.d, p, c, a.dtype);
+      st16(kd + c * 16, x);
+      st16(kd + c2 * 16, y);
+      st16(vd + c * 16, ld16(a.v + src + c * 16));
+      st16(vd + c2 * 16, ld16(a.v + src + c2 * 16));
+    }
+  }
+}
+
+// Prefill with rotary positions: chunk row i of batch row b at position
+// p0[b] + i, one thread per (row, dimension pair); queries and keys.
+__global__ void rope_kernel(RopeArgs a) {
+  const int half = a.d / 2;
+  const int64_t q_pairs = (int64_t)a.B * a.n_q * a.C * half;
+  const int64_t total = q_pairs + (int64_t)a.B * a.n_kv * a.C * half;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total; t += stride) {
+    const bool isq = t < q_pairs;
+    const int64_t u = isq ? t : t - q_pairs;
+    const int i = (int)(u % half);
+    const int64_t row = u / half;  // (b, head, chunk row)
+    const int64_t ci = row % a.C;
+    const int b = (int)(row / a.C / (isq ? a.n_q : a.n_kv));
+    float cs, sn;
+    rope_cs(a.rope, a.d, a.p0[b] + ci, i, cs, sn);
+    const size_t e0 = (size_t)row * a.d + i, e1 = e0 + half;
+    if (a.dtype == 1) {
+      const uint16_t* in = static_cast<const uint16_t*>(isq ? a.q : a.k);
+      uint16_t* out = static_cast<uint16_t*>(isq ? a.q_out : a.k_out);
+      const float x = __uint_as_float((uint32_t)in[e0] << 16), y = __uint_as_float((uint32_t)in[e1] << 16);
+      out[e0] = (uint16_t)f32_to_bf16_bits(x * cs - y * sn);
+      out[e1] = (uint16_t)f32_to_bf16_bits(y * cs + x * sn);
+    } else {
+      const float* in = static_cast<const float*>(isq ? a.q : a.k);
+      float* out = static_cast<float*>(isq ? a.q_out : a.k_out);
+      const float x = in[e0], y = in[e1];
+      out[e0] = x * cs - y * sn;
+      out[e1] = y * cs + x * sn;
+    }
   }
 }
 
@@ -361,6 +435,54 @@ __device__ __forceinline__ uint2 quant_row16(uint4 x, float& scale) {
 // Append to an FP8 cache: one group of 16 lanes per (batch row, KV head,
 // token, K or V) row, each lane taking 8 consecutive bf16 values.  Slot rules
 // as append_kernel.
+// Rotary positions in decode: rows [0, nq) of the staging area (the group's
+// queries, row_bytes apart) and, if with_k, the new token's K row at k_row,
+// rotated in place at position p; one thread per (row, dimension pair).
+template <int ES>
+__device__ __forceinline__ void rope_stage(char* stage, int nq, char* k_row, bool with_k, int row_bytes, int d,
+                                           int64_t p, const Rope& r) {
+  const int half = d / 2;
+  const int n = (nq + (with_k ? 1 : 0)) * half;
+  for (int t = threadIdx.x; t < n; t += kDecodeThreads) {
+    const int row = t / half, i = t % half;
+    char* base = row < nq ? stage + row * row_bytes : k_row;
+    float cs, sn;
+    rope_cs(r, d, p, i, cs, sn);
+    if constexpr (ES == 2) {
+      uint16_t* e = reinterpret_cast<uint16_t*>(base);
+      const float x = __uint_as_float((uint32_t)e[i] << 16), y = __uint_as_float((uint32_t)e[i + half] << 16);
+      e[i] = (uint16_t)f32_to_bf16_bits(x * cs - y * sn);
+      e[i + half] = (uint16_t)f32_to_bf16_bits(y * cs + x * sn);
+    } else {
+      float* e = reinterpret_cast<float*>(base);
+      const float x = e[i], y = e[i + half];
+      e[i] = x * cs - y * sn;
+      e[i + half] = y * cs + x * sn;
+    }
+  }
+}
+
+// A bf16 row of d = 128 held by the 16 lanes of a DPP row, lane j holding
+// dimensions 8j .. 8j+7, rotated at position p: the other half of lane j's
+// pairs sits in lane j ^ 8, read with a row rotation by 8 lanes.
+__device__ __forceinline__ uint4 rope_row16(uint4 x, const Rope& r, int64_t p, int j) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t o[4];
+  const bool first = j < 8;  // this lane holds x_i (else x_(i + d/2))
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t q = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w[k], 0x128, 0xF, 0xF, false);  // row_ror:8
+    float cs0, sn0, cs1, sn1;
+    rope_cs(r, 128, p, 8 * (j & 7) + 2 * k, cs0, sn0);
+    rope_cs(r, 128, p, 8 * (j & 7) + 2 * k + 1, cs1, sn1);
+    const float a0 = bf_lo(w[k]), a1 = bf_hi(w[k]), b0 = bf_lo(q), b1 = bf_hi(q);
+    const float v0 = first ? a0 * cs0 - b0 * sn0 : a0 * cs0 + b0 * sn0;
+    const float v1 = first ? a1 * cs1 - b1 * sn1 : a1 * cs1 + b1 * sn1;
+    o[k] = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 __global__ void append_fp8_kernel(AppendArgs a) {
   const int64_t rows = (int64_t)a.B * a.n_kv * a.n_new * 2;
   const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
@@ -376,7 +498,9 @@ __global__ void append_fp8_kernel(AppendArgs a) {
   const int64_t keep_from = max64d((int64_t)a.S, (int64_t)a.p0[b] + a.n_new - a.W);
   const size_t src = (((size_t)b * a.n_kv + kvh) * a.n_new + i) * a.in_row_bytes + (size_t)j * 16;
   float sc;
-  const uint2 codes = quant_row16(ld16((tensor ? a.v : a.k) + src), sc);
+  uint4 x = ld16((tensor ? a.v : a.k) + src);
+  if (a.rope.on && tensor == 0) x = rope_row16(x, a.rope, p, j);  // the whole group takes this branch
+  const uint2 codes = quant_row16(x, sc);
   char* dst;
   float* sdst;
   if (a.map.kind[kvh]) {
@@ -1009,6 +1133,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   issue(2, ring2);
   wait_vmcnt<WAITN>();  // unit 0 and the staging loads have landed
   lds_barrier();
+  if (a.rope.on) {
+    // the queries (and the new token's K row) turned at the query's position
+    const int64_t qpos = a.rows[w.row].new_pos - (a.new_k ? 0 : 1);
+    rope_stage<C::ES>(stage, G, stage + QSTAGE, add_new, C::IROWB, D, qpos, a.rope);
+    lds_barrier();
+  }
   // this wavefront's HW queries, in the lane's slice layout (of the four-lane
   // score layout when it is on)
   constexpr int QCPL = SC4 ? S4::CPL4 * S4::QPC : C::CPL;
@@ -1348,6 +1478,14 @@ int64_t round_rows_d(int g) {
 hipError_t launch_table_update(const TableUpdateArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
   table_update_kernel<<<1, kMaxTableUpdates, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope(const RopeArgs& a, hipStream_t s) {
+  const int64_t pairs = (int64_t)a.B * (a.n_q + a.n_kv) * a.C * (a.d / 2);
+  if (pairs == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((pairs + 255) / 256, 8192);
+  rope_kernel<<<(unsigned)blocks, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

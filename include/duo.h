@@ -81,7 +81,20 @@ typedef enum { DUO_KV_NATIVE = 0, DUO_KV_FP8 = 1 } duo_kv_format;
  * positions of every retrieval head of one batch row, and a row takes a page
  * from the pool when it grows past its last page.  T_cap still bounds each
  * row (it sizes the page tables).  Streaming heads keep their S + W slots per
- * batch row either way. */
+ * batch row either way.
+ *
+ * rope_theta > 0 applies rotary position embedding at each token's logical
+ * position, not at the slot a ring buffer gives it ("Attention Variants and
+ * Memory Efficiency", "Sliding-Window and Mixed Attention"; "What the
+ * Inference Runtime Can Change": the kernel applies the checkpoint's
+ * positional treatment).  The rotation is the one of Su et al., "RoFormer:
+ * Enhanced Transformer with Rotary Position Embedding": dimensions i and
+ * i + d/2 (i < d/2) turn by the angle p * rope_theta^(-2i/d) at position p.
+ * Keys are stored rotated (appends, prefill commits, fused appends); queries
+ * are rotated at their own position by decode and prefill.  Values are never
+ * rotated.  The angle is formed and reduced modulo 2 pi in double precision;
+ * the rotation runs in fp32 and the result is rounded to the cache dtype.
+ * rope_theta = 0: queries and keys are used as given. */
 typedef struct {
   int32_t L, B, n_q, n_kv, d_head;
   int64_t T_cap;
@@ -91,6 +104,7 @@ typedef struct {
   int32_t kv_format; /* duo_kv_format of the stored K/V rows (0 = native) */
   int32_t page_rows; /* 0: contiguous retrieval rows; else rows per page (power of two >= 256) */
   int32_t n_pages;   /* paged: pages per layer (>= 1); ignored when page_rows = 0 */
+  float rope_theta;  /* 0: no rotary embedding; else its base (> 1, e.g. 10000) */
 } duo_config;
 
 typedef struct duo_cache duo_cache; /* opaque host handle */
@@ -185,10 +199,19 @@ int duo_decode_append(duo_cache* c, int layer, const void* k, const void* v, con
  * attended first and then appended as by duo_append.  With DUO_KV_FP8 the held
  * rows are read as stored (code value * scale) and the chunk's own rows as
  * given, and ws must hold duo_cache_bytes' workspace_bytes (DUO_EWORKSPACE
- * otherwise); a native cache needs no workspace here.  DUO_ECAPACITY if
- * P + C > T_cap or (paged) the chunk needs more pages than are free. */
+ * otherwise); a native cache needs no workspace here.  With rope_theta > 0
+ * the chunk's queries and keys are rotated at positions P + i into the
+ * workspace first (ws must then hold duo_prefill_workspace_bytes for B rows
+ * and C tokens).  DUO_ECAPACITY if P + C > T_cap or (paged) the chunk needs
+ * more pages than are free. */
 int duo_prefill_chunk(duo_cache* c, int layer, const void* q, const void* k, const void* v,
                       int64_t C, void* out, float scale, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes duo_prefill_chunk (rows = B) or duo_prefill_chunk_row
+ * (rows = 1) needs for a chunk of C tokens: 0 for a native cache without
+ * rotary positions; the decode workspace for DUO_KV_FP8; with rotary
+ * positions the decode workspace plus room for the rotated chunk. */
+int duo_prefill_workspace_bytes(const duo_cache* c, int rows, int64_t C, size_t* bytes);
 
 /* duo_prefill_chunk for batch row `row` alone, at P = that row's token count:
  * q, out device [1][n_q][C][d]; k, v device [1][n_kv][C][d]. */

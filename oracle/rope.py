@@ -76,31 +76,46 @@ def round_to(x, dtype: str) -> np.ndarray:
     return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
 
 
-def stored_keys(K, theta: float, dtype: str) -> np.ndarray:
+def stored_keys(K, theta: float, dtype: str, kv_format=None) -> np.ndarray:
     """K [n_kv][T][d] (row = position) -> what the cache holds: each row
-    rotated at its position and rounded to the cache dtype, float64."""
+    rotated at its position and rounded to the cache dtype, float64.  With
+    FP8 rows (oracle.quant) the rotated, rounded row is what is quantized."""
     K = np.asarray(K, dtype=np.float64)
-    return round_to(rotate(K, np.arange(K.shape[-2]), theta), dtype)
+    Ks = round_to(rotate(K, np.arange(K.shape[-2]), theta), dtype)
+    if kv_format == "fp8":
+        from . import quant as _q
+        Ks = _q.stored_values(Ks.astype(np.float32))
+    return Ks
+
+
+def stored_values(V, kv_format=None) -> np.ndarray:
+    """What the cache holds for value rows V (float32 inputs): as given, or
+    dequantized FP8 rows."""
+    if kv_format == "fp8":
+        from . import quant as _q
+        return _q.stored_values(np.asarray(V, dtype=np.float32))
+    return np.asarray(V, dtype=np.float64)
 
 
 def decode_step_rope(q, K, V, mask: Sequence[int], S: int, W: int, scale: float, theta: float, dtype: str,
-                     route: str = "cache"):
+                     route: str = "cache", kv_format=None):
     """Decode at position T - 1 (T = K.shape[1]): the query q [n_q][d]
-    rotated at T - 1 against the stored (rotated, rounded) keys; V as given."""
+    rotated at T - 1 against the stored (rotated, rounded) keys and the
+    stored values."""
     from . import attention as _att
     K = np.asarray(K, dtype=np.float64)
     T = K.shape[1]
     qr = rotate(np.asarray(q, dtype=np.float64)[:, None, :], [T - 1], theta)[:, 0, :]
-    return _att.decode_step(qr, stored_keys(K, theta, dtype), np.asarray(V, dtype=np.float64), mask, S, W, scale,
-                            route=route)
+    return _att.decode_step(qr, stored_keys(K, theta, dtype, kv_format), stored_values(V, kv_format), mask, S, W,
+                            scale, route=route)
 
 
 def prefill_chunked_rope(Q, K, V, mask: Sequence[int], S: int, W: int, scale: float, theta: float, dtype: str,
-                         chunks) -> np.ndarray:
+                         chunks, kv_format=None) -> np.ndarray:
     """Chunked prefill ([n_q][N][d], [n_kv][N][d]; N = sum(chunks)): chunk
     row i at position P + i attends, with its query rotated at P + i, over the
-    held keys as stored and the chunk's own keys as rotated; then the chunk is
-    stored."""
+    held keys and values as stored and the chunk's own keys as rotated (its
+    values as given); then the chunk is stored."""
     from . import attention as _att
     from . import cache as _cache
     Q = np.asarray(Q, dtype=np.float64)
@@ -110,7 +125,8 @@ def prefill_chunked_rope(Q, K, V, mask: Sequence[int], S: int, W: int, scale: fl
     n_kv = K.shape[0]
     Qr = rotate(Q, np.arange(N), theta)
     Kr = rotate(K, np.arange(N), theta)
-    Ks = round_to(Kr, dtype)
+    Ks = stored_keys(K, theta, dtype, kv_format)
+    Vs = stored_values(V.astype(np.float32) if kv_format == "fp8" else V, kv_format)
     out = np.empty((n_q, N, d), dtype=np.float64)
     heads = [_cache.make_head_cache(bool(mask[k]), S, W) for k in range(n_kv)]
     P = 0
@@ -121,7 +137,7 @@ def prefill_chunked_rope(Q, K, V, mask: Sequence[int], S: int, W: int, scale: fl
             held = np.asarray(heads[k].positions(), dtype=np.int64)
             kp = np.concatenate([held, np.arange(P, P + C)])
             keys = np.concatenate([Ks[k][held], Kr[k][P:P + C]])
-            vals = np.concatenate([V[k][held], V[k][P:P + C]])
+            vals = np.concatenate([Vs[k][held], V[k][P:P + C]])
             out[h, P:P + C] = _att.attend_rows(Qr[h, P:P + C], np.arange(P, P + C), keys, vals, kp, bool(mask[k]),
                                                S, W, scale)
         for k in range(n_kv):

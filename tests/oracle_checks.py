@@ -521,6 +521,13 @@ def check_rope_cache_route_uses_logical_positions():
     Q2[:, T - 1] = q
     pre = RP.prefill_chunked_rope(Q2, K, V, [1, 0], S, W, 0.25, 1e4, "f32", [T - 1, 1])
     assert np.allclose(pre[:, T - 1], dec, atol=1e-12)
+    # FP8 rows: the cache's decode equals the FP8 route over keys rotated and
+    # rounded to bf16 beforehand (with the query rotated at T - 1)
+    qr = RP.rotate(q[:, None, :], [T - 1], 1e4)[:, 0, :]
+    Kb = RP.round_bf16(RP.rotate(K, np.arange(T), 1e4)).astype(np.float32)
+    want = QZ.decode_step_fp8(qr, Kb, V.astype(np.float32), [1, 0], S, W, 0.25)
+    got = RP.decode_step_rope(q, K, V.astype(np.float32), [1, 0], S, W, 0.25, 1e4, "bf16", kv_format="fp8")
+    assert np.allclose(got, want, atol=1e-12)
 
 
 ALL_CHECKS = [

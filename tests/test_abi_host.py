@@ -106,6 +106,10 @@ BAD = [
     (dict(page_rows=384, n_pages=4), H.DUO_EINVAL),          # a power of two
     (dict(page_rows=256, n_pages=0), H.DUO_EINVAL),          # an empty pool
     (dict(page_rows=-256, n_pages=4), H.DUO_EINVAL),
+    (dict(rope_theta=-1.0), H.DUO_EINVAL),
+    (dict(rope_theta=1.0), H.DUO_EINVAL),                    # a base must exceed 1
+    (dict(rope_theta=float("nan")), H.DUO_EINVAL),
+    (dict(rope_theta=float("inf")), H.DUO_EINVAL),
 ]
 
 
@@ -119,7 +123,7 @@ def test_validation_codes(over, code):
     cfg = H.duo_config(base["L"], base["B"], base["n_q"], base["n_kv"], base["d_head"], base["T_cap"],
                        base["sink"], base["recent"], over.get("dtype_code", H.DUO_BF16),
                        ctypes.cast(buf, ctypes.POINTER(ctypes.c_uint8)), over.get("kv_format", 0),
-                       over.get("page_rows", 0), over.get("n_pages", 0))
+                       over.get("page_rows", 0), over.get("n_pages", 0), over.get("rope_theta", 0.0))
     a = ctypes.c_size_t()
     rc = H.lib.duo_cache_bytes(ctypes.byref(cfg), ctypes.byref(a), None)
     assert rc == code, H.lib.duo_last_error()
@@ -146,6 +150,8 @@ def test_calls_on_null_handle_fail_cleanly():
     assert H.lib.duo_cache_fork_row(None, 0, 0, 1, None) == H.DUO_EINVAL
     assert H.lib.duo_cache_free_pages(None, 0, ctypes.byref(x)) == H.DUO_EINVAL
     assert H.lib.duo_cache_row_pages(None, 0, 0, None, 0, ctypes.byref(x)) == H.DUO_EINVAL
+    sz = ctypes.c_size_t()
+    assert H.lib.duo_prefill_workspace_bytes(None, 1, 10, ctypes.byref(sz)) == H.DUO_EINVAL
     H.lib.duo_cache_free(None)
 
 
