@@ -96,7 +96,9 @@ def bench_decode(w: WL.Workload, steps: int, warmup: int, layers: int):
     T = w.T
     fill = T - 1 if append else T
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    cache = H.DuoCache(L, w.B, w.n_q, w.n_kv, w.d, T, w.S, w.W, w.dtype, mask, device=dev, kv_format=w.kv_format)
+    pages = dict(page_rows=w.page_rows, n_pages=w.B * -(-T // w.page_rows)) if w.page_rows else {}
+    cache = H.DuoCache(L, w.B, w.n_q, w.n_kv, w.d, T, w.S, w.W, w.dtype, mask, device=dev, kv_format=w.kv_format,
+                       rope_theta=w.rope_theta, **pages)
     log(f"{w.name}: arena {cache.arena_bytes / 1e9:.2f} GB, filling {L} layers x {fill} tokens")
     t0 = time.time()
     buf_k = torch.empty(w.B, w.n_kv, fill, w.d, dtype=dt, device=dev)
@@ -303,7 +305,8 @@ def main():
     ap.add_argument("--workload", default="gqa70b_decode_128k",
                     choices=[n for n, w in WL.WORKLOADS.items() if w.mode in ("decode", "decode_append")])
     ap.add_argument("--layers", type=int, default=0, help="limit layers (profiling only; 0 = all)")
-    ap.add_argument("--also", default="mha7b_decode_128k,gqa70b_decode_128k_fp8,mha7b_decode_128k_fp8",
+    ap.add_argument("--also", default="mha7b_decode_128k,gqa70b_decode_128k_fp8,mha7b_decode_128k_fp8,"
+                                      "gqa70b_decode_128k_paged,gqa70b_decode_128k_rope",
                     help="comma-separated extra decode workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-gated", action="store_true")
@@ -364,7 +367,8 @@ def main():
         wa = WL.WORKLOADS[name]
         ra = bench_decode(wa, args.steps, args.warmup, wa.L)
         va = ra["step_bytes"] / (ra["ms_step"] * 1e-3) / 1e9
-        also.append({"workload": name, "kv_rows": wa.kv_format or wa.dtype,
+        also.append({"workload": name, "kv_rows": wa.kv_format or wa.dtype, "page_rows": wa.page_rows,
+                     "rope_theta": wa.rope_theta,
                      "value": round(va, 2), "unit": "GB/s", "us_per_step": round(ra["ms_step"] * 1e3, 1),
                      "hbm_frac": round(va / HBM_PEAK_GBS, 4),
                      "decode_kernel_gbs": round(ra["decode_avg_bytes"] / ra["decode_avg_s"] / 1e9, 2),

@@ -437,17 +437,17 @@ __device__ __forceinline__ uint2 quant_row16(uint4 x, float& scale) {
 // as append_kernel.
 // Rotary positions in decode: rows [0, nq) of the staging area (the group's
 // queries, row_bytes apart) and, if with_k, the new token's K row at k_row,
-// rotated in place at position p; one thread per (row, dimension pair).
+// rotated in place; one thread per (row, dimension pair).  Every row turns by
+// the same angles: (cs, sn) are those of pair lane % (d/2), which is the pair
+// of every thread's share (d/2 divides 64).
 template <int ES>
 __device__ __forceinline__ void rope_stage(char* stage, int nq, char* k_row, bool with_k, int row_bytes, int d,
-                                           int64_t p, const Rope& r) {
+                                           float cs, float sn) {
   const int half = d / 2;
   const int n = (nq + (with_k ? 1 : 0)) * half;
   for (int t = threadIdx.x; t < n; t += kDecodeThreads) {
     const int row = t / half, i = t % half;
     char* base = row < nq ? stage + row * row_bytes : k_row;
-    float cs, sn;
-    rope_cs(r, d, p, i, cs, sn);
     if constexpr (ES == 2) {
       uint16_t* e = reinterpret_cast<uint16_t*>(base);
       const float x = __uint_as_float((uint32_t)e[i] << 16), y = __uint_as_float((uint32_t)e[i + half] << 16);
@@ -1131,12 +1131,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   }
   issue(1, ring1);
   issue(2, ring2);
+  // rotary positions: this lane's angle (pair lane % (D/2)) at the query's
+  // position, computed while the loads are in flight
+  float rcs = 1.f, rsn = 0.f;
+  if (a.rope.on) rope_cs(a.rope, D, a.rows[w.row].new_pos - (a.new_k ? 0 : 1), lane % (D / 2), rcs, rsn);
   wait_vmcnt<WAITN>();  // unit 0 and the staging loads have landed
   lds_barrier();
   if (a.rope.on) {
     // the queries (and the new token's K row) turned at the query's position
-    const int64_t qpos = a.rows[w.row].new_pos - (a.new_k ? 0 : 1);
-    rope_stage<C::ES>(stage, G, stage + QSTAGE, add_new, C::IROWB, D, qpos, a.rope);
+    rope_stage<C::ES>(stage, G, stage + QSTAGE, add_new, C::IROWB, D, rcs, rsn);
     lds_barrier();
   }
   // this wavefront's HW queries, in the lane's slice layout (of the four-lane

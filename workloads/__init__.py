@@ -59,6 +59,8 @@ class Workload:
     chunk: int = 0          # prefill chunk length
     fixed_mask: Optional[tuple] = None  # explicit per-layer mask rows, else seeded
     kv_format: Optional[str] = None     # "fp8": K/V rows stored as FP8 codes + row scales
+    page_rows: int = 0                  # > 0: retrieval rows in pages of this many rows
+    rope_theta: float = 0.0             # > 0: rotary positions with this base
 
     @property
     def g(self) -> int:
@@ -112,9 +114,18 @@ WORKLOADS: Dict[str, Workload] = {
 # (same shapes and inputs).
 for _n in ("gqa70b_decode_128k", "mha7b_decode_128k"):
     WORKLOADS[_n + "_fp8"] = WORKLOADS[_n].with_(name=_n + "_fp8", kv_format="fp8")
-# Workloads that run on the mixed cache in the cache dtype (the gated forward
-# runs on none, the FP8 variants repeat shapes already listed).
-ORDER: List[str] = [n for n, w in WORKLOADS.items() if w.mode != "gated" and w.kv_format is None]
+# The 70B decode again with the retrieval rows in 256-row pages (same shapes
+# and inputs; the pool holds exactly the rows the batch needs).
+WORKLOADS["gqa70b_decode_128k_paged"] = WORKLOADS["gqa70b_decode_128k"].with_(name="gqa70b_decode_128k_paged",
+                                                                            page_rows=256)
+# ... and with rotary positions (base 500,000, as LLaMA-3 checkpoints use).
+WORKLOADS["gqa70b_decode_128k_rope"] = WORKLOADS["gqa70b_decode_128k"].with_(name="gqa70b_decode_128k_rope",
+                                                                           rope_theta=500000.0)
+# Workloads that run on the mixed cache in the cache dtype, contiguous (the
+# gated forward runs on none, the FP8 and paged variants repeat shapes
+# already listed).
+ORDER: List[str] = [n for n, w in WORKLOADS.items()
+                    if w.mode != "gated" and w.kv_format is None and w.page_rows == 0 and w.rope_theta == 0]
 
 
 def _rng(w: Workload, layer: int, b: int, head: int, tensor_id: int, block: int) -> np.random.Generator:
