@@ -306,7 +306,8 @@ def main():
                     choices=[n for n, w in WL.WORKLOADS.items() if w.mode in ("decode", "decode_append")])
     ap.add_argument("--layers", type=int, default=0, help="limit layers (profiling only; 0 = all)")
     ap.add_argument("--also", default="mha7b_decode_128k,gqa70b_decode_128k_fp8,mha7b_decode_128k_fp8,"
-                                      "gqa70b_decode_128k_paged,gqa70b_decode_128k_rope",
+                                      "gqa70b_decode_128k_paged,gqa70b_decode_128k_rope,"
+                                      "gqa70b_decode_128k_full,mha7b_decode_128k_full",
                     help="comma-separated extra decode workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-gated", action="store_true")
@@ -375,6 +376,16 @@ def main():
                      "decode_kernel_us": round(ra["decode_avg_s"] * 1e6, 2)})
     if also:
         line["also"] = also
+        # decode speedup of the mixed cache over full attention (every head a
+        # retrieval head) through the same kernels, attention only
+        steps_us = {x["workload"]: x["us_per_step"] for x in also}
+        if L == w.L:  # the whole model, like the entries above
+            steps_us[w.name] = round(r["ms_step"] * 1e3, 1)
+        vs_full = {n: {"mixed_us_per_step": steps_us[n], "full_us_per_step": steps_us[n + "_full"],
+                       "speedup": round(steps_us[n + "_full"] / steps_us[n], 3)}
+                   for n in steps_us if n + "_full" in steps_us}
+        if vs_full:
+            line["duo_vs_full_attention"] = vs_full
     if not args.no_prefill:
         pw = WL.WORKLOADS["llama3_8b_prefill_64k"]
         p = bench_prefill(pw)

@@ -121,11 +121,17 @@ WORKLOADS["gqa70b_decode_128k_paged"] = WORKLOADS["gqa70b_decode_128k"].with_(na
 # ... and with rotary positions (base 500,000, as LLaMA-3 checkpoints use).
 WORKLOADS["gqa70b_decode_128k_rope"] = WORKLOADS["gqa70b_decode_128k"].with_(name="gqa70b_decode_128k_rope",
                                                                            rope_theta=500000.0)
+# The two 128k decodes with every KV head a retrieval head: full attention
+# through the same kernels, the reference point of the decode speedup the
+# DuoAttention guide claims.
+for _n in ("gqa70b_decode_128k", "mha7b_decode_128k"):
+    WORKLOADS[_n + "_full"] = WORKLOADS[_n].with_(name=_n + "_full", n_ret=WORKLOADS[_n].n_kv)
 # Workloads that run on the mixed cache in the cache dtype, contiguous (the
 # gated forward runs on none, the FP8 and paged variants repeat shapes
 # already listed).
 ORDER: List[str] = [n for n, w in WORKLOADS.items()
-                    if w.mode != "gated" and w.kv_format is None and w.page_rows == 0 and w.rope_theta == 0]
+                    if w.mode != "gated" and w.kv_format is None and w.page_rows == 0 and w.rope_theta == 0
+                    and not n.endswith("_full")]
 
 
 def _rng(w: Workload, layer: int, b: int, head: int, tensor_id: int, block: int) -> np.random.Generator:
