@@ -14,6 +14,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "duo_internal.h"
@@ -280,7 +281,8 @@ int check_layer(const duo_cache* c, int layer) {
 // it needs to hold n_new more tokens, and enqueue the page-table writes ahead
 // of the kernels that use them.  DUO_ECAPACITY (nothing taken) if the pool
 // has too few free pages.  A row never holds fewer pages than its count
-// needs; it may hold more after a failed launch, which later growth reuses.
+// needs; it may hold more after a later launch of the call fails (their
+// table entries are written), which later growth reuses.
 int reserve_pages(duo_cache* c, int layer, int row, int64_t n_new, hipStream_t s) {
   if (!c->paged(layer)) return DUO_OK;
   duo_cache::Pages& pg = c->pages[layer];
@@ -293,10 +295,22 @@ int reserve_pages(duo_cache* c, int layer, int row, int64_t n_new, hipStream_t s
                 pg.free_list.size(), c->cfg.n_pages);
   duo::TableUpdateArgs u{};
   u.table = c->ptrs(layer).table;
-  auto flush = [&]() -> hipError_t {
+  // pages taken by this call whose table entries are not enqueued yet: given
+  // back if a launch fails, so no row ever holds a page its table does not name
+  std::vector<std::pair<int, int32_t>> pending;
+  auto flush = [&]() -> int {
     const hipError_t e = duo::launch_table_update(u, s);
     u.n = 0;
-    return e;
+    if (e != hipSuccess) {
+      for (auto it = pending.rbegin(); it != pending.rend(); ++it) {
+        pg.rows[it->first].pop_back();
+        pg.refs[it->second] = 0;
+        pg.free_list.push_back(it->second);
+      }
+      return hip_fail(e, "page table update launch");
+    }
+    pending.clear();
+    return DUO_OK;
   };
   for (int b = b0; b < b1; ++b) {
     const int64_t want = c->pages_for(c->len(layer, b) + n_new);
@@ -308,12 +322,12 @@ int reserve_pages(duo_cache* c, int layer, int row, int64_t n_new, hipStream_t s
       u.page[u.n] = page;
       ++u.n;
       pg.rows[b].push_back(page);
+      pending.emplace_back(b, page);
       if (u.n == duo::kMaxTableUpdates)
-        if (hipError_t e = flush()) return hip_fail(e, "page table update launch");
+        if (int r = flush()) return r;
     }
   }
-  if (hipError_t e = flush()) return hip_fail(e, "page table update launch");
-  return DUO_OK;
+  return flush();
 }
 
 // Enqueue the append of n_new tokens to every batch row at its own token
