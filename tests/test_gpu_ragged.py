@@ -251,3 +251,41 @@ def test_ragged_gqa70b_128k_layer():
     for b, (K, V, Q) in enumerate(rows):
         ref = OA.decode_step(stored(Q, w.dtype)[0], stored(K, w.dtype)[0], stored(V, w.dtype)[0], mask, w.S, w.W, w.scale)
         check_close(out[b], ref, w.dtype, f"ragged 70B row {b} (len {lens[b]})")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("page_rows,theta", [(0, 0.0), (256, 0.0), (256, 10000.0)])
+def test_ragged_max_rows(page_rows, theta):
+    """64 batch rows (the most a cache takes) of 1 to 2,016 tokens, grown in
+    two rounds of per-row appends and decoded together: the decode's row
+    table is full, and the longest rows split over several work items."""
+    need_gpu()
+    from head_wise_kv_amd import DuoCache
+    from oracle import rope as RP
+    say("ragged 64 rows", page_rows, theta)
+    B, n_kv, g, d, S, W = 64, 2, 4, 128, 4, 32
+    n_q = n_kv * g
+    mask = [1, 0]
+    lens = [1 + (37 * b * b + 11 * b) % 2016 for b in range(B)]
+    N = max(lens)
+    K, V, Q = _rows(B, n_kv, N, d, 2300, n_q)
+    kw = dict(page_rows=page_rows, n_pages=sum(-(-n // page_rows) for n in lens)) if page_rows else {}
+    c = DuoCache(1, B, n_q, n_kv, d, N, S, W, "bf16", [mask], rope_theta=theta, **kw)
+    Kd, Vd, Qd = (WL.to_torch(x, "bf16").cuda() for x in (K, V, Q))
+    for b, n in enumerate(lens):
+        h = n // 2
+        if h:
+            c.append_row(0, b, Kd[b:b + 1, :, :h].contiguous(), Vd[b:b + 1, :, :h].contiguous())
+        c.append_row(0, b, Kd[b:b + 1, :, h:n].contiguous(), Vd[b:b + 1, :, h:n].contiguous())
+    if page_rows:
+        assert c.free_pages(0) == 0
+    q = torch.stack([Qd[b, :, n - 1] for b, n in enumerate(lens)]).contiguous()
+    out = c.decode(0, q)
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        qs, Ks, Vs = stored(Q[b, :, n - 1], "bf16"), stored(K[b, :, :n], "bf16"), stored(V[b, :, :n], "bf16")
+        if theta:
+            ref = RP.decode_step_rope(qs, Ks, Vs, mask, S, W, d ** -0.5, theta, "bf16")
+        else:
+            ref = OA.decode_step(qs, Ks, Vs, mask, S, W, d ** -0.5)
+        check_close(out[b], ref, "bf16", f"64 rows: row {b} (len {n})")
