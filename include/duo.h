@@ -46,7 +46,7 @@ extern "C" {
 #define DUO_EINVAL (-1)        /* bad argument, shape, pointer or layer index     */
 #define DUO_EUNSUPPORTED (-2)  /* d_head, dtype or group size not built           */
 #define DUO_ECAPACITY (-3)     /* seq_len + n_new would exceed T_cap, or no free page */
-#define DUO_EEMPTY (-4)        /* decode on a layer that holds no token           */
+#define DUO_EEMPTY (-4)        /* decode of a batch row that holds no token       */
 #define DUO_EWORKSPACE (-5)    /* workspace missing or smaller than required      */
 #define DUO_EHIP (-6)          /* a HIP call or kernel launch failed              */
 
@@ -119,8 +119,9 @@ typedef struct duo_cache duo_cache; /* opaque host handle */
  * [B][ceil(T_cap / page_rows)] per layer.
  * *workspace_bytes: the device scratch that duo_decode, duo_decode_append and
  * duo_prefill_chunk need (partial softmax results; for DUO_KV_FP8 also room
- * for one layer's held rows in bf16, which prefill reads).  Either output
- * pointer may be NULL.  Returns DUO_OK or DUO_EINVAL/DUO_EUNSUPPORTED. */
+ * for one layer's held rows in bf16, which prefill reads; a prefill with
+ * rotary positions needs more, see duo_prefill_workspace_bytes).  Either
+ * output pointer may be NULL.  Returns DUO_OK or DUO_EINVAL/DUO_EUNSUPPORTED. */
 int duo_cache_bytes(const duo_config* cfg, size_t* arena_bytes, size_t* workspace_bytes);
 
 /* K+V payload bytes of the arena (the KV-cache size the guide's section 2
