@@ -37,17 +37,22 @@ METRIC = "mixed-head decode attention: KV GB/s (% HBM peak), µs/step at 128k ct
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SRC = os.path.join(ROOT, "head_wise_kv_amd", "csrc", "duo_kernels.hip")
-PREFILL_SRC = os.path.join(ROOT, "head_wise_kv_amd", "csrc", "duo_prefill.hip")
+# every source the decode kernels are compiled from: counters taken on an
+# older version of any of them no longer describe the kernel
+KERNEL_SRC = [os.path.join(ROOT, "head_wise_kv_amd", "csrc", f)
+              for f in ("duo_kernels.hip", "duo_internal.h", "duo_rows.h", "duo_rope.h")]
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def src_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def src_hash(paths) -> str:
+    h = hashlib.sha256()
+    for path in ([paths] if isinstance(paths, str) else paths):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic(name: str, kernel_hash: str):
