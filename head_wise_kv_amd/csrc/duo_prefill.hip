@@ -32,6 +32,11 @@
 //     the rest test each key's visible-row interval with one compare.
 //   * The online softmax rescales the O accumulators only when a row's
 //     running max has grown by more than a fixed slack.
+//   * Paged retrieval heads: a cached tile (64 keys from a multiple of 64)
+//     lies in one page, found through the batch row's page table with a
+//     scalar load when the tile is issued.  Rotary positions are applied
+//     before this kernel (queries and the chunk's keys rotated into the
+//     workspace), so it sees them as plain inputs.
 //
 // fp32: a plain vector-ALU path (one wavefront per query row) kept for
 // completeness of the dtype surface; it is not tuned.
