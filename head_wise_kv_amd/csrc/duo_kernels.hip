@@ -114,27 +114,28 @@ __global__ void copy_kernel(CopyArgs a) {
 // once.
 
 // Rotate the pairs of chunk x (dimensions c * E .. c * E + E - 1, E = 16 /
-// element size) and chunk y (the same dimensions + d/2) at position p.
+// element size) and chunk y (the same dimensions + d/2) at position p: a
+// key about to be stored, so in double, rounded once to the dtype.
 __device__ __forceinline__ void rope_chunks(uint4& x, uint4& y, const Rope& r, int d, int64_t p, int c, int dtype) {
   uint32_t xw[4] = {x.x, x.y, x.z, x.w}, yw[4] = {y.x, y.y, y.z, y.w};
   if (dtype == 1) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      float cs0, sn0, cs1, sn1;
-      rope_cs(r, d, p, c * 8 + 2 * w, cs0, sn0);
-      rope_cs(r, d, p, c * 8 + 2 * w + 1, cs1, sn1);
-      const float x0 = bf_lo(xw[w]), x1 = bf_hi(xw[w]), y0 = bf_lo(yw[w]), y1 = bf_hi(yw[w]);
-      xw[w] = f32_to_bf16_bits(x0 * cs0 - y0 * sn0) | (f32_to_bf16_bits(x1 * cs1 - y1 * sn1) << 16);
-      yw[w] = f32_to_bf16_bits(y0 * cs0 + x0 * sn0) | (f32_to_bf16_bits(y1 * cs1 + x1 * sn1) << 16);
+      double c0, s0, c1, s1;
+      rope_cs(r, d, p, c * 8 + 2 * w, c0, s0);
+      rope_cs(r, d, p, c * 8 + 2 * w + 1, c1, s1);
+      const double x0 = bf_lo(xw[w]), x1 = bf_hi(xw[w]), y0 = bf_lo(yw[w]), y1 = bf_hi(yw[w]);
+      xw[w] = bf16_bits_from_double(x0 * c0 - y0 * s0) | (bf16_bits_from_double(x1 * c1 - y1 * s1) << 16);
+      yw[w] = bf16_bits_from_double(y0 * c0 + x0 * s0) | (bf16_bits_from_double(y1 * c1 + x1 * s1) << 16);
     }
   } else {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      float cs, sn;
+      double cs, sn;
       rope_cs(r, d, p, c * 4 + w, cs, sn);
-      const float xv = __uint_as_float(xw[w]), yv = __uint_as_float(yw[w]);
-      xw[w] = __float_as_uint(xv * cs - yv * sn);
-      yw[w] = __float_as_uint(yv * cs + xv * sn);
+      const double xv = __uint_as_float(xw[w]), yv = __uint_as_float(yw[w]);
+      xw[w] = __float_as_uint((float)(xv * cs - yv * sn));
+      yw[w] = __float_as_uint((float)(yv * cs + xv * sn));
     }
   }
   x = make_uint4(xw[0], xw[1], xw[2], xw[3]);
@@ -208,21 +209,21 @@ __global__ void rope_kernel(RopeArgs a) {
     const int64_t row = u / half;  // (b, head, chunk row)
     const int64_t ci = row % a.C;
     const int b = (int)(row / a.C / (isq ? a.n_q : a.n_kv));
-    float cs, sn;
+    double cs, sn;  // keys are stored from these copies: rotated in double, rounded once
     rope_cs(a.rope, a.d, a.p0[b] + ci, i, cs, sn);
     const size_t e0 = (size_t)row * a.d + i, e1 = e0 + half;
     if (a.dtype == 1) {
       const uint16_t* in = static_cast<const uint16_t*>(isq ? a.q : a.k);
       uint16_t* out = static_cast<uint16_t*>(isq ? a.q_out : a.k_out);
-      const float x = __uint_as_float((uint32_t)in[e0] << 16), y = __uint_as_float((uint32_t)in[e1] << 16);
-      out[e0] = (uint16_t)f32_to_bf16_bits(x * cs - y * sn);
-      out[e1] = (uint16_t)f32_to_bf16_bits(y * cs + x * sn);
+      const double x = __uint_as_float((uint32_t)in[e0] << 16), y = __uint_as_float((uint32_t)in[e1] << 16);
+      out[e0] = (uint16_t)bf16_bits_from_double(x * cs - y * sn);
+      out[e1] = (uint16_t)bf16_bits_from_double(y * cs + x * sn);
     } else {
       const float* in = static_cast<const float*>(isq ? a.q : a.k);
       float* out = static_cast<float*>(isq ? a.q_out : a.k_out);
-      const float x = in[e0], y = in[e1];
-      out[e0] = x * cs - y * sn;
-      out[e1] = y * cs + x * sn;
+      const double x = in[e0], y = in[e1];
+      out[e0] = (float)(x * cs - y * sn);
+      out[e1] = (float)(y * cs + x * sn);
     }
   }
 }
@@ -439,15 +440,31 @@ __device__ __forceinline__ uint2 quant_row16(uint4 x, float& scale) {
 // queries, row_bytes apart) and, if with_k, the new token's K row at k_row,
 // rotated in place; one thread per (row, dimension pair).  Every row turns by
 // the same angles: (cs, sn) are those of pair lane % (d/2), which is the pair
-// of every thread's share (d/2 divides 64).
+// of every thread's share (d/2 divides 64).  Queries turn in float; the K
+// row, which the step stores, in double (rounded once, as the append does).
 template <int ES>
 __device__ __forceinline__ void rope_stage(char* stage, int nq, char* k_row, bool with_k, int row_bytes, int d,
-                                           float cs, float sn) {
+                                           double dcs, double dsn) {
   const int half = d / 2;
   const int n = (nq + (with_k ? 1 : 0)) * half;
+  const float cs = (float)dcs, sn = (float)dsn;
   for (int t = threadIdx.x; t < n; t += kDecodeThreads) {
     const int row = t / half, i = t % half;
-    char* base = row < nq ? stage + row * row_bytes : k_row;
+    if (row == nq) {  // the new key
+      if constexpr (ES == 2) {
+        uint16_t* e = reinterpret_cast<uint16_t*>(k_row);
+        const double x = __uint_as_float((uint32_t)e[i] << 16), y = __uint_as_float((uint32_t)e[i + half] << 16);
+        e[i] = (uint16_t)bf16_bits_from_double(x * dcs - y * dsn);
+        e[i + half] = (uint16_t)bf16_bits_from_double(y * dcs + x * dsn);
+      } else {
+        float* e = reinterpret_cast<float*>(k_row);
+        const double x = e[i], y = e[i + half];
+        e[i] = (float)(x * dcs - y * dsn);
+        e[i + half] = (float)(y * dcs + x * dsn);
+      }
+      continue;
+    }
+    char* base = stage + row * row_bytes;
     if constexpr (ES == 2) {
       uint16_t* e = reinterpret_cast<uint16_t*>(base);
       const float x = __uint_as_float((uint32_t)e[i] << 16), y = __uint_as_float((uint32_t)e[i + half] << 16);
@@ -463,8 +480,9 @@ __device__ __forceinline__ void rope_stage(char* stage, int nq, char* k_row, boo
 }
 
 // A bf16 row of d = 128 held by the 16 lanes of a DPP row, lane j holding
-// dimensions 8j .. 8j+7, rotated at position p: the other half of lane j's
-// pairs sits in lane j ^ 8, read with a row rotation by 8 lanes.
+// dimensions 8j .. 8j+7, rotated at position p (in double, rounded once to
+// bf16, as every stored key): the other half of lane j's pairs sits in lane
+// j ^ 8, read with a row rotation by 8 lanes.
 __device__ __forceinline__ uint4 rope_row16(uint4 x, const Rope& r, int64_t p, int j) {
   const uint32_t w[4] = {x.x, x.y, x.z, x.w};
   uint32_t o[4];
@@ -472,13 +490,13 @@ __device__ __forceinline__ uint4 rope_row16(uint4 x, const Rope& r, int64_t p, i
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const uint32_t q = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w[k], 0x128, 0xF, 0xF, false);  // row_ror:8
-    float cs0, sn0, cs1, sn1;
+    double cs0, sn0, cs1, sn1;
     rope_cs(r, 128, p, 8 * (j & 7) + 2 * k, cs0, sn0);
     rope_cs(r, 128, p, 8 * (j & 7) + 2 * k + 1, cs1, sn1);
-    const float a0 = bf_lo(w[k]), a1 = bf_hi(w[k]), b0 = bf_lo(q), b1 = bf_hi(q);
-    const float v0 = first ? a0 * cs0 - b0 * sn0 : a0 * cs0 + b0 * sn0;
-    const float v1 = first ? a1 * cs1 - b1 * sn1 : a1 * cs1 + b1 * sn1;
-    o[k] = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+    const double a0 = bf_lo(w[k]), a1 = bf_hi(w[k]), b0 = bf_lo(q), b1 = bf_hi(q);
+    const double v0 = first ? a0 * cs0 - b0 * sn0 : a0 * cs0 + b0 * sn0;
+    const double v1 = first ? a1 * cs1 - b1 * sn1 : a1 * cs1 + b1 * sn1;
+    o[k] = bf16_bits_from_double(v0) | (bf16_bits_from_double(v1) << 16);
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
@@ -1133,7 +1151,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   issue(2, ring2);
   // rotary positions: this lane's angle (pair lane % (D/2)) at the query's
   // position, computed while the loads are in flight
-  float rcs = 1.f, rsn = 0.f;
+  double rcs = 1.0, rsn = 0.0;
   if (a.rope.on) rope_cs(a.rope, D, a.rows[w.row].new_pos - (a.new_k ? 0 : 1), lane % (D / 2), rcs, rsn);
   wait_vmcnt<WAITN>();  // unit 0 and the staging loads have landed
   lds_barrier();
