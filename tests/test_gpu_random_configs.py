@@ -14,7 +14,7 @@ from oracle import quant as OQ
 from oracle import rope as RP
 from tests.gpu_util import check_close, need_gpu, say, stored
 
-N_CASES = 24
+N_CASES = 64
 
 
 def _draw(seed):
