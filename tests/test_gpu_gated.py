@@ -159,3 +159,33 @@ def test_gated_errors():
     assert e.value.code == H.DUO_EINVAL
     with pytest.raises(ValueError):
         H.gated_attention(q, k, k, a[:1].contiguous(), 1, 4)
+
+
+def _draw_gated(seed):
+    r = np.random.default_rng(seed)
+    dtype = str(r.choice(["bf16", "bf16", "f32"]))
+    d = int(r.choice([64, 128]))
+    n_kv = int(r.integers(1, 5))
+    g = int(r.choice([1, 2, 3, 4, 5, 8]))   # any group size, odd ones included
+    B = int(r.integers(1, 3))
+    N = int(r.integers(1, 900 if dtype == "bf16" else 300))
+    S = int(r.choice([0, 1, 7, 64]))
+    W = int(r.choice([1, 5, 64, 300]))
+    alpha = r.uniform(0.0, 1.0, n_kv).astype(np.float32)
+    alpha[r.random(n_kv) < 0.25] = 0.0
+    alpha[r.random(n_kv) < 0.25] = 1.0
+    return dtype, d, n_kv, g, B, N, S, W, alpha
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("seed", range(24))
+def test_gated_random_config(seed):
+    """Seeded random shapes: dtype, d, group size (odd included), batch,
+    sequence length (one token up), sinks, windows and gates (0 and 1
+    included), against the oracle."""
+    need_gpu()
+    dtype, d, n_kv, g, B, N, S, W, alpha = _draw_gated(8000 + seed)
+    say("gated random", dtype, d, n_kv, g, B, N, S, W)
+    Q, K, V = _inputs(B, n_kv * g, n_kv, d, N, seed=8100 + seed, sink_rows=min(S, 4))
+    out = _run(Q, K, V, alpha, S, W, dtype)
+    check_close(out, _oracle(Q, K, V, alpha, S, W, dtype), dtype, f"gated random {seed}")
