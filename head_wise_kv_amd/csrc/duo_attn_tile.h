@@ -1,9 +1,16 @@
 // MFMA attention tile pieces shared by the bf16 prefill and the gated forward
-// kernels (gfx950, v_mfma_f32_32x32x16_bf16).  One wavefront owns 64 query
-// rows (two 32-row N tiles) and consumes 64-key tiles of K and V that sit in
-// LDS, XOR-swizzled in 16-byte chunks; scores are computed as S^T = K Q^T so a
-// lane holds one query's scores, the online softmax runs in log2 units with a
-// lazy rescale, and O^T = V^T P^T is accumulated in fp32 registers.
+// kernels (gfx950, v_mfma_f32_32x32x16_bf16).  One wavefront owns 32 query
+// rows (one 32-row MFMA N tile; the pieces take kPfNT tiles) and consumes
+// 64-key tiles of K and V that sit in LDS, XOR-swizzled in 16-byte chunks;
+// scores are computed as S^T = K Q^T so a lane holds one query's scores, the
+// online softmax runs in log2 units with a lazy rescale, and O^T = V^T P^T is
+// accumulated in fp32 registers.
+//
+// 32 rows per wavefront keeps a wavefront under 256 registers, so two of them
+// share each SIMD: one's MFMA work then overlaps the other's softmax and
+// LDS waits.  (64 rows halve the LDS operand reads per MFMA but need about
+// 330 registers, one wavefront per SIMD, and every latency of that single
+// wavefront stays exposed.)
 //
 // Only included by the HIP sources of this library; everything is internal.
 #pragma once
@@ -21,10 +28,11 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kPfRowWaves = 2;                    // wavefronts per key half (one 64-row block each)
+constexpr int kPfRowWaves = 4;                    // wavefronts per key half (one row block each)
 constexpr int kPfHalves = 2;                      // key halves: even / odd key tiles
 constexpr int kPfThreads = 64 * kPfRowWaves * kPfHalves;
-constexpr int kPfRowsPerWave = 64;                // query rows per wavefront
+constexpr int kPfRowsPerWave = 32;                // query rows per wavefront
+constexpr int kPfNT = kPfRowsPerWave / 32;        // 32-row MFMA N tiles per wavefront
 constexpr int kBN = 64;                           // keys per tile
 
 // Integer min / max by plain comparison (kept off any floating-point path).
@@ -119,14 +127,11 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
 // ---- per-tile pieces of the MFMA path (one wavefront, 64 query rows = two
 // 32-row N tiles nt, one 64-key tile = two 32-key halves ct)
 
-// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
-
 // S^T = K Q^T for the keys ct*32 .. ct*32+31 of the tile: s[nt] register r of
 // lane (n, hf) is the score of key ct*32 + 8*(r/4) + 4*hf + r%4 and query
 // 32*nt + n.
 template <int D>
-__device__ __forceinline__ void pf_scores(f32x16_t (&s)[2], const bf16x8_t (&qb)[2][D / 16], const char* kt, int ct,
+__device__ __forceinline__ void pf_scores(f32x16_t (&s)[kPfNT], const bf16x8_t (&qb)[kPfNT][D / 16], const char* kt, int ct,
                                           int lane) {
   using SH = PfShape<D>;
   const int key = ct * 32 + (lane & 31);
@@ -137,14 +142,14 @@ __device__ __forceinline__ void pf_scores(f32x16_t (&s)[2], const bf16x8_t (&qb)
     const u32x4_t av = *reinterpret_cast<const u32x4_t*>(kt + key * (SH::CPR * 16) + ((c ^ SH::swz_k(key)) * 16));
     const bf16x8_t aop = __builtin_bit_cast(bf16x8_t, av);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < kPfNT; ++nt)
       s[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qb[nt][ks], ks == 0 ? f32x16_t{} : s[nt], 0, 0, 0);
   }
 }
 
 // Scores of keys a row does not see (half ct of the tile) become -inf.
-__device__ __forceinline__ void pf_mask(f32x16_t (&s)[2], const int32_t* klo, const uint32_t* kspan,
-                                        const int32_t (&iq)[2], int ct, int lane) {
+__device__ __forceinline__ void pf_mask(f32x16_t (&s)[kPfNT], const int32_t* klo, const uint32_t* kspan,
+                                        const int32_t (&iq)[kPfNT], int ct, int lane) {
   const int hf = lane >> 5;
 #pragma unroll
   for (int r4 = 0; r4 < 4; ++r4) {
@@ -156,7 +161,7 @@ __device__ __forceinline__ void pf_mask(f32x16_t (&s)[2], const int32_t* klo, co
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < kPfNT; ++nt)
         if (!sees(iq[nt], lo[j], sp[j])) s[nt][4 * r4 + j] = -INFINITY;
   }
 }
@@ -166,11 +171,11 @@ __device__ __forceinline__ void pf_mask(f32x16_t (&s)[2], const int32_t* klo, co
 // returns P^T as bf16 pairs pb[nt][k-step st][dword] plus the factor
 // alpha[nt] the accumulators must be scaled by; the result says whether any
 // lane's alpha differs from 1.
-__device__ __forceinline__ bool pf_softmax(const f32x16_t (&s)[2], float (&m_run)[2], float (&l_run)[2],
-                                           uint32_t (&pb)[2][2][4], float (&alpha)[2], float scale_log2) {
+__device__ __forceinline__ bool pf_softmax(const f32x16_t (&s)[kPfNT], float (&m_run)[kPfNT], float (&l_run)[kPfNT],
+                                           uint32_t (&pb)[kPfNT][2][4], float (&alpha)[kPfNT], float scale_log2) {
   bool grow = false;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < kPfNT; ++nt) {
     const f32x16_t& x = s[nt];
     const float v = fmaxf(max3(max3(x[0], x[1], x[2]), max3(x[3], x[4], x[5]), max3(x[6], x[7], x[8])),
                           max3(max3(x[9], x[10], x[11]), max3(x[12], x[13], x[14]), x[15]));
@@ -200,20 +205,19 @@ __device__ __forceinline__ bool pf_softmax(const f32x16_t (&s)[2], float (&m_run
 // Keeps the probabilities computed where they are written in the source: an
 // empty asm statement that reads them (it emits no instruction), so the
 // compiler cannot sink their computation past the branch that follows.
-__device__ __forceinline__ void pf_pin(const uint32_t (&pb)[2][2][4], const float (&l_run)[2]) {
-  asm volatile("" ::"v"(l_run[0]), "v"(l_run[1]));
-  asm volatile("" ::"v"(pb[0][0][0]), "v"(pb[0][0][1]), "v"(pb[0][0][2]), "v"(pb[0][0][3]), "v"(pb[0][1][0]),
-               "v"(pb[0][1][1]), "v"(pb[0][1][2]), "v"(pb[0][1][3]), "v"(pb[1][0][0]), "v"(pb[1][0][1]),
-               "v"(pb[1][0][2]), "v"(pb[1][0][3]), "v"(pb[1][1][0]), "v"(pb[1][1][1]), "v"(pb[1][1][2]),
-               "v"(pb[1][1][3]));
+__device__ __forceinline__ void pf_pin(const uint32_t (&pb)[kPfNT][2][4], const float (&l_run)[kPfNT]) {
+#pragma unroll
+  for (int nt = 0; nt < kPfNT; ++nt)
+    asm volatile("" ::"v"(l_run[nt]), "v"(pb[nt][0][0]), "v"(pb[nt][0][1]), "v"(pb[nt][0][2]), "v"(pb[nt][0][3]),
+                 "v"(pb[nt][1][0]), "v"(pb[nt][1][1]), "v"(pb[nt][1][2]), "v"(pb[nt][1][3]));
 }
 
 template <int DT>
-__device__ __forceinline__ void pf_rescale(f32x16_t (&o)[DT][2], const float (&alpha)[2]) {
+__device__ __forceinline__ void pf_rescale(f32x16_t (&o)[DT][kPfNT], const float (&alpha)[kPfNT]) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < kPfNT; ++nt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[dt][nt][r] *= alpha[nt];
 }
@@ -223,15 +227,15 @@ __device__ __forceinline__ void pf_rescale(f32x16_t (&o)[DT][2], const float (&a
 // row kb + i16/4 at columns dt*32 + 16*(g16%2) + 4*(i16%4) and receives
 // V[kb + 0..3][its d].
 template <int D>
-__device__ __forceinline__ void pf_pv(f32x16_t (&o)[D / 32][2], const uint32_t (&pb)[2][2][4], const char* vt,
+__device__ __forceinline__ void pf_pv(f32x16_t (&o)[D / 32][kPfNT], const uint32_t (&pb)[kPfNT][2][4], const char* vt,
                                       int ct, int lane) {
   using SH = PfShape<D>;
   const int hf = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
-    bf16x8_t bop[2];
+    bf16x8_t bop[kPfNT];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < kPfNT; ++nt) {
       const u32x4_t bw = {pb[nt][st][0], pb[nt][st][1], pb[nt][st][2], pb[nt][st][3]};
       bop[nt] = __builtin_bit_cast(bf16x8_t, bw);
     }
@@ -251,29 +255,26 @@ __device__ __forceinline__ void pf_pv(f32x16_t (&o)[D / 32][2], const uint32_t (
       const u32x4_t aw = {h0[0], h0[1], h1[0], h1[1]};
       const bf16x8_t aop = __builtin_bit_cast(bf16x8_t, aw);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < kPfNT; ++nt)
         o[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop[nt], o[dt][nt], 0, 0, 0);
     }
   }
 }
 
-// One 64-key tile, software pipelined over its halves so that MFMA work of
-// one half overlaps the softmax of the other:
+// One 64-key tile, ordered over its halves so that the MFMA work of one half
+// is independent of the softmax next to it:
 //   S(0) | mask(0) | S(1) + softmax(0) | rescale(0), mask(1) | P V(0) + softmax(1) | rescale(1) | P V(1)
-// The masks and rescales are wavefront-uniform branches between the
-// overlapped regions.
+// The masks and rescales are wavefront-uniform branches between the regions;
+// the compiler orders the instructions within a region.
 template <int D>
-__device__ __forceinline__ void pf_tile(f32x16_t (&o)[D / 32][2], float (&m_run)[2], float (&l_run)[2],
-                                        const bf16x8_t (&qb)[2][D / 16], const char* kt, const char* vt,
+__device__ __forceinline__ void pf_tile(f32x16_t (&o)[D / 32][kPfNT], float (&m_run)[kPfNT], float (&l_run)[kPfNT],
+                                        const bf16x8_t (&qb)[kPfNT][D / 16], const char* kt, const char* vt,
                                         bool masked, const int32_t* klo, const uint32_t* kspan,
-                                        const int32_t (&iq)[2], float scale_log2, int lane) {
-  constexpr int KSTEPS = D / 16, DT = D / 32;
-  constexpr int kMfmaHalf = 2 * KSTEPS;  // MFMAs per half for S, and 2 * 2 * DT for P V (equal for both)
-  static_assert(2 * 2 * DT == kMfmaHalf, "S and P V halves carry equal MFMA counts");
-  constexpr int kValuPerMfma = 8;
-  f32x16_t s0[2], s1[2];
-  uint32_t p0[2][2][4], p1[2][2][4];
-  float a0[2], a1[2];
+                                        const int32_t (&iq)[kPfNT], float scale_log2, int lane) {
+  constexpr int DT = D / 32;
+  f32x16_t s0[kPfNT], s1[kPfNT];
+  uint32_t p0[kPfNT][2][4], p1[kPfNT][2][4];
+  float a0[kPfNT], a1[kPfNT];
 
   pf_scores<D>(s0, qb, kt, 0, lane);
   __builtin_amdgcn_sched_barrier(0);
@@ -281,11 +282,6 @@ __device__ __forceinline__ void pf_tile(f32x16_t (&o)[D / 32][2], float (&m_run)
   __builtin_amdgcn_sched_barrier(0);
   pf_scores<D>(s1, qb, kt, 1, lane);
   const bool g0 = pf_softmax(s0, m_run, l_run, p0, a0, scale_log2);
-#pragma unroll
-  for (int i = 0; i < kMfmaHalf; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerMfma, 0);
-  }
   __builtin_amdgcn_sched_barrier(0);
   pf_pin(p0, l_run);
   if (g0) pf_rescale<DT>(o, a0);
@@ -293,20 +289,11 @@ __device__ __forceinline__ void pf_tile(f32x16_t (&o)[D / 32][2], float (&m_run)
   __builtin_amdgcn_sched_barrier(0);
   pf_pv<D>(o, p0, vt, 0, lane);
   const bool g1 = pf_softmax(s1, m_run, l_run, p1, a1, scale_log2);
-#pragma unroll
-  for (int i = 0; i < kMfmaHalf; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerMfma, 0);
-  }
   __builtin_amdgcn_sched_barrier(0);
   pf_pin(p1, l_run);
   if (g1) pf_rescale<DT>(o, a1);
   __builtin_amdgcn_sched_barrier(0);
   pf_pv<D>(o, p1, vt, 1, lane);
-  // all V operand reads of the last half first, then its MFMAs
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4 * DT, 0);
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMfmaHalf, 0);
 }
 
 }  // namespace

@@ -19,7 +19,7 @@
 // edge crosses are visited in both phases (with complementary masks).  The
 // output mixes the two normalised results.
 //
-// bf16: the MFMA tile pipeline of the prefill (four wavefronts: two 64-row
+// bf16: the MFMA tile pipeline of the prefill (eight wavefronts: four 32-row
 // blocks x two key halves that take the even and the odd tiles of each phase,
 // direct buffer->LDS loads, double buffered), with the saved phase-1 state
 // held in registers through phase 2; the halves merge both states through LDS
@@ -94,14 +94,14 @@ __device__ __forceinline__ GatedTiles gated_tiles(int64_t i0, int64_t i1, int S,
 }
 
 // Folds the other key half's softmax state (x: its O registers, one float per
-// lane and register, 64 apart; ml: its m at [nt*64], l at [(2+nt)*64]) into
-// this half's.
+// lane and register, 64 apart; ml: its m at [nt*64], l at [(kPfNT+nt)*64])
+// into this half's.
 template <int DT>
-__device__ __forceinline__ void merge_half(f32x16_t (&o)[DT][2], float (&m)[2], float (&l)[2], const float* x,
-                                           const float* ml) {
+__device__ __forceinline__ void merge_half(f32x16_t (&o)[DT][kPfNT], float (&m)[kPfNT], float (&l)[kPfNT],
+                                           const float* x, const float* ml) {
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const float m2 = ml[nt * 64], l2 = ml[(2 + nt) * 64];
+  for (int nt = 0; nt < kPfNT; ++nt) {
+    const float m2 = ml[nt * 64], l2 = ml[(kPfNT + nt) * 64];
     const float m_new = fmaxf(m[nt], m2);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float a1 = fast_exp2(m[nt] - m_use), a2 = fast_exp2(m2 - m_use);
@@ -110,23 +110,23 @@ __device__ __forceinline__ void merge_half(f32x16_t (&o)[DT][2], float (&m)[2], 
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][nt][r] = o[dt][nt][r] * a1 + x[((dt * 2 + nt) * 16 + r) * 64] * a2;
+      for (int r = 0; r < 16; ++r) o[dt][nt][r] = o[dt][nt][r] * a1 + x[((dt * kPfNT + nt) * 16 + r) * 64] * a2;
   }
 }
 
 template <int DT>
-__device__ __forceinline__ void spill_half(const f32x16_t (&o)[DT][2], const float (&m)[2], const float (&l)[2],
-                                           float* x, float* ml) {
+__device__ __forceinline__ void spill_half(const f32x16_t (&o)[DT][kPfNT], const float (&m)[kPfNT],
+                                           const float (&l)[kPfNT], float* x, float* ml) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < kPfNT; ++nt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[((dt * 2 + nt) * 16 + r) * 64] = o[dt][nt][r];
+      for (int r = 0; r < 16; ++r) x[((dt * kPfNT + nt) * 16 + r) * 64] = o[dt][nt][r];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < kPfNT; ++nt) {
     ml[nt * 64] = m[nt];
-    ml[(2 + nt) * 64] = l[nt];
+    ml[(kPfNT + nt) * 64] = l[nt];
   }
 }
 
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kPfThreads) void gated_mfma_kernel(GatedArgs a, int
   __shared__ int32_t klo_lds[kPfHalves][2][kBN];
   __shared__ uint32_t kspan_lds[kPfHalves][2][kBN];
   __shared__ int s_full[kPfHalves][2];
-  __shared__ float ml_lds[2][kPfRowWaves][4 * 64];  // [state][row wavefront]: m and l of the odd half
+  __shared__ float ml_lds[2][kPfRowWaves][2 * kPfNT * 64];  // [state][row wavefront]: m and l of the odd half
 
   const int ngrp = g / hpi;
   const int per_level = a.B * a.n_kv * ngrp;
@@ -171,11 +171,11 @@ __global__ __launch_bounds__(kPfThreads) void gated_mfma_kernel(GatedArgs a, int
   const size_t rowb = (size_t)D * 2;
 
   // Q^T operands: lane holds 8 consecutive d of query row (wr0 + 32*nt + n) per k-step.
-  bf16x8_t qb[2][KSTEPS];
-  int32_t iq[2];
-  bool qvalid[2];
+  bf16x8_t qb[kPfNT][KSTEPS];
+  int32_t iq[kPfNT];
+  bool qvalid[kPfNT];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < kPfNT; ++nt) {
     const int64_t qrow = wr0 + 32 * nt + n;
     qvalid[nt] = qrow < a.N;
     iq[nt] = (int32_t)qrow;
@@ -252,17 +252,20 @@ __global__ __launch_bounds__(kPfThreads) void gated_mfma_kernel(GatedArgs a, int
     }
   };
 
-  f32x16_t o[DT][2];
+  f32x16_t o[DT][kPfNT];
+  float m_run[kPfNT], l_run[kPfNT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int nt = 0; nt < kPfNT; ++nt) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[dt][nt][r] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    m_run[nt] = -INFINITY;
+    l_run[nt] = 0.f;
+  }
   // the state after phase 1 (sink + window keys only)
-  f32x16_t o_w[DT][2];
-  float m_w[2], l_w[2];
+  f32x16_t o_w[DT][kPfNT];
+  float m_w[kPfNT], l_w[kPfNT];
 
   {
     bool rest;
@@ -274,9 +277,9 @@ __global__ __launch_bounds__(kPfThreads) void gated_mfma_kernel(GatedArgs a, int
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) o_w[dt][nt] = o[dt][nt];
+        for (int nt = 0; nt < kPfNT; ++nt) o_w[dt][nt] = o[dt][nt];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < kPfNT; ++nt) {
         m_w[nt] = m_run[nt];
         l_w[nt] = l_run[nt];
       }
@@ -300,9 +303,9 @@ __global__ __launch_bounds__(kPfThreads) void gated_mfma_kernel(GatedArgs a, int
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) o_w[dt][nt] = o[dt][nt];
+      for (int nt = 0; nt < kPfNT; ++nt) o_w[dt][nt] = o[dt][nt];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < kPfNT; ++nt) {
       m_w[nt] = m_run[nt];
       l_w[nt] = l_run[nt];
     }
@@ -310,7 +313,7 @@ __global__ __launch_bounds__(kPfThreads) void gated_mfma_kernel(GatedArgs a, int
 
   // ---- merge the odd half's two states into the even half's through LDS
   // (the tile buffers are free now): per lane, registers in order (dt, nt, r).
-  constexpr int NREG = DT * 2 * 16;
+  constexpr int NREG = DT * kPfNT * 16;
   static_assert(kPfRowWaves * NREG * 64 * 4 <= kPfHalves * 2 * SH::TILE_BYTES, "one state fits a K or V buffer");
   float* x_full = reinterpret_cast<float*>(&k_lds[0][0][0]) + sub * NREG * 64 + lane;
   float* x_win = reinterpret_cast<float*>(&v_lds[0][0][0]) + sub * NREG * 64 + lane;
@@ -330,7 +333,7 @@ __global__ __launch_bounds__(kPfThreads) void gated_mfma_kernel(GatedArgs a, int
   // ---- mix and store: lane holds d = dt*32 + 8*(r/4) + 4*hf + r%4 of query 32*nt + n
   const float alpha = a.alpha[kvh];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < kPfNT; ++nt) {
     const float l_full = l_run[nt] + __shfl_xor(l_run[nt], 32);
     const float l_win = l_w[nt] + __shfl_xor(l_w[nt], 32);
     if (!qvalid[nt]) continue;

@@ -8,14 +8,14 @@
 // chunk is committed to the cache by the append kernel afterwards.
 //
 // bf16: a dense contraction, tiled on MFMA (v_mfma_f32_32x32x16_bf16).
-//   * Work item = one workgroup of four wavefronts: two row wavefronts, each
-//     owning 64 query rows of one query head (two 32-row MFMA N tiles; two
-//     heads of a GQA group, or two row blocks of one head), times two key
-//     halves that take the even and the odd key tiles of the same rows.  The
-//     halves merge their softmax states through LDS at the end, so every SIMD
-//     has a wavefront even when the item count is small.  64 query rows per
-//     wavefront keeps the LDS operand traffic (K and V re-read by every
-//     wavefront) well under the LDS bandwidth at full MFMA rate.
+//   * Work item = one workgroup of eight wavefronts: four row wavefronts,
+//     each owning 32 query rows of one query head (one 32-row MFMA N tile;
+//     up to four heads of a GQA group, or row blocks of one head), times two
+//     key halves that take the even and the odd key tiles of the same rows.
+//     The halves merge their softmax states through LDS at the end.  Every
+//     SIMD runs two wavefronts, so one's MFMA work overlaps the other's
+//     softmax; 128 query rows share each K / V tile a workgroup loads, and
+//     the LDS operand reads (1 KB per MFMA) stay under the LDS bandwidth.
 //   * K and V tiles of 64 keys are brought into LDS with direct buffer->LDS
 //     loads, double buffered per half: the next tile streams in while the
 //     current one is consumed.  Rows are XOR-swizzled in 16-byte chunks (the
@@ -178,11 +178,11 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
   const size_t rowb = (size_t)D * 2;
 
   // Q^T operands: lane holds 8 consecutive d of query row (wr0 + 32*nt + n) per k-step.
-  bf16x8_t qb[2][KSTEPS];
-  int32_t iq[2];  // chunk row of the lane's query in tile nt
-  bool qvalid[2];
+  bf16x8_t qb[kPfNT][KSTEPS];
+  int32_t iq[kPfNT];  // chunk row of the lane's query in tile nt
+  bool qvalid[kPfNT];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < kPfNT; ++nt) {
     const int64_t qrow = wr0 + 32 * nt + n;
     qvalid[nt] = qrow < a.C;
     iq[nt] = (int32_t)qrow;
@@ -296,14 +296,17 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
     }
   };
 
-  f32x16_t o[DT][2];
+  f32x16_t o[DT][kPfNT];
+  float m_run[kPfNT], l_run[kPfNT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int nt = 0; nt < kPfNT; ++nt) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[dt][nt][r] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    m_run[nt] = -INFINITY;
+    l_run[nt] = 0.f;
+  }
 
   // The two halves walk the tile list in lockstep, one barrier per step.
   const int64_t n_steps = (n_tiles + 1) / 2;
@@ -325,31 +328,31 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
 
   // ---- merge the odd half into the even half through LDS (the tile buffers
   // are free now): per lane, registers in order (dt, nt, r), then m and l.
-  constexpr int NREG = DT * 2 * 16;
+  constexpr int NREG = DT * kPfNT * 16;
   static_assert(kPfRowWaves * NREG * 64 * 4 <= kPfHalves * 2 * SH::TILE_BYTES, "exchange fits the K buffers");
-  static_assert(kPfRowWaves * 4 * 64 * 4 <= kPfHalves * 2 * SH::TILE_BYTES, "m, l fit the V buffers");
+  static_assert(kPfRowWaves * 2 * kPfNT * 64 * 4 <= kPfHalves * 2 * SH::TILE_BYTES, "m, l fit the V buffers");
   float* xo = reinterpret_cast<float*>(&k_lds[0][0][0]) + sub * NREG * 64 + lane;
-  float* xml = reinterpret_cast<float*>(&v_lds[0][0][0]) + sub * 4 * 64 + lane;
+  float* xml = reinterpret_cast<float*>(&v_lds[0][0][0]) + sub * 2 * kPfNT * 64 + lane;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (kh == 1) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < kPfNT; ++nt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) xo[((dt * 2 + nt) * 16 + r) * 64] = o[dt][nt][r];
+        for (int r = 0; r < 16; ++r) xo[((dt * kPfNT + nt) * 16 + r) * 64] = o[dt][nt][r];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < kPfNT; ++nt) {
       xml[nt * 64] = m_run[nt];
-      xml[(2 + nt) * 64] = l_run[nt];
+      xml[(kPfNT + nt) * 64] = l_run[nt];
     }
   }
   __syncthreads();
   if (kh == 1) return;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const float m2 = xml[nt * 64], l2 = xml[(2 + nt) * 64];
+  for (int nt = 0; nt < kPfNT; ++nt) {
+    const float m2 = xml[nt * 64], l2 = xml[(kPfNT + nt) * 64];
     const float m_new = fmaxf(m_run[nt], m2);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float a1 = fast_exp2(m_run[nt] - m_use), a2 = fast_exp2(m2 - m_use);
@@ -357,12 +360,12 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][nt][r] = o[dt][nt][r] * a1 + xo[((dt * 2 + nt) * 16 + r) * 64] * a2;
+      for (int r = 0; r < 16; ++r) o[dt][nt][r] = o[dt][nt][r] * a1 + xo[((dt * kPfNT + nt) * 16 + r) * 64] * a2;
   }
 
   // ---- normalise and store: lane holds d = dt*32 + 8*(r/4) + 4*hf + r%4 of query 32*nt + n
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < kPfNT; ++nt) {
     const float l_tot = l_run[nt] + __shfl_xor(l_run[nt], 32);
     if (!qvalid[nt]) continue;
     const float inv = 1.f / l_tot;
