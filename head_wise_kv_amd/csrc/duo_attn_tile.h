@@ -46,6 +46,19 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Max and sum over the lane pair (i, i ^ 32).  One v_permlane32_swap exchanges
+// the two 32-lane halves on the vector ALU (no LDS round trip): result r[0]
+// holds the lower half's values in both halves and r[1] the upper half's, so
+// both lanes of a pair combine the same two values in the same order.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 __device__ __forceinline__ float max3(float x, float y, float z) { return fmaxf(fmaxf(x, y), z); }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -179,7 +192,7 @@ __device__ __forceinline__ bool pf_softmax(const f32x16_t (&s)[kPfNT], float (&m
     const f32x16_t& x = s[nt];
     const float v = fmaxf(max3(max3(x[0], x[1], x[2]), max3(x[3], x[4], x[5]), max3(x[6], x[7], x[8])),
                           max3(max3(x[9], x[10], x[11]), max3(x[12], x[13], x[14]), x[15]));
-    const float mx = fmaxf(v, __shfl_xor(v, 32)) * scale_log2;
+    const float mx = pair_max(v) * scale_log2;
     const bool g = mx > m_run[nt] + kRescaleSlack;
     grow |= g;
     const float m_new = g ? mx : m_run[nt];  // mx > m_run here

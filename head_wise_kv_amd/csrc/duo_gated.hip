@@ -334,8 +334,8 @@ __global__ __launch_bounds__(kPfThreads) void gated_mfma_kernel(GatedArgs a, int
   const float alpha = a.alpha[kvh];
 #pragma unroll
   for (int nt = 0; nt < kPfNT; ++nt) {
-    const float l_full = l_run[nt] + __shfl_xor(l_run[nt], 32);
-    const float l_win = l_w[nt] + __shfl_xor(l_w[nt], 32);
+    const float l_full = pair_sum(l_run[nt]);
+    const float l_win = pair_sum(l_w[nt]);
     if (!qvalid[nt]) continue;
     const float cf = alpha / l_full, cw = (1.f - alpha) / l_win;
     const int64_t qrow = wr0 + 32 * nt + n;

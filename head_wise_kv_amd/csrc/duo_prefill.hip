@@ -23,7 +23,7 @@
 //     free of bank conflicts.
 //   * Scores S^T = K Q^T put keys on the MFMA M axis and queries on N, so each
 //     lane holds one query's scores and the softmax needs one exchange with
-//     the partner lane.  P^T then feeds O^T = V^T P^T directly from the
+//     the partner lane (v_permlane32_swap).  P^T then feeds O^T = V^T P^T from the
 //     accumulator registers; the V^T operand comes straight from the
 //     row-major V tile through LDS transpose reads (ds_read_b64_tr_b16).
 //   * Streaming heads visit only the sink tiles, the ring tiles some row's
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
   // ---- normalise and store: lane holds d = dt*32 + 8*(r/4) + 4*hf + r%4 of query 32*nt + n
 #pragma unroll
   for (int nt = 0; nt < kPfNT; ++nt) {
-    const float l_tot = l_run[nt] + __shfl_xor(l_run[nt], 32);
+    const float l_tot = pair_sum(l_run[nt]);
     if (!qvalid[nt]) continue;
     const float inv = 1.f / l_tot;
     const int64_t qrow = wr0 + 32 * nt + n;
