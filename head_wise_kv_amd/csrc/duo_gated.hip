@@ -434,9 +434,12 @@ __global__ __launch_bounds__(256) void gated_f32_kernel(GatedArgs a, int g) {
 
 }  // namespace
 
+// Query heads per work item: the largest of 4, 2, 1 that divides g (each
+// K / V tile then serves that many heads' rows).
 int gated_heads_per_item(int dtype, int g) {
   if (dtype != 1) return 1;
-  return (g % kPfRowWaves == 0) ? kPfRowWaves : 1;
+  static_assert(kPfRowWaves == 4, "head packing assumes four row wavefronts");
+  return (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;
 }
 
 int gated_rows_per_item(int dtype, int g) {
