@@ -122,8 +122,11 @@ struct PfItem {
   bool ret;
 };
 
-// Work items: retrieval items first (longest rows first), then streaming.
-// Within a kind: (b, kv head, head group, query tile), query tile fastest.
+// Work items: retrieval items first, then streaming.  Within a kind the
+// index runs (b, head group, query tile, KV head) with the KV head fastest:
+// workgroups are dealt to the XCDs in turn, so the items of one KV head land
+// on the same XCDs and share its K and V in their L2; query tiles with the
+// most keys come first.
 __device__ __forceinline__ PfItem pf_item(const PrefillArgs& a, int g, int hpi) {
   PfItem w;
   int rem = blockIdx.x;
@@ -137,12 +140,12 @@ __device__ __forceinline__ PfItem pf_item(const PrefillArgs& a, int g, int hpi) 
     n_kind = a.n_str;
   }
   const int ngrp = g / hpi;
+  w.cidx = rem % n_kind;
+  rem /= n_kind;
   const int qt_rev = rem % a.q_tiles;
   rem /= a.q_tiles;
   const int hg = rem % ngrp;
-  rem /= ngrp;
-  w.cidx = rem % n_kind;
-  w.b = rem / n_kind;
+  w.b = rem / ngrp;
   w.qt = a.q_tiles - 1 - qt_rev;
   w.kvh = w.ret ? a.map.orig_ret[w.cidx] : a.map.orig_str[w.cidx];
   w.h_first = w.kvh * g + hg * hpi;
