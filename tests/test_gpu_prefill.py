@@ -40,7 +40,9 @@ def _oracle_prefill(Q, K, V, mask, S, W, dtype, rows=None):
 CASES = []
 for dtype in ("bf16", "f32"):
     for d in (64, 128):
-        for g in (1, 4):
+        # bf16 takes every group size the MFMA path packs differently: one head
+        # per work item (g = 1), two (g = 2), four (g = 4), two head groups (g = 8)
+        for g in ((1, 2, 4, 8) if dtype == "bf16" else (1, 4)):
             CASES.append((dtype, d, g))
 
 
