@@ -5,7 +5,7 @@ checks shapes, dtypes and devices of torch tensors, hands their device
 pointers and the current HIP stream to the C ABI, and turns error codes into
 exceptions.  There is no fallback: if libduo.so is missing this import fails.
 
-Build the library first with ``python -m head_wise_kv_amd.build`` (or
+Build the library first with ``python head_wise_kv_amd/build.py`` (or
 ``__graft_entry__.build()``).
 """
 from __future__ import annotations
@@ -53,7 +53,7 @@ class duo_gated_shape(ctypes.Structure):
 
 def _load():
     if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"libduo.so is not built ({_LIB_PATH}); run `python -m head_wise_kv_amd.build`")
+        raise ImportError(f"libduo.so is not built ({_LIB_PATH}); run `python head_wise_kv_amd/build.py`")
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
     cfgp = ctypes.POINTER(duo_config)
