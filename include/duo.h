@@ -74,8 +74,8 @@ typedef enum { DUO_KV_NATIVE = 0, DUO_KV_FP8 = 1 } duo_kv_format;
  * Retrieval rows are stored one of two ways.  page_rows = 0: contiguous, T_cap
  * rows per retrieval head and batch row.  page_rows > 0 (a power of two, at
  * least 256): paged ("Attention Variants and Memory Efficiency", "What the
- * Inference Runtime Can Change": a request's cache in fixed-size blocks that
- * need not be contiguous, shareable between requests; "A Closer Look at
+ * Inference Runtime Can Change": the runtime may cut a request's rows into
+ * equal blocks placed anywhere and shared between requests; "A Closer Look at
  * Attention Memory": a ragged batch then holds only what each request needs).
  * Each layer has a pool of n_pages pages; a page holds page_rows consecutive
  * positions of every retrieval head of one batch row, and a row takes a page

@@ -1,13 +1,13 @@
 """Paged retrieval rows and prefix sharing (oracle; test infrastructure only).
 
 What is modelled.  "Attention Variants and Memory Efficiency", "What the
-Inference Runtime Can Change": paged attention keeps a request's cache in
-fixed-size blocks that need not be contiguous in memory; it changes how the
-cache is allocated and shared, not the logical cache or the number of cached
-values; prefix sharing keeps one copy of the blocks that hold a matching
-prefix.  Its section "A Closer Look at Attention Memory": padding every
-request of a batch to one length allocates cache for the padding, where a
-ragged implementation allocates only what each request needs.
+Inference Runtime Can Change", lists paging among the runtime's storage
+choices: a request's rows are cut into equal blocks that may sit anywhere in
+memory, which makes allocation and sharing easier while the set of cached
+values stays what the attention rule needs; prefix sharing stores the blocks
+of a common prefix once.  Its section "A Closer Look at Attention Memory"
+contrasts padding every request to the longest one with a ragged layout that
+sizes each request's cache to its own length.
 
 Readings taken where the pages leave a step open:
   * a page holds P consecutive positions of one request (batch row), for

@@ -27,7 +27,10 @@ attention rule.  The pages fix no format; the readings taken here:
 Pinned by ``tests/oracle_checks.py``: the encoder against torch's
 float8_e4m3fn cast on a dense sweep of float32 values (every tie and the
 subnormal range included), the decoder against the same library on all 256
-codes, and the row quantizer against the format's error bound.
+codes, the row quantizer against the format's error bound, and the chunked
+prefill and decode routes, off the E4M3 grid and over several chunks, against
+an enumeration over positions whose held rows are built with the library's
+E4M3 conversion (a held row read as given fails that pin).
 """
 from __future__ import annotations
 

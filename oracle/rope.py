@@ -31,8 +31,10 @@ Readings taken where the pages leave a step open:
 Pinned by tests/oracle_checks.py: unit vectors at position 1 for d = 8,
 theta = 10^4 (frequencies 1, 0.1, 0.01, 0.001 exactly), the complex-number
 form of the rotation, the relative-position property of scores, the bf16
-rounding against torch's conversion, and decode over the cache's slots
-against the definition route over logical positions.
+rounding against torch's conversion, decode over the cache's slots
+against the definition route over logical positions, and chunked prefill over
+FP8 rows against an enumeration built from the complex-number rotation,
+torch's bf16 rounding and torch's E4M3 conversion.
 """
 from __future__ import annotations
 

@@ -60,39 +60,44 @@ def check_mixed_payload_closed_forms():
 # ------------------------------------------------------------------ cache placement
 
 def check_ring_example():
+    # The printed circular-buffer example: window 3, positions 0..4 with values
+    # 10 p, held oldest first as [(2, 20), (3, 30), (4, 40)].  A streaming head
+    # with no sinks is exactly that window.
     lines = _golden_lines("ring_window3.txt")
     kv = {ln[0]: ln[1:] for ln in lines}
     W = int(kv["window_size"][0])
-    ring = Cc.RingWindow(W)
-    for p in map(int, kv["appended"]):
-        ring.append(p, 10 * p)
-    want = [tuple(int(x) for x in s.strip("()").split(",")) for s in kv["ordered"]]
-    assert ring.ordered() == want, ring.ordered()
-    # The same example through a streaming head with no sinks: same slots.
     h = Cc.StreamingHeadCache(0, W)
     slots = [h.append(p, 10 * p) for p in map(int, kv["appended"])]
+    want = [tuple(int(x) for x in s.strip("()").split(",")) for s in kv["ordered"]]
+    assert h.ordered() == want, h.ordered()
+    # arrival count modulo the window: slots 0, 1, 2, 0, 1
     assert slots == [0, 1, 2, 0, 1]
-    assert {s: e for s, e in h.slots().items()} == {0: (3, 30), 1: (4, 40), 2: (2, 20)}
+    assert h.slots() == {0: (3, 30), 1: (4, 40), 2: (2, 20)}
 
 
 def check_streaming_composition():
     # A streaming head = the guide's append rule (sinks fill first, later tokens go
-    # to the window) composed with the ring of "Sliding-Window and Mixed Attention"
-    # fed only the tokens that arrive after the sinks are full.
-    for S, W, T in [(2, 3, 11), (4, 5, 23), (1, 4, 9), (3, 3, 3), (5, 2, 4)]:
+    # to the window) composed with the window of "Sliding-Window and Mixed
+    # Attention" (an S = 0 head, pinned by the printed example above) fed only the
+    # tokens that arrive after the sinks are full.
+    for S, W, T in [(2, 3, 11), (4, 5, 23), (1, 4, 9), (3, 3, 3), (5, 2, 4), (3, 4, 30)]:
         h = Cc.StreamingHeadCache(S, W)
-        ring = Cc.RingWindow(W)
+        window = Cc.StreamingHeadCache(0, W)
         for p in range(T):
             h.append(p, p)
             if p >= S:
-                ring.append(p, p)
+                window.append(p, p)
         slots = h.slots()
         for i in range(min(S, T)):
             assert slots[i] == (i, i)
-        for r, e in enumerate(ring.items):
-            if e is not None:
-                assert slots[S + r] == e, (S, W, T, r)
+        for r, e in window.slots().items():
+            assert slots[S + r] == e, (S, W, T, r)
         assert len(slots) == min(T, S + W)
+    # Hand-derived: S = 2, W = 3, positions 0..7.  Positions 0, 1 are sinks;
+    # 2, 3, 4 fill window slots 2, 3, 4; 5, 6, 7 then replace 2, 3, 4 in turn.
+    h = Cc.StreamingHeadCache(2, 3)
+    assert [h.append(p) for p in range(8)] == [0, 1, 2, 3, 4, 2, 3, 4]
+    assert {s: p for s, (p, _) in h.slots().items()} == {0: 0, 1: 1, 2: 5, 3: 6, 4: 7}
 
 
 def check_simulation_counts():
@@ -384,6 +389,100 @@ def check_fp8_attention_routes():
     assert np.allclose(QZ.decode_step_fp8(Q[:, -1], K2, V2, [1, 0], S, W, 0.3), dq, atol=1e-12, rtol=0)
 
 
+def _fp8_stored_by_library(X):
+    """What a row-scaled E4M3 cache holds for float32 rows X, built with
+    torch's float8_e4m3fn conversion: s = max|x| / 448 and x / s in float32,
+    the cast, then code value * s (a zero row stays zero)."""
+    X = np.asarray(X, dtype=np.float32)
+    s = (np.max(np.abs(X), axis=-1) / np.float32(448.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    y = np.ascontiguousarray((X / safe[..., None]).astype(np.float32))
+    v = torch.from_numpy(y).to(torch.float8_e4m3fn).double().numpy()
+    return np.where(s[..., None] > 0, v * s[..., None].astype(np.float64), 0.0)
+
+
+def _chunked_by_enumeration(Qrows, held_k, given_k, held_v, given_v, mask, S, W, scale, chunks):
+    """Chunk row t = P + i enumerates positions 0..t: a key or value at
+    j < P (cached before the chunk) is taken from held_*, one at j >= P
+    (the chunk's own) from given_*; softmax in pure Python."""
+    n_q, N, d = Qrows.shape
+    n_kv = given_k.shape[0]
+    out = np.empty((n_q, N, d))
+    P = 0
+    for C in chunks:
+        for h in range(n_q):
+            k = A.kv_head_of(h, n_q, n_kv)
+            for t in range(P, P + C):
+                keys = [(held_k[k][j] if j < P else given_k[k][j]).tolist() for j in range(t + 1)]
+                vals = [(held_v[k][j] if j < P else given_v[k][j]).tolist() for j in range(t + 1)]
+                out[h, t] = A.attend_row_bruteforce(Qrows[h, t].tolist(), keys, vals, t, bool(mask[k]), S, W, scale)
+        P += C
+    return out
+
+
+def check_fp8_prefill_held_rows():
+    # Off the E4M3 grid and over several chunks: a chunk row sees every key and
+    # value cached before its chunk as stored (code value x row scale) and the
+    # chunk's own as given.  Expected values by enumeration over positions with
+    # the library's E4M3 conversion; decode sees every held row as stored.
+    rng = np.random.default_rng(91)
+    n_q, n_kv, N, d, S, W = 4, 2, 23, 8, 2, 5
+    chunks = [5, 7, 4, 7]
+    K = rng.standard_normal((n_kv, N, d)).astype(np.float32)
+    V = rng.standard_normal((n_kv, N, d)).astype(np.float32)
+    Q = rng.standard_normal((n_q, N, d))
+    Ks, Vs = _fp8_stored_by_library(K), _fp8_stored_by_library(V)
+    K64, V64 = K.astype(np.float64), V.astype(np.float64)
+    for mask in ([1, 0], [0, 1]):
+        want = _chunked_by_enumeration(Q, Ks, K64, Vs, V64, mask, S, W, 0.35, chunks)
+        got = QZ.prefill_chunked_fp8(Q, K, V, mask, S, W, 0.35, chunks)
+        assert np.allclose(got, want, atol=1e-12, rtol=0), float(np.abs(got - want).max())
+        # not vacuous: reading the held rows as given moves the result
+        as_given = _chunked_by_enumeration(Q, K64, K64, V64, V64, mask, S, W, 0.35, chunks)
+        assert np.abs(as_given - want).max() > 1e-3
+        # decode at T = N: the query's own row was appended first, so it too is as stored
+        kv = [A.kv_head_of(h, n_q, n_kv) for h in range(n_q)]
+        dq = np.stack([A.attend_row_bruteforce(Q[h, N - 1].tolist(), Ks[kv[h]].tolist(), Vs[kv[h]].tolist(), N - 1,
+                                               bool(mask[kv[h]]), S, W, 0.35) for h in range(n_q)])
+        got_d = QZ.decode_step_fp8(Q[:, N - 1], K, V, mask, S, W, 0.35)
+        assert np.allclose(got_d, dq, atol=1e-12, rtol=0), float(np.abs(got_d - dq).max())
+
+
+def _rotate_by_complex(X, positions, theta):
+    """Pair (x_i, x_(i + d/2)) as x_i + j x_(i + d/2), times exp(j p theta^(-2i/d))."""
+    X = np.asarray(X, dtype=np.float64)
+    h = X.shape[-1] // 2
+    f = np.array([theta ** (-(2.0 * i) / X.shape[-1]) for i in range(h)])
+    z = (X[..., :h] + 1j * X[..., h:]) * np.exp(1j * np.asarray(positions, dtype=np.float64)[:, None] * f[None, :])
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def check_rope_fp8_prefill_held_rows():
+    # Rotary positions over FP8 rows, several chunks: a held key is the key
+    # rotated at its position, rounded to bf16 and then stored as FP8; a held
+    # value is stored as FP8; the chunk's own keys are rotated but not rounded,
+    # its values as given; the query is rotated at its own position.
+    rng = np.random.default_rng(92)
+    n_q, n_kv, N, d, S, W, theta = 4, 2, 21, 8, 2, 4, 1e4
+    chunks = [6, 1, 9, 5]
+    K = rng.standard_normal((n_kv, N, d)).astype(np.float32)
+    V = rng.standard_normal((n_kv, N, d)).astype(np.float32)
+    Q = rng.standard_normal((n_q, N, d))
+    pos = np.arange(N)
+    Kr = _rotate_by_complex(K, pos, theta)
+    Kb = torch.from_numpy(Kr.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(Kb.astype(np.float64), RP.round_bf16(Kr))  # one rounding, float64 -> bf16
+    Ks, Vs = _fp8_stored_by_library(Kb), _fp8_stored_by_library(V)
+    Qr = _rotate_by_complex(Q, pos, theta)
+    for mask in ([1, 0], [0, 1]):
+        want = _chunked_by_enumeration(Qr, Ks, Kr, Vs, V.astype(np.float64), mask, S, W, 0.35, chunks)
+        got = RP.prefill_chunked_rope(Q, K, V, mask, S, W, 0.35, theta, "bf16", chunks, kv_format="fp8")
+        assert np.allclose(got, want, atol=1e-9, rtol=0), float(np.abs(got - want).max())
+        as_given = _chunked_by_enumeration(Qr, Kr, Kr, V.astype(np.float64), V.astype(np.float64), mask, S, W,
+                                           0.35, chunks)
+        assert np.abs(as_given - want).max() > 1e-3
+
+
 # ------------------------------------------------------------------ paged rows
 
 def check_paging_closed_forms():
@@ -537,7 +636,8 @@ ALL_CHECKS = [
     check_softmax_invariants, check_chunk_invariance, check_gqa_expansion,
     check_gated_hand_case, check_gated_library_endpoints, check_gated_bruteforce_agrees,
     check_gated_gqa_expansion, check_e4m3_against_library, check_fp8_row_quantizer,
-    check_fp8_attention_routes, check_paging_closed_forms, check_paging_capacity,
+    check_fp8_attention_routes, check_fp8_prefill_held_rows, check_rope_fp8_prefill_held_rows,
+    check_paging_closed_forms, check_paging_capacity,
     check_rope_unit_vectors, check_rope_complex_form, check_rope_relative_positions,
     check_bf16_rounding_against_library, check_rope_cache_route_uses_logical_positions,
 ]

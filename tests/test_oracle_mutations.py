@@ -58,14 +58,8 @@ def _attend_sign(q, keys, values, key_pos, t, is_retrieval, S, W, scale):
 _orig_attend_row = A.attend_row
 
 
-def _ring_slot_by_position(self, position, payload=None):
-    if len(self.sinks) < self.S:
-        self.sinks.append((position, payload))
-        return len(self.sinks) - 1
-    slot = position % self.W                       # ring indexed by absolute position
-    self.ring.items[slot] = (position, payload)
-    self.ring.length += 1
-    return self.S + slot
+def _ring_slot_by_position(n, S, W):
+    return n if n < S else S + n % W               # window indexed by absolute position
 
 
 def _blend_swapped(full, stream, a):
@@ -142,6 +136,33 @@ def _decode_query_unrotated(q, K, V, mask, S, W, scale, theta, dtype, route="cac
                          np.asarray(V, dtype=np.float64), mask, S, W, scale, route=route)
 
 
+def _fp8_prefill_held_as_given(Q, K, V, mask, S, W, scale, chunk):
+    # held rows read unquantized: every key and value as given
+    Q = np.asarray(Q, dtype=np.float64)
+    K64, V64 = np.asarray(K, dtype=np.float64), np.asarray(V, dtype=np.float64)
+    n_q, N, d = Q.shape
+    n_kv = K.shape[0]
+    out = np.empty((n_q, N, d))
+    lengths = [chunk] * ((N + chunk - 1) // chunk) if np.isscalar(chunk) else list(chunk)
+    P = 0
+    for C in lengths:
+        C = int(min(C, N - P))
+        for h in range(n_q):
+            k = A.kv_head_of(h, n_q, n_kv)
+            kp = np.asarray(Cc.kept_positions(P, bool(mask[k]), S, W) + list(range(P, P + C)), dtype=np.int64)
+            out[h, P:P + C] = A.attend_rows(Q[h, P:P + C], np.arange(P, P + C), K64[k][kp], V64[k][kp], kp,
+                                            bool(mask[k]), S, W, scale)
+        P += C
+    return out
+
+
+_orig_prefill_rope = RP.prefill_chunked_rope
+
+
+def _rope_fp8_held_unquantized(Q, K, V, mask, S, W, scale, theta, dtype, chunks, kv_format=None):
+    return _orig_prefill_rope(Q, K, V, mask, S, W, scale, theta, dtype, chunks, kv_format=None)  # FP8 dropped
+
+
 MUTATIONS = {
     "window_too_wide": (A, "visible_matrix", _window_too_wide),
     "sinks_off_by_one": (A, "visible_matrix", _sinks_off_by_one),
@@ -150,7 +171,7 @@ MUTATIONS = {
     "gqa_mod_mapping": (A, "kv_head_of", _head_mod),
     "dropped_scale": (A, "attend_row", _attend_no_scale),
     "flipped_sign": (A, "attend_row", _attend_sign),
-    "ring_by_position": (Cc.StreamingHeadCache, "append", _ring_slot_by_position),
+    "ring_by_position": (Cc, "streaming_slot", _ring_slot_by_position),
     "kv_bytes_factor": (Z, "kv_cache_bytes", _kv_bytes_one_factor),
     "gate_swapped": (G, "blend", _blend_swapped),
     "gate_mod_mapping": (G, "gate_of_query_heads", _gate_by_query_mod),
@@ -164,6 +185,8 @@ MUTATIONS = {
     "rope_freq": (RP, "inv_freq", _rope_freq),
     "bf16_half_up": (RP, "round_bf16", _bf16_half_up),
     "rope_query_unrotated": (RP, "decode_step_rope", _decode_query_unrotated),
+    "fp8_held_as_given": (QZ, "prefill_chunked_fp8", _fp8_prefill_held_as_given),
+    "rope_fp8_held_unquantized": (RP, "prefill_chunked_rope", _rope_fp8_held_unquantized),
 }
 
 
