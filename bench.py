@@ -5,8 +5,10 @@ Default workload: one full-model decode step of a 70B-GQA-shaped model
 W=1024, 2 of 8 KV heads retrieval per layer): per layer, one new token per
 KV head is appended and the layer's queries decoded, in one duo_decode_append
 call (the same work as duo_append of the token followed by duo_decode).  The
-step is captured once in a HIP graph and replayed; every replay re-does the
-full work (the append writes, the decode reads every held K/V row).
+step is captured once in a HIP graph and replayed; each replay is the next
+generation step (the kernels read every row's token count when they run), so
+the timed steps hold T + warmup .. T + warmup + steps - 1 tokens and the
+bytes are taken at their mean.
 
 Prints one JSON line.  `value` is the step's algorithmic KV bytes (held K+V
 rows read once per KV head, plus the appended rows, queries and outputs)
@@ -37,6 +39,10 @@ METRIC = "mixed-head decode attention: KV GB/s (% HBM peak), µs/step at 128k ct
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
+# Cache copies a step rotates through: the batch-8 32k decode reads 294 MB, close
+# to the 256 MiB last-level (Infinity) cache, so four copies (1.2 GB) keep its
+# rows from being served from that cache between steps.
+MALL_COPIES = {"llama3_8b_decode_b8_32k": 4}
 # every source the decode kernels are compiled from: counters taken on an
 # older version of any of them no longer describe the kernel
 KERNEL_SRC = [os.path.join(ROOT, "head_wise_kv_amd", "csrc", f)
@@ -89,7 +95,33 @@ def decode_layer_bytes(w: WL.Workload, mask_row, T: int, append: bool) -> int:
     return kv + qo + app
 
 
-def bench_decode(w: WL.Workload, steps: int, warmup: int, layers: int):
+def _timed_replays(graph, steps: int, stream=None):
+    """Replay `graph` `steps` times with a HIP event between replays (on the
+    launch stream): (total seconds, list of per-replay seconds)."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    if stream is None:
+        evs[0].record()
+        for i in range(steps):
+            graph.replay()
+            evs[i + 1].record()
+    else:
+        evs[0].record(stream)
+        with torch.cuda.stream(stream):
+            for i in range(steps):
+                graph.replay()
+                evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) * 1e-3 for i in range(steps)]
+    return evs[0].elapsed_time(evs[steps]) * 1e-3, per
+
+
+def bench_decode(w: WL.Workload, steps: int, warmup: int, layers: int, copies: int = 1):
+    """One step = every layer's decode (or fused append + decode) of `copies`
+    separate caches in turn, captured in one HIP graph; per-step figures are
+    per cache copy (copies > 1 keeps a working set near the 256 MiB
+    last-level cache from being served by it)."""
     import torch
     import head_wise_kv_amd as H
 
@@ -100,18 +132,22 @@ def bench_decode(w: WL.Workload, steps: int, warmup: int, layers: int):
     append = w.mode == "decode_append"
     T = w.T
     fill = T - 1 if append else T
+    # every replay of a fused step appends one more token (the kernels read the
+    # rows' counts when they run), so the rows have room for all of them
+    T_cap = T + (warmup + steps if append else 0)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    pages = dict(page_rows=w.page_rows, n_pages=w.B * -(-T // w.page_rows)) if w.page_rows else {}
-    cache = H.DuoCache(L, w.B, w.n_q, w.n_kv, w.d, T, w.S, w.W, w.dtype, mask, device=dev, kv_format=w.kv_format,
-                       rope_theta=w.rope_theta, **pages)
-    log(f"{w.name}: arena {cache.arena_bytes / 1e9:.2f} GB, filling {L} layers x {fill} tokens")
+    pages = dict(page_rows=w.page_rows, n_pages=w.B * -(-T_cap // w.page_rows)) if w.page_rows else {}
+    caches = [H.DuoCache(L, w.B, w.n_q, w.n_kv, w.d, T_cap, w.S, w.W, w.dtype, mask, device=dev,
+                         kv_format=w.kv_format, rope_theta=w.rope_theta, **pages) for _ in range(copies)]
+    log(f"{w.name}: {copies} x arena {caches[0].arena_bytes / 1e9:.2f} GB, filling {L} layers x {fill} tokens")
     t0 = time.time()
     buf_k = torch.empty(w.B, w.n_kv, fill, w.d, dtype=dt, device=dev)
     buf_v = torch.empty_like(buf_k)
     for l in range(L):
         WL.device_fill_normal(buf_k, WL.device_seed(w, l, WL.TENSOR_K), w.S, w.sink_scale)
         WL.device_fill_normal(buf_v, WL.device_seed(w, l, WL.TENSOR_V))
-        cache.append(l, buf_k, buf_v)
+        for cache in caches:
+            cache.append(l, buf_k, buf_v)
     del buf_k, buf_v
     q = torch.empty(L, w.B, w.n_q, w.d, dtype=dt, device=dev)
     WL.device_fill_normal(q, WL.device_seed(w, 0, WL.TENSOR_Q))
@@ -131,28 +167,36 @@ def bench_decode(w: WL.Workload, steps: int, warmup: int, layers: int):
     graph = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
     with torch.cuda.graph(graph, stream=stream):
-        for l in range(L):
-            if append:
-                cache.decode_append(l, kn_l[l], vn_l[l], q_l[l], out=o_l[l], scale=w.scale)
-            else:
-                cache.decode(l, q_l[l], out=o_l[l], scale=w.scale)
+        for cache in caches:
+            for l in range(L):
+                if append:
+                    cache.decode_append(l, kn_l[l], vn_l[l], q_l[l], out=o_l[l], scale=w.scale)
+                else:
+                    cache.decode(l, q_l[l], out=o_l[l], scale=w.scale)
     torch.cuda.synchronize()
-    T_step = T  # tokens held at the measured step (the graph re-appends position T-1)
+    if append:
+        for cache in caches:
+            for l in range(L):
+                cache.reserve(l, warmup + steps - 1)  # pages for the replays (the capture counted one step)
+    # tokens held after the appends of the timed steps: T + warmup .. T + warmup
+    # + steps - 1 (replay i of the graph stores position T - 1 + i); bytes at the mean
+    T_step = T + warmup + (steps - 1) / 2.0 if append else T
     step_bytes = sum(decode_layer_bytes(w, mask[l], T_step, append) for l in range(L))
 
     for _ in range(warmup):
         graph.replay()
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(steps):
-        graph.replay()
-    ev1.record()
-    torch.cuda.synchronize()
+    total, per = _timed_replays(graph, steps)
     wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / steps
-    log(f"graph: {ms_step * 1e3:.1f} us/step (wall {wall / steps * 1e6:.1f} us/step)")
+    ms_step = total * 1e3 / (steps * copies)
+    per_step = np.asarray(per) / copies
+    for cache in caches:
+        cache.sync()  # host counts from the device (raises if a step found no room)
+    if append:
+        assert caches[0].seq_len(0) == T - 1 + warmup + steps, caches[0].seq_len(0)
+    log(f"graph: {ms_step * 1e3:.1f} us/step mean, {np.median(per_step) * 1e6:.1f} median, "
+        f"{per_step.min() * 1e6:.1f} min (wall {wall / steps * 1e6:.1f} us/replay)")
 
     # Decode alone: the L duo_decode calls of one step (split kernel + combine
     # kernel each, over the T held rows) captured in a second graph, replayed
@@ -160,23 +204,19 @@ def bench_decode(w: WL.Workload, steps: int, warmup: int, layers: int):
     # the average covers both kernels of a call plus the graph's dispatch gaps.
     dgraph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(dgraph, stream=stream):
-        for l in range(L):
-            cache.decode(l, q_l[l], out=o_l[l], scale=w.scale)
+        for cache in caches:
+            for l in range(L):
+                cache.decode(l, q_l[l], out=o_l[l], scale=w.scale)
     torch.cuda.synchronize()
     reps = max(3, min(steps, 10))
     dgraph.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    with torch.cuda.stream(stream):
-        for _ in range(reps):
-            dgraph.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    avg_s = e0.elapsed_time(e1) * 1e-3 / (reps * L)
-    avg_bytes = float(np.mean([decode_layer_bytes(w, mask[l], T_step, False) for l in range(L)]))
-    return dict(ms_step=ms_step, step_bytes=step_bytes, decode_avg_s=avg_s, decode_avg_bytes=avg_bytes,
-                mask=mask, T=T_step, layers=L, graph_wall_us=wall / steps * 1e6)
+    dtotal, _ = _timed_replays(dgraph, reps, stream)
+    avg_s = dtotal / (reps * L * copies)
+    T_dec = caches[0].seq_len(0)  # plain decodes do not append: every replay reads these rows
+    avg_bytes = float(np.mean([decode_layer_bytes(w, mask[l], T_dec, False) for l in range(L)]))
+    return dict(ms_step=ms_step, median_s=float(np.median(per_step)), min_s=float(per_step.min()),
+                step_bytes=step_bytes, decode_avg_s=avg_s, decode_avg_bytes=avg_bytes,
+                mask=mask, T=T_step, T_decode=T_dec, layers=L, graph_wall_us=wall / steps * 1e6, copies=copies)
 
 
 # ------------------------------------------------------------------ prefill (secondary)
@@ -270,16 +310,23 @@ def bench_gated(w: WL.Workload, reps: int = 3):
 
 # ------------------------------------------------------------------ CPU oracle baseline
 
-def cpu_baseline(w: WL.Workload, budget_s: float = 15.0):
-    """The oracle's decode on host cores over as many whole layers of the
-    workload as fit in about `budget_s` seconds (inputs generated on the host
-    by the seeded recipe; generation is not timed)."""
-    from oracle import attention as OA
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
     except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(w: WL.Workload, budget_s: float = 15.0, prefill_rows: int = 256):
+    """The oracle on host cores, on bounded samples (inputs generated on the
+    host by the seeded recipe; generation is not timed):
+      * decode: as many whole layers of workload `w` as fit in about
+        `budget_s` seconds;
+      * prefill: the first `prefill_rows` rows of the last 4,096-token chunk
+        of the 64k chunked prefill, every query head, against the 61,440
+        cached positions plus the chunk."""
+    from oracle import attention as OA
     append = w.mode == "decode_append"
     spent, nbytes, layers = 0.0, 0, 0
     for l in range(w.L):
@@ -296,8 +343,31 @@ def cpu_baseline(w: WL.Workload, budget_s: float = 15.0):
         del K, V
         if spent >= budget_s:
             break
-    return dict(value=nbytes / spent / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
-                sample=f"{layers} of {w.L} layers of {w.name}, fp64 numpy oracle, {spent:.1f} s")
+    pw = WL.WORKLOADS["llama3_8b_prefill_64k"]
+    pmask = WL.retrieval_mask(pw, 0)
+    N, C = pw.T, pw.chunk
+    p0 = N - C
+    rows = p0 + np.arange(prefill_rows)
+    Qp = WL.round_to_dtype(WL.stacked_rows_f32(pw, 0, WL.TENSOR_Q, pw.n_q, p0, p0 + prefill_rows)[0], pw.dtype)
+    hi = int(rows.max()) + 1
+    Kp = WL.round_to_dtype(WL.stacked_rows_f32(pw, 0, WL.TENSOR_K, pw.n_kv, 0, hi)[0], pw.dtype)
+    Vp = WL.round_to_dtype(WL.stacked_rows_f32(pw, 0, WL.TENSOR_V, pw.n_kv, 0, hi)[0], pw.dtype)
+    Qfull = np.zeros((pw.n_q, hi, pw.d))
+    Qfull[:, rows] = Qp
+    t0 = time.perf_counter()
+    OA.prefill_full(Qfull, Kp, Vp, pmask, pw.S, pw.W, pw.scale, rows=rows)
+    pspent = time.perf_counter() - t0
+    t = rows.astype(np.float64)
+    lam = np.minimum(t + 1, np.minimum(pw.S, t + 1) + np.minimum(pw.W, np.maximum(t + 1 - pw.S, 0)))
+    n_ret = int(np.sum(pmask))
+    pflops = 4.0 * pw.d * pw.g * (n_ret * float(np.sum(t + 1)) + (pw.n_kv - n_ret) * float(np.sum(lam)))
+    return dict(value=nbytes / spent / 1e9, unit="GB/s", cores=_blas_threads(), cpu_count=os.cpu_count(),
+                kind="oracle",
+                sample=f"{layers} of {w.L} layers of {w.name}, fp64 numpy oracle, {spent:.1f} s",
+                prefill={"value": pflops / pspent / 1e12, "unit": "TFLOP/s",
+                         "sample": f"rows {p0}..{p0 + prefill_rows - 1} (first {prefill_rows} of chunk "
+                                   f"{N // C - 1}) of {pw.name}, all {pw.n_q} query heads, {pspent:.1f} s",
+                         "algorithmic_tflop": pflops / 1e12})
 
 
 # ------------------------------------------------------------------ main
@@ -310,7 +380,8 @@ def main():
     ap.add_argument("--workload", default="gqa70b_decode_128k",
                     choices=[n for n, w in WL.WORKLOADS.items() if w.mode in ("decode", "decode_append")])
     ap.add_argument("--layers", type=int, default=0, help="limit layers (profiling only; 0 = all)")
-    ap.add_argument("--also", default="mha7b_decode_128k,gqa70b_decode_128k_fp8,mha7b_decode_128k_fp8,"
+    ap.add_argument("--also", default="tiny_decode,llama3_8b_decode_b8_32k,"
+                                      "mha7b_decode_128k,gqa70b_decode_128k_fp8,mha7b_decode_128k_fp8,"
                                       "gqa70b_decode_128k_paged,gqa70b_decode_128k_rope,"
                                       "gqa70b_decode_128k_full,mha7b_decode_128k_full",
                     help="comma-separated extra decode workloads reported under 'also' ('' for none)")
@@ -349,6 +420,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(r["ms_step"], 4),
         "us_per_step": round(r["ms_step"] * 1e3, 1),
+        "us_per_step_median": round(r["median_s"] * 1e6, 1),
+        "us_per_step_min": round(r["min_s"] * 1e6, 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -356,7 +429,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) on device; mask seeded per layer)",
         "config": {"workload": w.name, "layers": L, "batch": w.B, "n_q": w.n_q, "n_kv": w.n_kv, "d_head": w.d,
-                   "context": r["T"], "sink": w.S, "recent": w.W, "retrieval_kv_heads_per_layer": w.n_ret,
+                   "context": w.T, "context_mean_timed": r["T"], "sink": w.S, "recent": w.W, "retrieval_kv_heads_per_layer": w.n_ret,
                    "step": ("append 1 token + decode, every layer (duo_decode_append)" if w.mode == "decode_append"
                             else "decode, every layer"),
                    "parallelism": "single GPU"},
@@ -371,11 +444,14 @@ def main():
         gc.collect()
         torch.cuda.empty_cache()
         wa = WL.WORKLOADS[name]
-        ra = bench_decode(wa, args.steps, args.warmup, wa.L)
+        copies = MALL_COPIES.get(name, 1)
+        ra = bench_decode(wa, max(args.steps, 20), args.warmup, wa.L, copies=copies)
         va = ra["step_bytes"] / (ra["ms_step"] * 1e-3) / 1e9
         also.append({"workload": name, "kv_rows": wa.kv_format or wa.dtype, "page_rows": wa.page_rows,
-                     "rope_theta": wa.rope_theta,
-                     "value": round(va, 2), "unit": "GB/s", "us_per_step": round(ra["ms_step"] * 1e3, 1),
+                     "rope_theta": wa.rope_theta, "cache_copies": copies,
+                     "value": round(va, 2), "unit": "GB/s", "us_per_step": round(ra["ms_step"] * 1e3, 2),
+                     "us_per_step_median": round(ra["median_s"] * 1e6, 2),
+                     "us_per_step_min": round(ra["min_s"] * 1e6, 2),
                      "hbm_frac": round(va / HBM_PEAK_GBS, 4),
                      "decode_kernel_gbs": round(ra["decode_avg_bytes"] / ra["decode_avg_s"] / 1e9, 2),
                      "decode_kernel_us": round(ra["decode_avg_s"] * 1e6, 2)})

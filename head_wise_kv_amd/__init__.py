@@ -29,7 +29,8 @@ EXPORTS = ("duo_cache_bytes", "duo_cache_payload_bytes", "duo_cache_init", "duo_
            "duo_decode_append", "duo_prefill_chunk", "duo_cache_seq_len", "duo_cache_head_view", "duo_cache_free",
            "duo_last_error", "duo_gated_attention", "duo_cache_head_scales", "duo_append_row", "duo_prefill_chunk_row",
            "duo_cache_row_len", "duo_cache_reset_row", "duo_cache_fork_row", "duo_cache_free_pages",
-           "duo_cache_row_pages", "duo_prefill_workspace_bytes")
+           "duo_cache_row_pages", "duo_prefill_workspace_bytes",
+           "duo_cache_sync", "duo_cache_reserve")
 
 
 class DuoError(RuntimeError):
@@ -78,6 +79,8 @@ def _load():
     lib.duo_cache_free_pages.argtypes = [vp, i32, ctypes.POINTER(i64)]
     lib.duo_cache_row_pages.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_int32), i64, ctypes.POINTER(i64)]
     lib.duo_prefill_workspace_bytes.argtypes = [vp, i32, i64, ctypes.POINTER(sz)]
+    lib.duo_cache_sync.argtypes = [vp, vp]
+    lib.duo_cache_reserve.argtypes = [vp, i32, i64, vp]
     lib.duo_cache_free.argtypes = [vp]
     lib.duo_cache_free.restype = None
     lib.duo_last_error.argtypes = []
@@ -261,6 +264,17 @@ class DuoCache:
                                      ctypes.c_void_p(self.workspace.data_ptr()), self.workspace.numel(),
                                      _stream_handle(stream)))
         return out
+
+    def sync(self, stream=None) -> None:
+        """Host-side token counts from the device-side ones (after replays of
+        captured steps); raises DuoError(DUO_ECAPACITY) if a replayed step
+        found no room for its tokens."""
+        _check(lib.duo_cache_sync(self._h, _stream_handle(stream)))
+
+    def reserve(self, layer: int, n_tokens: int, stream=None) -> None:
+        """Room for n_tokens more tokens in every row of `layer` (pages of a
+        paged layer), for replays of captured steps."""
+        _check(lib.duo_cache_reserve(self._h, layer, int(n_tokens), _stream_handle(stream)))
 
     def seq_len(self, layer: int) -> int:
         """Token count of the layer's rows (they must hold equal counts)."""

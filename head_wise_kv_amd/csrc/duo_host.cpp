@@ -56,6 +56,7 @@ struct LayerPlan {
 };
 
 struct Plan {
+  size_t off_status = 0, off_len = 0;  // int32 status word, int32 token counts [L][B]
   std::vector<LayerPlan> layers;
   size_t arena = 0, workspace = 0, payload = 0;
   size_t ws_records = 0;  // decode partial records at the start of the workspace
@@ -112,7 +113,10 @@ void make_plan(const duo_config* c, Plan* p) {
   size_t dequant = 0;
   const int64_t cap_str = (int64_t)c->sink + c->recent;
   p->layers.assign(c->L, LayerPlan{});
-  size_t off = 0;
+  // header: the status word, then every layer's per-row token counts
+  p->off_status = 0;
+  p->off_len = sizeof(int32_t);
+  size_t off = align_up(p->off_len + (size_t)c->L * c->B * sizeof(int32_t));
   p->payload = 0;
   for (int l = 0; l < c->L; ++l) {
     LayerPlan& lp = p->layers[l];
@@ -186,6 +190,10 @@ struct duo_cache {
     std::vector<int32_t> free_list;
   };
   std::vector<Pages> pages;
+  // Device words a host-only call (duo_cache_reset_row) left to write: per
+  // layer, rows whose count becomes 0 and page-table entries that become -1.
+  // Written ahead of the next call on the layer that takes a stream.
+  std::vector<std::vector<int32_t>> pend_len, pend_tab;
 
   duo::LayerPtrs ptrs(int l) const {
     const LayerPlan& lp = plan.layers[l];
@@ -203,6 +211,9 @@ struct duo_cache {
     p.table = paged(l) ? reinterpret_cast<int32_t*>(arena + lp.off_tab) : nullptr;
     p.max_pages = paged(l) ? (int32_t)max_pages() : 0;
     p.page_shift = paged(l) ? page_shift() : 0;
+    p.len = reinterpret_cast<int32_t*>(arena + plan.off_len) + (size_t)l * cfg.B;
+    p.status = reinterpret_cast<int32_t*>(arena + plan.off_status);
+    p.cap = cfg.T_cap;
     return p;
   }
   // a layer stores paged retrieval rows (a layer with no retrieval head needs no pages)
@@ -250,6 +261,7 @@ struct duo_cache {
       p.vsc_str += str_rows;
     }
     if (p.table) p.table += (size_t)b * p.max_pages;
+    p.len += b;
     return p;
   }
   duo::Rope rope() const {
@@ -274,6 +286,37 @@ namespace {
 int check_layer(const duo_cache* c, int layer) {
   if (!c) return fail(DUO_EINVAL, "cache handle is NULL");
   if (layer < 0 || layer >= c->cfg.L) return fail(DUO_EINVAL, "layer %d out of range [0, %d)", layer, c->cfg.L);
+  return DUO_OK;
+}
+
+// Write the device words a host-only call left for `layer` (counts of reset
+// rows, their released page-table entries), ahead of the call's own work.
+int flush_pending(duo_cache* c, int layer, hipStream_t s) {
+  if (c->pend_len.empty()) return DUO_OK;
+  std::vector<int32_t>& pl = c->pend_len[layer];
+  std::vector<int32_t>& pt = c->pend_tab[layer];
+  const duo::LayerPtrs p = c->ptrs(layer);
+  auto write = [&](int32_t* base, const std::vector<int32_t>& idx, int32_t value) -> hipError_t {
+    duo::TableUpdateArgs u{};
+    u.table = base;
+    for (size_t i = 0; i < idx.size(); i += duo::kMaxTableUpdates) {
+      u.n = (int)std::min<size_t>(duo::kMaxTableUpdates, idx.size() - i);
+      for (int j = 0; j < u.n; ++j) {
+        u.index[j] = idx[i + j];
+        u.page[j] = value;
+      }
+      if (hipError_t e = duo::launch_table_update(u, s)) return e;
+    }
+    return hipSuccess;
+  };
+  if (!pt.empty()) {
+    if (hipError_t e = write(p.table, pt, -1)) return hip_fail(e, "page table update launch");
+    pt.clear();
+  }
+  if (!pl.empty()) {
+    if (hipError_t e = write(p.len, pl, 0)) return hip_fail(e, "token count update launch");
+    pl.clear();
+  }
   return DUO_OK;
 }
 
@@ -333,10 +376,15 @@ int reserve_pages(duo_cache* c, int layer, int row, int64_t n_new, hipStream_t s
 // Enqueue the append of n_new tokens to every batch row at its own token
 // count, or (row >= 0) to that one row only, the inputs then being
 // [1][n_kv][n_new][d] (no validation).
+// With device_p0 each row's first position is its device count when the
+// kernel runs, and an advance kernel follows (duo_append, duo_append_row);
+// otherwise the positions start at the host count and the kernel sets the
+// device counts to the host's new ones (a prefill commit).
 hipError_t enqueue_append(duo_cache* c, int layer, const void* k, const void* v, int64_t n_new, hipStream_t s,
-                          int row = -1, bool rotate = true) {
+                          int row = -1, bool rotate = true, bool device_p0 = false) {
   const LayerPlan& lp = c->plan.layers[layer];
   duo::AppendArgs a{};
+  a.p0_from_device = device_p0 ? 1 : 0;
   a.k = static_cast<const char*>(k);
   a.v = static_cast<const char*>(v);
   a.lp = row < 0 ? c->ptrs(layer) : c->row_ptrs(layer, row);
@@ -356,7 +404,13 @@ hipError_t enqueue_append(duo_cache* c, int layer, const void* k, const void* v,
   a.dtype = c->cfg.dtype;
   a.d = c->cfg.d_head;
   if (rotate) a.rope = c->rope();  // else the keys come rotated already
-  return duo::launch_append(a, c->cfg.dtype, c->cfg.d_head, c->fp8(), s);
+  hipError_t e = duo::launch_append(a, c->cfg.dtype, c->cfg.d_head, c->fp8(), s);
+  if (e != hipSuccess || !device_p0) return e;
+  duo::AdvanceArgs adv{};
+  adv.lp = a.lp;
+  adv.B = a.B;
+  adv.n = n_new;
+  return duo::launch_advance(adv, s);
 }
 
 }  // namespace
@@ -399,6 +453,8 @@ int duo_cache_init(const duo_config* cfg, void* arena, size_t arena_bytes, void*
   c->arena = static_cast<char*>(arena);
   c->arena_bytes = arena_bytes;
   c->row_len.assign((size_t)cfg->L * cfg->B, 0);
+  c->pend_len.assign(cfg->L, {});
+  c->pend_tab.assign(cfg->L, {});
   if (cfg->page_rows) {
     c->pages.resize(cfg->L);
     for (int l = 0; l < cfg->L; ++l) {
@@ -415,15 +471,21 @@ int duo_cache_init(const duo_config* cfg, void* arena, size_t arena_bytes, void*
         hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
       c->num_cu = n;
   }
+  hipError_t s_err = hipSuccess;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  for (int l = 0; l < cfg->L; ++l) {
+  // the status word and every token count start at zero
+  s_err = duo::launch_fill_zero(c->arena, p.off_len + (size_t)cfg->L * cfg->B * sizeof(int32_t), s);
+  for (int l = 0; l < cfg->L && s_err == hipSuccess; ++l) {
     const LayerPlan& lp = p.layers[l];
     // positions start at zero (payload rows need no clearing)
-    hipError_t e = duo::launch_fill_zero(c->arena + lp.off_pos, (size_t)cfg->B * lp.n_str * c->cap_str() * sizeof(int32_t), s);
-    if (e != hipSuccess) {
-      delete c;
-      return hip_fail(e, "zeroing positions");
-    }
+    s_err = duo::launch_fill_zero(c->arena + lp.off_pos, (size_t)cfg->B * lp.n_str * c->cap_str() * sizeof(int32_t), s);
+    // page-table entries start at -1: no page
+    if (s_err == hipSuccess && c->paged(l))
+      s_err = duo::launch_fill_ones(c->arena + lp.off_tab, (size_t)cfg->B * c->max_pages() * sizeof(int32_t), s);
+  }
+  if (s_err != hipSuccess) {
+    delete c;
+    return hip_fail(s_err, "initialising the arena");
   }
   *out = c;
   return ok();
@@ -438,8 +500,9 @@ int duo_append(duo_cache* c, int layer, const void* k, const void* v, int64_t n_
   if (pmax + n_new > c->cfg.T_cap)
     return fail(DUO_ECAPACITY, "layer %d has a row of %lld tokens; %lld more exceed T_cap %lld", layer,
                 (long long)pmax, (long long)n_new, (long long)c->cfg.T_cap);
+  if (int r = flush_pending(c, layer, static_cast<hipStream_t>(stream))) return r;
   if (int r = reserve_pages(c, layer, -1, n_new, static_cast<hipStream_t>(stream))) return r;
-  hipError_t e = enqueue_append(c, layer, k, v, n_new, static_cast<hipStream_t>(stream));
+  hipError_t e = enqueue_append(c, layer, k, v, n_new, static_cast<hipStream_t>(stream), -1, true, true);
   if (e != hipSuccess) return hip_fail(e, "append launch");
   for (int b = 0; b < c->cfg.B; ++b) c->len(layer, b) += n_new;
   return ok();
@@ -455,8 +518,9 @@ int duo_append_row(duo_cache* c, int layer, int row, const void* k, const void* 
   if (p0 + n_new > c->cfg.T_cap)
     return fail(DUO_ECAPACITY, "row %d of layer %d holds %lld tokens; %lld more exceed T_cap %lld", row, layer,
                 (long long)p0, (long long)n_new, (long long)c->cfg.T_cap);
+  if (int r = flush_pending(c, layer, static_cast<hipStream_t>(stream))) return r;
   if (int r = reserve_pages(c, layer, row, n_new, static_cast<hipStream_t>(stream))) return r;
-  hipError_t e = enqueue_append(c, layer, k, v, n_new, static_cast<hipStream_t>(stream), row);
+  hipError_t e = enqueue_append(c, layer, k, v, n_new, static_cast<hipStream_t>(stream), row, true, true);
   if (e != hipSuccess) return hip_fail(e, "append launch");
   c->len(layer, row) = p0 + n_new;
   return ok();
@@ -475,14 +539,16 @@ int check_decode_args(const duo_cache* c, const void* q, void* out, float scale,
   return DUO_OK;
 }
 
-// Enqueue the decode kernels over the rows each batch row holds (its token
+// Plan the decode kernels over the rows each batch row holds (its token
 // count); with new_k / new_v set, every row's next token (at its token count)
-// is appended and attended by the same launch.
-hipError_t enqueue_decode(duo_cache* c, int layer, const void* q, void* out, float scale, void* ws,
-                          const void* new_k, const void* new_v, hipStream_t stream) {
+// is appended and attended by the same launch.  Fills *a (all but the
+// workspace pointer) and returns the number of work items.  Host only.
+int plan_decode(const duo_cache* c, int layer, const void* q, void* out, float scale, const void* new_k,
+                const void* new_v, duo::DecodeArgs* ap) {
   const LayerPlan& lp = c->plan.layers[layer];
   const duo_config& cf = c->cfg;
-  duo::DecodeArgs a{};
+  duo::DecodeArgs& a = *ap;
+  a = duo::DecodeArgs{};
   a.q = q;
   a.out = out;
   a.lp = c->ptrs(layer);
@@ -494,15 +560,13 @@ hipError_t enqueue_decode(duo_cache* c, int layer, const void* q, void* out, flo
   a.n_str = lp.n_str;
   a.cap_ret = cf.T_cap;
   a.cap_str = c->cap_str();
-  const int64_t S = cf.sink, W = cf.recent;
+  a.S = cf.sink;
+  a.W = cf.recent;
   for (int b = 0; b < cf.B; ++b) {
     duo::DecodeRow& R = a.rows[b];
     const int64_t held = c->len(layer, b);
     R.rows_ret = (int32_t)held;
     R.rows_str = (int32_t)std::min<int64_t>(held, c->cap_str());
-    R.new_pos = (int32_t)held;
-    R.new_slot_str = (int32_t)(held < S ? held : S + (held - S) % W);
-    R.excl_str = (new_k && held >= S + W) ? R.new_slot_str : -1;  // the ring is full: the new token evicts
   }
   if (new_k) {
     a.new_k = static_cast<const char*>(new_k);
@@ -562,10 +626,26 @@ hipError_t enqueue_decode(duo_cache* c, int layer, const void* q, void* out, flo
     next += lp.n_str * R.nb_str;
     if (lp.n_str > 0 && R.nb_str > 1) a.multi = 1;
   }
-  const int blocks = (int)next;
-  a.ws1 = static_cast<float*>(ws);
   a.scale_log2 = scale * 1.4426950408889634f;
-  return duo::launch_decode(a, cf.dtype, cf.d_head, g, c->fp8(), blocks, stream);
+  return (int)next;
+}
+
+// Bytes of partial records a decode of `blocks` work items writes.
+size_t decode_records_bytes(const duo_cache* c, int blocks) {
+  return (size_t)blocks * decode_rec_floats(&c->cfg) * sizeof(float);
+}
+
+hipError_t launch_planned_decode(const duo_cache* c, duo::DecodeArgs& a, int blocks, void* ws, hipStream_t stream) {
+  a.ws1 = static_cast<float*>(ws);
+  const int g = c->cfg.n_q / c->cfg.n_kv;
+  return duo::launch_decode(a, c->cfg.dtype, c->cfg.d_head, g, c->fp8(), blocks, stream);
+}
+
+hipError_t enqueue_decode(duo_cache* c, int layer, const void* q, void* out, float scale, void* ws,
+                          const void* new_k, const void* new_v, hipStream_t stream) {
+  duo::DecodeArgs a;
+  const int blocks = plan_decode(c, layer, q, out, scale, new_k, new_v, &a);
+  return launch_planned_decode(c, a, blocks, ws, stream);
 }
 
 }  // namespace
@@ -576,6 +656,7 @@ int duo_decode(duo_cache* c, int layer, const void* q, void* out, float scale, v
   if (int e = check_decode_args(c, q, out, scale, ws, ws_bytes)) return e;
   for (int b = 0; b < c->cfg.B; ++b)
     if (c->len(layer, b) < 1) return fail(DUO_EEMPTY, "row %d of layer %d holds no token", b, layer);
+  if (int r = flush_pending(c, layer, static_cast<hipStream_t>(stream))) return r;
   hipError_t e = enqueue_decode(c, layer, q, out, scale, ws, nullptr, nullptr, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
@@ -594,6 +675,7 @@ int duo_decode_append(duo_cache* c, int layer, const void* k, const void* v, con
   // one launch: each row attends over what it holds and its new token, which
   // the kernel also stores (a row that holds nothing yet attends to the new
   // token alone)
+  if (int r = flush_pending(c, layer, static_cast<hipStream_t>(stream))) return r;
   if (int r = reserve_pages(c, layer, -1, 1, static_cast<hipStream_t>(stream))) return r;
   hipError_t e = enqueue_decode(c, layer, q, out, scale, ws, k, v, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
@@ -664,6 +746,7 @@ int prefill_impl(duo_cache* c, int layer, int row, const void* q, const void* k,
   duo::prefill_plan(cf.dtype, cf.d_head, g, &rows, &hpi);
   a.q_tiles = (int)ceil_div(C, rows);
   a.items_ret = a.B * lp.n_ret * (g / hpi) * a.q_tiles;
+  if (int r = flush_pending(c, layer, s)) return r;
   // pages for the chunk's rows (the attention reads only the held rows)
   if (int r = reserve_pages(c, layer, row, C, s)) return r;
   hipError_t e = hipSuccess;
@@ -782,11 +865,16 @@ int duo_cache_reset_row(duo_cache* c, int layer, int row) {
   if (row < 0 || row >= c->cfg.B) return fail(DUO_EINVAL, "row %d out of range [0, %d)", row, c->cfg.B);
   if (c->paged(layer)) {
     duo_cache::Pages& pg = c->pages[layer];
-    for (int32_t page : pg.rows[row])
+    for (size_t i = 0; i < pg.rows[row].size(); ++i) {
+      const int32_t page = pg.rows[row][i];
       if (--pg.refs[page] == 0) pg.free_list.push_back(page);
+      // the row's table entry names no page any more
+      c->pend_tab[layer].push_back((int32_t)((int64_t)row * c->max_pages() + (int64_t)i));
+    }
     pg.rows[row].clear();
   }
   c->len(layer, row) = 0;
+  c->pend_len[layer].push_back(row);  // the device count, ahead of the next call on the layer
   return ok();
 }
 
@@ -803,6 +891,7 @@ int duo_cache_fork_row(duo_cache* c, int layer, int src_row, int dst_row, void* 
   if (n == 0) return ok();
   const LayerPlan& lp = c->plan.layers[layer];
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (int r = flush_pending(c, layer, s)) return r;
   const duo::LayerPtrs src = c->row_ptrs(layer, src_row), dst = c->row_ptrs(layer, dst_row);
   const int64_t rb = c->row_bytes();
   duo::CopyArgs cp{};
@@ -870,7 +959,53 @@ int duo_cache_fork_row(duo_cache* c, int layer, int src_row, int dst_row, void* 
     seg(src.vsc_str, dst.vsc_str, slots * 4);
   }
   if (hipError_t e = duo::launch_copy(cp, s)) return hip_fail(e, "row copy launch");
+  {  // the device count of dst
+    duo::TableUpdateArgs u{};
+    u.table = c->ptrs(layer).len;
+    u.n = 1;
+    u.index[0] = dst_row;
+    u.page[0] = (int32_t)n;
+    if (hipError_t e = duo::launch_table_update(u, s)) return hip_fail(e, "token count update launch");
+  }
   c->len(layer, dst_row) = n;
+  return ok();
+}
+
+int duo_cache_sync(duo_cache* c, void* stream) {
+  if (!c) return fail(DUO_EINVAL, "cache handle is NULL");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int l = 0; l < c->cfg.L; ++l)
+    if (int r = flush_pending(c, l, s)) return r;
+  const size_t n = (size_t)c->cfg.L * c->cfg.B;
+  std::vector<int32_t> host(n + 1);
+  hipError_t e = hipMemcpyAsync(host.data(), c->arena + c->plan.off_status, (n + 1) * sizeof(int32_t),
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "reading the token counts back");
+  // the layout puts the counts right after the status word
+  static_assert(sizeof(int32_t) == 4, "int32 words");
+  const int32_t status = host[0];
+  for (size_t i = 0; i < n; ++i) c->row_len[i] = host[1 + i];
+  if (status != 0) {
+    e = duo::launch_fill_zero(c->arena + c->plan.off_status, sizeof(int32_t), s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "clearing the status word");
+    return fail(DUO_ECAPACITY, "a step found no room for its tokens (T_cap reached, or a paged row without a "
+                "reserved page): it stored nothing and its token count did not advance");
+  }
+  return ok();
+}
+
+int duo_cache_reserve(duo_cache* c, int layer, int64_t n_tokens, void* stream) {
+  if (int e = check_layer(c, layer)) return e;
+  if (n_tokens < 0) return fail(DUO_EINVAL, "n_tokens must be >= 0 (got %lld)", (long long)n_tokens);
+  const int64_t pmax = c->max_len(layer);
+  if (pmax + n_tokens > c->cfg.T_cap)
+    return fail(DUO_ECAPACITY, "layer %d has a row of %lld tokens; %lld more exceed T_cap %lld", layer,
+                (long long)pmax, (long long)n_tokens, (long long)c->cfg.T_cap);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (int r = flush_pending(c, layer, s)) return r;
+  if (int r = reserve_pages(c, layer, -1, n_tokens, s)) return r;
   return ok();
 }
 

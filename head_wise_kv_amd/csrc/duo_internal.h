@@ -42,7 +42,16 @@ struct LayerPtrs {
   int32_t* table;
   int32_t max_pages;
   int32_t page_shift;
+  // Token count of each batch row ([B], device), read by the kernels when they
+  // run and advanced by the appends: a step captured in a HIP graph replays
+  // as the next step.  `status` (one word per cache): bit 0 is set when a
+  // step found no room for its tokens (it then stored nothing and the count
+  // did not advance).
+  int32_t* len;
+  int32_t* status;
+  int64_t cap;     // T_cap: positions a row may hold
 };
+
 
 // Rotary position embedding (on = 0: keys and queries are used as given).
 // Pair i of a head's dimensions, (i, i + d/2), turns by p * theta^(-2i/d) at
@@ -52,13 +61,22 @@ struct Rope {
   int on;
 };
 
-// Page table entries written before the kernels that read them (same stream).
+// int32 words written before the kernels that read them (same stream): page
+// table entries, and token counts set by the host (prefill, fork, reset).
 constexpr int kMaxTableUpdates = 240;
 struct TableUpdateArgs {
   int32_t* table;
   int n;
   int32_t index[kMaxTableUpdates];
   int32_t page[kMaxTableUpdates];
+};
+
+// Advance the token counts of rows [0, B) of a layer by n after an append
+// that read them (each row only if it had room, else the status bit).
+struct AdvanceArgs {
+  LayerPtrs lp;
+  int B;
+  int64_t n;
 };
 
 // Device copies of byte ranges: segment i copies `count` blocks of `bytes`
@@ -75,6 +93,10 @@ struct CopyArgs {
 };
 
 struct AppendArgs {
+  // p0 from the device: each row's first position is its count in lp.len
+  // at execution (duo_append, duo_append_row), else p0[] (a prefill commit,
+  // which then sets the counts to p0 + n_new).
+  int p0_from_device;
   const char* k;   // [B][n_kv][n_new][d]
   const char* v;
   LayerPtrs lp;
@@ -91,15 +113,15 @@ struct AppendArgs {
   Rope rope;              // K rows are rotated at their position before they are stored
 };
 
-// Per batch row of a decode: its held rows, its work items and, for a fused
-// append, where its new token goes.
+// Per batch row of a decode: the rows it held when the call was planned and
+// its work items.  The kernel reads the row's count (lp.len) when it runs:
+// the last work item of a head ends at the rows held then, and a fused
+// append's new token goes to that position, so a replayed step that finds
+// more tokens than were planned for covers them.
 struct DecodeRow {
-  int32_t rows_ret, rows_str;    // rows held per retrieval / streaming head (before a fused append)
+  int32_t rows_ret, rows_str;    // rows per retrieval / streaming head at planning (before a fused append)
   int32_t nb_ret, nb_str;        // work items per retrieval / streaming head of this row (each >= 1)
   int32_t first_ret, first_str;  // index of the first work item of the row's retrieval / streaming heads
-  int32_t new_pos;               // fused append: position of the new token (its retrieval row)
-  int32_t new_slot_str;          // ... its streaming slot
-  int32_t excl_str;              // ... the streaming slot whose old token it evicts (-1: none)
 };
 
 struct DecodeArgs {
@@ -112,6 +134,7 @@ struct DecodeArgs {
   int64_t cap_ret, cap_str;     // rows reserved per head
   int32_t items_ret;            // work items of all retrieval heads (they come first)
   int32_t multi;                // nonzero if some head spans several work items
+  int32_t S, W;
   float scale_log2;             // softmax scale * log2(e)
   // Fused append (decode of a token appended by the same call); new_k is
   // null for a plain decode.  The rows counts are then those held before the
@@ -120,7 +143,7 @@ struct DecodeArgs {
   const char* new_k;            // [B][n_kv][d]
   const char* new_v;
   // Queries (and a fused append's new K row) are rotated at the query's
-  // position: rows[b].new_pos for a fused append, rows[b].new_pos - 1 otherwise.
+  // position: the row's count for a fused append, the count - 1 otherwise.
   Rope rope;
   DecodeRow rows[kMaxRows];     // items ordered: row 0's retrieval heads, row 1's, ..., then streaming likewise
 };
@@ -173,6 +196,8 @@ struct RopeArgs {
 
 // Launchers (duo_kernels.hip, duo_prefill.hip, duo_gated.hip).  dtype: 0 = fp32, 1 = bf16.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_fill_ones(void* p, size_t bytes, hipStream_t s);  // every byte 0xFF (int32 -1)
+hipError_t launch_advance(const AdvanceArgs& a, hipStream_t s);
 hipError_t launch_table_update(const TableUpdateArgs& a, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
 hipError_t launch_rope(const RopeArgs& a, hipStream_t s);

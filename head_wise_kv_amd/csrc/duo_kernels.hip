@@ -23,6 +23,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <cstddef>
 #include <type_traits>
 
 namespace duo {
@@ -74,11 +75,21 @@ __device__ __forceinline__ void st16(char* p, uint4 v) { *reinterpret_cast<uint4
 
 // ------------------------------------------------------------------ fill
 
-__global__ void fill_zero_kernel(uint4* p, size_t n16, unsigned char* tail, size_t ntail) {
+__global__ void fill_kernel(uint4* p, size_t n16, unsigned char* tail, size_t ntail, uint32_t word) {
   size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
   size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t j = i; j < n16; j += stride) p[j] = make_uint4(0, 0, 0, 0);
-  if (i < ntail) tail[i] = 0;
+  for (size_t j = i; j < n16; j += stride) p[j] = make_uint4(word, word, word, word);
+  if (i < ntail) tail[i] = (unsigned char)word;
+}
+
+// Token counts after an append that read them: row b advances by n if it had
+// room (the append then stored its tokens), else the cache's status bit is set.
+__global__ void advance_kernel(AdvanceArgs a) {
+  const int b = threadIdx.x;
+  if (b >= a.B) return;
+  const int32_t cnt = a.lp.len[b];
+  if (room_for(a.lp, b, cnt, a.n)) a.lp.len[b] = (int32_t)(cnt + a.n);
+  else *a.lp.status = 1;
 }
 
 // ------------------------------------------------------------------ page tables and row copies
@@ -155,8 +166,18 @@ __global__ void append_kernel(AppendArgs a) {
     const int64_t i = rest % a.n_new;
     const int kvh = (int)((rest / a.n_new) % a.n_kv);
     const int b = (int)(rest / a.n_new / a.n_kv);
-    const int64_t p = a.p0[b] + i;
-    const int64_t keep_from = max64d((int64_t)a.S, (int64_t)a.p0[b] + a.n_new - a.W);
+    int64_t p0 = a.p0[b];
+    if (a.p0_from_device) {
+      p0 = a.lp.len[b];
+      if (!room_for(a.lp, b, p0, a.n_new)) {  // nothing of this row is stored
+        if (i == 0 && kvh == 0 && c == 0) *a.lp.status = 1;
+        continue;
+      }
+    } else if (idx < a.B) {
+      a.lp.len[idx] = (int32_t)(a.p0[idx] + a.n_new);  // nothing in this launch reads the counts
+    }
+    const int64_t p = p0 + i;
+    const int64_t keep_from = max64d((int64_t)a.S, p0 + a.n_new - a.W);
     const size_t src = (size_t)rest * a.row_bytes;
     char *kd, *vd;
     if (a.map.kind[kvh]) {
@@ -512,8 +533,21 @@ __global__ void append_fp8_kernel(AppendArgs a) {
   rest /= a.n_new;
   const int kvh = (int)(rest % a.n_kv);
   const int b = (int)(rest / a.n_kv);
-  const int64_t p = a.p0[b] + i;
-  const int64_t keep_from = max64d((int64_t)a.S, (int64_t)a.p0[b] + a.n_new - a.W);
+  int64_t p0 = a.p0[b];
+  if (a.p0_from_device) {
+    p0 = a.lp.len[b];
+    if (!room_for(a.lp, b, p0, a.n_new)) {  // nothing of this row is stored (the whole group leaves)
+      if (i == 0 && kvh == 0 && tensor == 0 && j == 0) *a.lp.status = 1;
+      return;
+    }
+  } else {
+    // nothing in this launch reads the counts; the first B threads set them
+    // (they all hold a row: there are 2 B n_kv n_new rows of 16 threads)
+    const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gt < a.B) a.lp.len[gt] = (int32_t)(a.p0[gt] + a.n_new);
+  }
+  const int64_t p = p0 + i;
+  const int64_t keep_from = max64d((int64_t)a.S, p0 + a.n_new - a.W);
   const size_t src = (((size_t)b * a.n_kv + kvh) * a.n_new + i) * a.in_row_bytes + (size_t)j * 16;
   float sc;
   uint4 x = ld16((tensor ? a.v : a.k) + src);
@@ -611,6 +645,7 @@ __device__ __forceinline__ void lds_barrier() {
 struct DecodeItem {
   int64_t hh;       // head number
   int64_t r0, r1;   // rows of the head
+  int64_t cnt;      // the batch row's token count when the kernel runs (before a fused append), -1 if not read
   int part, nparts;
   int b, kvh;
   int row;          // batch row (index into DecodeArgs::rows)
@@ -630,26 +665,41 @@ struct DecodeItem {
   __device__ __forceinline__ int64_t at(int64_t row) const { return ptab ? paged_row(ptab, shift, pstride, row) : row; }
 };
 
+// Entry i (wavefront-uniform) of an int8 table in the kernel arguments: the
+// dword that holds it comes by a scalar load and the byte is extracted (gfx9
+// has no scalar byte load, and a vector byte load would have to be waited for
+// before the item's first loads are issued).
+static_assert(offsetof(DecodeArgs, map) % 4 == 0 && offsetof(HeadMap, orig_ret) % 4 == 0 &&
+                  offsetof(HeadMap, orig_str) % 4 == 0 && kMaxKV % 4 == 0,
+              "head-map tables are read as aligned dwords");
+__device__ __forceinline__ int arg_byte(const int8_t* table, int i) {
+  const uint32_t word = *reinterpret_cast<const uint32_t*>(table + (i & ~3));
+  return (int)(int8_t)(word >> (8 * (i & 3)));
+}
+
 template <int ROWB, int RR>
-__device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a, int64_t blk) {
+__device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a, int blk) {
+  // Index arithmetic in 32 bits (item and row counts fit), the head index
+  // made wavefront-uniform so the head-map lookups are scalar loads: this
+  // runs before the first loads of the item are issued.
   DecodeItem w;
   w.ptab = nullptr;
   w.shift = 0;
   w.pstride = 0;
-  int64_t rows;
+  int rows;
   if (blk < a.items_ret) {
     int b = 0;
     while (b + 1 < a.B && blk >= a.rows[b + 1].first_ret) ++b;  // batch row of the item (uniform)
     const DecodeRow& R = a.rows[b];
-    const int64_t rel = blk - R.first_ret;
-    const int r = (int)(rel / R.nb_ret);
-    w.part = (int)(rel % R.nb_ret);
+    const int rel = blk - R.first_ret;
+    const int r = __builtin_amdgcn_readfirstlane(rel / R.nb_ret);
+    w.part = rel - r * R.nb_ret;
     w.nparts = R.nb_ret;
     rows = R.rows_ret;
     w.row = b;
     w.b = b;
     w.hh = (int64_t)b * a.n_ret + r;
-    w.kvh = a.map.orig_ret[r];
+    w.kvh = arg_byte(a.map.orig_ret, r);
     // first row of the head: row 0 of its contiguous rows, or its part of page 0
     size_t srow = ((size_t)b * a.n_ret + r) * a.cap_ret;
     if (a.lp.table) {
@@ -666,15 +716,15 @@ __device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a, int64_t b
     int b = 0;
     while (b + 1 < a.B && blk >= a.rows[b + 1].first_str) ++b;
     const DecodeRow& R = a.rows[b];
-    const int64_t rel = blk - R.first_str;
-    const int si = (int)(rel / R.nb_str);
-    w.part = (int)(rel % R.nb_str);
+    const int rel = blk - R.first_str;
+    const int si = __builtin_amdgcn_readfirstlane(rel / R.nb_str);
+    w.part = rel - si * R.nb_str;
     w.nparts = R.nb_str;
     rows = R.rows_str;
     w.row = b;
     w.b = b;
     w.hh = (int64_t)a.B * a.n_ret + (int64_t)b * a.n_str + si;
-    w.kvh = a.map.orig_str[si];
+    w.kvh = arg_byte(a.map.orig_str, si);
     const size_t off = ((size_t)b * a.n_str + si) * a.cap_str * ROWB;
     w.kbase = a.lp.k_str + off;
     w.vbase = a.lp.v_str + off;
@@ -682,12 +732,30 @@ __device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a, int64_t b
     w.ksc = a.lp.ksc_str ? a.lp.ksc_str + srow : nullptr;
     w.vsc = a.lp.vsc_str ? a.lp.vsc_str + srow : nullptr;
   }
-  int64_t per = (rows + w.nparts - 1) / w.nparts;
+  // The items of a head split the rows held at planning.  The last one ends
+  // at the rows held when the kernel runs (end_last_item: a replayed step
+  // may find more); until then it ends where the plan did.
+  int per = __builtin_amdgcn_readfirstlane((rows + w.nparts - 1) / w.nparts);
   if (w.ptab) per = (per + RR - 1) / RR * RR;  // paged: every round of rows lies in one page
-  w.r0 = w.part * per;
+  w.r0 = (int64_t)w.part * per;
   w.r1 = w.r0 + per < rows ? w.r0 + per : rows;
   if (w.r0 > rows) w.r0 = rows;
+  w.cnt = -1;
   return w;
+}
+
+// The batch row's token count when the kernel runs, read through the scalar
+// cache (the decode kernel never writes the counts), so the read adds nothing
+// to the vector-memory counts the ring's waits rely on.
+__device__ __forceinline__ int64_t row_count(const DecodeArgs& a, int b) {
+  return *(const __attribute__((address_space(4))) int32_t*)(a.lp.len + b);
+}
+
+// The last item of a head ends at the rows its batch row holds now.
+__device__ __forceinline__ void end_last_item(const DecodeArgs& a, DecodeItem& w) {
+  const int64_t now = w.hh < (int64_t)a.B * a.n_ret ? w.cnt : (w.cnt < a.cap_str ? w.cnt : a.cap_str);
+  w.r1 = now;
+  if (w.r0 > now) w.r0 = now;
 }
 
 // Per-lane softmax state.  m is a reference maximum (log2 units); l and acc
@@ -965,10 +1033,17 @@ __device__ __forceinline__ bool tile_scores4(float& m, float& l, uint16_t* pbuf,
 #pragma unroll
   for (int j = 0; j < S4::RPL4; ++j) {
     const float pj = fast_exp2(fmaf(sc[j], scale_log2, -mu));
-    l += pj;
     // FP8 rows: the V row's scale joins the probability the weighted sum uses
-    const float pw = C::KV8 ? pj * vsc[r16 + 16 * j] : pj;
-    if (s4 < HW) pbuf[((rg * S4::NQ + j) * HW + s4) * 2 + half] = bf16_bits(pw);
+    const float vs = C::KV8 ? vsc[r16 + 16 * j] : 1.f;
+    const uint16_t pb = bf16_bits(C::KV8 ? pj * vs : pj);
+    const float pr = __uint_as_float((uint32_t)pb << 16);
+    // The sum takes the weight the weighted sum really applies to the row --
+    // the rounded probability (divided by the V row's scale for FP8 rows; a
+    // zero row contributes nothing either way) -- so the weights of the result
+    // sum to one: an unrounded sum would leave a relative error of up to 2^-9
+    // in every output element.
+    l += C::KV8 ? (vs > 0.f ? pr * __builtin_amdgcn_rcpf(vs) : pj) : pr;
+    if (s4 < HW) pbuf[((rg * S4::NQ + j) * HW + s4) * 2 + half] = pb;
   }
   return any;
 }
@@ -1080,15 +1155,27 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   const int hg = wave % C::HSPLIT;     // which HW query heads of the group it scores
   const bool active = slot < SLOTS;
   const int rg = lane >> 3, s = lane & 7;
-  const DecodeItem w = decode_item<C::ROWB, C::ROUND_ROWS>(a, blockIdx.x);
+  DecodeItem w = decode_item<C::ROWB, C::ROUND_ROWS>(a, blockIdx.x);
+  // The row's token count: needed before the first loads by the last item of
+  // a head (where it ends, where a fused append's token goes) and by the items
+  // of a streaming head under a fused append (the slot the new token evicts);
+  // other items wait for it only if rotary positions need the query's position.
+  if (w.part == w.nparts - 1 || (a.new_k != nullptr && w.hh >= (int64_t)a.B * a.n_ret)) {
+    w.cnt = row_count(a, w.b);
+    if (w.part == w.nparts - 1) end_last_item(a, w);
+  }
   const int64_t nrounds = ((w.r1 - w.r0 + TR - 1) / TR + SLOTS - 1) / SLOTS;
   const size_t q_off = ((size_t)w.b * a.n_q + (size_t)w.kvh * G) * D;  // first query of the group
 
-  // fused append: the last item of every head adds the new token
+  // fused append: the last item of every head adds the new token at position
+  // w.cnt; the step stores it only if the row has room (else it is attended
+  // from the staging area alone and the cache's status bit is set)
   const bool add_new = a.new_k != nullptr && w.part == w.nparts - 1;
   const bool ret_head = w.hh < (int64_t)a.B * a.n_ret;
+  const int64_t cap_str = a.cap_str;
   // streaming slot masked in the held rows (its token is evicted by the new one)
-  const int64_t excl_row = (a.new_k != nullptr && !ret_head) ? a.rows[w.row].excl_str : -1;
+  const int64_t excl_row =
+      (a.new_k != nullptr && !ret_head && w.cnt >= cap_str) ? a.S + (w.cnt - a.S) % a.W : -1;
   // per-lane byte offset, within a round of rows, of this wavefront's load
   // pieces: piece n of a unit covers LDS bytes [n*1024, n*1024+1024), lane i
   // byte n*1024 + 16 i, i.e. row (n*1024 + 16 i) / ROWB of the round at a
@@ -1152,7 +1239,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   // rotary positions: this lane's angle (pair lane % (D/2)) at the query's
   // position, computed while the loads are in flight
   double rcs = 1.0, rsn = 0.0;
-  if (a.rope.on) rope_cs(a.rope, D, a.rows[w.row].new_pos - (a.new_k ? 0 : 1), lane % (D / 2), rcs, rsn);
+  if (a.rope.on) {
+    const int64_t cnt = w.cnt >= 0 ? w.cnt : row_count(a, w.b);
+    rope_cs(a.rope, D, cnt - (a.new_k ? 0 : 1), lane % (D / 2), rcs, rsn);
+  }
   wait_vmcnt<WAITN>();  // unit 0 and the staging loads have landed
   lds_barrier();
   if (a.rope.on) {
@@ -1263,22 +1353,27 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
         tile_pv<KT, D, G>(st, p, ring1, rg, s);
       }
     }
-    const int64_t row = ret_head ? w.at(a.rows[w.row].new_pos) : a.rows[w.row].new_slot_str;
-    if constexpr (KV8) {
-      if (wave == 0 && lane < 32) {
-        const int t = lane >> 4, j = lane & 15;
-        *reinterpret_cast<uint2*>((t ? w.vbase : w.kbase) + (size_t)row * C::ROWB + j * 8) = ncodes;
-        if (j == 0) (t ? w.vsc : w.ksc)[row] = nscale;
+    const int64_t slot_str = w.cnt < a.S ? w.cnt : a.S + (w.cnt - a.S) % a.W;
+    if (room_for(a.lp, w.b, w.cnt, 1)) {
+      const int64_t row = ret_head ? w.at(w.cnt) : slot_str;
+      if constexpr (KV8) {
+        if (wave == 0 && lane < 32) {
+          const int t = lane >> 4, j = lane & 15;
+          *reinterpret_cast<uint2*>((t ? w.vbase : w.kbase) + (size_t)row * C::ROWB + j * 8) = ncodes;
+          if (j == 0) (t ? w.vsc : w.ksc)[row] = nscale;
+        }
+      } else {
+        if (wave == 0 && lane < 2 * C::CPR) {
+          char* dst = (lane < C::CPR ? w.kbase : w.vbase) + (size_t)row * C::ROWB + (lane % C::CPR) * 16;
+          *reinterpret_cast<uint4*>(dst) = nkv;
+        }
       }
-    } else {
-      if (wave == 0 && lane < 2 * C::CPR) {
-        char* dst = (lane < C::CPR ? w.kbase : w.vbase) + (size_t)row * C::ROWB + (lane % C::CPR) * 16;
-        *reinterpret_cast<uint4*>(dst) = nkv;
+      if (wave == 0 && lane == 0 && !ret_head) {
+        const int64_t si = w.hh - (int64_t)a.B * a.n_ret;  // b * n_str + streaming index
+        a.lp.pos[si * a.cap_str + slot_str] = (int32_t)w.cnt;
       }
-    }
-    if (wave == 0 && lane == 0 && !ret_head) {
-      const int64_t si = w.hh - (int64_t)a.B * a.n_ret;  // b * n_str + streaming index
-      a.lp.pos[si * a.cap_str + a.rows[w.row].new_slot_str] = a.rows[w.row].new_pos;
+    } else if (wave == 0 && lane == 0) {
+      *a.lp.status = 1;
     }
   }
 
@@ -1391,6 +1486,13 @@ __global__ __launch_bounds__(kDecodeThreads) void combine_kernel(DecodeArgs a) {
   constexpr int DC = D / kCombineElems;
   __shared__ float c_m[kCombineGroups][kCombineElems], c_l[kCombineGroups][kCombineElems],
       c_a[kCombineGroups][kCombineElems];
+  if (a.new_k != nullptr && blockIdx.x == 0 && threadIdx.x < a.B) {
+    // a fused append's step is done: every row advances by its new token if
+    // it had room (the decode kernel, which read the counts, has finished)
+    const int b = threadIdx.x;
+    const int32_t cnt = a.lp.len[b];
+    if (room_for(a.lp, b, cnt, 1)) a.lp.len[b] = cnt + 1;
+  }
   const int64_t hh = blockIdx.x / (G * DC);
   const int h = (int)((blockIdx.x / DC) % G);
   const int dcn = (int)(blockIdx.x % DC);
@@ -1402,14 +1504,14 @@ __global__ __launch_bounds__(kDecodeThreads) void combine_kernel(DecodeArgs a) {
     const int r = (int)(hh % a.n_ret);
     first = a.rows[b].first_ret + (int64_t)r * a.rows[b].nb_ret;
     n_seg = a.rows[b].nb_ret;
-    kvh = a.map.orig_ret[r];
+    kvh = arg_byte(a.map.orig_ret, r);
   } else {
     const int64_t x = hh - n_ret_heads;
     b = (int)(x / a.n_str);
     const int si = (int)(x % a.n_str);
     first = a.rows[b].first_str + (int64_t)si * a.rows[b].nb_str;
     n_seg = a.rows[b].nb_str;
-    kvh = a.map.orig_str[si];
+    kvh = arg_byte(a.map.orig_str, si);
   }
   if (n_seg == 1) return;  // written by the decode kernel
   const float* rec0 = a.ws1 + (size_t)first * C::REC;
@@ -1466,7 +1568,14 @@ hipError_t launch_decode_g(const DecodeArgs& a, int blocks, hipStream_t s) {
   decode_kernel<KT, D, G><<<blocks, kDecodeThreads, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (!a.multi) return hipSuccess;  // every head finished in one item
+  if (!a.multi) {  // every head finished in one item; a fused append's counts still advance
+    if (a.new_k == nullptr) return hipSuccess;
+    AdvanceArgs v{};
+    v.lp = a.lp;
+    v.B = a.B;
+    v.n = 1;
+    return launch_advance(v, s);
+  }
   const int64_t heads = (int64_t)a.B * (a.n_ret + a.n_str);
   combine_kernel<KT, D, G><<<(unsigned)(heads * G * (D / kCombineElems)), kDecodeThreads, 0, s>>>(a);
   return hipGetLastError();
@@ -1519,14 +1628,24 @@ hipError_t launch_copy(const CopyArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+namespace {
+hipError_t launch_fill(void* p, size_t bytes, uint32_t word, hipStream_t s) {
   if (bytes == 0) return hipSuccess;
   const size_t n16 = bytes / 16, ntail = bytes % 16;
   const int threads = 256;
   size_t want = (n16 + threads - 1) / threads;
   const int grid = (int)std::max<size_t>(1, std::min<size_t>(want, 4096));
-  fill_zero_kernel<<<grid, threads, 0, s>>>(reinterpret_cast<uint4*>(p), n16,
-                                           reinterpret_cast<unsigned char*>(p) + n16 * 16, ntail);
+  fill_kernel<<<grid, threads, 0, s>>>(reinterpret_cast<uint4*>(p), n16,
+                                       reinterpret_cast<unsigned char*>(p) + n16 * 16, ntail, word);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) { return launch_fill(p, bytes, 0u, s); }
+hipError_t launch_fill_ones(void* p, size_t bytes, hipStream_t s) { return launch_fill(p, bytes, 0xffffffffu, s); }
+
+hipError_t launch_advance(const AdvanceArgs& a, hipStream_t s) {
+  advance_kernel<<<1, kMaxRows, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -29,4 +29,14 @@ __device__ __forceinline__ int64_t paged_row(const int32_t* row_table, int shift
   return (int64_t)page * page_stride + (p & ((int64_t{1} << shift) - 1));
 }
 
+// Whether batch row b, holding `cnt` tokens, has room for n more: within
+// T_cap and, for paged retrieval rows, on pages the row's table names (a
+// row's table names the pages of a prefix of its positions; the entries past
+// them hold -1).
+__device__ __forceinline__ bool room_for(const LayerPtrs& lp, int64_t b, int64_t cnt, int64_t n) {
+  if (cnt + n > lp.cap) return false;
+  if (lp.table && n > 0) return lp.table[b * lp.max_pages + ((cnt + n - 1) >> lp.page_shift)] >= 0;
+  return true;
+}
+
 }  // namespace duo

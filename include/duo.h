@@ -24,8 +24,24 @@
  *     only thing it allocates is the small host-side handle.
  *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the
  *     default stream) with no implicit synchronisation.  Calls on one cache
- *     must be issued in order on one stream.  The host-side token count of a
- *     layer advances when a call is enqueued.
+ *     must be issued in order on one stream.
+ *   - Token counts are kept twice.  The host-side count of each (layer, batch
+ *     row) advances when a call is enqueued and is what the library validates
+ *     against.  The device-side count, in the arena, is what the kernels read
+ *     when they run: an append or a fused decode-append stores its tokens at
+ *     the row's device count and advances it, so a step captured in a HIP
+ *     graph ("DuoAttention: Dual Retrieval & Streaming Heads Guide",
+ *     "Production Advantages and Deployment Considerations", item 1: static
+ *     execution graphs) replays as the next step, at the next position.
+ *     Replays do not move the host count: call duo_cache_sync before the next
+ *     call that is not a replay.  A captured call must be replayed only while
+ *     every row holds at least the tokens it held when the call was captured
+ *     (replays only move counts forward, so this holds for replays of steps).
+ *     A replayed append or decode-append that finds no room (T_cap, or a paged
+ *     row past its reserved pages, see duo_cache_reserve) stores nothing,
+ *     does not advance, and sets a flag duo_cache_sync reports.  Prefill
+ *     chunks and forks set the device counts to the host's values: replaying
+ *     one repeats it.
  *   - Errors: 0 (DUO_OK) or a negative DUO_E* code.  Every argument is
  *     validated before anything is enqueued, so a failing call changes no
  *     state.  duo_last_error() returns a message for the calling thread.
@@ -278,8 +294,10 @@ int duo_cache_head_scales(const duo_cache* c, int layer, int kv_head, float** k_
 
 /* Forget batch row `row` of `layer`: its token count becomes 0 and the pages
  * it alone held return to the layer's pool (a finished request of a ragged
- * batch leaves room for the next).  Host only, no device work; later calls
- * on the row see an empty row. */
+ * batch leaves room for the next).  Host only: the device-side count and
+ * page-table entries are written ahead of the next call on the layer that
+ * takes a stream (or by duo_cache_sync); later calls on the row see an empty
+ * row.  Captured calls that involve the row must be captured again. */
 int duo_cache_reset_row(duo_cache* c, int layer, int row);
 
 /* Prefix sharing: batch row dst (which must hold no token) becomes a copy of
@@ -293,6 +311,21 @@ int duo_cache_reset_row(duo_cache* c, int layer, int row);
  * copies every held row.  Enqueued on `stream`.  DUO_ECAPACITY if no page is
  * free for the copy. */
 int duo_cache_fork_row(duo_cache* c, int layer, int src_row, int dst_row, void* stream);
+
+/* Bring the host-side token counts up to date with the device-side counts
+ * after replays of captured calls: waits for `stream`, then reads every
+ * layer's counts back (also writes the counts a duo_cache_reset_row left
+ * pending).  DUO_ECAPACITY if some replayed append or decode-append found no
+ * room for its tokens since the last sync (it stored nothing and its count
+ * did not advance); the flag is then cleared.  Not to be captured. */
+int duo_cache_sync(duo_cache* c, void* stream);
+
+/* Give every batch row of `layer` room for n_tokens more tokens now, so that
+ * replays of captured steps can advance that far: on a paged layer the pages
+ * they will need are taken from the pool (DUO_ECAPACITY if the pool has too
+ * few, nothing taken); on a contiguous one the rows already have their T_cap.
+ * DUO_ECAPACITY if some row would exceed T_cap. */
+int duo_cache_reserve(duo_cache* c, int layer, int64_t n_tokens, void* stream);
 
 /* Pages of `layer` not held by any row (0 for a contiguous cache). */
 int duo_cache_free_pages(const duo_cache* c, int layer, int64_t* out);

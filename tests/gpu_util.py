@@ -2,6 +2,7 @@
 oracle, and the tolerance check."""
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -13,12 +14,10 @@ from oracle import attention as OA
 from oracle import cache as OC
 
 # Tolerances.  bf16 inputs with fp32 accumulation: max |err| <= 2e-2 and
-# relative RMS <= 1e-2.  fp32 inputs: the kernel rounds nothing but the
-# order of fp32 sums, so 1e-3 / 1e-4.  The bound is on the computed result;
-# outputs are returned in the cache dtype, so each element is then rounded
-# once more, and the element bound grows by half a step of that dtype at the
-# reference value (for bf16 below 0.002 where |out| < 1, but 0.0156 where a
-# few-key softmax makes |out| >= 4, more than the 2e-2 leaves).
+# relative RMS <= 1e-2 on the output as the library returns it (rounded to
+# the cache dtype).  fp32 inputs: the kernel rounds nothing but the order of
+# fp32 sums, so 1e-3 / 1e-4.  Every case's raw errors are printed, and
+# appended to the file DUO_ERRLOG names when that variable is set.
 TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-3, 1e-4)}
 _MANT_BITS = {"bf16": 7, "f32": 23}
 
@@ -50,16 +49,26 @@ def stored(x_f32: np.ndarray, dtype: str) -> np.ndarray:
     return WL.round_to_dtype(x_f32, dtype)
 
 
+def _log_errors(what: str, dtype: str, max_err: float, rel: float, ref_max: float) -> None:
+    say(f"{what}: max|err| {max_err:.3e} rel-RMS {rel:.3e} (max|ref| {ref_max:.3g}, {dtype})")
+    path = os.environ.get("DUO_ERRLOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(f"{what}\t{dtype}\t{max_err:.4e}\t{rel:.4e}\t{ref_max:.4g}\n")
+
+
 def check_close(got: torch.Tensor, ref: np.ndarray, dtype: str, what: str = ""):
+    """max |got - ref| <= atol and ||got - ref|| / ||ref|| <= rel-RMS bound, on
+    the output as returned (no allowance for its rounding)."""
     g = got.detach().float().cpu().double().numpy()
     atol, rrms = TOL[dtype]
     err = np.abs(g - ref)
     assert np.isfinite(g).all(), f"{what}: non-finite output"
     max_err = float(err.max()) if err.size else 0.0
-    over = float((err - half_step(ref, dtype)).max()) if err.size else 0.0  # error beyond the output's rounding
     rel = float(np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30)) if err.size else 0.0
-    assert over <= atol and rel <= rrms, (f"{what}: max|err| {max_err:.3e} ({over:.3e} beyond the output rounding, "
-                                          f"tol {atol}), rel-RMS {rel:.3e} (tol {rrms})")
+    _log_errors(what, dtype, max_err, rel, float(np.abs(ref).max()) if err.size else 0.0)
+    assert max_err <= atol and rel <= rrms, (f"{what}: max|err| {max_err:.3e} (tol {atol}), "
+                                            f"rel-RMS {rel:.3e} (tol {rrms})")
     return max_err, rel
 
 

@@ -112,10 +112,12 @@ def test_prefill_then_decode():
 
 
 @pytest.mark.gpu
+@pytest.mark.timeout(400)
 def test_llama3_8b_prefill_64k():
     """Chunked prefill workload at full size: n_q=32, n_kv=8, d=128, bf16,
     65,536 tokens in 16 chunks of 4,096, 2/8 retrieval, S=64, W=1024; every
-    chunk's output checked on sampled rows of every head."""
+    chunk's output checked on sampled rows of every head, and every row of
+    chunks 0 and 15 for one retrieval and one streaming query head."""
     need_gpu()
     from head_wise_kv_amd import DuoCache
     w = WL.WORKLOADS["llama3_8b_prefill_64k"]
@@ -136,4 +138,13 @@ def test_llama3_8b_prefill_64k():
         got = out[0][:, rows].float().cpu().double().numpy()
         ref = OA.prefill_full(q64, k64, v64, mask, w.S, w.W, w.scale, rows=p + rows)
         check_close(torch.from_numpy(got), ref, w.dtype, f"{w.name} chunk {ci}")
+        if ci in (0, N // C - 1):
+            # every row of the first and the last chunk, for the first query
+            # head of a retrieval KV head and of a streaming KV head
+            for kvh in (int(np.argmax(mask == 1)), int(np.argmax(mask == 0))):
+                h = kvh * w.g
+                ref_h = OA.prefill_full(q64[h:h + 1], k64[kvh:kvh + 1], v64[kvh:kvh + 1], [mask[kvh]], w.S, w.W,
+                                        w.scale, rows=p + np.arange(C))
+                kind = "retrieval" if mask[kvh] else "streaming"
+                check_close(out[0][h:h + 1], ref_h, w.dtype, f"{w.name} chunk {ci} all rows, {kind} head {h}")
     assert c.seq_len(0) == N
