@@ -29,7 +29,7 @@ EXPORTS = ("duo_cache_bytes", "duo_cache_payload_bytes", "duo_cache_init", "duo_
            "duo_decode_append", "duo_prefill_chunk", "duo_cache_seq_len", "duo_cache_head_view", "duo_cache_free",
            "duo_last_error", "duo_gated_attention", "duo_cache_head_scales", "duo_append_row", "duo_prefill_chunk_row",
            "duo_cache_row_len", "duo_cache_reset_row", "duo_cache_fork_row", "duo_cache_free_pages",
-           "duo_cache_row_pages", "duo_prefill_workspace_bytes",
+           "duo_cache_row_pages", "duo_prefill_workspace_bytes", "duo_decode_append_noalloc",
            "duo_cache_sync", "duo_cache_reserve")
 
 
@@ -64,6 +64,7 @@ def _load():
     lib.duo_append.argtypes = [vp, i32, vp, vp, i64, vp]
     lib.duo_decode.argtypes = [vp, i32, vp, vp, ctypes.c_float, vp, sz, vp]
     lib.duo_decode_append.argtypes = [vp, i32, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp]
+    lib.duo_decode_append_noalloc.argtypes = [vp, i32, vp, vp, vp, vp, ctypes.c_float, vp]
     lib.duo_prefill_chunk.argtypes = [vp, i32, vp, vp, vp, i64, vp, ctypes.c_float, vp, sz, vp]
     lib.duo_cache_seq_len.argtypes = [vp, i32, ctypes.POINTER(i64)]
     lib.duo_cache_head_view.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(vp),

@@ -471,6 +471,16 @@ int duo_cache_init(const duo_config* cfg, void* arena, size_t arena_bytes, void*
         hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
       c->num_cu = n;
   }
+  {
+    // the allocation-free decode's scratch: its device address on this
+    // device, resolved once per device
+    void* scratch = nullptr;
+    const hipError_t e = duo::static_scratch(&scratch);
+    if (e != hipSuccess) {
+      delete c;
+      return hip_fail(e, "address of the library's device scratch");
+    }
+  }
   hipError_t s_err = hipSuccess;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // the status word and every token count start at zero
@@ -678,6 +688,37 @@ int duo_decode_append(duo_cache* c, int layer, const void* k, const void* v, con
   if (int r = flush_pending(c, layer, static_cast<hipStream_t>(stream))) return r;
   if (int r = reserve_pages(c, layer, -1, 1, static_cast<hipStream_t>(stream))) return r;
   hipError_t e = enqueue_decode(c, layer, q, out, scale, ws, k, v, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  for (int b = 0; b < c->cfg.B; ++b) c->len(layer, b) += 1;
+  return ok();
+}
+
+int duo_decode_append_noalloc(duo_cache* c, int layer, const void* k, const void* v, const void* q, void* out,
+                              float scale, void* stream) {
+  if (int e = check_layer(c, layer)) return e;
+  if (!k || !v) return fail(DUO_EINVAL, "k or v is NULL");
+  if (!aligned16(k) || !aligned16(v)) return fail(DUO_EINVAL, "k and v must be 16-byte aligned");
+  if (!q || !out) return fail(DUO_EINVAL, "q or out is NULL");
+  if (!aligned16(q) || !aligned16(out)) return fail(DUO_EINVAL, "q and out must be 16-byte aligned");
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(DUO_EINVAL, "scale must be finite and > 0");
+  const int64_t pmax = c->max_len(layer);
+  if (pmax + 1 > c->cfg.T_cap)
+    return fail(DUO_ECAPACITY, "layer %d has a row of %lld tokens; one more exceeds T_cap %lld", layer,
+                (long long)pmax, (long long)c->cfg.T_cap);
+  void* scratch = nullptr;
+  const hipError_t se = duo::static_scratch(&scratch);
+  if (se != hipSuccess) return hip_fail(se, "address of the library's device scratch");
+  duo::DecodeArgs a;
+  const int blocks = plan_decode(c, layer, q, out, scale, k, v, &a);
+  const size_t need = decode_records_bytes(c, blocks);
+  if (need > duo::kStaticScratchBytes)
+    return fail(DUO_EWORKSPACE,
+                "this decode writes %zu bytes of partial results (%d work items); the library's device scratch "
+                "holds %zu: use duo_decode_append with a workspace",
+                need, blocks, duo::kStaticScratchBytes);
+  if (int r = flush_pending(c, layer, static_cast<hipStream_t>(stream))) return r;
+  if (int r = reserve_pages(c, layer, -1, 1, static_cast<hipStream_t>(stream))) return r;
+  const hipError_t e = launch_planned_decode(c, a, blocks, scratch, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   for (int b = 0; b < c->cfg.B; ++b) c->len(layer, b) += 1;
   return ok();

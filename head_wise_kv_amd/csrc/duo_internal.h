@@ -194,6 +194,13 @@ struct RopeArgs {
   Rope rope;
 };
 
+// The allocation-free decode's partial records live in a file-scope device
+// array of this many bytes (duo_kernels.hip), one copy per device.
+constexpr size_t kStaticScratchBytes = size_t{8} << 20;
+// Device address of that array on the current device (looked up once per
+// device, then cached).
+hipError_t static_scratch(void** ptr);
+
 // Launchers (duo_kernels.hip, duo_prefill.hip, duo_gated.hip).  dtype: 0 = fp32, 1 = bf16.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_fill_ones(void* p, size_t bytes, hipStream_t s);  // every byte 0xFF (int32 -1)

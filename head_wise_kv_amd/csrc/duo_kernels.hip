@@ -24,6 +24,7 @@
 #include <algorithm>
 #include <climits>
 #include <cstddef>
+#include <mutex>
 #include <type_traits>
 
 namespace duo {
@@ -1604,6 +1605,34 @@ int64_t round_rows_d(int g) {
 }
 
 }  // namespace
+
+// Partial records of duo_decode_append_noalloc.  In host code `scratch` only
+// names the variable; its device address comes from hipGetSymbolAddress, once
+// per device (each device holds its own copy), and only that address is
+// passed to kernels.
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_table_update(const TableUpdateArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;

@@ -204,6 +204,22 @@ int duo_decode(duo_cache* c, int layer, const void* q, void* out, float scale, v
 int duo_decode_append(duo_cache* c, int layer, const void* k, const void* v, const void* q, void* out,
                       float scale, void* ws, size_t ws_bytes, void* stream);
 
+/* duo_decode_append for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same launch, result and cache state, but the partial
+ * softmax records go to a device array inside the library instead of a
+ * caller workspace.  That array holds 8 MiB on each GPU the library runs on
+ * (it is part of the loaded code object and stays until the process ends);
+ * a call whose work items need more (about 2,000 work items at g = 8,
+ * d_head = 128) fails with DUO_EWORKSPACE and changes no state, and
+ * duo_decode_append with a workspace serves it.  The call allocates nothing.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind (no call reads what an earlier one left): calls that may run at the
+ * same time on one GPU (other streams, other caches, other threads) race on
+ * it and must be ordered by the caller.  Other errors as duo_decode_append. */
+int duo_decode_append_noalloc(duo_cache* c, int layer, const void* k, const void* v, const void* q, void* out,
+                              float scale, void* stream);
+
 /* Chunked prefill of C >= 1 tokens on `layer`, at positions P .. P+C-1 with
  * P = the rows' token count, equal in every row (DUO_EINVAL otherwise)
  * ("Attention Variants and KV-Cache Compression", "When Is Reuse
