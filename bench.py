@@ -407,7 +407,7 @@ def main():
         torch.cuda.synchronize()
         log("calibration copy: 1073741824 bytes read, 1073741824 bytes written")
         del a, b
-    r = bench_decode(w, args.steps, args.warmup, L)
+    r = bench_decode(w, args.steps, args.warmup, L, copies=MALL_COPIES.get(w.name, 1))
     value = r["step_bytes"] / (r["ms_step"] * 1e-3) / 1e9
     achieved = r["decode_avg_bytes"] / r["decode_avg_s"] / 1e9
     traffic = stored_traffic(f"decode_{w.name}_traffic.txt", src_hash(KERNEL_SRC))
