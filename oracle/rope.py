@@ -33,8 +33,8 @@ theta = 10^4 (frequencies 1, 0.1, 0.01, 0.001 exactly), the complex-number
 form of the rotation, the relative-position property of scores, the bf16
 rounding against torch's conversion, decode over the cache's slots
 against the definition route over logical positions, and chunked prefill over
-FP8 rows against an enumeration built from the complex-number rotation,
-torch's bf16 rounding and torch's E4M3 conversion.
+FP8 and INT4 rows against enumerations built from the complex-number
+rotation, torch's bf16 rounding and torch's E4M3 conversion or rounding.
 """
 from __future__ import annotations
 
@@ -78,24 +78,36 @@ def round_to(x, dtype: str) -> np.ndarray:
     return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
 
 
+def _low_bit_store(kv_format):
+    """What a cache of low-bit rows keeps for float32 rows (None: as given)."""
+    if kv_format == "fp8":
+        from . import quant as _q
+        return _q.stored_values
+    if kv_format == "int4":
+        from . import quant4 as _q4
+        return _q4.stored_values_int4
+    return None
+
+
 def stored_keys(K, theta: float, dtype: str, kv_format=None) -> np.ndarray:
     """K [n_kv][T][d] (row = position) -> what the cache holds: each row
     rotated at its position and rounded to the cache dtype, float64.  With
-    FP8 rows (oracle.quant) the rotated, rounded row is what is quantized."""
+    FP8 rows (oracle.quant) or INT4 rows (oracle.quant4) the rotated, rounded
+    row is what is quantized."""
     K = np.asarray(K, dtype=np.float64)
     Ks = round_to(rotate(K, np.arange(K.shape[-2]), theta), dtype)
-    if kv_format == "fp8":
-        from . import quant as _q
-        Ks = _q.stored_values(Ks.astype(np.float32))
+    store = _low_bit_store(kv_format)
+    if store is not None:
+        Ks = store(Ks.astype(np.float32))
     return Ks
 
 
 def stored_values(V, kv_format=None) -> np.ndarray:
     """What the cache holds for value rows V (float32 inputs): as given, or
-    dequantized FP8 rows."""
-    if kv_format == "fp8":
-        from . import quant as _q
-        return _q.stored_values(np.asarray(V, dtype=np.float32))
+    the dequantized low-bit rows."""
+    store = _low_bit_store(kv_format)
+    if store is not None:
+        return store(np.asarray(V, dtype=np.float32))
     return np.asarray(V, dtype=np.float64)
 
 
@@ -128,7 +140,7 @@ def prefill_chunked_rope(Q, K, V, mask: Sequence[int], S: int, W: int, scale: fl
     Qr = rotate(Q, np.arange(N), theta)
     Kr = rotate(K, np.arange(N), theta)
     Ks = stored_keys(K, theta, dtype, kv_format)
-    Vs = stored_values(V.astype(np.float32) if kv_format == "fp8" else V, kv_format)
+    Vs = stored_values(V.astype(np.float32) if kv_format else V, kv_format)
     out = np.empty((n_q, N, d), dtype=np.float64)
     heads = [_cache.make_head_cache(bool(mask[k]), S, W) for k in range(n_kv)]
     P = 0

@@ -19,6 +19,7 @@ from oracle import gating as G
 from oracle import paging as PG
 from oracle import rope as RP
 from oracle import quant as QZ
+from oracle import quant4 as Q4
 from oracle import sizes as Z
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -483,6 +484,100 @@ def check_rope_fp8_prefill_held_rows():
         assert np.abs(as_given - want).max() > 1e-3
 
 
+# ------------------------------------------------------------------ INT4 rows
+
+def check_int4_golden_rows():
+    # the level table and rows worked by hand (tests/golden/int4_rows.txt)
+    lines = [ln for ln in open(os.path.join(GOLDEN, "int4_rows.txt")) if ln.strip() and not ln.startswith("#")]
+    levels = [int(v) for v in lines[0].split()[1:]]
+    assert Q4.int4_levels().tolist() == levels == list(range(-8, 8))
+    assert np.array_equal(Q4.unpack_nibbles(Q4.pack_nibbles(np.arange(16, dtype=np.uint8))), np.arange(16))
+    for ln in lines[1:]:
+        x, sc, lv, by = [part.split() for part in ln[4:].split("|")]
+        codes, scale = Q4.quantize_rows_int4(np.array([float(v) for v in x], dtype=np.float32)[None])
+        assert scale[0] == np.float32(float(sc[0])), (x, scale)
+        assert Q4.int4_levels()[codes[0].astype(np.int64)].tolist() == [int(v) for v in lv], (x, codes)
+        assert [f"{b:02x}" for b in Q4.pack_nibbles(codes[0])] == by, (x, Q4.pack_nibbles(codes[0]))
+        assert np.array_equal(Q4.unpack_nibbles(Q4.pack_nibbles(codes)), codes)
+
+
+def _int4_stored_by_library(X):
+    """What a row-scaled INT4 cache holds for float32 rows X, built with
+    torch's round (half to even): s = max|x| / 7 and x / s in float32."""
+    X = np.asarray(X, dtype=np.float32)
+    s = (np.max(np.abs(X), axis=-1) / np.float32(7.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    y = np.ascontiguousarray((X / safe[..., None]).astype(np.float32))
+    c = torch.round(torch.from_numpy(y)).clamp(-7, 7).double().numpy()
+    return np.where(s[..., None] > 0, c * s[..., None].astype(np.float64), 0.0)
+
+
+def check_int4_row_quantizer():
+    rng = np.random.default_rng(73)
+    X = (rng.standard_normal((400, 64)) * np.exp(rng.uniform(-8, 8, (400, 1)))).astype(np.float32)
+    X[3] = 0.0
+    X[7, :] = np.resize(np.array([7, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5], np.float32), 64)  # s = 1: ties
+    codes, scale = Q4.quantize_rows_int4(X)
+    assert np.array_equal(scale, (np.max(np.abs(X), axis=1) / np.float32(7.0)).astype(np.float32))
+    assert scale[3] == 0 and np.all(codes[3] == 8)
+    assert codes.min() >= 1 and codes.max() <= 15            # level -8 never produced
+    R = Q4.dequantize_rows_int4(codes, scale)
+    assert np.array_equal(R, _int4_stored_by_library(X))    # torch's rounding, independently
+    # within half a step (plus the float32 rounding of x / s)
+    x64 = X.astype(np.float64)
+    assert np.all(np.abs(R - x64) <= scale[:, None].astype(np.float64) * (0.5 + 2.0 ** -20))
+    # the largest element of every nonzero row takes level +-7
+    big = np.argmax(np.abs(X), axis=1)
+    nz = scale > 0
+    assert np.all(np.abs(Q4.int4_levels()[codes[np.arange(400), big].astype(np.int64)][nz]) == 7)
+    # rows on the grid (levels times a power of two, a level 7 in each) come back exactly
+    lv = rng.integers(-7, 8, (10, 64)).astype(np.float64)
+    lv[:, 0] = 7
+    grid = (lv * 0.25).astype(np.float32)
+    c2, s2 = Q4.quantize_rows_int4(grid)
+    assert np.all(s2 == np.float32(0.25)) and np.array_equal(Q4.dequantize_rows_int4(c2, s2), lv * 0.25)
+
+
+def check_int4_attention_routes():
+    rng = np.random.default_rng(83)
+    n_q, n_kv, N, d, S, W = 4, 2, 23, 8, 2, 5
+    # on the grid the INT4 routes are the native ones
+    lvk = rng.integers(-7, 8, (n_kv, N, d)).astype(np.float64); lvk[..., 0] = 7
+    lvv = rng.integers(-7, 8, (n_kv, N, d)).astype(np.float64); lvv[..., 0] = -7
+    K, V = (lvk * 0.5).astype(np.float32), (lvv * 0.125).astype(np.float32)
+    Q = rng.standard_normal((n_q, N, d)) * 0.3
+    for mask in ([1, 0], [0, 1]):
+        ref = A.prefill_full(Q, K, V, mask, S, W, 0.3)
+        for C in (1, 5, N):
+            assert np.allclose(Q4.prefill_chunked_int4(Q, K, V, mask, S, W, 0.3, C), ref, atol=1e-12, rtol=0)
+        assert np.allclose(Q4.decode_step_int4(Q[:, -1], K, V, mask, S, W, 0.3), ref[:, -1], atol=1e-12, rtol=0)
+    # off the grid, over several chunks: held rows as stored, the chunk's own as given
+    chunks = [5, 7, 4, 7]
+    K2 = rng.standard_normal((n_kv, N, d)).astype(np.float32)
+    V2 = rng.standard_normal((n_kv, N, d)).astype(np.float32)
+    Ks, Vs = _int4_stored_by_library(K2), _int4_stored_by_library(V2)
+    K64, V64 = K2.astype(np.float64), V2.astype(np.float64)
+    for mask in ([1, 0], [0, 1]):
+        want = _chunked_by_enumeration(Q, Ks, K64, Vs, V64, mask, S, W, 0.35, chunks)
+        got = Q4.prefill_chunked_int4(Q, K2, V2, mask, S, W, 0.35, chunks)
+        assert np.allclose(got, want, atol=1e-12, rtol=0), float(np.abs(got - want).max())
+        assert np.abs(_chunked_by_enumeration(Q, K64, K64, V64, V64, mask, S, W, 0.35, chunks) - want).max() > 1e-3
+        kv = [A.kv_head_of(h, n_q, n_kv) for h in range(n_q)]
+        dq = np.stack([A.attend_row_bruteforce(Q[h, N - 1].tolist(), Ks[kv[h]].tolist(), Vs[kv[h]].tolist(), N - 1,
+                                               bool(mask[kv[h]]), S, W, 0.35) for h in range(n_q)])
+        got_d = Q4.decode_step_int4(Q[:, N - 1], K2, V2, mask, S, W, 0.35)
+        assert np.allclose(got_d, dq, atol=1e-12, rtol=0), float(np.abs(got_d - dq).max())
+    # rotary positions over INT4 rows: held keys rotated, rounded to bf16, then stored
+    theta, chunks = 1e4, [6, 1, 9, 7]
+    Kr = _rotate_by_complex(K2, np.arange(N), theta)
+    Kb = torch.from_numpy(Kr.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    Qr = _rotate_by_complex(Q, np.arange(N), theta)
+    want = _chunked_by_enumeration(Qr, _int4_stored_by_library(Kb), Kr, _int4_stored_by_library(V2), V64, [1, 0], S,
+                                   W, 0.35, chunks)
+    got = RP.prefill_chunked_rope(Q, K2, V2, [1, 0], S, W, 0.35, theta, "bf16", chunks, kv_format="int4")
+    assert np.allclose(got, want, atol=1e-9, rtol=0), float(np.abs(got - want).max())
+
+
 # ------------------------------------------------------------------ paged rows
 
 def check_paging_closed_forms():
@@ -637,6 +732,7 @@ ALL_CHECKS = [
     check_gated_hand_case, check_gated_library_endpoints, check_gated_bruteforce_agrees,
     check_gated_gqa_expansion, check_e4m3_against_library, check_fp8_row_quantizer,
     check_fp8_attention_routes, check_fp8_prefill_held_rows, check_rope_fp8_prefill_held_rows,
+    check_int4_golden_rows, check_int4_row_quantizer, check_int4_attention_routes,
     check_paging_closed_forms, check_paging_capacity,
     check_rope_unit_vectors, check_rope_complex_form, check_rope_relative_positions,
     check_bf16_rounding_against_library, check_rope_cache_route_uses_logical_positions,

@@ -9,6 +9,7 @@ from oracle import gating as G
 from oracle import paging as PG
 from oracle import rope as RP
 from oracle import quant as QZ
+from oracle import quant4 as Q4
 from oracle import sizes as Z
 from tests import oracle_checks as OC
 
@@ -163,6 +164,55 @@ def _rope_fp8_held_unquantized(Q, K, V, mask, S, W, scale, theta, dtype, chunks,
     return _orig_prefill_rope(Q, K, V, mask, S, W, scale, theta, dtype, chunks, kv_format=None)  # FP8 dropped
 
 
+_orig_q4 = Q4.quantize_rows_int4
+
+
+def _int4_ties_up(X):
+    X = np.asarray(X, dtype=np.float32)
+    scale = (np.max(np.abs(X), axis=-1) / np.float32(7.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    c = np.floor((X / safe[..., None]).astype(np.float32).astype(np.float64) + 0.5)  # ties rounded up
+    c = np.where(scale[..., None] > 0, np.clip(c, -7, 7), 0.0)
+    return (c + 8).astype(np.uint8), scale
+
+
+def _int4_scale_8(X):
+    X = np.asarray(X, dtype=np.float32)
+    codes, _ = _orig_q4(X)
+    scale = (np.max(np.abs(X), axis=-1) / np.float32(8.0)).astype(np.float32)  # wrong range
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    c = np.clip(np.rint((X / safe[..., None]).astype(np.float32).astype(np.float64)), -7, 7)
+    return (np.where(scale[..., None] > 0, c, 0.0) + 8).astype(np.uint8), scale
+
+
+def _int4_nibbles_swapped(codes):
+    c = np.asarray(codes, dtype=np.uint8)
+    return ((c[..., 0::2] << 4) | c[..., 1::2]).astype(np.uint8)  # element 2k in the high nibble
+
+
+def _int4_levels_offset7():
+    return np.arange(16, dtype=np.int64) - 7
+
+
+def _int4_prefill_held_as_given(Q, K, V, mask, S, W, scale, chunk):
+    Q = np.asarray(Q, dtype=np.float64)
+    K64, V64 = np.asarray(K, dtype=np.float64), np.asarray(V, dtype=np.float64)
+    n_q, N, d = Q.shape
+    n_kv = K.shape[0]
+    out = np.empty((n_q, N, d))
+    lengths = [chunk] * ((N + chunk - 1) // chunk) if np.isscalar(chunk) else list(chunk)
+    P = 0
+    for C in lengths:
+        C = int(min(C, N - P))
+        for h in range(n_q):
+            k = A.kv_head_of(h, n_q, n_kv)
+            kp = np.asarray(Cc.kept_positions(P, bool(mask[k]), S, W) + list(range(P, P + C)), dtype=np.int64)
+            out[h, P:P + C] = A.attend_rows(Q[h, P:P + C], np.arange(P, P + C), K64[k][kp], V64[k][kp], kp,
+                                            bool(mask[k]), S, W, scale)   # held rows as given
+        P += C
+    return out
+
+
 MUTATIONS = {
     "window_too_wide": (A, "visible_matrix", _window_too_wide),
     "sinks_off_by_one": (A, "visible_matrix", _sinks_off_by_one),
@@ -187,6 +237,11 @@ MUTATIONS = {
     "rope_query_unrotated": (RP, "decode_step_rope", _decode_query_unrotated),
     "fp8_held_as_given": (QZ, "prefill_chunked_fp8", _fp8_prefill_held_as_given),
     "rope_fp8_held_unquantized": (RP, "prefill_chunked_rope", _rope_fp8_held_unquantized),
+    "int4_ties_up": (Q4, "quantize_rows_int4", _int4_ties_up),
+    "int4_scale_range": (Q4, "quantize_rows_int4", _int4_scale_8),
+    "int4_nibbles_swapped": (Q4, "pack_nibbles", _int4_nibbles_swapped),
+    "int4_levels_offset": (Q4, "int4_levels", _int4_levels_offset7),
+    "int4_held_as_given": (Q4, "prefill_chunked_int4", _int4_prefill_held_as_given),
 }
 
 
