@@ -382,6 +382,7 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="limit layers (profiling only; 0 = all)")
     ap.add_argument("--also", default="tiny_decode,llama3_8b_decode_b8_32k,"
                                       "mha7b_decode_128k,gqa70b_decode_128k_fp8,mha7b_decode_128k_fp8,"
+                                      "gqa70b_decode_128k_int4,mha7b_decode_128k_int4,"
                                       "gqa70b_decode_128k_paged,gqa70b_decode_128k_rope,"
                                       "gqa70b_decode_128k_full,mha7b_decode_128k_full",
                     help="comma-separated extra decode workloads reported under 'also' ('' for none)")

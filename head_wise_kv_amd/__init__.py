@@ -20,7 +20,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libduo.so"
 
 DUO_OK, DUO_EINVAL, DUO_EUNSUPPORTED, DUO_ECAPACITY, DUO_EEMPTY, DUO_EWORKSPACE, DUO_EHIP = 0, -1, -2, -3, -4, -5, -6
 DUO_F32, DUO_BF16 = 0, 1
-DUO_KV_NATIVE, DUO_KV_FP8 = 0, 1
+DUO_KV_NATIVE, DUO_KV_FP8, DUO_KV_INT4 = 0, 1, 2
 ERROR_NAMES = {DUO_EINVAL: "DUO_EINVAL", DUO_EUNSUPPORTED: "DUO_EUNSUPPORTED", DUO_ECAPACITY: "DUO_ECAPACITY",
                DUO_EEMPTY: "DUO_EEMPTY", DUO_EWORKSPACE: "DUO_EWORKSPACE", DUO_EHIP: "DUO_EHIP"}
 
@@ -114,6 +114,8 @@ def _kv_code(kv_format) -> int:
         return DUO_KV_NATIVE
     if kv_format in (1, "fp8"):
         return DUO_KV_FP8
+    if kv_format in (2, "int4"):
+        return DUO_KV_INT4
     if isinstance(kv_format, int):
         return kv_format  # passed through; the library rejects unknown codes
     raise ValueError(f"unknown kv_format {kv_format}")
@@ -160,7 +162,8 @@ class DuoCache:
     scale per row (bf16 caches with d_head 128).  page_rows > 0 stores the
     retrieval rows in pages (n_pages per layer) that rows take as they grow
     and can share (fork_row).  rope_theta > 0 applies rotary positions (keys
-    stored rotated, queries rotated by decode and prefill).
+    stored rotated, queries rotated by decode and prefill).  kv_format
+    "int4" stores 4-bit codes (two per byte) with one scale per row.
     """
 
     def __init__(self, L: int, B: int, n_q: int, n_kv: int, d_head: int, T_cap: int, sink: int, recent: int,
@@ -401,11 +404,12 @@ class DuoCache:
         hv = self.head_view(layer, kv_head)
         base = self.arena.data_ptr()
         es = 2 if self.torch_dtype == torch.bfloat16 else 4
-        if self.kv_format == DUO_KV_FP8:
-            es = 1
+        if self.kv_format in (DUO_KV_FP8, DUO_KV_INT4):
+            es = 1  # codes as bytes (INT4: two per byte, d / 2 per row)
+        width = hv["row_bytes"] // es
         if self._paged_head(hv):
             kv = [self._gather_pages(layer, hv[key] - base, hv["head_stride_bytes"], hv["row_bytes"])
-                  .view(torch.uint8 if es == 1 else self.torch_dtype).reshape(self.B, -1, self.d)
+                  .view(torch.uint8 if es == 1 else self.torch_dtype).reshape(self.B, -1, width)
                   for key in ("k_base", "v_base")]
             return kv[0], kv[1], None
         rows = hv["n_slots"]
@@ -414,7 +418,7 @@ class DuoCache:
             off = hv[key] - base
             seg = torch.stack([self.arena[off + b * hv["head_stride_bytes"]: off + b * hv["head_stride_bytes"]
                                           + rows * hv["row_bytes"]] for b in range(self.B)])
-            out.append(seg.cpu().view(torch.uint8 if es == 1 else self.torch_dtype).reshape(self.B, rows, self.d))
+            out.append(seg.cpu().view(torch.uint8 if es == 1 else self.torch_dtype).reshape(self.B, rows, width))
         pos = None
         if hv["pos"]:
             off = hv["pos"] - base

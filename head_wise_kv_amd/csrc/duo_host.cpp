@@ -76,16 +76,19 @@ int validate(const duo_config* c) {
     return fail(DUO_EUNSUPPORTED, "group size g = %d not built (1, 2, 4, 8)", c->n_q / c->n_kv);
   if (c->d_head != 64 && c->d_head != 128) return fail(DUO_EUNSUPPORTED, "d_head %d not built (64, 128)", c->d_head);
   if (c->dtype != DUO_F32 && c->dtype != DUO_BF16) return fail(DUO_EUNSUPPORTED, "dtype %d", c->dtype);
-  if (c->kv_format != DUO_KV_NATIVE && c->kv_format != DUO_KV_FP8)
+  if (c->kv_format != DUO_KV_NATIVE && c->kv_format != DUO_KV_FP8 && c->kv_format != DUO_KV_INT4)
     return fail(DUO_EUNSUPPORTED, "kv_format %d", c->kv_format);
-  if (c->kv_format == DUO_KV_FP8 && (c->dtype != DUO_BF16 || c->d_head != 128))
-    return fail(DUO_EUNSUPPORTED, "FP8 K/V rows are built for bf16 and d_head 128");
+  if (c->kv_format != DUO_KV_NATIVE && (c->dtype != DUO_BF16 || c->d_head != 128))
+    return fail(DUO_EUNSUPPORTED, "FP8 and INT4 K/V rows are built for bf16 and d_head 128");
   if (c->T_cap < 1) return fail(DUO_EINVAL, "T_cap must be >= 1");
   if (c->T_cap > INT32_MAX) return fail(DUO_EINVAL, "T_cap must fit int32 (positions are int32)");
   if (c->page_rows != 0) {
     if (c->page_rows < 256 || c->page_rows > (1 << 20) || (c->page_rows & (c->page_rows - 1)) != 0)
       return fail(DUO_EINVAL, "page_rows %d must be 0 or a power of two in [256, 2^20]", c->page_rows);
     if (c->n_pages < 1) return fail(DUO_EINVAL, "a paged cache needs n_pages >= 1 (got %d)", c->n_pages);
+    // a decode round of rows (INT4: 512) must lie within one page
+    if (c->kv_format == DUO_KV_INT4 && c->page_rows < 512)
+      return fail(DUO_EUNSUPPORTED, "INT4 rows need pages of at least 512 rows (got %d)", c->page_rows);
   } else if ((uint64_t)c->T_cap * (uint64_t)c->d_head * (c->dtype == DUO_BF16 ? 2u : 4u) > 0xffffffffull) {
     return fail(DUO_EUNSUPPORTED, "one head's rows (T_cap * d_head * element size) must fit 4 GiB");
   }
@@ -99,8 +102,13 @@ int validate(const duo_config* c) {
 }
 
 int elem_bytes(const duo_config* c) { return c->dtype == DUO_BF16 ? 2 : 4; }
-// bytes per stored K/V element (FP8 rows: one byte)
-int kv_elem_bytes(const duo_config* c) { return c->kv_format == DUO_KV_FP8 ? 1 : elem_bytes(c); }
+// bytes per stored K/V row: d elements in the cache dtype, d FP8 codes, or d
+// INT4 codes two to a byte
+int kv_row_bytes(const duo_config* c) {
+  if (c->kv_format == DUO_KV_FP8) return c->d_head;
+  if (c->kv_format == DUO_KV_INT4) return c->d_head / 2;
+  return c->d_head * elem_bytes(c);
+}
 
 size_t decode_rec_floats(const duo_config* c) {  // acc[g][d], max[g], sum[g], padded to 16 bytes
   const int g = c->n_q / c->n_kv;
@@ -108,8 +116,8 @@ size_t decode_rec_floats(const duo_config* c) {  // acc[g][d], max[g], sum[g], p
 }
 
 void make_plan(const duo_config* c, Plan* p) {
-  const size_t row = (size_t)c->d_head * kv_elem_bytes(c);
-  const bool fp8 = c->kv_format == DUO_KV_FP8;
+  const size_t row = (size_t)kv_row_bytes(c);
+  const bool lowbit = c->kv_format != DUO_KV_NATIVE;  // rows carry an fp32 scale each
   size_t dequant = 0;
   const int64_t cap_str = (int64_t)c->sink + c->recent;
   p->layers.assign(c->L, LayerPlan{});
@@ -146,7 +154,7 @@ void make_plan(const duo_config* c, Plan* p) {
       off = align_up(off + (size_t)c->B * ceil_div(c->T_cap, c->page_rows) * sizeof(int32_t));
     }
     p->payload += 2 * (ret_bytes + str_bytes);
-    if (fp8) {
+    if (lowbit) {
       const size_t ret_sc = ret_rows * lp.n_ret * sizeof(float);
       const size_t str_sc = (size_t)c->B * lp.n_str * cap_str * sizeof(float);
       lp.off_skr = off; off = align_up(off + ret_sc);
@@ -203,11 +211,11 @@ struct duo_cache {
     p.k_str = arena + lp.off_ks;
     p.v_str = arena + lp.off_vs;
     p.pos = reinterpret_cast<int32_t*>(arena + lp.off_pos);
-    const bool fp8 = cfg.kv_format == DUO_KV_FP8;
-    p.ksc_ret = fp8 ? reinterpret_cast<float*>(arena + lp.off_skr) : nullptr;
-    p.vsc_ret = fp8 ? reinterpret_cast<float*>(arena + lp.off_svr) : nullptr;
-    p.ksc_str = fp8 ? reinterpret_cast<float*>(arena + lp.off_sks) : nullptr;
-    p.vsc_str = fp8 ? reinterpret_cast<float*>(arena + lp.off_svs) : nullptr;
+    const bool lb = cfg.kv_format != DUO_KV_NATIVE;
+    p.ksc_ret = lb ? reinterpret_cast<float*>(arena + lp.off_skr) : nullptr;
+    p.vsc_ret = lb ? reinterpret_cast<float*>(arena + lp.off_svr) : nullptr;
+    p.ksc_str = lb ? reinterpret_cast<float*>(arena + lp.off_sks) : nullptr;
+    p.vsc_str = lb ? reinterpret_cast<float*>(arena + lp.off_svs) : nullptr;
     p.table = paged(l) ? reinterpret_cast<int32_t*>(arena + lp.off_tab) : nullptr;
     p.max_pages = paged(l) ? (int32_t)max_pages() : 0;
     p.page_shift = paged(l) ? page_shift() : 0;
@@ -276,9 +284,11 @@ struct duo_cache {
     const size_t row = (size_t)cfg.d_head * elem_bytes(&cfg);
     return align_up((size_t)B * cfg.n_q * C * row) + align_up((size_t)B * cfg.n_kv * C * row);
   }
-  int row_bytes() const { return cfg.d_head * kv_elem_bytes(&cfg); }     // stored K/V row
+  int row_bytes() const { return kv_row_bytes(&cfg); }                  // stored K/V row
   int in_row_bytes() const { return cfg.d_head * elem_bytes(&cfg); }     // input / query row
-  bool fp8() const { return cfg.kv_format == DUO_KV_FP8; }
+  // low-bit rows (FP8 or INT4 codes with one fp32 scale per row)
+  bool lowbit() const { return cfg.kv_format != DUO_KV_NATIVE; }
+  int kvfmt() const { return cfg.kv_format; }
 };
 
 namespace {
@@ -404,7 +414,7 @@ hipError_t enqueue_append(duo_cache* c, int layer, const void* k, const void* v,
   a.dtype = c->cfg.dtype;
   a.d = c->cfg.d_head;
   if (rotate) a.rope = c->rope();  // else the keys come rotated already
-  hipError_t e = duo::launch_append(a, c->cfg.dtype, c->cfg.d_head, c->fp8(), s);
+  hipError_t e = duo::launch_append(a, c->cfg.dtype, c->cfg.d_head, c->kvfmt(), s);
   if (e != hipSuccess || !device_p0) return e;
   duo::AdvanceArgs adv{};
   adv.lp = a.lp;
@@ -594,7 +604,7 @@ int plan_decode(const duo_cache* c, int layer, const void* q, void* out, float s
   const int g = cf.n_q / cf.n_kv;
   const int64_t heads = (int64_t)cf.B * (lp.n_ret + lp.n_str);
   const int64_t slots = std::max<int64_t>(std::min(c->num_cu, duo::kMaxDecodeBlocks), heads);
-  const int64_t R0 = duo::decode_round_rows(cf.dtype, cf.d_head, g, c->fp8());
+  const int64_t R0 = duo::decode_round_rows(cf.dtype, cf.d_head, g, c->kvfmt());
   const bool paged = a.lp.table != nullptr;
   auto items = [&](int64_t rows, int64_t t) { return std::max<int64_t>(1, ceil_div(rows, t)); };
   // A paged head's items start at multiples of R0 rows (the kernel rounds
@@ -648,7 +658,7 @@ size_t decode_records_bytes(const duo_cache* c, int blocks) {
 hipError_t launch_planned_decode(const duo_cache* c, duo::DecodeArgs& a, int blocks, void* ws, hipStream_t stream) {
   a.ws1 = static_cast<float*>(ws);
   const int g = c->cfg.n_q / c->cfg.n_kv;
-  return duo::launch_decode(a, c->cfg.dtype, c->cfg.d_head, g, c->fp8(), blocks, stream);
+  return duo::launch_decode(a, c->cfg.dtype, c->cfg.d_head, g, c->kvfmt(), blocks, stream);
 }
 
 hipError_t enqueue_decode(duo_cache* c, int layer, const void* q, void* out, float scale, void* ws,
@@ -733,7 +743,7 @@ namespace {
 // rotated chunk after those.  0 if none.
 size_t prefill_ws_bytes(const duo_cache* c, int64_t B, int64_t C) {
   if (c->rope().on) return c->plan.workspace + c->rope_ws_bytes(B, C);
-  return c->fp8() ? c->plan.workspace : 0;
+  return c->lowbit() ? c->plan.workspace : 0;
 }
 
 // Chunked prefill of every batch row (row < 0; the rows must hold equal
@@ -791,7 +801,7 @@ int prefill_impl(duo_cache* c, int layer, int row, const void* q, const void* k,
   // pages for the chunk's rows (the attention reads only the held rows)
   if (int r = reserve_pages(c, layer, row, C, s)) return r;
   hipError_t e = hipSuccess;
-  if (c->fp8()) {
+  if (c->lowbit()) {
     // the held rows, dequantized to bf16 in the workspace (after the decode
     // records), stand in for the cache's rows during the attention
     const int64_t cap_r = std::max<int64_t>(P, 1);
@@ -815,6 +825,7 @@ int prefill_impl(duo_cache* c, int layer, int row, const void* q, const void* k,
     d.rows_str = a.held_str;
     d.d = cf.d_head;
     d.n_ret = lp.n_ret;
+    d.int4 = cf.kv_format == DUO_KV_INT4 ? 1 : 0;
     e = duo::launch_dequant(d, s);
     if (e != hipSuccess) return hip_fail(e, "dequant launch");
     a.lp.k_ret = d.dst.k_ret;
@@ -941,7 +952,7 @@ int duo_cache_fork_row(duo_cache* c, int layer, int src_row, int dst_row, void* 
     cp.seg[cp.n++] = duo::CopySegment{static_cast<const char*>(from), static_cast<char*>(to), bytes, count, stride,
                                       stride};
   };
-  const bool f8 = c->fp8();
+  const bool f8 = c->lowbit();  // rows carry scales
   if (c->paged(layer)) {
     duo_cache::Pages& pg = c->pages[layer];
     for (int32_t page : pg.rows[dst_row])  // spares left by a failed launch
@@ -1150,7 +1161,7 @@ int duo_cache_head_scales(const duo_cache* c, int layer, int kv_head, float** k_
   const int ci = lp.map.cidx[kv_head];
   const int64_t slots = ret ? (c->paged(layer) ? c->cfg.page_rows : c->cfg.T_cap) : c->cap_str();
   const int n_kind = ret ? lp.n_ret : lp.n_str;
-  const bool f8 = c->fp8();
+  const bool f8 = c->lowbit();  // rows carry scales
   if (k_scale) *k_scale = f8 ? (ret ? p.ksc_ret : p.ksc_str) + (size_t)ci * slots : nullptr;
   if (v_scale) *v_scale = f8 ? (ret ? p.vsc_ret : p.vsc_str) + (size_t)ci * slots : nullptr;
   if (scale_stride) *scale_stride = f8 ? (int64_t)n_kind * slots : 0;

@@ -208,7 +208,8 @@ hipError_t launch_advance(const AdvanceArgs& a, hipStream_t s);
 hipError_t launch_table_update(const TableUpdateArgs& a, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
 hipError_t launch_rope(const RopeArgs& a, hipStream_t s);
-hipError_t launch_append(const AppendArgs& a, int dtype, int d, bool fp8, hipStream_t s);
+// kvfmt: 0 = rows in the cache dtype, 1 = FP8 codes, 2 = INT4 codes (with row scales).
+hipError_t launch_append(const AppendArgs& a, int dtype, int d, int kvfmt, hipStream_t s);
 // FP8 caches: the held rows of one layer, dequantized to bf16 for prefill.
 struct DequantArgs {
   LayerPtrs src;               // codes and scales in the arena
@@ -218,13 +219,14 @@ struct DequantArgs {
   int64_t cap_str, rows_str;
   int d;
   int n_ret;
+  int int4;                    // rows are INT4 codes (two per byte) rather than FP8
 };
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
 // Split phase over `blocks` work items (retrieval heads' items first), then
 // the combine of heads cut into several items.
-hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int g, bool fp8, int blocks, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int g, int kvfmt, int blocks, hipStream_t s);
 // Rows one round of the decode kernel covers (a work item should span at least one).
-int64_t decode_round_rows(int dtype, int d, int g, bool fp8);
+int64_t decode_round_rows(int dtype, int d, int g, int kvfmt);
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int d, int g, hipStream_t s);
 // Query rows and query heads one prefill work item covers.
 void prefill_plan(int dtype, int d, int g, int* rows_per_item, int* heads_per_item);

@@ -333,18 +333,24 @@ constexpr int kPiecesPerWave = kUnitPieces / kDecWaves;     // 4
 static_assert(kUnitPieces % kDecWaves == 0, "unit pieces split evenly over the wavefronts");
 
 // KT: 0 = fp32 everywhere, 1 = bf16 everywhere, 2 = bf16 queries, inputs and
-// outputs with FP8 (E4M3) K/V rows in the cache plus one fp32 scale per row.
+// outputs with FP8 (E4M3) K/V rows in the cache plus one fp32 scale per row,
+// 3 = the same with INT4 rows (two codes per byte) plus one fp32 scale per row.
 template <int KT, int D, int G>
 struct DecodeCfg {
   static constexpr bool BF16 = KT != 0;          // queries, inputs, outputs in bf16
   static constexpr bool KV8 = KT == 2;           // K/V rows stored as FP8 codes + row scales
+  static constexpr bool KV4 = KT == 3;           // K/V rows stored as INT4 codes + row scales
+  static constexpr bool LOWBIT = KV8 || KV4;     // rows carry an fp32 scale each
   static constexpr int ES = BF16 ? 2 : 4;        // query / input / output element bytes
   static constexpr int IROWB = D * ES;           // bytes per query or input row
-  static constexpr int KES = KV8 ? 1 : ES;       // stored K/V element bytes
-  static constexpr int ROWB = D * KES;           // bytes per stored K/V row
+  static constexpr int KES = KV8 ? 1 : ES;       // stored K/V element bytes (INT4: half a byte)
+  static constexpr int ROWB = KV4 ? D / 2 : D * KES;  // bytes per stored K/V row
   static constexpr int CPR = ROWB / 16;          // 16-byte chunks per stored row
-  static constexpr int CPL = CPR / 8;            // chunks per lane
-  static constexpr int EPC = 16 / KES;           // elements per chunk
+  // Weighted sum: the 8 lanes of a row each take CPL pieces of the V row;
+  // INT4 rows (64 bytes) give each lane one 8-byte piece of 16 codes.
+  static constexpr int CPL = KV4 ? 1 : CPR / 8;  // V pieces per lane
+  static constexpr int EPC = KV4 ? 32 : 16 / KES;  // elements per 16-byte chunk
+  static constexpr int EPV = KV4 ? 16 : EPC;     // elements per V piece
   static constexpr int HW = G < 4 ? G : 4;       // query heads per wavefront
   static constexpr int HSPLIT = G / HW;          // wavefronts per slot
   static constexpr int SLOTS_W = kDecWaves / HSPLIT;
@@ -354,9 +360,9 @@ struct DecodeCfg {
   static constexpr int RPL = TR / 8;             // rows per lane
   static constexpr int SLOT_BYTES = TR * ROWB;
   static constexpr int ROUND_ROWS = SLOTS * TR;
-  static constexpr int NACC = CPL * EPC;         // output elements per lane per head
+  static constexpr int NACC = CPL * EPV;         // output elements per lane per head
   static constexpr int REC = (G * (D + 2) + 3) / 4 * 4;  // floats per partial record (16-byte multiple)
-  static_assert(CPR % 8 == 0, "rows must span a multiple of 8 chunks");
+  static_assert(KV4 ? (CPR == 4 && D == 128) : CPR % 8 == 0, "rows must span a multiple of 8 chunks");
   static_assert(RPL >= 2 && RPL % 2 == 0, "rows are paired for the weighted sum");
   static_assert(SLOT_BYTES % 1024 == 0, "a load piece stays within one tile");
   static_assert(G % HW == 0, "head split must tile the group");
@@ -455,9 +461,40 @@ __device__ __forceinline__ uint2 quant_row16(uint4 x, float& scale) {
   return make_uint2(fp8x4(y[0], y[1], y[2], y[3]), fp8x4(y[4], y[5], y[6], y[7]));
 }
 
-// Append to an FP8 cache: one group of 16 lanes per (batch row, KV head,
-// token, K or V) row, each lane taking 8 consecutive bf16 values.  Slot rules
-// as append_kernel.
+// INT4 rows: s = max|x| / 7 (a correctly rounded fp32 division) and c =
+// x / s (the same) rounded to the nearest integer, ties to even, kept in
+// -7 .. 7; the code c + 8 goes to a nibble, element 2k of the lane's 8 in the
+// low nibble of byte k.  A row of zeros has s = 0 and codes 8.  The row's 16
+// pieces sit in the 16 lanes of a DPP row, as for quant_row16.
+__device__ __forceinline__ uint32_t quant_row16_int4(uint4 x, float& scale) {
+  const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf_lo(w4[i]);
+    f[2 * i + 1] = bf_hi(w4[i]);
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+  m = fmaxf(m, dpp<0xB1>(m));   // quad_perm [1,0,3,2]
+  m = fmaxf(m, dpp<0x4E>(m));   // quad_perm [2,3,0,1]
+  m = fmaxf(m, dpp<0x141>(m));  // row_half_mirror
+  m = fmaxf(m, dpp<0x140>(m));  // row_mirror
+  scale = m / 7.f;
+  if (!(scale > 0.f)) return 0x88888888u;
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float c = fminf(fmaxf(rintf(f[i] / scale), -7.f), 7.f);
+    w |= (uint32_t)((int)c + 8) << (4 * i);
+  }
+  return w;
+}
+
+// Append to an FP8 or INT4 cache: one group of 16 lanes per (batch row, KV
+// head, token, K or V) row, each lane taking 8 consecutive bf16 values.  Slot
+// rules as append_kernel.
 // Rotary positions in decode: rows [0, nq) of the staging area (the group's
 // queries, row_bytes apart) and, if with_k, the new token's K row at k_row,
 // rotated in place; one thread per (row, dimension pair).  Every row turns by
@@ -523,7 +560,8 @@ __device__ __forceinline__ uint4 rope_row16(uint4 x, const Rope& r, int64_t p, i
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-__global__ void append_fp8_kernel(AppendArgs a) {
+template <bool INT4>
+__global__ void append_lowbit_kernel(AppendArgs a) {
   const int64_t rows = (int64_t)a.B * a.n_kv * a.n_new * 2;
   const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
   const int j = threadIdx.x & 15;
@@ -553,7 +591,10 @@ __global__ void append_fp8_kernel(AppendArgs a) {
   float sc;
   uint4 x = ld16((tensor ? a.v : a.k) + src);
   if (a.rope.on && tensor == 0) x = rope_row16(x, a.rope, p, j);  // the whole group takes this branch
-  const uint2 codes = quant_row16(x, sc);
+  uint2 codes = make_uint2(0u, 0u);
+  uint32_t codes4 = 0u;
+  if constexpr (INT4) codes4 = quant_row16_int4(x, sc);
+  else codes = quant_row16(x, sc);
   char* dst;
   float* sdst;
   if (a.map.kind[kvh]) {
@@ -570,12 +611,13 @@ __global__ void append_fp8_kernel(AppendArgs a) {
     sdst = (tensor ? a.lp.vsc_str : a.lp.ksc_str) + hrow;
     if (tensor == 0 && j == 0) a.lp.pos[hrow] = (int32_t)p;
   }
-  *reinterpret_cast<uint2*>(dst + j * 8) = codes;
+  if constexpr (INT4) *reinterpret_cast<uint32_t*>(dst + j * 4) = codes4;
+  else *reinterpret_cast<uint2*>(dst + j * 8) = codes;
   if (j == 0) *sdst = sc;
 }
 
-// FP8 rows -> bf16 rows (code value times the row scale, rounded to nearest
-// even), 8 values per thread.
+// FP8 or INT4 rows -> bf16 rows (code value times the row scale, rounded to
+// nearest even), 8 values per thread.
 __global__ void dequant_kernel(DequantArgs a) {
   const int pieces = a.d / 8;
   const int64_t n_ret = a.heads_ret * a.rows_ret, n_str = a.heads_str * a.rows_str;
@@ -593,27 +635,36 @@ __global__ void dequant_kernel(DequantArgs a) {
       const int64_t h = rr / a.rows_ret, r = rr % a.rows_ret;
       const int64_t srow = ret_row(a.src, a.n_ret, a.cap_ret_src, h / a.n_ret, (int)(h % a.n_ret), r);
       const int64_t drow = h * a.cap_ret_dst + r;
-      codes = reinterpret_cast<const uint8_t*>(tensor ? a.src.v_ret : a.src.k_ret) + srow * a.d;
+      codes = reinterpret_cast<const uint8_t*>(tensor ? a.src.v_ret : a.src.k_ret) + srow * (a.int4 ? a.d / 2 : a.d);
       sc = (tensor ? a.src.vsc_ret : a.src.ksc_ret) + srow;
       dst = reinterpret_cast<uint16_t*>(tensor ? a.dst.v_ret : a.dst.k_ret) + drow * a.d;
     } else {
       rr -= n_ret;
       const int64_t h = rr / a.rows_str, r = rr % a.rows_str;
       const int64_t row = h * a.cap_str + r;
-      codes = reinterpret_cast<const uint8_t*>(tensor ? a.src.v_str : a.src.k_str) + row * a.d;
+      codes = reinterpret_cast<const uint8_t*>(tensor ? a.src.v_str : a.src.k_str) + row * (a.int4 ? a.d / 2 : a.d);
       sc = (tensor ? a.src.vsc_str : a.src.ksc_str) + row;
       dst = reinterpret_cast<uint16_t*>(tensor ? a.dst.v_str : a.dst.k_str) + row * a.d;
     }
-    const uint2 c8 = *reinterpret_cast<const uint2*>(codes + pc * 8);
     const float s = *sc;
-    const uint32_t cw[2] = {c8.x, c8.y};
     uint32_t o[4];
+    if (a.int4) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + pc * 4);  // 8 nibbles
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[k], false);
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[k], true);
-      o[2 * k] = f32_to_bf16_bits(lo[0] * s) | (f32_to_bf16_bits(lo[1] * s) << 16);
-      o[2 * k + 1] = f32_to_bf16_bits(hi[0] * s) | (f32_to_bf16_bits(hi[1] * s) << 16);
+      for (int k = 0; k < 4; ++k) {
+        const float c0 = (float)((int)((w >> (8 * k)) & 15u) - 8), c1 = (float)((int)((w >> (8 * k + 4)) & 15u) - 8);
+        o[k] = f32_to_bf16_bits(c0 * s) | (f32_to_bf16_bits(c1 * s) << 16);
+      }
+    } else {
+      const uint2 c8 = *reinterpret_cast<const uint2*>(codes + pc * 8);
+      const uint32_t cw[2] = {c8.x, c8.y};
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[k], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[k], true);
+        o[2 * k] = f32_to_bf16_bits(lo[0] * s) | (f32_to_bf16_bits(lo[1] * s) << 16);
+        o[2 * k + 1] = f32_to_bf16_bits(hi[0] * s) | (f32_to_bf16_bits(hi[1] * s) << 16);
+      }
     }
     *reinterpret_cast<uint4*>(dst + pc * 8) = make_uint4(o[0], o[1], o[2], o[3]);
   }
@@ -770,6 +821,9 @@ struct DecodeState {
   using C = DecodeCfg<KT, D, G>;
   float m[C::HW], l[C::HW];
   float acc[C::HW][C::NACC];
+  // INT4 rows: the sum of the (rounded) weights the lane's weighted sum
+  // applied, times which the accumulators exceed the sum over the levels
+  float wsum[C::KV4 ? C::HW : 1];
 };
 
 // Scores of the lane's rows against its HW queries, online-softmax update,
@@ -942,7 +996,21 @@ __device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
 // K-tile chunk swizzle of the 4-lane layout: the 4 rows a group of 16 lanes
 // reads fall into 4 distinct quarters of the 256-byte bank space.
 template <int CPR>
-__device__ __forceinline__ int dec_swz_k4(int r) { return CPR >= 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+__device__ __forceinline__ int dec_swz_k4(int r) { return CPR >= 16 ? 4 * (r & 3) : CPR >= 8 ? 4 * ((r >> 1) & 1) : 0; }
+
+// INT4 codes to bf16 pairs.  A nibble n read as the low mantissa bits of
+// 0x4300 (the bf16 value 128) gives the bf16 value 128 + n = c + 136 exactly
+// (c = n - 8 is the level), so dot products over these pairs exceed the ones
+// over the levels by 136 times the other factor's sum, which the callers
+// subtract.  lo / hi hold the low / high nibbles of four code bytes, one per
+// byte; pair t takes byte t of lo (low half) and of hi (high half), i.e. the
+// elements 2t and 2t + 1 of the four bytes.
+template <int T>
+__device__ __forceinline__ uint32_t int4_pair(uint32_t lo, uint32_t hi) {
+  constexpr uint32_t sel = (uint32_t)T | (0x0Cu << 8) | ((4u + T) << 16) | (0x0Cu << 24);  // 0x0C: zero byte
+  return __builtin_amdgcn_perm(hi, lo, sel) | 0x43004300u;
+}
+constexpr float kInt4Bias = 136.f;  // (128 + n) - (n - 8)
 
 // all-reduce over the 4 lanes of a row
 __device__ __forceinline__ float row4_sum(float x) {
@@ -962,6 +1030,7 @@ template <int KT, int D, int G>
 __device__ __forceinline__ bool tile_scores4(float& m, float& l, uint16_t* pbuf, float* abuf, const char* kt,
                                              const uint4 (&q)[Score4<KT, D, G>::HW]
                                                              [Score4<KT, D, G>::CPL4 * Score4<KT, D, G>::QPC],
+                                             const float (&qbias)[Score4<KT, D, G>::HW],
                                              const float* ksc, const float* vsc, int nv, int excl, int r16, int s4,
                                              float scale_log2) {
   using C = DecodeCfg<KT, D, G>;
@@ -983,7 +1052,22 @@ __device__ __forceinline__ bool tile_scores4(float& m, float& l, uint16_t* pbuf,
 #pragma unroll
     for (int cc = 0; cc < S4::CPL4; ++cc) {
       const uint32_t kw[4] = {k[cc].x, k[cc].y, k[cc].z, k[cc].w};
-      if constexpr (C::KV8) {
+      if constexpr (C::KV4) {
+        // 32 codes: dword i holds elements 8i .. 8i+7, against query piece i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t lo = kw[i] & 0x0F0F0F0Fu, hi = (kw[i] >> 4) & 0x0F0F0F0Fu;
+          const uint32_t kb[4] = {int4_pair<0>(lo, hi), int4_pair<1>(lo, hi), int4_pair<2>(lo, hi),
+                                  int4_pair<3>(lo, hi)};
+#pragma unroll
+          for (int h = 0; h < HW; ++h) {
+            const uint4 qv = q[h][4 * cc + i];
+            const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[h] = dot2_bf16(qw[t], kb[t], acc[h]);
+          }
+        }
+      } else if constexpr (C::KV8) {
         // 16 codes -> 8 bf16 pairs (exact), dotted with the query's values
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1012,7 +1096,8 @@ __device__ __forceinline__ bool tile_scores4(float& m, float& l, uint16_t* pbuf,
     float own = acc[0];
 #pragma unroll
     for (int h = 1; h < HW; ++h) own = hown == h ? acc[h] : own;
-    if constexpr (C::KV8) own *= ksc[row];  // the K row's scale
+    if constexpr (C::KV4) own -= qbias[hown];     // the pairs' +136 times the query's sum
+    if constexpr (C::LOWBIT) own *= ksc[row];  // the K row's scale
     sc[j] = (row < nv && row != excl) ? own : -INFINITY;
   }
   // reference max of (rg, s4), shared with the partner lane 32 away
@@ -1035,15 +1120,15 @@ __device__ __forceinline__ bool tile_scores4(float& m, float& l, uint16_t* pbuf,
   for (int j = 0; j < S4::RPL4; ++j) {
     const float pj = fast_exp2(fmaf(sc[j], scale_log2, -mu));
     // FP8 rows: the V row's scale joins the probability the weighted sum uses
-    const float vs = C::KV8 ? vsc[r16 + 16 * j] : 1.f;
-    const uint16_t pb = bf16_bits(C::KV8 ? pj * vs : pj);
+    const float vs = C::LOWBIT ? vsc[r16 + 16 * j] : 1.f;
+    const uint16_t pb = bf16_bits(C::LOWBIT ? pj * vs : pj);
     const float pr = __uint_as_float((uint32_t)pb << 16);
     // The sum takes the weight the weighted sum really applies to the row --
     // the rounded probability (divided by the V row's scale for FP8 rows; a
     // zero row contributes nothing either way) -- so the weights of the result
     // sum to one: an unrounded sum would leave a relative error of up to 2^-9
     // in every output element.
-    l += C::KV8 ? (vs > 0.f ? pr * __builtin_amdgcn_rcpf(vs) : pj) : pr;
+    l += C::LOWBIT ? (vs > 0.f ? pr * __builtin_amdgcn_rcpf(vs) : pj) : pr;
     if (s4 < HW) pbuf[((rg * S4::NQ + j) * HW + s4) * 2 + half] = pb;
   }
   return any;
@@ -1064,6 +1149,7 @@ __device__ __forceinline__ void tile_pv4(DecodeState<KT, D, G>& st, const uint16
       const float al = abuf[rg * HW + h];
 #pragma unroll
       for (int e = 0; e < C::NACC; ++e) st.acc[h][e] *= al;
+      if constexpr (C::KV4) st.wsum[h] *= al;
     }
   }
 #pragma unroll
@@ -1073,6 +1159,34 @@ __device__ __forceinline__ void tile_pv4(DecodeState<KT, D, G>& st, const uint16
     const uint32_t* pq = reinterpret_cast<const uint32_t*>(pbuf) + (rg * S4::NQ + qq) * HW;
 #pragma unroll
     for (int h = 0; h < HW; ++h) P[h] = pq[h];
+    if constexpr (C::KV4) {
+      // lane s takes bytes 8s .. 8s+7 of both rows: elements 16s .. 16s+15,
+      // dword i of it elements 8i .. 8i+7 (pairs of one row's nibbles by
+      // element, then both rows' values of an element side by side)
+      const uint2 va = *reinterpret_cast<const uint2*>(vt + row0 * C::ROWB + s * 8);
+      const uint2 vb = *reinterpret_cast<const uint2*>(vt + row1 * C::ROWB + s * 8);
+      const uint32_t a2[2] = {va.x, va.y}, b2[2] = {vb.x, vb.y};
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t alo = a2[i] & 0x0F0F0F0Fu, ahi = (a2[i] >> 4) & 0x0F0F0F0Fu;
+        const uint32_t blo = b2[i] & 0x0F0F0F0Fu, bhi = (b2[i] >> 4) & 0x0F0F0F0Fu;
+        // (row0, row1) of element 8i + 2t (low nibbles) and 8i + 2t + 1 (high)
+        const uint32_t pe[4] = {int4_pair<0>(alo, blo), int4_pair<1>(alo, blo), int4_pair<2>(alo, blo),
+                                int4_pair<3>(alo, blo)};
+        const uint32_t po[4] = {int4_pair<0>(ahi, bhi), int4_pair<1>(ahi, bhi), int4_pair<2>(ahi, bhi),
+                                int4_pair<3>(ahi, bhi)};
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int h = 0; h < HW; ++h) {
+            st.acc[h][8 * i + 2 * t] = dot2_bf16(P[h], pe[t], st.acc[h][8 * i + 2 * t]);
+            st.acc[h][8 * i + 2 * t + 1] = dot2_bf16(P[h], po[t], st.acc[h][8 * i + 2 * t + 1]);
+          }
+      }
+#pragma unroll
+      for (int h = 0; h < HW; ++h) st.wsum[h] = dot2_bf16(P[h], 0x3F803F80u, st.wsum[h]);  // + p0 + p1
+      continue;
+    }
 #pragma unroll
     for (int cc = 0; cc < C::CPL; ++cc) {
       const int off = ((s + 8 * cc) ^ dec_swz<C::CPR>(row0)) * 16;
@@ -1139,14 +1253,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   // four-lane score layout: per-wavefront probability pairs and rescale factors
   __shared__ __attribute__((aligned(16))) uint16_t pbuf_all[SC4 ? kDecWaves : 1][SC4 ? 2 * S4::PBUF : 8];
   __shared__ __attribute__((aligned(16))) float abuf_all[SC4 ? kDecWaves : 1][32];
-  // FP8 rows: the K scales, then the V scales, of the rows of a round; one
-  // buffer per K unit of the ring (units 0 and 2), loaded with that unit
-  constexpr bool KV8 = C::KV8;
-  __shared__ __attribute__((aligned(16))) float sbuf[KV8 ? 2 : 1][KV8 ? 2 * C::ROUND_ROWS : 4];
-  static_assert(!KV8 || C::ROUND_ROWS == 4 * 64, "a round's scales are 4 wavefront loads per tensor");
-  // vector-memory loads per unit and wavefront: the ring pieces, plus one
-  // scale load with each K unit of FP8 rows; units u+1 and u+2 hold WAITN
-  constexpr int WAITN = 2 * kPiecesPerWave + (KV8 ? 1 : 0);
+  // FP8 / INT4 rows: the K scales, then the V scales, of the rows of a round;
+  // one buffer per K unit of the ring (units 0 and 2), loaded with that unit
+  constexpr bool KV8 = C::KV8, KV4 = C::KV4, LOWBIT = C::LOWBIT;
+  __shared__ __attribute__((aligned(16))) float sbuf[LOWBIT ? 2 : 1][LOWBIT ? 2 * C::ROUND_ROWS : 4];
+  // a round's scales: SPW wavefront loads of 64 rows per wavefront (waves 0-3
+  // the K scales, 4-7 the V scales); FP8 rounds hold 256 rows, INT4 rounds 512
+  constexpr int SPW = LOWBIT ? C::ROUND_ROWS / 256 : 0;
+  static_assert(!LOWBIT || C::ROUND_ROWS % 256 == 0, "a round's scales are whole wavefront loads");
+  // vector-memory loads per unit and wavefront: the ring pieces, plus SPW
+  // scale loads with each K unit of low-bit rows; units u+1 and u+2 hold WAITN
+  constexpr int WAITN = 2 * kPiecesPerWave + SPW;
   char* const rings[kRingUnits] = {ring0, ring1, ring2, ring3};  // indexed by constants only
   auto ring_at = [&](int i) -> char* { return i == 0 ? ring0 : i == 1 ? ring1 : i == 2 ? ring2 : ring3; };
 
@@ -1210,13 +1327,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < kPiecesPerWave; ++j)
       dec_dma(rs, dst + (wave + kDecWaves * j) * 1024, (uu & 1) ? poff_v[j] : poff_k[j]);
-    if constexpr (KV8) {
-      if ((uu & 1) == 0) {  // wavefronts 0-3: K scales, 4-7: V scales, 64 rows each
+    if constexpr (LOWBIT) {
+      if ((uu & 1) == 0) {  // wavefronts 0-3: K scales, 4-7: V scales, SPW x 64 rows each
         const int tensor = wave >> 2, part = wave & 3;
         const float* ssrc = (tensor ? w.vsc : w.ksc) + roff;
-        dec_dma4(dec_rsrc(reinterpret_cast<const char*>(ssrc), rows * 4),
-                 reinterpret_cast<char*>(&sbuf[(uu >> 1) & 1][tensor * C::ROUND_ROWS + part * 64]),
-                 (uint32_t)((part * 64 + lane) * 4));
+        const i32x4_t srs = dec_rsrc(reinterpret_cast<const char*>(ssrc), rows * 4);
+#pragma unroll
+        for (int j = 0; j < SPW; ++j)
+          dec_dma4(srs, reinterpret_cast<char*>(&sbuf[(uu >> 1) & 1][tensor * C::ROUND_ROWS + (part * SPW + j) * 64]),
+                   (uint32_t)(((part * SPW + j) * 64 + lane) * 4));
       }
     }
   };
@@ -1263,6 +1382,23 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
       q[h][c2] = *reinterpret_cast<const uint4*>(
           stage + (size_t)(hg * HW + h) * C::IROWB +
           (SC4 ? ((s4 + 4 * (c2 / S4::QPC)) * S4::QPC + c2 % S4::QPC) : (s + 8 * c2)) * 16);
+  // INT4 rows: 136 times each query's sum (the scores' bias, see int4_pair);
+  // the four lanes of a row group hold the query's four quarters
+  float qbias[HW];
+#pragma unroll
+  for (int h = 0; h < HW; ++h) {
+    float sum = 0.f;
+    if constexpr (KV4) {
+#pragma unroll
+      for (int c2 = 0; c2 < QCPL; ++c2) {
+        const uint32_t qw[4] = {q[h][c2].x, q[h][c2].y, q[h][c2].z, q[h][c2].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sum += bf_lo(qw[i]) + bf_hi(qw[i]);
+      }
+      sum = row4_sum(sum) * kInt4Bias;
+    }
+    qbias[h] = sum;
+  }
   uint16_t* const pbuf = pbuf_all[SC4 ? wave : 0];
   float* const abuf = abuf_all[SC4 ? wave : 0];
   float m4 = -INFINITY, l4 = 0.f;  // four-lane layout: softmax state of (r16 % 8, head s4)
@@ -1276,6 +1412,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < C::NACC; ++e) st.acc[h][e] = 0.f;
   }
+#pragma unroll
+  for (int h = 0; h < (KV4 ? HW : 1); ++h) st.wsum[h] = 0.f;
   float p[C::RPL][HW];
 
   // Unit u of the stream, held in ring unit X = u % 4 (K rows when X is even).
@@ -1300,9 +1438,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
       const int exr = (ex >= 0 && ex < TR) ? (int)ex : -1;
       if constexpr (SC4) {
         resc = false;
-        const float* ks = &sbuf[KV8 ? (u >> 1) & 1 : 0][KV8 ? slot * TR : 0];
-        const float* vs = ks + (KV8 ? C::ROUND_ROWS : 0);
-        if (nv > 0) resc = tile_scores4<KT, D, G>(m4, l4, pbuf, abuf, tile, q, ks, vs, nv, exr, r16, s4, a.scale_log2);
+        const float* ks = &sbuf[LOWBIT ? (u >> 1) & 1 : 0][LOWBIT ? slot * TR : 0];
+        const float* vs = ks + (LOWBIT ? C::ROUND_ROWS : 0);
+        if (nv > 0)
+          resc = tile_scores4<KT, D, G>(m4, l4, pbuf, abuf, tile, q, qbias, ks, vs, nv, exr, r16, s4, a.scale_log2);
       } else {
         if (nv > 0) tile_scores<KT, D, G>(st, p, tile, q, nv, exr, rg, s, a.scale_log2);
       }
@@ -1325,6 +1464,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   // ring0, V in row 0 of ring1; the other rows are masked), then store it
   uint4 nkv = make_uint4(0, 0, 0, 0);
   uint2 ncodes = make_uint2(0u, 0u);  // FP8 rows: the new token's codes (lanes 0-31 of wavefront 0)
+  uint32_t ncodes4 = 0u;              // INT4 rows: the same
   float nscale = 0.f;
   if (add_new) {
     lds_barrier();  // every wavefront is done with the ring
@@ -1337,6 +1477,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
         *reinterpret_cast<uint2*>((t ? ring1 : ring0) + j * 8) = ncodes;  // row 0: no swizzle
         if (j == 0) sbuf[0][t * C::ROUND_ROWS] = nscale;
       }
+    } else if constexpr (KV4) {
+      if (wave == 0 && lane < 32) {
+        const int t = lane >> 4, j = lane & 15;
+        ncodes4 = quant_row16_int4(*reinterpret_cast<const uint4*>(stage + QSTAGE + t * NSTAGE + j * 16), nscale);
+        *reinterpret_cast<uint32_t*>((t ? ring1 : ring0) + j * 4) = ncodes4;  // row 0
+        if (j == 0) sbuf[0][t * C::ROUND_ROWS] = nscale;
+      }
     } else {
       if (wave == 0 && lane < 2 * C::CPR) {
         nkv = *reinterpret_cast<const uint4*>(stage + QSTAGE + (lane < C::CPR ? 0 : NSTAGE) + (lane % C::CPR) * 16);
@@ -1346,8 +1493,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     lds_barrier();
     if (slot == 0) {
       if constexpr (SC4) {
-        const bool r1 = tile_scores4<KT, D, G>(m4, l4, pbuf, abuf, ring0, q, &sbuf[0][0], &sbuf[0][KV8 ? C::ROUND_ROWS : 0],
-                                               1, -1, r16, s4, a.scale_log2);
+        const bool r1 = tile_scores4<KT, D, G>(m4, l4, pbuf, abuf, ring0, q, qbias, &sbuf[0][0],
+                                               &sbuf[0][LOWBIT ? C::ROUND_ROWS : 0], 1, -1, r16, s4, a.scale_log2);
         tile_pv4<KT, D, G>(st, pbuf, abuf, r1, ring1, rg, s);
       } else {
         tile_scores<KT, D, G>(st, p, ring0, q, 1, -1, rg, s, a.scale_log2);
@@ -1361,6 +1508,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
         if (wave == 0 && lane < 32) {
           const int t = lane >> 4, j = lane & 15;
           *reinterpret_cast<uint2*>((t ? w.vbase : w.kbase) + (size_t)row * C::ROWB + j * 8) = ncodes;
+          if (j == 0) (t ? w.vsc : w.ksc)[row] = nscale;
+        }
+      } else if constexpr (KV4) {
+        if (wave == 0 && lane < 32) {
+          const int t = lane >> 4, j = lane & 15;
+          *reinterpret_cast<uint32_t*>((t ? w.vbase : w.kbase) + (size_t)row * C::ROWB + j * 4) = ncodes4;
           if (j == 0) (t ? w.vsc : w.ksc)[row] = nscale;
         }
       } else {
@@ -1388,15 +1541,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int h = 0; h < HW; ++h) {
       const int hG = hg * HW + h;
+      if constexpr (KV4) {  // the weighted sum's pairs held level + 136
+#pragma unroll
+        for (int e = 0; e < C::NACC; ++e) st.acc[h][e] = fmaf(-kInt4Bias, st.wsum[h], st.acc[h][e]);
+      }
 #pragma unroll
       for (int c2 = 0; c2 < C::CPL; ++c2) {
-        const int off = ((((slot * 8 + rg) * G + hG) * D) + (c2 * 8 + s) * C::EPC) * 4;
+        const int off = ((((slot * 8 + rg) * G + hG) * D) + (c2 * 8 + s) * C::EPV) * 4;
         float* dst = reinterpret_cast<float*>(ring_at(off / XB) + off % XB);
 #pragma unroll
-        for (int e = 0; e < C::EPC; e += 4)
+        for (int e = 0; e < C::EPV; e += 4)
           *reinterpret_cast<float4*>(dst + e) =
-              make_float4(st.acc[h][c2 * C::EPC + e], st.acc[h][c2 * C::EPC + e + 1], st.acc[h][c2 * C::EPC + e + 2],
-                          st.acc[h][c2 * C::EPC + e + 3]);
+              make_float4(st.acc[h][c2 * C::EPV + e], st.acc[h][c2 * C::EPV + e + 1], st.acc[h][c2 * C::EPV + e + 2],
+                          st.acc[h][c2 * C::EPV + e + 3]);
       }
       if constexpr (!SC4) {
         if (s == 0) {
@@ -1678,14 +1835,15 @@ hipError_t launch_advance(const AdvanceArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_append(const AppendArgs& a, int dtype, int d, bool fp8, hipStream_t s) {
+hipError_t launch_append(const AppendArgs& a, int dtype, int d, int kvfmt, hipStream_t s) {
   (void)dtype;
   (void)d;
-  if (fp8) {
+  if (kvfmt != 0) {
     const int64_t threads = (int64_t)a.B * a.n_kv * a.n_new * 2 * 16;
     const int64_t grid = (threads + 255) / 256;
     if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
-    append_fp8_kernel<<<(unsigned)grid, 256, 0, s>>>(a);
+    if (kvfmt == 2) append_lowbit_kernel<true><<<(unsigned)grid, 256, 0, s>>>(a);
+    else append_lowbit_kernel<false><<<(unsigned)grid, 256, 0, s>>>(a);
     return hipGetLastError();
   }
   const int64_t total = (int64_t)a.B * a.n_kv * a.n_new * (a.row_bytes / 16);
@@ -1705,16 +1863,17 @@ hipError_t launch_dequant(const DequantArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-int64_t decode_round_rows(int dtype, int d, int g, bool fp8) {
-  if (fp8) return round_rows_d<2, 128>(g);
+int64_t decode_round_rows(int dtype, int d, int g, int kvfmt) {
+  if (kvfmt == 2) return round_rows_d<3, 128>(g);
+  if (kvfmt == 1) return round_rows_d<2, 128>(g);
   if (dtype == 1) return d == 128 ? round_rows_d<1, 128>(g) : round_rows_d<1, 64>(g);
   return d == 128 ? round_rows_d<0, 128>(g) : round_rows_d<0, 64>(g);
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int g, bool fp8, int blocks, hipStream_t s) {
-  if (fp8) {
-    if (dtype == 1 && d == 128) return launch_decode_d<2, 128>(a, g, blocks, s);
-    return hipErrorInvalidValue;
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, int g, int kvfmt, int blocks, hipStream_t s) {
+  if (kvfmt != 0) {
+    if (dtype != 1 || d != 128) return hipErrorInvalidValue;
+    return kvfmt == 2 ? launch_decode_d<3, 128>(a, g, blocks, s) : launch_decode_d<2, 128>(a, g, blocks, s);
   }
   if (dtype == 1) {
     if (d == 128) return launch_decode_d<1, 128>(a, g, blocks, s);

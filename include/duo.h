@@ -77,9 +77,15 @@ typedef enum { DUO_F32 = 0, DUO_BF16 = 1 } duo_dtype;
  * Heads Guide", "Production Advantages and Deployment Considerations", item 2;
  * "Attention Variants and Memory Efficiency", "What the Inference Runtime Can
  * Change": cache precision changes the bytes per stored element, not the
- * attention rule).  Built for dtype bf16 and d_head 128; queries, new tokens
- * and outputs stay bf16. */
-typedef enum { DUO_KV_NATIVE = 0, DUO_KV_FP8 = 1 } duo_kv_format;
+ * attention rule).
+ * DUO_KV_INT4: as 4-bit integer codes with one fp32 scale per stored row, K
+ * and V separately: s = max|x| / 7, c_i = x_i / s rounded to the nearest
+ * integer (ties to even, |c_i| <= 7), stored as the nibble c_i + 8, two per
+ * byte (element 2k in the low nibble of byte k); a zero row: s = 0, c = 0;
+ * attention sees c_i * s (the same guide item: 4 bits per element).
+ * Both are built for dtype bf16 and d_head 128; queries, new tokens and
+ * outputs stay bf16. */
+typedef enum { DUO_KV_NATIVE = 0, DUO_KV_FP8 = 1, DUO_KV_INT4 = 2 } duo_kv_format;
 
 /* Cache configuration.  d_head in {64, 128}; g = n_q / n_kv in {1, 2, 4, 8};
  * n_kv <= 128; 1 <= B <= 64; S >= 0; W >= 1; T_cap >= 1.  Each batch row keeps
@@ -89,7 +95,7 @@ typedef enum { DUO_KV_NATIVE = 0, DUO_KV_FP8 = 1 } duo_kv_format;
  *
  * Retrieval rows are stored one of two ways.  page_rows = 0: contiguous, T_cap
  * rows per retrieval head and batch row.  page_rows > 0 (a power of two, at
- * least 256): paged ("Attention Variants and Memory Efficiency", "What the
+ * least 256, at least 512 for DUO_KV_INT4): paged ("Attention Variants and Memory Efficiency", "What the
  * Inference Runtime Can Change": the runtime may cut a request's rows into
  * equal blocks placed anywhere and shared between requests; "A Closer Look at
  * Attention Memory": a ragged batch then holds only what each request needs).

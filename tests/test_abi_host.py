@@ -51,6 +51,34 @@ def test_fp8_payload_closed_form(name):
     assert payload < native * 0.52 and ws > ws_native
 
 
+@pytest.mark.parametrize("name", ["gqa70b_decode_128k", "mha7b_decode_128k", "llama3_8b_prefill_64k"])
+def test_int4_payload_closed_form(name):
+    """INT4 rows: d / 2 bytes of codes plus one fp32 scale per stored K and V row."""
+    w = WL.WORKLOADS[name]
+    mask = WL.mask_table(w)
+    _, ws, payload = H.cache_bytes(w.L, w.B, w.n_q, w.n_kv, w.d, w.T, w.S, w.W, w.dtype, mask, "int4")
+    codes = Z.mixed_payload_bytes(mask.tolist(), w.B, w.T, w.S, w.W, w.d // 2, 1)
+    scales = Z.mixed_payload_bytes(mask.tolist(), w.B, w.T, w.S, w.W, 1, 4)
+    assert payload == codes + scales
+    _, _, native = H.cache_bytes(w.L, w.B, w.n_q, w.n_kv, w.d, w.T, w.S, w.W, w.dtype, mask)
+    assert payload * 3.7 < native < payload * 3.8   # 256 bytes against 64 + 4
+
+
+def test_int4_pages_hold_a_decode_round():
+    with pytest.raises(H.DuoError) as e:
+        H.cache_bytes(1, 1, 8, 2, 128, 4096, 4, 8, "bf16", [[1, 0]], "int4", page_rows=256, n_pages=16)
+    assert e.value.code == H.DUO_EUNSUPPORTED
+    H.cache_bytes(1, 1, 8, 2, 128, 4096, 4, 8, "bf16", [[1, 0]], "int4", page_rows=512, n_pages=8)
+
+
+def test_low_bit_rows_need_bf16_d128():
+    for kvf in ("fp8", "int4"):
+        for dtype, d in (("f32", 128), ("bf16", 64)):
+            with pytest.raises(H.DuoError) as e:
+                H.cache_bytes(1, 1, 8, 2, d, 64, 4, 8, dtype, [[1, 0]], kvf)
+            assert e.value.code == H.DUO_EUNSUPPORTED
+
+
 @pytest.mark.parametrize("kvf", [None, "fp8"])
 def test_paged_payload_closed_form(kvf):
     """A paged cache's retrieval payload is its pools (n_pages * page_rows rows

@@ -24,6 +24,8 @@ CASES = [
     (0, 0.0, "fp8", 300),
     (256, 10000.0, "fp8", 253),
     (0, 10000.0, None, 65),      # the streaming heads' S + W = 68 slots fill during the replays
+    (0, 0.0, "int4", 300),
+    (512, 10000.0, "int4", 1021),  # INT4 rows in 512-row pages, crossing into page 2
 ]
 STEPS = 6
 B, N_Q, N_KV, D, S, W = 2, 16, 4, 128, 4, 64
@@ -125,6 +127,9 @@ def _oracle_step(K, V, Q, i, b, p, mask, theta, kvf):
                                    kv_format=kvf)
     if kvf == "fp8":
         return OQ.decode_step_fp8(q, Kb.astype(np.float32), Vb.astype(np.float32), mask, S, W, D ** -0.5)
+    if kvf == "int4":
+        from oracle import quant4 as OQ4
+        return OQ4.decode_step_int4(q, Kb.astype(np.float32), Vb.astype(np.float32), mask, S, W, D ** -0.5)
     return OA.decode_step(q, Kb, Vb, mask, S, W, D ** -0.5)
 
 

@@ -1,7 +1,7 @@
 """Seeded random configurations: the features combined in ways the targeted
 tests do not list one by one -- dtype, d_head, group size, sink and window
 sizes, retrieval masks, ragged rows grown by appends and per-row prefill
-chunks, 256-row pages, rotary positions and FP8 rows -- each followed by a
+chunks, pages, rotary positions and FP8 or INT4 rows -- each followed by a
 decode and two fused decode-append steps, every row checked against the fp64
 oracle over its own sequence."""
 import numpy as np
@@ -11,6 +11,7 @@ import torch
 import workloads as WL
 from oracle import attention as OA
 from oracle import quant as OQ
+from oracle import quant4 as OQ4
 from oracle import rope as RP
 from tests.gpu_util import check_close, need_gpu, say, stored
 
@@ -32,18 +33,22 @@ def _draw(seed):
     theta = float(r.choice([0.0, 0.0, 10000.0, 500000.0]))
     lens = [int(x) for x in r.integers(1, 700, B)]
     prefill = [bool(x) for x in r.random(B) < 0.5]  # rows grown by prefill chunks (else appends)
-    return dict(fp8=fp8, dtype=dtype, d=d, g=g, n_kv=n_kv, mask=mask, B=B, S=S, W=W, paged=paged, theta=theta,
-                lens=lens, prefill=prefill, seed=seed)
+    kvf = ("int4" if r.random() < 0.5 else "fp8") if fp8 else None  # low-bit rows: half of them INT4
+    return dict(fp8=fp8, kvf=kvf, dtype=dtype, d=d, g=g, n_kv=n_kv, mask=mask, B=B, S=S, W=W, paged=paged,
+                theta=theta, lens=lens, prefill=prefill, seed=seed)
 
 
 def _ref_decode(cfg, Q, K, V, b, t):
     """Oracle output of row b's query at position t over positions 0..t."""
     dt, d = cfg["dtype"], cfg["d"]
     q, Ks, Vs = stored(Q[b, :, t], dt), stored(K[b, :, :t + 1], dt), stored(V[b, :, :t + 1], dt)
-    kvf = "fp8" if cfg["fp8"] else None
+    kvf = cfg["kvf"]
     if cfg["theta"]:
         return RP.decode_step_rope(q, Ks, Vs.astype(np.float32), cfg["mask"], cfg["S"], cfg["W"], d ** -0.5,
                                    cfg["theta"], dt, kv_format=kvf)
+    if kvf == "int4":
+        return OQ4.decode_step_int4(q, Ks.astype(np.float32), Vs.astype(np.float32), cfg["mask"], cfg["S"],
+                                    cfg["W"], d ** -0.5)
     if cfg["fp8"]:
         return OQ.decode_step_fp8(q, Ks.astype(np.float32), Vs.astype(np.float32), cfg["mask"], cfg["S"], cfg["W"],
                                   d ** -0.5)
@@ -55,7 +60,10 @@ def _ref_prefill(cfg, Q, K, V, b, n, chunks):
     Qs, Ks, Vs = stored(Q[b, :, :n], dt), stored(K[b, :, :n], dt), stored(V[b, :, :n], dt)
     if cfg["theta"]:
         return RP.prefill_chunked_rope(Qs, Ks, Vs, cfg["mask"], cfg["S"], cfg["W"], d ** -0.5, cfg["theta"], dt,
-                                       chunks, kv_format="fp8" if cfg["fp8"] else None)
+                                       chunks, kv_format=cfg["kvf"])
+    if cfg["kvf"] == "int4":
+        return OQ4.prefill_chunked_int4(Qs, Ks.astype(np.float32), Vs.astype(np.float32), cfg["mask"], cfg["S"],
+                                        cfg["W"], d ** -0.5, chunks)
     if cfg["fp8"]:
         return OQ.prefill_chunked_fp8(Qs, Ks.astype(np.float32), Vs.astype(np.float32), cfg["mask"], cfg["S"],
                                       cfg["W"], d ** -0.5, chunks)
@@ -76,9 +84,10 @@ def test_random_config(seed):
     K = WL.normal_f32((B, n_kv, N, d), 3 * seed + 1)
     V = WL.normal_f32((B, n_kv, N, d), 3 * seed + 2)
     Q = WL.normal_f32((B, n_q, N, d), 3 * seed + 3)
-    kw = dict(kv_format="fp8" if cfg["fp8"] else None, rope_theta=cfg["theta"])
+    kw = dict(kv_format=cfg["kvf"], rope_theta=cfg["theta"])
     if cfg["paged"]:
-        kw.update(page_rows=256, n_pages=sum(-(-(n + steps) // 256) for n in cfg["lens"]))
+        pr = 512 if cfg["kvf"] == "int4" else 256  # a decode round (INT4: 512 rows) fits a page
+        kw.update(page_rows=pr, n_pages=sum(-(-(n + steps) // pr) for n in cfg["lens"]))
     c = DuoCache(1, B, n_q, n_kv, d, N, cfg["S"], cfg["W"], dt, [cfg["mask"]], **kw)
     Kd, Vd, Qd = (WL.to_torch(x, dt).cuda() for x in (K, V, Q))
     rng = np.random.default_rng(seed)

@@ -58,7 +58,7 @@ class Workload:
     mode: str               # "decode" | "decode_append" | "prefill" | "gated"
     chunk: int = 0          # prefill chunk length
     fixed_mask: Optional[tuple] = None  # explicit per-layer mask rows, else seeded
-    kv_format: Optional[str] = None     # "fp8": K/V rows stored as FP8 codes + row scales
+    kv_format: Optional[str] = None     # "fp8" / "int4": K/V rows stored as low-bit codes + row scales
     page_rows: int = 0                  # > 0: retrieval rows in pages of this many rows
     rope_theta: float = 0.0             # > 0: rotary positions with this base
 
@@ -72,8 +72,13 @@ class Workload:
 
     @property
     def kv_row_bytes(self) -> int:
-        """Bytes of one stored K (or V) row: d elements, plus an fp32 scale for FP8 rows."""
-        return self.d + 4 if self.kv_format == "fp8" else self.d * self.elem_bytes
+        """Bytes of one stored K (or V) row: d elements, plus an fp32 scale for
+        FP8 rows (one byte per element) and INT4 rows (two elements per byte)."""
+        if self.kv_format == "fp8":
+            return self.d + 4
+        if self.kv_format == "int4":
+            return self.d // 2 + 4
+        return self.d * self.elem_bytes
 
     @property
     def scale(self) -> float:
@@ -111,9 +116,10 @@ WORKLOADS: Dict[str, Workload] = {
                                     sink_scale=1.0, mode="gated"),
 }
 # The two 128k decode workloads again with the cache's K/V rows stored as FP8
-# (same shapes and inputs).
+# and as INT4 (same shapes and inputs).
 for _n in ("gqa70b_decode_128k", "mha7b_decode_128k"):
     WORKLOADS[_n + "_fp8"] = WORKLOADS[_n].with_(name=_n + "_fp8", kv_format="fp8")
+    WORKLOADS[_n + "_int4"] = WORKLOADS[_n].with_(name=_n + "_int4", kv_format="int4")
 # The 70B decode again with the retrieval rows in 256-row pages (same shapes
 # and inputs; the pool holds exactly the rows the batch needs).
 WORKLOADS["gqa70b_decode_128k_paged"] = WORKLOADS["gqa70b_decode_128k"].with_(name="gqa70b_decode_128k_paged",
