@@ -19,6 +19,8 @@
 
 #include <cstdint>
 
+#include "duo_dma.h"
+
 namespace duo {
 namespace {
 
@@ -113,28 +115,13 @@ __device__ __forceinline__ uint32_t dma_offset(int n, int lane) {
   return (uint32_t)(r * (D * 2) + c * 16);
 }
 
-constexpr int kBufferRsrcWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
-
 // Issue this wavefront's pieces (wave, wave + kPfRowWaves, ...) of one tile.
+// The loads are not waited for here: the kernel waits for them (vmcnt) and
+// publishes them with a barrier before any wavefront reads the tile.
 template <int N>
-__device__ __forceinline__ void dma_pieces(__amdgpu_buffer_rsrc_t rsrc, char* lds_tile, int wave,
-                                           const uint32_t (&off)[N]) {
+__device__ __forceinline__ void dma_pieces(i32x4_t rsrc, char* lds_tile, int wave, const uint32_t (&off)[N]) {
 #pragma unroll
-  for (int j = 0; j < N; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc, (__attribute__((address_space(3))) void*)(lds_tile + (wave + kPfRowWaves * j) * 1024), 16, off[j], 0, 0,
-        0);
-}
-
-// Values that are the same in every lane, moved to scalar registers (a buffer
-// resource must live there).
-__device__ __forceinline__ int64_t uniform64(int64_t x) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-__device__ __forceinline__ const char* uniform_ptr(const char* p) {
-  return reinterpret_cast<const char*>(uniform64(reinterpret_cast<int64_t>(p)));
+  for (int j = 0; j < N; ++j) dma_lds16(rsrc, lds_tile + (wave + kPfRowWaves * j) * 1024, off[j]);
 }
 
 // ---- per-tile pieces of the MFMA path (one wavefront, 64 query rows = two

@@ -235,10 +235,8 @@ __global__ __launch_bounds__(kPfThreads) void gated_mfma_kernel(GatedArgs a, int
   auto issue = [&](int64_t tile, bool rest, int buf) {
     const int64_t base = tile * kBN;
     const int nbytes = __builtin_amdgcn_readfirstlane((int)min64(a.N - base, kBN) * (int)rowb);
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)uniform_ptr(kn + (size_t)base * rowb), (short)0, nbytes, kBufferRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)uniform_ptr(vn + (size_t)base * rowb), (short)0, nbytes, kBufferRsrcWord3);
+    const i32x4_t rk = dma_rsrc(kn + (size_t)base * rowb, nbytes);
+    const i32x4_t rv = dma_rsrc(vn + (size_t)base * rowb, nbytes);
     dma_pieces(rk, k_lds[kh][buf], sub, koff);
     dma_pieces(rv, v_lds[kh][buf], sub, voff);
     if (sub == 0) {

@@ -15,6 +15,7 @@
 // items that share a head are merged by a second kernel (combine_kernel).
 // Retrieval rows may live in pages (a per-row page table); a paged head's
 // items then start at round boundaries so that every round lies in one page.
+#include "duo_dma.h"
 #include "duo_internal.h"
 #include "duo_rope.h"
 #include "duo_rows.h"
@@ -248,58 +249,6 @@ __global__ void rope_kernel(RopeArgs a) {
       out[e1] = (float)(y * cs + x * sn);
     }
   }
-}
-
-// One wavefront-wide direct buffer->LDS load of 16 bytes per lane: lane i
-// writes LDS bytes [lds + 16 i, lds + 16 i + 16) from byte offset voff of the
-// buffer resource; offsets out of the resource's range read as zero.
-//
-// Written as inline assembly on purpose: the load has no register result
-// (its data goes to LDS), and the compiler, not knowing that it writes LDS,
-// adds no wait of its own before later LDS reads.  Every read of a unit is
-// ordered after its loads by an explicit vmcnt wait and a barrier (see
-// wait_vmcnt / lds_barrier), which keeps three units in flight; the compiler's
-// own analysis would wait for all of them.  The "memory" clobber stops the
-// compiler from assuming LDS contents across the load.  M0 (the LDS base of
-// the load) is saved and restored.
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ i32x4_t dec_rsrc(const char* base, int nbytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  return i32x4_t{(int)__builtin_amdgcn_readfirstlane((uint32_t)b),
-                 (int)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu),  // stride 0
-                 __builtin_amdgcn_readfirstlane(nbytes), 0x00020000};                 // raw buffer
-}
-
-__device__ __forceinline__ void dec_dma(i32x4_t rsrc, char* lds, uint32_t voff) {
-  const uint32_t m0v =
-      __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) char*)lds);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(m0v), "v"(voff), "s"(rsrc)
-      : "memory");
-}
-
-// The same with 4 bytes per lane: lane i writes LDS bytes [lds + 4 i, lds + 4 i + 4).
-__device__ __forceinline__ void dec_dma4(i32x4_t rsrc, char* lds, uint32_t voff) {
-  const uint32_t m0v =
-      __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) char*)lds);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dword %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(m0v), "v"(voff), "s"(rsrc)
-      : "memory");
 }
 
 // ------------------------------------------------------------------ decode
@@ -1323,18 +1272,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     const int rows = (int)(left <= 0 ? 0 : (left > C::ROUND_ROWS ? C::ROUND_ROWS : left));
     const int64_t roff = rows > 0 ? w.at(row0) : 0;
     const char* src = ((uu & 1) ? w.vbase : w.kbase) + (size_t)roff * C::ROWB;
-    const i32x4_t rs = dec_rsrc(src, rows * C::ROWB);
+    const i32x4_t rs = dma_rsrc(src, rows * C::ROWB);
 #pragma unroll
     for (int j = 0; j < kPiecesPerWave; ++j)
-      dec_dma(rs, dst + (wave + kDecWaves * j) * 1024, (uu & 1) ? poff_v[j] : poff_k[j]);
+      dma_lds16(rs, dst + (wave + kDecWaves * j) * 1024, (uu & 1) ? poff_v[j] : poff_k[j]);
     if constexpr (LOWBIT) {
       if ((uu & 1) == 0) {  // wavefronts 0-3: K scales, 4-7: V scales, SPW x 64 rows each
         const int tensor = wave >> 2, part = wave & 3;
         const float* ssrc = (tensor ? w.vsc : w.ksc) + roff;
-        const i32x4_t srs = dec_rsrc(reinterpret_cast<const char*>(ssrc), rows * 4);
+        const i32x4_t srs = dma_rsrc(reinterpret_cast<const char*>(ssrc), rows * 4);
 #pragma unroll
         for (int j = 0; j < SPW; ++j)
-          dec_dma4(srs, reinterpret_cast<char*>(&sbuf[(uu >> 1) & 1][tensor * C::ROUND_ROWS + (part * SPW + j) * 64]),
+          dma_lds4(srs, reinterpret_cast<char*>(&sbuf[(uu >> 1) & 1][tensor * C::ROUND_ROWS + (part * SPW + j) * 64]),
                    (uint32_t)(((part * SPW + j) * 64 + lane) * 4));
       }
     }
@@ -1348,10 +1297,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     constexpr int NQP = QSTAGE / 1024;  // query pieces
     if (wave < NQP) {
       const char* qsrc = static_cast<const char*>(a.q) + q_off * C::ES;
-      dec_dma(dec_rsrc(qsrc, G * C::IROWB), stage + wave * 1024, (uint32_t)(wave * 1024 + lane * 16));
+      dma_lds16(dma_rsrc(qsrc, G * C::IROWB), stage + wave * 1024, (uint32_t)(wave * 1024 + lane * 16));
     } else if (add_new && wave < NQP + 2) {
       const char* nsrc = (wave == NQP ? a.new_k : a.new_v) + ((size_t)w.b * a.n_kv + w.kvh) * C::IROWB;
-      dec_dma(dec_rsrc(nsrc, C::IROWB), stage + QSTAGE + (wave - NQP) * NSTAGE, (uint32_t)(lane * 16));
+      dma_lds16(dma_rsrc(nsrc, C::IROWB), stage + QSTAGE + (wave - NQP) * NSTAGE, (uint32_t)(lane * 16));
     }
   }
   issue(1, ring1);

@@ -274,12 +274,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
                              ? paged_row(a.lp.table + (size_t)w.b * a.lp.max_pages, a.lp.page_shift,
                                          (int64_t)a.n_ret << a.lp.page_shift, base)
                              : base;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)uniform_ptr(ks + (size_t)roff * rowb), (short)0, nbytes, kBufferRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)uniform_ptr(vs + (size_t)roff * rowb), (short)0, nbytes, kBufferRsrcWord3);
-    dma_pieces(rk, k_lds[kh][buf], sub, koff);
-    dma_pieces(rv, v_lds[kh][buf], sub, voff);
+    // The key bookkeeping goes first: the stored positions of a streaming
+    // head's slots are a global load whose wait must not also wait for this
+    // tile's direct loads (waits count loads in issue order).
     if (sub == 0) {  // one wavefront, all lanes: lane = key of the tile
       const int64_t row = base + lane;
       int64_t kp = -1;  // past the end: never visible
@@ -288,15 +285,19 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
         else if (src == SRC_CACHE_SLOTS) kp = posc[row];
         else kp = a.P + row;
       }
-      const KeySpan ks = key_span(kp, a.P, w.ret, a.S, a.W);
-      klo_lds[kh][buf][lane] = ks.lo;
-      kspan_lds[kh][buf][lane] = ks.span;
+      const KeySpan sp = key_span(kp, a.P, w.ret, a.S, a.W);
+      klo_lds[kh][buf][lane] = sp.lo;
+      kspan_lds[kh][buf][lane] = sp.span;
       // the tile needs no mask iff every key is seen by the item's first and
       // last row (the visible rows of a key form an interval)
-      const bool all = sees((int32_t)i0, ks.lo, ks.span) && sees((int32_t)(i1 - 1), ks.lo, ks.span);
+      const bool all = sees((int32_t)i0, sp.lo, sp.span) && sees((int32_t)(i1 - 1), sp.lo, sp.span);
       const uint64_t bal = __builtin_amdgcn_ballot_w64(all);
       if (lane == 0) s_full[kh][buf] = (bal == ~0ull) ? 1 : 0;
     }
+    const i32x4_t rk = dma_rsrc(ks + (size_t)roff * rowb, nbytes);
+    const i32x4_t rv = dma_rsrc(vs + (size_t)roff * rowb, nbytes);
+    dma_pieces(rk, k_lds[kh][buf], sub, koff);
+    dma_pieces(rv, v_lds[kh][buf], sub, voff);
   };
 
   f32x16_t o[DT][kPfNT];
