@@ -37,6 +37,10 @@ constexpr int kPfRowsPerWave = 32;                // query rows per wavefront
 constexpr int kPfNT = kPfRowsPerWave / 32;        // 32-row MFMA N tiles per wavefront
 constexpr int kBN = 64;                           // keys per tile
 
+// A value the same in every lane, moved to a scalar register (so that the
+// compiler treats what is computed from it as wavefront-uniform).
+__device__ __forceinline__ int32_t uniform32(int64_t x) { return (int32_t)__builtin_amdgcn_readfirstlane((int)x); }
+
 // Integer min / max by plain comparison (kept off any floating-point path).
 __device__ __forceinline__ int64_t min64(int64_t x, int64_t y) { return x < y ? x : y; }
 __device__ __forceinline__ int64_t max64(int64_t x, int64_t y) { return x > y ? x : y; }
@@ -49,19 +53,24 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Maxima of scores with IEEE maximum (a NaN would propagate; scores are
+// finite or -inf).  Unlike fmaxf it needs no quieting of its inputs, so it
+// lowers to bare v_maximum3_f32 on MFMA results.
+__device__ __forceinline__ float max2(float x, float y) { return __builtin_elementwise_maximum(x, y); }
+__device__ __forceinline__ float max3(float x, float y, float z) { return max2(max2(x, y), z); }
+
 // Max and sum over the lane pair (i, i ^ 32).  One v_permlane32_swap exchanges
 // the two 32-lane halves on the vector ALU (no LDS round trip): result r[0]
 // holds the lower half's values in both halves and r[1] the upper half's, so
 // both lanes of a pair combine the same two values in the same order.
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-__device__ __forceinline__ float max3(float x, float y, float z) { return fmaxf(fmaxf(x, y), z); }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 constexpr bf16x2_t kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
@@ -92,10 +101,10 @@ struct PfShape {
   static_assert(DMA_PER_TILE % kPfRowWaves == 0, "tile loads split over the wavefronts");
   // K rows: chunk c of key r sits at chunk slot c ^ swz_k(r) (A-operand reads
   // of 16 consecutive keys at one chunk hit 16 distinct bank groups).
-  __device__ static __forceinline__ int swz_k(int r) { return CPR == 16 ? (r & 15) : ((r >> 1) & 7); }
+  __host__ __device__ static constexpr int swz_k(int r) { return CPR == 16 ? (r & 15) : ((r >> 1) & 7); }
   // V rows: chunk c of key r at c ^ swz_v(r) (a transpose read of 4 rows x
   // 4 chunks by 32 lanes hits 16 distinct bank groups).
-  __device__ static __forceinline__ int swz_v(int r) { return CPR == 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+  __host__ __device__ static constexpr int swz_v(int r) { return CPR == 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
 // Direct global->LDS copies of a 64-row tile (K or V) through a buffer
@@ -107,7 +116,7 @@ struct PfShape {
 // only rebuilds the scalar resource (base = first row, size = rows present).
 // Rows past the end are out of range for the resource and read as zero.
 template <int D, bool IS_V>
-__device__ __forceinline__ uint32_t dma_offset(int n, int lane) {
+__host__ __device__ constexpr uint32_t dma_offset(int n, int lane) {
   using SH = PfShape<D>;
   const int piece = n * 64 + lane;
   const int r = piece / SH::CPR;
@@ -115,14 +124,64 @@ __device__ __forceinline__ uint32_t dma_offset(int n, int lane) {
   return (uint32_t)(r * (D * 2) + c * 16);
 }
 
-// Issue this wavefront's pieces (wave, wave + kPfRowWaves, ...) of one tile.
-// The loads are not waited for here: the kernel waits for them (vmcnt) and
-// publishes them with a barrier before any wavefront reads the tile.
-template <int N>
-__device__ __forceinline__ void dma_pieces(i32x4_t rsrc, char* lds_tile, int wave, const uint32_t (&off)[N]) {
-#pragma unroll
-  for (int j = 0; j < N; ++j) dma_lds16(rsrc, lds_tile + (wave + kPfRowWaves * j) * 1024, off[j]);
+// The property TileLoads relies on: a wavefront's piece wave + kPfRowWaves j
+// is its piece `wave` moved by j * kPfRowWaves KB (checked at compile time
+// for every wavefront, piece and lane).
+template <int D, bool IS_V>
+constexpr bool pieces_are_strided() {
+  for (int wave = 0; wave < kPfRowWaves; ++wave)
+    for (int j = 0; j < PfShape<D>::DMA_PER_TILE / kPfRowWaves; ++j)
+      for (int lane = 0; lane < 64; ++lane)
+        if (dma_offset<D, IS_V>(wave + kPfRowWaves * j, lane) !=
+            dma_offset<D, IS_V>(wave, lane) + (uint32_t)(kPfRowWaves * j * 1024))
+          return false;
+  return true;
 }
+static_assert(pieces_are_strided<128, false>() && pieces_are_strided<128, true>(), "d = 128 pieces");
+static_assert(pieces_are_strided<64, false>() && pieces_are_strided<64, true>(), "d = 64 pieces");
+
+// This wavefront's direct loads of one K/V tile (its pieces wave,
+// wave + kPfRowWaves, ... of each tensor), issued in four parts: the K
+// pieces in two, then the V pieces in two.  The kernels spread the parts of
+// the next tile over the four regions of the current tile's work, so that no
+// wavefront stalls on a burst of load issues right after a barrier (all
+// eight wavefronts would issue their loads at once).  The loads are not
+// waited for here: the kernel waits for them (vmcnt) and publishes them with
+// a barrier before any wavefront reads the tile.
+template <int D>
+struct TileLoads {
+  static constexpr int N = PfShape<D>::DMA_PER_TILE / kPfRowWaves;  // pieces per tensor and wavefront
+  static_assert(N % 2 == 0, "two parts per tensor");
+  // Buffer resources over the tile's K and V rows.  Without a tile to load
+  // they cover no bytes: every piece is then out of range, reads as zero and
+  // touches no memory (it fills a buffer nobody reads), and the loads need
+  // no branch.
+  i32x4_t rk, rv;
+  uint32_t kdst, vdst;   // LDS byte addresses of this wavefront's first K / V piece
+  uint32_t koff, voff;   // the lane's offsets (dma_offset) within its first K / V piece
+
+  // The wavefront's pieces n = wave + kPfRowWaves j lie kPfRowWaves KB apart
+  // both in LDS and in the tile's rows (the swizzle only permutes chunks
+  // within a row, and rows wave + kPfRowWaves j share it), so piece j is piece
+  // 0 moved by j * kPfRowWaves KB on both sides.
+  __device__ __forceinline__ void operator()(int part) const {
+    const bool v = part >= 2;
+    const int j0 = (part & 1) * (N / 2);
+#pragma unroll
+    for (int j = j0; j < j0 + N / 2; ++j)
+      dma_lds16_at(v ? rv : rk, (v ? vdst : kdst) + kPfRowWaves * j * 1024, v ? voff : koff,
+                   kPfRowWaves * j * 1024);
+  }
+  __device__ __forceinline__ void all() const {
+#pragma unroll
+    for (int part = 0; part < 4; ++part) (*this)(part);
+  }
+};
+
+// A pf_tile `next` that issues nothing (the loads were issued before the tile).
+struct NoLoads {
+  __device__ __forceinline__ void operator()(int) const {}
+};
 
 // ---- per-tile pieces of the MFMA path (one wavefront, 64 query rows = two
 // 32-row N tiles nt, one 64-key tile = two 32-key halves ct)
@@ -177,8 +236,8 @@ __device__ __forceinline__ bool pf_softmax(const f32x16_t (&s)[kPfNT], float (&m
 #pragma unroll
   for (int nt = 0; nt < kPfNT; ++nt) {
     const f32x16_t& x = s[nt];
-    const float v = fmaxf(max3(max3(x[0], x[1], x[2]), max3(x[3], x[4], x[5]), max3(x[6], x[7], x[8])),
-                          max3(max3(x[9], x[10], x[11]), max3(x[12], x[13], x[14]), x[15]));
+    const float v = max2(max3(max3(x[0], x[1], x[2]), max3(x[3], x[4], x[5]), max3(x[6], x[7], x[8])),
+                         max3(max3(x[9], x[10], x[11]), max3(x[12], x[13], x[14]), x[15]));
     const float mx = pair_max(v) * scale_log2;
     const bool g = mx > m_run[nt] + kRescaleSlack;
     grow |= g;
@@ -265,21 +324,24 @@ __device__ __forceinline__ void pf_pv(f32x16_t (&o)[D / 32][kPfNT], const uint32
 // is independent of the softmax next to it:
 //   S(0) | mask(0) | S(1) + softmax(0) | rescale(0), mask(1) | P V(0) + softmax(1) | rescale(1) | P V(1)
 // The masks and rescales are wavefront-uniform branches between the regions;
-// the compiler orders the instructions within a region.
-template <int D>
+// the compiler orders the instructions within a region.  `next` issues part
+// k of the next tile's loads at the start of the k-th main region.
+template <int D, class Next>
 __device__ __forceinline__ void pf_tile(f32x16_t (&o)[D / 32][kPfNT], float (&m_run)[kPfNT], float (&l_run)[kPfNT],
                                         const bf16x8_t (&qb)[kPfNT][D / 16], const char* kt, const char* vt,
                                         bool masked, const int32_t* klo, const uint32_t* kspan,
-                                        const int32_t (&iq)[kPfNT], float scale_log2, int lane) {
+                                        const int32_t (&iq)[kPfNT], float scale_log2, int lane, const Next& next) {
   constexpr int DT = D / 32;
   f32x16_t s0[kPfNT], s1[kPfNT];
   uint32_t p0[kPfNT][2][4], p1[kPfNT][2][4];
   float a0[kPfNT], a1[kPfNT];
 
+  next(0);
   pf_scores<D>(s0, qb, kt, 0, lane);
   __builtin_amdgcn_sched_barrier(0);
   if (masked) pf_mask(s0, klo, kspan, iq, 0, lane);
   __builtin_amdgcn_sched_barrier(0);
+  next(1);
   pf_scores<D>(s1, qb, kt, 1, lane);
   const bool g0 = pf_softmax(s0, m_run, l_run, p0, a0, scale_log2);
   __builtin_amdgcn_sched_barrier(0);
@@ -287,12 +349,14 @@ __device__ __forceinline__ void pf_tile(f32x16_t (&o)[D / 32][kPfNT], float (&m_
   if (g0) pf_rescale<DT>(o, a0);
   if (masked) pf_mask(s1, klo, kspan, iq, 1, lane);
   __builtin_amdgcn_sched_barrier(0);
+  next(2);
   pf_pv<D>(o, p0, vt, 0, lane);
   const bool g1 = pf_softmax(s1, m_run, l_run, p1, a1, scale_log2);
   __builtin_amdgcn_sched_barrier(0);
   pf_pin(p1, l_run);
   if (g1) pf_rescale<DT>(o, a1);
   __builtin_amdgcn_sched_barrier(0);
+  next(3);
   pf_pv<D>(o, p1, vt, 1, lane);
 }
 

@@ -41,19 +41,29 @@ __device__ __forceinline__ i32x4_t dma_rsrc(const char* base, int nbytes) {
                  __builtin_amdgcn_readfirstlane(nbytes), 0x00020000};                 // raw buffer
 }
 
-__device__ __forceinline__ void dma_lds16(i32x4_t rsrc, char* lds, uint32_t voff) {
-  const uint32_t m0v =
-      __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) char*)lds);
+// LDS byte address of a pointer into LDS (a workgroup-uniform value).
+__device__ __forceinline__ uint32_t lds_addr(const void* lds) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)(const char*)lds);
+}
+
+// The load with its LDS destination given as an LDS byte address, reading
+// from byte offset voff + soff of the resource (soff the same in every lane).
+__device__ __forceinline__ void dma_lds16_at(i32x4_t rsrc, uint32_t m0v, uint32_t voff, uint32_t soff) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(m0v), "v"(voff), "s"(rsrc)
+      : "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff)
       : "memory");
+}
+
+__device__ __forceinline__ void dma_lds16(i32x4_t rsrc, char* lds, uint32_t voff) {
+  dma_lds16_at(rsrc, lds_addr(lds), voff, 0);
 }
 
 // The same with 4 bytes per lane: lane i writes LDS bytes [lds + 4 i, lds + 4 i + 4).

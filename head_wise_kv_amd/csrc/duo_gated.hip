@@ -198,13 +198,9 @@ __global__ __launch_bounds__(kPfThreads) void gated_mfma_kernel(GatedArgs a, int
   const int64_t steps_w = (n_w + 1) / 2;  // the halves take tiles 2s and 2s+1 of a phase at step s
   const int64_t n_steps = steps_w + (n_r + 1) / 2;
 
-  constexpr int kPieces = SH::DMA_PER_TILE / kPfRowWaves;
-  uint32_t koff[kPieces], voff[kPieces];
-#pragma unroll
-  for (int j = 0; j < kPieces; ++j) {
-    koff[j] = dma_offset<D, false>(sub + kPfRowWaves * j, lane);
-    voff[j] = dma_offset<D, true>(sub + kPfRowWaves * j, lane);
-  }
+  // per-lane byte offsets of this wavefront's first K / V piece within a tile
+  const uint32_t koff = dma_offset<D, false>(sub, lane);
+  const uint32_t voff = dma_offset<D, true>(sub, lane);
   // Rows past the end read as zero; clear both buffers once so no stale bit
   // pattern (which could be a NaN) ever meets a zero probability.
   {
@@ -229,17 +225,33 @@ __global__ __launch_bounds__(kPfThreads) void gated_mfma_kernel(GatedArgs a, int
     const int64_t i = 2 * (step - steps_w) + kh;
     return i < n_r ? tt.r_lo + i : -1;
   };
-  // Issue a tile into buffer `buf` of this half: K/V by direct loads split over
-  // the half's wavefronts; the keys' visible-row intervals and the no-mask
-  // flag by the half's first wavefront.
-  auto issue = [&](int64_t tile, bool rest, int buf) {
+  // Whether every row of the item sees every key of a tile in its phase,
+  // decided from scalars: then the tile needs no mask and no per-key
+  // bookkeeping.  Phase 2 keys j >= S are seen by the rows from j + W on;
+  // phase 1 keys by the rows j .. j + W - 1 (every row from j on for a sink).
+  auto tile_full = [&](int64_t tile, bool rest) -> bool {
+    const int64_t base = tile * kBN;
+    if (base + kBN > a.N) return false;
+    if (rest) return base >= a.S && base + kBN - 1 + a.W <= i0;
+    return base + kBN - 1 <= i0 && (base + kBN - 1 < a.S || base + a.W >= i1);
+  };
+  // Prepare a tile (-1: none) for buffer `buf` of this half: for a tile that
+  // does not pass tile_full, the keys' visible-row intervals and the no-mask
+  // flag by the half's first wavefront; and the direct loads of its K/V
+  // pieces (split over the half's wavefronts), which the caller issues.
+  auto prepare = [&](int64_t tile, bool rest, int buf) -> TileLoads<D> {
+    TileLoads<D> ld;
+    ld.kdst = lds_addr(k_lds[kh][buf] + sub * 1024);
+    ld.vdst = lds_addr(v_lds[kh][buf] + sub * 1024);
+    ld.koff = koff;
+    ld.voff = voff;
+    if (!(tile >= 0)) {
+      ld.rk = ld.rv = dma_rsrc(kn, 0);
+      return ld;
+    }
     const int64_t base = tile * kBN;
     const int nbytes = __builtin_amdgcn_readfirstlane((int)min64(a.N - base, kBN) * (int)rowb);
-    const i32x4_t rk = dma_rsrc(kn + (size_t)base * rowb, nbytes);
-    const i32x4_t rv = dma_rsrc(vn + (size_t)base * rowb, nbytes);
-    dma_pieces(rk, k_lds[kh][buf], sub, koff);
-    dma_pieces(rv, v_lds[kh][buf], sub, voff);
-    if (sub == 0) {
+    if (sub == 0 && !tile_full(tile, rest)) {
       const int64_t j = base + lane;
       const KeySpan ks = rest ? span_rest(j, a.N, a.S, a.W) : span_window(j, a.N, a.S, a.W);
       klo_lds[kh][buf][lane] = ks.lo;
@@ -248,6 +260,9 @@ __global__ __launch_bounds__(kPfThreads) void gated_mfma_kernel(GatedArgs a, int
       const uint64_t bal = __builtin_amdgcn_ballot_w64(all);
       if (lane == 0) s_full[kh][buf] = (bal == ~0ull) ? 1 : 0;
     }
+    ld.rk = dma_rsrc(kn + (size_t)base * rowb, nbytes);
+    ld.rv = dma_rsrc(vn + (size_t)base * rowb, nbytes);
+    return ld;
   };
 
   f32x16_t o[DT][kPfNT];
@@ -268,7 +283,7 @@ __global__ __launch_bounds__(kPfThreads) void gated_mfma_kernel(GatedArgs a, int
   {
     bool rest;
     const int64_t t0 = tile_at(0, rest);
-    if (t0 >= 0) issue(t0, rest, 0);
+    prepare(t0, rest, 0).all();
   }
   for (int64_t step = 0; step < n_steps; ++step) {
     if (step == steps_w) {  // phase 1 done (wavefront-uniform)
@@ -287,15 +302,18 @@ __global__ __launch_bounds__(kPfThreads) void gated_mfma_kernel(GatedArgs a, int
     // the barrier every wavefront's have, and the previous tile is consumed.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (step + 1 < n_steps) {
-      bool rest_n;
-      const int64_t tn = tile_at(step + 1, rest_n);
-      if (tn >= 0) issue(tn, rest_n, buf ^ 1);
-    }
+    // the next tile's loads, issued before the current tile's work (spread
+    // over it as the prefill does, they would push this kernel, which also
+    // holds the saved phase-1 state, past 256 registers)
+    bool rest_n = false;
+    const int64_t tn = step + 1 < n_steps ? tile_at(step + 1, rest_n) : -1;
+    prepare(tn, rest_n, buf ^ 1).all();
     bool rest;
-    if (tile_at(step, rest) < 0) continue;  // wavefront-uniform
-    pf_tile<D>(o, m_run, l_run, qb, k_lds[kh][buf], v_lds[kh][buf], s_full[kh][buf] == 0, klo_lds[kh][buf],
-               kspan_lds[kh][buf], iq, a.scale_log2, lane);
+    const int64_t tc = tile_at(step, rest);
+    if (tc < 0) continue;  // wavefront-uniform: no tile for this half at this step
+    const bool masked = !tile_full(tc, rest) && s_full[kh][buf] == 0;
+    pf_tile<D>(o, m_run, l_run, qb, k_lds[kh][buf], v_lds[kh][buf], masked, klo_lds[kh][buf],
+               kspan_lds[kh][buf], iq, a.scale_log2, lane, NoLoads{});
   }
   if (n_steps == steps_w) {  // no phase-2 tile at all
 #pragma unroll

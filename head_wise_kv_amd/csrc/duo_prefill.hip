@@ -215,22 +215,25 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
   const size_t chunk_off = ((size_t)w.b * a.n_kv + w.kvh) * a.C * rowb;
   const char* kn = static_cast<const char*>(a.k) + chunk_off;
   const char* vn = static_cast<const char*>(a.v) + chunk_off;
-  const int64_t cache_rows = w.ret ? a.P : a.held_str;
 
+  // The item's key tiles: up to three runs of consecutive tiles (cache, then
+  // one or two of the chunk), in 32-bit tile and row numbers (positions stay
+  // below 2^31), held as wavefront-uniform values so that the per-tile
+  // arithmetic below is a few scalar instructions without branches.
   const TileRanges tr = plan_tiles(a, w.ret, i0, i1);
-  const int64_t n_cache = tr.cache_hi - tr.cache_lo;
-  const int64_t n_c0 = tr.chunk_hi0 - tr.chunk_lo0;
-  const int64_t n_c1 = tr.chunk_hi1 - tr.chunk_lo1;
-  const int64_t n_tiles = n_cache + n_c0 + n_c1;
+  const int32_t n_cache = uniform32(tr.cache_hi - tr.cache_lo);
+  const int32_t n_c0 = uniform32(tr.chunk_hi0 - tr.chunk_lo0);
+  const int32_t n_c1 = uniform32(tr.chunk_hi1 - tr.chunk_lo1);
+  const int32_t n_tiles = n_cache + n_c0 + n_c1;
+  const int32_t cache_lo = uniform32(tr.cache_lo), c0_lo = uniform32(tr.chunk_lo0), c1_lo = uniform32(tr.chunk_lo1);
+  const int32_t cache_rows = uniform32(w.ret ? a.P : a.held_str), chunk_rows = uniform32(a.C);
+  const int32_t r0 = uniform32(i0), r1 = uniform32(i1);  // the item's chunk rows [r0, r1)
+  const int32_t win_lo = r1 - a.W;                         // first chunk row in every row's window
+  const int32_t sink_rows = uniform32(max64(-1, min64((int64_t)a.S - a.P, 1 << 30)));  // chunk rows that are sinks
 
-  // per-lane byte offsets of this wavefront's pieces within a K / V tile
-  constexpr int kPieces = SH::DMA_PER_TILE / kPfRowWaves;
-  uint32_t koff[kPieces], voff[kPieces];
-#pragma unroll
-  for (int j = 0; j < kPieces; ++j) {
-    koff[j] = dma_offset<D, false>(sub + kPfRowWaves * j, lane);
-    voff[j] = dma_offset<D, true>(sub + kPfRowWaves * j, lane);
-  }
+  // per-lane byte offsets of this wavefront's first K / V piece within a tile
+  const uint32_t koff = dma_offset<D, false>(sub, lane);
+  const uint32_t voff = dma_offset<D, true>(sub, lane);
   // Rows past a source's end read as zero; clear both buffers once so no
   // stale bit pattern (which could be a NaN) ever meets a zero probability.
   {
@@ -242,43 +245,64 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
     __syncthreads();
   }
 
-  // Tile `it` -> (source, first row, row limit).
-  auto tile_src = [&](int64_t it, int& src, int64_t& base, int64_t& limit) {
-    if (it < n_cache) {
-      src = w.ret ? SRC_CACHE_LINEAR : SRC_CACHE_SLOTS;
-      base = (tr.cache_lo + it) * kBN;
-      limit = cache_rows;
-    } else if (it < n_cache + n_c0) {
-      src = SRC_CHUNK;
-      base = (tr.chunk_lo0 + (it - n_cache)) * kBN;
-      limit = a.C;
-    } else {
-      src = SRC_CHUNK;
-      base = (tr.chunk_lo1 + (it - n_cache - n_c0)) * kBN;
-      limit = a.C;
-    }
+  // Tile `it` -> (source, first row, row limit), as selects of per-run
+  // constants (tile number = first tile of the run + offset within it).
+  const int32_t skip0 = c0_lo - cache_lo - n_cache, skip1 = c1_lo - c0_lo - n_c0;
+  auto tile_src = [&](int32_t it, int& src, int32_t& base, int32_t& limit) {
+    const bool in_cache = it < n_cache, in_c0 = it < n_cache + n_c0;
+    base = (cache_lo + it + (in_cache ? 0 : skip0) + (in_c0 ? 0 : skip1)) * kBN;
+    limit = in_cache ? cache_rows : chunk_rows;
+    src = in_cache ? (w.ret ? SRC_CACHE_LINEAR : SRC_CACHE_SLOTS) : SRC_CHUNK;
   };
-  // Issue tile `it` into buffer `buf` of this wavefront's key half: K/V by
-  // direct loads (pieces split over the half's wavefronts), key visibility by
-  // plain stores (the half's first wavefront), and a flag telling whether
-  // every row of the item sees every key of the tile (then the mask is skipped).
-  auto issue = [&](int64_t it, int buf) {
+  // Whether every row of the item sees every key of tile `it`, decided from
+  // scalars where the keys' positions follow from their rows (a retrieval
+  // head's cached rows, the chunk's rows); the cached slots of a streaming
+  // head, whose positions are read from the cache, take the per-key test.
+  // A tile that passes needs no mask and no per-key bookkeeping.
+  auto tile_full = [&](int32_t it) -> bool {
     int src;
-    int64_t base, limit;
+    int32_t base, limit;
+    tile_src(it, src, base, limit);
+    const bool whole = base + kBN <= limit;  // no key past the end of the source
+    // chunk keys: causal for the item's first row; for a streaming head also
+    // all sinks (chunk rows below S - P), or all inside the window of the
+    // item's last row
+    const bool chunk_ok = base + kBN - 1 <= r0 && (w.ret || base + kBN - 1 < sink_rows || base >= win_lo);
+    // a retrieval head's cached positions (< P) are seen by every chunk row
+    return whole && (src == SRC_CACHE_LINEAR || (src == SRC_CHUNK && chunk_ok));
+  };
+  // Prepare tile `it` for buffer `buf` of this wavefront's key half: its key
+  // visibility, for a tile that does not pass tile_full, by plain stores (the
+  // half's first wavefront) with a flag telling whether every row of the item
+  // sees every key of the tile all the same (then the mask is skipped); and
+  // the direct loads of its K/V pieces (split over the half's wavefronts),
+  // which the caller issues.
+  auto prepare = [&](int32_t it, int buf) -> TileLoads<D> {
+    TileLoads<D> ld;
+    ld.kdst = lds_addr(k_lds[kh][buf] + sub * 1024);
+    ld.vdst = lds_addr(v_lds[kh][buf] + sub * 1024);
+    ld.koff = koff;
+    ld.voff = voff;
+    if (it >= n_tiles) {
+      ld.rk = ld.rv = dma_rsrc(kn, 0);
+      return ld;
+    }
+    int src;
+    int32_t base, limit;
     tile_src(it, src, base, limit);
     const char* ks = (src == SRC_CHUNK) ? kn : kc;
     const char* vs = (src == SRC_CHUNK) ? vn : vc;
-    const int nbytes = __builtin_amdgcn_readfirstlane((int)min64(limit - base, kBN) * (int)rowb);
+    const int nbytes = min(limit - base, kBN) * (int)rowb;
     // a paged head's tile (64 rows from a multiple of 64) lies in one page
     const int64_t roff = (src == SRC_CACHE_LINEAR && a.lp.table)
                              ? paged_row(a.lp.table + (size_t)w.b * a.lp.max_pages, a.lp.page_shift,
                                          (int64_t)a.n_ret << a.lp.page_shift, base)
                              : base;
-    // The key bookkeeping goes first: the stored positions of a streaming
-    // head's slots are a global load whose wait must not also wait for this
-    // tile's direct loads (waits count loads in issue order).
-    if (sub == 0) {  // one wavefront, all lanes: lane = key of the tile
-      const int64_t row = base + lane;
+    // The stored positions of a streaming head's slots are a global load:
+    // it is waited for here, before any of the tile's direct loads is issued
+    // (waits count loads in issue order).
+    if (sub == 0 && !tile_full(it)) {  // one wavefront, all lanes: lane = key of the tile
+      const int32_t row = base + lane;
       int64_t kp = -1;  // past the end: never visible
       if (row < limit) {
         if (src == SRC_CACHE_LINEAR) kp = row;
@@ -290,14 +314,13 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
       kspan_lds[kh][buf][lane] = sp.span;
       // the tile needs no mask iff every key is seen by the item's first and
       // last row (the visible rows of a key form an interval)
-      const bool all = sees((int32_t)i0, sp.lo, sp.span) && sees((int32_t)(i1 - 1), sp.lo, sp.span);
+      const bool all = sees(r0, sp.lo, sp.span) && sees(r1 - 1, sp.lo, sp.span);
       const uint64_t bal = __builtin_amdgcn_ballot_w64(all);
       if (lane == 0) s_full[kh][buf] = (bal == ~0ull) ? 1 : 0;
     }
-    const i32x4_t rk = dma_rsrc(ks + (size_t)roff * rowb, nbytes);
-    const i32x4_t rv = dma_rsrc(vs + (size_t)roff * rowb, nbytes);
-    dma_pieces(rk, k_lds[kh][buf], sub, koff);
-    dma_pieces(rv, v_lds[kh][buf], sub, voff);
+    ld.rk = dma_rsrc(ks + (size_t)roff * rowb, nbytes);
+    ld.rv = dma_rsrc(vs + (size_t)roff * rowb, nbytes);
+    return ld;
   };
 
   f32x16_t o[DT][kPfNT];
@@ -313,21 +336,23 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
   }
 
   // The two halves walk the tile list in lockstep, one barrier per step.
-  const int64_t n_steps = (n_tiles + 1) / 2;
-  if (kh < n_tiles) issue(kh, 0);
-  for (int64_t step = 0; step < n_steps; ++step) {
+  // The next tile's loads are issued during the current tile's work.
+  const int32_t n_steps = (n_tiles + 1) / 2;
+  prepare(kh, 0).all();
+  for (int32_t step = 0; step < n_steps; ++step) {
     const int buf = (int)(step & 1);
     // this wavefront's direct loads for the current tile have landed; after
     // the barrier every wavefront's have, and the previous tile is consumed.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (2 * (step + 1) + kh < n_tiles) issue(2 * (step + 1) + kh, buf ^ 1);
-    if (2 * step + kh >= n_tiles) continue;  // this half has no tile left (wavefront-uniform)
-
+    // this half has no tile left, and so no next one (wavefront-uniform)
+    if (2 * step + kh >= n_tiles) continue;
+    const TileLoads<D> next = prepare(2 * (step + 1) + kh, buf ^ 1);
     const char* kt = k_lds[kh][buf];
     const char* vt = v_lds[kh][buf];
-    pf_tile<D>(o, m_run, l_run, qb, kt, vt, s_full[kh][buf] == 0, klo_lds[kh][buf], kspan_lds[kh][buf], iq,
-               a.scale_log2, lane);
+    const bool masked = !tile_full(2 * step + kh) && s_full[kh][buf] == 0;
+    pf_tile<D>(o, m_run, l_run, qb, kt, vt, masked, klo_lds[kh][buf], kspan_lds[kh][buf], iq, a.scale_log2, lane,
+               next);
   }
 
   // ---- merge the odd half into the even half through LDS (the tile buffers
