@@ -46,7 +46,7 @@ MALL_COPIES = {"llama3_8b_decode_b8_32k": 4}
 # every source the decode kernels are compiled from: counters taken on an
 # older version of any of them no longer describe the kernel
 KERNEL_SRC = [os.path.join(ROOT, "head_wise_kv_amd", "csrc", f)
-              for f in ("duo_kernels.hip", "duo_internal.h", "duo_rows.h", "duo_rope.h")]
+              for f in ("duo_kernels.hip", "duo_internal.h", "duo_rows.h", "duo_rope.h", "duo_dma.h")]
 
 
 def log(*a):
