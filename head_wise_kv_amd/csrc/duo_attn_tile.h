@@ -338,6 +338,11 @@ __device__ __forceinline__ void pf_tile(f32x16_t (&o)[D / 32][kPfNT], float (&m_
 
   next(0);
   pf_scores<D>(s0, qb, kt, 0, lane);
+  // the first and last regions are MFMA runs with nothing to overlap: their
+  // LDS operand reads are issued ahead of the MFMAs (eight K reads; the V
+  // transpose reads of each k-step's four MFMAs), not one or two ahead
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // MFMA
   __builtin_amdgcn_sched_barrier(0);
   if (masked) pf_mask(s0, klo, kspan, iq, 0, lane);
   __builtin_amdgcn_sched_barrier(0);
@@ -358,6 +363,10 @@ __device__ __forceinline__ void pf_tile(f32x16_t (&o)[D / 32][kPfNT], float (&m_
   __builtin_amdgcn_sched_barrier(0);
   next(3);
   pf_pv<D>(o, p1, vt, 1, lane);
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
 }  // namespace
