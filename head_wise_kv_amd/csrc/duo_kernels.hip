@@ -300,7 +300,11 @@ struct DecodeCfg {
   static constexpr int CPL = KV4 ? 1 : CPR / 8;  // V pieces per lane
   static constexpr int EPC = KV4 ? 32 : 16 / KES;  // elements per 16-byte chunk
   static constexpr int EPV = KV4 ? 16 : EPC;     // elements per V piece
-  static constexpr int HW = G < 4 ? G : 4;       // query heads per wavefront
+  // bf16 rows with eight query heads per KV head: scores and weighted sums on
+  // the matrix cores (see mf_scores), each wavefront taking all eight heads
+  // over its own 16 rows of a round
+  static constexpr bool MF = KT == 1 && D == 128 && G == 8;
+  static constexpr int HW = MF ? G : (G < 4 ? G : 4);  // query heads per wavefront
   static constexpr int HSPLIT = G / HW;          // wavefronts per slot
   static constexpr int SLOTS_W = kDecWaves / HSPLIT;
   static constexpr int SLOTS_B = kUnitBytes / (16 * ROWB);  // keeps TR >= 16
@@ -925,14 +929,14 @@ __device__ __forceinline__ void tile_pv(DecodeState<KT, D, G>& st, const float (
 template <int KT, int D, int G>
 struct Score4 {
   using C = DecodeCfg<KT, D, G>;
-  static constexpr bool ON = C::BF16;
+  static constexpr bool ON = C::BF16 && !C::MF;
   static constexpr int HW = C::HW;
   static constexpr int CPL4 = C::CPR / 4;   // chunks per lane
   static constexpr int RPL4 = C::TR / 16;   // rows per lane
   static constexpr int NQ = C::RPL / 2;     // row pairs per weighted-sum lane
   static constexpr int PBUF = 8 * NQ * HW;  // probability pairs per wavefront (dwords)
   static constexpr int QPC = C::EPC >= 8 ? C::EPC / 8 : 1;  // 16-byte query pieces per stored chunk (FP8 rows: 2)
-  static_assert(4 % HW == 0, "heads per wavefront divide the 4 lanes of a row");
+  static_assert(!ON || 4 % HW == 0, "heads per wavefront divide the 4 lanes of a row");
 };
 
 // Two bf16 values (exact) from the FP8 codes in bytes 0, 1 (hi = false) or
@@ -1171,6 +1175,96 @@ __device__ __forceinline__ void tile_pv4(DecodeState<KT, D, G>& st, const uint16
   }
 }
 
+// ---- matrix-core tiles (bf16 rows, d = 128, eight query heads)
+//
+// A wavefront scores its 16 rows of a round against the group's eight
+// queries as S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (keys on M, queries
+// on N; the queries fill 8 of the 16 columns, the others are zero), and
+// accumulates O^T += V^T P^T with v_mfma_f32_16x16x16_bf16 (d on M).  Lane
+// l = 16 g + j holds query j: its scores of rows 4 g .. 4 g + 3, the bf16
+// probabilities of those rows (the B operand of the weighted sum as they
+// are), and the output elements d = 16 t + 4 g .. + 3 of each 16-row d tile
+// t.  The K operand (key j's 8 elements 32 k + 8 g ..) is a 16-byte read;
+// the V^T operand (d = 16 t + j of rows 4 g .. 4 g + 3) a transpose read.
+// Rows are stored in the round with the chunk swizzles of the prefill tiles
+// (K: chunk c at c ^ (r & 15); V: c ^ 4 (r & 3)), so both reads are free of
+// bank conflicts.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int mf_swz_k(int r) { return r & 15; }
+__device__ __forceinline__ int mf_swz_v(int r) { return 4 * (r & 3); }
+
+struct MfState {
+  f32x4_t o[8];    // O^T tiles: d = 16 t + 4 g + e of query j
+  float m, l;      // running max (log2 units; the same in the four lanes of a query) and the lane's partial sum
+  uint32_t p[2];   // the current tile's probabilities: rows 4 g .. 4 g + 3 as two bf16 pairs
+};
+
+__device__ __forceinline__ void mf_init(MfState& st) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) st.o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  st.p[0] = st.p[1] = 0u;
+}
+
+// Scores of the tile's rows (nv valid; row excl, tile-relative, masked; -1
+// for none), the lazy online-softmax update and the probabilities.
+__device__ __forceinline__ void mf_scores(MfState& st, const char* kt, const bf16x8v_t (&qm)[4], int nv, int excl,
+                                          int lane, float scale_log2) {
+  const int j = lane & 15, g = lane >> 4;
+  f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = 4 * k + g;
+    const u32x4_t av = *reinterpret_cast<const u32x4_t*>(kt + j * 256 + ((c ^ mf_swz_k(j)) * 16));
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v_t, av), qm[k], sc, 0, 0, 0);
+  }
+  if (nv < 16 || excl >= 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * g + e;
+      if (r >= nv || r == excl) sc[e] = -INFINITY;
+    }
+  }
+  // the query's max over the tile: the lane's four rows, then the four lanes g
+  const float mx = swap32_max(swap16_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])))) * scale_log2;
+  if (__builtin_amdgcn_ballot_w64(mx > st.m + kRescaleSlack) != 0) {  // some query raises its reference
+    const float mn = fmaxf(st.m, mx);
+    const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(st.m - mn);
+    st.m = mn;
+    st.l *= alpha;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) st.o[t] *= alpha;
+  }
+  const float mu = (st.m == -INFINITY) ? 0.f : st.m;
+  const float p0 = fast_exp2(fmaf(sc[0], scale_log2, -mu)), p1 = fast_exp2(fmaf(sc[1], scale_log2, -mu));
+  const float p2 = fast_exp2(fmaf(sc[2], scale_log2, -mu)), p3 = fast_exp2(fmaf(sc[3], scale_log2, -mu));
+  st.p[0] = pack_bf16x2(p0, p1);
+  st.p[1] = pack_bf16x2(p2, p3);
+  // the row sums add the bf16-rounded probabilities, the values P V uses
+  constexpr uint32_t kOnes = 0x3f803f80u;
+  st.l = dot2_bf16(st.p[1], kOnes, dot2_bf16(st.p[0], kOnes, st.l));
+}
+
+// O^T += V^T P^T over the tile's rows (rows past nv carry probability 0).
+__device__ __forceinline__ void mf_pv(MfState& st, const char* vt, int lane) {
+  const int i16 = lane & 15, g = lane >> 4;
+  const i16x4_t pb = __builtin_bit_cast(i16x4_t, u32x2_t{st.p[0], st.p[1]});
+  const int row = 4 * g + (i16 >> 2);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int col = 16 * t + 4 * (i16 & 3);
+    const char* ptr = vt + row * 256 + (((col >> 3) ^ mf_swz_v(row)) * 16) + (col & 7) * 2;
+    const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(ptr));
+    st.o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, st.o[t], 0, 0, 0);
+  }
+}
+
 template <int X>
 using UnitTag = std::integral_constant<int, X>;
 
@@ -1199,6 +1293,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char stage[QSTAGE + 2 * NSTAGE];
   using S4 = Score4<KT, D, G>;
   constexpr bool SC4 = S4::ON;
+  constexpr bool MF = C::MF;
   // four-lane score layout: per-wavefront probability pairs and rescale factors
   __shared__ __attribute__((aligned(16))) uint16_t pbuf_all[SC4 ? kDecWaves : 1][SC4 ? 2 * S4::PBUF : 8];
   __shared__ __attribute__((aligned(16))) float abuf_all[SC4 ? kDecWaves : 1][32];
@@ -1254,9 +1349,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     const int off = (wave + kDecWaves * j) * 1024 + lane * 16;
     const int r = off / C::ROWB;  // row of the round; a slot's tile starts at a multiple of 4 rows
     const int c = (off % C::ROWB) / 16;
-    const int ck = c ^ (SC4 ? dec_swz_k4<C::CPR>(r % TR) : dec_swz<C::CPR>(r % TR));
+    const int ck = c ^ (MF ? mf_swz_k(r % TR) : SC4 ? dec_swz_k4<C::CPR>(r % TR) : dec_swz<C::CPR>(r % TR));
+    const int cv = c ^ (MF ? mf_swz_v(r % TR) : dec_swz<C::CPR>(r % TR));
     poff_k[j] = (uint32_t)(r * C::ROWB + ck * 16);
-    poff_v[j] = (uint32_t)(r * C::ROWB + (c ^ dec_swz<C::CPR>(r % TR)) * 16);
+    poff_v[j] = (uint32_t)(r * C::ROWB + cv * 16);
   }
   static_assert(TR % 4 == 0, "tiles start at a multiple of 4 rows");
 
@@ -1364,6 +1460,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int h = 0; h < (KV4 ? HW : 1); ++h) st.wsum[h] = 0.f;
   float p[C::RPL][HW];
+  // matrix-core tiles: the queries as the B operand (lane 16 g + j: query j,
+  // elements 32 k + 8 g .. + 7 of k-step k; columns 8 .. 15 zero) and the state
+  bf16x8v_t qm[4];
+  MfState mst;
+  if constexpr (MF) {
+    const int j = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const u32x4_t v = j < G ? *reinterpret_cast<const u32x4_t*>(stage + (size_t)j * C::IROWB + (32 * k + 8 * g) * 2)
+                              : u32x4_t{0u, 0u, 0u, 0u};
+      qm[k] = __builtin_bit_cast(bf16x8v_t, v);
+    }
+    mf_init(mst);
+  }
 
   // Unit u of the stream, held in ring unit X = u % 4 (K rows when X is even).
   auto unit = [&](auto tag, int64_t u) {
@@ -1377,7 +1487,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     const int nv = active ? (int)(left < 0 ? 0 : (left > TR ? TR : left)) : 0;
     const char* tile = rings[X] + slot * C::SLOT_BYTES;
     if (V_PART) {
-      if constexpr (SC4) {
+      if constexpr (MF) {
+        if (nv > 0) mf_pv(mst, tile, lane);
+      } else if constexpr (SC4) {
         if (nv > 0) tile_pv4<KT, D, G>(st, pbuf, abuf, resc, tile, rg, s);
       } else {
         if (nv > 0) tile_pv<KT, D, G>(st, p, tile, rg, s);
@@ -1385,7 +1497,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     } else {
       const int64_t ex = excl_row - row0;
       const int exr = (ex >= 0 && ex < TR) ? (int)ex : -1;
-      if constexpr (SC4) {
+      if constexpr (MF) {
+        if (nv > 0) mf_scores(mst, tile, qm, nv, exr, lane, a.scale_log2);
+      } else if constexpr (SC4) {
         resc = false;
         const float* ks = &sbuf[LOWBIT ? (u >> 1) & 1 : 0][LOWBIT ? slot * TR : 0];
         const float* vs = ks + (LOWBIT ? C::ROUND_ROWS : 0);
@@ -1441,7 +1555,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     }
     lds_barrier();
     if (slot == 0) {
-      if constexpr (SC4) {
+      if constexpr (MF) {
+        mf_scores(mst, ring0, qm, 1, -1, lane, a.scale_log2);
+        mf_pv(mst, ring1, lane);
+      } else if constexpr (SC4) {
         const bool r1 = tile_scores4<KT, D, G>(m4, l4, pbuf, abuf, ring0, q, qbias, &sbuf[0][0],
                                                &sbuf[0][LOWBIT ? C::ROUND_ROWS : 0], 1, -1, r16, s4, a.scale_log2);
         tile_pv4<KT, D, G>(st, pbuf, abuf, r1, ring1, rg, s);
@@ -1480,101 +1597,157 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     }
   }
 
-  // ---- merge the partials of the SLOTS x 8 row groups through LDS.  The ring
-  // is free now; it holds every lane's accumulators as X[slot][rg][h][d]
-  // (SLOTS * 8 * G * D floats <= 128 KB), split over the four ring arrays.
-  constexpr int XB = kUnitBytes;  // bytes per ring array
-  static_assert(SLOTS * 8 * G * D * 4 <= kRingUnits * XB, "partials fit the ring");
-  lds_barrier();  // every wavefront is done with the ring
-  if (active) {
+  if constexpr (MF) {
+    // ---- merge the eight wavefronts' states through LDS (the ring is free):
+    // X[wave][h][d] in ring0, the (max, sum) pairs in ring1
+    lds_barrier();  // every wavefront is done with the ring
+    float* xo = reinterpret_cast<float*>(ring0);
+    float* xml = reinterpret_cast<float*>(ring1);
+    const int j = lane & 15, g = lane >> 4;
+    const float lsum = swap32_sum(swap16_sum(mst.l));  // the query's sum over its four lanes
+    if (j < G) {
 #pragma unroll
-    for (int h = 0; h < HW; ++h) {
-      const int hG = hg * HW + h;
-      if constexpr (KV4) {  // the weighted sum's pairs held level + 136
-#pragma unroll
-        for (int e = 0; e < C::NACC; ++e) st.acc[h][e] = fmaf(-kInt4Bias, st.wsum[h], st.acc[h][e]);
-      }
-#pragma unroll
-      for (int c2 = 0; c2 < C::CPL; ++c2) {
-        const int off = ((((slot * 8 + rg) * G + hG) * D) + (c2 * 8 + s) * C::EPV) * 4;
-        float* dst = reinterpret_cast<float*>(ring_at(off / XB) + off % XB);
-#pragma unroll
-        for (int e = 0; e < C::EPV; e += 4)
-          *reinterpret_cast<float4*>(dst + e) =
-              make_float4(st.acc[h][c2 * C::EPV + e], st.acc[h][c2 * C::EPV + e + 1], st.acc[h][c2 * C::EPV + e + 2],
-                          st.acc[h][c2 * C::EPV + e + 3]);
-      }
-      if constexpr (!SC4) {
-        if (s == 0) {
-          w_m[hG][slot * 8 + rg] = st.m[h];
-          w_l[hG][slot * 8 + rg] = st.l[h];
-        }
+      for (int t = 0; t < 8; ++t)
+        *reinterpret_cast<float4*>(xo + ((size_t)wave * G + j) * D + 16 * t + 4 * g) =
+            make_float4(mst.o[t][0], mst.o[t][1], mst.o[t][2], mst.o[t][3]);
+      if (g == 0) {
+        xml[wave * G + j] = mst.m;
+        xml[kDecWaves * G + wave * G + j] = lsum;
       }
     }
-    if constexpr (SC4) {  // (rg, h) state: lanes (r16 = rg, s4) and (rg + 8, s4), s4 % HW = h
-      const float l_pair = l4 + __shfl_xor(l4, 32);
-      if (r16 < 8 && s4 < HW) {
-        w_m[hg * HW + s4][slot * 8 + r16] = m4;
-        w_l[hg * HW + s4][slot * 8 + r16] = l_pair;
+    lds_barrier();
+    // four consecutive output elements per thread: head h = e4 / D
+    float* rec = a.ws1 + (size_t)blockIdx.x * C::REC;
+    for (int e4 = threadIdx.x * 4; e4 < G * D; e4 += kDecodeThreads * 4) {
+      const int h = e4 / D, d = e4 % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < kDecWaves; ++v) M = fmaxf(M, xml[v * G + h]);
+      float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+      float L = 0.f;
+#pragma unroll
+      for (int v = 0; v < kDecWaves; ++v) {
+        const float mv = xml[v * G + h];
+        const float wt = (mv == -INFINITY) ? 0.f : fast_exp2(mv - M);
+        L = fmaf(xml[kDecWaves * G + v * G + h], wt, L);
+        const float4 x = *reinterpret_cast<const float4*>(xo + ((size_t)v * G + h) * D + d);
+        A.x = fmaf(x.x, wt, A.x);
+        A.y = fmaf(x.y, wt, A.y);
+        A.z = fmaf(x.z, wt, A.z);
+        A.w = fmaf(x.w, wt, A.w);
       }
-    }
-  }
-  __syncthreads();
-  constexpr int NP = SLOTS * 8;  // partials per query head
-  static_assert(NP * G <= kDecodeThreads && NP % 4 == 0, "one thread per (partial, head)");
-  if (threadIdx.x < NP * G) {  // weight of partial i of head h in the merged result
-    const int h = threadIdx.x / NP, i = threadIdx.x % NP;
-    float M = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < NP; j += 4) {
-      const float4 m4 = *reinterpret_cast<const float4*>(&w_m[h][j]);
-      M = fmaxf(fmaxf(M, fmaxf(m4.x, m4.y)), fmaxf(m4.z, m4.w));
-    }
-    const float wt = (w_m[h][i] == -INFINITY) ? 0.f : fast_exp2(w_m[h][i] - M);
-    w_w[h][i] = wt;
-    w_lw[h][i] = w_l[h][i] * wt;
-    if (i == 0) w_mt[h] = M;
-  }
-  __syncthreads();
-  // four consecutive output elements per thread
-  float* rec = a.ws1 + (size_t)blockIdx.x * C::REC;
-  for (int e4 = threadIdx.x * 4; e4 < G * D; e4 += kDecodeThreads * 4) {
-    const int h = e4 / D, d = e4 % D;
-    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
-    float L = 0.f;
-#pragma unroll
-    for (int i0 = 0; i0 < NP; i0 += 4) {
-      const float4 wt4 = *reinterpret_cast<const float4*>(&w_w[h][i0]);
-      const float4 lw4 = *reinterpret_cast<const float4*>(&w_lw[h][i0]);
-      L += (lw4.x + lw4.y) + (lw4.z + lw4.w);
-      const float wv[4] = {wt4.x, wt4.y, wt4.z, wt4.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int off = (((i0 + k) * G + h) * D + d) * 4;
-        const float4 x = *reinterpret_cast<const float4*>(ring_at(off / XB) + off % XB);
-        A.x = fmaf(x.x, wv[k], A.x);
-        A.y = fmaf(x.y, wv[k], A.y);
-        A.z = fmaf(x.z, wv[k], A.z);
-        A.w = fmaf(x.w, wv[k], A.w);
-      }
-    }
-    if (w.nparts == 1) {
-      const float inv = 1.f / L;
-      if (BF16) {
+      if (w.nparts == 1) {
+        const float inv = 1.f / L;
         uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + q_off + e4;
         o[0] = (uint16_t)f32_to_bf16_bits(A.x * inv);
         o[1] = (uint16_t)f32_to_bf16_bits(A.y * inv);
         o[2] = (uint16_t)f32_to_bf16_bits(A.z * inv);
         o[3] = (uint16_t)f32_to_bf16_bits(A.w * inv);
       } else {
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + q_off + e4) =
-            make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
+        *reinterpret_cast<float4*>(rec + e4) = A;
+        if (d == 0) {
+          rec[G * D + h] = M;
+          rec[G * D + G + h] = L;
+        }
       }
-    } else {
-      *reinterpret_cast<float4*>(rec + e4) = A;
-      if (d == 0) {
-        rec[G * D + h] = w_mt[h];
-        rec[G * D + G + h] = L;
+    }
+  } else {
+    // ---- merge the partials of the SLOTS x 8 row groups through LDS.  The ring
+    // is free now; it holds every lane's accumulators as X[slot][rg][h][d]
+    // (SLOTS * 8 * G * D floats <= 128 KB), split over the four ring arrays.
+    constexpr int XB = kUnitBytes;  // bytes per ring array
+    static_assert(SLOTS * 8 * G * D * 4 <= kRingUnits * XB, "partials fit the ring");
+    lds_barrier();  // every wavefront is done with the ring
+    if (active) {
+  #pragma unroll
+      for (int h = 0; h < HW; ++h) {
+        const int hG = hg * HW + h;
+        if constexpr (KV4) {  // the weighted sum's pairs held level + 136
+  #pragma unroll
+          for (int e = 0; e < C::NACC; ++e) st.acc[h][e] = fmaf(-kInt4Bias, st.wsum[h], st.acc[h][e]);
+        }
+  #pragma unroll
+        for (int c2 = 0; c2 < C::CPL; ++c2) {
+          const int off = ((((slot * 8 + rg) * G + hG) * D) + (c2 * 8 + s) * C::EPV) * 4;
+          float* dst = reinterpret_cast<float*>(ring_at(off / XB) + off % XB);
+  #pragma unroll
+          for (int e = 0; e < C::EPV; e += 4)
+            *reinterpret_cast<float4*>(dst + e) =
+                make_float4(st.acc[h][c2 * C::EPV + e], st.acc[h][c2 * C::EPV + e + 1], st.acc[h][c2 * C::EPV + e + 2],
+                            st.acc[h][c2 * C::EPV + e + 3]);
+        }
+        if constexpr (!SC4) {
+          if (s == 0) {
+            w_m[hG][slot * 8 + rg] = st.m[h];
+            w_l[hG][slot * 8 + rg] = st.l[h];
+          }
+        }
+      }
+      if constexpr (SC4) {  // (rg, h) state: lanes (r16 = rg, s4) and (rg + 8, s4), s4 % HW = h
+        const float l_pair = l4 + __shfl_xor(l4, 32);
+        if (r16 < 8 && s4 < HW) {
+          w_m[hg * HW + s4][slot * 8 + r16] = m4;
+          w_l[hg * HW + s4][slot * 8 + r16] = l_pair;
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int NP = SLOTS * 8;  // partials per query head
+    static_assert(NP * G <= kDecodeThreads && NP % 4 == 0, "one thread per (partial, head)");
+    if (threadIdx.x < NP * G) {  // weight of partial i of head h in the merged result
+      const int h = threadIdx.x / NP, i = threadIdx.x % NP;
+      float M = -INFINITY;
+  #pragma unroll
+      for (int j = 0; j < NP; j += 4) {
+        const float4 m4 = *reinterpret_cast<const float4*>(&w_m[h][j]);
+        M = fmaxf(fmaxf(M, fmaxf(m4.x, m4.y)), fmaxf(m4.z, m4.w));
+      }
+      const float wt = (w_m[h][i] == -INFINITY) ? 0.f : fast_exp2(w_m[h][i] - M);
+      w_w[h][i] = wt;
+      w_lw[h][i] = w_l[h][i] * wt;
+      if (i == 0) w_mt[h] = M;
+    }
+    __syncthreads();
+    // four consecutive output elements per thread
+    float* rec = a.ws1 + (size_t)blockIdx.x * C::REC;
+    for (int e4 = threadIdx.x * 4; e4 < G * D; e4 += kDecodeThreads * 4) {
+      const int h = e4 / D, d = e4 % D;
+      float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+      float L = 0.f;
+  #pragma unroll
+      for (int i0 = 0; i0 < NP; i0 += 4) {
+        const float4 wt4 = *reinterpret_cast<const float4*>(&w_w[h][i0]);
+        const float4 lw4 = *reinterpret_cast<const float4*>(&w_lw[h][i0]);
+        L += (lw4.x + lw4.y) + (lw4.z + lw4.w);
+        const float wv[4] = {wt4.x, wt4.y, wt4.z, wt4.w};
+  #pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int off = (((i0 + k) * G + h) * D + d) * 4;
+          const float4 x = *reinterpret_cast<const float4*>(ring_at(off / XB) + off % XB);
+          A.x = fmaf(x.x, wv[k], A.x);
+          A.y = fmaf(x.y, wv[k], A.y);
+          A.z = fmaf(x.z, wv[k], A.z);
+          A.w = fmaf(x.w, wv[k], A.w);
+        }
+      }
+      if (w.nparts == 1) {
+        const float inv = 1.f / L;
+        if (BF16) {
+          uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + q_off + e4;
+          o[0] = (uint16_t)f32_to_bf16_bits(A.x * inv);
+          o[1] = (uint16_t)f32_to_bf16_bits(A.y * inv);
+          o[2] = (uint16_t)f32_to_bf16_bits(A.z * inv);
+          o[3] = (uint16_t)f32_to_bf16_bits(A.w * inv);
+        } else {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + q_off + e4) =
+              make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
+        }
+      } else {
+        *reinterpret_cast<float4*>(rec + e4) = A;
+        if (d == 0) {
+          rec[G * D + h] = w_mt[h];
+          rec[G * D + G + h] = L;
+        }
       }
     }
   }
