@@ -300,10 +300,10 @@ struct DecodeCfg {
   static constexpr int CPL = KV4 ? 1 : CPR / 8;  // V pieces per lane
   static constexpr int EPC = KV4 ? 32 : 16 / KES;  // elements per 16-byte chunk
   static constexpr int EPV = KV4 ? 16 : EPC;     // elements per V piece
-  // bf16 rows with eight query heads per KV head: scores and weighted sums on
-  // the matrix cores (see mf_scores), each wavefront taking all eight heads
-  // over its own 16 rows of a round
-  static constexpr bool MF = KT == 1 && D == 128 && G == 8;
+  // bf16 rows, d = 128: scores and weighted sums on the matrix cores (see
+  // mf_scores), each wavefront taking all the group's query heads over its
+  // own 16 rows of a round
+  static constexpr bool MF = KT == 1 && D == 128;
   static constexpr int HW = MF ? G : (G < 4 ? G : 4);  // query heads per wavefront
   static constexpr int HSPLIT = G / HW;          // wavefronts per slot
   static constexpr int SLOTS_W = kDecWaves / HSPLIT;
@@ -1175,11 +1175,11 @@ __device__ __forceinline__ void tile_pv4(DecodeState<KT, D, G>& st, const uint16
   }
 }
 
-// ---- matrix-core tiles (bf16 rows, d = 128, eight query heads)
+// ---- matrix-core tiles (bf16 rows, d = 128)
 //
-// A wavefront scores its 16 rows of a round against the group's eight
+// A wavefront scores its 16 rows of a round against the group's g <= 8
 // queries as S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (keys on M, queries
-// on N; the queries fill 8 of the 16 columns, the others are zero), and
+// on N; the queries fill g of the 16 columns, the others are zero), and
 // accumulates O^T += V^T P^T with v_mfma_f32_16x16x16_bf16 (d on M).  Lane
 // l = 16 g + j holds query j: its scores of rows 4 g .. 4 g + 3, the bf16
 // probabilities of those rows (the B operand of the weighted sum as they
