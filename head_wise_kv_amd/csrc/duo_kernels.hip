@@ -300,10 +300,10 @@ struct DecodeCfg {
   static constexpr int CPL = KV4 ? 1 : CPR / 8;  // V pieces per lane
   static constexpr int EPC = KV4 ? 32 : 16 / KES;  // elements per 16-byte chunk
   static constexpr int EPV = KV4 ? 16 : EPC;     // elements per V piece
-  // bf16 rows, d = 128: scores and weighted sums on the matrix cores (see
-  // mf_scores), each wavefront taking all the group's query heads over its
-  // own 16 rows of a round
-  static constexpr bool MF = KT == 1 && D == 128;
+  // bf16 and FP8 rows, d = 128: scores and weighted sums on the matrix cores
+  // (see mf_scores, mf8_scores), each wavefront taking all the group's query
+  // heads over its own rows of a round (16 bf16 or 32 FP8 rows)
+  static constexpr bool MF = (KT == 1 || KT == 2) && D == 128;
   static constexpr int HW = MF ? G : (G < 4 ? G : 4);  // query heads per wavefront
   static constexpr int HSPLIT = G / HW;          // wavefronts per slot
   static constexpr int SLOTS_W = kDecWaves / HSPLIT;
@@ -1194,6 +1194,7 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int mf_swz_k(int r) { return r & 15; }
 __device__ __forceinline__ int mf_swz_v(int r) { return 4 * (r & 3); }
@@ -1201,7 +1202,9 @@ __device__ __forceinline__ int mf_swz_v(int r) { return 4 * (r & 3); }
 struct MfState {
   f32x4_t o[8];    // O^T tiles: d = 16 t + 4 g + e of query j
   float m, l;      // running max (log2 units; the same in the four lanes of a query) and the lane's partial sum
-  uint32_t p[2];   // the current tile's probabilities: rows 4 g .. 4 g + 3 as two bf16 pairs
+  // the current tile's probabilities as bf16 pairs: rows 4 g .. 4 g + 3
+  // (FP8 rows: then rows 16 + 4 g .. 16 + 4 g + 3, each times its V scale)
+  uint32_t p[4];
 };
 
 __device__ __forceinline__ void mf_init(MfState& st) {
@@ -1209,7 +1212,7 @@ __device__ __forceinline__ void mf_init(MfState& st) {
   for (int t = 0; t < 8; ++t) st.o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   st.m = -INFINITY;
   st.l = 0.f;
-  st.p[0] = st.p[1] = 0u;
+  st.p[0] = st.p[1] = st.p[2] = st.p[3] = 0u;
 }
 
 // Scores of the tile's rows (nv valid; row excl, tile-relative, masked; -1
@@ -1262,6 +1265,113 @@ __device__ __forceinline__ void mf_pv(MfState& st, const char* vt, int lane) {
     const char* ptr = vt + row * 256 + (((col >> 3) ^ mf_swz_v(row)) * 16) + (col & 7) * 2;
     const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(ptr));
     st.o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, st.o[t], 0, 0, 0);
+  }
+}
+
+// ---- matrix-core tiles over FP8 rows (d = 128, 128-byte rows)
+//
+// A wavefront takes 32 rows of a round, two groups of 16 for the scores.
+// The K operand is key j's 8 codes 32 k + 8 g .. (an 8-byte read), turned
+// into bf16 exactly (every E4M3 value is a bf16 value); the scores are then
+// scaled by their rows' K scales.  The weighted sum contracts over all 32
+// rows at once with v_mfma_f32_16x16x32_bf16: lane 16 g + j's eight
+// contraction slots are its own rows 4 g .. 4 g + 3 and 16 + 4 g .. + 3,
+// whose probabilities (times the rows' V scales, in bf16) it already holds;
+// the V^T operand comes from a transpose read of bytes (ds_read_b64_tr_b8:
+// lane i of a 16-lane group receives byte column i of the eight rows the
+// group's lanes 2 e and 2 e + 1 address), each lane addressing the row of
+// its group's slot e >> 1.  The denominator adds the same rounded values
+// divided back by the V scales.  Chunk swizzles: K chunk c of row r at
+// c ^ ((r >> 1) & 7); V at c ^ ((r >> 1) & 7) ^ 4 ((r >> 4) & 1); both reads
+// are then free of bank conflicts.
+__device__ __forceinline__ int mf8_swz_k(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int mf8_swz_v(int r) { return ((r >> 1) & 7) ^ (4 * ((r >> 4) & 1)); }
+
+// eight FP8 codes (two words) as an exact bf16 operand
+__device__ __forceinline__ bf16x8v_t fp8x8_bf16(uint32_t w0, uint32_t w1) {
+  const u32x4_t v = {fp8x2_bf16<false>(w0), fp8x2_bf16<true>(w0), fp8x2_bf16<false>(w1), fp8x2_bf16<true>(w1)};
+  return __builtin_bit_cast(bf16x8v_t, v);
+}
+
+__device__ __forceinline__ void mf8_scores(MfState& st, const char* kt, const bf16x8v_t (&qm)[4], const float* ks,
+                                           const float* vs, int nv, int excl, int lane, float scale_log2) {
+  const int j = lane & 15, g = lane >> 4;
+  f32x4_t sc[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    sc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int row = 16 * q + j;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = 2 * k + (g >> 1);
+      const u32x2_t w = *reinterpret_cast<const u32x2_t*>(kt + row * 128 + ((c ^ mf8_swz_k(row)) * 16) + 8 * (g & 1));
+      sc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_bf16(w[0], w[1]), qm[k], sc[q], 0, 0, 0);
+    }
+  }
+  float vsc[2][4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const float4 k4 = *reinterpret_cast<const float4*>(ks + 16 * q + 4 * g);
+    const float4 v4 = *reinterpret_cast<const float4*>(vs + 16 * q + 4 * g);
+    sc[q][0] *= k4.x;
+    sc[q][1] *= k4.y;
+    sc[q][2] *= k4.z;
+    sc[q][3] *= k4.w;
+    vsc[q][0] = v4.x;
+    vsc[q][1] = v4.y;
+    vsc[q][2] = v4.z;
+    vsc[q][3] = v4.w;
+  }
+  if (nv < 32 || excl >= 0) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * q + 4 * g + e;
+        if (r >= nv || r == excl) sc[q][e] = -INFINITY;
+      }
+  }
+  const float m8 = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+  const float mx = swap32_max(swap16_max(m8)) * scale_log2;
+  if (__builtin_amdgcn_ballot_w64(mx > st.m + kRescaleSlack) != 0) {
+    const float mn = fmaxf(st.m, mx);
+    const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(st.m - mn);
+    st.m = mn;
+    st.l *= alpha;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) st.o[t] *= alpha;
+  }
+  const float mu = (st.m == -INFINITY) ? 0.f : st.m;
+  float l = st.l;
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      const float p0 = fast_exp2(fmaf(sc[q][e], scale_log2, -mu));
+      const float p1 = fast_exp2(fmaf(sc[q][e + 1], scale_log2, -mu));
+      const uint32_t pp = pack_bf16x2(p0 * vsc[q][e], p1 * vsc[q][e + 1]);
+      st.p[2 * q + e / 2] = pp;
+      // the weight the weighted sum applies, divided back by the V scale (a
+      // row of zeros, scale 0, adds its probability itself)
+      l += vsc[q][e] > 0.f ? bf_lo(pp) * __builtin_amdgcn_rcpf(vsc[q][e]) : p0;
+      l += vsc[q][e + 1] > 0.f ? bf_hi(pp) * __builtin_amdgcn_rcpf(vsc[q][e + 1]) : p1;
+    }
+  st.l = l;
+}
+
+__device__ __forceinline__ void mf8_pv(MfState& st, const char* vt, int lane) {
+  const int i16 = lane & 15, g = lane >> 4;
+  const bf16x8v_t pb = __builtin_bit_cast(bf16x8v_t, u32x4_t{st.p[0], st.p[1], st.p[2], st.p[3]});
+  const int e = i16 >> 1;                                    // the group's slot this lane addresses
+  const int row = e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);  // that slot's row
+  const int half = i16 & 1;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const char* ptr = vt + row * 128 + ((t ^ mf8_swz_v(row)) * 16) + 8 * half;
+    const u32x2_t v = __builtin_bit_cast(
+        u32x2_t, __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(ptr)));
+    st.o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_bf16(v[0], v[1]), pb, st.o[t], 0, 0, 0);
   }
 }
 
@@ -1349,8 +1459,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     const int off = (wave + kDecWaves * j) * 1024 + lane * 16;
     const int r = off / C::ROWB;  // row of the round; a slot's tile starts at a multiple of 4 rows
     const int c = (off % C::ROWB) / 16;
-    const int ck = c ^ (MF ? mf_swz_k(r % TR) : SC4 ? dec_swz_k4<C::CPR>(r % TR) : dec_swz<C::CPR>(r % TR));
-    const int cv = c ^ (MF ? mf_swz_v(r % TR) : dec_swz<C::CPR>(r % TR));
+    const int ck = c ^ (MF ? (KV8 ? mf8_swz_k(r % TR) : mf_swz_k(r % TR))
+                          : SC4 ? dec_swz_k4<C::CPR>(r % TR) : dec_swz<C::CPR>(r % TR));
+    const int cv = c ^ (MF ? (KV8 ? mf8_swz_v(r % TR) : mf_swz_v(r % TR)) : dec_swz<C::CPR>(r % TR));
     poff_k[j] = (uint32_t)(r * C::ROWB + ck * 16);
     poff_v[j] = (uint32_t)(r * C::ROWB + cv * 16);
   }
@@ -1487,7 +1598,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     const int nv = active ? (int)(left < 0 ? 0 : (left > TR ? TR : left)) : 0;
     const char* tile = rings[X] + slot * C::SLOT_BYTES;
     if (V_PART) {
-      if constexpr (MF) {
+      if constexpr (MF && KV8) {
+        if (nv > 0) mf8_pv(mst, tile, lane);
+      } else if constexpr (MF) {
         if (nv > 0) mf_pv(mst, tile, lane);
       } else if constexpr (SC4) {
         if (nv > 0) tile_pv4<KT, D, G>(st, pbuf, abuf, resc, tile, rg, s);
@@ -1497,7 +1610,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     } else {
       const int64_t ex = excl_row - row0;
       const int exr = (ex >= 0 && ex < TR) ? (int)ex : -1;
-      if constexpr (MF) {
+      if constexpr (MF && KV8) {
+        const float* ks = &sbuf[(u >> 1) & 1][slot * TR];
+        if (nv > 0) mf8_scores(mst, tile, qm, ks, ks + C::ROUND_ROWS, nv, exr, lane, a.scale_log2);
+      } else if constexpr (MF) {
         if (nv > 0) mf_scores(mst, tile, qm, nv, exr, lane, a.scale_log2);
       } else if constexpr (SC4) {
         resc = false;
@@ -1555,7 +1671,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     }
     lds_barrier();
     if (slot == 0) {
-      if constexpr (MF) {
+      if constexpr (MF && KV8) {
+        mf8_scores(mst, ring0, qm, &sbuf[0][0], &sbuf[0][C::ROUND_ROWS], 1, -1, lane, a.scale_log2);
+        mf8_pv(mst, ring1, lane);
+      } else if constexpr (MF) {
         mf_scores(mst, ring0, qm, 1, -1, lane, a.scale_log2);
         mf_pv(mst, ring1, lane);
       } else if constexpr (SC4) {
