@@ -300,10 +300,11 @@ struct DecodeCfg {
   static constexpr int CPL = KV4 ? 1 : CPR / 8;  // V pieces per lane
   static constexpr int EPC = KV4 ? 32 : 16 / KES;  // elements per 16-byte chunk
   static constexpr int EPV = KV4 ? 16 : EPC;     // elements per V piece
-  // bf16 and FP8 rows, d = 128: scores and weighted sums on the matrix cores
-  // (see mf_scores, mf8_scores), each wavefront taking all the group's query
-  // heads over its own rows of a round (16 bf16 or 32 FP8 rows)
-  static constexpr bool MF = (KT == 1 || KT == 2) && D == 128;
+  // bf16, FP8 and INT4 rows, d = 128: scores and weighted sums on the matrix
+  // cores (see mf_scores, mf8_scores, mf4_scores), each wavefront taking all
+  // the group's query heads over its own rows of a round (16 bf16, 32 FP8 or
+  // 64 INT4 rows)
+  static constexpr bool MF = KT >= 1 && D == 128;
   static constexpr int HW = MF ? G : (G < 4 ? G : 4);  // query heads per wavefront
   static constexpr int HSPLIT = G / HW;          // wavefronts per slot
   static constexpr int SLOTS_W = kDecWaves / HSPLIT;
@@ -1203,8 +1204,10 @@ struct MfState {
   f32x4_t o[8];    // O^T tiles: d = 16 t + 4 g + e of query j
   float m, l;      // running max (log2 units; the same in the four lanes of a query) and the lane's partial sum
   // the current tile's probabilities as bf16 pairs: rows 4 g .. 4 g + 3
-  // (FP8 rows: then rows 16 + 4 g .. 16 + 4 g + 3, each times its V scale)
-  uint32_t p[4];
+  // (FP8 rows: then rows 16 + 4 g .. + 3; INT4 rows: 16 q + 4 g .. + 3 for
+  // q = 0 .. 3; low-bit rows each times its V scale)
+  uint32_t p[8];
+  float w;         // INT4 rows: the lane's sum of the weights it applied (the levels' bias, see mf4_pv)
 };
 
 __device__ __forceinline__ void mf_init(MfState& st) {
@@ -1212,7 +1215,9 @@ __device__ __forceinline__ void mf_init(MfState& st) {
   for (int t = 0; t < 8; ++t) st.o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   st.m = -INFINITY;
   st.l = 0.f;
-  st.p[0] = st.p[1] = st.p[2] = st.p[3] = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) st.p[i] = 0u;
+  st.w = 0.f;
 }
 
 // Scores of the tile's rows (nv valid; row excl, tile-relative, masked; -1
@@ -1375,6 +1380,116 @@ __device__ __forceinline__ void mf8_pv(MfState& st, const char* vt, int lane) {
   }
 }
 
+// ---- matrix-core tiles over INT4 rows (d = 128, 64-byte rows)
+//
+// A wavefront takes 64 rows of a round, four groups of 16 for the scores.
+// The K operand is key j's eight codes 32 k + 8 g .. (a 4-byte read), each
+// nibble n read as the bf16 value 128 + n = c + 136 (see int4_pair); the
+// scores then drop 136 times the query's element sum and take their rows'
+// K scales.  The weighted sum runs two v_mfma_f32_16x16x32_bf16 per d tile:
+// a 4-bit transpose read (ds_read_b64_tr_b4: lane i of a 16-lane group
+// receives element i of the 16 rows its group's lanes address, one nibble
+// per row) gives a lane element d = 16 t + i of the 16 rows 16 q + 4 g + b
+// its group holds probabilities for, the first eight (q = 0, 1) for one
+// MFMA and the last eight for the other.  The accumulators then exceed the
+// weighted sums over the levels by 136 times the sum of the weights, which
+// the merge subtracts.  Chunk swizzles: K chunk c of row r at c ^ ((r >> 2)
+// & 3), V at c ^ ((r >> 4) & 3); both reads are free of bank conflicts.
+__device__ __forceinline__ int mf4_swz_k(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int mf4_swz_v(int r) { return (r >> 4) & 3; }
+
+// eight INT4 codes (one word, element 2k in the low nibble of byte k) as
+// the bf16 operand of their values + 136
+__device__ __forceinline__ bf16x8v_t int4x8_bf16(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  const u32x4_t v = {int4_pair<0>(lo, hi), int4_pair<1>(lo, hi), int4_pair<2>(lo, hi), int4_pair<3>(lo, hi)};
+  return __builtin_bit_cast(bf16x8v_t, v);
+}
+
+__device__ __forceinline__ void mf4_scores(MfState& st, const char* kt, const bf16x8v_t (&qm)[4], float qbias,
+                                           const float* ks, const float* vs, int nv, int excl, int lane,
+                                           float scale_log2) {
+  const int j = lane & 15, g = lane >> 4;
+  f32x4_t sc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    sc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int row = 16 * q + j;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(kt + row * 64 + ((k ^ mf4_swz_k(row)) * 16) + 4 * g);
+      sc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(int4x8_bf16(w), qm[k], sc[q], 0, 0, 0);
+    }
+  }
+  float vsc[4][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 k4 = *reinterpret_cast<const float4*>(ks + 16 * q + 4 * g);
+    const float4 v4 = *reinterpret_cast<const float4*>(vs + 16 * q + 4 * g);
+    sc[q][0] = (sc[q][0] - qbias) * k4.x;
+    sc[q][1] = (sc[q][1] - qbias) * k4.y;
+    sc[q][2] = (sc[q][2] - qbias) * k4.z;
+    sc[q][3] = (sc[q][3] - qbias) * k4.w;
+    vsc[q][0] = v4.x;
+    vsc[q][1] = v4.y;
+    vsc[q][2] = v4.z;
+    vsc[q][3] = v4.w;
+  }
+  if (nv < 64 || excl >= 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * q + 4 * g + e;
+        if (r >= nv || r == excl) sc[q][e] = -INFINITY;
+      }
+  }
+  float m16 = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) m16 = fmaxf(m16, fmaxf(fmaxf(sc[q][0], sc[q][1]), fmaxf(sc[q][2], sc[q][3])));
+  const float mx = swap32_max(swap16_max(m16)) * scale_log2;
+  if (__builtin_amdgcn_ballot_w64(mx > st.m + kRescaleSlack) != 0) {
+    const float mn = fmaxf(st.m, mx);
+    const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(st.m - mn);
+    st.m = mn;
+    st.l *= alpha;
+    st.w *= alpha;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) st.o[t] *= alpha;
+  }
+  const float mu = (st.m == -INFINITY) ? 0.f : st.m;
+  float l = st.l, wsum = st.w;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      const float p0 = fast_exp2(fmaf(sc[q][e], scale_log2, -mu));
+      const float p1 = fast_exp2(fmaf(sc[q][e + 1], scale_log2, -mu));
+      const uint32_t pp = pack_bf16x2(p0 * vsc[q][e], p1 * vsc[q][e + 1]);
+      st.p[2 * q + e / 2] = pp;
+      wsum += bf_lo(pp) + bf_hi(pp);
+      l += vsc[q][e] > 0.f ? bf_lo(pp) * __builtin_amdgcn_rcpf(vsc[q][e]) : p0;
+      l += vsc[q][e + 1] > 0.f ? bf_hi(pp) * __builtin_amdgcn_rcpf(vsc[q][e + 1]) : p1;
+    }
+  st.l = l;
+  st.w = wsum;
+}
+
+__device__ __forceinline__ void mf4_pv(MfState& st, const char* vt, int lane) {
+  const int i16 = lane & 15, g = lane >> 4;
+  const bf16x8v_t pa = __builtin_bit_cast(bf16x8v_t, u32x4_t{st.p[0], st.p[1], st.p[2], st.p[3]});
+  const bf16x8v_t pb = __builtin_bit_cast(bf16x8v_t, u32x4_t{st.p[4], st.p[5], st.p[6], st.p[7]});
+  const int row = 16 * (i16 >> 2) + 4 * g + (i16 & 3);  // the row this lane addresses: slot i16 of its group
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const char* ptr = vt + row * 64 + (((t >> 1) ^ mf4_swz_v(row)) * 16) + 8 * (t & 1);
+    const u32x2_t v = __builtin_bit_cast(
+        u32x2_t, __builtin_amdgcn_ds_read_tr4_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(ptr)));
+    st.o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(int4x8_bf16(v[0]), pa, st.o[t], 0, 0, 0);
+    st.o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(int4x8_bf16(v[1]), pb, st.o[t], 0, 0, 0);
+  }
+}
+
 template <int X>
 using UnitTag = std::integral_constant<int, X>;
 
@@ -1459,9 +1574,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     const int off = (wave + kDecWaves * j) * 1024 + lane * 16;
     const int r = off / C::ROWB;  // row of the round; a slot's tile starts at a multiple of 4 rows
     const int c = (off % C::ROWB) / 16;
-    const int ck = c ^ (MF ? (KV8 ? mf8_swz_k(r % TR) : mf_swz_k(r % TR))
+    const int ck = c ^ (MF ? (KV4 ? mf4_swz_k(r % TR) : KV8 ? mf8_swz_k(r % TR) : mf_swz_k(r % TR))
                           : SC4 ? dec_swz_k4<C::CPR>(r % TR) : dec_swz<C::CPR>(r % TR));
-    const int cv = c ^ (MF ? (KV8 ? mf8_swz_v(r % TR) : mf_swz_v(r % TR)) : dec_swz<C::CPR>(r % TR));
+    const int cv = c ^ (MF ? (KV4 ? mf4_swz_v(r % TR) : KV8 ? mf8_swz_v(r % TR) : mf_swz_v(r % TR))
+                          : dec_swz<C::CPR>(r % TR));
     poff_k[j] = (uint32_t)(r * C::ROWB + ck * 16);
     poff_v[j] = (uint32_t)(r * C::ROWB + cv * 16);
   }
@@ -1575,14 +1691,21 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   // elements 32 k + 8 g .. + 7 of k-step k; columns 8 .. 15 zero) and the state
   bf16x8v_t qm[4];
   MfState mst;
+  float mqbias = 0.f;  // INT4 rows: 136 times the lane's query's element sum
   if constexpr (MF) {
     const int j = lane & 15, g = lane >> 4;
+    float qs = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const u32x4_t v = j < G ? *reinterpret_cast<const u32x4_t*>(stage + (size_t)j * C::IROWB + (32 * k + 8 * g) * 2)
                               : u32x4_t{0u, 0u, 0u, 0u};
       qm[k] = __builtin_bit_cast(bf16x8v_t, v);
+      if constexpr (KV4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qs += bf_lo(v[i]) + bf_hi(v[i]);
+      }
     }
+    if constexpr (KV4) mqbias = swap32_sum(swap16_sum(qs)) * kInt4Bias;
     mf_init(mst);
   }
 
@@ -1598,7 +1721,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     const int nv = active ? (int)(left < 0 ? 0 : (left > TR ? TR : left)) : 0;
     const char* tile = rings[X] + slot * C::SLOT_BYTES;
     if (V_PART) {
-      if constexpr (MF && KV8) {
+      if constexpr (MF && KV4) {
+        if (nv > 0) mf4_pv(mst, tile, lane);
+      } else if constexpr (MF && KV8) {
         if (nv > 0) mf8_pv(mst, tile, lane);
       } else if constexpr (MF) {
         if (nv > 0) mf_pv(mst, tile, lane);
@@ -1610,9 +1735,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     } else {
       const int64_t ex = excl_row - row0;
       const int exr = (ex >= 0 && ex < TR) ? (int)ex : -1;
-      if constexpr (MF && KV8) {
+      if constexpr (MF && LOWBIT) {
         const float* ks = &sbuf[(u >> 1) & 1][slot * TR];
-        if (nv > 0) mf8_scores(mst, tile, qm, ks, ks + C::ROUND_ROWS, nv, exr, lane, a.scale_log2);
+        if constexpr (KV4) {
+          if (nv > 0) mf4_scores(mst, tile, qm, mqbias, ks, ks + C::ROUND_ROWS, nv, exr, lane, a.scale_log2);
+        } else {
+          if (nv > 0) mf8_scores(mst, tile, qm, ks, ks + C::ROUND_ROWS, nv, exr, lane, a.scale_log2);
+        }
       } else if constexpr (MF) {
         if (nv > 0) mf_scores(mst, tile, qm, nv, exr, lane, a.scale_log2);
       } else if constexpr (SC4) {
@@ -1671,7 +1800,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     }
     lds_barrier();
     if (slot == 0) {
-      if constexpr (MF && KV8) {
+      if constexpr (MF && KV4) {
+        mf4_scores(mst, ring0, qm, mqbias, &sbuf[0][0], &sbuf[0][C::ROUND_ROWS], 1, -1, lane, a.scale_log2);
+        mf4_pv(mst, ring1, lane);
+      } else if constexpr (MF && KV8) {
         mf8_scores(mst, ring0, qm, &sbuf[0][0], &sbuf[0][C::ROUND_ROWS], 1, -1, lane, a.scale_log2);
         mf8_pv(mst, ring1, lane);
       } else if constexpr (MF) {
@@ -1724,6 +1856,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     float* xml = reinterpret_cast<float*>(ring1);
     const int j = lane & 15, g = lane >> 4;
     const float lsum = swap32_sum(swap16_sum(mst.l));  // the query's sum over its four lanes
+    if constexpr (KV4) {  // the accumulators held the levels + 136: drop 136 times the weights' sum
+      const float wb = swap32_sum(swap16_sum(mst.w)) * kInt4Bias;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) mst.o[t] -= wb;
+    }
     if (j < G) {
 #pragma unroll
       for (int t = 0; t < 8; ++t)
