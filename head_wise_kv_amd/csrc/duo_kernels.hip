@@ -320,6 +320,7 @@ struct DecodeCfg {
   static_assert(RPL >= 2 && RPL % 2 == 0, "rows are paired for the weighted sum");
   static_assert(SLOT_BYTES % 1024 == 0, "a load piece stays within one tile");
   static_assert(G % HW == 0, "head split must tile the group");
+  static_assert(!LOWBIT || MF, "FP8 and INT4 rows are decoded on the matrix cores, at d = 128");
 };
 
 // Chunk slot of chunk c of row r in LDS.
@@ -775,9 +776,6 @@ struct DecodeState {
   using C = DecodeCfg<KT, D, G>;
   float m[C::HW], l[C::HW];
   float acc[C::HW][C::NACC];
-  // INT4 rows: the sum of the (rounded) weights the lane's weighted sum
-  // applied, times which the accumulators exceed the sum over the levels
-  float wsum[C::KV4 ? C::HW : 1];
 };
 
 // Scores of the lane's rows against its HW queries, online-softmax update,
@@ -936,7 +934,6 @@ struct Score4 {
   static constexpr int RPL4 = C::TR / 16;   // rows per lane
   static constexpr int NQ = C::RPL / 2;     // row pairs per weighted-sum lane
   static constexpr int PBUF = 8 * NQ * HW;  // probability pairs per wavefront (dwords)
-  static constexpr int QPC = C::EPC >= 8 ? C::EPC / 8 : 1;  // 16-byte query pieces per stored chunk (FP8 rows: 2)
   static_assert(!ON || 4 % HW == 0, "heads per wavefront divide the 4 lanes of a row");
 };
 
@@ -983,12 +980,10 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_ca
 template <int KT, int D, int G>
 __device__ __forceinline__ bool tile_scores4(float& m, float& l, uint16_t* pbuf, float* abuf, const char* kt,
                                              const uint4 (&q)[Score4<KT, D, G>::HW]
-                                                             [Score4<KT, D, G>::CPL4 * Score4<KT, D, G>::QPC],
-                                             const float (&qbias)[Score4<KT, D, G>::HW],
-                                             const float* ksc, const float* vsc, int nv, int excl, int r16, int s4,
-                                             float scale_log2) {
+                                                             [Score4<KT, D, G>::CPL4],
+                                             int nv, int excl, int r16, int s4, float scale_log2) {
   using C = DecodeCfg<KT, D, G>;
-  [[maybe_unused]] constexpr bool BF16 = C::BF16;
+  static_assert(C::BF16 && !C::LOWBIT, "the four-lane layout serves bf16 rows (low-bit rows take the matrix cores)");
   using S4 = Score4<KT, D, G>;
   constexpr int HW = S4::HW;
   const int hown = s4 % HW;  // the head whose state this lane keeps
@@ -1006,52 +1001,19 @@ __device__ __forceinline__ bool tile_scores4(float& m, float& l, uint16_t* pbuf,
 #pragma unroll
     for (int cc = 0; cc < S4::CPL4; ++cc) {
       const uint32_t kw[4] = {k[cc].x, k[cc].y, k[cc].z, k[cc].w};
-      if constexpr (C::KV4) {
-        // 32 codes: dword i holds elements 8i .. 8i+7, against query piece i
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t lo = kw[i] & 0x0F0F0F0Fu, hi = (kw[i] >> 4) & 0x0F0F0F0Fu;
-          const uint32_t kb[4] = {int4_pair<0>(lo, hi), int4_pair<1>(lo, hi), int4_pair<2>(lo, hi),
-                                  int4_pair<3>(lo, hi)};
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int h = 0; h < HW; ++h) {
-            const uint4 qv = q[h][4 * cc + i];
-            const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-            for (int t = 0; t < 4; ++t) acc[h] = dot2_bf16(qw[t], kb[t], acc[h]);
-          }
+        for (int h = 0; h < HW; ++h) {
+          const uint32_t qw[4] = {q[h][cc].x, q[h][cc].y, q[h][cc].z, q[h][cc].w};
+          acc[h] = dot2_bf16(qw[i], kw[i], acc[h]);
         }
-      } else if constexpr (C::KV8) {
-        // 16 codes -> 8 bf16 pairs (exact), dotted with the query's values
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t kb[2] = {fp8x2_bf16<false>(kw[i]), fp8x2_bf16<true>(kw[i])};
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int h = 0; h < HW; ++h) {
-              const uint4 qv = q[h][2 * cc + i / 2];
-              const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-              acc[h] = dot2_bf16(qw[(2 * i + t) % 4], kb[t], acc[h]);
-            }
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int h = 0; h < HW; ++h) {
-            const uint32_t qw[4] = {q[h][cc].x, q[h][cc].y, q[h][cc].z, q[h][cc].w};
-            acc[h] = dot2_bf16(qw[i], kw[i], acc[h]);
-          }
-      }
     }
 #pragma unroll
     for (int h = 0; h < HW; ++h) acc[h] = row4_sum(acc[h]);
     float own = acc[0];
 #pragma unroll
     for (int h = 1; h < HW; ++h) own = hown == h ? acc[h] : own;
-    if constexpr (C::KV4) own -= qbias[hown];     // the pairs' +136 times the query's sum
-    if constexpr (C::LOWBIT) own *= ksc[row];  // the K row's scale
     sc[j] = (row < nv && row != excl) ? own : -INFINITY;
   }
   // reference max of (rg, s4), shared with the partner lane 32 away
@@ -1073,16 +1035,12 @@ __device__ __forceinline__ bool tile_scores4(float& m, float& l, uint16_t* pbuf,
 #pragma unroll
   for (int j = 0; j < S4::RPL4; ++j) {
     const float pj = fast_exp2(fmaf(sc[j], scale_log2, -mu));
-    // FP8 rows: the V row's scale joins the probability the weighted sum uses
-    const float vs = C::LOWBIT ? vsc[r16 + 16 * j] : 1.f;
-    const uint16_t pb = bf16_bits(C::LOWBIT ? pj * vs : pj);
-    const float pr = __uint_as_float((uint32_t)pb << 16);
-    // The sum takes the weight the weighted sum really applies to the row --
-    // the rounded probability (divided by the V row's scale for FP8 rows; a
-    // zero row contributes nothing either way) -- so the weights of the result
-    // sum to one: an unrounded sum would leave a relative error of up to 2^-9
-    // in every output element.
-    l += C::LOWBIT ? (vs > 0.f ? pr * __builtin_amdgcn_rcpf(vs) : pj) : pr;
+    const uint16_t pb = bf16_bits(pj);
+    // The sum takes the weight the weighted sum really applies to the row,
+    // the rounded probability, so the weights of the result sum to one: an
+    // unrounded sum would leave a relative error of up to 2^-9 in every
+    // output element.
+    l += __uint_as_float((uint32_t)pb << 16);
     if (s4 < HW) pbuf[((rg * S4::NQ + j) * HW + s4) * 2 + half] = pb;
   }
   return any;
@@ -1094,7 +1052,7 @@ template <int KT, int D, int G>
 __device__ __forceinline__ void tile_pv4(DecodeState<KT, D, G>& st, const uint16_t* pbuf, const float* abuf,
                                          bool rescale, const char* vt, int rg, int s) {
   using C = DecodeCfg<KT, D, G>;
-  [[maybe_unused]] constexpr bool BF16 = C::BF16;
+  static_assert(C::BF16 && !C::LOWBIT, "the four-lane layout serves bf16 rows");
   using S4 = Score4<KT, D, G>;
   constexpr int HW = S4::HW;
   if (rescale) {
@@ -1103,7 +1061,6 @@ __device__ __forceinline__ void tile_pv4(DecodeState<KT, D, G>& st, const uint16
       const float al = abuf[rg * HW + h];
 #pragma unroll
       for (int e = 0; e < C::NACC; ++e) st.acc[h][e] *= al;
-      if constexpr (C::KV4) st.wsum[h] *= al;
     }
   }
 #pragma unroll
@@ -1113,34 +1070,6 @@ __device__ __forceinline__ void tile_pv4(DecodeState<KT, D, G>& st, const uint16
     const uint32_t* pq = reinterpret_cast<const uint32_t*>(pbuf) + (rg * S4::NQ + qq) * HW;
 #pragma unroll
     for (int h = 0; h < HW; ++h) P[h] = pq[h];
-    if constexpr (C::KV4) {
-      // lane s takes bytes 8s .. 8s+7 of both rows: elements 16s .. 16s+15,
-      // dword i of it elements 8i .. 8i+7 (pairs of one row's nibbles by
-      // element, then both rows' values of an element side by side)
-      const uint2 va = *reinterpret_cast<const uint2*>(vt + row0 * C::ROWB + s * 8);
-      const uint2 vb = *reinterpret_cast<const uint2*>(vt + row1 * C::ROWB + s * 8);
-      const uint32_t a2[2] = {va.x, va.y}, b2[2] = {vb.x, vb.y};
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint32_t alo = a2[i] & 0x0F0F0F0Fu, ahi = (a2[i] >> 4) & 0x0F0F0F0Fu;
-        const uint32_t blo = b2[i] & 0x0F0F0F0Fu, bhi = (b2[i] >> 4) & 0x0F0F0F0Fu;
-        // (row0, row1) of element 8i + 2t (low nibbles) and 8i + 2t + 1 (high)
-        const uint32_t pe[4] = {int4_pair<0>(alo, blo), int4_pair<1>(alo, blo), int4_pair<2>(alo, blo),
-                                int4_pair<3>(alo, blo)};
-        const uint32_t po[4] = {int4_pair<0>(ahi, bhi), int4_pair<1>(ahi, bhi), int4_pair<2>(ahi, bhi),
-                                int4_pair<3>(ahi, bhi)};
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int h = 0; h < HW; ++h) {
-            st.acc[h][8 * i + 2 * t] = dot2_bf16(P[h], pe[t], st.acc[h][8 * i + 2 * t]);
-            st.acc[h][8 * i + 2 * t + 1] = dot2_bf16(P[h], po[t], st.acc[h][8 * i + 2 * t + 1]);
-          }
-      }
-#pragma unroll
-      for (int h = 0; h < HW; ++h) st.wsum[h] = dot2_bf16(P[h], 0x3F803F80u, st.wsum[h]);  // + p0 + p1
-      continue;
-    }
 #pragma unroll
     for (int cc = 0; cc < C::CPL; ++cc) {
       const int off = ((s + 8 * cc) ^ dec_swz<C::CPR>(row0)) * 16;
@@ -1150,26 +1079,12 @@ __device__ __forceinline__ void tile_pv4(DecodeState<KT, D, G>& st, const uint16
       const uint32_t b4[4] = {vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if constexpr (C::KV8) {
-          // codes of d = 4i .. 4i+3 of the two rows, interleaved by row, then
-          // converted to the (row0, row1) bf16 pairs the dot products take
-          const uint32_t x0 = __builtin_amdgcn_perm(b4[i], a4[i], 0x05010400u);  // d = 4i, 4i+1
-          const uint32_t x1 = __builtin_amdgcn_perm(b4[i], a4[i], 0x07030602u);  // d = 4i+2, 4i+3
-          const uint32_t pr[4] = {fp8x2_bf16<false>(x0), fp8x2_bf16<true>(x0), fp8x2_bf16<false>(x1),
-                                  fp8x2_bf16<true>(x1)};
+        const uint32_t lo = __builtin_amdgcn_perm(b4[i], a4[i], 0x05040100u);  // (row0, row1) at d = 2i
+        const uint32_t hi = __builtin_amdgcn_perm(b4[i], a4[i], 0x07060302u);  // at d = 2i+1
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int h = 0; h < HW; ++h)
-              st.acc[h][cc * 16 + 4 * i + t] = dot2_bf16(P[h], pr[t], st.acc[h][cc * 16 + 4 * i + t]);
-        } else {
-          const uint32_t lo = __builtin_amdgcn_perm(b4[i], a4[i], 0x05040100u);  // (row0, row1) at d = 2i
-          const uint32_t hi = __builtin_amdgcn_perm(b4[i], a4[i], 0x07060302u);  // at d = 2i+1
-#pragma unroll
-          for (int h = 0; h < HW; ++h) {
-            st.acc[h][cc * 8 + 2 * i] = dot2_bf16(P[h], lo, st.acc[h][cc * 8 + 2 * i]);
-            st.acc[h][cc * 8 + 2 * i + 1] = dot2_bf16(P[h], hi, st.acc[h][cc * 8 + 2 * i + 1]);
-          }
+        for (int h = 0; h < HW; ++h) {
+          st.acc[h][cc * 8 + 2 * i] = dot2_bf16(P[h], lo, st.acc[h][cc * 8 + 2 * i]);
+          st.acc[h][cc * 8 + 2 * i + 1] = dot2_bf16(P[h], hi, st.acc[h][cc * 8 + 2 * i + 1]);
         }
       }
     }
@@ -1644,7 +1559,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   }
   // this wavefront's HW queries, in the lane's slice layout (of the four-lane
   // score layout when it is on)
-  constexpr int QCPL = SC4 ? S4::CPL4 * S4::QPC : C::CPL;
+  constexpr int QCPL = SC4 ? S4::CPL4 : C::CPL;
   const int r16 = lane >> 2, s4 = lane & 3;
   uint4 q[HW][QCPL];
 #pragma unroll
@@ -1653,24 +1568,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     for (int c2 = 0; c2 < QCPL; ++c2)
       q[h][c2] = *reinterpret_cast<const uint4*>(
           stage + (size_t)(hg * HW + h) * C::IROWB +
-          (SC4 ? ((s4 + 4 * (c2 / S4::QPC)) * S4::QPC + c2 % S4::QPC) : (s + 8 * c2)) * 16);
-  // INT4 rows: 136 times each query's sum (the scores' bias, see int4_pair);
-  // the four lanes of a row group hold the query's four quarters
-  float qbias[HW];
-#pragma unroll
-  for (int h = 0; h < HW; ++h) {
-    float sum = 0.f;
-    if constexpr (KV4) {
-#pragma unroll
-      for (int c2 = 0; c2 < QCPL; ++c2) {
-        const uint32_t qw[4] = {q[h][c2].x, q[h][c2].y, q[h][c2].z, q[h][c2].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sum += bf_lo(qw[i]) + bf_hi(qw[i]);
-      }
-      sum = row4_sum(sum) * kInt4Bias;
-    }
-    qbias[h] = sum;
-  }
+          (SC4 ? (s4 + 4 * c2) : (s + 8 * c2)) * 16);
   uint16_t* const pbuf = pbuf_all[SC4 ? wave : 0];
   float* const abuf = abuf_all[SC4 ? wave : 0];
   float m4 = -INFINITY, l4 = 0.f;  // four-lane layout: softmax state of (r16 % 8, head s4)
@@ -1684,8 +1582,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < C::NACC; ++e) st.acc[h][e] = 0.f;
   }
-#pragma unroll
-  for (int h = 0; h < (KV4 ? HW : 1); ++h) st.wsum[h] = 0.f;
   float p[C::RPL][HW];
   // matrix-core tiles: the queries as the B operand (lane 16 g + j: query j,
   // elements 32 k + 8 g .. + 7 of k-step k; columns 8 .. 15 zero) and the state
@@ -1746,10 +1642,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
         if (nv > 0) mf_scores(mst, tile, qm, nv, exr, lane, a.scale_log2);
       } else if constexpr (SC4) {
         resc = false;
-        const float* ks = &sbuf[LOWBIT ? (u >> 1) & 1 : 0][LOWBIT ? slot * TR : 0];
-        const float* vs = ks + (LOWBIT ? C::ROUND_ROWS : 0);
-        if (nv > 0)
-          resc = tile_scores4<KT, D, G>(m4, l4, pbuf, abuf, tile, q, qbias, ks, vs, nv, exr, r16, s4, a.scale_log2);
+        if (nv > 0) resc = tile_scores4<KT, D, G>(m4, l4, pbuf, abuf, tile, q, nv, exr, r16, s4, a.scale_log2);
       } else {
         if (nv > 0) tile_scores<KT, D, G>(st, p, tile, q, nv, exr, rg, s, a.scale_log2);
       }
@@ -1810,8 +1703,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
         mf_scores(mst, ring0, qm, 1, -1, lane, a.scale_log2);
         mf_pv(mst, ring1, lane);
       } else if constexpr (SC4) {
-        const bool r1 = tile_scores4<KT, D, G>(m4, l4, pbuf, abuf, ring0, q, qbias, &sbuf[0][0],
-                                               &sbuf[0][LOWBIT ? C::ROUND_ROWS : 0], 1, -1, r16, s4, a.scale_log2);
+        const bool r1 = tile_scores4<KT, D, G>(m4, l4, pbuf, abuf, ring0, q, 1, -1, r16, s4, a.scale_log2);
         tile_pv4<KT, D, G>(st, pbuf, abuf, r1, ring1, rg, s);
       } else {
         tile_scores<KT, D, G>(st, p, ring0, q, 1, -1, rg, s, a.scale_log2);
@@ -1918,10 +1810,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   #pragma unroll
       for (int h = 0; h < HW; ++h) {
         const int hG = hg * HW + h;
-        if constexpr (KV4) {  // the weighted sum's pairs held level + 136
-  #pragma unroll
-          for (int e = 0; e < C::NACC; ++e) st.acc[h][e] = fmaf(-kInt4Bias, st.wsum[h], st.acc[h][e]);
-        }
   #pragma unroll
         for (int c2 = 0; c2 < C::CPL; ++c2) {
           const int off = ((((slot * 8 + rg) * G + hG) * D) + (c2 * 8 + s) * C::EPV) * 4;
