@@ -2,19 +2,20 @@
 // per-KV-head mixed KV cache (DuoAttention: retrieval heads hold every token,
 // streaming heads hold S sinks + a W-slot ring).
 //
-// Decode is bound by HBM bandwidth (g = n_q / n_kv flops per byte of K/V), so
-// it runs on the vector ALUs, not on MFMA.  The rows held by every (batch, KV
-// head) -- all T rows of a retrieval head, the min(T, S+W) sink and ring slots
-// of a streaming head -- form one flattened row space cut into equal work
-// items, one per compute unit, so long retrieval heads and short streaming
-// heads are balanced by bytes.  Within an item, K and V rows reach LDS by
-// direct buffer->LDS loads into a ring of four 32 KB units (three in flight);
-// the wavefronts score them with packed bf16 dot products against the GQA
-// query group held in registers, keep online softmax statistics per lane, and
-// accumulate P.V with bf16 dot products.  Partial (max, sum, acc) results of
-// items that share a head are merged by a second kernel (combine_kernel).
-// Retrieval rows may live in pages (a per-row page table); a paged head's
-// items then start at round boundaries so that every round lies in one page.
+// Decode is bound by HBM bandwidth (g = n_q / n_kv flops per byte of K/V).
+// The rows held by every (batch, KV head) -- all T rows of a retrieval head,
+// the min(T, S+W) sink and ring slots of a streaming head -- are cut into work
+// items of one common length, at most one per compute unit, so long retrieval
+// heads and short streaming heads are balanced by bytes; an item is a
+// contiguous row range of one head.  Within an item, K and V rows reach LDS by
+// direct buffer->LDS loads into a ring of four 32 KB units (two or three in
+// flight); at d = 128 the wavefronts score them and form P.V on the matrix
+// cores (the GQA query group as one operand), elsewhere with packed bf16 dot
+// products on the vector ALUs, keeping online softmax statistics.  Partial
+// (max, sum, acc) results of items that share a head are merged by a second
+// kernel (combine_kernel).  Retrieval rows may live in pages (a per-row page
+// table); a paged head's items then start at round boundaries so that every
+// round lies in one page.
 #include "duo_dma.h"
 #include "duo_internal.h"
 #include "duo_rope.h"
@@ -253,20 +254,19 @@ __global__ void rope_kernel(RopeArgs a) {
 
 // ------------------------------------------------------------------ decode
 //
-// One workgroup of 8 wavefronts per compute unit walks a contiguous range of
-// the flattened row space.  K and V rows reach LDS through direct buffer->LDS
-// loads into a ring of four 32 KB units (the K rows, then the V rows, of one
-// round of tiles); three units are in flight while one is consumed, so the
-// prefetch depth costs no registers.  A round is SLOTS tiles of TR rows; the
-// wavefronts of a slot split the g query heads (HW heads each) and read the
-// slot's tile from LDS, so no row is fetched twice.  Rounds never straddle two
-// heads: a range that covers parts of several heads is a sequence of
-// segments, and at the end of each segment the wavefronts' softmax states are
-// merged into one partial (max, sum, acc) per query head.  A segment that is a
-// whole head writes the output; otherwise its partial goes to the workspace
-// and the combine kernel merges the partials of the head.
+// One workgroup of 8 wavefronts per compute unit walks the contiguous rows of
+// one work item (part of one head).  K and V rows reach LDS through direct
+// buffer->LDS loads into a ring of four 32 KB units (the K rows, then the V
+// rows, of one round of tiles); DEPTH units are in flight while one is
+// consumed, so the prefetch depth costs no registers.  A round is SLOTS tiles
+// of TR rows; each wavefront reads its slot's tile from LDS, so no row is
+// fetched twice.  At the end the wavefronts' softmax states are merged into one
+// partial (max, sum, acc) per query head: an item that is a whole head writes
+// the output, otherwise its partial goes to the workspace and the combine
+// kernel merges the partials of the head.
 //
-// Lane layout within a tile: 8 lanes share a row.  Lane l has row group
+// Vector-ALU lane layout within a tile (d = 64 and fp32 rows; the matrix-core
+// layouts are described at mf_scores): 8 lanes share a row.  Lane l has row group
 // rg = l / 8 and slice s = l % 8; it holds the 16-byte chunks s, s+8, ... of
 // rows rg, rg+8, ...  Rows are XOR-swizzled in LDS (odd rows swap the two
 // halves of every 256 bytes) so the 8-row reads are free of bank conflicts.
@@ -316,6 +316,10 @@ struct DecodeCfg {
   static constexpr int ROUND_ROWS = SLOTS * TR;
   static constexpr int NACC = CPL * EPV;         // output elements per lane per head
   static constexpr int REC = (G * (D + 2) + 3) / 4 * 4;  // floats per partial record (16-byte multiple)
+  // Ring units in flight ahead of the one being consumed: FP8 and INT4 rows
+  // (256 and 512 rows a unit) measured faster with two, bf16 and fp32 rows
+  // with three.
+  static constexpr int DEPTH = LOWBIT ? 2 : 3;
   static_assert(KV4 ? (CPR == 4 && D == 128) : CPR % 8 == 0, "rows must span a multiple of 8 chunks");
   static_assert(RPL >= 2 && RPL % 2 == 0, "rows are paired for the weighted sum");
   static_assert(SLOT_BYTES % 1024 == 0, "a load piece stays within one tile");
@@ -1445,9 +1449,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   // the K scales, 4-7 the V scales); FP8 rounds hold 256 rows, INT4 rounds 512
   constexpr int SPW = LOWBIT ? C::ROUND_ROWS / 256 : 0;
   static_assert(!LOWBIT || C::ROUND_ROWS % 256 == 0, "a round's scales are whole wavefront loads");
-  // vector-memory loads per unit and wavefront: the ring pieces, plus SPW
-  // scale loads with each K unit of low-bit rows; units u+1 and u+2 hold WAITN
-  constexpr int WAITN = 2 * kPiecesPerWave + SPW;
+  // Vector-memory loads per unit and wavefront: the ring pieces, plus SPW
+  // scale loads with each K unit of low-bit rows.  When unit u has landed,
+  // the DEPTH - 1 units after it may be in flight: WAITN loads after a K
+  // unit, WAITV after a V unit.
+  constexpr int DEPTH = C::DEPTH;
+  static_assert(DEPTH == 2 || DEPTH == 3, "ring depth");
+  constexpr int WAITN = DEPTH == 3 ? 2 * kPiecesPerWave + SPW : kPiecesPerWave;
+  constexpr int WAITV = DEPTH == 3 ? 2 * kPiecesPerWave + SPW : kPiecesPerWave + SPW;
   char* const rings[kRingUnits] = {ring0, ring1, ring2, ring3};  // indexed by constants only
   auto ring_at = [&](int i) -> char* { return i == 0 ? ring0 : i == 1 ? ring1 : i == 2 ? ring2 : ring3; };
 
@@ -1528,8 +1537,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   };
   // The first unit, then the group's queries and the new token's K and V rows
   // into the staging area (one load piece per wavefront for the first
-  // wavefronts), then two more units.  Unit 0's wait below covers the staging
-  // loads, which were issued before units 1 and 2.
+  // wavefronts), then the next DEPTH - 1 units.  Unit 0's wait below covers
+  // the staging loads, which were issued before those units.
   issue(0, ring0);
   {
     constexpr int NQP = QSTAGE / 1024;  // query pieces
@@ -1542,7 +1551,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     }
   }
   issue(1, ring1);
-  issue(2, ring2);
+  if constexpr (DEPTH == 3) issue(2, ring2);
   // rotary positions: this lane's angle (pair lane % (D/2)) at the query's
   // position, computed while the loads are in flight
   double rcs = 1.0, rsn = 0.0;
@@ -1609,9 +1618,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   auto unit = [&](auto tag, int64_t u) {
     constexpr int X = decltype(tag)::value;
     constexpr bool V_PART = (X & 1) != 0;
-    wait_vmcnt<WAITN>();  // unit u has landed; u+1, u+2 may be in flight
-    lds_barrier();                     // ... for every wavefront; unit u-1 is consumed
-    issue(u + 3, rings[(X + 3) % kRingUnits]);
+    wait_vmcnt<V_PART ? WAITV : WAITN>();  // unit u has landed; the next DEPTH - 1 may be in flight
+    lds_barrier();                          // ... for every wavefront; unit u-1 is consumed
+    issue(u + DEPTH, rings[(X + DEPTH) % kRingUnits]);
     const int64_t row0 = w.r0 + ((u >> 1) * SLOTS + slot) * (int64_t)TR;
     const int64_t left = w.r1 - row0;
     const int nv = active ? (int)(left < 0 ? 0 : (left > TR ? TR : left)) : 0;
