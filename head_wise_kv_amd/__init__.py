@@ -30,7 +30,7 @@ EXPORTS = ("duo_cache_bytes", "duo_cache_payload_bytes", "duo_cache_init", "duo_
            "duo_last_error", "duo_gated_attention", "duo_cache_head_scales", "duo_append_row", "duo_prefill_chunk_row",
            "duo_cache_row_len", "duo_cache_reset_row", "duo_cache_fork_row", "duo_cache_free_pages",
            "duo_cache_row_pages", "duo_prefill_workspace_bytes", "duo_decode_append_noalloc",
-           "duo_cache_sync", "duo_cache_reserve")
+           "duo_cache_sync", "duo_cache_reserve", "duo_rope_apply")
 
 
 class DuoError(RuntimeError):
@@ -82,6 +82,7 @@ def _load():
     lib.duo_prefill_workspace_bytes.argtypes = [vp, i32, i64, ctypes.POINTER(sz)]
     lib.duo_cache_sync.argtypes = [vp, vp]
     lib.duo_cache_reserve.argtypes = [vp, i32, i64, vp]
+    lib.duo_rope_apply.argtypes = [ctypes.c_float, i32, i32, i32, i64, i32, ctypes.POINTER(i64), vp, vp, vp]
     lib.duo_cache_free.argtypes = [vp]
     lib.duo_cache_free.restype = None
     lib.duo_last_error.argtypes = []
@@ -462,4 +463,24 @@ def gated_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: to
     _check(lib.duo_gated_attention(ctypes.byref(shape), ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
                                    ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(alpha.data_ptr()),
                                    ctypes.c_void_p(out.data_ptr()), sc, _stream_handle(stream)))
+    return out
+
+
+def rope_apply(x: torch.Tensor, p0, theta: float, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Rotary position embedding as the cache applies it (duo_rope_apply):
+    row c of x[b][h] rotated at position p0[b] + c with base theta.
+    x: contiguous device [B][H][C][d], bf16 or float32; p0: B ints."""
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or not x.is_contiguous() or x.dim() != 4:
+        raise ValueError("x must be a contiguous device tensor [B][H][C][d]")
+    B, Hh, C, d = x.shape
+    p = [int(v) for v in p0]
+    if len(p) != B:
+        raise ValueError(f"p0 must hold {B} positions")
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype or out.device != x.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like x")
+    arr = (ctypes.c_int64 * B)(*p)
+    _check(lib.duo_rope_apply(float(theta), _dtype_code(x.dtype), B, Hh, C, d, arr, ctypes.c_void_p(x.data_ptr()),
+                              ctypes.c_void_p(out.data_ptr()), _stream_handle(stream)))
     return out

@@ -102,6 +102,48 @@ int validate(const duo_config* c) {
 }
 
 int elem_bytes(const duo_config* c) { return c->dtype == DUO_BF16 ? 2 : 4; }
+
+// (h, l) * (bh, bl) in double-double arithmetic (contraction off: a fused
+// h = p + e would count the product's rounding error twice)
+void dd_mul_host(double& h, double& l, double bh, double bl) {
+#pragma clang fp contract(off)
+  const double p = h * bh;
+  double e = std::fma(h, bh, -p);
+  e = std::fma(h, bl, std::fma(l, bh, e));
+  h = p + e;
+  l = e - (h - p);
+}
+
+// Rotary positions of base theta for heads of d dimensions: b = theta^(-2/d)
+// as a double-double, to about 104 bits, and its squares b^(2^k).  A
+// long-double estimate of b is refined by one Newton step on b^m theta = 1
+// (m = d / 2) taken in double-double arithmetic: b <- b - b (b^m theta - 1) / m.
+duo::Rope make_rope(float theta, int d) {
+#pragma clang fp contract(off)
+  duo::Rope r{};
+  if (!(theta > 0.f)) return r;
+  r.on = 1;
+  const long double x = powl((long double)theta, -2.0L / (long double)d);
+  double bh = (double)x, bl = (double)(x - (long double)bh);
+  const int m = d / 2;
+  double th = 1.0, tl = 0.0, ph = bh, pl = bl;  // b^m by binary powers
+  for (int e = m; e != 0; e >>= 1) {
+    if (e & 1) dd_mul_host(th, tl, ph, pl);
+    if (e > 1) dd_mul_host(ph, pl, ph, pl);
+  }
+  const double tt = (double)theta;  // exact
+  const double p = th * tt;
+  const double pe = std::fma(th, tt, -p) + tl * tt;  // b^m theta = p + pe, p within an ulp of 1
+  const double g = (p - 1.0) + pe;                  // p - 1 is exact
+  const double lo = bl - bh * g / m;
+  double h = bh + lo, l = lo - ((bh + lo) - bh);
+  for (int k = 0; k < duo::kRopeBits; ++k) {
+    r.hi[k] = h;
+    r.lo[k] = l;
+    dd_mul_host(h, l, h, l);
+  }
+  return r;
+}
 // bytes per stored K/V row: d elements in the cache dtype, d FP8 codes, or d
 // INT4 codes two to a byte
 int kv_row_bytes(const duo_config* c) {
@@ -272,12 +314,7 @@ struct duo_cache {
     p.len += b;
     return p;
   }
-  duo::Rope rope() const {
-    duo::Rope r{};
-    r.on = cfg.rope_theta > 0.f ? 1 : 0;
-    r.log2_theta = r.on ? std::log2((double)cfg.rope_theta) : 0.0;
-    return r;
-  }
+  duo::Rope rope() const { return make_rope(cfg.rope_theta, cfg.d_head); }
   // prefill with rotary positions: the chunk's rotated queries and keys in the
   // workspace, after the decode records and the FP8 prefill copies
   size_t rope_ws_bytes(int64_t B, int64_t C) const {
@@ -1165,6 +1202,37 @@ int duo_cache_head_scales(const duo_cache* c, int layer, int kv_head, float** k_
   if (k_scale) *k_scale = f8 ? (ret ? p.ksc_ret : p.ksc_str) + (size_t)ci * slots : nullptr;
   if (v_scale) *v_scale = f8 ? (ret ? p.vsc_ret : p.vsc_str) + (size_t)ci * slots : nullptr;
   if (scale_stride) *scale_stride = f8 ? (int64_t)n_kind * slots : 0;
+  return ok();
+}
+
+int duo_rope_apply(float theta, int dtype, int B, int H, int64_t C, int d, const int64_t* p0, const void* x,
+                   void* out, void* stream) {
+  if (!std::isfinite(theta) || !(theta > 0.f)) return fail(DUO_EINVAL, "theta must be finite and > 0");
+  if (dtype != DUO_F32 && dtype != DUO_BF16) return fail(DUO_EINVAL, "dtype %d is not a duo_dtype", dtype);
+  if (B < 1 || B > duo::kMaxRows) return fail(DUO_EINVAL, "B = %d outside 1 .. %d", B, duo::kMaxRows);
+  if (H < 1) return fail(DUO_EINVAL, "H = %d must be >= 1", H);
+  if (C < 0) return fail(DUO_EINVAL, "C = %lld must be >= 0", (long long)C);
+  if (d < 2 || d > 256 || d % 2 != 0) return fail(DUO_EINVAL, "d = %d must be even, 2 .. 256", d);
+  if (!p0) return fail(DUO_EINVAL, "p0 is NULL");
+  for (int b = 0; b < B; ++b)
+    if (p0[b] < 0 || p0[b] + C > (int64_t{1} << 31))
+      return fail(DUO_EINVAL, "p0[%d] = %lld: positions must lie in 0 .. 2^31 - 1", b, (long long)p0[b]);
+  if (C == 0) return ok();
+  if (!x || !out) return fail(DUO_EINVAL, "x or out is NULL");
+  if ((double)B * H * C * d > 9.0e18) return fail(DUO_EINVAL, "tensor too large");
+  duo::RopeArgs r{};
+  r.q = x;
+  r.q_out = out;
+  r.B = B;
+  r.n_q = H;
+  r.n_kv = 0;  // no second tensor
+  r.d = d;
+  r.dtype = dtype;
+  r.C = C;
+  for (int b = 0; b < B; ++b) r.p0[b] = (int32_t)p0[b];
+  r.rope = make_rope(theta, d);
+  const hipError_t e = duo::launch_rope(r, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rotary launch");
   return ok();
 }
 

@@ -55,9 +55,12 @@ struct LayerPtrs {
 
 // Rotary position embedding (on = 0: keys and queries are used as given).
 // Pair i of a head's dimensions, (i, i + d/2), turns by p * theta^(-2i/d) at
-// position p.
+// position p.  b_k = theta^(-2 * 2^k / d) as double-doubles
+// (hi[k] + lo[k]) for k < kRopeBits, from make_rope, so that the frequency
+// of pair i is the product of the b_k of i's set bits; on = 0 for none.
+constexpr int kRopeBits = 7;  // pairs i < 128 (d <= 256)
 struct Rope {
-  double log2_theta;
+  double hi[kRopeBits], lo[kRopeBits];
   int on;
 };
 
@@ -142,10 +145,13 @@ struct DecodeArgs {
   // it to the cache.
   const char* new_k;            // [B][n_kv][d]
   const char* new_v;
+  DecodeRow rows[kMaxRows];     // items ordered: row 0's retrieval heads, row 1's, ..., then streaming likewise
   // Queries (and a fused append's new K row) are rotated at the query's
   // position: the row's count for a fused append, the count - 1 otherwise.
+  // Last: it is read after the first loads are issued, and the fields before
+  // it keep the argument lines the item lookup reads (moving them measured
+  // up to 1% slower decode steps).
   Rope rope;
-  DecodeRow rows[kMaxRows];     // items ordered: row 0's retrieval heads, row 1's, ..., then streaming likewise
 };
 
 struct PrefillArgs {

@@ -136,8 +136,8 @@ __device__ __forceinline__ void rope_chunks(uint4& x, uint4& y, const Rope& r, i
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       double c0, s0, c1, s1;
-      rope_cs(r, d, p, c * 8 + 2 * w, c0, s0);
-      rope_cs(r, d, p, c * 8 + 2 * w + 1, c1, s1);
+      rope_cs(r, p, c * 8 + 2 * w, c0, s0);
+      rope_cs(r, p, c * 8 + 2 * w + 1, c1, s1);
       const double x0 = bf_lo(xw[w]), x1 = bf_hi(xw[w]), y0 = bf_lo(yw[w]), y1 = bf_hi(yw[w]);
       xw[w] = bf16_bits_from_double(x0 * c0 - y0 * s0) | (bf16_bits_from_double(x1 * c1 - y1 * s1) << 16);
       yw[w] = bf16_bits_from_double(y0 * c0 + x0 * s0) | (bf16_bits_from_double(y1 * c1 + x1 * s1) << 16);
@@ -146,7 +146,7 @@ __device__ __forceinline__ void rope_chunks(uint4& x, uint4& y, const Rope& r, i
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       double cs, sn;
-      rope_cs(r, d, p, c * 4 + w, cs, sn);
+      rope_cs(r, p, c * 4 + w, cs, sn);
       const double xv = __uint_as_float(xw[w]), yv = __uint_as_float(yw[w]);
       xw[w] = __float_as_uint((float)(xv * cs - yv * sn));
       yw[w] = __float_as_uint((float)(yv * cs + xv * sn));
@@ -234,7 +234,7 @@ __global__ void rope_kernel(RopeArgs a) {
     const int64_t ci = row % a.C;
     const int b = (int)(row / a.C / (isq ? a.n_q : a.n_kv));
     double cs, sn;  // keys are stored from these copies: rotated in double, rounded once
-    rope_cs(a.rope, a.d, a.p0[b] + ci, i, cs, sn);
+    rope_cs(a.rope, a.p0[b] + ci, i, cs, sn);
     const size_t e0 = (size_t)row * a.d + i, e1 = e0 + half;
     if (a.dtype == 1) {
       const uint16_t* in = static_cast<const uint16_t*>(isq ? a.q : a.k);
@@ -509,8 +509,8 @@ __device__ __forceinline__ uint4 rope_row16(uint4 x, const Rope& r, int64_t p, i
   for (int k = 0; k < 4; ++k) {
     const uint32_t q = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w[k], 0x128, 0xF, 0xF, false);  // row_ror:8
     double cs0, sn0, cs1, sn1;
-    rope_cs(r, 128, p, 8 * (j & 7) + 2 * k, cs0, sn0);
-    rope_cs(r, 128, p, 8 * (j & 7) + 2 * k + 1, cs1, sn1);
+    rope_cs(r, p, 8 * (j & 7) + 2 * k, cs0, sn0);
+    rope_cs(r, p, 8 * (j & 7) + 2 * k + 1, cs1, sn1);
     const double a0 = bf_lo(w[k]), a1 = bf_hi(w[k]), b0 = bf_lo(q), b1 = bf_hi(q);
     const double v0 = first ? a0 * cs0 - b0 * sn0 : a0 * cs0 + b0 * sn0;
     const double v1 = first ? a1 * cs1 - b1 * sn1 : a1 * cs1 + b1 * sn1;
@@ -1557,7 +1557,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   double rcs = 1.0, rsn = 0.0;
   if (a.rope.on) {
     const int64_t cnt = w.cnt >= 0 ? w.cnt : row_count(a, w.b);
-    rope_cs(a.rope, D, cnt - (a.new_k ? 0 : 1), lane % (D / 2), rcs, rsn);
+    rope_cs(a.rope, cnt - (a.new_k ? 0 : 1), lane % (D / 2), rcs, rsn);
   }
   wait_vmcnt<WAITN>();  // unit 0 and the staging loads have landed
   lds_barrier();

@@ -114,8 +114,11 @@ typedef enum { DUO_KV_NATIVE = 0, DUO_KV_FP8 = 1, DUO_KV_INT4 = 2 } duo_kv_forma
  * i + d/2 (i < d/2) turn by the angle p * rope_theta^(-2i/d) at position p.
  * Keys are stored rotated (appends, prefill commits, fused appends); queries
  * are rotated at their own position by decode and prefill.  Values are never
- * rotated.  The angle is formed and reduced modulo 2 pi in double precision;
- * the rotation runs in fp32 and the result is rounded to the cache dtype.
+ * rotated.  The angle is formed from rope_theta^(-2/d) held to about 104
+ * bits and reduced modulo 2 pi in three parts, so that its cosine and sine
+ * are within a few double roundings of the exact ones at every position up
+ * to 2^31 (see duo_rope_apply); keys are rotated in double and rounded once
+ * to the cache dtype, queries are rotated in fp32.
  * rope_theta = 0: queries and keys are used as given. */
 typedef struct {
   int32_t L, B, n_q, n_kv, d_head;
@@ -304,6 +307,20 @@ typedef struct {
  * workspace; enqueued on `stream`. */
 int duo_gated_attention(const duo_gated_shape* shape, const void* q, const void* k, const void* v,
                         const float* alpha, void* out, float scale, void* stream);
+
+/* The rotary position embedding the cache applies (rope_theta in
+ * duo_config), on its own: row c of x[b][h] is rotated at position
+ * p0[b] + c, dimensions i and i + d/2 turning by the angle
+ * (p0[b] + c) * theta^(-2i/d), in double, and rounded once to the dtype.
+ * For callers that rotate queries or keys outside the cache so that they
+ * agree with the keys it stores, and for checking the angle arithmetic at
+ * positions up to the largest a cache row can reach.  x, out: device
+ * [B][H][C][d] of `dtype` (duo_dtype); out may be x.  p0: host array of B
+ * starting positions, 0 <= p0[b] and p0[b] + C <= 2^31.  1 <= B <= 64,
+ * H >= 1, C >= 0, d even with 2 <= d <= 256, theta finite and > 0
+ * (DUO_EINVAL otherwise).  Enqueued on `stream`. */
+int duo_rope_apply(float theta, int dtype, int B, int H, int64_t C, int d, const int64_t* p0, const void* x,
+                   void* out, void* stream);
 
 /* Row scales of one KV head of a DUO_KV_FP8 cache: *k_scale / *v_scale
  * receive the device float [n_slots] scales of batch row 0 (batch row b at

@@ -28,6 +28,11 @@ Readings taken where the pages leave a step open:
     rotated; in prefill the chunk's own keys are attended as rotated (before
     they are stored) and the held keys as stored.  Values are not rotated.
 
+cos_sin_exact / rotate_exact (positions up to 2^31) are pinned by integer
+angles (pair 0 at any base, and base 10^4 with d = 8 at positions that are
+multiples of 1000) against the C library's cosine and sine, and by agreement
+with rotate() at positions where float64 angles are exact to 1e-10.
+
 Pinned by tests/oracle_checks.py: unit vectors at position 1 for d = 8,
 theta = 10^4 (frequencies 1, 0.1, 0.01, 0.001 exactly), the complex-number
 form of the rotation, the relative-position property of scores, the bf16
@@ -38,6 +43,7 @@ rotation, torch's bf16 rounding and torch's E4M3 conversion or rounding.
 """
 from __future__ import annotations
 
+from decimal import Context, Decimal, localcontext
 from typing import Sequence
 
 import numpy as np
@@ -60,6 +66,68 @@ def rotate(X, positions, theta: float) -> np.ndarray:
     c, s = np.cos(a), np.sin(a)
     lo, hi = X[..., :h], X[..., h:]
     return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+
+
+def _dec_pi(ctx):
+    """pi in the context's precision from Machin's formula
+    pi = 16 arctan(1/5) - 4 arctan(1/239), arctan(1/n) by its series."""
+    def arctan_inv(n):
+        x = ctx.divide(1, n)
+        x2 = x * x
+        term, total, k = x, x, 1
+        eps = Decimal(10) ** (-(ctx.prec + 2))
+        while True:
+            term = -term * x2
+            k += 2
+            t = term / k
+            if abs(t) < eps:
+                return total
+            total += t
+    return 16 * arctan_inv(5) - 4 * arctan_inv(239)
+
+
+def cos_sin_exact(p: int, i: int, d: int, theta: float, digits: int = 40):
+    """(cos a, sin a) of the angle a = p * theta^(-2i/d) of pair i at position
+    p, to about `digits` decimal digits, as Decimals: theta^(-2i/d) by
+    Python's decimal power (correctly rounded in its context), a reduced
+    modulo 2 pi with pi from Machin's formula, then the Taylor series of cosine
+    and sine.  For positions where a float64 angle p * f is off by up to
+    p * f * 2^-53 (about 2.4e-7 rad at p = 2^31)."""
+    ctx = Context(prec=digits + 25)
+    with localcontext(ctx) as c:
+        f = Decimal(float(theta)) ** (Decimal(-2 * i) / Decimal(d))
+        a = Decimal(int(p)) * f
+        two_pi = 2 * _dec_pi(c)
+        r = a - (a / two_pi).to_integral_value() * two_pi  # |r| <= pi
+        r2 = r * r
+        cos_t, sin_t = Decimal(1), r
+        cs, sn, k = cos_t, sin_t, 0
+        eps = Decimal(10) ** (-(digits + 20))
+        while True:
+            k += 2
+            cos_t = -cos_t * r2 / ((k - 1) * k)
+            sin_t = -sin_t * r2 / (k * (k + 1))
+            cs += cos_t
+            sn += sin_t
+            if abs(cos_t) < eps and abs(sin_t) < eps:
+                return +cs, +sn
+
+
+def rotate_exact(X, positions, theta: float) -> np.ndarray:
+    """rotate() with every angle from cos_sin_exact and every rotated value
+    computed in decimal and rounded once to float64: X [n][d] (few rows)."""
+    X = np.asarray(X, dtype=np.float64)
+    n, d = X.shape
+    h = d // 2
+    out = np.empty_like(X)
+    for r in range(n):
+        for i in range(h):
+            cs, sn = cos_sin_exact(int(positions[r]), i, d, theta)
+            x, y = Decimal(float(X[r, i])), Decimal(float(X[r, i + h]))
+            with localcontext(Context(prec=60)):
+                out[r, i] = float(x * cs - y * sn)
+                out[r, i + h] = float(y * cs + x * sn)
+    return out
 
 
 def round_bf16(x) -> np.ndarray:

@@ -683,6 +683,29 @@ def check_rope_relative_positions():
         assert abs(score(pq, pk) - float(q @ RP.rotate(k[None], [pk - pq], 1e4)[0])) < 1e-9
 
 
+def check_rope_exact_integer_angles():
+    # Integer angles, whose cosine and sine the C library gives after an exact
+    # reduction: pair 0 turns by p (frequency 1 at any base); with base 10^4
+    # and d = 8 the frequencies are 10^(-i), so at a multiple of 1000 every
+    # pair's angle p / 10^i is an integer.
+    p_big = (2 ** 31 - 1) // 1000 * 1000
+    for p in (1, 7, 123456789, 2 ** 31 - 1):
+        cs, sn = RP.cos_sin_exact(p, 0, 128, 5e5)
+        assert abs(float(cs) - math.cos(p)) < 2e-16 and abs(float(sn) - math.sin(p)) < 2e-16, p
+    for p in (1000, 5_000_000, p_big):
+        for i in range(4):
+            n = p // 10 ** i
+            cs, sn = RP.cos_sin_exact(p, i, 8, 1e4)
+            assert abs(float(cs) - math.cos(n)) < 2e-16 and abs(float(sn) - math.sin(n)) < 2e-16, (p, i)
+
+
+def check_rope_exact_matches_float64_at_small_positions():
+    # below 2^17 a float64 angle p * f is off by at most p * 2^-53 < 2e-11
+    X = np.random.default_rng(9).standard_normal((3, 16))
+    pos = [0, 4095, 131071]
+    assert np.allclose(RP.rotate_exact(X, pos, 5e5), RP.rotate(X, pos, 5e5), atol=1e-10, rtol=0)
+
+
 def check_bf16_rounding_against_library():
     mags = 10.0 ** np.random.default_rng(8).uniform(-3, 3, 20000)
     ties = [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 1.0 + 2 ** -9, 255.5, 0.0]  # halfway cases
@@ -736,6 +759,7 @@ ALL_CHECKS = [
     check_paging_closed_forms, check_paging_capacity,
     check_rope_unit_vectors, check_rope_complex_form, check_rope_relative_positions,
     check_bf16_rounding_against_library, check_rope_cache_route_uses_logical_positions,
+    check_rope_exact_integer_angles, check_rope_exact_matches_float64_at_small_positions,
 ]
 
 

@@ -225,6 +225,52 @@ def test_rope_large_positions():
     assert c.row_pages(0, 1)[:511] == c.row_pages(0, 0)[:511]
 
 
+def _ulp32(x):
+    x = np.abs(np.asarray(x, dtype=np.float64)).astype(np.float32)
+    return np.spacing(x).astype(np.float64)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("d,theta", [(128, 500000.0), (64, 10000.0)])
+def test_rope_apply_up_to_largest_position(d, theta):
+    """duo_rope_apply at positions up to 2^31 - 1, the largest a cache row can
+    reach, against the exact rotation (oracle.rope.rotate_exact: decimal
+    angles, reduced with a 40-digit pi).  float32 rows: every value within
+    half a float32 step of the exact rotation (plus 1e-15 of the pair's size
+    for the double arithmetic before the rounding); a float64 angle p * f
+    would be off by up to ~2.4e-7 rad there, which shows as several float32
+    steps.  bf16 rows: the exact rotation rounded once, bit for bit."""
+    need_gpu()
+    import head_wise_kv_amd as H
+    C = 3
+    p0 = [2 ** 31 - C, 2 ** 30 + 12345, 1_000_000_007, 0]
+    B = len(p0)
+    say("rope_apply", d, theta)
+    X = WL.normal_f32((B, 1, C, d), 1950 + d)
+    want = np.stack([RP.rotate_exact(X[b, 0], [p0[b] + c for c in range(C)], theta) for b in range(B)])[:, None]
+    got = H.rope_apply(torch.from_numpy(X).cuda(), p0, theta).cpu().double().numpy()
+    h = d // 2
+    pair = np.sqrt(X[..., :h] ** 2 + X[..., h:] ** 2).astype(np.float64)
+    pair = np.concatenate([pair, pair], axis=-1)
+    err = np.abs(got - want)
+    bound = 0.5 * _ulp32(want) + 1e-15 * pair
+    say("rope_apply f32 max err", float(err.max()), "max err / bound", float((err / bound).max()))
+    assert (err <= bound).all(), np.argwhere(err > bound)[:5]
+    # bf16: the exact rotation of the bf16 inputs, rounded once to bf16
+    Xb = stored(X, "bf16")
+    want_b = np.stack([RP.rotate_exact(Xb[b, 0], [p0[b] + c for c in range(C)], theta) for b in range(B)])[:, None]
+    got_b = H.rope_apply(WL.to_torch(X, "bf16").cuda(), p0, theta).cpu().double().numpy()
+    assert np.array_equal(got_b, RP.round_bf16(want_b)), np.argwhere(got_b != RP.round_bf16(want_b))[:5]
+    # in place, and the argument checks
+    xt = torch.from_numpy(X).cuda()
+    H.rope_apply(xt, p0, theta, out=xt)
+    assert np.array_equal(xt.cpu().double().numpy(), got)
+    for bad_p0 in ([2 ** 31 - C + 1, 0, 0, 0], [-1, 0, 0, 0]):
+        with pytest.raises(H.DuoError) as e:
+            H.rope_apply(torch.from_numpy(X).cuda(), bad_p0, theta)
+        assert e.value.code == H.DUO_EINVAL
+
+
 @pytest.mark.gpu
 def test_rope_errors_and_workspace():
     """Bad bases are rejected; a prefill workspace too small for the rotated

@@ -213,6 +213,15 @@ def _int4_prefill_held_as_given(Q, K, V, mask, S, W, scale, chunk):
     return out
 
 
+def _cos_sin_double_reduction(p, i, d, theta, digits=40):
+    # the angle reduced with a float64 2 pi, as a kernel might: off by ~1e-7 rad at 2^31
+    from decimal import Decimal
+    f = float(theta) ** (-2.0 * i / d)
+    a = float(p) * f
+    r = a - round(a / (2 * np.pi)) * (2 * np.pi)
+    return Decimal(np.cos(r)), Decimal(np.sin(r))
+
+
 MUTATIONS = {
     "window_too_wide": (A, "visible_matrix", _window_too_wide),
     "sinks_off_by_one": (A, "visible_matrix", _sinks_off_by_one),
@@ -242,6 +251,7 @@ MUTATIONS = {
     "int4_nibbles_swapped": (Q4, "pack_nibbles", _int4_nibbles_swapped),
     "int4_levels_offset": (Q4, "int4_levels", _int4_levels_offset7),
     "int4_held_as_given": (Q4, "prefill_chunked_int4", _int4_prefill_held_as_given),
+    "rope_exact_double_reduction": (RP, "cos_sin_exact", _cos_sin_double_reduction),
 }
 
 
