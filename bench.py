@@ -89,6 +89,9 @@ def decode_layer_bytes(w: WL.Workload, mask_row, T: int, append: bool) -> int:
     n_ret = int(np.sum(mask_row))
     n_str = w.n_kv - n_ret
     rows = w.B * (n_ret * T + n_str * min(T, w.S + w.W))
+    if w.forked:  # the prefix's full pages, shared by the B rows, are read once
+        shared = (w.T - 1) // w.page_rows * w.page_rows
+        rows -= (w.B - 1) * n_ret * shared
     kv = rows * w.kv_row_bytes * 2  # FP8 rows: codes plus the row scale
     qo = 2 * w.B * w.n_q * w.d * w.elem_bytes
     app = 2 * w.B * w.n_kv * (w.d * w.elem_bytes + w.kv_row_bytes) if append else 0
@@ -141,13 +144,18 @@ def bench_decode(w: WL.Workload, steps: int, warmup: int, layers: int, copies: i
                          kv_format=w.kv_format, rope_theta=w.rope_theta, **pages) for _ in range(copies)]
     log(f"{w.name}: {copies} x arena {caches[0].arena_bytes / 1e9:.2f} GB, filling {L} layers x {fill} tokens")
     t0 = time.time()
-    buf_k = torch.empty(w.B, w.n_kv, fill, w.d, dtype=dt, device=dev)
+    buf_k = torch.empty(1 if w.forked else w.B, w.n_kv, fill, w.d, dtype=dt, device=dev)
     buf_v = torch.empty_like(buf_k)
     for l in range(L):
         WL.device_fill_normal(buf_k, WL.device_seed(w, l, WL.TENSOR_K), w.S, w.sink_scale)
         WL.device_fill_normal(buf_v, WL.device_seed(w, l, WL.TENSOR_V))
         for cache in caches:
-            cache.append(l, buf_k, buf_v)
+            if w.forked:  # row 0 holds the prefix; the other rows are forks of it
+                cache.append_row(l, 0, buf_k, buf_v)
+                for b in range(1, w.B):
+                    cache.fork_row(l, 0, b)
+            else:
+                cache.append(l, buf_k, buf_v)
     del buf_k, buf_v
     q = torch.empty(L, w.B, w.n_q, w.d, dtype=dt, device=dev)
     WL.device_fill_normal(q, WL.device_seed(w, 0, WL.TENSOR_Q))

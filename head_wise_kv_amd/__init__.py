@@ -30,7 +30,7 @@ EXPORTS = ("duo_cache_bytes", "duo_cache_payload_bytes", "duo_cache_init", "duo_
            "duo_last_error", "duo_gated_attention", "duo_cache_head_scales", "duo_append_row", "duo_prefill_chunk_row",
            "duo_cache_row_len", "duo_cache_reset_row", "duo_cache_fork_row", "duo_cache_free_pages",
            "duo_cache_row_pages", "duo_prefill_workspace_bytes", "duo_decode_append_noalloc",
-           "duo_cache_sync", "duo_cache_reserve", "duo_rope_apply")
+           "duo_cache_sync", "duo_cache_reserve", "duo_rope_apply", "duo_decode_plan")
 
 
 class DuoError(RuntimeError):
@@ -82,6 +82,7 @@ def _load():
     lib.duo_prefill_workspace_bytes.argtypes = [vp, i32, i64, ctypes.POINTER(sz)]
     lib.duo_cache_sync.argtypes = [vp, vp]
     lib.duo_cache_reserve.argtypes = [vp, i32, i64, vp]
+    lib.duo_decode_plan.argtypes = [vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.duo_rope_apply.argtypes = [ctypes.c_float, i32, i32, i32, i64, i32, ctypes.POINTER(i64), vp, vp, vp]
     lib.duo_cache_free.argtypes = [vp]
     lib.duo_cache_free.restype = None
@@ -309,6 +310,12 @@ class DuoCache:
     def fork_row(self, layer: int, src_row: int, dst_row: int, stream=None) -> None:
         """Make empty row dst_row a copy of row src_row (paged: sharing its full pages)."""
         _check(lib.duo_cache_fork_row(self._h, layer, src_row, dst_row, _stream_handle(stream)))
+
+    def decode_plan(self, layer: int) -> tuple:
+        """(work items, shared items) a decode of `layer` would launch now."""
+        n, sh = ctypes.c_int32(), ctypes.c_int32()
+        _check(lib.duo_decode_plan(self._h, layer, ctypes.byref(n), ctypes.byref(sh)))
+        return n.value, sh.value
 
     def free_pages(self, layer: int) -> int:
         x = ctypes.c_int64()

@@ -215,7 +215,7 @@ void make_plan(const duo_config* c, Plan* p) {
   // decode partial records: one per (work item, head) overlap, indexed by
   // first work item of the head + flat head index + segment
   const size_t rec = decode_rec_floats(c) * sizeof(float);
-  p->ws_records = align_up(((size_t)duo::kMaxDecodeBlocks + (size_t)c->B * c->n_kv) * rec);
+  p->ws_records = align_up(((size_t)duo::kMaxDecodeRecords + (size_t)c->B * c->n_kv) * rec);
   p->ws_dequant = dequant;
   p->workspace = p->ws_records + p->ws_dequant;
 }
@@ -630,6 +630,53 @@ int plan_decode(const duo_cache* c, int layer, const void* q, void* out, float s
     a.new_v = static_cast<const char*>(new_v);
   }
   a.rope = c->rope();
+  const int g = cf.n_q / cf.n_kv;
+  const int64_t heads = (int64_t)cf.B * (lp.n_ret + lp.n_str);
+  const int64_t slots = std::max<int64_t>(std::min(c->num_cu, duo::kMaxDecodeBlocks), heads);
+  const int64_t R0 = duo::decode_round_rows(cf.dtype, cf.d_head, g, c->kvfmt());
+  const bool paged = a.lp.table != nullptr;
+  // Share groups ("Attention Variants and Memory Efficiency", "What the
+  // Inference Runtime Can Change": a matching prefix is stored once; here it
+  // is also read once).  Consecutive batch rows whose first pages are the
+  // same physical pages -- rows forked from one prefix -- form a group of up
+  // to 16 / g rows (their g queries each fill the 16 columns of one
+  // matrix-core tile; bf16 queries of d = 128 and g >= 4, so that a row's
+  // queries are whole 1 KB staging pieces).  The group's shared items attend
+  // all its rows' queries to the shared rows; each row's own items cover the
+  // rest of its rows.
+  a.n_share = 0;
+  if (paged && lp.n_ret > 0 && cf.dtype == DUO_BF16 && cf.d_head == 128 && (g == 4 || g == 8)) {
+    const std::vector<std::vector<int32_t>>& pr = c->pages[layer].rows;
+    // full pages that rows b0 and b hold at the same positions
+    auto common = [&](int b0, int b) {
+      const int64_t held = std::min(c->len(layer, b0), c->len(layer, b));
+      const int64_t full = std::min<int64_t>(held / cf.page_rows, (int64_t)std::min(pr[b0].size(), pr[b].size()));
+      int64_t k = 0;
+      while (k < full && pr[b0][k] == pr[b][k]) ++k;
+      return k;
+    };
+    const int rmax = 16 / g;
+    for (int b0 = 0; b0 < cf.B && a.n_share < duo::kMaxShares;) {
+      int n = 1;
+      int64_t k = INT64_MAX;
+      while (b0 + n < cf.B && n < rmax) {
+        const int64_t kk = common(b0, b0 + n);
+        if (kk < 1) break;
+        k = std::min(k, kk);
+        ++n;
+      }
+      if (n >= 2) {
+        duo::DecodeShare& S = a.share[a.n_share++];
+        S.b0 = b0;
+        S.R = n;
+        S.rows = (int32_t)(k * cf.page_rows);
+        for (int b = b0; b < b0 + n; ++b) a.rsh[b].sh_rows = S.rows;
+        b0 += n;
+      } else {
+        ++b0;
+      }
+    }
+  }
   // Work items: contiguous row ranges of one head, at most one workgroup per
   // compute unit (or one per head if there are more heads), none shorter
   // than one round of the kernel where the head allows.  All heads are cut to
@@ -638,11 +685,6 @@ int plan_decode(const duo_cache* c, int layer, const void* q, void* out, float s
   // across retrieval and streaming heads and across batch rows of different
   // lengths (e.g. a 1,088-row streaming head is cut in two when a 128k
   // retrieval head's items hold about 1,050 rows).
-  const int g = cf.n_q / cf.n_kv;
-  const int64_t heads = (int64_t)cf.B * (lp.n_ret + lp.n_str);
-  const int64_t slots = std::max<int64_t>(std::min(c->num_cu, duo::kMaxDecodeBlocks), heads);
-  const int64_t R0 = duo::decode_round_rows(cf.dtype, cf.d_head, g, c->kvfmt());
-  const bool paged = a.lp.table != nullptr;
   auto items = [&](int64_t rows, int64_t t) { return std::max<int64_t>(1, ceil_div(rows, t)); };
   // A paged head's items start at multiples of R0 rows (the kernel rounds
   // its item length up to R0), so that each round of rows lies in one page.
@@ -650,11 +692,16 @@ int plan_decode(const duo_cache* c, int layer, const void* q, void* out, float s
   auto count = [&](int64_t t) {
     int64_t n = 0;
     for (int b = 0; b < cf.B; ++b)
-      n += lp.n_ret * items_ret(a.rows[b].rows_ret, t) + lp.n_str * items(a.rows[b].rows_str, t);
+      n += lp.n_ret * items_ret(a.rows[b].rows_ret - a.rsh[b].sh_rows, t) + lp.n_str * items(a.rows[b].rows_str, t);
+    for (int k = 0; k < a.n_share; ++k) n += lp.n_ret * items_ret(a.share[k].rows, t);
     return n;
   };
   int64_t longest = 1;
   for (int b = 0; b < cf.B; ++b) longest = std::max<int64_t>(longest, std::max(a.rows[b].rows_ret, a.rows[b].rows_str));
+  if (a.n_share > 0 && count(longest) > slots) {  // one item per head already fills the launch
+    a.n_share = 0;
+    for (int b = 0; b < cf.B; ++b) a.rsh[b].sh_rows = 0;
+  }
   int64_t lo = std::min(R0, longest), hi = longest;  // count(hi) <= heads <= slots
   while (lo < hi) {
     const int64_t mid = lo + (hi - lo) / 2;
@@ -666,10 +713,12 @@ int plan_decode(const duo_cache* c, int layer, const void* q, void* out, float s
   a.multi = 0;
   for (int b = 0; b < cf.B; ++b) {  // retrieval items of every row, then streaming
     duo::DecodeRow& R = a.rows[b];
-    const int64_t nr = items_ret(R.rows_ret, t);
+    const int64_t own = R.rows_ret - a.rsh[b].sh_rows;
+    const int64_t nr = items_ret(own, t);
     // no empty item: contiguous heads are cut evenly; a paged head's items of
-    // ceil(rows / nr) rows rounded up to R0 all hold rows
-    R.nb_ret = (int32_t)(paged || R.rows_ret == 0 ? nr : ceil_div(R.rows_ret, ceil_div(R.rows_ret, nr)));
+    // ceil(rows / nr) rows rounded up to R0 all hold rows (a row whose rows
+    // are all shared keeps one empty item, which takes a fused append's token)
+    R.nb_ret = (int32_t)(paged || own == 0 ? nr : ceil_div(own, ceil_div(own, nr)));
     R.first_ret = next;
     next += lp.n_ret * R.nb_ret;
     if (lp.n_ret > 0 && R.nb_ret > 1) a.multi = 1;
@@ -683,13 +732,34 @@ int plan_decode(const duo_cache* c, int layer, const void* q, void* out, float s
     next += lp.n_str * R.nb_str;
     if (lp.n_str > 0 && R.nb_str > 1) a.multi = 1;
   }
+  a.items_sh = next;
+  for (int k = 0; k < a.n_share; ++k) {
+    duo::DecodeShare& S = a.share[k];
+    S.nb = (int32_t)items_ret(S.rows, t);
+    S.first = next;
+    next += lp.n_ret * S.nb;
+    a.multi = 1;
+  }
+  int32_t rec = next;  // records past the items': the shared items', group by group
+  for (int k = 0; k < a.n_share; ++k) {
+    duo::DecodeShare& S = a.share[k];
+    S.rec = rec;
+    for (int i = 0; i < S.R; ++i) {
+      a.rsh[S.b0 + i].sh_rec = rec + i * lp.n_ret * S.nb;
+      a.rsh[S.b0 + i].sh_nb = S.nb;
+    }
+    rec += S.R * lp.n_ret * S.nb;
+  }
+  a.n_records = rec;
   a.scale_log2 = scale * 1.4426950408889634f;
   return (int)next;
 }
 
-// Bytes of partial records a decode of `blocks` work items writes.
-size_t decode_records_bytes(const duo_cache* c, int blocks) {
-  return (size_t)blocks * decode_rec_floats(&c->cfg) * sizeof(float);
+// Bytes of partial records a planned decode writes: one per work item, and
+// with share groups one per (row of the group, shared item) after those.
+size_t decode_records_bytes(const duo_cache* c, const duo::DecodeArgs& a, int blocks) {
+  const size_t n = a.n_share > 0 ? (size_t)a.n_records : (size_t)blocks;
+  return n * decode_rec_floats(&c->cfg) * sizeof(float);
 }
 
 hipError_t launch_planned_decode(const duo_cache* c, duo::DecodeArgs& a, int blocks, void* ws, hipStream_t stream) {
@@ -757,7 +827,7 @@ int duo_decode_append_noalloc(duo_cache* c, int layer, const void* k, const void
   if (se != hipSuccess) return hip_fail(se, "address of the library's device scratch");
   duo::DecodeArgs a;
   const int blocks = plan_decode(c, layer, q, out, scale, k, v, &a);
-  const size_t need = decode_records_bytes(c, blocks);
+  const size_t need = decode_records_bytes(c, a, blocks);
   if (need > duo::kStaticScratchBytes)
     return fail(DUO_EWORKSPACE,
                 "this decode writes %zu bytes of partial results (%d work items); the library's device scratch "
@@ -1202,6 +1272,16 @@ int duo_cache_head_scales(const duo_cache* c, int layer, int kv_head, float** k_
   if (k_scale) *k_scale = f8 ? (ret ? p.ksc_ret : p.ksc_str) + (size_t)ci * slots : nullptr;
   if (v_scale) *v_scale = f8 ? (ret ? p.vsc_ret : p.vsc_str) + (size_t)ci * slots : nullptr;
   if (scale_stride) *scale_stride = f8 ? (int64_t)n_kind * slots : 0;
+  return ok();
+}
+
+int duo_decode_plan(const duo_cache* c, int layer, int* n_items, int* n_shared) {
+  if (int e = check_layer(c, layer)) return e;
+  if (!n_items || !n_shared) return fail(DUO_EINVAL, "n_items or n_shared is NULL");
+  duo::DecodeArgs a;
+  const int blocks = plan_decode(c, layer, nullptr, nullptr, 1.f, nullptr, nullptr, &a);
+  *n_items = blocks;
+  *n_shared = blocks - a.items_sh;
   return ok();
 }
 

@@ -127,6 +127,29 @@ struct DecodeRow {
   int32_t first_ret, first_str;  // index of the first work item of the row's retrieval / streaming heads
 };
 
+// A row of a share group: the rows of its retrieval heads that shared items
+// read for it (the full pages it shares with the other rows of its group;
+// 0: none).  The row's own retrieval items cover positions sh_rows ..
+// rows_ret; the shared items' sh_nb partial records for its retrieval head r
+// are records sh_rec + r * sh_nb + part.
+struct DecodeRowShare {
+  int32_t sh_rows, sh_rec, sh_nb;
+};
+
+// Rows R of a share group (batch rows b0 .. b0 + R - 1, forked from one
+// prefix) hold the same physical pages for positions 0 .. rows - 1.  Shared
+// work items read those rows once and attend every row's queries to them:
+// nb items per retrieval head, head r's at first + r * nb.  Item (head r,
+// part p) writes a record for each row i of the group: record
+// rec + (i * n_ret + r) * nb + p.
+constexpr int kMaxShares = 16;
+struct DecodeShare {
+  int32_t first, b0, R, rows, nb, rec;
+};
+// Partial records of one decode at most: one per work item, and up to four
+// per shared item (one per row of its group).
+constexpr int64_t kMaxDecodeRecords = 5 * (int64_t)kMaxDecodeBlocks;
+
 struct DecodeArgs {
   const void* q;   // [B][n_q][d]
   void* out;       // [B][n_q][d]
@@ -152,6 +175,13 @@ struct DecodeArgs {
   // it keep the argument lines the item lookup reads (moving them measured
   // up to 1% slower decode steps).
   Rope rope;
+  // Share groups, read only by the kernels launched for a plan that has
+  // some (kept after the fields above so that those keep their places).
+  // Shared items come after the streaming items, from items_sh; records end
+  // at n_records.
+  int32_t items_sh, n_share, n_records;
+  DecodeShare share[kMaxShares];
+  DecodeRowShare rsh[kMaxRows];
 };
 
 struct PrefillArgs {

@@ -660,6 +660,13 @@ struct DecodeItem {
   int part, nparts;
   int b, kvh;
   int row;          // batch row (index into DecodeArgs::rows)
+  // A shared item (share group rows b .. b + qrows - 1, their shared rows of
+  // retrieval head hh - b * n_ret): its queries are the group's qrows * g
+  // queries; it is never the last item of a head.  single: the item is its
+  // head's only partial result (it writes the output).
+  int qrows;
+  bool shared, single;
+  int sh_rec, sh_stride;  // a shared item: its record for row i of the group is sh_rec + i * sh_stride
   char* kbase;
   char* vbase;
   float* ksc;       // FP8 rows: per-row scales of the head (else null)
@@ -688,7 +695,7 @@ __device__ __forceinline__ int arg_byte(const int8_t* table, int i) {
   return (int)(int8_t)(word >> (8 * (i & 3)));
 }
 
-template <int ROWB, int RR>
+template <int ROWB, int RR, bool SH>
 __device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a, int blk) {
   // Index arithmetic in 32 bits (item and row counts fit), the head index
   // made wavefront-uniform so the head-map lookups are scalar loads: this
@@ -697,8 +704,38 @@ __device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a, int blk) 
   w.ptab = nullptr;
   w.shift = 0;
   w.pstride = 0;
-  int rows;
-  if (blk < a.items_ret) {
+  w.qrows = 1;
+  w.shared = false;
+  int rows, base = 0;  // the item's rows are positions base .. rows - 1 of its head, cut in nparts
+  if (SH && blk >= a.items_sh) {
+    int k = 0;
+    while (k + 1 < a.n_share && blk >= a.share[k + 1].first) ++k;  // share group of the item (uniform)
+    const DecodeShare& S = a.share[k];
+    const int rel = blk - S.first;
+    const int r = __builtin_amdgcn_readfirstlane(rel / S.nb);
+    const int b = S.b0;
+    w.part = rel - r * S.nb;
+    w.nparts = S.nb;
+    rows = S.rows;
+    w.row = b;
+    w.b = b;
+    w.hh = (int64_t)b * a.n_ret + r;
+    w.kvh = arg_byte(a.map.orig_ret, r);
+    w.qrows = S.R;
+    w.shared = true;
+    w.single = false;
+    w.sh_rec = S.rec + r * S.nb + w.part;
+    w.sh_stride = a.n_ret * S.nb;
+    // the group's shared pages, as row b's table names them
+    w.ptab = a.lp.table + (size_t)b * a.lp.max_pages;
+    w.shift = a.lp.page_shift;
+    w.pstride = (int64_t)a.n_ret << a.lp.page_shift;
+    const size_t srow = (size_t)r << a.lp.page_shift;
+    w.kbase = a.lp.k_ret + srow * ROWB;
+    w.vbase = a.lp.v_ret + srow * ROWB;
+    w.ksc = a.lp.ksc_ret ? a.lp.ksc_ret + srow : nullptr;
+    w.vsc = a.lp.vsc_ret ? a.lp.vsc_ret + srow : nullptr;
+  } else if (blk < a.items_ret) {
     int b = 0;
     while (b + 1 < a.B && blk >= a.rows[b + 1].first_ret) ++b;  // batch row of the item (uniform)
     const DecodeRow& R = a.rows[b];
@@ -707,6 +744,8 @@ __device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a, int blk) 
     w.part = rel - r * R.nb_ret;
     w.nparts = R.nb_ret;
     rows = R.rows_ret;
+    if constexpr (SH) base = a.rsh[b].sh_rows;  // rows shared items read for this row
+    w.single = w.nparts == 1 && base == 0;
     w.row = b;
     w.b = b;
     w.hh = (int64_t)b * a.n_ret + r;
@@ -732,6 +771,7 @@ __device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a, int blk) 
     w.part = rel - si * R.nb_str;
     w.nparts = R.nb_str;
     rows = R.rows_str;
+    w.single = w.nparts == 1;
     w.row = b;
     w.b = b;
     w.hh = (int64_t)a.B * a.n_ret + (int64_t)b * a.n_str + si;
@@ -746,9 +786,9 @@ __device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a, int blk) 
   // The items of a head split the rows held at planning.  The last one ends
   // at the rows held when the kernel runs (end_last_item: a replayed step
   // may find more); until then it ends where the plan did.
-  int per = __builtin_amdgcn_readfirstlane((rows + w.nparts - 1) / w.nparts);
-  if (w.ptab) per = (per + RR - 1) / RR * RR;  // paged: every round of rows lies in one page
-  w.r0 = (int64_t)w.part * per;
+  int per = __builtin_amdgcn_readfirstlane((rows - base + w.nparts - 1) / w.nparts);
+  if (w.ptab) per = (per + RR - 1) / RR * RR;  // paged: every round of rows lies in one page (base is whole pages)
+  w.r0 = (int64_t)base + (int64_t)w.part * per;
   w.r1 = w.r0 + per < rows ? w.r0 + per : rows;
   if (w.r0 > rows) w.r0 = rows;
   w.cnt = -1;
@@ -761,6 +801,38 @@ __device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a, int blk) 
 __device__ __forceinline__ int64_t row_count(const DecodeArgs& a, int b) {
   return *(const __attribute__((address_space(4))) int32_t*)(a.lp.len + b);
 }
+
+// rope_stage for a shared item's queries: rows [0, nrows * nq) of the
+// staging area, query row q of batch row b0 + q / nq turned at that batch
+// row's position (its count, less one unless the call appends).
+template <int ES>
+__device__ __forceinline__ void rope_stage_rows(const DecodeArgs& a, int b0, char* stage, int nq, int nrows,
+                                                int row_bytes, int d) {
+  const int half = d / 2;
+  const int n = nrows * nq * half;
+  for (int t = threadIdx.x; t < n; t += kDecodeThreads) {
+    const int row = t / half, i = t % half;
+    // rows 64 t' / d .. of 512 threads: the batch row is uniform in each
+    // wavefront (nq >= 4, d = 128), so its count comes by a scalar load
+    const int set = __builtin_amdgcn_readfirstlane(row / nq);
+    double dc, ds;
+    rope_cs(a.rope, row_count(a, b0 + set) - (a.new_k ? 0 : 1), i, dc, ds);
+    const float c = (float)dc, s = (float)ds;
+    char* base = stage + row * row_bytes;
+    if constexpr (ES == 2) {
+      uint16_t* e = reinterpret_cast<uint16_t*>(base);
+      const float x = __uint_as_float((uint32_t)e[i] << 16), y = __uint_as_float((uint32_t)e[i + half] << 16);
+      e[i] = (uint16_t)f32_to_bf16_bits(x * c - y * s);
+      e[i + half] = (uint16_t)f32_to_bf16_bits(y * c + x * s);
+    } else {
+      float* e = reinterpret_cast<float*>(base);
+      const float x = e[i], y = e[i + half];
+      e[i] = x * c - y * s;
+      e[i + half] = y * c + x * s;
+    }
+  }
+}
+
 
 // The last item of a head ends at the rows its batch row holds now.
 __device__ __forceinline__ void end_last_item(const DecodeArgs& a, DecodeItem& w) {
@@ -1412,7 +1484,9 @@ __device__ __forceinline__ void mf4_pv(MfState& st, const char* vt, int lane) {
 template <int X>
 using UnitTag = std::integral_constant<int, X>;
 
-template <int KT, int D, int G>
+// SH: the plan has share groups (the kernel then also runs shared items);
+// only the matrix-core instantiations with g = 4 or 8 take them.
+template <int KT, int D, int G, bool SH>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   using C = DecodeCfg<KT, D, G>;
   [[maybe_unused]] constexpr bool BF16 = C::BF16;
@@ -1430,8 +1504,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float w_m[G][SLOTS * 8], w_l[G][SLOTS * 8], w_w[G][SLOTS * 8],
       w_lw[G][SLOTS * 8];
   __shared__ float w_mt[G];
-  // the group's queries and the new token's K and V rows, loaded by direct loads
-  constexpr int QSTAGE = (G * C::IROWB + 1023) / 1024 * 1024;
+  // the group's queries (a shared item: the queries of its share group's
+  // rows, up to 16) and the new token's K and V rows, loaded by direct loads
+  constexpr bool SHARE = SH && C::MF && (G == 4 || G == 8);  // shared items (bf16 queries, d = 128)
+  constexpr int QGROUP = (G * C::IROWB + 1023) / 1024 * 1024;  // one row's query group, whole pieces
+  constexpr int QSTAGE = SHARE ? 16 * C::IROWB : QGROUP;
+  static_assert(!SHARE || (G * C::IROWB) % 1024 == 0, "a row's queries are whole staging pieces");
   constexpr int NSTAGE = (C::IROWB + 1023) / 1024 * 1024;
   static_assert(QSTAGE / 1024 + 2 <= kDecWaves, "one staging piece per wavefront");
   __shared__ __attribute__((aligned(1024))) char stage[QSTAGE + 2 * NSTAGE];
@@ -1466,14 +1544,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   const int hg = wave % C::HSPLIT;     // which HW query heads of the group it scores
   const bool active = slot < SLOTS;
   const int rg = lane >> 3, s = lane & 7;
-  DecodeItem w = decode_item<C::ROWB, C::ROUND_ROWS>(a, blockIdx.x);
+  DecodeItem w = decode_item<C::ROWB, C::ROUND_ROWS, SHARE>(a, blockIdx.x);
   // The row's token count: needed before the first loads by the last item of
   // a head (where it ends, where a fused append's token goes) and by the items
   // of a streaming head under a fused append (the slot the new token evicts);
   // other items wait for it only if rotary positions need the query's position.
-  if (w.part == w.nparts - 1 || (a.new_k != nullptr && w.hh >= (int64_t)a.B * a.n_ret)) {
+  const bool last_item = w.part == w.nparts - 1 && !w.shared;
+  if (last_item || (a.new_k != nullptr && w.hh >= (int64_t)a.B * a.n_ret)) {
     w.cnt = row_count(a, w.b);
-    if (w.part == w.nparts - 1) end_last_item(a, w);
+    if (last_item) end_last_item(a, w);
   }
   const int64_t nrounds = ((w.r1 - w.r0 + TR - 1) / TR + SLOTS - 1) / SLOTS;
   const size_t q_off = ((size_t)w.b * a.n_q + (size_t)w.kvh * G) * D;  // first query of the group
@@ -1481,7 +1560,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   // fused append: the last item of every head adds the new token at position
   // w.cnt; the step stores it only if the row has room (else it is attended
   // from the staging area alone and the cache's status bit is set)
-  const bool add_new = a.new_k != nullptr && w.part == w.nparts - 1;
+  const bool add_new = a.new_k != nullptr && last_item;
   const bool ret_head = w.hh < (int64_t)a.B * a.n_ret;
   const int64_t cap_str = a.cap_str;
   // streaming slot masked in the held rows (its token is evicted by the new one)
@@ -1541,21 +1620,25 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   // the staging loads, which were issued before those units.
   issue(0, ring0);
   {
-    constexpr int NQP = QSTAGE / 1024;  // query pieces
-    if (wave < NQP) {
-      const char* qsrc = static_cast<const char*>(a.q) + q_off * C::ES;
-      dma_lds16(dma_rsrc(qsrc, G * C::IROWB), stage + wave * 1024, (uint32_t)(wave * 1024 + lane * 16));
-    } else if (add_new && wave < NQP + 2) {
-      const char* nsrc = (wave == NQP ? a.new_k : a.new_v) + ((size_t)w.b * a.n_kv + w.kvh) * C::IROWB;
-      dma_lds16(dma_rsrc(nsrc, C::IROWB), stage + QSTAGE + (wave - NQP) * NSTAGE, (uint32_t)(lane * 16));
+    constexpr int PPR = QGROUP / 1024;  // query pieces per batch row
+    const int nqp = w.qrows * PPR;      // query pieces of this item
+    if (wave < nqp) {
+      const int qi = wave / PPR;        // row of the share group (0 for other items)
+      const char* qsrc = static_cast<const char*>(a.q) + (q_off + (size_t)qi * a.n_q * D) * C::ES;
+      dma_lds16(dma_rsrc(qsrc, G * C::IROWB), stage + wave * 1024, (uint32_t)((wave % PPR) * 1024 + lane * 16));
+    } else if (add_new && wave < nqp + 2) {
+      const char* nsrc = (wave == nqp ? a.new_k : a.new_v) + ((size_t)w.b * a.n_kv + w.kvh) * C::IROWB;
+      dma_lds16(dma_rsrc(nsrc, C::IROWB), stage + QSTAGE + (wave - nqp) * NSTAGE, (uint32_t)(lane * 16));
     }
   }
   issue(1, ring1);
   if constexpr (DEPTH == 3) issue(2, ring2);
   // rotary positions: this lane's angle (pair lane % (D/2)) at the query's
   // position, computed while the loads are in flight
+  // (a shared item's rows each have their own position: it takes their
+  // angles in its rotation pass below)
   double rcs = 1.0, rsn = 0.0;
-  if (a.rope.on) {
+  if (a.rope.on && !(SHARE && w.shared)) {
     const int64_t cnt = w.cnt >= 0 ? w.cnt : row_count(a, w.b);
     rope_cs(a.rope, cnt - (a.new_k ? 0 : 1), lane % (D / 2), rcs, rsn);
   }
@@ -1563,7 +1646,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   lds_barrier();
   if (a.rope.on) {
     // the queries (and the new token's K row) turned at the query's position
-    rope_stage<C::ES>(stage, G, stage + QSTAGE, add_new, C::IROWB, D, rcs, rsn);
+    if (SHARE && w.shared) rope_stage_rows<C::ES>(a, w.b, stage, G, w.qrows, C::IROWB, D);
+    else rope_stage<C::ES>(stage, G, stage + QSTAGE, add_new, C::IROWB, D, rcs, rsn);
     lds_barrier();
   }
   // this wavefront's HW queries, in the lane's slice layout (of the four-lane
@@ -1602,7 +1686,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     float qs = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const u32x4_t v = j < G ? *reinterpret_cast<const u32x4_t*>(stage + (size_t)j * C::IROWB + (32 * k + 8 * g) * 2)
+      const u32x4_t v = j < w.qrows * G ? *reinterpret_cast<const u32x4_t*>(stage + (size_t)j * C::IROWB + (32 * k + 8 * g) * 2)
                               : u32x4_t{0u, 0u, 0u, 0u};
       qm[k] = __builtin_bit_cast(bf16x8v_t, v);
       if constexpr (KV4) {
@@ -1751,49 +1835,56 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
 
   if constexpr (MF) {
     // ---- merge the eight wavefronts' states through LDS (the ring is free):
-    // X[wave][h][d] in ring0, the (max, sum) pairs in ring1
+    // query column j's accumulators X[wave][j][d] in ring0 (with shared
+    // items: columns 0-7 in ring0, 8-15 in ring1), the (max, sum) pairs in
+    // ring1 (ring2 with shared items)
     lds_barrier();  // every wavefront is done with the ring
-    float* xo = reinterpret_cast<float*>(ring0);
-    float* xml = reinterpret_cast<float*>(ring1);
+    constexpr int XS = SHARE ? 8 : G;    // columns per wavefront block of X
+    constexpr int MS = SHARE ? 16 : G;   // columns per wavefront block of the (max, sum) pairs
+    float* const xlo = reinterpret_cast<float*>(ring0);
+    float* const xhi = reinterpret_cast<float*>(ring1);
+    float* const xml = reinterpret_cast<float*>(SHARE ? ring2 : ring1);
+    auto xcol = [&](int v, int col) { return (col < XS ? xlo : xhi) + ((size_t)v * XS + (col % XS)) * D; };
     const int j = lane & 15, g = lane >> 4;
+    const int ncol = SHARE ? w.qrows * G : G;  // query columns in use
     const float lsum = swap32_sum(swap16_sum(mst.l));  // the query's sum over its four lanes
     if constexpr (KV4) {  // the accumulators held the levels + 136: drop 136 times the weights' sum
       const float wb = swap32_sum(swap16_sum(mst.w)) * kInt4Bias;
 #pragma unroll
       for (int t = 0; t < 8; ++t) mst.o[t] -= wb;
     }
-    if (j < G) {
+    if (j < ncol) {
 #pragma unroll
       for (int t = 0; t < 8; ++t)
-        *reinterpret_cast<float4*>(xo + ((size_t)wave * G + j) * D + 16 * t + 4 * g) =
+        *reinterpret_cast<float4*>(xcol(wave, j) + 16 * t + 4 * g) =
             make_float4(mst.o[t][0], mst.o[t][1], mst.o[t][2], mst.o[t][3]);
       if (g == 0) {
-        xml[wave * G + j] = mst.m;
-        xml[kDecWaves * G + wave * G + j] = lsum;
+        xml[wave * MS + j] = mst.m;
+        xml[kDecWaves * MS + wave * MS + j] = lsum;
       }
     }
     lds_barrier();
-    // four consecutive output elements per thread: head h = e4 / D
-    float* rec = a.ws1 + (size_t)blockIdx.x * C::REC;
-    for (int e4 = threadIdx.x * 4; e4 < G * D; e4 += kDecodeThreads * 4) {
+    // four consecutive output elements per thread: query column h = e4 / D
+    // (a shared item: row h / G of its group, query head h % G)
+    for (int e4 = threadIdx.x * 4; e4 < ncol * D; e4 += kDecodeThreads * 4) {
       const int h = e4 / D, d = e4 % D;
       float M = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < kDecWaves; ++v) M = fmaxf(M, xml[v * G + h]);
+      for (int v = 0; v < kDecWaves; ++v) M = fmaxf(M, xml[v * MS + h]);
       float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
       float L = 0.f;
 #pragma unroll
       for (int v = 0; v < kDecWaves; ++v) {
-        const float mv = xml[v * G + h];
+        const float mv = xml[v * MS + h];
         const float wt = (mv == -INFINITY) ? 0.f : fast_exp2(mv - M);
-        L = fmaf(xml[kDecWaves * G + v * G + h], wt, L);
-        const float4 x = *reinterpret_cast<const float4*>(xo + ((size_t)v * G + h) * D + d);
+        L = fmaf(xml[kDecWaves * MS + v * MS + h], wt, L);
+        const float4 x = *reinterpret_cast<const float4*>(xcol(v, h) + d);
         A.x = fmaf(x.x, wt, A.x);
         A.y = fmaf(x.y, wt, A.y);
         A.z = fmaf(x.z, wt, A.z);
         A.w = fmaf(x.w, wt, A.w);
       }
-      if (w.nparts == 1) {
+      if (w.single) {
         const float inv = 1.f / L;
         uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + q_off + e4;
         o[0] = (uint16_t)f32_to_bf16_bits(A.x * inv);
@@ -1801,10 +1892,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
         o[2] = (uint16_t)f32_to_bf16_bits(A.z * inv);
         o[3] = (uint16_t)f32_to_bf16_bits(A.w * inv);
       } else {
-        *reinterpret_cast<float4*>(rec + e4) = A;
+        const int qi = h / G, hq = h % G;
+        const size_t slot = w.shared ? (size_t)w.sh_rec + (size_t)qi * w.sh_stride : (size_t)blockIdx.x;
+        float* rec = a.ws1 + slot * C::REC;
+        *reinterpret_cast<float4*>(rec + hq * D + d) = A;
         if (d == 0) {
-          rec[G * D + h] = M;
-          rec[G * D + G + h] = L;
+          rec[G * D + hq] = M;
+          rec[G * D + G + hq] = L;
         }
       }
     }
@@ -1883,7 +1977,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
           A.w = fmaf(x.w, wv[k], A.w);
         }
       }
-      if (w.nparts == 1) {
+      if (w.single) {
         const float inv = 1.f / L;
         if (BF16) {
           uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + q_off + e4;
@@ -1912,7 +2006,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
 constexpr int kCombineElems = 32;
 constexpr int kCombineGroups = kDecodeThreads / kCombineElems;  // 16
 
-template <int KT, int D, int G>
+template <int KT, int D, int G, bool SH>
 __global__ __launch_bounds__(kDecodeThreads) void combine_kernel(DecodeArgs a) {
   using C = DecodeCfg<KT, D, G>;
   [[maybe_unused]] constexpr bool BF16 = C::BF16;
@@ -1932,12 +2026,19 @@ __global__ __launch_bounds__(kDecodeThreads) void combine_kernel(DecodeArgs a) {
   const int64_t n_ret_heads = (int64_t)a.B * a.n_ret;
   int64_t first;
   int n_seg, b, kvh;
+  int n_all;                       // the head's records: its own items', then its shared items'
+  const float* rec_sh = nullptr;   // the first shared item's record for this row and head
   if (hh < n_ret_heads) {
     b = (int)(hh / a.n_ret);
     const int r = (int)(hh % a.n_ret);
     first = a.rows[b].first_ret + (int64_t)r * a.rows[b].nb_ret;
     n_seg = a.rows[b].nb_ret;
     kvh = arg_byte(a.map.orig_ret, r);
+    n_all = n_seg;
+    if (SH && a.rsh[b].sh_rows > 0) {
+      rec_sh = a.ws1 + ((size_t)a.rsh[b].sh_rec + (size_t)r * a.rsh[b].sh_nb) * C::REC;
+      n_all += a.rsh[b].sh_nb;
+    }
   } else {
     const int64_t x = hh - n_ret_heads;
     b = (int)(x / a.n_str);
@@ -1945,20 +2046,22 @@ __global__ __launch_bounds__(kDecodeThreads) void combine_kernel(DecodeArgs a) {
     first = a.rows[b].first_str + (int64_t)si * a.rows[b].nb_str;
     n_seg = a.rows[b].nb_str;
     kvh = arg_byte(a.map.orig_str, si);
+    n_all = n_seg;
   }
-  if (n_seg == 1) return;  // written by the decode kernel
+  if (n_all == 1) return;  // written by the decode kernel
   const float* rec0 = a.ws1 + (size_t)first * C::REC;
+  auto rec_at = [&](int i) { return i < n_seg ? rec0 + (size_t)i * C::REC : rec_sh + (size_t)(i - n_seg) * C::REC; };
   const int el = threadIdx.x % kCombineElems, grp = threadIdx.x / kCombineElems;
   const int e = h * D + dcn * kCombineElems + el;
   float M = -INFINITY, L = 0.f, A = 0.f;
   constexpr int NB = 8;  // records per batch, loads issued together
-  for (int i0 = grp; i0 < n_seg; i0 += NB * kCombineGroups) {
+  for (int i0 = grp; i0 < n_all; i0 += NB * kCombineGroups) {
     float mv[NB], lv[NB], av[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int i = i0 + j * kCombineGroups;
-      const float* r = rec0 + (size_t)(i < n_seg ? i : i0) * C::REC;
-      mv[j] = i < n_seg ? r[G * D + h] : -INFINITY;
+      const float* r = rec_at(i < n_all ? i : i0);
+      mv[j] = i < n_all ? r[G * D + h] : -INFINITY;
       lv[j] = r[G * D + G + h];
       av[j] = r[e];
     }
@@ -1996,9 +2099,9 @@ __global__ __launch_bounds__(kDecodeThreads) void combine_kernel(DecodeArgs a) {
   else reinterpret_cast<float*>(a.out)[o] = At / Lt;
 }
 
-template <int KT, int D, int G>
-hipError_t launch_decode_g(const DecodeArgs& a, int blocks, hipStream_t s) {
-  decode_kernel<KT, D, G><<<blocks, kDecodeThreads, 0, s>>>(a);
+template <int KT, int D, int G, bool SH>
+hipError_t launch_decode_sh(const DecodeArgs& a, int blocks, hipStream_t s) {
+  decode_kernel<KT, D, G, SH><<<blocks, kDecodeThreads, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (!a.multi) {  // every head finished in one item; a fused append's counts still advance
@@ -2010,8 +2113,17 @@ hipError_t launch_decode_g(const DecodeArgs& a, int blocks, hipStream_t s) {
     return launch_advance(v, s);
   }
   const int64_t heads = (int64_t)a.B * (a.n_ret + a.n_str);
-  combine_kernel<KT, D, G><<<(unsigned)(heads * G * (D / kCombineElems)), kDecodeThreads, 0, s>>>(a);
+  combine_kernel<KT, D, G, SH><<<(unsigned)(heads * G * (D / kCombineElems)), kDecodeThreads, 0, s>>>(a);
   return hipGetLastError();
+}
+
+template <int KT, int D, int G>
+hipError_t launch_decode_g(const DecodeArgs& a, int blocks, hipStream_t s) {
+  // plans with share groups exist only at d = 128, bf16 queries, g = 4 or 8
+  if constexpr (DecodeCfg<KT, D, G>::MF && (G == 4 || G == 8)) {
+    if (a.n_share > 0) return launch_decode_sh<KT, D, G, true>(a, blocks, s);
+  }
+  return launch_decode_sh<KT, D, G, false>(a, blocks, s);
 }
 
 template <int KT, int D>

@@ -339,6 +339,17 @@ int duo_cache_head_scales(const duo_cache* c, int layer, int kv_head, float** k_
  * row.  Captured calls that involve the row must be captured again. */
 int duo_cache_reset_row(duo_cache* c, int layer, int row);
 
+/* How duo_decode / duo_decode_append would cut `layer`'s rows into work
+ * items as the rows stand now: *n_items in one launch, *n_shared of them
+ * shared items that read the pages a group of forked rows holds in common
+ * once for the whole group ("Attention Variants and Memory Efficiency",
+ * "What the Inference Runtime Can Change": a matching prefix is stored once;
+ * the decode also reads it once).  Groups are consecutive batch rows that
+ * hold the same physical pages from position 0 (rows forked from one
+ * prefix, see duo_cache_fork_row), at most 16 / g rows each, in bf16 caches
+ * of d_head = 128 with g = 4 or 8.  Host only. */
+int duo_decode_plan(const duo_cache* c, int layer, int* n_items, int* n_shared);
+
 /* Prefix sharing: batch row dst (which must hold no token) becomes a copy of
  * batch row src of `layer`, with src's token count ("Attention Variants and
  * Memory Efficiency", "What the Inference Runtime Can Change": matching

@@ -344,3 +344,73 @@ def test_paged_gqa70b_128k_layer():
     Ks, Vs = stored(K, w.dtype), stored(V, w.dtype)
     ref = OA.decode_step(stored(Q, w.dtype)[0], Ks[0], Vs[0], mask, w.S, w.W, w.scale)
     check_close(out[0], ref, w.dtype, f"{w.name} paged fused layer {layer}")
+
+
+SHARED = [(8, 2, None, 0.0, False), (4, 4, None, 0.0, False), (4, 3, None, 10000.0, True),
+          (8, 2, "fp8", 0.0, False), (8, 2, "int4", 0.0, True)]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("g,R,kvf,theta,exact", SHARED)
+def test_shared_prefix_decode(g, R, kvf, theta, exact):
+    """Rows forked from one prefix decode as a share group: the prefix's full
+    pages are read once by shared work items that attend every row's queries
+    to them, each row's own items take the rest, and the combine merges both.
+    R rows forked from row 0 (one of them with no tokens of its own when the
+    prefix is whole pages), plus an unrelated row; plain decodes and fused
+    steps against the oracle, with the plan checked to use shared items."""
+    need_gpu()
+    from head_wise_kv_amd import DuoCache
+    from oracle import quant4 as Q4
+    from oracle import rope as RP
+    say("shared prefix", g, R, kvf, theta, exact)
+    pr = 512 if kvf == "int4" else P  # INT4 rounds are 512 rows: pages of >= 512
+    B, n_kv, d, S, W = R + 1, 2, 128, 4, 64
+    n_q = n_kv * g
+    mask = [1, 0]
+    n = 4 * pr if exact else 3 * pr + 37
+    own = [5, 0 if exact else 9] + [40 * i for i in range(2, R)] + [n + 11]  # the last row is not a fork
+    steps = 3
+    N = n + max(own) + steps
+    K, V, Q = _seq(B, n_kv, N, d, 2600 + g + R, n_q)
+    K[1:R, :, :n], V[1:R, :, :n] = K[0, :, :n], V[0, :, :n]
+    c = DuoCache(1, B, n_q, n_kv, d, N, S, W, "bf16", [mask], kv_format=kvf, page_rows=pr,
+                 n_pages=B * (-(-N // pr)), rope_theta=theta)
+    Kd, Vd, Qd = (WL.to_torch(x, "bf16").cuda() for x in (K, V, Q))
+    c.append_row(0, 0, Kd[:1, :, :n].contiguous(), Vd[:1, :, :n].contiguous())
+    for r in range(1, R):
+        c.fork_row(0, 0, r)
+    for r, m in enumerate(own):
+        p0 = n if r < R else 0
+        if m:
+            c.append_row(0, r, Kd[r:r + 1, :, p0:p0 + m].contiguous(), Vd[r:r + 1, :, p0:p0 + m].contiguous())
+    lens = [n + m if r < R else m for r, m in enumerate(own)]
+    items, shared = c.decode_plan(0)
+    assert shared > 0, (items, shared)
+
+    def ref(r, t):
+        q = stored(Q[r, :, t], "bf16")
+        Ks, Vs = stored(K[r, :, :t + 1], "bf16"), stored(V[r, :, :t + 1], "bf16")
+        if theta > 0:
+            return RP.decode_step_rope(q, Ks, Vs, mask, S, W, d ** -0.5, theta, "bf16", kv_format=kvf)
+        if kvf == "int4":
+            return Q4.decode_step_int4(q, Ks.astype(np.float32), Vs.astype(np.float32), mask, S, W, d ** -0.5)
+        if kvf == "fp8":
+            return OQ.decode_step_fp8(q, Ks.astype(np.float32), Vs.astype(np.float32), mask, S, W, d ** -0.5)
+        return OA.decode_step(q, Ks, Vs, mask, S, W, d ** -0.5)
+
+    q = torch.stack([Qd[r, :, lens[r] - 1] for r in range(B)]).contiguous()
+    out = c.decode(0, q)
+    torch.cuda.synchronize()
+    for r in range(B):
+        check_close(out[r], ref(r, lens[r] - 1), "bf16", f"shared decode row {r}")
+    for i in range(steps):
+        t = [m + i for m in lens]
+        kn = torch.stack([Kd[r, :, t[r]:t[r] + 1] for r in range(B)]).contiguous()
+        vn = torch.stack([Vd[r, :, t[r]:t[r] + 1] for r in range(B)]).contiguous()
+        q = torch.stack([Qd[r, :, t[r]] for r in range(B)]).contiguous()
+        out = c.decode_append(0, kn, vn, q)
+        torch.cuda.synchronize()
+        for r in range(B):
+            check_close(out[r], ref(r, t[r]), "bf16", f"shared step {i} row {r}")
+    assert c.decode_plan(0)[1] > 0

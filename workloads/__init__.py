@@ -61,6 +61,7 @@ class Workload:
     kv_format: Optional[str] = None     # "fp8" / "int4": K/V rows stored as low-bit codes + row scales
     page_rows: int = 0                  # > 0: retrieval rows in pages of this many rows
     rope_theta: float = 0.0             # > 0: rotary positions with this base
+    forked: bool = False                # rows 1 .. B-1 forked from row 0's prefix (paged: its full pages shared)
 
     @property
     def g(self) -> int:
@@ -124,6 +125,13 @@ for _n in ("gqa70b_decode_128k", "mha7b_decode_128k"):
 # and inputs; the pool holds exactly the rows the batch needs).
 WORKLOADS["gqa70b_decode_128k_paged"] = WORKLOADS["gqa70b_decode_128k"].with_(name="gqa70b_decode_128k_paged",
                                                                             page_rows=256)
+# Two requests that share a 128k prefix (row 1 forked from row 0 in every
+# layer, the prefix's full 256-row pages shared) against the same two rows
+# held apart: the shared pages are read once per step for both rows.
+WORKLOADS["gqa70b_decode_128k_b2_forked"] = WORKLOADS["gqa70b_decode_128k"].with_(
+    name="gqa70b_decode_128k_b2_forked", B=2, page_rows=256, forked=True)
+WORKLOADS["gqa70b_decode_128k_b2_paged"] = WORKLOADS["gqa70b_decode_128k"].with_(
+    name="gqa70b_decode_128k_b2_paged", B=2, page_rows=256)
 # ... and with rotary positions (base 500,000, as LLaMA-3 checkpoints use).
 WORKLOADS["gqa70b_decode_128k_rope"] = WORKLOADS["gqa70b_decode_128k"].with_(name="gqa70b_decode_128k_rope",
                                                                            rope_theta=500000.0)
