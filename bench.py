@@ -392,7 +392,8 @@ def main():
                                       "mha7b_decode_128k,gqa70b_decode_128k_fp8,mha7b_decode_128k_fp8,"
                                       "gqa70b_decode_128k_int4,mha7b_decode_128k_int4,"
                                       "gqa70b_decode_128k_paged,gqa70b_decode_128k_rope,"
-                                      "gqa70b_decode_128k_full,mha7b_decode_128k_full",
+                                      "gqa70b_decode_128k_full,mha7b_decode_128k_full,"
+                                      "gqa70b_decode_128k_b2_forked,gqa70b_decode_128k_b2_paged",
                     help="comma-separated extra decode workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-gated", action="store_true")
@@ -476,6 +477,11 @@ def main():
                    for n in steps_us if n + "_full" in steps_us}
         if vs_full:
             line["duo_vs_full_attention"] = vs_full
+        # two requests sharing a 128k prefix (forked rows: its pages stored and
+        # read once) against the same two rows held apart
+        if "gqa70b_decode_128k_b2_forked" in steps_us and "gqa70b_decode_128k_b2_paged" in steps_us:
+            f, p = steps_us["gqa70b_decode_128k_b2_forked"], steps_us["gqa70b_decode_128k_b2_paged"]
+            line["shared_prefix"] = {"forked_us_per_step": f, "apart_us_per_step": p, "speedup": round(p / f, 3)}
     if not args.no_prefill:
         pw = WL.WORKLOADS["llama3_8b_prefill_64k"]
         p = bench_prefill(pw)

@@ -219,8 +219,9 @@ int duo_decode_append(duo_cache* c, int layer, const void* k, const void* v, con
  * softmax records go to a device array inside the library instead of a
  * caller workspace.  That array holds 8 MiB on each GPU the library runs on
  * (it is part of the loaded code object and stays until the process ends);
- * a call whose work items need more (about 2,000 work items at g = 8,
- * d_head = 128) fails with DUO_EWORKSPACE and changes no state, and
+ * a call whose partial records need more (one per work item, and one per
+ * row of a share group for each shared work item: about 2,000 records at
+ * g = 8, d_head = 128) fails with DUO_EWORKSPACE and changes no state, and
  * duo_decode_append with a workspace serves it.  The call allocates nothing.
  * Every call on one GPU shares that GPU's array and leaves its contents
  * behind (no call reads what an earlier one left): calls that may run at the
@@ -359,7 +360,9 @@ int duo_decode_plan(const duo_cache* c, int layer, int* n_items, int* n_shared);
  * again.  src's last page, if partly filled, is copied to a page of dst's own;
  * so are the streaming heads' slots, positions and scales.  A contiguous cache
  * copies every held row.  Enqueued on `stream`.  DUO_ECAPACITY if no page is
- * free for the copy. */
+ * free for the copy.  Decodes read the shared pages once for all the rows
+ * holding them when those rows are consecutive batch rows (bf16 queries,
+ * d_head = 128, g = 4 or 8, up to 16 / g rows a group; see duo_decode_plan). */
 int duo_cache_fork_row(duo_cache* c, int layer, int src_row, int dst_row, void* stream);
 
 /* Bring the host-side token counts up to date with the device-side counts
