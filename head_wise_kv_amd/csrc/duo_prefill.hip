@@ -117,6 +117,11 @@ __device__ __forceinline__ TileRanges plan_tiles(const PrefillArgs& a, bool ret,
 
 // ------------------------------------------------------------------ bf16 MFMA path
 
+// Tile descriptors a workgroup keeps in LDS (16 bytes each): 16 KB at
+// d = 128; 8 KB at d = 64, where two workgroups still share a CU.
+template <int D>
+constexpr int pf_tile_table() { return D >= 128 ? 1024 : 512; }
+
 struct PfItem {
   int b, kvh, cidx, h_first, qt;
   bool ret;
@@ -164,6 +169,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
   __shared__ int32_t klo_lds[kPfHalves][2][kBN];
   __shared__ uint32_t kspan_lds[kPfHalves][2][kBN];
   __shared__ int s_full[kPfHalves][2];
+  constexpr int TT = pf_tile_table<D>();
+  static_assert(TT / 2 <= kPfThreads, "half the table filled at once, one tile per thread");
+  __shared__ uint4 tdesc[TT];
 
   const PfItem w = pf_item(a, g, hpi);
   const int tid = threadIdx.x;
@@ -242,7 +250,6 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
       *reinterpret_cast<u32x4_t*>(&k_lds[0][0][0] + off) = z;
       *reinterpret_cast<u32x4_t*>(&v_lds[0][0][0] + off) = z;
     }
-    __syncthreads();
   }
 
   // Tile `it` -> (source, first row, row limit), as selects of per-run
@@ -271,37 +278,64 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
     // a retrieval head's cached positions (< P) are seen by every chunk row
     return whole && (src == SRC_CACHE_LINEAR || (src == SRC_CHUNK && chunk_ok));
   };
-  // Prepare tile `it` for buffer `buf` of this wavefront's key half: its key
-  // visibility, for a tile that does not pass tile_full, by plain stores (the
-  // half's first wavefront) with a flag telling whether every row of the item
-  // sees every key of the tile all the same (then the mask is skipped); and
-  // the direct loads of its K/V pieces (split over the half's wavefronts),
-  // which the caller issues.
-  auto prepare = [&](int32_t it, int buf) -> TileLoads<D> {
-    TileLoads<D> ld;
-    ld.kdst = lds_addr(k_lds[kh][buf] + sub * 1024);
-    ld.vdst = lds_addr(v_lds[kh][buf] + sub * 1024);
-    ld.koff = koff;
-    ld.voff = voff;
-    if (it >= n_tiles) {
-      ld.rk = ld.rv = dma_rsrc(kn, 0);
-      return ld;
-    }
+  // Tile descriptors, one per tile of the item, computed once by the whole
+  // workgroup (one tile per thread) into an LDS table: the byte offset of the
+  // tile's first row in its source (after the page lookup of a paged head),
+  // the tile's first row number, its byte count, source and whether it needs
+  // no mask.  Every wavefront of a key half then reads the descriptor of its
+  // next tile instead of working it out in scalar code each step.  The table
+  // holds TT tiles; an item with more tiles has the entries of tiles it has
+  // passed refilled, well before they are read (see the loop).
+  auto fill_desc = [&](int32_t t0) {  // tiles t0 .. t0 + TT / 2 - 1
+    const int32_t it = t0 + tid;
+    if (tid >= TT / 2 || it >= n_tiles) return;
     int src;
     int32_t base, limit;
     tile_src(it, src, base, limit);
-    const char* ks = (src == SRC_CHUNK) ? kn : kc;
-    const char* vs = (src == SRC_CHUNK) ? vn : vc;
     const int nbytes = min(limit - base, kBN) * (int)rowb;
     // a paged head's tile (64 rows from a multiple of 64) lies in one page
     const int64_t roff = (src == SRC_CACHE_LINEAR && a.lp.table)
                              ? paged_row(a.lp.table + (size_t)w.b * a.lp.max_pages, a.lp.page_shift,
                                          (int64_t)a.n_ret << a.lp.page_shift, base)
                              : base;
+    const uint64_t boff = (uint64_t)roff * rowb;
+    tdesc[it & (TT - 1)] =
+        make_uint4((uint32_t)boff, (uint32_t)(boff >> 32), (uint32_t)base,
+                   (uint32_t)nbytes | ((uint32_t)src << 16) | ((uint32_t)tile_full(it) << 18));
+  };
+
+  // Prepare tile `it` for buffer `buf` of this wavefront's key half: its key
+  // visibility, for a tile that needs a mask, by plain stores (the half's
+  // first wavefront) with a flag telling whether every row of the item sees
+  // every key of the tile all the same (then the mask is skipped); and the
+  // direct loads of its K/V pieces (split over the half's wavefronts), which
+  // the caller issues.  `full` tells whether the tile needs no mask at all.
+  auto prepare = [&](int32_t it, int buf, bool& full) -> TileLoads<D> {
+    TileLoads<D> ld;
+    ld.kdst = lds_addr(k_lds[kh][buf] + sub * 1024);
+    ld.vdst = lds_addr(v_lds[kh][buf] + sub * 1024);
+    ld.koff = koff;
+    ld.voff = voff;
+    full = true;
+    if (it >= n_tiles) {
+      ld.rk = ld.rv = dma_rsrc(kn, 0);
+      return ld;
+    }
+    const uint4 dsc = tdesc[it & (TT - 1)];
+    // (readfirstlane gives an int: each word goes through uint32_t so that
+    // the low one is not sign-extended)
+    const uint32_t meta = (uint32_t)__builtin_amdgcn_readfirstlane(dsc.w);
+    const uint64_t boff = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(dsc.y) << 32) |
+                          (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(dsc.x);
+    const int src = (int)((meta >> 16) & 3u);
+    full = ((meta >> 18) & 1u) != 0;
+    const int nbytes = (int)(meta & 0xffffu);
     // The stored positions of a streaming head's slots are a global load:
     // it is waited for here, before any of the tile's direct loads is issued
     // (waits count loads in issue order).
-    if (sub == 0 && !tile_full(it)) {  // one wavefront, all lanes: lane = key of the tile
+    if (sub == 0 && !full) {  // one wavefront, all lanes: lane = key of the tile
+      const int32_t base = (int32_t)__builtin_amdgcn_readfirstlane(dsc.z);
+      const int32_t limit = src == SRC_CHUNK ? chunk_rows : cache_rows;
       const int32_t row = base + lane;
       int64_t kp = -1;  // past the end: never visible
       if (row < limit) {
@@ -318,8 +352,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
       const uint64_t bal = __builtin_amdgcn_ballot_w64(all);
       if (lane == 0) s_full[kh][buf] = (bal == ~0ull) ? 1 : 0;
     }
-    ld.rk = dma_rsrc(ks + (size_t)roff * rowb, nbytes);
-    ld.rv = dma_rsrc(vs + (size_t)roff * rowb, nbytes);
+    const char* ks = (src == SRC_CHUNK) ? kn : kc;
+    const char* vs = (src == SRC_CHUNK) ? vn : vc;
+    ld.rk = dma_rsrc(ks + boff, nbytes);
+    ld.rv = dma_rsrc(vs + boff, nbytes);
     return ld;
   };
 
@@ -337,22 +373,35 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a,
 
   // The two halves walk the tile list in lockstep, one barrier per step.
   // The next tile's loads are issued during the current tile's work.
+  // The table starts with tiles [0, TT); the zero fill above and these
+  // stores are published by one barrier.
+  fill_desc(0);
+  fill_desc(TT / 2);
+  __syncthreads();
   const int32_t n_steps = (n_tiles + 1) / 2;
-  prepare(kh, 0).all();
+  bool full_cur;  // the current tile needs no mask
+  prepare(kh, 0, full_cur).all();
   for (int32_t step = 0; step < n_steps; ++step) {
     const int buf = (int)(step & 1);
     // this wavefront's direct loads for the current tile have landed; after
     // the barrier every wavefront's have, and the previous tile is consumed.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    // Every TT / 4 steps (tiles 2 step .. 2 step + TT / 2 - 1 are in the
+    // table), the entries of the TT / 2 tiles before 2 step, all consumed,
+    // take the tiles 2 step + TT / 2 onwards, which are first read
+    // TT / 4 - 1 steps (and as many barriers) later.
+    if (step > 0 && step % (TT / 4) == 0) fill_desc(2 * step + TT / 2);
     // this half has no tile left, and so no next one (wavefront-uniform)
     if (2 * step + kh >= n_tiles) continue;
-    const TileLoads<D> next = prepare(2 * (step + 1) + kh, buf ^ 1);
+    bool full_next;
+    const TileLoads<D> next = prepare(2 * (step + 1) + kh, buf ^ 1, full_next);
     const char* kt = k_lds[kh][buf];
     const char* vt = v_lds[kh][buf];
-    const bool masked = !tile_full(2 * step + kh) && s_full[kh][buf] == 0;
+    const bool masked = !full_cur && s_full[kh][buf] == 0;
     pf_tile<D>(o, m_run, l_run, qb, kt, vt, masked, klo_lds[kh][buf], kspan_lds[kh][buf], iq, a.scale_log2, lane,
                next);
+    full_cur = full_next;
   }
 
   // ---- merge the odd half into the even half through LDS (the tile buffers
