@@ -63,7 +63,10 @@ struct Plan {
   size_t ws_dequant = 0;  // FP8 caches: one layer's held rows in bf16 for prefill (after the records)
 };
 
-bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+// Group sizes the decode kernels are built for: 1 .. 16 where scores run on
+// the matrix cores (bf16 queries, d_head 128, every K/V row format), 1 .. 8
+// on the vector ALU (fp32, or d_head 64).
+int max_group(const duo_config* c) { return (c->dtype == DUO_BF16 && c->d_head == 128) ? 16 : 8; }
 
 int validate(const duo_config* c) {
   if (!c) return fail(DUO_EINVAL, "config is NULL");
@@ -72,10 +75,11 @@ int validate(const duo_config* c) {
   if (c->n_q % c->n_kv != 0) return fail(DUO_EINVAL, "n_q (%d) must be a multiple of n_kv (%d)", c->n_q, c->n_kv);
   if (c->n_kv > duo::kMaxKV) return fail(DUO_EUNSUPPORTED, "n_kv %d > %d", c->n_kv, duo::kMaxKV);
   if (c->B > duo::kMaxRows) return fail(DUO_EUNSUPPORTED, "B %d > %d batch rows", c->B, duo::kMaxRows);
-  if (!supported_group(c->n_q / c->n_kv))
-    return fail(DUO_EUNSUPPORTED, "group size g = %d not built (1, 2, 4, 8)", c->n_q / c->n_kv);
   if (c->d_head != 64 && c->d_head != 128) return fail(DUO_EUNSUPPORTED, "d_head %d not built (64, 128)", c->d_head);
   if (c->dtype != DUO_F32 && c->dtype != DUO_BF16) return fail(DUO_EUNSUPPORTED, "dtype %d", c->dtype);
+  if (c->n_q / c->n_kv > max_group(c))
+    return fail(DUO_EUNSUPPORTED, "group size g = %d not built (1 .. %d for this dtype and d_head)", c->n_q / c->n_kv,
+                max_group(c));
   if (c->kv_format != DUO_KV_NATIVE && c->kv_format != DUO_KV_FP8 && c->kv_format != DUO_KV_INT4)
     return fail(DUO_EUNSUPPORTED, "kv_format %d", c->kv_format);
   if (c->kv_format != DUO_KV_NATIVE && (c->dtype != DUO_BF16 || c->d_head != 128))

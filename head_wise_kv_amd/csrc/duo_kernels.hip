@@ -305,7 +305,10 @@ struct DecodeCfg {
   // the group's query heads over its own rows of a round (16 bf16, 32 FP8 or
   // 64 INT4 rows)
   static constexpr bool MF = KT >= 1 && D == 128;
-  static constexpr int HW = MF ? G : (G < 4 ? G : 4);  // query heads per wavefront
+  // query heads per wavefront: the whole group on the matrix cores (up to 16,
+  // one column each of the 16-column tile); otherwise 4, 2 or 1, whichever
+  // divides the group (the four-lane score layout needs a divisor of 4)
+  static constexpr int HW = MF ? G : (G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1);
   static constexpr int HSPLIT = G / HW;          // wavefronts per slot
   static constexpr int SLOTS_W = kDecWaves / HSPLIT;
   static constexpr int SLOTS_B = kUnitBytes / (16 * ROWB);  // keeps TR >= 16
@@ -324,6 +327,7 @@ struct DecodeCfg {
   static_assert(RPL >= 2 && RPL % 2 == 0, "rows are paired for the weighted sum");
   static_assert(SLOT_BYTES % 1024 == 0, "a load piece stays within one tile");
   static_assert(G % HW == 0, "head split must tile the group");
+  static_assert(MF ? G <= 16 : HSPLIT <= kDecWaves, "a slot's head split fits the workgroup");
   static_assert(!LOWBIT || MF, "FP8 and INT4 rows are decoded on the matrix cores, at d = 128");
 };
 
@@ -1839,11 +1843,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     // items: columns 0-7 in ring0, 8-15 in ring1), the (max, sum) pairs in
     // ring1 (ring2 with shared items)
     lds_barrier();  // every wavefront is done with the ring
-    constexpr int XS = SHARE ? 8 : G;    // columns per wavefront block of X
+    // (more than 8 query columns, in shared items or groups of g > 8: columns
+    // 0-7 in ring0, 8-15 in ring1, the (max, sum) pairs in ring2)
+    constexpr bool WIDE = SHARE || G > 8;
+    constexpr int XS = WIDE ? 8 : G;     // columns per wavefront block of X
     constexpr int MS = SHARE ? 16 : G;   // columns per wavefront block of the (max, sum) pairs
+    static_assert(kDecWaves * XS * D * 4 <= kUnitBytes, "a ring unit holds X for 8 columns");
     float* const xlo = reinterpret_cast<float*>(ring0);
     float* const xhi = reinterpret_cast<float*>(ring1);
-    float* const xml = reinterpret_cast<float*>(SHARE ? ring2 : ring1);
+    float* const xml = reinterpret_cast<float*>(WIDE ? ring2 : ring1);
     auto xcol = [&](int v, int col) { return (col < XS ? xlo : xhi) + ((size_t)v * XS + (col % XS)) * D; };
     const int j = lane & 15, g = lane >> 4;
     const int ncol = SHARE ? w.qrows * G : G;  // query columns in use
@@ -2126,25 +2134,28 @@ hipError_t launch_decode_g(const DecodeArgs& a, int blocks, hipStream_t s) {
   return launch_decode_sh<KT, D, G, false>(a, blocks, s);
 }
 
+// Group sizes built: 1 .. 16 on the matrix cores (bf16, FP8 and INT4 rows
+// at d = 128), 1 .. 8 on the vector ALU (fp32 rows, d = 64).
 template <int KT, int D>
+constexpr int max_group() { return DecodeCfg<KT, D, 1>::MF ? 16 : 8; }
+
+template <int KT, int D, int G = 1>
 hipError_t launch_decode_d(const DecodeArgs& a, int g, int blocks, hipStream_t s) {
-  switch (g) {
-    case 1: return launch_decode_g<KT, D, 1>(a, blocks, s);
-    case 2: return launch_decode_g<KT, D, 2>(a, blocks, s);
-    case 4: return launch_decode_g<KT, D, 4>(a, blocks, s);
-    case 8: return launch_decode_g<KT, D, 8>(a, blocks, s);
-    default: return hipErrorInvalidValue;
+  if constexpr (G > max_group<KT, D>()) {
+    return hipErrorInvalidValue;
+  } else {
+    if (g == G) return launch_decode_g<KT, D, G>(a, blocks, s);
+    return launch_decode_d<KT, D, G + 1>(a, g, blocks, s);
   }
 }
 
-template <int KT, int D>
+template <int KT, int D, int G = 1>
 int64_t round_rows_d(int g) {
-  switch (g) {
-    case 1: return DecodeCfg<KT, D, 1>::ROUND_ROWS;
-    case 2: return DecodeCfg<KT, D, 2>::ROUND_ROWS;
-    case 4: return DecodeCfg<KT, D, 4>::ROUND_ROWS;
-    case 8: return DecodeCfg<KT, D, 8>::ROUND_ROWS;
-    default: return 0;
+  if constexpr (G > max_group<KT, D>()) {
+    return 0;
+  } else {
+    if (g == G) return DecodeCfg<KT, D, G>::ROUND_ROWS;
+    return round_rows_d<KT, D, G + 1>(g);
   }
 }
 

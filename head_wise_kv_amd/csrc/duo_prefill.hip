@@ -554,7 +554,9 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a, int g) 
 void prefill_plan(int dtype, int d, int g, int* rows_per_item, int* heads_per_item) {
   (void)d;
   if (dtype == 1) {
-    const int hpi = g >= kPfRowWaves ? kPfRowWaves : g;  // query heads per work item
+    // query heads per work item: four when 4 divides g, two when 2 does,
+    // otherwise one (its four row wavefronts then take four row blocks)
+    const int hpi = g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1;
     *heads_per_item = hpi;
     *rows_per_item = kPfRowsPerWave * (kPfRowWaves / hpi);
   } else {

@@ -118,8 +118,9 @@ def test_payload_reproduces_printed_examples():
 BAD = [
     (dict(n_q=6, n_kv=4), H.DUO_EINVAL),
     (dict(d_head=96), H.DUO_EUNSUPPORTED),
-    (dict(n_q=12, n_kv=4), H.DUO_EUNSUPPORTED),   # g = 3
-    (dict(n_q=32, n_kv=2), H.DUO_EUNSUPPORTED),   # g = 16
+    (dict(n_q=68, n_kv=4), H.DUO_EUNSUPPORTED),   # g = 17: above the 16 query columns of a matrix-core tile
+    (dict(n_q=36, n_kv=4, dtype_code=0), H.DUO_EUNSUPPORTED),  # g = 9 on the vector ALU (fp32)
+    (dict(n_q=36, n_kv=4, d_head=64), H.DUO_EUNSUPPORTED),     # g = 9 on the vector ALU (d_head 64)
     (dict(sink=-1), H.DUO_EINVAL),
     (dict(recent=0), H.DUO_EINVAL),
     (dict(T_cap=0), H.DUO_EINVAL),
@@ -139,6 +140,21 @@ BAD = [
     (dict(rope_theta=float("nan")), H.DUO_EINVAL),
     (dict(rope_theta=float("inf")), H.DUO_EINVAL),
 ]
+
+
+GOOD_GROUPS = [(g, dt, d) for g in (3, 5, 6, 7, 12, 16) for dt, d in ((H.DUO_BF16, 128),)] + \
+              [(g, dt, d) for g in (3, 5, 6, 7) for dt, d in ((H.DUO_F32, 128), (H.DUO_F32, 64), (H.DUO_BF16, 64))]
+
+
+@pytest.mark.parametrize("g,dtype_code,d_head", GOOD_GROUPS)
+def test_group_sizes_accepted(g, dtype_code, d_head):
+    """Any group size up to 16 where the scores run on the matrix cores (bf16,
+    d_head 128), up to 8 on the vector ALU."""
+    buf = (ctypes.c_uint8 * 4)(1, 0, 1, 0)
+    cfg = H.duo_config(2, 1, 2 * g, 2, d_head, 100, 2, 8, dtype_code,
+                       ctypes.cast(buf, ctypes.POINTER(ctypes.c_uint8)), 0, 0, 0, 0.0)
+    a = ctypes.c_size_t()
+    assert H.lib.duo_cache_bytes(ctypes.byref(cfg), ctypes.byref(a), None) == H.DUO_OK, H.lib.duo_last_error()
 
 
 @pytest.mark.parametrize("over,code", BAD)

@@ -47,8 +47,10 @@ def test_tiny_decode_workload():
 GRID = []
 for dtype in ("bf16", "f32"):
     for d in (64, 128):
-        for g in (1, 2, 4, 8):
+        for g in (1, 2, 3, 4, 5, 6, 7, 8):
             GRID.append((dtype, d, g))
+# groups above 8 run only where the scores use the matrix cores (bf16, d = 128)
+GRID += [("bf16", 128, 12), ("bf16", 128, 16)]
 
 
 @pytest.mark.gpu

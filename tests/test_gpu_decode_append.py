@@ -47,7 +47,7 @@ def test_decode_append_each_step(T0):
     _steps_case(2, 8, 4, 64, "bf16", T0, 24, 4, 16, [1, 0, 1, 0], seed=300 + T0)
 
 
-GRID = [(dt, d, g) for dt in ("bf16", "f32") for d in (64, 128) for g in (1, 2, 4, 8)]
+GRID = [(dt, d, g) for dt in ("bf16", "f32") for d in (64, 128) for g in (1, 2, 3, 4, 6, 8)] + [("bf16", 128, 16)]
 
 
 @pytest.mark.gpu

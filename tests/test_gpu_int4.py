@@ -85,7 +85,7 @@ def _decode_case(B, n_q, n_kv, d, T, S, W, mask, seed):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("g", [1, 2, 4, 8])
+@pytest.mark.parametrize("g", [1, 2, 3, 4, 5, 8, 16])
 @pytest.mark.parametrize("T", [1, 7, 300, 2049])
 def test_int4_decode_grid(g, T):
     """Every group size; contexts from one token to several 512-row rounds with

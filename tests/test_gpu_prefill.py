@@ -41,8 +41,9 @@ CASES = []
 for dtype in ("bf16", "f32"):
     for d in (64, 128):
         # bf16 takes every group size the MFMA path packs differently: one head
-        # per work item (g = 1), two (g = 2), four (g = 4), two head groups (g = 8)
-        for g in ((1, 2, 4, 8) if dtype == "bf16" else (1, 4)):
+        # per work item (g = 1, 3), two (g = 2, 6: three head groups), four
+        # (g = 4), two head groups of four (g = 8)
+        for g in ((1, 2, 3, 4, 6, 8) if dtype == "bf16" else (1, 3, 4)):
             CASES.append((dtype, d, g))
 
 

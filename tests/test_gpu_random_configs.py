@@ -23,7 +23,8 @@ def _draw(seed):
     fp8 = bool(r.random() < 0.3)
     dtype = "bf16" if fp8 else str(r.choice(["bf16", "bf16", "f32"]))
     d = 128 if fp8 else int(r.choice([64, 128]))
-    g = int(r.choice([1, 2, 4, 8]))
+    # any group size; above 8 only where the scores use the matrix cores
+    g = int(r.choice([1, 2, 3, 4, 5, 6, 7, 8] + ([12, 16] if dtype == "bf16" and d == 128 else [])))
     n_kv = int(r.choice([1, 2, 3, 4]))
     mask = [int(x) for x in r.integers(0, 2, n_kv)]
     B = int(r.integers(1, 5))
