@@ -156,11 +156,15 @@ __device__ __forceinline__ void rope_chunks(uint4& x, uint4& y, const Rope& r, i
   y = make_uint4(yw[0], yw[1], yw[2], yw[3]);
 }
 
+// ROPE: keys rotated at their positions (a.rope.on).  The two cases are
+// separate kernels: the rotation's double-precision angle code would
+// otherwise hold the plain copy at a quarter of the occupancy, with spills.
+template <bool ROPE>
 __global__ void append_kernel(AppendArgs a) {
   const int cpr = a.row_bytes / 16;
   // work per row: its 16-byte chunks, or with rotary positions its chunk
   // pairs (c, c + cpr/2), which hold the rotation's dimension pairs
-  const int units = a.rope.on ? cpr / 2 : cpr;
+  const int units = ROPE ? cpr / 2 : cpr;
   const int64_t total = (int64_t)a.B * a.n_kv * a.n_new * units;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total; idx += stride) {
@@ -204,7 +208,7 @@ __global__ void append_kernel(AppendArgs a) {
       vd = a.lp.v_str + off;
       if (c == 0) a.lp.pos[hrow] = (int32_t)p;
     }
-    if (!a.rope.on) {
+    if constexpr (!ROPE) {
       st16(kd + c * 16, ld16(a.k + src + c * 16));
       st16(vd + c * 16, ld16(a.v + src + c * 16));
     } else {
@@ -523,7 +527,8 @@ __device__ __forceinline__ uint4 rope_row16(uint4 x, const Rope& r, int64_t p, i
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-template <bool INT4>
+// ROPE as for append_kernel: the rotation is a kernel of its own.
+template <bool INT4, bool ROPE>
 __global__ void append_lowbit_kernel(AppendArgs a) {
   const int64_t rows = (int64_t)a.B * a.n_kv * a.n_new * 2;
   const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
@@ -553,7 +558,7 @@ __global__ void append_lowbit_kernel(AppendArgs a) {
   const size_t src = (((size_t)b * a.n_kv + kvh) * a.n_new + i) * a.in_row_bytes + (size_t)j * 16;
   float sc;
   uint4 x = ld16((tensor ? a.v : a.k) + src);
-  if (a.rope.on && tensor == 0) x = rope_row16(x, a.rope, p, j);  // the whole group takes this branch
+  if (ROPE && tensor == 0) x = rope_row16(x, a.rope, p, j);  // the whole group takes this branch
   uint2 codes = make_uint2(0u, 0u);
   uint32_t codes4 = 0u;
   if constexpr (INT4) codes4 = quant_row16_int4(x, sc);
@@ -2240,15 +2245,21 @@ hipError_t launch_append(const AppendArgs& a, int dtype, int d, int kvfmt, hipSt
     const int64_t threads = (int64_t)a.B * a.n_kv * a.n_new * 2 * 16;
     const int64_t grid = (threads + 255) / 256;
     if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
-    if (kvfmt == 2) append_lowbit_kernel<true><<<(unsigned)grid, 256, 0, s>>>(a);
-    else append_lowbit_kernel<false><<<(unsigned)grid, 256, 0, s>>>(a);
+    if (kvfmt == 2) {
+      if (a.rope.on) append_lowbit_kernel<true, true><<<(unsigned)grid, 256, 0, s>>>(a);
+      else append_lowbit_kernel<true, false><<<(unsigned)grid, 256, 0, s>>>(a);
+    } else {
+      if (a.rope.on) append_lowbit_kernel<false, true><<<(unsigned)grid, 256, 0, s>>>(a);
+      else append_lowbit_kernel<false, false><<<(unsigned)grid, 256, 0, s>>>(a);
+    }
     return hipGetLastError();
   }
   const int64_t total = (int64_t)a.B * a.n_kv * a.n_new * (a.row_bytes / 16);
   const int threads = 256;
   const int64_t want = (total + threads - 1) / threads;
   const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, 65536));
-  append_kernel<<<grid, threads, 0, s>>>(a);
+  if (a.rope.on) append_kernel<true><<<grid, threads, 0, s>>>(a);
+  else append_kernel<false><<<grid, threads, 0, s>>>(a);
   return hipGetLastError();
 }
 
