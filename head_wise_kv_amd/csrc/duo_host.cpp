@@ -87,12 +87,15 @@ int validate(const duo_config* c) {
   if (c->T_cap < 1) return fail(DUO_EINVAL, "T_cap must be >= 1");
   if (c->T_cap > INT32_MAX) return fail(DUO_EINVAL, "T_cap must fit int32 (positions are int32)");
   if (c->page_rows != 0) {
-    if (c->page_rows < 256 || c->page_rows > (1 << 20) || (c->page_rows & (c->page_rows - 1)) != 0)
-      return fail(DUO_EINVAL, "page_rows %d must be 0 or a power of two in [256, 2^20]", c->page_rows);
+    if (c->page_rows < 64 || c->page_rows > (1 << 20) || (c->page_rows & (c->page_rows - 1)) != 0)
+      return fail(DUO_EINVAL, "page_rows %d must be 0 or a power of two in [64, 2^20]", c->page_rows);
     if (c->n_pages < 1) return fail(DUO_EINVAL, "a paged cache needs n_pages >= 1 (got %d)", c->n_pages);
-    // a decode round of rows (INT4: 512) must lie within one page
-    if (c->kv_format == DUO_KV_INT4 && c->page_rows < 512)
-      return fail(DUO_EUNSUPPORTED, "INT4 rows need pages of at least 512 rows (got %d)", c->page_rows);
+    // a decode round of rows (32 KB of stored K rows: 128 bf16 rows of d_head
+    // 128, 256 FP8 rows, 512 INT4 rows) must lie within one page
+    const int64_t round = duo::decode_round_rows(c->dtype, c->d_head, c->n_q / c->n_kv, c->kv_format);
+    if (c->page_rows < round)
+      return fail(DUO_EUNSUPPORTED, "pages of this row format hold at least %lld rows, one decode round (got %d)",
+                  (long long)round, c->page_rows);
   } else if ((uint64_t)c->T_cap * (uint64_t)c->d_head * (c->dtype == DUO_BF16 ? 2u : 4u) > 0xffffffffull) {
     return fail(DUO_EUNSUPPORTED, "one head's rows (T_cap * d_head * element size) must fit 4 GiB");
   }

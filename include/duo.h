@@ -96,8 +96,11 @@ typedef enum { DUO_KV_NATIVE = 0, DUO_KV_FP8 = 1, DUO_KV_INT4 = 2 } duo_kv_forma
  * 0 = streaming head); it is copied.
  *
  * Retrieval rows are stored one of two ways.  page_rows = 0: contiguous, T_cap
- * rows per retrieval head and batch row.  page_rows > 0 (a power of two, at
- * least 256, at least 512 for DUO_KV_INT4): paged ("Attention Variants and Memory Efficiency", "What the
+ * rows per retrieval head and batch row.  page_rows > 0 (a power of two of at
+ * least 64 rows and at least one decode round, 32 KB of stored K rows: 128
+ * rows for bf16 at d_head 128, 256 for bf16 at d_head 64 and for DUO_KV_FP8,
+ * 512 for DUO_KV_INT4, 64 for fp32 at d_head 128, 128 for fp32 at d_head 64;
+ * smaller is DUO_EUNSUPPORTED): paged ("Attention Variants and Memory Efficiency", "What the
  * Inference Runtime Can Change": the runtime may cut a request's rows into
  * equal blocks placed anywhere and shared between requests; "A Closer Look at
  * Attention Memory": a ragged batch then holds only what each request needs).
@@ -129,7 +132,7 @@ typedef struct {
   int32_t dtype; /* duo_dtype: Q, K, V and outputs; accumulation is fp32 */
   const uint8_t* retrieval_mask;
   int32_t kv_format; /* duo_kv_format of the stored K/V rows (0 = native) */
-  int32_t page_rows; /* 0: contiguous retrieval rows; else rows per page (power of two >= 256) */
+  int32_t page_rows; /* 0: contiguous retrieval rows; else rows per page (power of two, >= one decode round) */
   int32_t n_pages;   /* paged: pages per layer (>= 1); ignored when page_rows = 0 */
   float rope_theta;  /* 0: no rotary embedding; else its base (> 1, e.g. 10000) */
 } duo_config;

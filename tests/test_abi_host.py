@@ -131,7 +131,10 @@ BAD = [
     (dict(B=65), H.DUO_EUNSUPPORTED),                          # at most 64 batch rows
     (dict(kv_format=1, dtype_code=0), H.DUO_EUNSUPPORTED),   # FP8 rows need bf16
     (dict(kv_format=1, d_head=64), H.DUO_EUNSUPPORTED),      # FP8 rows are built for d_head 128
-    (dict(page_rows=128, n_pages=4), H.DUO_EINVAL),          # pages of at least 256 rows
+    (dict(page_rows=32, n_pages=4), H.DUO_EINVAL),           # pages of at least 64 rows
+    (dict(page_rows=64, n_pages=4), H.DUO_EUNSUPPORTED),     # below a decode round (128 bf16 rows of d 128)
+    (dict(page_rows=128, n_pages=4, kv_format=1), H.DUO_EUNSUPPORTED),  # FP8: a round is 256 rows
+    (dict(page_rows=256, n_pages=4, kv_format=2), H.DUO_EUNSUPPORTED),  # INT4: a round is 512 rows
     (dict(page_rows=384, n_pages=4), H.DUO_EINVAL),          # a power of two
     (dict(page_rows=256, n_pages=0), H.DUO_EINVAL),          # an empty pool
     (dict(page_rows=-256, n_pages=4), H.DUO_EINVAL),

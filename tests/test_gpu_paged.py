@@ -78,28 +78,31 @@ def _check_rows(c, K, V, lens, mask, S, W, dtype, fp8):
                     assert int(pos[b, slot]) == p, (h, b, slot)
 
 
-CASES = [("bf16", 128, 4, None), ("bf16", 128, 8, None), ("bf16", 64, 2, None), ("f32", 128, 1, None),
-         ("f32", 64, 8, None), ("bf16", 128, 8, "fp8"), ("bf16", 128, 1, "fp8")]
+# (dtype, d, g, K/V row format, page rows): 256-row pages, and the smallest
+# page each row format allows (one decode round)
+CASES = [("bf16", 128, 4, None, P), ("bf16", 128, 8, None, P), ("bf16", 64, 2, None, P), ("f32", 128, 1, None, P),
+         ("f32", 64, 8, None, P), ("bf16", 128, 8, "fp8", P), ("bf16", 128, 1, "fp8", P),
+         ("bf16", 128, 8, None, 128), ("bf16", 128, 3, None, 128), ("f32", 128, 2, None, 64), ("f32", 64, 4, None, 128)]
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("dtype,d,g,kvf", CASES)
-def test_paged_ragged_decode(dtype, d, g, kvf):
+@pytest.mark.parametrize("dtype,d,g,kvf,pr", CASES)
+def test_paged_ragged_decode(dtype, d, g, kvf, pr):
     """Rows of 1, 255, 256, 600 and 2,049 tokens appended in pieces that cross
     page edges, decoded together: every row against the oracle, the pages
     against the model, the rows bit-exact."""
     need_gpu()
     from head_wise_kv_amd import DuoCache
-    say("paged decode", dtype, d, g, kvf)
+    say("paged decode", dtype, d, g, kvf, pr)
     lens = [1, 255, 256, 600, 2049]
     B, n_kv, S, W = len(lens), 4, 4, 64
     mask = [1, 0, 1, 1]
     n_q = n_kv * g
     N = max(lens)
-    n_pages = 20
+    n_pages = 20 * (P // pr)
     K, V, Q = _seq(B, n_kv, N, d, 1200 + d + g, n_q)
-    c = DuoCache(1, B, n_q, n_kv, d, N, S, W, dtype, [mask], kv_format=kvf, page_rows=P, n_pages=n_pages)
-    model = OP.PagedRows(P, n_pages, B)
+    c = DuoCache(1, B, n_q, n_kv, d, N, S, W, dtype, [mask], kv_format=kvf, page_rows=pr, n_pages=n_pages)
+    model = OP.PagedRows(pr, n_pages, B)
     Kd, Vd, Qd = (WL.to_torch(x, dtype).cuda() for x in (K, V, Q))
     for b, n in enumerate(lens):
         p = 0
@@ -159,24 +162,26 @@ def test_paged_decode_append_steps(kvf):
     _check_rows(c, K, V, [n + steps for n in start], mask, S, W, "bf16", kvf == "fp8")
 
 
-PREFILL = [("bf16", 128, 4, None), ("bf16", 64, 8, None), ("f32", 64, 2, None), ("bf16", 128, 8, "fp8")]
+PREFILL = [("bf16", 128, 4, None, P), ("bf16", 64, 8, None, P), ("f32", 64, 2, None, P), ("bf16", 128, 8, "fp8", P),
+           ("bf16", 128, 4, None, 128), ("bf16", 128, 6, None, 128), ("f32", 128, 1, None, 64)]
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("dtype,d,g,kvf", PREFILL)
-def test_paged_prefill_chunked(dtype, d, g, kvf):
+@pytest.mark.parametrize("dtype,d,g,kvf,pr", PREFILL)
+def test_paged_prefill_chunked(dtype, d, g, kvf, pr):
     """Chunked prefill of two rows (chunks of 300, 1, 256 and 200 tokens:
     held rows on several pages, chunk edges inside pages), then one decode."""
     need_gpu()
     from head_wise_kv_amd import DuoCache
     chunks = [300, 1, 256, 200]
     N = sum(chunks)
-    say("paged prefill", dtype, d, g, kvf)
+    say("paged prefill", dtype, d, g, kvf, pr)
     B, n_kv, S, W = 2, 2, 5, 40
     mask = [1, 0]
     n_q = n_kv * g
+    npg = 6 * (P // pr)
     K, V, Q = _seq(B, n_kv, N + 1, d, 1400 + d + g, n_q)
-    c = DuoCache(1, B, n_q, n_kv, d, N + 1, S, W, dtype, [mask], kv_format=kvf, page_rows=P, n_pages=6)
+    c = DuoCache(1, B, n_q, n_kv, d, N + 1, S, W, dtype, [mask], kv_format=kvf, page_rows=pr, n_pages=npg)
     Kd, Vd, Qd = (WL.to_torch(x, dtype).cuda() for x in (K, V, Q))
     outs, p = [], 0
     for C in chunks:
@@ -193,7 +198,7 @@ def test_paged_prefill_chunked(dtype, d, g, kvf):
         else:
             ref = OA.prefill_full(Qs[b, :, :N], Ks[b, :, :N], Vs[b, :, :N], mask, S, W, d ** -0.5)
         check_close(out[b], ref, dtype, f"paged prefill row {b}")
-    model = OP.PagedRows(P, 6, B)
+    model = OP.PagedRows(pr, npg, B)
     model.append_rows([(b, N) for b in range(B)])
     _check_pages(c, model)
     _check_rows(c, K[:, :, :N], V[:, :, :N], [N, N], mask, S, W, dtype, kvf == "fp8")
@@ -287,10 +292,13 @@ def test_paged_errors():
     say("paged errors")
     B, n_q, n_kv, d, S, W = 2, 4, 2, 128, 4, 16
     mask = [1, 0]
-    for pr, npg in ((100, 4), (384, 4), (128, 4), (256, 0)):
+    for pr, npg in ((100, 4), (384, 4), (32, 4), (256, 0)):
         with pytest.raises(H.DuoError) as e:
             DuoCache(1, B, n_q, n_kv, d, 4096, S, W, "bf16", [mask], page_rows=pr, n_pages=npg)
         assert e.value.code == H.DUO_EINVAL, (pr, npg)
+    with pytest.raises(H.DuoError) as e:  # below one decode round (128 bf16 rows of d 128)
+        DuoCache(1, B, n_q, n_kv, d, 4096, S, W, "bf16", [mask], page_rows=64, n_pages=4)
+    assert e.value.code == H.DUO_EUNSUPPORTED
     c = DuoCache(1, B, n_q, n_kv, d, 4096, S, W, "bf16", [mask], page_rows=P, n_pages=3)
     x = torch.randn(1, n_kv, 600, d, device="cuda").to(torch.bfloat16)
     c.append_row(0, 0, x, x)

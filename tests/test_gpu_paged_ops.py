@@ -29,24 +29,25 @@ def _pages_ok(c, model, B):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("seed,theta", [(0, 0.0), (1, 0.0), (2, 10000.0), (3, 0.0), (4, 500000.0)])
-def test_paged_random_ops(seed, theta):
+@pytest.mark.parametrize("seed,theta,pr", [(0, 0.0, P), (1, 0.0, P), (2, 10000.0, P), (3, 0.0, P), (4, 500000.0, P),
+                                           (5, 0.0, 128), (6, 10000.0, 128)])
+def test_paged_random_ops(seed, theta, pr):
     need_gpu()
     from head_wise_kv_amd import DuoCache
-    say("paged random ops", seed, theta)
+    say("paged random ops", seed, theta, pr)
     rng = np.random.default_rng(100 + seed)
     B, n_kv, g, d, S, W = 4, 2, 4, 128, 4, 64
     n_q = n_kv * g
     mask = [1, 0]
     T_cap = 1400
-    n_pages = 12  # tight: appends can be refused, and that must change nothing
+    n_pages = 12 * (P // pr)  # tight: appends can be refused, and that must change nothing
     pool = 6000   # seeded K/V/Q rows that appends draw from
     Kp = WL.normal_f32((n_kv, pool, d), 4000 + seed)
     Vp = WL.normal_f32((n_kv, pool, d), 4001 + seed)
     Qp = WL.normal_f32((n_q, pool, d), 4002 + seed)
     Kd, Vd, Qd = (WL.to_torch(x, "bf16").cuda() for x in (Kp, Vp, Qp))
-    c = DuoCache(1, B, n_q, n_kv, d, T_cap, S, W, "bf16", [mask], page_rows=P, n_pages=n_pages, rope_theta=theta)
-    model = OP.PagedRows(P, n_pages, B)
+    c = DuoCache(1, B, n_q, n_kv, d, T_cap, S, W, "bf16", [mask], page_rows=pr, n_pages=n_pages, rope_theta=theta)
+    model = OP.PagedRows(pr, n_pages, B)
     seqs = [[] for _ in range(B)]  # token ids per row
     next_id = 0
     n_checked = 0

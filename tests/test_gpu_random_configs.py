@@ -87,7 +87,9 @@ def test_random_config(seed):
     Q = WL.normal_f32((B, n_q, N, d), 3 * seed + 3)
     kw = dict(kv_format=cfg["kvf"], rope_theta=cfg["theta"])
     if cfg["paged"]:
-        pr = 512 if cfg["kvf"] == "int4" else 256  # a decode round (INT4: 512 rows) fits a page
+        # the smallest page the row format allows: one decode round, 32 KB of stored K rows
+        row_bytes = {"int4": d // 2, "fp8": d}.get(cfg["kvf"], d * (4 if dt == "f32" else 2))
+        pr = max(64, 32768 // row_bytes)
         kw.update(page_rows=pr, n_pages=sum(-(-(n + steps) // pr) for n in cfg["lens"]))
     c = DuoCache(1, B, n_q, n_kv, d, N, cfg["S"], cfg["W"], dt, [cfg["mask"]], **kw)
     Kd, Vd, Qd = (WL.to_torch(x, dt).cuda() for x in (K, V, Q))
