@@ -149,3 +149,39 @@ def test_llama3_8b_prefill_64k():
                 kind = "retrieval" if mask[kvh] else "streaming"
                 check_close(out[0][h:h + 1], ref_h, w.dtype, f"{w.name} chunk {ci} all rows, {kind} head {h}")
     assert c.seq_len(0) == N
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("d,chunks,page_rows", [(128, [36000, 34000], 0), (128, [36000, 34000], 256),
+                                                (64, [20000, 20000], 0)])
+def test_prefill_past_tile_table(d, chunks, page_rows):
+    """Work items with more key tiles than the workgroup's descriptor table
+    holds (1,024 tiles of 64 keys at d = 128, 512 at d = 64): the entries of
+    passed tiles are refilled during the item; rows of the second chunk whose
+    keys reach past the table (cache and chunk tiles both), checked against
+    the oracle, contiguous and paged."""
+    need_gpu()
+    from head_wise_kv_amd import DuoCache
+    N = sum(chunks)
+    B, n_q, n_kv, S, W = 1, 4, 2, 16, 256
+    mask = [1, 0]
+    say("prefill past tile table", d, chunks, page_rows)
+    Q = WL.normal_f32((B, n_q, N, d), 2100 + d)
+    K = WL.normal_f32((B, n_kv, N, d), 2101 + d)
+    V = WL.normal_f32((B, n_kv, N, d), 2102 + d)
+    Qd, Kd, Vd = (WL.to_torch(x, "bf16").cuda() for x in (Q, K, V))
+    kw = dict(page_rows=page_rows, n_pages=-(-N // page_rows)) if page_rows else {}
+    c = DuoCache(1, B, n_q, n_kv, d, N, S, W, "bf16", [mask], **kw)
+    p = 0
+    for C in chunks:
+        out = c.prefill_chunk(0, Qd[:, :, p:p + C].contiguous(), Kd[:, :, p:p + C].contiguous(),
+                              Vd[:, :, p:p + C].contiguous())
+        p += C
+    torch.cuda.synchronize()
+    C, P0 = chunks[-1], N - chunks[-1]
+    rng = np.random.default_rng(d)
+    rows = np.unique(np.concatenate([np.arange(C - 64, C), [0, 1, 63, 64], rng.integers(0, C, 12)]))
+    got = out[0][:, rows].float().cpu().double().numpy()
+    ref = OA.prefill_full(stored(Q[0], "bf16"), stored(K[0], "bf16"), stored(V[0], "bf16"), mask, S, W,
+                          d ** -0.5, rows=P0 + rows)
+    check_close(torch.from_numpy(got), ref, "bf16", f"prefill past tile table d{d} pages {page_rows}")
