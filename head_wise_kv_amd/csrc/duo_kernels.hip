@@ -1844,20 +1844,24 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
 
   if constexpr (MF) {
     // ---- merge the eight wavefronts' states through LDS (the ring is free):
-    // query column j's accumulators X[wave][j][d] in ring0 (with shared
-    // items: columns 0-7 in ring0, 8-15 in ring1), the (max, sum) pairs in
-    // ring1 (ring2 with shared items)
+    // query column j's accumulators X[wave][j][d], WPR wavefront blocks to a
+    // ring unit (units 0-2), the (max, sum) pairs in ring unit 3.  A column
+    // takes D + 16 floats: the 64-byte pad puts the columns a lane group
+    // stores at once (16 t + 4 g of columns j) on different banks; at D
+    // floats apart they all met on the same banks, eight-way.
     lds_barrier();  // every wavefront is done with the ring
-    // (more than 8 query columns, in shared items or groups of g > 8: columns
-    // 0-7 in ring0, 8-15 in ring1, the (max, sum) pairs in ring2)
-    constexpr bool WIDE = SHARE || G > 8;
-    constexpr int XS = WIDE ? 8 : G;     // columns per wavefront block of X
-    constexpr int MS = SHARE ? 16 : G;   // columns per wavefront block of the (max, sum) pairs
-    static_assert(kDecWaves * XS * D * 4 <= kUnitBytes, "a ring unit holds X for 8 columns");
-    float* const xlo = reinterpret_cast<float*>(ring0);
-    float* const xhi = reinterpret_cast<float*>(ring1);
-    float* const xml = reinterpret_cast<float*>(WIDE ? ring2 : ring1);
-    auto xcol = [&](int v, int col) { return (col < XS ? xlo : xhi) + ((size_t)v * XS + (col % XS)) * D; };
+    constexpr int NCOL = (SHARE || G > 8) ? 16 : G;  // columns per wavefront block of X
+    constexpr int MS = SHARE ? 16 : G;               // columns per wavefront block of the (max, sum) pairs
+    constexpr int CS = D + 16;                       // floats per column of X
+    constexpr int XB = NCOL * CS * 4;                // bytes per wavefront block
+    constexpr int WPR = kUnitBytes / XB;             // wavefront blocks per ring unit
+    static_assert(WPR >= 1 && (kDecWaves + WPR - 1) / WPR <= 3, "X fits ring units 0-2");
+    float* const xml = reinterpret_cast<float*>(ring3);
+    // element e of column col of wavefront v (v wavefront-uniform, so the
+    // ring unit is a scalar choice; a compile-time one in the merge loop)
+    auto xat = [&](int v, int col, int e) -> float* {
+      return reinterpret_cast<float*>(ring_at(v / WPR) + (v % WPR) * XB + (col * CS + e) * 4);
+    };
     const int j = lane & 15, g = lane >> 4;
     const int ncol = SHARE ? w.qrows * G : G;  // query columns in use
     const float lsum = swap32_sum(swap16_sum(mst.l));  // the query's sum over its four lanes
@@ -1869,7 +1873,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     if (j < ncol) {
 #pragma unroll
       for (int t = 0; t < 8; ++t)
-        *reinterpret_cast<float4*>(xcol(wave, j) + 16 * t + 4 * g) =
+        *reinterpret_cast<float4*>(xat(wave, j, 16 * t + 4 * g)) =
             make_float4(mst.o[t][0], mst.o[t][1], mst.o[t][2], mst.o[t][3]);
       if (g == 0) {
         xml[wave * MS + j] = mst.m;
@@ -1878,24 +1882,31 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     }
     lds_barrier();
     // four consecutive output elements per thread: query column h = e4 / D
-    // (a shared item: row h / G of its group, query head h % G)
+    // (a shared item: row h / G of its group, query head h % G); every LDS
+    // read of the thread is issued before the arithmetic that needs it
     for (int e4 = threadIdx.x * 4; e4 < ncol * D; e4 += kDecodeThreads * 4) {
       const int h = e4 / D, d = e4 % D;
+      float mv[kDecWaves], lv[kDecWaves];
+      float4 xv[kDecWaves];
+#pragma unroll
+      for (int v = 0; v < kDecWaves; ++v) {
+        mv[v] = xml[v * MS + h];
+        lv[v] = xml[kDecWaves * MS + v * MS + h];
+        xv[v] = *reinterpret_cast<const float4*>(xat(v, h, d));
+      }
       float M = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < kDecWaves; ++v) M = fmaxf(M, xml[v * MS + h]);
+      for (int v = 0; v < kDecWaves; ++v) M = fmaxf(M, mv[v]);
       float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
       float L = 0.f;
 #pragma unroll
       for (int v = 0; v < kDecWaves; ++v) {
-        const float mv = xml[v * MS + h];
-        const float wt = (mv == -INFINITY) ? 0.f : fast_exp2(mv - M);
-        L = fmaf(xml[kDecWaves * MS + v * MS + h], wt, L);
-        const float4 x = *reinterpret_cast<const float4*>(xcol(v, h) + d);
-        A.x = fmaf(x.x, wt, A.x);
-        A.y = fmaf(x.y, wt, A.y);
-        A.z = fmaf(x.z, wt, A.z);
-        A.w = fmaf(x.w, wt, A.w);
+        const float wt = (mv[v] == -INFINITY) ? 0.f : fast_exp2(mv[v] - M);
+        L = fmaf(lv[v], wt, L);
+        A.x = fmaf(xv[v].x, wt, A.x);
+        A.y = fmaf(xv[v].y, wt, A.y);
+        A.z = fmaf(xv[v].z, wt, A.z);
+        A.w = fmaf(xv[v].w, wt, A.w);
       }
       if (w.single) {
         const float inv = 1.f / L;
