@@ -2037,12 +2037,18 @@ __global__ __launch_bounds__(kDecodeThreads) void combine_kernel(DecodeArgs a) {
   constexpr int DC = D / kCombineElems;
   __shared__ float c_m[kCombineGroups][kCombineElems], c_l[kCombineGroups][kCombineElems],
       c_a[kCombineGroups][kCombineElems];
-  if (a.new_k != nullptr && blockIdx.x == 0 && threadIdx.x < a.B) {
-    // a fused append's step is done: every row advances by its new token if
-    // it had room (the decode kernel, which read the counts, has finished)
-    const int b = threadIdx.x;
-    const int32_t cnt = a.lp.len[b];
-    if (room_for(a.lp, b, cnt, 1)) a.lp.len[b] = cnt + 1;
+  const int64_t n_heads = (int64_t)a.B * (a.n_ret + a.n_str);
+  if ((int64_t)blockIdx.x >= n_heads * G * DC) {
+    // the launch's extra last workgroup (fused appends only): the step is
+    // done, so every row advances by its new token if it had room (the
+    // decode kernel, which read the counts, has finished).  A workgroup of
+    // its own, so that its two dependent loads do not delay a merge.
+    if (threadIdx.x < a.B) {
+      const int b = threadIdx.x;
+      const int32_t cnt = a.lp.len[b];
+      if (room_for(a.lp, b, cnt, 1)) a.lp.len[b] = cnt + 1;
+    }
+    return;
   }
   const int64_t hh = blockIdx.x / (G * DC);
   const int h = (int)((blockIdx.x / DC) % G);
@@ -2108,15 +2114,23 @@ __global__ __launch_bounds__(kDecodeThreads) void combine_kernel(DecodeArgs a) {
   c_a[grp][el] = A;
   __syncthreads();
   if (grp != 0) return;
+  // every group's (max, sum, accumulator) read before the arithmetic
+  float gm[kCombineGroups], gl[kCombineGroups], ga[kCombineGroups];
+#pragma unroll
+  for (int k = 0; k < kCombineGroups; ++k) {
+    gm[k] = c_m[k][el];
+    gl[k] = c_l[k][el];
+    ga[k] = c_a[k][el];
+  }
   float Mt = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < kCombineGroups; ++k) Mt = fmaxf(Mt, c_m[k][el]);
+  for (int k = 0; k < kCombineGroups; ++k) Mt = fmaxf(Mt, gm[k]);
   float Lt = 0.f, At = 0.f;
 #pragma unroll
   for (int k = 0; k < kCombineGroups; ++k) {
-    const float w = (c_m[k][el] == -INFINITY) ? 0.f : fast_exp2(c_m[k][el] - Mt);
-    Lt += c_l[k][el] * w;
-    At += c_a[k][el] * w;
+    const float w = (gm[k] == -INFINITY) ? 0.f : fast_exp2(gm[k] - Mt);
+    Lt += gl[k] * w;
+    At += ga[k] * w;
   }
   const size_t o = ((size_t)b * a.n_q + (size_t)kvh * G) * D + e;
   if (BF16) reinterpret_cast<uint16_t*>(a.out)[o] = (uint16_t)f32_to_bf16_bits(At / Lt);
@@ -2137,7 +2151,8 @@ hipError_t launch_decode_sh(const DecodeArgs& a, int blocks, hipStream_t s) {
     return launch_advance(v, s);
   }
   const int64_t heads = (int64_t)a.B * (a.n_ret + a.n_str);
-  combine_kernel<KT, D, G, SH><<<(unsigned)(heads * G * (D / kCombineElems)), kDecodeThreads, 0, s>>>(a);
+  const int64_t extra = a.new_k != nullptr ? 1 : 0;  // the workgroup that advances a fused append's counts
+  combine_kernel<KT, D, G, SH><<<(unsigned)(heads * G * (D / kCombineElems) + extra), kDecodeThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
