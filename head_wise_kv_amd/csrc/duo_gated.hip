@@ -191,12 +191,18 @@ __global__ __launch_bounds__(kPfThreads) void gated_mfma_kernel(GatedArgs a, int
   const char* kn = static_cast<const char*>(a.k) + head_off;
   const char* vn = static_cast<const char*>(a.v) + head_off;
 
+  // Tile numbers and rows in 32-bit wavefront-uniform values (N + W fits
+  // int32, checked on the host), so the per-step arithmetic is a few scalar
+  // instructions.
   const GatedTiles tt = gated_tiles(i0, i1, a.S, a.W);
-  const int64_t n_w0 = tt.w_hi0 - tt.w_lo0;
-  const int64_t n_w = n_w0 + (tt.w_hi1 - tt.w_lo1);
-  const int64_t n_r = tt.r_hi - tt.r_lo;
-  const int64_t steps_w = (n_w + 1) / 2;  // the halves take tiles 2s and 2s+1 of a phase at step s
-  const int64_t n_steps = steps_w + (n_r + 1) / 2;
+  const int32_t n_w0 = uniform32(tt.w_hi0 - tt.w_lo0);
+  const int32_t n_w = n_w0 + uniform32(tt.w_hi1 - tt.w_lo1);
+  const int32_t n_r = uniform32(tt.r_hi - tt.r_lo);
+  const int32_t steps_w = (n_w + 1) / 2;  // the halves take tiles 2s and 2s+1 of a phase at step s
+  const int32_t n_steps = steps_w + (n_r + 1) / 2;
+  const int32_t w_lo0 = uniform32(tt.w_lo0), w_lo1 = uniform32(tt.w_lo1), r_lo = uniform32(tt.r_lo);
+  const int32_t n_rows = uniform32(a.N), r0 = uniform32(i0), r1 = uniform32(i1);
+  const int32_t S = a.S, W = a.W;
 
   // per-lane byte offsets of this wavefront's first K / V piece within a tile
   const uint32_t koff = dma_offset<D, false>(sub, lane);
@@ -214,32 +220,33 @@ __global__ __launch_bounds__(kPfThreads) void gated_mfma_kernel(GatedArgs a, int
 
   // Step -> this half's key tile (or -1 when the half has none at that step)
   // and its phase.
-  auto tile_at = [&](int64_t step, bool& rest) -> int64_t {
+  auto tile_at = [&](int32_t step, bool& rest) -> int32_t {
     if (step < steps_w) {
       rest = false;
-      const int64_t i = 2 * step + kh;
+      const int32_t i = 2 * step + kh;
       if (i >= n_w) return -1;
-      return i < n_w0 ? tt.w_lo0 + i : tt.w_lo1 + (i - n_w0);
+      return i < n_w0 ? w_lo0 + i : w_lo1 + (i - n_w0);
     }
     rest = true;
-    const int64_t i = 2 * (step - steps_w) + kh;
-    return i < n_r ? tt.r_lo + i : -1;
+    const int32_t i = 2 * (step - steps_w) + kh;
+    return i < n_r ? r_lo + i : -1;
   };
   // Whether every row of the item sees every key of a tile in its phase,
   // decided from scalars: then the tile needs no mask and no per-key
   // bookkeeping.  Phase 2 keys j >= S are seen by the rows from j + W on;
   // phase 1 keys by the rows j .. j + W - 1 (every row from j on for a sink).
-  auto tile_full = [&](int64_t tile, bool rest) -> bool {
-    const int64_t base = tile * kBN;
-    if (base + kBN > a.N) return false;
-    if (rest) return base >= a.S && base + kBN - 1 + a.W <= i0;
-    return base + kBN - 1 <= i0 && (base + kBN - 1 < a.S || base + a.W >= i1);
+  auto tile_full = [&](int32_t tile, bool rest) -> bool {
+    const int32_t base = tile * kBN;  // < N: a tile starts at a row that exists
+    if (base > n_rows - kBN) return false;
+    const int32_t last = base + kBN - 1;
+    if (rest) return base >= S && last <= r0 - W;
+    return last <= r0 && (last < S || base >= r1 - W);
   };
   // Prepare a tile (-1: none) for buffer `buf` of this half: for a tile that
   // does not pass tile_full, the keys' visible-row intervals and the no-mask
   // flag by the half's first wavefront; and the direct loads of its K/V
   // pieces (split over the half's wavefronts), which the caller issues.
-  auto prepare = [&](int64_t tile, bool rest, int buf) -> TileLoads<D> {
+  auto prepare = [&](int32_t tile, bool rest, int buf) -> TileLoads<D> {
     TileLoads<D> ld;
     ld.kdst = lds_addr(k_lds[kh][buf] + sub * 1024);
     ld.vdst = lds_addr(v_lds[kh][buf] + sub * 1024);
@@ -249,8 +256,8 @@ __global__ __launch_bounds__(kPfThreads) void gated_mfma_kernel(GatedArgs a, int
       ld.rk = ld.rv = dma_rsrc(kn, 0);
       return ld;
     }
-    const int64_t base = tile * kBN;
-    const int nbytes = __builtin_amdgcn_readfirstlane((int)min64(a.N - base, kBN) * (int)rowb);
+    const int32_t base = tile * kBN;
+    const int nbytes = min(n_rows - base, kBN) * (int)rowb;
     if (sub == 0 && !tile_full(tile, rest)) {
       const int64_t j = base + lane;
       const KeySpan ks = rest ? span_rest(j, a.N, a.S, a.W) : span_window(j, a.N, a.S, a.W);
@@ -282,10 +289,10 @@ __global__ __launch_bounds__(kPfThreads) void gated_mfma_kernel(GatedArgs a, int
 
   {
     bool rest;
-    const int64_t t0 = tile_at(0, rest);
+    const int32_t t0 = tile_at(0, rest);
     prepare(t0, rest, 0).all();
   }
-  for (int64_t step = 0; step < n_steps; ++step) {
+  for (int32_t step = 0; step < n_steps; ++step) {
     if (step == steps_w) {  // phase 1 done (wavefront-uniform)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -306,10 +313,10 @@ __global__ __launch_bounds__(kPfThreads) void gated_mfma_kernel(GatedArgs a, int
     // over it as the prefill does, they would push this kernel, which also
     // holds the saved phase-1 state, past 256 registers)
     bool rest_n = false;
-    const int64_t tn = step + 1 < n_steps ? tile_at(step + 1, rest_n) : -1;
+    const int32_t tn = step + 1 < n_steps ? tile_at(step + 1, rest_n) : -1;
     prepare(tn, rest_n, buf ^ 1).all();
     bool rest;
-    const int64_t tc = tile_at(step, rest);
+    const int32_t tc = tile_at(step, rest);
     if (tc < 0) continue;  // wavefront-uniform: no tile for this half at this step
     const bool masked = !tile_full(tc, rest) && s_full[kh][buf] == 0;
     pf_tile<D>(o, m_run, l_run, qb, k_lds[kh][buf], v_lds[kh][buf], masked, klo_lds[kh][buf],

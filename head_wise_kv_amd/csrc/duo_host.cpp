@@ -1235,8 +1235,9 @@ int duo_gated_attention(const duo_gated_shape* shape, const void* q, const void*
   if (sh.dtype != DUO_F32 && sh.dtype != DUO_BF16) return fail(DUO_EUNSUPPORTED, "dtype %d", sh.dtype);
   if (sh.N < 1) return fail(DUO_EINVAL, "N must be >= 1 (got %lld)", (long long)sh.N);
   if (sh.sink < 0 || sh.recent < 1) return fail(DUO_EINVAL, "need sink >= 0 and recent >= 1");
-  if (sh.N + (int64_t)sh.recent > INT32_MAX)
-    return fail(DUO_EINVAL, "N + recent must fit int32 (positions are int32)");
+  // positions and key-tile ends (N plus a 64-key tile) stay within int32
+  if (sh.N + std::max<int64_t>(sh.recent, 64) > INT32_MAX)
+    return fail(DUO_EINVAL, "N + max(recent, 64) must fit int32 (positions are int32)");
   if (!q || !k || !v || !alpha || !out) return fail(DUO_EINVAL, "q, k, v, alpha or out is NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(DUO_EINVAL, "q, k, v and out must be 16-byte aligned");
