@@ -290,7 +290,7 @@ int duo_cache_head_view(const duo_cache* c, int layer, int kv_head, int* is_retr
 
 /* Shape of a head-gated forward: one whole sequence of N tokens at positions
  * 0 .. N-1, no cache.  d_head in {64, 128}; n_q a multiple of n_kv (any group
- * size); S = sink >= 0; W = recent >= 1; N >= 1 and N + W < 2^31. */
+ * size); S = sink >= 0; W = recent >= 1; N >= 1 and N + max(W, 64) < 2^31. */
 typedef struct {
   int32_t B, n_q, n_kv, d_head;
   int64_t N;
