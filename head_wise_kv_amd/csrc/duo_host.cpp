@@ -85,7 +85,9 @@ int validate(const duo_config* c) {
   if (c->kv_format != DUO_KV_NATIVE && (c->dtype != DUO_BF16 || c->d_head != 128))
     return fail(DUO_EUNSUPPORTED, "FP8 and INT4 K/V rows are built for bf16 and d_head 128");
   if (c->T_cap < 1) return fail(DUO_EINVAL, "T_cap must be >= 1");
-  if (c->T_cap > INT32_MAX) return fail(DUO_EINVAL, "T_cap must fit int32 (positions are int32)");
+  // positions are int32, and the decode's row arithmetic runs a few rounds
+  // past a head's end in int32
+  if (c->T_cap > INT32_MAX - 4096) return fail(DUO_EINVAL, "T_cap must be at most 2^31 - 4097 (positions are int32)");
   if (c->page_rows != 0) {
     if (c->page_rows < 64 || c->page_rows > (1 << 20) || (c->page_rows & (c->page_rows - 1)) != 0)
       return fail(DUO_EINVAL, "page_rows %d must be 0 or a power of two in [64, 2^20]", c->page_rows);

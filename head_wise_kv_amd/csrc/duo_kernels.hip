@@ -1563,7 +1563,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     w.cnt = row_count(a, w.b);
     if (last_item) end_last_item(a, w);
   }
-  const int64_t nrounds = ((w.r1 - w.r0 + TR - 1) / TR + SLOTS - 1) / SLOTS;
+  // The item's rows in 32-bit wavefront-uniform values (the host keeps T_cap
+  // at least 4,096 under 2^31, so a round past the item's end still fits),
+  // so the per-unit row arithmetic is a few scalar instructions.
+  const int32_t r0 = __builtin_amdgcn_readfirstlane((int)w.r0), r1 = __builtin_amdgcn_readfirstlane((int)w.r1);
+  const int32_t nrounds = ((r1 - r0 + TR - 1) / TR + SLOTS - 1) / SLOTS;
   const size_t q_off = ((size_t)w.b * a.n_q + (size_t)w.kvh * G) * D;  // first query of the group
 
   // fused append: the last item of every head adds the new token at position
@@ -1573,8 +1577,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   const bool ret_head = w.hh < (int64_t)a.B * a.n_ret;
   const int64_t cap_str = a.cap_str;
   // streaming slot masked in the held rows (its token is evicted by the new one)
-  const int64_t excl_row =
-      (a.new_k != nullptr && !ret_head && w.cnt >= cap_str) ? a.S + (w.cnt - a.S) % a.W : -1;
+  const int32_t excl_row =
+      (a.new_k != nullptr && !ret_head && w.cnt >= cap_str) ? (int32_t)(a.S + (w.cnt - a.S) % a.W) : -1;
   // per-lane byte offset, within a round of rows, of this wavefront's load
   // pieces: piece n of a unit covers LDS bytes [n*1024, n*1024+1024), lane i
   // byte n*1024 + 16 i, i.e. row (n*1024 + 16 i) / ROWB of the round at a
@@ -1601,10 +1605,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   // piece is out of range (it reads nothing and writes zeros to LDS) but is
   // still issued, so each wavefront has the same number of loads per unit,
   // and every byte of a unit is written before it is read.
-  auto issue = [&](int64_t uu, char* dst) {
-    const int64_t row0 = w.r0 + (uu >> 1) * (int64_t)C::ROUND_ROWS;
-    const int64_t left = w.r1 - row0;
-    const int rows = (int)(left <= 0 ? 0 : (left > C::ROUND_ROWS ? C::ROUND_ROWS : left));
+  auto issue = [&](int32_t uu, char* dst) {
+    const int32_t row0 = r0 + (uu >> 1) * C::ROUND_ROWS;
+    const int32_t left = r1 - row0;
+    const int rows = left <= 0 ? 0 : (left > C::ROUND_ROWS ? C::ROUND_ROWS : left);
     const int64_t roff = rows > 0 ? w.at(row0) : 0;
     const char* src = ((uu & 1) ? w.vbase : w.kbase) + (size_t)roff * C::ROWB;
     const i32x4_t rs = dma_rsrc(src, rows * C::ROWB);
@@ -1708,14 +1712,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   }
 
   // Unit u of the stream, held in ring unit X = u % 4 (K rows when X is even).
-  auto unit = [&](auto tag, int64_t u) {
+  auto unit = [&](auto tag, int32_t u) {
     constexpr int X = decltype(tag)::value;
     constexpr bool V_PART = (X & 1) != 0;
     wait_vmcnt<V_PART ? WAITV : WAITN>();  // unit u has landed; the next DEPTH - 1 may be in flight
     lds_barrier();                          // ... for every wavefront; unit u-1 is consumed
     issue(u + DEPTH, rings[(X + DEPTH) % kRingUnits]);
-    const int64_t row0 = w.r0 + ((u >> 1) * SLOTS + slot) * (int64_t)TR;
-    const int64_t left = w.r1 - row0;
+    const int32_t row0 = r0 + ((u >> 1) * SLOTS + slot) * TR;
+    const int32_t left = r1 - row0;
     const int nv = active ? (int)(left < 0 ? 0 : (left > TR ? TR : left)) : 0;
     const char* tile = rings[X] + slot * C::SLOT_BYTES;
     if (V_PART) {
@@ -1731,7 +1735,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
         if (nv > 0) tile_pv<KT, D, G>(st, p, tile, rg, s);
       }
     } else {
-      const int64_t ex = excl_row - row0;
+      const int32_t ex = excl_row - row0;
       const int exr = (ex >= 0 && ex < TR) ? (int)ex : -1;
       if constexpr (MF && LOWBIT) {
         const float* ks = &sbuf[(u >> 1) & 1][slot * TR];
@@ -1750,8 +1754,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
       }
     }
   };
-  const int64_t n_units = 2 * nrounds;
-  for (int64_t u = 0; u < n_units; u += 4) {  // n_units is even
+  const int32_t n_units = 2 * nrounds;
+  for (int32_t u = 0; u < n_units; u += 4) {  // n_units is even
     unit(UnitTag<0>{}, u);
     unit(UnitTag<1>{}, u + 1);
     if (u + 2 >= n_units) break;

@@ -90,7 +90,8 @@ typedef enum { DUO_KV_NATIVE = 0, DUO_KV_FP8 = 1, DUO_KV_INT4 = 2 } duo_kv_forma
 /* Cache configuration.  d_head in {64, 128}; g = n_q / n_kv any integer from 1
  * to 16 for bf16 with d_head 128 (every kv_format: the scores run on the
  * matrix cores, one query per column of a 16-column tile), from 1 to 8 for
- * fp32 or d_head 64 (the vector-ALU decode); n_kv <= 128; 1 <= B <= 64; S >= 0; W >= 1; T_cap >= 1.  Each batch row keeps
+ * fp32 or d_head 64 (the vector-ALU decode); n_kv <= 128; 1 <= B <= 64; S >= 0; W >= 1;
+ * 1 <= T_cap <= 2^31 - 4097.  Each batch row keeps
  * its own token count and attends over what it holds (a ragged batch).
  * retrieval_mask is a host array uint8 [L][n_kv] (1 = retrieval head,
  * 0 = streaming head); it is copied.

@@ -124,6 +124,7 @@ BAD = [
     (dict(sink=-1), H.DUO_EINVAL),
     (dict(recent=0), H.DUO_EINVAL),
     (dict(T_cap=0), H.DUO_EINVAL),
+    (dict(T_cap=2 ** 31 - 4096), H.DUO_EINVAL),              # within 4,096 of 2^31
     (dict(L=0), H.DUO_EINVAL),
     (dict(mask_value=2), H.DUO_EINVAL),
     (dict(dtype_code=7), H.DUO_EUNSUPPORTED),
