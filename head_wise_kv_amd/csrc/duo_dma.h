@@ -66,10 +66,9 @@ __device__ __forceinline__ void dma_lds16(i32x4_t rsrc, char* lds, uint32_t voff
   dma_lds16_at(rsrc, lds_addr(lds), voff, 0);
 }
 
-// The same with 4 bytes per lane: lane i writes LDS bytes [lds + 4 i, lds + 4 i + 4).
-__device__ __forceinline__ void dma_lds4(i32x4_t rsrc, char* lds, uint32_t voff) {
-  const uint32_t m0v =
-      __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) char*)lds);
+// The same with 4 bytes per lane: lane i writes LDS bytes [m0v + 4 i, m0v + 4 i + 4),
+// m0v an LDS byte address.
+__device__ __forceinline__ void dma_lds4_at(i32x4_t rsrc, uint32_t m0v, uint32_t voff) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -80,6 +79,10 @@ __device__ __forceinline__ void dma_lds4(i32x4_t rsrc, char* lds, uint32_t voff)
       : "=&s"(saved)
       : "s"(m0v), "v"(voff), "s"(rsrc)
       : "memory");
+}
+
+__device__ __forceinline__ void dma_lds4(i32x4_t rsrc, char* lds, uint32_t voff) {
+  dma_lds4_at(rsrc, lds_addr(lds), voff);
 }
 
 }  // namespace

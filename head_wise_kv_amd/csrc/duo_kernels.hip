@@ -1532,6 +1532,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   // one buffer per K unit of the ring (units 0 and 2), loaded with that unit
   constexpr bool KV8 = C::KV8, KV4 = C::KV4, LOWBIT = C::LOWBIT;
   __shared__ __attribute__((aligned(16))) float sbuf[LOWBIT ? 2 : 1][LOWBIT ? 2 * C::ROUND_ROWS : 4];
+  [[maybe_unused]] const uint32_t sbuf_lds = lds_addr(&sbuf[0][0]);  // its LDS byte address
   // a round's scales: SPW wavefront loads of 64 rows per wavefront (waves 0-3
   // the K scales, 4-7 the V scales); FP8 rounds hold 256 rows, INT4 rounds 512
   constexpr int SPW = LOWBIT ? C::ROUND_ROWS / 256 : 0;
@@ -1545,6 +1546,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   constexpr int WAITN = DEPTH == 3 ? 2 * kPiecesPerWave + SPW : kPiecesPerWave;
   constexpr int WAITV = DEPTH == 3 ? 2 * kPiecesPerWave + SPW : kPiecesPerWave + SPW;
   char* const rings[kRingUnits] = {ring0, ring1, ring2, ring3};  // indexed by constants only
+  // their LDS byte addresses (constants), where the direct loads write
+  const uint32_t ring_lds[kRingUnits] = {lds_addr(ring0), lds_addr(ring1), lds_addr(ring2), lds_addr(ring3)};
   auto ring_at = [&](int i) -> char* { return i == 0 ? ring0 : i == 1 ? ring1 : i == 2 ? ring2 : ring3; };
 
   const int lane = threadIdx.x & 63;
@@ -1605,7 +1608,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   // piece is out of range (it reads nothing and writes zeros to LDS) but is
   // still issued, so each wavefront has the same number of loads per unit,
   // and every byte of a unit is written before it is read.
-  auto issue = [&](int32_t uu, char* dst) {
+  auto issue = [&](int32_t uu, uint32_t dst) {  // dst: the ring unit's LDS byte address
     const int32_t row0 = r0 + (uu >> 1) * C::ROUND_ROWS;
     const int32_t left = r1 - row0;
     const int rows = left <= 0 ? 0 : (left > C::ROUND_ROWS ? C::ROUND_ROWS : left);
@@ -1614,7 +1617,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     const i32x4_t rs = dma_rsrc(src, rows * C::ROWB);
 #pragma unroll
     for (int j = 0; j < kPiecesPerWave; ++j)
-      dma_lds16(rs, dst + (wave + kDecWaves * j) * 1024, (uu & 1) ? poff_v[j] : poff_k[j]);
+      dma_lds16_at(rs, dst + (uint32_t)((wave + kDecWaves * j) * 1024), (uu & 1) ? poff_v[j] : poff_k[j], 0u);
     if constexpr (LOWBIT) {
       if ((uu & 1) == 0) {  // wavefronts 0-3: K scales, 4-7: V scales, SPW x 64 rows each
         const int tensor = wave >> 2, part = wave & 3;
@@ -1622,8 +1625,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
         const i32x4_t srs = dma_rsrc(reinterpret_cast<const char*>(ssrc), rows * 4);
 #pragma unroll
         for (int j = 0; j < SPW; ++j)
-          dma_lds4(srs, reinterpret_cast<char*>(&sbuf[(uu >> 1) & 1][tensor * C::ROUND_ROWS + (part * SPW + j) * 64]),
-                   (uint32_t)(((part * SPW + j) * 64 + lane) * 4));
+          dma_lds4_at(srs,
+                      sbuf_lds + (uint32_t)((((uu >> 1) & 1) * 2 * C::ROUND_ROWS + tensor * C::ROUND_ROWS +
+                                             (part * SPW + j) * 64) * 4),
+                      (uint32_t)(((part * SPW + j) * 64 + lane) * 4));
       }
     }
   };
@@ -1631,7 +1636,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   // into the staging area (one load piece per wavefront for the first
   // wavefronts), then the next DEPTH - 1 units.  Unit 0's wait below covers
   // the staging loads, which were issued before those units.
-  issue(0, ring0);
+  issue(0, ring_lds[0]);
   {
     constexpr int PPR = QGROUP / 1024;  // query pieces per batch row
     const int nqp = w.qrows * PPR;      // query pieces of this item
@@ -1644,8 +1649,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
       dma_lds16(dma_rsrc(nsrc, C::IROWB), stage + QSTAGE + (wave - nqp) * NSTAGE, (uint32_t)(lane * 16));
     }
   }
-  issue(1, ring1);
-  if constexpr (DEPTH == 3) issue(2, ring2);
+  issue(1, ring_lds[1]);
+  if constexpr (DEPTH == 3) issue(2, ring_lds[2]);
   // rotary positions: this lane's angle (pair lane % (D/2)) at the query's
   // position, computed while the loads are in flight
   // (a shared item's rows each have their own position: it takes their
@@ -1717,7 +1722,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     constexpr bool V_PART = (X & 1) != 0;
     wait_vmcnt<V_PART ? WAITV : WAITN>();  // unit u has landed; the next DEPTH - 1 may be in flight
     lds_barrier();                          // ... for every wavefront; unit u-1 is consumed
-    issue(u + DEPTH, rings[(X + DEPTH) % kRingUnits]);
+    issue(u + DEPTH, ring_lds[(X + DEPTH) % kRingUnits]);
     const int32_t row0 = r0 + ((u >> 1) * SLOTS + slot) * TR;
     const int32_t left = r1 - row0;
     const int nv = active ? (int)(left < 0 ? 0 : (left > TR ? TR : left)) : 0;
